@@ -1,0 +1,239 @@
+"""fp64 CPU oracle for the exact-attention forward pass (ctypes front end).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this package; the library's compute path never
+does.  It shares no code with the HIP path.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, S and P materialised,
+three-pass softmax); this module only marshals numpy arrays.  Inputs are raw
+bfloat16 bit patterns as ``numpy.uint16`` arrays.  Outputs are float64.
+
+Parity-pin status of each function is listed in the header of ``oracle.c``
+and in the tests under ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so next to it (always recompiles)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-fPIC", "-shared", "-o", tmp, _SRC,
+           "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    L = ctypes.c_long
+    D = ctypes.c_double
+    I64 = ctypes.c_int64
+    lib.oracle_version.restype = I
+    lib.oracle_fwd_dense.argtypes = [P, P, P, I, L, L, I, I, I, D, I, L, L, D, P, I64, P, P, I]
+    lib.oracle_fwd_dense.restype = I
+    lib.oracle_fwd_varlen.argtypes = [P, P, P, P, P, I, I, I, I, D, I, L, L, D, P, I64, P, P, I]
+    lib.oracle_fwd_varlen.restype = I
+    lib.oracle_fwd_paged.argtypes = [P, P, P, P, P, I, L, I, I, I, L, L, D, I, L, L, D, I, I,
+                                     P, I64, P, P, I]
+    lib.oracle_fwd_paged.restype = I
+    lib.oracle_combine.argtypes = [P, P, I, I64, I, P, P]
+    lib.oracle_combine.restype = None
+    lib.oracle_online_dense.argtypes = [P, P, P, I, L, L, I, I, I, D, I, L, L, D, L, P, I64, P, P]
+    lib.oracle_online_dense.restype = I
+    lib.oracle_probs_dense.argtypes = [P, P, P, I, L, L, I, I, I, D, I, L, L, D, L, P]
+    lib.oracle_probs_dense.restype = I
+    _lib = lib
+    return lib
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("oracle inputs are bfloat16 bit patterns (numpy.uint16)")
+    return a
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a) -> int | None:
+    return None if a is None else a.ctypes.data
+
+
+def _rows(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    return r, int(r.size)
+
+
+def _scale(scale, d):
+    # default softmax scale d^-0.5 ("FA4 (CuTeDSL) and engineering interfaces", section 3)
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _window(window):
+    wl, wr = (-1, -1) if window is None else window
+    return int(wl), int(wr)
+
+
+def fwd_dense(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0,
+              rows=None, nthreads=0):
+    """Dense BSHD forward.  q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] (uint16 bf16 bits).
+
+    Returns (O, LSE).  With rows=None: O [B, Nq, Hq, d], LSE [B, Hq, Nq].
+    With rows (flat indices r = (b*Hq + h)*Nq + i): O [n, d], LSE [n].
+    """
+    lib = _load()
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    rr, n = _rows(rows)
+    total = B * Hq * Nq if rr is None else n
+    o = np.empty((total, d), np.float64)
+    lse = np.empty((total,), np.float64)
+    wl, wr = _window(window)
+    rc = lib.oracle_fwd_dense(_ptr(q), _ptr(k), _ptr(v), B, Nq, Nk, Hq, Hkv, d,
+                              _scale(scale, d), int(bool(causal)), wl, wr, float(softcap),
+                              _ptr(rr), n, _ptr(o), _ptr(lse), int(nthreads))
+    if rc < 0:
+        raise ValueError("oracle_fwd_dense rejected its arguments")
+    if rr is None:
+        o = o.reshape(B, Hq, Nq, d).transpose(0, 2, 1, 3).copy()
+        lse = lse.reshape(B, Hq, Nq)
+    return o, lse
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, *, scale=None, causal=False, window=None,
+               softcap=0.0, rows=None, nthreads=0):
+    """Varlen forward.  q [Tq, Hq, d], k/v [Tk, Hkv, d], cu_q/cu_k [B+1].
+
+    Returns (O, LSE).  With rows=None: O [Tq, Hq, d], LSE [Hq, Tq].
+    With rows (flat indices r = h*Tq + t): O [n, d], LSE [n].
+    """
+    lib = _load()
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    cu_q, cu_k = _i32(cu_q), _i32(cu_k)
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    B = cu_q.size - 1
+    rr, n = _rows(rows)
+    total = Hq * Tq if rr is None else n
+    o = np.empty((total, d), np.float64)
+    lse = np.empty((total,), np.float64)
+    wl, wr = _window(window)
+    rc = lib.oracle_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_k), B, Hq, Hkv, d,
+                               _scale(scale, d), int(bool(causal)), wl, wr, float(softcap),
+                               _ptr(rr), n, _ptr(o), _ptr(lse), int(nthreads))
+    if rc < 0:
+        raise ValueError("oracle_fwd_varlen rejected its arguments")
+    if rr is None:
+        o = o.reshape(Hq, Tq, d).transpose(1, 0, 2).copy()
+        lse = lse.reshape(Hq, Tq)
+    return o, lse
+
+
+def fwd_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, scale=None,
+              causal=True, window=None, softcap=0.0, num_splits=0, split=0,
+              rows=None, nthreads=0):
+    """Paged-KV forward.  q [B, Nq, Hq, d]; caches [num_pages, page, Hkv, d];
+    block_table [B, max_blocks]; cache_seqlens [B].
+
+    num_splits == 0 attends over the whole cache; num_splits > 0 returns the
+    normalised partial (O_s, LSE_s) of split `split` only.
+    Returns (O, LSE) shaped like fwd_dense.
+    """
+    lib = _load()
+    q, kc, vc = _u16(q), _u16(k_cache), _u16(v_cache)
+    bt, sl = _i32(block_table), _i32(cache_seqlens)
+    B, Nq, Hq, d = q.shape
+    page, Hkv = kc.shape[1], kc.shape[2]
+    max_blocks = bt.shape[1]
+    rr, n = _rows(rows)
+    total = B * Hq * Nq if rr is None else n
+    o = np.empty((total, d), np.float64)
+    lse = np.empty((total,), np.float64)
+    wl, wr = _window(window)
+    rc = lib.oracle_fwd_paged(_ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Nq, Hq, Hkv, d,
+                              page, max_blocks, _scale(scale, d), int(bool(causal)), wl, wr,
+                              float(softcap), int(num_splits), int(split), _ptr(rr), n,
+                              _ptr(o), _ptr(lse), int(nthreads))
+    if rc < 0:
+        raise ValueError("oracle_fwd_paged rejected its arguments")
+    if rr is None:
+        o = o.reshape(B, Hq, Nq, d).transpose(0, 2, 1, 3).copy()
+        lse = lse.reshape(B, Hq, Nq)
+    return o, lse
+
+
+def combine(o_part, lse_part):
+    """Merge partial states.  o_part [S, rows, d], lse_part [S, rows] (float64).
+    Returns (O [rows, d], LSE [rows])."""
+    lib = _load()
+    o_part = np.ascontiguousarray(o_part, dtype=np.float64)
+    lse_part = np.ascontiguousarray(lse_part, dtype=np.float64)
+    S, rows, d = o_part.shape
+    o = np.empty((rows, d), np.float64)
+    lse = np.empty((rows,), np.float64)
+    lib.oracle_combine(_ptr(o_part), _ptr(lse_part), S, rows, d, _ptr(o), _ptr(lse))
+    return o, lse
+
+
+def online_dense(q, k, v, *, block_n, scale=None, causal=False, window=None, softcap=0.0,
+                 rows=None):
+    """The (m, l, O) recurrence over key blocks of block_n keys; outputs as fwd_dense."""
+    lib = _load()
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    rr, n = _rows(rows)
+    total = B * Hq * Nq if rr is None else n
+    o = np.empty((total, d), np.float64)
+    lse = np.empty((total,), np.float64)
+    wl, wr = _window(window)
+    rc = lib.oracle_online_dense(_ptr(q), _ptr(k), _ptr(v), B, Nq, Nk, Hq, Hkv, d,
+                                 _scale(scale, d), int(bool(causal)), wl, wr, float(softcap),
+                                 int(block_n), _ptr(rr), n, _ptr(o), _ptr(lse))
+    if rc < 0:
+        raise ValueError("oracle_online_dense rejected its arguments")
+    if rr is None:
+        o = o.reshape(B, Hq, Nq, d).transpose(0, 2, 1, 3).copy()
+        lse = lse.reshape(B, Hq, Nq)
+    return o, lse
+
+
+def probs_dense(q, k, v, row, *, scale=None, causal=False, window=None, softcap=0.0):
+    """The materialised probability row P[row, :] (length Nk) of a dense problem."""
+    lib = _load()
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    p = np.empty((Nk,), np.float64)
+    wl, wr = _window(window)
+    rc = lib.oracle_probs_dense(_ptr(q), _ptr(k), _ptr(v), B, Nq, Nk, Hq, Hkv, d,
+                                _scale(scale, d), int(bool(causal)), wl, wr, float(softcap),
+                                int(row), _ptr(p))
+    if rc < 0:
+        raise ValueError("oracle_probs_dense rejected its arguments")
+    return p

@@ -1,0 +1,320 @@
+"""Pins for the fp64 oracle: each test ties it to something other than itself.
+
+Kinds of pin used here:
+  * worked examples the pages print (fixtures under tests/golden/, each cited);
+  * closed forms (Q = 0 makes every visible logit equal, so O is the mean of
+    the visible V rows and exp(LSE) is the number of visible keys; a single
+    visible key gives O = v exactly);
+  * invariants the pages state (probability rows sum to one, the online
+    recurrence equals the three-pass softmax, split + merge equals one pass);
+  * library routines on special cases (torch fp64 scaled_dot_product_attention
+    and logsumexp on the CPU, the pages' own reference).
+All inputs are tiny so the whole file runs in seconds on the CPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from exact_attention_72_amd import workloads as W
+
+
+def bits(t):
+    return W.to_bits(t)
+
+
+def zeros_bf16(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def v_double(t):
+    return t.double().numpy()
+
+
+# ---------------------------------------------------------------- worked examples
+
+def test_cu_seqlens_worked_example(golden):
+    g = golden("cu_seqlens_example.json")
+    cu = W.prefix_sum(g["lengths"])
+    assert cu.tolist() == g["cu_seqlens"]
+    T, d, H = g["total"], 8, 2
+    q = zeros_bf16(T, H, d)
+    k = W.randn_bf16(W.generator(11), (T, H, d))
+    v = W.randn_bf16(W.generator(12), (T, H, d))
+    o, lse = oracle.fwd_varlen(bits(q), bits(k), bits(v), g["cu_seqlens"], g["cu_seqlens"])
+    # every row sees exactly the keys of its own sequence, no more, no fewer
+    expected = np.repeat(np.array(g["lengths"]), g["lengths"])
+    for h in range(H):
+        assert np.array_equal(np.rint(np.exp(lse[h])).astype(int), expected)
+    # uniform weights: O is the mean of the sequence's V rows
+    vd = v_double(v)
+    for s in range(len(g["lengths"])):
+        a, b = g["cu_seqlens"][s], g["cu_seqlens"][s + 1]
+        np.testing.assert_allclose(o[a:b], np.broadcast_to(vd[a:b].mean(0), o[a:b].shape),
+                                   rtol=0, atol=1e-14)
+
+
+def test_bottom_right_causal_example(golden):
+    g = golden("bottom_right_causal_example.json")
+    d = 8
+    q = zeros_bf16(1, g["seqlen_q"], 1, d)
+    k = W.randn_bf16(W.generator(21), (1, g["seqlen_k"], 1, d))
+    v = W.randn_bf16(W.generator(22), (1, g["seqlen_k"], 1, d))
+    _, lse = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=True)
+    assert np.rint(np.exp(lse[0, 0])).astype(int).tolist() == g["visible_counts"]
+
+
+def test_chunked_prefill_example(golden):
+    g = golden("chunked_prefill_example.json")
+    cu_q = g["cu_seqlens_q"]
+    cu_k = W.prefix_sum(g["seq_lens_k"]).tolist()
+    d, H = 8, 1
+    q = zeros_bf16(cu_q[-1], H, d)
+    k = W.randn_bf16(W.generator(31), (cu_k[-1], H, d))
+    v = W.randn_bf16(W.generator(32), (cu_k[-1], H, d))
+    _, lse = oracle.fwd_varlen(bits(q), bits(k), bits(v), cu_q, cu_k, causal=True)
+    assert np.rint(np.exp(lse[0])).astype(int).tolist() == g["visible_counts"]
+
+
+def test_block_table_example(golden):
+    g = golden("block_table_example.json")
+    P, npages, d = g["page_size"], g["num_pages"], 8
+    L = P * len(g["block_table"])
+    kc = W.randn_bf16(W.generator(41), (npages, P, 1, d))
+    vc = W.randn_bf16(W.generator(42), (npages, P, 1, d))
+    q = W.randn_bf16(W.generator(43), (1, L, 1, d))
+    bt = np.array([g["block_table"]], np.int32)
+    # window (0, 0) with L queries over L keys: row i sees only logical key i
+    o, lse = oracle.fwd_paged(bits(q), bits(kc), bits(vc), bt, [L], causal=False, window=(0, 0))
+    vd, kd, qd = v_double(vc), v_double(kc), v_double(q)
+    for lo, hi, phys in g["token_ranges_to_physical"]:
+        for t in range(lo, hi + 1):
+            assert np.array_equal(o[0, t, 0], vd[phys, t - lo, 0])
+            s = float(qd[0, t, 0] @ kd[phys, t - lo, 0]) / math.sqrt(d)
+            assert abs(lse[0, 0, t] - s) < 1e-12
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (True, (5, 0)),
+                                           (False, (3, 2)), (False, (0, 4))])
+def test_zero_query_counts_and_means(causal, window):
+    N, d = 37, 16
+    q = zeros_bf16(2, N, 3, d)
+    k = W.randn_bf16(W.generator(51), (2, N, 3, d))
+    v = W.randn_bf16(W.generator(52), (2, N, 3, d))
+    o, lse = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=causal, window=window)
+    i = np.arange(N)
+    wl, wr = window
+    lo = np.zeros(N, int) if wl < 0 else np.maximum(0, i - wl)
+    hi = np.full(N, N - 1) if (wr < 0 and not causal) else np.minimum(N - 1, i + (0 if causal else wr))
+    if causal and wr > 0:
+        hi = np.minimum(hi, i)
+    counts = hi - lo + 1
+    vd = v_double(v)
+    for b in range(2):
+        for h in range(3):
+            assert np.array_equal(np.rint(np.exp(lse[b, h])).astype(int), counts)
+            np.testing.assert_allclose(lse[b, h], np.log(counts), rtol=0, atol=1e-14)
+            for r in range(N):
+                np.testing.assert_allclose(o[b, r, h], vd[b, lo[r]:hi[r] + 1, h].mean(0),
+                                           rtol=0, atol=1e-14)
+
+
+def test_single_key_gives_its_value():
+    d = 32
+    q = W.randn_bf16(W.generator(61), (3, 1, 2, d))
+    k = W.randn_bf16(W.generator(62), (3, 1, 2, d))
+    v = W.randn_bf16(W.generator(63), (3, 1, 2, d))
+    for softcap in (0.0, 5.0):
+        o, lse = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=True, softcap=softcap)
+        assert np.array_equal(o, v_double(v))
+        s = np.einsum("bnhd,bnhd->bhn", v_double(q), v_double(k)) / math.sqrt(d)
+        if softcap:
+            s = softcap * np.tanh(s / softcap)
+        np.testing.assert_allclose(lse, s, rtol=0, atol=1e-12)
+
+
+def test_row_without_visible_key_is_zero_and_minus_inf():
+    # more queries than keys under bottom-right causal: the first rows see nothing
+    d = 8
+    q = W.randn_bf16(W.generator(71), (1, 6, 1, d))
+    k = W.randn_bf16(W.generator(72), (1, 3, 1, d))
+    v = W.randn_bf16(W.generator(73), (1, 3, 1, d))
+    o, lse = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=True)
+    assert np.all(np.isneginf(lse[0, 0, :3])) and np.all(np.isfinite(lse[0, 0, 3:]))
+    assert np.all(o[0, :3] == 0.0)
+    assert not np.any(np.isnan(o))
+
+
+def test_softcap_two_key_closed_form():
+    # q = a e0, k_j = b_j e0: raw logits scale*a*b_j; the cap acts on the scaled logit
+    d, c = 4, 3.0
+    a, b1, b2 = 4.0, 3.0, -1.5            # exactly representable in bf16
+    q = torch.zeros(1, 1, 1, d); q[..., 0] = a
+    k = torch.zeros(1, 2, 1, d); k[0, 0, 0, 0] = b1; k[0, 1, 0, 0] = b2
+    v = W.randn_bf16(W.generator(81), (1, 2, 1, d))
+    scale = 0.5
+    o, lse = oracle.fwd_dense(bits(q.bfloat16()), bits(k.bfloat16()), bits(v), scale=scale,
+                              softcap=c)
+    s1, s2 = c * math.tanh(scale * a * b1 / c), c * math.tanh(scale * a * b2 / c)
+    p1 = 1.0 / (1.0 + math.exp(s2 - s1))
+    vd = v_double(v)
+    np.testing.assert_allclose(o[0, 0, 0], p1 * vd[0, 0, 0] + (1 - p1) * vd[0, 1, 0], atol=1e-14)
+    assert abs(lse[0, 0, 0] - (max(s1, s2) + math.log(math.exp(s1 - max(s1, s2))
+                                                     + math.exp(s2 - max(s1, s2))))) < 1e-14
+
+
+def test_huge_softcap_is_no_softcap():
+    q, k, v = (W.dense(91, 1, 24, 2, 2, 16)[n] for n in "qkv")
+    o0, l0 = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=True)
+    o1, l1 = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=True, softcap=1e7)
+    np.testing.assert_allclose(o1, o0, atol=1e-10)
+    np.testing.assert_allclose(l1, l0, atol=1e-10)
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("causal,window,softcap", [(False, None, 0.0), (True, None, 0.0),
+                                                   (True, (6, 0), 2.0), (False, (2, 3), 0.0)])
+def test_probability_rows_sum_to_one(causal, window, softcap):
+    t = W.dense(101, 1, 20, 2, 1, 16, mult=2.0)
+    for r in range(0, 40, 3):
+        p = oracle.probs_dense(bits(t["q"]), bits(t["k"]), bits(t["v"]), r, causal=causal,
+                               window=window, softcap=softcap)
+        assert np.all(p >= 0)
+        assert abs(p.sum() - 1.0) < 1e-12
+
+
+@pytest.mark.parametrize("block_n", [1, 3, 16, 64])
+@pytest.mark.parametrize("causal,window,softcap", [(False, None, 0.0), (True, None, 0.0),
+                                                   (True, (9, 0), 4.0)])
+def test_online_recurrence_equals_three_pass(block_n, causal, window, softcap):
+    t = W.dense(111, 2, 45, 4, 2, 32, mult=2.0)
+    args = [bits(t[n]) for n in "qkv"]
+    o3, l3 = oracle.fwd_dense(*args, causal=causal, window=window, softcap=softcap)
+    o1, l1 = oracle.online_dense(*args, block_n=block_n, causal=causal, window=window,
+                                 softcap=softcap)
+    assert np.max(np.abs(o1 - o3)) <= 1e-12
+    assert np.max(np.abs(l1 - l3)) <= 1e-12
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 16])
+def test_split_and_merge_equals_one_pass(S):
+    page = 16
+    lens = [1, 15, 16, 17, 40, 100, 160]   # some splits are empty at S = 16
+    t = W.paged(121, len(lens), 4, 2, 32, page, 0, 0, cache_seqlens=lens)
+    args = [bits(t["q"]), bits(t["k_cache"]), bits(t["v_cache"]), t["block_table"].numpy(),
+            t["cache_seqlens"].numpy()]
+    o, lse = oracle.fwd_paged(*args)
+    parts = [oracle.fwd_paged(*args, num_splits=S, split=s) for s in range(S)]
+    B, Nq, Hq, d = t["q"].shape
+    # partial O in row order [B, Hq, Nq] to match LSE rows
+    op = np.stack([p[0].transpose(0, 2, 1, 3).reshape(-1, d) for p in parts])
+    lp = np.stack([p[1].reshape(-1) for p in parts])
+    om, lm = oracle.combine(op, lp)
+    assert np.max(np.abs(om - o.transpose(0, 2, 1, 3).reshape(-1, d))) <= 1e-12
+    assert np.max(np.abs(lm - lse.reshape(-1))) <= 1e-12
+    if S == 16:  # at least one split is empty and contributes weight zero
+        assert np.any(np.isneginf(lp))
+
+
+def test_combine_of_all_empty_parts():
+    op = np.zeros((3, 2, 4))
+    lp = np.full((3, 2), -np.inf)
+    o, l = oracle.combine(op, lp)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+# ---------------------------------------------------------------- library routines
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (6, 1)])
+def test_against_torch_fp64_sdpa(causal, Hq, Hkv):
+    B, N, d = 2, 33, 16
+    t = W.dense(131, B, N, Hq, Hkv, d)
+    o, lse = oracle.fwd_dense(*(bits(t[n]) for n in "qkv"), causal=causal)
+    q, k, v = (t[n].double().transpose(1, 2) for n in "qkv")    # [B, H, N, d]
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=causal, enable_gqa=True)
+    np.testing.assert_allclose(o, ref.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            s = (q[b, h] @ k[b, h // g].T) / math.sqrt(d)
+            if causal:
+                s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+            np.testing.assert_allclose(lse[b, h], torch.logsumexp(s, -1).numpy(), rtol=0,
+                                       atol=1e-12)
+
+
+def test_window_against_torch_fp64_sdpa_with_band_mask():
+    B, N, H, d, wl = 1, 40, 2, 16, 7
+    t = W.dense(141, B, N, H, H, d)
+    o, lse = oracle.fwd_dense(*(bits(t[n]) for n in "qkv"), causal=True, window=(wl, 0))
+    band = torch.ones(N, N, dtype=torch.bool).tril(0).triu(-wl)      # keys i-wl .. i
+    q, k, v = (t[n].double().transpose(1, 2) for n in "qkv")
+    ref = F.scaled_dot_product_attention(q, k, v, attn_mask=band)
+    np.testing.assert_allclose(o, ref.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- reductions between layouts
+
+def test_gqa_equals_mha_with_repeated_kv():
+    t = W.dense(151, 2, 19, 8, 2, 16)
+    o_g, l_g = oracle.fwd_dense(*(bits(t[n]) for n in "qkv"), causal=True)
+    k4 = t["k"].repeat_interleave(4, dim=2)
+    v4 = t["v"].repeat_interleave(4, dim=2)
+    o_m, l_m = oracle.fwd_dense(bits(t["q"]), bits(k4), bits(v4), causal=True)
+    assert np.array_equal(o_g, o_m) and np.array_equal(l_g, l_m)
+
+
+def test_varlen_equals_dense_per_sequence():
+    lens = [5, 1, 17, 9]
+    t = W.varlen(161, 4, 0, 0, 4, 2, 16, lengths=lens)
+    cu = t["cu_seqlens"].tolist()
+    o, lse = oracle.fwd_varlen(*(bits(t[n]) for n in "qkv"), cu, cu, causal=True)
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        sub = [bits(t[n][a:b].unsqueeze(0)) for n in "qkv"]
+        od, ld = oracle.fwd_dense(*sub, causal=True)
+        assert np.array_equal(o[a:b], od[0]) and np.array_equal(lse[:, a:b], ld[0])
+
+
+def test_paged_equals_dense_on_logical_sequence():
+    page, lens = 8, [3, 8, 29]
+    t = W.paged(171, 3, 4, 2, 16, page, 0, 0, cache_seqlens=lens, Nq=2)
+    bt = t["block_table"]
+    for b, L in enumerate(lens):
+        pages = bt[b, : (L + page - 1) // page].long()
+        kl = t["k_cache"][pages].reshape(-1, 2, 16)[:L].unsqueeze(0)
+        vl = t["v_cache"][pages].reshape(-1, 2, 16)[:L].unsqueeze(0)
+        q = t["q"][b:b + 1]
+        od, ld = oracle.fwd_dense(bits(q), bits(kl), bits(vl), causal=True)
+        op, lp = oracle.fwd_paged(bits(q), bits(t["k_cache"]), bits(t["v_cache"]),
+                                  bt[b:b + 1].numpy(), [L], causal=True)
+        assert np.array_equal(op, od) and np.array_equal(lp, ld)
+
+
+def test_decode_query_sees_whole_cache():
+    page, lens = 16, [1, 16, 33, 250]
+    t = W.paged(181, 4, 4, 1, 8, page, 0, 0, cache_seqlens=lens)
+    q = zeros_bf16(*t["q"].shape)
+    _, lse = oracle.fwd_paged(bits(q), bits(t["k_cache"]), bits(t["v_cache"]),
+                              t["block_table"].numpy(), lens, causal=True)
+    for b, L in enumerate(lens):
+        assert np.all(np.rint(np.exp(lse[b, :, 0])).astype(int) == L)
+
+
+def test_rows_subset_matches_full_output():
+    t = W.dense(191, 2, 30, 4, 2, 16)
+    args = [bits(t[n]) for n in "qkv"]
+    o, lse = oracle.fwd_dense(*args, causal=True, window=(7, 0), softcap=3.0)
+    rows = np.array([0, 7, 29, 30, 119, 200, 239])
+    os_, ls_ = oracle.fwd_dense(*args, causal=True, window=(7, 0), softcap=3.0, rows=rows)
+    B, N, H = 2, 30, 4
+    for n, r in enumerate(rows):
+        b, h, i = r // (H * N), (r // N) % H, r % N
+        assert np.array_equal(os_[n], o[b, i, h]) and ls_[n] == lse[b, h, i]
