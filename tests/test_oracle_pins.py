@@ -75,8 +75,16 @@ def test_chunked_prefill_example(golden):
     q = zeros_bf16(cu_q[-1], H, d)
     k = W.randn_bf16(W.generator(31), (cu_k[-1], H, d))
     v = W.randn_bf16(W.generator(32), (cu_k[-1], H, d))
-    _, lse = oracle.fwd_varlen(bits(q), bits(k), bits(v), cu_q, cu_k, causal=True)
+    o, lse = oracle.fwd_varlen(bits(q), bits(k), bits(v), cu_q, cu_k, causal=True)
     assert np.rint(np.exp(lse[0])).astype(int).tolist() == g["visible_counts"]
+    # uniform weights: each row's O is the mean of the first `count` V rows of its own
+    # request's keys (keys are addressed through cu_seqlens_k, queries through cu_seqlens_q)
+    vd = v_double(v)
+    for s in range(len(cu_q) - 1):
+        for t in range(cu_q[s], cu_q[s + 1]):
+            n = g["visible_counts"][t]
+            np.testing.assert_allclose(o[t, 0], vd[cu_k[s]:cu_k[s] + n, 0].mean(0), rtol=0,
+                                       atol=1e-14)
 
 
 def test_block_table_example(golden):
