@@ -1,0 +1,215 @@
+"""Thin ctypes binding over the C ABI in include/fa.h.
+
+Argument marshalling only: torch tensors supply device pointers, strides and
+the current HIP stream; every step of the computation runs in the HIP kernels
+of libfa72.so.  There is no fallback: if the library is missing or a call
+fails, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa72.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_HIP = -3
+
+EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_kvcache_workspace_size",
+           "fa_combine", "fa_tile_class", "fa_last_error", "fa_version")
+
+
+class FaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+class fa_attn_opts(ctypes.Structure):
+    _fields_ = [("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int),
+                ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
+                ("softcap", ctypes.c_float), ("pack_gqa", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libfa72.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with exact_attention_72_amd._build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    S3 = ctypes.POINTER(ctypes.c_int64)
+    OPT = ctypes.POINTER(fa_attn_opts)
+    L.fa_fwd.argtypes = [OPT, P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, S3, P]
+    L.fa_fwd_varlen.argtypes = [OPT, P, P, P, P, P, P, P, I, I, I, I, I, I, I, S3, S3, S3, S3, P]
+    L.fa_fwd_kvcache_paged.argtypes = [OPT, P, P, P, P, P, P, P, I, I, I, I, I, I64, I, I, I, P, SZ,
+                                       S3, S3, S3, S3, P]
+    L.fa_kvcache_workspace_size.argtypes = [I, I, I, I, I]
+    L.fa_kvcache_workspace_size.restype = SZ
+    L.fa_combine.argtypes = [P, P, I, I64, I, P, I64, P, P]
+    L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
+    L.fa_last_error.restype = ctypes.c_char_p
+    L.fa_version.restype = I
+    for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_combine", "fa_tile_class"):
+        getattr(L, name).restype = I
+    _lib = L
+    return L
+
+
+def _check(rc):
+    if rc != FA_OK:
+        raise FaError(rc, lib().fa_last_error().decode())
+
+
+def _strides(t, dims):
+    arr = (ctypes.c_int64 * len(dims))(*[t.stride(i) for i in dims])
+    return arr
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _opts(softmax_scale, causal, window, softcap, pack_gqa):
+    wl, wr = (-1, -1) if window is None else window
+    return fa_attn_opts(float(softmax_scale) if softmax_scale else 0.0, int(bool(causal)), int(wl),
+                        int(wr), float(softcap), int(pack_gqa))
+
+
+def _bf16_cuda(*ts):
+    for t in ts:
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, k, v, out must be bfloat16 tensors on a HIP device")
+        if t.stride(-1) != 1:
+            raise ValueError("the head_dim dimension must be contiguous")
+
+
+def fa_fwd(q, k, v, *, softmax_scale=None, causal=False, window=None, softcap=0.0, pack_gqa=-1,
+           out=None, lse=None, return_lse=True, stream=None):
+    """Dense forward.  q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] bf16 -> (out, lse [B, Hq, Nq])."""
+    _bf16_cuda(q, k, v)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _bf16_cuda(out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
+    _check(lib().fa_fwd(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Nq, Nk,
+                        Hq, Hkv, d, _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)),
+                        _strides(v, (0, 1, 2)), _strides(out, (0, 1, 2)), _stream(stream)))
+    return out, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *, softmax_scale=None,
+                  causal=False, window=None, softcap=0.0, pack_gqa=-1, out=None, lse=None,
+                  return_lse=True, stream=None):
+    """Varlen forward.  q [Tq, Hq, d], k/v [Tk, Hkv, d], cu_seqlens int32 on device
+    -> (out [Tq, Hq, d], lse [Hq, Tq])."""
+    _bf16_cuda(q, k, v)
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous():
+            raise TypeError("cu_seqlens must be contiguous int32 device tensors")
+    B = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _bf16_cuda(out)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
+    _check(lib().fa_fwd_varlen(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                               _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(max_seqlen_q), Tq, Tk,
+                               Hq, Hkv, d, _strides(q, (0, 1)), _strides(k, (0, 1)),
+                               _strides(v, (0, 1)), _strides(out, (0, 1)), _stream(stream)))
+    return out, lse
+
+
+def fa_kvcache_workspace_size(batch, seqlen_q, heads_q, head_dim, num_splits):
+    return int(lib().fa_kvcache_workspace_size(batch, seqlen_q, heads_q, head_dim, num_splits))
+
+
+def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num_splits=1,
+                         softmax_scale=None, causal=True, window=None, softcap=0.0, out=None,
+                         lse=None, workspace=None, return_lse=True, stream=None):
+    """Paged-KV forward.  q [B, Nq, Hq, d]; caches [num_pages, page, Hkv, d];
+    block_table int32 [B, max_blocks]; cache_seqlens int32 [B] -> (out, lse [B, Hq, Nq])."""
+    _bf16_cuda(q, k_cache, v_cache)
+    B, Nq, Hq, d = q.shape
+    num_pages, page, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    for c in (block_table, cache_seqlens):
+        if c.dtype != torch.int32 or not c.is_cuda:
+            raise TypeError("block_table and cache_seqlens must be int32 device tensors")
+    if block_table.stride(-1) != 1 or block_table.stride(0) != block_table.shape[1]:
+        raise ValueError("block_table must be a contiguous [batch, max_blocks] tensor")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _bf16_cuda(out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = fa_kvcache_workspace_size(B, Nq, Hq, d, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    o = _opts(softmax_scale, causal, window, softcap, 0)
+    _check(lib().fa_fwd_kvcache_paged(ctypes.byref(o), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(block_table), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
+                                      B, Nq, Hq, Hkv, d, num_pages, page, block_table.shape[1],
+                                      int(num_splits), _ptr(workspace), ws_bytes,
+                                      _strides(q, (0, 1, 2)), _strides(k_cache, (0, 1, 2)),
+                                      _strides(v_cache, (0, 1, 2)), _strides(out, (0, 1, 2)),
+                                      _stream(stream)))
+    return out, lse
+
+
+def fa_combine(o_part, lse_part, *, out=None, lse=None, stream=None):
+    """Merge partial states.  o_part fp32 [S, rows, d], lse_part fp32 [S, rows]
+    -> (out bf16 [rows, d], lse fp32 [rows])."""
+    S, rows, d = o_part.shape
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise TypeError("partials are float32")
+    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=o_part.device)
+    _check(lib().fa_combine(_ptr(o_part), _ptr(lse_part), S, rows, d, _ptr(out), out.stride(0),
+                            _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def fa_tile_class(tok_lo, tok_hi, seqlen_q, seqlen_k, causal, window_left, window_right, block_n, n):
+    return int(lib().fa_tile_class(tok_lo, tok_hi, seqlen_q, seqlen_k, int(bool(causal)),
+                                   window_left, window_right, block_n, n))
+
+
+def fa_last_error():
+    return lib().fa_last_error().decode()
+
+
+def fa_version():
+    return int(lib().fa_version())
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

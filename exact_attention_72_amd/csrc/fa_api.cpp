@@ -1,0 +1,296 @@
+// C ABI of the attention forward library: argument validation, launch
+// parameters, dispatch.  Declarations and the contract live in include/fa.h.
+//
+// Validation happens before any HIP call, so an invalid call returns an error
+// code with nothing enqueued and without touching the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/fa.h"
+#include "fa_blockinfo.h"
+#include "fa_internal.h"
+
+#define FA_VERSION_NUMBER 100  // 0.1.0
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Options -> score-transform constants.  softmax_scale <= 0 or NaN selects d^-0.5
+// ("FA4 (CuTeDSL) and engineering interfaces", section 3).
+int fill_opts(const fa_attn_opts* o, int d, FaParams* p, bool* softcap) {
+  if (!o) return fail(FA_ERR_INVALID_ARG, "opts is NULL");
+  float scale = o->softmax_scale;
+  if (!(scale > 0.0f) || isnan(scale) || isinf(scale)) scale = 1.0f / sqrtf((float)d);
+  if (isnan(o->softcap) || o->softcap < 0.0f || isinf(o->softcap))
+    return fail(FA_ERR_INVALID_ARG, "softcap must be a finite value >= 0");
+  const float log2e = 1.4426950408889634f;
+  p->scale_log2 = scale * log2e;
+  *softcap = o->softcap > 0.0f;
+  p->cap_in = *softcap ? scale / o->softcap : 0.0f;
+  p->cap_out = *softcap ? o->softcap * log2e : 0.0f;
+  p->causal = o->causal ? 1 : 0;
+  p->wl = o->window_left < 0 ? -1 : o->window_left;
+  p->wr = o->window_right < 0 ? -1 : o->window_right;
+  return FA_OK;
+}
+
+int check_dims(int d, int hq, int hkv) {
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d);
+  if (hq <= 0 || hkv <= 0) return fail(FA_ERR_INVALID_ARG, "head counts must be positive");
+  if (hq % hkv != 0) return fail(FA_ERR_INVALID_ARG, "heads_q %d is not a multiple of heads_kv %d", hq, hkv);
+  return FA_OK;
+}
+
+// Every row start must be 16-byte aligned: base pointer and all strides * 2 bytes.
+int check_strides(const char* name, const void* base, const int64_t* s, int n) {
+  if (!s) return fail(FA_ERR_INVALID_ARG, "%s strides are NULL", name);
+  if (!aligned16(base)) return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  for (int i = 0; i < n; ++i) {
+    if (s[i] < 0) return fail(FA_ERR_INVALID_ARG, "%s stride %d is negative", name, i);
+    if ((s[i] * 2) % 16 != 0)
+      return fail(FA_ERR_INVALID_ARG, "%s stride %d (%lld elements) breaks 16-byte row alignment", name, i,
+                  (long long)s[i]);
+  }
+  return FA_OK;
+}
+
+bool resolve_pack(const fa_attn_opts* o, int hq, int hkv) {
+  if (o->pack_gqa > 0) return true;
+  if (o->pack_gqa == 0) return false;
+  return hq > hkv;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_last_error(void) { return g_err; }
+
+int fa_version(void) { return FA_VERSION_NUMBER; }
+
+int fa_tile_class(int tok_lo, int tok_hi, int seqlen_q, int seqlen_k, int causal, int window_left,
+                  int window_right, int block_n, int n) {
+  if (block_n <= 0 || tok_hi < tok_lo) return 0;
+  FaRowSpan s;
+  s.pos_lo = (int64_t)tok_lo + (seqlen_k - seqlen_q);
+  s.pos_hi = (int64_t)tok_hi + (seqlen_k - seqlen_q);
+  return fa_tile_class(s, seqlen_k, causal ? 1 : 0, window_left < 0 ? -1 : window_left,
+                       window_right < 0 ? -1 : window_right, block_n, n);
+}
+
+int fa_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v, void* out, float* lse,
+           int batch, int seqlen_q, int seqlen_k, int heads_q, int heads_kv, int head_dim,
+           const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+           const int64_t o_strides[3], void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
+  if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_k <= 0)
+    return fail(FA_ERR_INVALID_ARG, "batch, seqlen_q and seqlen_k must be positive");
+  if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k", k, k_strides, 3)) ||
+      (rc = check_strides("v", v, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)))
+    return rc;
+  FaParams p;
+  memset(&p, 0, sizeof p);
+  bool softcap = false;
+  if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
+  const bool pack = resolve_pack(opts, heads_q, heads_kv);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.q_bs = q_strides[0]; p.q_ss = q_strides[1]; p.q_hs = q_strides[2];
+  p.k_bs = k_strides[0]; p.k_ss = k_strides[1]; p.k_hs = k_strides[2];
+  p.v_bs = v_strides[0]; p.v_ss = v_strides[1]; p.v_hs = v_strides[2];
+  p.o_bs = o_strides[0]; p.o_ss = o_strides[1]; p.o_hs = o_strides[2];
+  p.lse_bs = (int64_t)heads_q * seqlen_q;
+  p.lse_hs = seqlen_q;
+  p.B = batch; p.Nq = seqlen_q; p.Nk = seqlen_k; p.Hq = heads_q; p.Hkv = heads_kv;
+  p.g = heads_q / heads_kv;
+  p.hg_count = pack ? heads_kv : heads_q;
+  p.gp = pack ? p.g : 1;
+  const int64_t rows = (int64_t)seqlen_q * p.gp;
+  if (rows > (int64_t)1 << 30) return fail(FA_ERR_UNSUPPORTED, "too many rows per sequence");
+  p.m_blocks = (int)((rows + FA_BLOCK_M - 1) / FA_BLOCK_M);
+  p.total_tiles = (int64_t)p.m_blocks * batch * p.hg_count;
+  p.persistent = 0;
+  hipError_t e = fa_launch_prefill(p, head_dim, false, pack, softcap, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return FA_OK;
+}
+
+int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const void* v, void* out,
+                  float* lse, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                  int max_seqlen_q, int total_q, int total_k, int heads_q, int heads_kv, int head_dim,
+                  const int64_t q_strides[2], const int64_t k_strides[2], const int64_t v_strides[2],
+                  const int64_t o_strides[2], void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
+  if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "batch must be positive and sizes non-negative");
+  if ((rc = check_strides("q", q, q_strides, 2)) || (rc = check_strides("k", k, k_strides, 2)) ||
+      (rc = check_strides("v", v, v_strides, 2)) || (rc = check_strides("out", out, o_strides, 2)))
+    return rc;
+  FaParams p;
+  memset(&p, 0, sizeof p);
+  bool softcap = false;
+  if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
+  if (total_q == 0 || max_seqlen_q == 0) return FA_OK;  // nothing to compute
+  const bool pack = resolve_pack(opts, heads_q, heads_kv);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.q_bs = 0; p.q_ss = q_strides[0]; p.q_hs = q_strides[1];
+  p.k_bs = 0; p.k_ss = k_strides[0]; p.k_hs = k_strides[1];
+  p.v_bs = 0; p.v_ss = v_strides[0]; p.v_hs = v_strides[1];
+  p.o_bs = 0; p.o_ss = o_strides[0]; p.o_hs = o_strides[1];
+  p.lse_bs = 0;
+  p.lse_hs = total_q;
+  p.B = batch; p.Nq = max_seqlen_q; p.Nk = 0; p.Hq = heads_q; p.Hkv = heads_kv;
+  p.g = heads_q / heads_kv;
+  p.hg_count = pack ? heads_kv : heads_q;
+  p.gp = pack ? p.g : 1;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  const int64_t rows = (int64_t)max_seqlen_q * p.gp;
+  if (rows > (int64_t)1 << 30) return fail(FA_ERR_UNSUPPORTED, "too many rows per sequence");
+  p.m_blocks = (int)((rows + FA_BLOCK_M - 1) / FA_BLOCK_M);
+  // upper bound: every row block of every sequence, but no more than the rows exist
+  int64_t bound = (int64_t)p.m_blocks * batch;
+  int64_t bound2 = ((int64_t)total_q * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M + batch;
+  p.total_tiles = (bound < bound2 ? bound : bound2) * p.hg_count;
+  p.persistent = 1;
+  hipError_t e = fa_launch_prefill(p, head_dim, true, pack, softcap, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "varlen launch");
+  return FA_OK;
+}
+
+size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_dim, int num_splits) {
+  if (num_splits <= 1 || batch <= 0 || seqlen_q <= 0 || heads_q <= 0 || head_dim <= 0) return 0;
+  size_t rows = (size_t)batch * seqlen_q * heads_q;
+  size_t bytes = (size_t)num_splits * rows * ((size_t)head_dim + 1) * 4;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* cache_seqlens, void* out, float* lse,
+                         int batch, int seqlen_q, int heads_q, int heads_kv, int head_dim, int64_t num_pages,
+                         int page_size, int max_blocks_per_seq, int num_splits, void* workspace,
+                         size_t workspace_bytes, const int64_t q_strides[3], const int64_t k_strides[3],
+                         const int64_t v_strides[3], const int64_t o_strides[3], void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
+  if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || seqlen_q <= 0 || num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0)
+    return fail(FA_ERR_INVALID_ARG, "batch, seqlen_q, num_pages, page_size and max_blocks_per_seq must be positive");
+  if (num_splits < 1) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
+    return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
+  if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
+      (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)))
+    return rc;
+  const int g = heads_q / heads_kv;
+  if ((int64_t)seqlen_q * g > FA_PAGED_MAX_ROWS)
+    return fail(FA_ERR_UNSUPPORTED, "seqlen_q * heads_q / heads_kv = %lld exceeds %d packed rows",
+                (long long)seqlen_q * g, FA_PAGED_MAX_ROWS);
+  const size_t need = fa_kvcache_workspace_size(batch, seqlen_q, heads_q, head_dim, num_splits);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  FaParams p;
+  memset(&p, 0, sizeof p);
+  bool softcap = false;
+  if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.q_bs = q_strides[0]; p.q_ss = q_strides[1]; p.q_hs = q_strides[2];
+  p.k_bs = k_strides[0]; p.k_ss = k_strides[1]; p.k_hs = k_strides[2];
+  p.v_bs = v_strides[0]; p.v_ss = v_strides[1]; p.v_hs = v_strides[2];
+  p.o_bs = o_strides[0]; p.o_ss = o_strides[1]; p.o_hs = o_strides[2];
+  p.B = batch; p.Nq = seqlen_q; p.Hq = heads_q; p.Hkv = heads_kv; p.g = g;
+  p.block_table = block_table;
+  p.cache_seqlens = cache_seqlens;
+  p.page = page_size;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_splits = num_splits;
+  const int64_t rows = (int64_t)batch * heads_q * seqlen_q;
+  if (num_splits > 1) {
+    p.o_part = static_cast<float*>(workspace);
+    p.lse_part = p.o_part + (size_t)num_splits * rows * head_dim;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fa_launch_paged(p, head_dim, softcap, s);
+  if (e != hipSuccess) return hip_fail(e, "paged launch");
+  if (num_splits > 1) {
+    FaCombineParams c;
+    c.o_part = p.o_part;
+    c.lse_part = p.lse_part;
+    c.num_splits = num_splits;
+    c.rows = rows;
+    c.Hq = heads_q;
+    c.Nq = seqlen_q;
+    c.o = p.o;
+    c.o_bs = p.o_bs; c.o_ss = p.o_ss; c.o_hs = p.o_hs;
+    c.lse = lse;
+    e = fa_launch_combine(c, head_dim, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return FA_OK;
+}
+
+int fa_combine(const float* o_part, const float* lse_part, int num_splits, int64_t rows, int head_dim,
+               void* out, int64_t out_row_stride, float* lse_out, void* stream) {
+  g_err[0] = 0;
+  if (head_dim != 64 && head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!o_part || !lse_part || !out) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (num_splits < 1 || rows < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 1 and rows >= 0");
+  if (out_row_stride < head_dim || (out_row_stride * 2) % 4 != 0 || (reinterpret_cast<uintptr_t>(out) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "out rows must be 4-byte aligned and not overlap");
+  if (reinterpret_cast<uintptr_t>(o_part) & 15u) return fail(FA_ERR_INVALID_ARG, "o_part is not 16-byte aligned");
+  FaCombineParams c;
+  c.o_part = o_part;
+  c.lse_part = lse_part;
+  c.num_splits = num_splits;
+  c.rows = rows;
+  c.Hq = 1;
+  c.Nq = 1;
+  c.o = static_cast<uint16_t*>(out);
+  c.o_bs = out_row_stride;
+  c.o_ss = 0;
+  c.o_hs = 0;
+  c.lse = lse_out;
+  hipError_t e = fa_launch_combine(c, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return FA_OK;
+}
+
+}  // extern "C"

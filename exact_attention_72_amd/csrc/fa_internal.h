@@ -1,0 +1,66 @@
+// Internal launch parameters shared by the C-ABI host code and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+// Everything one launch needs, passed by value as the kernel argument.
+struct FaParams {
+  const uint16_t* q;  // bfloat16 bit patterns
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  // strides in elements: (batch or page, token, head); head_dim is contiguous
+  int64_t q_bs, q_ss, q_hs;
+  int64_t k_bs, k_ss, k_hs;
+  int64_t v_bs, v_ss, v_hs;
+  int64_t o_bs, o_ss, o_hs;
+  // LSE: element (b, h, token) at lse + b * lse_bs + h * lse_hs + token
+  int64_t lse_bs, lse_hs;
+  int B, Nq, Nk, Hq, Hkv, g;
+  int hg_count;  // tile head axis: heads_kv when GQA heads are packed into rows, else heads_q
+  int gp;        // rows per token in a tile: g when packed, else 1
+  int m_blocks;  // row blocks per (sequence, head group); for varlen an upper bound
+  int64_t total_tiles;  // dense: exact tile count; varlen: an upper bound
+  int persistent;       // 1: grid-stride loop over tiles; 0: one tile per workgroup
+  // varlen
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  // paged KV
+  const int32_t* block_table;
+  const int32_t* cache_seqlens;
+  int page, max_blocks, num_splits;
+  float* o_part;
+  float* lse_part;
+  // score transform
+  float scale_log2;  // softmax_scale * log2(e)
+  float cap_in;      // softmax_scale / softcap
+  float cap_out;     // softcap * log2(e)
+  int causal, wl, wr;
+};
+
+struct FaCombineParams {
+  const float* o_part;
+  const float* lse_part;
+  int num_splits;
+  int64_t rows;  // rows per split; row r = (b * Hq + h) * Nq + t
+  int Hq, Nq;
+  uint16_t* o;
+  int64_t o_bs, o_ss, o_hs;
+  float* lse;  // [rows] in row order, may be null
+};
+
+// Launchers (fa_kernels.hip).  They return hipSuccess or the launch error.
+hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool pack, bool softcap,
+                             hipStream_t stream);
+hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t stream);
+hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t stream);
+
+// Tile geometry of the prefill kernel.
+constexpr int FA_BLOCK_M = 128;     // query rows per workgroup tile (4 waves x 32)
+constexpr int FA_BLOCK_N = 64;      // keys per K/V stage
+constexpr int FA_PAGED_STAGE = 128; // keys per stage in the paged kernel (4 waves x 32)
+constexpr int FA_PAGED_MAX_ROWS = 32;

@@ -1,0 +1,169 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) fused exact-attention forward library.
+ *
+ * The library computes O = softmax(scale * Q K^T) V per (sequence, query head)
+ * without writing S or P to memory, and the natural-log log-sum-exp of every
+ * row ("Attention kernels: FlashAttention and PagedAttention", sections 2.1,
+ * 3.2 and 4.3).  Each entry point enqueues its kernels on the caller's HIP
+ * stream and returns; nothing is synchronised.
+ *
+ * Conventions shared by every entry point
+ *   - Element type: Q, K, V and O are bfloat16 (passed as untyped pointers),
+ *     LSE is float32.  Head dimension d is 64 or 128.
+ *   - Pointers are device pointers owned by the caller.  Inputs are only read.
+ *     The library keeps no pointer after the call returns and never frees
+ *     caller memory.  The first call on a device queries device attributes
+ *     and the kernels' occupancy; no call allocates device memory.
+ *   - Strides are in elements; the last (head_dim) dimension must be
+ *     contiguous (stride 1) and every row must start 16-byte aligned.
+ *   - stream is a hipStream_t (NULL = the null stream).
+ *   - Return value: FA_OK, or a negative code with nothing enqueued:
+ *       FA_ERR_INVALID_ARG  null pointer, negative or zero size, bad stride or
+ *                           alignment, heads_q not a multiple of heads_kv,
+ *                           workspace too small, num_splits < 1;
+ *       FA_ERR_UNSUPPORTED  a head_dim other than 64 or 128, or a shape the
+ *                           kernels do not cover (stated per entry point);
+ *       FA_ERR_HIP          a HIP runtime error while launching.
+ *     fa_last_error() returns a message for the calling thread's last failure.
+ *   - Rows that see no key at all get O = 0 and LSE = -inf (no NaN).
+ *   - Results are bitwise reproducible for fixed arguments.
+ *
+ * Masking options (fa_attn_opts), from the pages' statement of the problem
+ * ("FA4 (CuTeDSL) and engineering interfaces", sections 3, 6.2 and 7):
+ *   softmax_scale  > 0: used as is; <= 0 or NaN: d^-0.5.
+ *   causal         non-zero: query t of a sequence with Lq queries and Lk keys
+ *                  sits at key position p = t + Lk - Lq (bottom-right) and sees
+ *                  keys j <= p.  Equal to top-left alignment when Lq == Lk.
+ *   window_left,   sliding window: row at position p sees keys in
+ *   window_right   [p - window_left, p + window_right] (inclusive); a negative
+ *                  bound is unbounded on that side.
+ *   softcap        > 0: logits become softcap * tanh(scale * q.k / softcap)
+ *                  before the softmax; 0 = off.
+ *   pack_gqa       > 0: fold the heads_q / heads_kv query heads that share a
+ *                  KV head into the rows of one tile so each K/V tile is read
+ *                  once for all of them ("FA4 ...", section 5; "Attention
+ *                  kernels ...", section 5.3); 0: one tile per query head;
+ *                  < 0: pick automatically (on when heads_q > heads_kv).
+ */
+#ifndef EXACT_ATTENTION_72_FA_H
+#define EXACT_ATTENTION_72_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_OK 0
+#define FA_ERR_INVALID_ARG (-1)
+#define FA_ERR_UNSUPPORTED (-2)
+#define FA_ERR_HIP (-3)
+
+typedef struct fa_attn_opts {
+  float softmax_scale;
+  int causal;
+  int window_left;
+  int window_right;
+  float softcap;
+  int pack_gqa;
+} fa_attn_opts;
+
+/* Dense (padded) attention forward ("FA4 ...", section 3 flash_attn_func).
+ *   q   [batch, seqlen_q, heads_q,  head_dim]  strides q_strides  = {batch, seq, head}
+ *   k   [batch, seqlen_k, heads_kv, head_dim]  strides k_strides
+ *   v   [batch, seqlen_k, heads_kv, head_dim]  strides v_strides
+ *   out [batch, seqlen_q, heads_q,  head_dim]  strides o_strides   (written)
+ *   lse [batch, heads_q, seqlen_q] float32, dense                  (written; may be NULL)
+ * Query head h uses KV head h / (heads_q / heads_kv). */
+int fa_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v, void* out,
+           float* lse, int batch, int seqlen_q, int seqlen_k, int heads_q, int heads_kv,
+           int head_dim, const int64_t q_strides[3], const int64_t k_strides[3],
+           const int64_t v_strides[3], const int64_t o_strides[3], void* stream);
+
+/* Variable-length attention forward over packed sequences ("FA4 ...", section 4;
+ * "Attention kernels ...", section 7.1).  Sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b], cu_seqlens_k[b+1]);
+ * attention never crosses sequences.
+ *   q   [total_q, heads_q,  head_dim]  strides q_strides = {token, head}
+ *   k,v [total_k, heads_kv, head_dim]  strides k_strides, v_strides
+ *   out [total_q, heads_q,  head_dim]  strides o_strides (written)
+ *   lse [heads_q, total_q] float32 (written; may be NULL)
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [batch + 1], non-decreasing, starting at 0.
+ *   max_seqlen_q: an upper bound of the query lengths (sizes the launch).
+ * Caller contract, not checked on the device: cu_seqlens_q[batch] == total_q,
+ * cu_seqlens_k[batch] <= total_k, every query length <= max_seqlen_q. */
+int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const void* v,
+                  void* out, float* lse, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int total_q,
+                  int total_k, int heads_q, int heads_kv, int head_dim,
+                  const int64_t q_strides[2], const int64_t k_strides[2],
+                  const int64_t v_strides[2], const int64_t o_strides[2], void* stream);
+
+/* Attention of new queries against a paged KV cache, with split-KV
+ * ("FA4 ...", sections 6.1 and 6.2; "Attention kernels ...", sections 6.1 and 6.3).
+ * Logical key t of sequence b lives in page block_table[b][t / page_size] at slot
+ * t % page_size.  The keys are cut into num_splits contiguous page ranges; each
+ * range produces a normalised partial O and its LSE, which a combine kernel merges
+ * on the same stream.  With num_splits == 1 the result is written directly.
+ *   q        [batch, seqlen_q, heads_q, head_dim]  strides q_strides = {batch, seq, head}
+ *   k_cache  [num_pages, page_size, heads_kv, head_dim]  strides k_strides = {page, slot, head}
+ *   v_cache  same shape, strides v_strides
+ *   block_table  device int32 [batch, max_blocks_per_seq] (row stride max_blocks_per_seq)
+ *   cache_seqlens device int32 [batch]: keys per sequence (Lk)
+ *   out      [batch, seqlen_q, heads_q, head_dim]  strides o_strides (written)
+ *   lse      [batch, heads_q, seqlen_q] float32 (written; may be NULL)
+ *   workspace: device memory of at least fa_kvcache_workspace_size(...) bytes
+ *              (may be NULL when that size is 0); holds the fp32 partials.
+ * Unsupported: seqlen_q * (heads_q / heads_kv) > 32.
+ * Caller contract, not checked on the device: block_table entries of live pages
+ * lie in [0, num_pages) and cache_seqlens[b] <= max_blocks_per_seq * page_size. */
+int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table,
+                         const int32_t* cache_seqlens, void* out, float* lse, int batch,
+                         int seqlen_q, int heads_q, int heads_kv, int head_dim,
+                         int64_t num_pages, int page_size, int max_blocks_per_seq,
+                         int num_splits, void* workspace, size_t workspace_bytes,
+                         const int64_t q_strides[3], const int64_t k_strides[3],
+                         const int64_t v_strides[3], const int64_t o_strides[3],
+                         void* stream);
+
+/* Bytes of workspace fa_fwd_kvcache_paged needs: 0 for num_splits == 1, else
+ * num_splits * batch * seqlen_q * heads_q * (head_dim + 1) * 4 rounded up to 256. */
+size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_dim,
+                                 int num_splits);
+
+/* Merge of partial attention states ("Attention kernels ...", section 6.3: the
+ * partial (O_s, LSE_s) of disjoint key ranges combine with the same rescale as
+ * the tiles of one pass):
+ *   M = max_s LSE_s,  w_s = exp(LSE_s - M),  LSE = M + ln(sum_s w_s),
+ *   O = sum_s (w_s / sum_s w_s) * O_s.
+ * A row whose every LSE_s is -inf gets O = 0 and LSE = -inf.
+ *   o_part   float32 [num_splits, rows, head_dim], split stride rows*head_dim, row stride head_dim
+ *   lse_part float32 [num_splits, rows]
+ *   out      bfloat16, row r at out + r * out_row_stride (written)
+ *   lse_out  float32 [rows] (written; may be NULL)
+ * With num_splits == 2 this is the two-state merge used for prefix/suffix attention. */
+int fa_combine(const float* o_part, const float* lse_part, int num_splits, int64_t rows,
+               int head_dim, void* out, int64_t out_row_stride, float* lse_out, void* stream);
+
+/* Host-only helper, no device work: the class of key tile n (keys
+ * [n*block_n, n*block_n + block_n)) for query rows at token indices
+ * [tok_lo, tok_hi] of a sequence with seqlen_q queries and seqlen_k keys, as the
+ * kernels decide it: 0 = skipped; otherwise bit 0 set and bit 1 when the causal
+ * diagonal, the right window edge or seqlen_k cuts the tile, bit 2 when the left
+ * window edge cuts it ("Attention kernels ...", section 7.2 figure). */
+int fa_tile_class(int tok_lo, int tok_hi, int seqlen_q, int seqlen_k, int causal,
+                  int window_left, int window_right, int block_n, int n);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+const char* fa_last_error(void);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_72_FA_H */

@@ -1,0 +1,169 @@
+"""Host-side checks that need no GPU: the C ABI loads and exports every symbol
+the header declares, the tile classifier the kernels use reproduces the pages'
+causal / sliding-window block picture, and invalid arguments are rejected with
+error codes before anything touches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_72_amd import api
+from exact_attention_72_amd.api import FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, fa_attn_opts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "fa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for n in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_combine"):
+        assert n in names
+    assert set(names) == set(api.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = api.lib()
+    for n in header_functions():
+        assert hasattr(L, n), n
+    assert api.fa_version() >= 100
+    assert api.fa_last_error() == "" or isinstance(api.fa_last_error(), str)
+
+
+def _grid(golden_rows, block, cls_of):
+    return ["".join(cls_of(I, J) for J in range(len(golden_rows))) for I in range(len(golden_rows))]
+
+
+def _symbol(c):
+    if c == 0:
+        return "."
+    if c == 1:
+        return "F"
+    if c & 4:
+        return "E"
+    return "D"
+
+
+def test_tile_classes_match_the_causal_figure(golden):
+    g = golden("causal_window_block_classes.json")
+    b = 4
+    N = b * g["blocks"]
+    got = _grid(g["causal"], b, lambda I, J: _symbol(
+        api.fa_tile_class(I * b, I * b + b - 1, N, N, True, -1, -1, b, J)))
+    assert got == g["causal"]
+
+
+def test_tile_classes_match_the_window_figure(golden):
+    g = golden("causal_window_block_classes.json")
+    b = 4
+    N = b * g["blocks"]
+    got = _grid(g["causal_window"], b, lambda I, J: _symbol(
+        api.fa_tile_class(I * b, I * b + b - 1, N, N, True, 2 * b, 0, b, J)))
+    assert got == g["causal_window"]
+
+
+def test_tile_class_bottom_right_and_tail():
+    # 2 queries over 5 keys, bottom-right: rows at positions 3 and 4
+    assert api.fa_tile_class(0, 1, 2, 5, True, -1, -1, 8, 0) == 1 | 2   # cut by diagonal and Lk
+    # non-causal, keys beyond seqlen_k cut the last tile
+    assert api.fa_tile_class(0, 7, 8, 10, False, -1, -1, 8, 1) == 1 | 2
+    assert api.fa_tile_class(0, 7, 8, 16, False, -1, -1, 8, 1) == 1
+    # a query block entirely before the keys it could see under a window: skipped
+    assert api.fa_tile_class(0, 3, 64, 64, True, 3, 0, 4, 5) == 0
+
+
+# ---------------------------------------------------------------- argument validation
+FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails before any device call
+S3 = (ctypes.c_int64 * 3)(2048, 128 * 16, 128)
+S2 = (ctypes.c_int64 * 2)(2048, 128)
+
+
+def _opts(**kw):
+    o = fa_attn_opts(0.0, 0, -1, -1, 0.0, -1)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def call_fwd(opts=None, q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, Nq=16, Nk=16, Hq=16, Hkv=16, d=128,
+             qs=S3, ks=S3, vs=S3, os_=S3):
+    o = opts or _opts()
+    return api.lib().fa_fwd(ctypes.byref(o), q, k, v, out, None, B, Nq, Nk, Hq, Hkv, d, qs, ks, vs,
+                            os_, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), FA_ERR_UNSUPPORTED),
+    (dict(d=256), FA_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), FA_ERR_INVALID_ARG),
+    (dict(q=None), FA_ERR_INVALID_ARG),
+    (dict(out=None), FA_ERR_INVALID_ARG),
+    (dict(B=0), FA_ERR_INVALID_ARG),
+    (dict(Nq=0), FA_ERR_INVALID_ARG),
+    (dict(Nk=-1), FA_ERR_INVALID_ARG),
+    (dict(q=ctypes.c_void_p((1 << 20) + 2)), FA_ERR_INVALID_ARG),      # misaligned base
+    (dict(ks=(ctypes.c_int64 * 3)(2048, 2050, 128)), FA_ERR_INVALID_ARG),  # misaligned row stride
+    (dict(vs=None), FA_ERR_INVALID_ARG),
+])
+def test_fwd_rejects_invalid_arguments(kw, code):
+    assert call_fwd(**kw) == code
+    assert api.fa_last_error() != ""
+
+
+def test_fwd_rejects_null_opts_and_bad_softcap():
+    L = api.lib()
+    assert L.fa_fwd(None, FAKE, FAKE, FAKE, FAKE, None, 1, 16, 16, 16, 16, 128, S3, S3, S3, S3,
+                    None) == FA_ERR_INVALID_ARG
+    assert call_fwd(opts=_opts(softcap=-1.0)) == FA_ERR_INVALID_ARG
+    assert call_fwd(opts=_opts(softcap=float("nan"))) == FA_ERR_INVALID_ARG
+
+
+def test_varlen_rejects_invalid_arguments():
+    L = api.lib()
+    o = _opts()
+    def call(cu=FAKE, d=128, B=2, Hq=32, Hkv=4):
+        return L.fa_fwd_varlen(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None, cu, cu, B, 64, 100,
+                               100, Hq, Hkv, d, S2, S2, S2, S2, None)
+    assert call(cu=None) == FA_ERR_INVALID_ARG
+    assert call(d=80) == FA_ERR_UNSUPPORTED
+    assert call(B=0) == FA_ERR_INVALID_ARG
+    assert call(Hq=30) == FA_ERR_INVALID_ARG
+
+
+def call_paged(num_splits=1, ws=None, ws_bytes=0, Nq=1, Hq=32, Hkv=8, page=256, d=128, bt=FAKE):
+    o = _opts(causal=1)
+    return api.lib().fa_fwd_kvcache_paged(ctypes.byref(o), FAKE, FAKE, FAKE, bt, FAKE, FAKE, None,
+                                          64, Nq, Hq, Hkv, d, 8192, page, 128, num_splits, ws,
+                                          ws_bytes, S3, S3, S3, S3, None)
+
+
+def test_paged_rejects_invalid_arguments():
+    assert call_paged(num_splits=0) == FA_ERR_INVALID_ARG
+    assert call_paged(num_splits=4) == FA_ERR_INVALID_ARG                  # no workspace
+    need = api.fa_kvcache_workspace_size(64, 1, 32, 128, 4)
+    assert call_paged(num_splits=4, ws=FAKE, ws_bytes=need - 256) == FA_ERR_INVALID_ARG
+    assert call_paged(Nq=9) == FA_ERR_UNSUPPORTED                           # 9 * 4 rows > 32
+    assert call_paged(page=0) == FA_ERR_INVALID_ARG
+    assert call_paged(bt=None) == FA_ERR_INVALID_ARG
+    assert call_paged(d=32) == FA_ERR_UNSUPPORTED
+
+
+def test_workspace_size_formula():
+    assert api.fa_kvcache_workspace_size(64, 1, 32, 128, 1) == 0
+    n = 16 * 64 * 32 * (128 + 1) * 4
+    assert api.fa_kvcache_workspace_size(64, 1, 32, 128, 16) == (n + 255) // 256 * 256
+
+
+def test_combine_rejects_invalid_arguments():
+    L = api.lib()
+    assert L.fa_combine(None, FAKE, 2, 10, 128, FAKE, 128, None, None) == FA_ERR_INVALID_ARG
+    assert L.fa_combine(FAKE, FAKE, 0, 10, 128, FAKE, 128, None, None) == FA_ERR_INVALID_ARG
+    assert L.fa_combine(FAKE, FAKE, 2, 10, 96, FAKE, 128, None, None) == FA_ERR_UNSUPPORTED
+    assert L.fa_combine(FAKE, FAKE, 2, 10, 128, FAKE, 64, None, None) == FA_ERR_INVALID_ARG
