@@ -1,0 +1,207 @@
+"""Benchmark of the attention forward on one MI355X.
+
+A step is one forward pass of the dense causal prefill workload
+(batch 4, 16 heads, N = 4096, d = 128, bf16) through the C ABI.  The line also
+carries the paged split-KV decode measurement (64 sequences, 32/8 heads,
+d = 128, 256-token pages, num_splits in {1, 4, 16}) as a secondary figure.
+
+Prints one JSON line:
+  value        prefill TFLOP/s, FLOPs counted as 4 * B * H * N^2 * d * 1/2 (the
+               pages' causal convention, "Attention kernels: FlashAttention and
+               PagedAttention", section 8.3)
+  roofline     achieved bf16 MFMA rate of the prefill kernel (FLOPs per launch /
+               average launch time from HIP events on the launch stream) against
+               the 2.5 PFLOP/s dense bf16 peak; traffic from the committed
+               rocprofv3 counter summary when it matches the current kernel source
+  cpu_baseline the fp64 oracle timed on host threads on a bounded row sample of
+               the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_72_amd", "csrc", "fa_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("fa_kernels.hip", "fa_blockinfo.h", "fa_internal.h"):
+        with open(os.path.join(ROOT, "exact_attention_72_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel)
+    if not e or e.get("source_sha") != kernel_source_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup):
+    """Warm up, then time `steps` calls; per-call HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]   # ms
+    return wall, per
+
+
+def prefill_flops(B, H, N, d, causal):
+    return 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+
+
+def cpu_baseline(W, t, c, target_s=15.0):
+    """The fp64 oracle on a row sample of the same workload; TFLOP/s on the same
+    FLOP convention (each sampled row counted with its visible keys)."""
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    threads = max(1, min(threads, os.cpu_count() or 1, 16))
+    B, N, H, d = c["B"], c["N"], c["Hq"], c["d"]
+    qb, kb, vb = (W.to_bits(t[n]) for n in "qkv")
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        rows = np.sort(rng.integers(0, B * H * N, n))
+        i = rows % N
+        keys = float(np.sum(i + 1)) if c["causal"] else float(n) * N
+        t0 = time.perf_counter()
+        used = oracle.fwd_dense(qb, kb, vb, causal=c["causal"], window=c["window"],
+                                softcap=c["softcap"], rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        return dt, keys * 4 * d, n
+    dt, fl, n = run(threads * 8)
+    n2 = int(max(threads * 8, min(200000, n * target_s / max(dt, 1e-3))))
+    dt, fl, n = run(n2)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} random query rows of the batch-4 x 16-head N=4096 d=128 causal "
+                      f"workload, fp64, {dt:.1f} s"}
+
+
+def bench_decode(api, W, steps, warmup):
+    import torch
+    c = W.WORKLOADS["paged_decode_b64_h32kv8_d128_page256"]
+    t = W.paged(c["seed"], c["B"], c["Hq"], c["Hkv"], c["d"], c["page"], c["lo"], c["hi"],
+                max_blocks=c["max_blocks"], device="cuda")
+    bt, sl = t["block_table"].cuda(), t["cache_seqlens"].cuda()
+    kv_bytes = 4096.0 * float(t["cache_seqlens"].sum())   # K and V of live tokens, bf16
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((c["B"], c["Hq"], 1), dtype=torch.float32, device="cuda")
+    res = {}
+    for S in (1, 4, 16):
+        need = api.fa_kvcache_workspace_size(c["B"], 1, c["Hq"], c["d"], S)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        fn = lambda: api.fa_fwd_kvcache_paged(t["q"], t["k_cache"], t["v_cache"], bt, sl,  # noqa
+                                              num_splits=S, causal=True, out=out, lse=lse,
+                                              workspace=ws)
+        wall, per = time_launches(fn, steps, warmup)
+        ms = sum(per) / len(per)
+        res[S] = {"ms": ms, "kv_GBps": kv_bytes / (ms * 1e-3) / 1e9}
+    best = max(res, key=lambda s: res[s]["kv_GBps"])
+    return {"metric": "paged decode KV GB/s", "unit": "GB/s",
+            "value": res[best]["kv_GBps"], "num_splits": best,
+            "kv_bytes": kv_bytes,
+            "per_split": {str(s): {"ms": round(r["ms"], 4), "kv_GBps": round(r["kv_GBps"], 1)}
+                          for s, r in res.items()},
+            "roofline": {"bound": "hbm", "achieved": res[best]["kv_GBps"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": res[best]["kv_GBps"] / PEAK_HBM_GBS,
+                         "traffic": stored_traffic("fa_paged_kernel")},
+            "config": {"workload": "paged_decode_b64_h32kv8_d128_page256", "batch": c["B"],
+                       "heads_q": c["Hq"], "heads_kv": c["Hkv"], "head_dim": c["d"],
+                       "page_size": c["page"], "cache_seqlens": "uniform [1024, 32768]"}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the attention forward here has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_attention_72_amd import api, workloads as W
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+
+    name = "prefill_b4_h16_n4096_d128_causal"
+    c = W.WORKLOADS[name]
+    B, N, H, d = c["B"], c["N"], c["Hq"], c["d"]
+    t = W.dense(c["seed"], B, N, H, c["Hkv"], d, device="cuda")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fn = lambda: api.fa_fwd(t["q"], t["k"], t["v"], causal=True, out=out, lse=lse)  # noqa
+    torch.cuda.synchronize()
+    wall, per = time_launches(fn, args.steps, args.warmup)
+    flops = prefill_flops(B, H, N, d, True)
+    ms_step = wall / args.steps * 1e3
+    kern_ms = sum(per) / len(per)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    line = {
+        "metric": "attn fwd TFLOPS (bf16 N=4k d=128 causal) + paged decode KV GB/s, 1 GPU",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "batch": B, "heads": H, "seq_len": N, "head_dim": d,
+                   "causal": True, "flop_convention": "4*B*H*N^2*d/2"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic("fa_prefill_kernel"),
+                     "kernel_ms": round(kern_ms, 4)},
+    }
+    if not args.no_decode:
+        del t, out, lse
+        torch.cuda.empty_cache()
+        line["decode"] = bench_decode(api, W, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        tc = W.dense(c["seed"], B, N, H, c["Hkv"], d)
+        line["cpu_baseline"] = cpu_baseline(W, tc, c)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -66,6 +66,19 @@ def _load():
     return lib
 
 
+def default_threads() -> int:
+    """Host threads for the oracle: OMP_NUM_THREADS if set, at most 16 and the CPU count."""
+    try:
+        n = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    except ValueError:
+        n = 16
+    return max(1, min(n, 16, os.cpu_count() or 1))
+
+
+def _threads(n):
+    return default_threads() if not n or n <= 0 else int(n)
+
+
 def _u16(a) -> np.ndarray:
     a = np.ascontiguousarray(a)
     if a.dtype != np.uint16:
@@ -116,7 +129,7 @@ def fwd_dense(q, k, v, *, scale=None, causal=False, window=None, softcap=0.0,
     wl, wr = _window(window)
     rc = lib.oracle_fwd_dense(_ptr(q), _ptr(k), _ptr(v), B, Nq, Nk, Hq, Hkv, d,
                               _scale(scale, d), int(bool(causal)), wl, wr, float(softcap),
-                              _ptr(rr), n, _ptr(o), _ptr(lse), int(nthreads))
+                              _ptr(rr), n, _ptr(o), _ptr(lse), _threads(nthreads))
     if rc < 0:
         raise ValueError("oracle_fwd_dense rejected its arguments")
     if rr is None:
@@ -145,7 +158,7 @@ def fwd_varlen(q, k, v, cu_q, cu_k, *, scale=None, causal=False, window=None,
     wl, wr = _window(window)
     rc = lib.oracle_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_q), _ptr(cu_k), B, Hq, Hkv, d,
                                _scale(scale, d), int(bool(causal)), wl, wr, float(softcap),
-                               _ptr(rr), n, _ptr(o), _ptr(lse), int(nthreads))
+                               _ptr(rr), n, _ptr(o), _ptr(lse), _threads(nthreads))
     if rc < 0:
         raise ValueError("oracle_fwd_varlen rejected its arguments")
     if rr is None:
@@ -178,7 +191,7 @@ def fwd_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, scale=None,
     rc = lib.oracle_fwd_paged(_ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(sl), B, Nq, Hq, Hkv, d,
                               page, max_blocks, _scale(scale, d), int(bool(causal)), wl, wr,
                               float(softcap), int(num_splits), int(split), _ptr(rr), n,
-                              _ptr(o), _ptr(lse), int(nthreads))
+                              _ptr(o), _ptr(lse), _threads(nthreads))
     if rc < 0:
         raise ValueError("oracle_fwd_paged rejected its arguments")
     if rr is None:
