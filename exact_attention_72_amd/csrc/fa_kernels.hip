@@ -20,10 +20,17 @@
 //    second product (the C-to-A fragment reuse of section 8.5, here C-to-B).
 //    Each 16-key chunk of P^T takes accumulator slots {8h..8h+7}; the V^T
 //    operand is then read with the same key order.
-//  * K is stored row-major in LDS with a 16-byte-chunk XOR swizzle so the 32
-//    rows a wave reads per MFMA hit distinct banks.  V is stored transposed in
-//    4-key groups, [key/4][d][key%4], written from registers after a 4x4 bf16
-//    transpose, so the V^T operand is two 8-byte LDS reads per lane.
+//  * K and V stages go from global memory straight into LDS with the gfx950
+//    LDS-DMA load (global_load_lds_dwordx4: lane l of a wave writes the 16
+//    bytes it fetched to LDS at base + 16 l), so no registers stage them.  Both
+//    are stored row-major; the source chunk each lane fetches is permuted so
+//    that the stored rows carry an XOR swizzle: K by 16-byte chunk (the 32 rows
+//    a wave reads with ds_read_b128 per MFMA hit distinct banks), V by 64-byte
+//    segment (the rows a transposed read touches hit distinct banks).
+//  * The V^T operand comes from ds_read_b64_tr_b16: within each 16-lane group,
+//    lane i receives element i % 4 of the 8-byte chunks addressed by lanes
+//    i / 4 + 4 k (k = 0..3), so four lanes addressing four consecutive keys of
+//    one 4-column span give every lane one column over those four keys.
 //  * Workgroup = 4 waves.  Prefill: the waves split the 128 query rows (32
 //    each) and share every 64-key stage.  Paged decode: the waves share the
 //    (at most 32) packed query rows and split each 128-key stage (32 keys
@@ -41,6 +48,9 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -51,7 +61,16 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// Value of lanes l and l ^ 32 combined: v_permlane32_swap returns the lower half's
+// values in one register and the upper half's in the other, for every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -63,153 +82,99 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
-// ------------------------------------------------------------------ LDS tiles
-// K: [key][d] bf16, 16-byte chunk c of row r stored at chunk c ^ swz(r).
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ------------------------------------------------------------------ LDS layout
+// A stage holds NK rows of K and NK rows of V, each row D bf16 (2D bytes),
+// row-major.  Stored 16-byte chunk = logical chunk ^ swizzle(row).
 template <int D>
-__device__ __forceinline__ int k_swz(int r) {
+__device__ __forceinline__ int k_swz(int r) {  // distinct chunk per row over 16 rows
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
-
 template <int D>
-__device__ __forceinline__ int k_lds_offset(int r, int chunk) {
-  return r * (D * 2) + ((chunk ^ k_swz<D>(r)) << 4);
+__device__ __forceinline__ int v_swz(int r) {  // rotates 64-byte segments over 4 rows
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-// V^T: element (key, d) at byte ((key / 4) * D + d) * 8 + (key % 4) * 2.
-template <int D>
-__device__ __forceinline__ int v_lds_offset(int quad, int d) {
-  return (quad * D + d) * 8;
-}
-
-// Source rows of one K/V stream: dense / varlen (contiguous keys) or paged.
-struct KvSource {
-  const uint16_t* kb;  // K base: sequence start (dense / varlen) or pool, plus head offset
-  const uint16_t* vb;
-  int64_t k_ss, v_ss;  // token strides
-  int64_t k_ps, v_ps;  // page strides (paged)
-  const int32_t* bt;   // block table row (paged), else null
-  int page;
-  int kend;            // keys >= kend are not loaded (zero-filled)
-};
-
-template <bool PAGED>
-__device__ __forceinline__ void kv_row_ptrs(const KvSource& s, int key, const uint16_t** kp,
-                                            const uint16_t** vp) {
-  if (PAGED) {
-    int64_t phys = s.bt[key / s.page];
-    int64_t slot = key % s.page;
-    *kp = s.kb + phys * s.k_ps + slot * s.k_ss;
-    *vp = s.vb + phys * s.v_ps + slot * s.v_ss;
-  } else {
-    *kp = s.kb + (int64_t)key * s.k_ss;
-    *vp = s.vb + (int64_t)key * s.v_ss;
-  }
-}
-
-// Registers staging one stage of NK keys between the global loads and the LDS
-// stores (register double buffering: loads for stage n+1 fly while stage n is
-// being computed).
+// One wave's share of an LDS-DMA stage load: IPW instructions per tensor, each
+// moving 1 KiB (RPK rows).  Instruction p of wave w fills rows
+// (4 p + w) * RPK .. + RPK - 1 of the stage.
 template <int D, int NK>
-struct Stage {
+struct DmaGeom {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kTensorBytes = NK * kRowBytes;
   static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kKChunks = NK * kChunksPerRow;
-  static constexpr int kKPer = (kKChunks + kThreads - 1) / kThreads;
-  static constexpr int kVBlocks = (NK / 4) * kChunksPerRow;  // 4 keys x 8 d each
-  static constexpr int kVPer = (kVBlocks + kThreads - 1) / kThreads;
-  u32x4 k[kKPer];
-  u32x4 v[kVPer][4];
-
-  template <bool PAGED>
-  __device__ __forceinline__ void load(const KvSource& s, int n0, int tid) {
-#pragma unroll
-    for (int i = 0; i < kKPer; ++i) {
-      int id = tid + i * kThreads;
-      int r = id / kChunksPerRow, c = id % kChunksPerRow;
-      int key = n0 + r;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if ((kKChunks % kThreads == 0 || id < kKChunks) && key < s.kend) {
-        const uint16_t *kp, *vp;
-        kv_row_ptrs<PAGED>(s, key, &kp, &vp);
-        x = *reinterpret_cast<const u32x4*>(kp + c * 8);
-      }
-      k[i] = x;
-    }
-#pragma unroll
-    for (int i = 0; i < kVPer; ++i) {
-      int id = tid + i * kThreads;
-      int quad = id / kChunksPerRow, dg = id % kChunksPerRow;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int key = n0 + quad * 4 + r;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if ((kVBlocks % kThreads == 0 || id < kVBlocks) && key < s.kend) {
-          const uint16_t *kp, *vp;
-          kv_row_ptrs<PAGED>(s, key, &kp, &vp);
-          x = *reinterpret_cast<const u32x4*>(vp + dg * 8);
-        }
-        v[i][r] = x;
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(char* lk, char* lv, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kKPer; ++i) {
-      int id = tid + i * kThreads;
-      if (kKChunks % kThreads != 0 && id >= kKChunks) continue;
-      int r = id / kChunksPerRow, c = id % kChunksPerRow;
-      *reinterpret_cast<u32x4*>(lk + k_lds_offset<D>(r, c)) = k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kVPer; ++i) {
-      int id = tid + i * kThreads;
-      if (kVBlocks % kThreads != 0 && id >= kVBlocks) continue;
-      int quad = id / kChunksPerRow, dg = id % kChunksPerRow;
-      // 4 keys x 8 d -> 8 d-rows of 4 keys: dword w of a key row holds d = 8dg+2w (low
-      // half) and 8dg+2w+1 (high half).
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t x0 = v[i][0][w], x1 = v[i][1][w], x2 = v[i][2][w], x3 = v[i][3][w];
-        u32x4 out;
-        out.x = (x0 & 0xffffu) | (x1 << 16);          // d even: keys 0, 1
-        out.y = (x2 & 0xffffu) | (x3 << 16);          // d even: keys 2, 3
-        out.z = (x0 >> 16) | (x1 & 0xffff0000u);      // d odd:  keys 0, 1
-        out.w = (x2 >> 16) | (x3 & 0xffff0000u);      // d odd:  keys 2, 3
-        *reinterpret_cast<u32x4*>(lv + v_lds_offset<D>(quad, dg * 8 + 2 * w)) = out;
-      }
-    }
-  }
+  static constexpr int kRowsPerKiB = 1024 / kRowBytes;
+  static constexpr int kInstPerWave = kTensorBytes / 1024 / 4;
+  static constexpr int kRowStep = 4 * kRowsPerKiB;  // rows between instructions of a wave
+  static_assert(kInstPerWave >= 1, "stage too small for four waves");
 };
+
+__device__ __forceinline__ void dma16(const uint16_t* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (FA_LDS void*)lds_dst, 16, 0, 0);
+}
 
 // ------------------------------------------------------------------ per-wave math
+// Per-lane LDS byte offsets of the MFMA operands, fixed for the whole kernel.
+template <int D>
+struct LaneOffsets {
+  int k[D / 16];  // K row (lane % 32), chunk (2 kk + kg) of the first 32-key block
+  int v[D / 32];  // V transposed-read address of d-block db for keys 4 kg + (j >> 2)
+  __device__ __forceinline__ void init(int lane) {
+    const int col = lane & 31, kg = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) k[kk] = col * (2 * D) + (((2 * kk + kg) ^ k_swz<D>(col)) << 4);
+    const int j = lane & 15, half = (lane >> 4) & 1;
+    const int row = 4 * kg + (j >> 2);
+    const int sw = v_swz<D>(row);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c16 = 4 * db + 2 * half + ((j & 3) >> 1);
+      v[db] = row * (2 * D) + ((c16 ^ sw) << 4) + (j & 1) * 8;
+    }
+  }
+};
+
 // S^T for the 32 keys [32 kb, 32 kb + 32) of the stage against the wave's 32
 // query columns.  Lane (j, kg) gets keys 32 kb + 8 (a / 4) + 4 kg + (a % 4).
 template <int D>
-__device__ __forceinline__ f32x16 qk_block(const char* lk, int kb, const bf16x8* qreg, int lane) {
-  f32x16 s = {};
-  const int row = kb * 32 + (lane & 31);
-  const int kg = lane >> 5;
+__device__ __forceinline__ f32x16 qk_block(const char* lk, int kb, const bf16x8* qreg,
+                                           const LaneOffsets<D>& off) {
+  bf16x8 a[D / 16];  // all operand reads in flight before the first product
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    bf16x8 a = *reinterpret_cast<const bf16x8*>(lk + k_lds_offset<D>(row, 2 * kk + kg));
-    s = mfma32(a, qreg[kk], s);
-  }
+  for (int kk = 0; kk < D / 16; ++kk)
+    a[kk] = *reinterpret_cast<const bf16x8*>(lk + kb * 32 * (2 * D) + off.k[kk]);
+  __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+  f32x16 s = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) s = mfma32(a[kk], qreg[kk], s);
   return s;
 }
 
 // O^T += V^T P^T for the 16 keys [16 c, 16 c + 16) of the stage.  pb holds P^T
-// for keys 16 c + 8 (slot / 4) + 4 kg + (slot % 4) of this lane's column.
+// for keys 16 c + 8 (slot / 4) + 4 kg + (slot % 4) of this lane's column; two
+// transposed reads give the V^T operand in the same key order.
 template <int D>
-__device__ __forceinline__ void pv_chunk(const char* lv, int c, bf16x8 pb, f32x16* o, int lane) {
-  const int kg = lane >> 5, i = lane & 31;
+__device__ __forceinline__ void pv_chunk(const char* lv, int c, bf16x8 pb, f32x16* o,
+                                         const LaneOffsets<D>& off) {
+  u32x4 w[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    const int d = 32 * db + i;
-    u32x2 lo = *reinterpret_cast<const u32x2*>(lv + v_lds_offset<D>(4 * c + kg, d));
-    u32x2 hi = *reinterpret_cast<const u32x2*>(lv + v_lds_offset<D>(4 * c + 2 + kg, d));
-    u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-    o[db] = mfma32(__builtin_bit_cast(bf16x8, w), pb, o[db]);
+    const char* base = lv + c * 16 * (2 * D) + off.v[db];
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + 8 * (2 * D)));
+    u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    w[db] = u32x4{l2.x, l2.y, h2.x, h2.y};
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = mfma32(__builtin_bit_cast(bf16x8, w[db]), pb, o[db]);
 }
 
 __device__ __forceinline__ bf16x8 pack_p(const f32x16& s, int half) {
@@ -219,64 +184,54 @@ __device__ __forceinline__ bf16x8 pack_p(const f32x16& s, int half) {
   return __builtin_convertvector(x, bf16x8);
 }
 
-// Score transform into the log2 domain: scale (and softcap), then mask.
-struct ScoreXf {
-  float scale_log2, cap_in, cap_out;
-};
-
-template <bool SOFTCAP>
-__device__ __forceinline__ float score(float s, const ScoreXf& x) {
-  if (SOFTCAP) {
-    // c * tanh(scale * s / c) * log2(e), tanh(y) = 1 - 2 / (exp(2y) + 1)
-    float y = s * x.cap_in;
-    float t = exp2_fast(y * (2.0f * kLog2e));
-    float th = 1.0f - 2.0f * rcp_fast(t + 1.0f);
-    return th * x.cap_out;
-  }
-  return s * x.scale_log2;
+// Softcap transform into the log2 domain: c * tanh(scale * s / c) * log2(e),
+// tanh(y) = 1 - 2 / (exp(2y) + 1).
+__device__ __forceinline__ float softcap_log2(float s, float cap_in, float cap_out) {
+  float y = s * cap_in;
+  float t = exp2_fast(y * (2.0f * kLog2e));
+  float th = 1.0f - 2.0f * rcp_fast(t + 1.0f);
+  return th * cap_out;
 }
 
 // Per-lane view of the mask: this lane's query position and the bounds.
 struct LaneMask {
-  int64_t pos;  // key-axis position of this lane's query row
+  int pos;      // key-axis position of this lane's query row
   int kend;     // keys >= kend are invisible (sequence / split end)
   int kbeg;     // keys < kbeg are invisible (split start)
   int causal, wl, wr;
-  __device__ __forceinline__ bool visible(int key) const {
-    if (key >= kend || key < kbeg) return false;
-    if (causal && key > pos) return false;
-    if (wl >= 0 && key < pos - wl) return false;
-    if (wr >= 0 && key > pos + wr) return false;
-    return true;
+  __device__ __forceinline__ bool visible(int key) const {  // branch-free
+    return (key < kend) & (key >= kbeg) & (!causal | (key <= pos)) & ((wl < 0) | (key >= pos - wl)) &
+           ((wr < 0) | (key <= pos + wr));
   }
 };
 
-// Online softmax over NB key blocks held in s[] (already in the log2 domain and
-// masked).  m_run is the running maximum, l_run this lane's partial row sum.
-template <int NB, int D>
-__device__ __forceinline__ void online_softmax(f32x16 (&s)[NB], float& m_run, float& l_run,
-                                               f32x16* o) {
-  float mx = kNegInf;
+// Online softmax over one 32-key block held in s.  Scores are in units where
+// p = exp2(s * c - m * c): raw scores with c = scale * log2(e), or softcapped
+// log2-domain scores with c = 1 (a positive c keeps the maximum where it is).
+// m_run is the running maximum in the same units, l_run this lane's partial row
+// sum; masked entries are -inf.
+template <int D>
+__device__ __forceinline__ void online_softmax(f32x16& s, float& m_run, float& l_run, f32x16* o,
+                                               float c) {
+  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[b][a]);
-  mx = fmaxf(mx, xor32(mx));
+  for (int a = 3; a < 15; a += 2) mx = fmaxf(fmaxf(mx, s[a]), s[a + 1]);
+  mx = fmaxf(mx, s[15]);
+  mx = pair_max(mx);
   const float m_new = fmaxf(m_run, mx);
   // a row that has seen no visible key yet keeps m = -inf; use 0 as the offset so
   // that exp2(-inf - offset) = 0 instead of NaN ("Attention kernels...", section 7.3)
   const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-  const float alpha = exp2_fast(m_run - m_use);
+  const float alpha = exp2_fast((m_run - m_use) * c);
+  const float nmc = -m_use * c;
   float rs = 0.0f;
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      float p = exp2_fast(s[b][a] - m_use);
-      s[b][a] = p;
-      rs += p;
-    }
-  l_run = l_run * alpha + rs;
+  for (int a = 0; a < 16; ++a) {
+    float pa = exp2_fast(__builtin_fmaf(s[a], c, nmc));
+    s[a] = pa;
+    rs += pa;
+  }
+  l_run = __builtin_fmaf(l_run, alpha, rs);
   if (!__all(alpha == 1.0f)) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
@@ -372,25 +327,32 @@ __device__ __forceinline__ bool dense_tile(const FaParams& p, int64_t t, TileId*
 }
 
 // ------------------------------------------------------------------ prefill kernel
+// ------------------------------------------------------------------ prefill kernel
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads) void fa_prefill_kernel(FaParams p) {
+__global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   constexpr int BN = FA_BLOCK_N;
-  constexpr int kStageBytes = BN * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kStageBytes];
-  // stage buffer `buf` holds K at smem + 2 * buf * kStageBytes and V right after it
-  auto lk = [&](int buf) { return smem + 2 * buf * kStageBytes; };
-  auto lv = [&](int buf) { return smem + (2 * buf + 1) * kStageBytes; };
+  using G = DmaGeom<D, BN>;
+  constexpr int kStage = 2 * G::kTensorBytes;  // K then V
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int kg = lane >> 5;
-  const ScoreXf xf = {p.scale_log2, p.cap_in, p.cap_out};
+  const float c = SOFTCAP ? 1.0f : p.scale_log2;
 
-  const int G = gridDim.x;
+  LaneOffsets<D> off;
+  off.init(lane);
+  // DMA geometry of this lane: stage row and the source chunk for K and V
+  const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
+  const int dma_pc = lane % G::kChunksPerRow;
+  const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
+  const int v_src = (dma_pc ^ v_swz<D>(dma_row)) * 8;
+
+  const int G_ = gridDim.x;
   for (int64_t round = 0;; ++round) {
-    const int64_t t = p.persistent ? tile_index(round, blockIdx.x, G) : (round == 0 ? (int64_t)blockIdx.x : -1);
+    const int64_t t = p.persistent ? tile_index(round, blockIdx.x, G_) : (round == 0 ? (int64_t)blockIdx.x : -1);
     if (t < 0) break;
     TileId tile;
     if (VARLEN) {
@@ -417,6 +379,18 @@ __global__ __launch_bounds__(kThreads) void fa_prefill_kernel(FaParams p) {
     span.pos_hi = (int64_t)((m_end - 1) / p.gp) + (Lk - Lq);
     int n_lo, n_hi;
     fa_key_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &n_lo, &n_hi);
+    // key tiles [n_full_lo, n_full_hi) need no element mask
+    int n_full_lo = n_hi, n_full_hi = n_hi;
+    for (int n = n_lo; n < n_hi; ++n)
+      if (!(fa_tile_class(span, Lk, p.causal, p.wl, p.wr, BN, n) & (FA_TILE_MASK_LEFT | FA_TILE_MASK_RIGHT))) {
+        n_full_lo = n;
+        break;
+      }
+    for (int n = n_full_lo; n < n_hi; ++n)
+      if (fa_tile_class(span, Lk, p.causal, p.wl, p.wr, BN, n) & (FA_TILE_MASK_LEFT | FA_TILE_MASK_RIGHT)) {
+        n_full_hi = n;
+        break;
+      }
 
     // ---- this lane's query row
     const int row = m0 + wave * 32 + col;
@@ -432,68 +406,80 @@ __global__ __launch_bounds__(kThreads) void fa_prefill_kernel(FaParams p) {
       qreg[kk] = __builtin_bit_cast(bf16x8, x);
     }
     LaneMask mask;
-    mask.pos = (int64_t)tok + (Lk - Lq);
+    mask.pos = tok + (Lk - Lq);
     mask.kend = Lk;
     mask.kbeg = 0;
     mask.causal = p.causal;
     mask.wl = p.wl;
     mask.wr = p.wr;
 
-    KvSource src;
-    src.kb = p.k + (int64_t)tile.b * p.k_bs + k_start * p.k_ss + (int64_t)kvh * p.k_hs;
-    src.vb = p.v + (int64_t)tile.b * p.v_bs + k_start * p.v_ss + (int64_t)kvh * p.v_hs;
-    src.k_ss = p.k_ss;
-    src.v_ss = p.v_ss;
-    src.k_ps = 0;
-    src.v_ps = 0;
-    src.bt = nullptr;
-    src.page = 1;
-    src.kend = Lk;
+    // DMA sources: this lane's row of every stage.  Rows past the last key (only
+    // in a final partial stage) are clamped to the last key so that they read
+    // real (finite) data, which the mask then drops.
+    const uint16_t* kbase = p.k + (int64_t)tile.b * p.k_bs + k_start * p.k_ss + (int64_t)kvh * p.k_hs;
+    const uint16_t* vbase = p.v + (int64_t)tile.b * p.v_bs + k_start * p.v_ss + (int64_t)kvh * p.v_hs;
+    const uint16_t* klane = kbase + (int64_t)dma_row * p.k_ss + k_src;
+    const uint16_t* vlane = vbase + (int64_t)dma_row * p.v_ss + v_src;
+    const int64_t k_step = (int64_t)G::kRowStep * p.k_ss, v_step = (int64_t)G::kRowStep * p.v_ss;
+    auto issue = [&](int n, int buf) {
+      char* dst = smem + buf * kStage + wave * 1024;
+      const int n0 = n * BN;
+      if (n0 + BN <= Lk) {
+        const uint16_t* kq = klane + (int64_t)n0 * p.k_ss;
+        const uint16_t* vq = vlane + (int64_t)n0 * p.v_ss;
+#pragma unroll
+        for (int i = 0; i < G::kInstPerWave; ++i) {
+          dma16(kq + i * k_step, dst + i * 4096);
+          dma16(vq + i * v_step, dst + G::kTensorBytes + i * 4096);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < G::kInstPerWave; ++i) {
+          int key = n0 + dma_row + i * G::kRowStep;
+          key = key < Lk ? key : Lk - 1;
+          dma16(kbase + (int64_t)key * p.k_ss + k_src, dst + i * 4096);
+          dma16(vbase + (int64_t)key * p.v_ss + v_src, dst + G::kTensorBytes + i * 4096);
+        }
+      }
+    };
 
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
     float m_run = kNegInf, l_run = 0.0f;
 
-    Stage<D, BN> st;
-    if (n_lo < n_hi) {
-      st.template load<false>(src, n_lo * BN, tid);
-      st.store(lk(0), lv(0), tid);
-      __syncthreads();
-    }
+    if (n_lo < n_hi) issue(n_lo, 0);
     for (int n = n_lo; n < n_hi; ++n) {
       const int buf = (n - n_lo) & 1;
-      const bool more = n + 1 < n_hi;
-      if (more) st.template load<false>(src, (n + 1) * BN, tid);
-
-      f32x16 s[2];
-      s[0] = qk_block<D>(lk(buf), 0, qreg, lane);
-      s[1] = qk_block<D>(lk(buf), 1, qreg, lane);
-      const int cls = fa_tile_class(span, Lk, p.causal, p.wl, p.wr, BN, n);
-      if (cls & (FA_TILE_MASK_LEFT | FA_TILE_MASK_RIGHT)) {
+      wait_vmcnt<0>();
+      __syncthreads();  // stage n is in LDS for everyone; the other buffer is free
+      if (n + 1 < n_hi) issue(n + 1, buf ^ 1);
+      const char* lk = smem + buf * kStage;
+      const char* lv = lk + G::kTensorBytes;
+      const bool masked = n < n_full_lo || n >= n_full_hi;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        f32x16 s = qk_block<D>(lk, kb, qreg, off);
+        if (masked) {
 #pragma unroll
           for (int a = 0; a < 16; ++a) {
-            const int key = n * BN + 32 * b + 8 * (a >> 2) + 4 * kg + (a & 3);
-            s[b][a] = mask.visible(key) ? score<SOFTCAP>(s[b][a], xf) : kNegInf;
+            const int key = n * BN + 32 * kb + 8 * (a >> 2) + 4 * kg + (a & 3);
+            float x = SOFTCAP ? softcap_log2(s[a], p.cap_in, p.cap_out) : s[a];
+            s[a] = mask.visible(key) ? x : kNegInf;
           }
-      } else {
+        } else if (SOFTCAP) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int a = 0; a < 16; ++a) s[b][a] = score<SOFTCAP>(s[b][a], xf);
+          for (int a = 0; a < 16; ++a) s[a] = softcap_log2(s[a], p.cap_in, p.cap_out);
+        }
+        online_softmax<D>(s, m_run, l_run, o, c);
+        pv_chunk<D>(lv, 2 * kb, pack_p(s, 0), o, off);
+        pv_chunk<D>(lv, 2 * kb + 1, pack_p(s, 1), o, off);
       }
-      online_softmax<2, D>(s, m_run, l_run, o);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) pv_chunk<D>(lv(buf), c, pack_p(s[c >> 1], c & 1), o, lane);
-
-      if (more) st.store(lk(buf ^ 1), lv(buf ^ 1), tid);
-      __syncthreads();
     }
+    __syncthreads();  // every wave is done with the stage buffers before the next tile
 
-    // ---- epilogue: O / l and LSE = (m + log2 l) ln 2
-    const float l_tot = l_run + xor32(l_run);
+    // ---- epilogue: O / l and LSE = (m c + log2 l) ln 2
+    const float l_tot = pair_sum(l_run);
     const bool empty = (m_run == kNegInf) || !(l_tot > 0.0f);
     const float inv = empty ? 0.0f : rcp_fast(l_tot);
     if (row_ok) {
@@ -511,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void fa_prefill_kernel(FaParams p) {
           *reinterpret_cast<u32x2*>(ob + 32 * db + 8 * q4 + 4 * kg) = z;
         }
       if (kg == 0 && p.lse) {
-        const float lse = empty ? kNegInf : (m_run + log2_fast(l_tot)) * kLn2;
+        const float lse = empty ? kNegInf : (m_run * c + log2_fast(l_tot)) * kLn2;
         p.lse[(int64_t)tile.b * p.lse_bs + (int64_t)head * p.lse_hs + q_start + tok] = lse;
       }
     }
@@ -524,22 +510,29 @@ __global__ __launch_bounds__(kThreads) void fa_prefill_kernel(FaParams p) {
 // (seqlen_q tokens x g heads, at most 32) are the same for all four waves; each
 // 128-key stage is split 32 keys per wave, and the waves' partial states are
 // merged through LDS at the end ("Attention kernels...", section 6.3: partial
-// states combine with the same rescale as the tiles).
+// states combine with the same rescale as the tiles).  When the page size is a
+// multiple of the stage, a stage lies in one page and its physical page is one
+// scalar block-table read; otherwise every row looks its page up.
 template <int D, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads) void fa_paged_kernel(FaParams p) {
+__global__ __launch_bounds__(kThreads, 1) void fa_paged_kernel(FaParams p) {
   constexpr int NK = FA_PAGED_STAGE;
-  constexpr int kStageBytes = NK * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kStageBytes];
-  // stage buffer `buf` holds K at smem + 2 * buf * kStageBytes and V right after it
-  auto lk = [&](int buf) { return smem + 2 * buf * kStageBytes; };
-  auto lv = [&](int buf) { return smem + (2 * buf + 1) * kStageBytes; };
+  using G = DmaGeom<D, NK>;
+  constexpr int kStage = 2 * G::kTensorBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int kg = lane >> 5;
-  const ScoreXf xf = {p.scale_log2, p.cap_in, p.cap_out};
+  const float c = SOFTCAP ? 1.0f : p.scale_log2;
+
+  LaneOffsets<D> off;
+  off.init(lane);
+  const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
+  const int dma_pc = lane % G::kChunksPerRow;
+  const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
+  const int v_src = (dma_pc ^ v_swz<D>(dma_row)) * 8;
 
   const int S = p.num_splits;
   const int unit = blockIdx.x;
@@ -556,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void fa_paged_kernel(FaParams p) {
   const int k_lo = p0 * p.page;
   const int k_hi = min(p1 * p.page, Lk);
 
-  // rows' key-range, intersected with this split
+  // rows' key range, intersected with this split
   FaRowSpan span;
   span.pos_lo = (int64_t)(Lk - Lq);
   span.pos_hi = (int64_t)(Lq - 1) + (Lk - Lq);
@@ -568,9 +561,10 @@ __global__ __launch_bounds__(kThreads) void fa_paged_kernel(FaParams p) {
     kb0 = 0;
     kb1 = 0;
   }
-  // stages start on a page boundary of the split so a stage never crosses splits
+  // stages start at the split start plus multiples of the stage size
   const int st_first = (int)(kb0 > k_lo ? k_lo + ((kb0 - k_lo) / NK) * NK : k_lo);
   const int nst = kb1 > kb0 ? (int)((kb1 - st_first + NK - 1) / NK) : 0;
+  const int kend = (int)kb1;
 
   const bool row_ok = col < rows;
   const int tok = row_ok ? col / p.g : 0;
@@ -584,60 +578,80 @@ __global__ __launch_bounds__(kThreads) void fa_paged_kernel(FaParams p) {
     qreg[kk] = __builtin_bit_cast(bf16x8, x);
   }
   LaneMask mask;
-  mask.pos = (int64_t)tok + (Lk - Lq);
-  mask.kend = (int)kb1;
+  mask.pos = tok + (Lk - Lq);
+  mask.kend = kend;
   mask.kbeg = (int)kb0;
   mask.causal = p.causal;
   mask.wl = p.wl;
   mask.wr = p.wr;
 
-  KvSource src;
-  src.kb = p.k + (int64_t)kvh * p.k_hs;
-  src.vb = p.v + (int64_t)kvh * p.v_hs;
-  src.k_ss = p.k_ss;
-  src.v_ss = p.v_ss;
-  src.k_ps = p.k_bs;
-  src.v_ps = p.v_bs;
-  src.bt = p.block_table + (int64_t)b * p.max_blocks;
-  src.page = p.page;
-  src.kend = (int)kb1;
+  const uint16_t* kpool = p.k + (int64_t)kvh * p.k_hs;
+  const uint16_t* vpool = p.v + (int64_t)kvh * p.v_hs;
+  const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks;
+  const bool page_aligned = (p.page % NK) == 0;
+  auto issue = [&](int n0, int buf) {
+    char* dst = smem + buf * kStage + wave * 1024;
+    if (page_aligned) {
+      // the whole stage is in one page: one scalar table read
+      const int64_t phys = bt[n0 / p.page];
+      const int slot0 = n0 % p.page;
+      const uint16_t* kp = kpool + phys * p.k_bs;
+      const uint16_t* vp = vpool + phys * p.v_bs;
+#pragma unroll
+      for (int i = 0; i < G::kInstPerWave; ++i) {
+        int r = dma_row + i * G::kRowStep;
+        int key = n0 + r;
+        int slot = (key < kend ? slot0 + r : (kend - 1) % p.page);
+        const int64_t ph = key < kend ? phys : (int64_t)bt[(kend - 1) / p.page];
+        const uint16_t* kq = key < kend ? kp : kpool + ph * p.k_bs;
+        const uint16_t* vq = key < kend ? vp : vpool + ph * p.v_bs;
+        dma16(kq + (int64_t)slot * p.k_ss + k_src, dst + i * 4096);
+        dma16(vq + (int64_t)slot * p.v_ss + v_src, dst + G::kTensorBytes + i * 4096);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::kInstPerWave; ++i) {
+        int key = n0 + dma_row + i * G::kRowStep;
+        key = key < kend ? key : kend - 1;
+        const int64_t phys = bt[key / p.page];
+        const int slot = key % p.page;
+        dma16(kpool + phys * p.k_bs + (int64_t)slot * p.k_ss + k_src, dst + i * 4096);
+        dma16(vpool + phys * p.v_bs + (int64_t)slot * p.v_ss + v_src, dst + G::kTensorBytes + i * 4096);
+      }
+    }
+  };
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.0f;
 
-  Stage<D, NK> st;
-  if (nst > 0) {
-    st.template load<true>(src, st_first, tid);
-    st.store(lk(0), lv(0), tid);
-    __syncthreads();
-  }
+  if (nst > 0) issue(st_first, 0);
   for (int i = 0; i < nst; ++i) {
     const int buf = i & 1;
-    const bool more = i + 1 < nst;
     const int n0 = st_first + i * NK;
-    if (more) st.template load<true>(src, n0 + NK, tid);
-
-    f32x16 s[1];
-    s[0] = qk_block<D>(lk(buf), wave, qreg, lane);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (i + 1 < nst) issue(n0 + NK, buf ^ 1);
+    const char* lk = smem + buf * kStage;
+    const char* lv = lk + G::kTensorBytes;
+    f32x16 s = qk_block<D>(lk, wave, qreg, off);
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
       const int key = n0 + 32 * wave + 8 * (a >> 2) + 4 * kg + (a & 3);
-      s[0][a] = mask.visible(key) ? score<SOFTCAP>(s[0][a], xf) : kNegInf;
+      float x = SOFTCAP ? softcap_log2(s[a], p.cap_in, p.cap_out) : s[a];
+      s[a] = mask.visible(key) ? x : kNegInf;
     }
-    online_softmax<1, D>(s, m_run, l_run, o);
-    pv_chunk<D>(lv(buf), 2 * wave, pack_p(s[0], 0), o, lane);
-    pv_chunk<D>(lv(buf), 2 * wave + 1, pack_p(s[0], 1), o, lane);
-
-    if (more) st.store(lk(buf ^ 1), lv(buf ^ 1), tid);
-    __syncthreads();
+    online_softmax<D>(s, m_run, l_run, o, c);
+    pv_chunk<D>(lv, 2 * wave, pack_p(s, 0), o, off);
+    pv_chunk<D>(lv, 2 * wave + 1, pack_p(s, 1), o, off);
   }
+  __syncthreads();
 
   // ---- merge the four waves' states through LDS
   float* mo = reinterpret_cast<float*>(smem);               // [4][32 cols][D]
   float* ml = mo + 4 * 32 * D;                              // [4][32] m, then [4][32] l
-  const float l_w = l_run + xor32(l_run);
+  const float l_w = pair_sum(l_run);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -646,60 +660,57 @@ __global__ __launch_bounds__(kThreads) void fa_paged_kernel(FaParams p) {
       mo[(wave * 32 + col) * D + d] = o[db][a];
     }
   if (kg == 0) {
-    ml[wave * 32 + col] = m_run;
+    ml[wave * 32 + col] = m_run * c;   // log2 units
     ml[128 + wave * 32 + col] = l_w;
   }
   __syncthreads();
 
   // thread -> (column, 16 consecutive d values)
   constexpr int kParts = D / 16;             // 8 for D = 128, 4 for D = 64
-  constexpr int kCols = kThreads / kParts;   // 32 for D = 128, 64 for D = 64
-  const int c = tid / kParts;
+  const int cc = tid / kParts;
   const int d0 = (tid % kParts) * 16;
-  if (kCols >= 32 ? c < 32 : true) {
-    if (c < rows) {
-      float M = kNegInf;
+  if (cc < 32 && cc < rows) {
+    float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[w * 32 + c]);
-      float e[4], L = 0.0f;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[w * 32 + cc]);
+    float e[4], L = 0.0f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = ml[w * 32 + c];
-        e[w] = (mw == kNegInf) ? 0.0f : exp2_fast(mw - M);
-        L += e[w] * ml[128 + w * 32 + c];
+    for (int w = 0; w < 4; ++w) {
+      const float mw = ml[w * 32 + cc];
+      e[w] = (mw == kNegInf) ? 0.0f : exp2_fast(mw - M);
+      L += e[w] * ml[128 + w * 32 + cc];
+    }
+    const bool empty = (M == kNegInf) || !(L > 0.0f);
+    const float inv = empty ? 0.0f : rcp_fast(L);
+    float acc[16];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) sum += e[w] * mo[(w * 32 + cc) * D + d0 + x];
+      acc[x] = sum * inv;
+    }
+    const float lse = empty ? kNegInf : (M + log2_fast(L)) * kLn2;
+    const int ctok = cc / p.g;
+    const int chead = kvh * p.g + cc % p.g;
+    const int64_t r = ((int64_t)b * p.Hq + chead) * Lq + ctok;  // LSE row order
+    if (S == 1) {
+      uint16_t* ob = p.o + (int64_t)b * p.o_bs + (int64_t)ctok * p.o_ss + (int64_t)chead * p.o_hs + d0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x8 x;
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) x[e2] = acc[8 * h + e2];
+        *reinterpret_cast<bf16x8*>(ob + 8 * h) = __builtin_convertvector(x, bf16x8);
       }
-      const bool empty = (M == kNegInf) || !(L > 0.0f);
-      const float inv = empty ? 0.0f : rcp_fast(L);
-      float acc[16];
+      if (d0 == 0 && p.lse) p.lse[r] = lse;
+    } else {
+      const int64_t rows_all = (int64_t)p.B * p.Hq * Lq;
+      float* op = p.o_part + ((int64_t)split * rows_all + r) * D + d0;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) sum += e[w] * mo[(w * 32 + c) * D + d0 + x];
-        acc[x] = sum * inv;
-      }
-      const float lse = empty ? kNegInf : (M + log2_fast(L)) * kLn2;
-      const int ctok = c / p.g;
-      const int chead = kvh * p.g + c % p.g;
-      const int64_t r = ((int64_t)b * p.Hq + chead) * Lq + ctok;  // LSE row order
-      if (S == 1) {
-        uint16_t* ob = p.o + (int64_t)b * p.o_bs + (int64_t)ctok * p.o_ss + (int64_t)chead * p.o_hs + d0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          f32x8 x;
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) x[e2] = acc[8 * h + e2];
-          *reinterpret_cast<bf16x8*>(ob + 8 * h) = __builtin_convertvector(x, bf16x8);
-        }
-        if (d0 == 0 && p.lse) p.lse[r] = lse;
-      } else {
-        const int64_t rows_all = (int64_t)p.B * p.Hq * Lq;
-        float* op = p.o_part + ((int64_t)split * rows_all + r) * D + d0;
-#pragma unroll
-        for (int x = 0; x < 16; x += 4)
-          *reinterpret_cast<float4*>(op + x) = make_float4(acc[x], acc[x + 1], acc[x + 2], acc[x + 3]);
-        if (d0 == 0) p.lse_part[(int64_t)split * rows_all + r] = lse;
-      }
+      for (int x = 0; x < 16; x += 4)
+        *reinterpret_cast<float4*>(op + x) = make_float4(acc[x], acc[x + 1], acc[x + 2], acc[x + 3]);
+      if (d0 == 0) p.lse_part[(int64_t)split * rows_all + r] = lse;
     }
   }
 }
