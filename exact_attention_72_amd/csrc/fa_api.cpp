@@ -8,7 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_blockinfo.h"
 #include "fa_internal.h"
 

@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_blockinfo.h"
 #include "fa_internal.h"
 
@@ -90,6 +92,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for the stage pipeline.  __syncthreads() adds a memory fence
+// that waits for every outstanding vector-memory operation, including the LDS-DMA
+// loads of later blocks that are meant to stay in flight across this barrier.
+// Here each wave has already waited (s_waitcnt vmcnt) for the DMA of the block
+// the barrier publishes, and its LDS reads of the buffer about to be refilled
+// have completed (their results were consumed), so a bare s_barrier suffices;
+// the empty asm statements keep the compiler from moving memory operations
+// across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ LDS layout
 // A stage holds NK rows of K and NK rows of V, each row D bf16 (2D bytes),
 // row-major.  Stored 16-byte chunk = logical chunk ^ swizzle(row).
@@ -121,67 +137,151 @@ __device__ __forceinline__ void dma16(const uint16_t* src, char* lds_dst) {
 }
 
 // ------------------------------------------------------------------ per-wave math
-// Per-lane LDS byte offsets of the MFMA operands, fixed for the whole kernel.
+// 32-bit LDS address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const FA_LDS char*)p);
+}
+
+// Per-lane LDS byte addresses of the MFMA operands within a stage buffer at
+// LDS address base, fixed for the whole kernel.
 template <int D>
 struct LaneOffsets {
-  int k[D / 16];  // K row (lane % 32), chunk (2 kk + kg) of the first 32-key block
-  int v[D / 32];  // V transposed-read address of d-block db for keys 4 kg + (j >> 2)
-  __device__ __forceinline__ void init(int lane) {
+  uint32_t k[D / 16];  // K row (lane % 32), chunk (2 kk + kg)
+  uint32_t v[D / 32];  // V transposed-read address of d-block db for keys 4 kg + (j >> 2)
+  __device__ __forceinline__ void init(int lane, uint32_t base) {
     const int col = lane & 31, kg = lane >> 5;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) k[kk] = col * (2 * D) + (((2 * kk + kg) ^ k_swz<D>(col)) << 4);
+    for (int kk = 0; kk < D / 16; ++kk) k[kk] = base + col * (2 * D) + (((2 * kk + kg) ^ k_swz<D>(col)) << 4);
     const int j = lane & 15, half = (lane >> 4) & 1;
     const int row = 4 * kg + (j >> 2);
     const int sw = v_swz<D>(row);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int c16 = 4 * db + 2 * half + ((j & 3) >> 1);
-      v[db] = row * (2 * D) + ((c16 ^ sw) << 4) + (j & 1) * 8;
+      v[db] = base + row * (2 * D) + ((c16 ^ sw) << 4) + (j & 1) * 8;
     }
   }
 };
 
-// S^T for the 32 keys [32 kb, 32 kb + 32) of the stage against the wave's 32
-// query columns.  Lane (j, kg) gets keys 32 kb + 8 (a / 4) + 4 kg + (a % 4).
-template <int D>
-__device__ __forceinline__ f32x16 qk_block(const char* lk, int kb, const bf16x8* qreg,
-                                           const LaneOffsets<D>& off) {
-  bf16x8 a[D / 16];  // all operand reads in flight before the first product
+// LDS operand reads issued as inline assembly.  The compiler cannot tell that
+// these reads and an in-flight LDS-DMA load into another stage buffer touch
+// different bytes, and would otherwise wait for every outstanding DMA (vmcnt(0))
+// before the reads.  The results are waited for explicitly with lgkmcnt(0),
+// tied to the result registers.
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// S^T for the 32 keys whose K rows start at byte OFF (plus delta) of the stage
+// buffers, against the wave's 32 query columns.  Lane (j, kg) gets keys
+// 8 (a / 4) + 4 kg + (a % 4) of the block.
+template <int D, int OFF>
+__device__ __forceinline__ f32x16 qk_block(uint32_t delta, const bf16x8* qreg, const LaneOffsets<D>& off) {
+  u32x4 a[D / 16];  // all operand reads in flight before the first product
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    a[kk] = *reinterpret_cast<const bf16x8*>(lk + kb * 32 * (2 * D) + off.k[kk]);
-  __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+  for (int kk = 0; kk < D / 16; ++kk) a[kk] = ds_read_b128<OFF>(off.k[kk] + delta);
+  if constexpr (D == 128) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+                   "+v"(a[7]));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+  }
   f32x16 s = {};
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) s = mfma32(a[kk], qreg[kk], s);
+  for (int kk = 0; kk < D / 16; ++kk) s = mfma32(__builtin_bit_cast(bf16x8, a[kk]), qreg[kk], s);
   return s;
 }
 
-// O^T += V^T P^T for the 16 keys [16 c, 16 c + 16) of the stage.  pb holds P^T
-// for keys 16 c + 8 (slot / 4) + 4 kg + (slot % 4) of this lane's column; two
-// transposed reads give the V^T operand in the same key order.
-template <int D>
-__device__ __forceinline__ void pv_chunk(const char* lv, int c, bf16x8 pb, f32x16* o,
-                                         const LaneOffsets<D>& off) {
-  u32x4 w[D / 32];
+// O^T += V^T P^T for the 16 keys whose V rows start at byte OFF (plus delta) of
+// the stage buffers.  pb holds P^T for keys 8 (slot / 4) + 4 kg + (slot % 4) of
+// those 16 and of this lane's column; two transposed reads per d-block give the
+// V^T operand in the same key order.
+template <int D, int OFF>
+__device__ __forceinline__ void pv_chunk(uint32_t delta, bf16x8 pb, f32x16* o, const LaneOffsets<D>& off) {
+  u32x2 lo[D / 32], hi[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    const char* base = lv + c * 16 * (2 * D) + off.v[db];
-    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base));
-    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(base + 8 * (2 * D)));
-    u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    w[db] = u32x4{l2.x, l2.y, h2.x, h2.y};
+    lo[db] = ds_read_tr16<OFF>(off.v[db] + delta);
+    hi[db] = ds_read_tr16<OFF + 8 * (2 * D)>(off.v[db] + delta);
   }
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (D == 128) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]), "+v"(lo[2]), "+v"(hi[2]),
+                   "+v"(lo[3]), "+v"(hi[3]));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]));
+  }
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = mfma32(__builtin_bit_cast(bf16x8, w[db]), pb, o[db]);
+  for (int db = 0; db < D / 32; ++db) {
+    u32x4 w = {lo[db].x, lo[db].y, hi[db].x, hi[db].y};
+    o[db] = mfma32(__builtin_bit_cast(bf16x8, w), pb, o[db]);
+  }
 }
 
-__device__ __forceinline__ bf16x8 pack_p(const f32x16& s, int half) {
-  f32x8 x;
+// Split forms of qk_block / pv_chunk for the software-pipelined prefill step:
+// the reads are issued early, and waited for with an LDS counter that lets the
+// reads issued after them stay in flight (LDS reads complete in issue order).
+template <int D, int OFF>
+__device__ __forceinline__ void read_k(uint32_t delta, const LaneOffsets<D>& off, u32x4 (&a)[D / 16]) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) x[t] = s[8 * half + t];
-  return __builtin_convertvector(x, bf16x8);
+  for (int kk = 0; kk < D / 16; ++kk) a[kk] = ds_read_b128<OFF>(off.k[kk] + delta);
+}
+template <int D, int OFF>
+__device__ __forceinline__ void read_v(uint32_t delta, const LaneOffsets<D>& off, u32x2 (&lo)[D / 32],
+                                       u32x2 (&hi)[D / 32]) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    lo[db] = ds_read_tr16<OFF>(off.v[db] + delta);
+    hi[db] = ds_read_tr16<OFF + 8 * (2 * D)>(off.v[db] + delta);
+  }
+}
+// Wait until at most N LDS operations are outstanding; the listed registers
+// are treated as written by the wait, so no use of them moves above it.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4 (&a)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+               : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4 (&a)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x2 (&lo)[4], u32x2 (&hi)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]), "+v"(lo[2]), "+v"(hi[2]), "+v"(lo[3]),
+                 "+v"(hi[3])
+               : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x2 (&lo)[2], u32x2 (&hi)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(lo[0]), "+v"(hi[0]), "+v"(lo[1]), "+v"(hi[1]) : "i"(N));
+}
+template <int D>
+__device__ __forceinline__ f32x16 qk_mma(const u32x4 (&a)[D / 16], const bf16x8* qreg) {
+  f32x16 s = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) s = mfma32(__builtin_bit_cast(bf16x8, a[kk]), qreg[kk], s);
+  return s;
+}
+template <int D>
+__device__ __forceinline__ void pv_mma(const u32x2 (&lo)[D / 32], const u32x2 (&hi)[D / 32], bf16x8 pb, f32x16* o) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    u32x4 w = {lo[db].x, lo[db].y, hi[db].x, hi[db].y};
+    o[db] = mfma32(__builtin_bit_cast(bf16x8, w), pb, o[db]);
+  }
 }
 
 // Softcap transform into the log2 domain: c * tanh(scale * s / c) * log2(e),
@@ -208,35 +308,115 @@ struct LaneMask {
 // Online softmax over one 32-key block held in s.  Scores are in units where
 // p = exp2(s * c - m * c): raw scores with c = scale * log2(e), or softcapped
 // log2-domain scores with c = 1 (a positive c keeps the maximum where it is).
-// m_run is the running maximum in the same units, l_run this lane's partial row
-// sum; masked entries are -inf.
+// m_run is the reference maximum in the same units.  Two partial row sums are
+// kept for this lane: l_run of the fp32 probabilities (for the log-sum-exp) and
+// l_bf of the bf16-rounded probabilities that enter the P V product (for the
+// division of O, so the weights of O sum to one exactly).  Masked entries are -inf.
+//
+// The reference moves only when the running maximum exceeds it by more than
+// 2^kRescaleLog2 (or on the first visible key): exponents stay below that bound,
+// and since O and l are both relative to the same reference the result is the
+// same up to rounding, while the rescale of O (a multiply per accumulator) and
+// its exponential are skipped on most blocks.  The decision is wave-uniform.
+constexpr float kRescaleLog2 = 8.0f;
+
 template <int D>
-__device__ __forceinline__ void online_softmax(f32x16& s, float& m_run, float& l_run, f32x16* o,
-                                               float c) {
+__device__ __forceinline__ void online_softmax(f32x16& s, float& m_run, float& l_run, float& l_bf,
+                                               f32x16* o, float c, bf16x8& p0, bf16x8& p1) {
   float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
   for (int a = 3; a < 15; a += 2) mx = fmaxf(fmaxf(mx, s[a]), s[a + 1]);
   mx = fmaxf(mx, s[15]);
   mx = pair_max(mx);
-  const float m_new = fmaxf(m_run, mx);
-  // a row that has seen no visible key yet keeps m = -inf; use 0 as the offset so
-  // that exp2(-inf - offset) = 0 instead of NaN ("Attention kernels...", section 7.3)
-  const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-  const float alpha = exp2_fast((m_run - m_use) * c);
-  const float nmc = -m_use * c;
-  float rs = 0.0f;
-#pragma unroll
-  for (int a = 0; a < 16; ++a) {
-    float pa = exp2_fast(__builtin_fmaf(s[a], c, nmc));
-    s[a] = pa;
-    rs += pa;
-  }
-  l_run = __builtin_fmaf(l_run, alpha, rs);
-  if (!__all(alpha == 1.0f)) {
+  const float m_cand = fmaxf(m_run, mx);
+  // (-inf) - (-inf) is NaN, which compares false: no move while nothing is visible
+  if (__any((m_cand - m_run) * c > kRescaleLog2)) {
+    // a row that has seen no visible key keeps m = -inf; use 0 as the offset so
+    // that exp2(-inf - offset) = 0 instead of NaN ("Attention kernels...", section 7.3)
+    const float m_use = (m_cand == kNegInf) ? 0.0f : m_cand;
+    const float alpha = exp2_fast((m_run - m_use) * c);
+    l_run *= alpha;
+    l_bf *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    m_run = m_cand;
   }
-  m_run = m_new;
+  const float nmc = (m_run == kNegInf) ? 0.0f : -m_run * c;
+  float rs = 0.0f;
+  f32x8 x0, x1;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    x0[a] = exp2_fast(__builtin_fmaf(s[a], c, nmc));
+    x1[a] = exp2_fast(__builtin_fmaf(s[a + 8], c, nmc));
+  }
+#pragma unroll
+  for (int a = 0; a < 8; ++a) rs += x0[a] + x1[a];
+  l_run += rs;
+  p0 = __builtin_convertvector(x0, bf16x8);
+  p1 = __builtin_convertvector(x1, bf16x8);
+  // the same weights the P V product uses: sum of the bf16-rounded probabilities
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    l_bf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * a], p0[2 * a + 1]}, one, l_bf, false);
+    l_bf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * a], p1[2 * a + 1]}, one, l_bf, false);
+  }
+}
+
+// The same online softmax split into the parts the prefill pipeline places in
+// different regions of its loop body (see the prefill kernel).
+
+// Block maximum of s over this lane pair.
+__device__ __forceinline__ float block_max(const f32x16& s) {
+  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+  for (int a = 3; a < 15; a += 2) mx = fmaxf(fmaxf(mx, s[a]), s[a + 1]);
+  mx = fmaxf(mx, s[15]);
+  return pair_max(mx);
+}
+
+// Move the reference maximum to max(m_run, mx) when it grew by more than
+// 2^kRescaleLog2 (or on the first visible key), rescaling O and the row sums.
+template <int D>
+__device__ __forceinline__ void update_reference(float mx, float& m_run, float& l_run, float& l_bf,
+                                                 f32x16* o, float c) {
+  const float m_cand = fmaxf(m_run, mx);
+  if (__any((m_cand - m_run) * c > kRescaleLog2)) {
+    const float m_use = (m_cand == kNegInf) ? 0.0f : m_cand;
+    const float alpha = exp2_fast((m_run - m_use) * c);
+    l_run *= alpha;
+    l_bf *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    m_run = m_cand;
+  }
+}
+
+// Probabilities of s relative to the reference m_run, as two bf16 MFMA operands,
+// and their contribution to both row sums.
+__device__ __forceinline__ void block_probs(const f32x16& s, float m_run, float c, float& l_run,
+                                            float& l_bf, bf16x8& p0, bf16x8& p1) {
+  const float nmc = (m_run == kNegInf) ? 0.0f : -m_run * c;
+  f32x8 x0, x1;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    x0[a] = exp2_fast(__builtin_fmaf(s[a], c, nmc));
+    x1[a] = exp2_fast(__builtin_fmaf(s[a + 8], c, nmc));
+  }
+  float rs = 0.0f;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) rs += x0[a] + x1[a];
+  l_run += rs;
+  p0 = __builtin_convertvector(x0, bf16x8);
+  p1 = __builtin_convertvector(x1, bf16x8);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    l_bf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * a], p0[2 * a + 1]}, one, l_bf, false);
+    l_bf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * a], p1[2 * a + 1]}, one, l_bf, false);
+  }
 }
 
 // ------------------------------------------------------------------ tile scheduling
@@ -327,13 +507,18 @@ __device__ __forceinline__ bool dense_tile(const FaParams& p, int64_t t, TileId*
 }
 
 // ------------------------------------------------------------------ prefill kernel
-// ------------------------------------------------------------------ prefill kernel
+// Key blocks of 32 stream through a ring of four LDS stage buffers, two blocks
+// ahead of use.  Iteration i (one barrier) issues the DMA of block i + 3,
+// forms S^T of block i + 1, runs the softmax of block i and accumulates
+// O^T += V^T P^T of block i, so matrix products of one block and the softmax of
+// the previous one are independent work within the wave.
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
-  constexpr int BN = FA_BLOCK_N;
+  constexpr int BN = FA_BLOCK_N;  // 32 keys per block
+  constexpr int NBUF = 4;
   using G = DmaGeom<D, BN>;
   constexpr int kStage = 2 * G::kTensorBytes;  // K then V
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -343,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   const float c = SOFTCAP ? 1.0f : p.scale_log2;
 
   LaneOffsets<D> off;
-  off.init(lane);
+  off.init(lane, lds_addr(smem));
   // DMA geometry of this lane: stage row and the source chunk for K and V
   const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
   const int dma_pc = lane % G::kChunksPerRow;
@@ -379,7 +564,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     span.pos_hi = (int64_t)((m_end - 1) / p.gp) + (Lk - Lq);
     int n_lo, n_hi;
     fa_key_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &n_lo, &n_hi);
-    // key tiles [n_full_lo, n_full_hi) need no element mask
+    // key blocks [n_full_lo, n_full_hi) need no element mask
     int n_full_lo = n_hi, n_full_hi = n_hi;
     for (int n = n_lo; n < n_hi; ++n)
       if (!(fa_tile_class(span, Lk, p.causal, p.wl, p.wr, BN, n) & (FA_TILE_MASK_LEFT | FA_TILE_MASK_RIGHT))) {
@@ -391,6 +576,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
         n_full_hi = n;
         break;
       }
+    const int nb = n_hi - n_lo;
 
     // ---- this lane's query row
     const int row = m0 + wave * 32 + col;
@@ -413,75 +599,142 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     mask.wl = p.wl;
     mask.wr = p.wr;
 
-    // DMA sources: this lane's row of every stage.  Rows past the last key (only
-    // in a final partial stage) are clamped to the last key so that they read
+    // DMA sources: this lane's row of every block.  Rows past the last key (only
+    // in a final partial block) are clamped to the last key so that they read
     // real (finite) data, which the mask then drops.
     const uint16_t* kbase = p.k + (int64_t)tile.b * p.k_bs + k_start * p.k_ss + (int64_t)kvh * p.k_hs;
     const uint16_t* vbase = p.v + (int64_t)tile.b * p.v_bs + k_start * p.v_ss + (int64_t)kvh * p.v_hs;
     const uint16_t* klane = kbase + (int64_t)dma_row * p.k_ss + k_src;
     const uint16_t* vlane = vbase + (int64_t)dma_row * p.v_ss + v_src;
     const int64_t k_step = (int64_t)G::kRowStep * p.k_ss, v_step = (int64_t)G::kRowStep * p.v_ss;
-    auto issue = [&](int n, int buf) {
-      char* dst = smem + buf * kStage + wave * 1024;
-      const int n0 = n * BN;
+    // block i of this tile (key block n_lo + i) goes to buffer i % NBUF
+    auto issue = [&](int i) {
+      char* dst = smem + (i % NBUF) * kStage + wave * 1024;
+      const int n0 = (n_lo + i) * BN;
       if (n0 + BN <= Lk) {
         const uint16_t* kq = klane + (int64_t)n0 * p.k_ss;
         const uint16_t* vq = vlane + (int64_t)n0 * p.v_ss;
 #pragma unroll
-        for (int i = 0; i < G::kInstPerWave; ++i) {
-          dma16(kq + i * k_step, dst + i * 4096);
-          dma16(vq + i * v_step, dst + G::kTensorBytes + i * 4096);
+        for (int j = 0; j < G::kInstPerWave; ++j) {
+          dma16(kq + j * k_step, dst + j * 4096);
+          dma16(vq + j * v_step, dst + G::kTensorBytes + j * 4096);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < G::kInstPerWave; ++i) {
-          int key = n0 + dma_row + i * G::kRowStep;
+        for (int j = 0; j < G::kInstPerWave; ++j) {
+          int key = n0 + dma_row + j * G::kRowStep;
           key = key < Lk ? key : Lk - 1;
-          dma16(kbase + (int64_t)key * p.k_ss + k_src, dst + i * 4096);
-          dma16(vbase + (int64_t)key * p.v_ss + v_src, dst + G::kTensorBytes + i * 4096);
+          dma16(kbase + (int64_t)key * p.k_ss + k_src, dst + j * 4096);
+          dma16(vbase + (int64_t)key * p.v_ss + v_src, dst + G::kTensorBytes + j * 4096);
         }
       }
     };
+    constexpr int kDmaPerBlock = 2 * G::kInstPerWave;  // this wave's DMA instructions per block
 
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    float m_run = kNegInf, l_run = 0.0f;
+    float m_run = kNegInf, l_run = 0.0f, l_bf = 0.0f;
 
-    if (n_lo < n_hi) issue(n_lo, 0);
-    for (int n = n_lo; n < n_hi; ++n) {
-      const int buf = (n - n_lo) & 1;
-      wait_vmcnt<0>();
-      __syncthreads();  // stage n is in LDS for everyone; the other buffer is free
-      if (n + 1 < n_hi) issue(n + 1, buf ^ 1);
-      const char* lk = smem + buf * kStage;
-      const char* lv = lk + G::kTensorBytes;
-      const bool masked = n < n_full_lo || n >= n_full_hi;
+    // Element mask of block i (key block n_lo + i), applied in place.
+    auto apply_mask = [&](f32x16& sv, int i) {
+      const int n = n_lo + i;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        f32x16 s = qk_block<D>(lk, kb, qreg, off);
-        if (masked) {
-#pragma unroll
-          for (int a = 0; a < 16; ++a) {
-            const int key = n * BN + 32 * kb + 8 * (a >> 2) + 4 * kg + (a & 3);
-            float x = SOFTCAP ? softcap_log2(s[a], p.cap_in, p.cap_out) : s[a];
-            s[a] = mask.visible(key) ? x : kNegInf;
-          }
-        } else if (SOFTCAP) {
-#pragma unroll
-          for (int a = 0; a < 16; ++a) s[a] = softcap_log2(s[a], p.cap_in, p.cap_out);
-        }
-        online_softmax<D>(s, m_run, l_run, o, c);
-        pv_chunk<D>(lv, 2 * kb, pack_p(s, 0), o, off);
-        pv_chunk<D>(lv, 2 * kb + 1, pack_p(s, 1), o, off);
+      for (int a = 0; a < 16; ++a) {
+        const int key = n * BN + 8 * (a >> 2) + 4 * kg + (a & 3);
+        sv[a] = mask.visible(key) ? sv[a] : kNegInf;
       }
+    };
+    auto transform = [&](f32x16& sv) {
+      if constexpr (SOFTCAP) {
+#pragma unroll
+        for (int a = 0; a < 16; ++a) sv[a] = softcap_log2(sv[a], p.cap_in, p.cap_out);
+      }
+    };
+    auto is_masked = [&](int i) { return n_lo + i < n_full_lo || n_lo + i >= n_full_hi; };
+
+    f32x16 s_cur = {};
+    if (nb > 0) {
+      issue(0);
+      if (nb > 1) issue(1);
+      if (nb > 2) issue(2);
+      // block 0 landed: at most the DMAs of blocks 1 and 2 may still be in flight
+      if (nb > 2) wait_vmcnt<2 * kDmaPerBlock>();
+      else if (nb > 1) wait_vmcnt<kDmaPerBlock>();
+      else wait_vmcnt<0>();
+      stage_barrier();
+      s_cur = qk_block<D, 0>(0u, qreg, off);
+      transform(s_cur);
+      if (is_masked(0)) apply_mask(s_cur, 0);
+      update_reference<D>(block_max(s_cur), m_run, l_run, l_bf, o, c);
+    }
+
+    // Pipeline step for block i (buffer B = i % NBUF) when block i + 1 exists.
+    // Region A: S^T of block i + 1 (MFMA) beside the probabilities of block i
+    // (VALU); region B: O^T += V^T P^T of block i (MFMA) beside the score
+    // transform and maximum of block i + 1 (VALU).  Neither region branches, so
+    // the scheduler can interleave the two kinds of work.  Blocks cut by a mask
+    // boundary (a few per tile) redo the maximum after the mask, and the rare move
+    // of the reference maximum follows.
+    auto step = [&](auto bufc, int i) {
+      constexpr int B = decltype(bufc)::value;
+      constexpr int BN1 = (B + 1) % NBUF;
+      constexpr int kV = B * kStage + G::kTensorBytes;
+      // block i + 1 landed (block i + 2 may still be in flight); everyone is done
+      // with block i - 1, whose buffer the DMA of block i + 3 reuses
+      if (i + 2 < nb) wait_vmcnt<kDmaPerBlock>();
+      else wait_vmcnt<0>();
+      stage_barrier();
+      if (i + 3 < nb) issue(i + 3);
+      // K of block i + 1 first: its latency hides under the softmax of block i
+      u32x4 ka[D / 16];
+      read_k<D, BN1 * kStage>(0u, off, ka);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 p0, p1;
+      block_probs(s_cur, m_run, c, l_run, l_bf, p0, p1);
+      u32x2 lo0[D / 32], hi0[D / 32], lo1[D / 32], hi1[D / 32];
+      read_v<D, kV>(0u, off, lo0, hi0);
+      lgkm_wait<2 * (D / 32)>(ka);  // only the V reads just issued may be outstanding
+      f32x16 s_next = qk_mma<D>(ka, qreg);
+      read_v<D, kV + 16 * (2 * D)>(0u, off, lo1, hi1);
+      transform(s_next);
+      float mx = block_max(s_next);
+      lgkm_wait<2 * (D / 32)>(lo0, hi0);
+      pv_mma<D>(lo0, hi0, p0, o);
+      lgkm_wait<0>(lo1, hi1);
+      pv_mma<D>(lo1, hi1, p1, o);
+      if (is_masked(i + 1)) {
+        apply_mask(s_next, i + 1);
+        mx = block_max(s_next);
+      }
+      update_reference<D>(mx, m_run, l_run, l_bf, o, c);
+      s_cur = s_next;
+    };
+    int i = 0;
+    for (; i + NBUF <= nb - 1; i += NBUF) {
+      step(std::integral_constant<int, 0>{}, i);
+      step(std::integral_constant<int, 1>{}, i + 1);
+      step(std::integral_constant<int, 2>{}, i + 2);
+      step(std::integral_constant<int, 3>{}, i + 3);
+    }
+    if (i + 1 <= nb - 1) step(std::integral_constant<int, 0>{}, i), ++i;
+    if (i + 1 <= nb - 1) step(std::integral_constant<int, 1>{}, i), ++i;
+    if (i + 1 <= nb - 1) step(std::integral_constant<int, 2>{}, i), ++i;
+    // last block (i == nb - 1, buffer i % NBUF): probabilities and P V only
+    if (nb > 0) {
+      bf16x8 p0, p1;
+      block_probs(s_cur, m_run, c, l_run, l_bf, p0, p1);
+      const uint32_t delta = (uint32_t)((i % NBUF) * kStage);
+      pv_chunk<D, G::kTensorBytes>(delta, p0, o, off);
+      pv_chunk<D, G::kTensorBytes + 16 * (2 * D)>(delta, p1, o, off);
     }
     __syncthreads();  // every wave is done with the stage buffers before the next tile
 
     // ---- epilogue: O / l and LSE = (m c + log2 l) ln 2
     const float l_tot = pair_sum(l_run);
-    const bool empty = (m_run == kNegInf) || !(l_tot > 0.0f);
-    const float inv = empty ? 0.0f : rcp_fast(l_tot);
+    const float l_o = pair_sum(l_bf);
+    const bool empty = (m_run == kNegInf) || !(l_tot > 0.0f) || !(l_o > 0.0f);
+    const float inv = empty ? 0.0f : rcp_fast(l_o);
     if (row_ok) {
       uint16_t* ob = p.o + (int64_t)tile.b * p.o_bs + (q_start + tok) * p.o_ss + (int64_t)head * p.o_hs;
 #pragma unroll
@@ -528,7 +781,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_paged_kernel(FaParams p) {
   const float c = SOFTCAP ? 1.0f : p.scale_log2;
 
   LaneOffsets<D> off;
-  off.init(lane);
+  off.init(lane, lds_addr(smem));
   const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
   const int dma_pc = lane % G::kChunksPerRow;
   const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
@@ -624,34 +877,36 @@ __global__ __launch_bounds__(kThreads, 1) void fa_paged_kernel(FaParams p) {
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  float m_run = kNegInf, l_run = 0.0f;
+  float m_run = kNegInf, l_run = 0.0f, l_bf = 0.0f;
 
   if (nst > 0) issue(st_first, 0);
   for (int i = 0; i < nst; ++i) {
     const int buf = i & 1;
     const int n0 = st_first + i * NK;
     wait_vmcnt<0>();
-    __syncthreads();
+    stage_barrier();
     if (i + 1 < nst) issue(n0 + NK, buf ^ 1);
-    const char* lk = smem + buf * kStage;
-    const char* lv = lk + G::kTensorBytes;
-    f32x16 s = qk_block<D>(lk, wave, qreg, off);
+    // this wave's 32 keys: rows 32 wave .. 32 wave + 31 of the stage buffer
+    const uint32_t delta = buf * kStage + wave * 32 * (2 * D);
+    f32x16 s = qk_block<D, 0>(delta, qreg, off);
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
       const int key = n0 + 32 * wave + 8 * (a >> 2) + 4 * kg + (a & 3);
       float x = SOFTCAP ? softcap_log2(s[a], p.cap_in, p.cap_out) : s[a];
       s[a] = mask.visible(key) ? x : kNegInf;
     }
-    online_softmax<D>(s, m_run, l_run, o, c);
-    pv_chunk<D>(lv, 2 * wave, pack_p(s, 0), o, off);
-    pv_chunk<D>(lv, 2 * wave + 1, pack_p(s, 1), o, off);
+    bf16x8 p0, p1;
+    online_softmax<D>(s, m_run, l_run, l_bf, o, c, p0, p1);
+    pv_chunk<D, G::kTensorBytes>(delta, p0, o, off);
+    pv_chunk<D, G::kTensorBytes + 16 * (2 * D)>(delta, p1, o, off);
   }
   __syncthreads();
 
   // ---- merge the four waves' states through LDS
   float* mo = reinterpret_cast<float*>(smem);               // [4][32 cols][D]
-  float* ml = mo + 4 * 32 * D;                              // [4][32] m, then [4][32] l
+  float* ml = mo + 4 * 32 * D;  // [4][32] m, then [4][32] l (fp32), then [4][32] l (bf16 weights)
   const float l_w = pair_sum(l_run);
+  const float lb_w = pair_sum(l_bf);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -662,6 +917,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_paged_kernel(FaParams p) {
   if (kg == 0) {
     ml[wave * 32 + col] = m_run * c;   // log2 units
     ml[128 + wave * 32 + col] = l_w;
+    ml[256 + wave * 32 + col] = lb_w;
   }
   __syncthreads();
 
@@ -673,15 +929,16 @@ __global__ __launch_bounds__(kThreads, 1) void fa_paged_kernel(FaParams p) {
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[w * 32 + cc]);
-    float e[4], L = 0.0f;
+    float e[4], L = 0.0f, Lb = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float mw = ml[w * 32 + cc];
       e[w] = (mw == kNegInf) ? 0.0f : exp2_fast(mw - M);
       L += e[w] * ml[128 + w * 32 + cc];
+      Lb += e[w] * ml[256 + w * 32 + cc];
     }
-    const bool empty = (M == kNegInf) || !(L > 0.0f);
-    const float inv = empty ? 0.0f : rcp_fast(L);
+    const bool empty = (M == kNegInf) || !(L > 0.0f) || !(Lb > 0.0f);
+    const float inv = empty ? 0.0f : rcp_fast(Lb);
     float acc[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
