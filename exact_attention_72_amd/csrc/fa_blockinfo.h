@@ -82,6 +82,26 @@ FA_HD void fa_key_tiles(FaRowSpan s, int64_t Lk, int causal, int wl, int wr, int
   *n_hi = (int)(hi / bn) + 1;
 }
 
+// Key tiles [*f_lo, *f_hi) that every row of the span sees in full (class
+// FA_TILE_VISIBLE with no mask bit); empty as [0, 0).  A tile is full when its
+// first key is at or right of the span's tightest left bound and its last key
+// at or left of the tightest right bound.
+FA_HD void fa_full_tiles(FaRowSpan s, int64_t Lk, int causal, int wl, int wr, int bn, int* f_lo,
+                         int* f_hi) {
+  int64_t left = 0, right_key = Lk - 1, right;
+  if (wl >= 0) left = fa_max64(left, s.pos_hi - wl);
+  if (fa_right_bound(causal, wr, &right)) right_key = fa_min64(right_key, s.pos_lo + right);
+  const int64_t lo = (left + bn - 1) / bn;
+  const int64_t hi = right_key + 1 > 0 ? (right_key + 1) / bn : 0;
+  if (hi <= lo) {
+    *f_lo = 0;
+    *f_hi = 0;
+    return;
+  }
+  *f_lo = (int)lo;
+  *f_hi = (int)hi;
+}
+
 // Class bits of key tile n (keys [n*bn, n*bn + bn)) for the span.
 FA_HD int fa_tile_class(FaRowSpan s, int64_t Lk, int causal, int wl, int wr, int bn, int n) {
   int64_t t0 = (int64_t)n * bn, t1 = t0 + bn - 1, lo, hi, right;

@@ -142,25 +142,25 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((const FA_LDS char*)p);
 }
 
-// Per-lane LDS byte addresses of the MFMA operands within a stage buffer at
-// LDS address base, fixed for the whole kernel.
+// Per-lane LDS byte addresses of the MFMA operands within a stage buffer,
+// fixed for the whole kernel.  Both swizzles only flip address bits below the
+// row size, so the address of K chunk pair kk is k0 ^ (kk << 5) and that of V
+// d-block db is v0 ^ (db << 6); two registers instead of one per operand.
 template <int D>
 struct LaneOffsets {
-  uint32_t k[D / 16];  // K row (lane % 32), chunk (2 kk + kg)
-  uint32_t v[D / 32];  // V transposed-read address of d-block db for keys 4 kg + (j >> 2)
-  __device__ __forceinline__ void init(int lane, uint32_t base) {
+  uint32_t k0;  // K row (lane % 32), chunk kg (kk = 0)
+  uint32_t v0;  // V transposed-read address for keys 4 kg + (j >> 2), d-block 0
+  __device__ __forceinline__ void init(int lane, uint32_t base) { init(lane, base, base); }
+  __device__ __forceinline__ void init(int lane, uint32_t kbase, uint32_t base) {
     const int col = lane & 31, kg = lane >> 5;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) k[kk] = base + col * (2 * D) + (((2 * kk + kg) ^ k_swz<D>(col)) << 4);
+    k0 = kbase + col * (2 * D) + ((kg ^ k_swz<D>(col)) << 4);
     const int j = lane & 15, half = (lane >> 4) & 1;
     const int row = 4 * kg + (j >> 2);
-    const int sw = v_swz<D>(row);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int c16 = 4 * db + 2 * half + ((j & 3) >> 1);
-      v[db] = base + row * (2 * D) + ((c16 ^ sw) << 4) + (j & 1) * 8;
-    }
+    const int c16 = 2 * half + ((j & 3) >> 1);
+    v0 = base + row * (2 * D) + ((c16 ^ v_swz<D>(row)) << 4) + (j & 1) * 8;
   }
+  __device__ __forceinline__ uint32_t k(int kk) const { return k0 ^ (uint32_t)(kk << 5); }
+  __device__ __forceinline__ uint32_t v(int db) const { return v0 ^ (uint32_t)(db << 6); }
 };
 
 // LDS operand reads issued as inline assembly.  The compiler cannot tell that
@@ -188,7 +188,7 @@ template <int D, int OFF>
 __device__ __forceinline__ f32x16 qk_block(uint32_t delta, const bf16x8* qreg, const LaneOffsets<D>& off) {
   u32x4 a[D / 16];  // all operand reads in flight before the first product
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) a[kk] = ds_read_b128<OFF>(off.k[kk] + delta);
+  for (int kk = 0; kk < D / 16; ++kk) a[kk] = ds_read_b128<OFF>(off.k(kk) + delta);
   if constexpr (D == 128) {
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
@@ -211,8 +211,8 @@ __device__ __forceinline__ void pv_chunk(uint32_t delta, bf16x8 pb, f32x16* o, c
   u32x2 lo[D / 32], hi[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    lo[db] = ds_read_tr16<OFF>(off.v[db] + delta);
-    hi[db] = ds_read_tr16<OFF + 8 * (2 * D)>(off.v[db] + delta);
+    lo[db] = ds_read_tr16<OFF>(off.v(db) + delta);
+    hi[db] = ds_read_tr16<OFF + 8 * (2 * D)>(off.v(db) + delta);
   }
   if constexpr (D == 128) {
     asm volatile("s_waitcnt lgkmcnt(0)"
@@ -234,15 +234,15 @@ __device__ __forceinline__ void pv_chunk(uint32_t delta, bf16x8 pb, f32x16* o, c
 template <int D, int OFF>
 __device__ __forceinline__ void read_k(uint32_t delta, const LaneOffsets<D>& off, u32x4 (&a)[D / 16]) {
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) a[kk] = ds_read_b128<OFF>(off.k[kk] + delta);
+  for (int kk = 0; kk < D / 16; ++kk) a[kk] = ds_read_b128<OFF>(off.k(kk) + delta);
 }
 template <int D, int OFF>
 __device__ __forceinline__ void read_v(uint32_t delta, const LaneOffsets<D>& off, u32x2 (&lo)[D / 32],
                                        u32x2 (&hi)[D / 32]) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    lo[db] = ds_read_tr16<OFF>(off.v[db] + delta);
-    hi[db] = ds_read_tr16<OFF + 8 * (2 * D)>(off.v[db] + delta);
+    lo[db] = ds_read_tr16<OFF>(off.v(db) + delta);
+    hi[db] = ds_read_tr16<OFF + 8 * (2 * D)>(off.v(db) + delta);
   }
 }
 // Wait until at most N LDS operations are outstanding; the listed registers
@@ -283,6 +283,25 @@ __device__ __forceinline__ void pv_mma(const u32x2 (&lo)[D / 32], const u32x2 (&
     o[db] = mfma32(__builtin_bit_cast(bf16x8, w), pb, o[db]);
   }
 }
+
+// O^T += V^T P^T product and exponential issued as inline assembly, so that
+// the P V phase of the prefill pipeline keeps the order written: one product,
+// then the exponentials that fill its 32 cycles.  The compiler does not see
+// these as a matrix product, so the asm statement pads the hazard itself: two
+// wait states after a VALU write of the operands (the A operand may be
+// assembled by moves just before).  Readers of the accumulators wait for the
+// last product explicitly (mfma_drain).
+__device__ __forceinline__ void pv_mfma_asm(f32x16& acc, u32x4 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ float exp2_asm(float x) {
+  float r;
+  asm volatile("v_exp_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+// Wait states for a VALU access to the accumulators of the last product issued
+// by pv_mfma_asm (an 8-pass XDL op).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
 
 // Softcap transform into the log2 domain: c * tanh(scale * s / c) * log2(e),
 // tanh(y) = 1 - 2 / (exp(2y) + 1).
@@ -419,6 +438,55 @@ __device__ __forceinline__ void block_probs(const f32x16& s, float m_run, float 
   }
 }
 
+// The softmax of a block split in two for the prefill pipeline: the
+// exponentials (relative to the reference) run beside the P V products of the
+// previous block, their sums and the bf16 MFMA operands beside the S products
+// of the next block.
+//
+// Reference decision for a block with maximum mx: returns true when the
+// reference moves (to max(m_run, mx)); then alpha rescales what was
+// accumulated relative to the old reference.  m_run is updated here, the
+// rescale itself is applied by the caller once the P V products in flight are
+// done.
+__device__ __forceinline__ bool move_reference(float mx, float& m_run, float c, float& alpha) {
+  const float m_cand = fmaxf(m_run, mx);
+  alpha = 1.0f;
+  if (__any((m_cand - m_run) * c > kRescaleLog2)) {
+    // a row that has seen no visible key keeps m = -inf; use 0 as the offset so
+    // that exp2(-inf - offset) = 0 instead of NaN ("Attention kernels...", section 7.3)
+    const float m_use = (m_cand == kNegInf) ? 0.0f : m_cand;
+    alpha = exp2_fast((m_run - m_use) * c);
+    m_run = m_cand;
+    return true;
+  }
+  return false;
+}
+// -m c for the exponentials (0 while the row has seen no visible key).
+__device__ __forceinline__ float neg_ref(float m_run, float c) { return (m_run == kNegInf) ? 0.0f : -m_run * c; }
+// Sums of the exponentials x into both row sums, and x as two bf16 operands.
+__device__ __forceinline__ void block_sums(const f32x16& x, float& l_run, float& l_bf, bf16x8& p0, bf16x8& p1) {
+  float r0 = (x[0] + x[1]) + (x[2] + x[3]);
+  float r1 = (x[4] + x[5]) + (x[6] + x[7]);
+  float r2 = (x[8] + x[9]) + (x[10] + x[11]);
+  float r3 = (x[12] + x[13]) + (x[14] + x[15]);
+  l_run += (r0 + r1) + (r2 + r3);
+  f32x8 x0, x1;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    x0[a] = x[a];
+    x1[a] = x[a + 8];
+  }
+  p0 = __builtin_convertvector(x0, bf16x8);
+  p1 = __builtin_convertvector(x1, bf16x8);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    l_bf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * a], p0[2 * a + 1]}, one, l_bf, false);
+    l_bf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * a], p1[2 * a + 1]}, one, l_bf, false);
+  }
+}
+
 // ------------------------------------------------------------------ tile scheduling
 // Linear tile index -> tile, longest first (row blocks nearer the end of a
 // sequence see more keys under a causal mask, so they go first).  Round r of a
@@ -506,6 +574,19 @@ __device__ __forceinline__ bool dense_tile(const FaParams& p, int64_t t, TileId*
   return true;
 }
 
+// s_waitcnt vmcnt(n * PER) for a wave-uniform n in [0, 5].
+template <int PER>
+__device__ __forceinline__ void wait_vmcnt_blocks(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER>(); break;
+    case 2: wait_vmcnt<2 * PER>(); break;
+    case 3: wait_vmcnt<3 * PER>(); break;
+    case 4: wait_vmcnt<4 * PER>(); break;
+    default: wait_vmcnt<5 * PER>(); break;
+  }
+}
+
 // ------------------------------------------------------------------ prefill kernel
 // Key blocks of 32 stream through a ring of four LDS stage buffers, two blocks
 // ahead of use.  Iteration i (one barrier) issues the DMA of block i + 3,
@@ -515,10 +596,12 @@ __device__ __forceinline__ bool dense_tile(const FaParams& p, int64_t t, TileId*
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   constexpr int BN = FA_BLOCK_N;  // 32 keys per block
-  constexpr int NBUF = 4;
+  constexpr int NBUF = 5;
   using G = DmaGeom<D, BN>;
-  constexpr int kStage = 2 * G::kTensorBytes;  // K then V
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kStage];
+  constexpr int T = G::kTensorBytes;  // one tensor of one block
+  static_assert(NBUF * T <= 65536, "stage offsets must fit the LDS immediate offset");
+  // K stages in the lower half, V stages in the upper half
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * T];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -528,7 +611,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   const float c = SOFTCAP ? 1.0f : p.scale_log2;
 
   LaneOffsets<D> off;
-  off.init(lane, lds_addr(smem));
+  off.init(lane, lds_addr(smem), lds_addr(smem) + NBUF * T);
   // DMA geometry of this lane: stage row and the source chunk for K and V
   const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
   const int dma_pc = lane % G::kChunksPerRow;
@@ -609,7 +692,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     const int64_t k_step = (int64_t)G::kRowStep * p.k_ss, v_step = (int64_t)G::kRowStep * p.v_ss;
     // block i of this tile (key block n_lo + i) goes to buffer i % NBUF
     auto issue = [&](int i) {
-      char* dst = smem + (i % NBUF) * kStage + wave * 1024;
+      char* dst = smem + (i % NBUF) * T + wave * 1024;
       const int n0 = (n_lo + i) * BN;
       if (n0 + BN <= Lk) {
         const uint16_t* kq = klane + (int64_t)n0 * p.k_ss;
@@ -617,7 +700,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
 #pragma unroll
         for (int j = 0; j < G::kInstPerWave; ++j) {
           dma16(kq + j * k_step, dst + j * 4096);
-          dma16(vq + j * v_step, dst + G::kTensorBytes + j * 4096);
+          dma16(vq + j * v_step, dst + NBUF * T + j * 4096);
         }
       } else {
 #pragma unroll
@@ -625,7 +708,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
           int key = n0 + dma_row + j * G::kRowStep;
           key = key < Lk ? key : Lk - 1;
           dma16(kbase + (int64_t)key * p.k_ss + k_src, dst + j * 4096);
-          dma16(vbase + (int64_t)key * p.v_ss + v_src, dst + G::kTensorBytes + j * 4096);
+          dma16(vbase + (int64_t)key * p.v_ss + v_src, dst + NBUF * T + j * 4096);
         }
       }
     };
@@ -638,10 +721,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
 
     // Element mask of block i (key block n_lo + i), applied in place.
     auto apply_mask = [&](f32x16& sv, int i) {
-      const int n = n_lo + i;
+      int base = (n_lo + i) * BN + 4 * kg;
+      // keep the per-element key offsets inside this (rarely taken) path rather
+      // than as sixteen loop-invariant registers
+      asm volatile("" : "+v"(base));
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
-        const int key = n * BN + 8 * (a >> 2) + 4 * kg + (a & 3);
+        const int key = base + 8 * (a >> 2) + (a & 3);
         sv[a] = mask.visible(key) ? sv[a] : kNegInf;
       }
     };
@@ -653,80 +739,106 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     };
     auto is_masked = [&](int i) { return n_lo + i < n_full_lo || n_lo + i >= n_full_hi; };
 
-    f32x16 s_cur = {};
+    // xs: exponentials of the current block relative to m_run, whose sums and
+    // bf16 operands are formed at the start of the next step
+    f32x16 xs = {};
+    auto exps = [&](const f32x16& sv, float nmc, int a0, int a1) {
+#pragma unroll
+      for (int a = a0; a < a1; ++a) xs[a] = exp2_fast(__builtin_fmaf(sv[a], c, nmc));
+    };
     if (nb > 0) {
-      issue(0);
-      if (nb > 1) issue(1);
-      if (nb > 2) issue(2);
-      // block 0 landed: at most the DMAs of blocks 1 and 2 may still be in flight
-      if (nb > 2) wait_vmcnt<2 * kDmaPerBlock>();
-      else if (nb > 1) wait_vmcnt<kDmaPerBlock>();
-      else wait_vmcnt<0>();
+      for (int j = 0; j < NBUF - 1 && j < nb; ++j) issue(j);
+      // block 0 landed: the DMAs of the blocks after it may still be in flight
+      wait_vmcnt_blocks<kDmaPerBlock>(min(NBUF - 2, nb - 1));
       stage_barrier();
-      s_cur = qk_block<D, 0>(0u, qreg, off);
-      transform(s_cur);
-      if (is_masked(0)) apply_mask(s_cur, 0);
-      update_reference<D>(block_max(s_cur), m_run, l_run, l_bf, o, c);
+      f32x16 s0 = qk_block<D, 0>(0u, qreg, off);
+      transform(s0);
+      if (is_masked(0)) apply_mask(s0, 0);
+      float alpha;
+      move_reference(block_max(s0), m_run, c, alpha);  // nothing accumulated yet
+      exps(s0, neg_ref(m_run, c), 0, 16);
     }
 
-    // Pipeline step for block i (buffer B = i % NBUF) when block i + 1 exists.
-    // Region A: S^T of block i + 1 (MFMA) beside the probabilities of block i
-    // (VALU); region B: O^T += V^T P^T of block i (MFMA) beside the score
-    // transform and maximum of block i + 1 (VALU).  Neither region branches, so
-    // the scheduler can interleave the two kinds of work.  Blocks cut by a mask
-    // boundary (a few per tile) redo the maximum after the mask, and the rare move
-    // of the reference maximum follows.
+    // Pipeline step for block i (stage B = i % NBUF) when block i + 1 exists.
+    // The sums and bf16 operands of block i cover the latency of the K reads of
+    // block i + 1; then S^T of block i + 1 (MFMA); its mask, maximum and
+    // reference decision; then O^T += V^T P^T of block i, one MFMA at a time
+    // beside two exponentials of block i + 1 (the fences keep that order).  A
+    // move of the reference rescales O and the sums after the products.
     auto step = [&](auto bufc, int i) {
       constexpr int B = decltype(bufc)::value;
       constexpr int BN1 = (B + 1) % NBUF;
-      constexpr int kV = B * kStage + G::kTensorBytes;
-      // block i + 1 landed (block i + 2 may still be in flight); everyone is done
-      // with block i - 1, whose buffer the DMA of block i + 3 reuses
-      if (i + 2 < nb) wait_vmcnt<kDmaPerBlock>();
-      else wait_vmcnt<0>();
+      constexpr int kV = B * T;  // V stage of block i
+      // block i + 1 landed (later blocks may still be in flight); everyone is done
+      // with block i - 1, whose stages the DMA of block i + NBUF - 1 reuses
+      wait_vmcnt_blocks<kDmaPerBlock>(min(i + NBUF - 2, nb - 1) - (i + 1));
       stage_barrier();
-      if (i + 3 < nb) issue(i + 3);
-      // K of block i + 1 first: its latency hides under the softmax of block i
+      if (i + NBUF - 1 < nb) issue(i + NBUF - 1);
       u32x4 ka[D / 16];
-      read_k<D, BN1 * kStage>(0u, off, ka);
-      __builtin_amdgcn_sched_barrier(0);
+      read_k<D, BN1 * T>(0u, off, ka);
+      // the sums of block i run while the K reads are in flight: the empty asm
+      // statements (ordered with the reads and waits) pin them there
+      asm volatile("" : "+v"(xs));
       bf16x8 p0, p1;
-      block_probs(s_cur, m_run, c, l_run, l_bf, p0, p1);
+      block_sums(xs, l_run, l_bf, p0, p1);
+      asm volatile("" : "+v"(p0), "+v"(p1), "+v"(l_run), "+v"(l_bf));
       u32x2 lo0[D / 32], hi0[D / 32], lo1[D / 32], hi1[D / 32];
       read_v<D, kV>(0u, off, lo0, hi0);
       lgkm_wait<2 * (D / 32)>(ka);  // only the V reads just issued may be outstanding
       f32x16 s_next = qk_mma<D>(ka, qreg);
       read_v<D, kV + 16 * (2 * D)>(0u, off, lo1, hi1);
       transform(s_next);
-      float mx = block_max(s_next);
+      if (is_masked(i + 1)) apply_mask(s_next, i + 1);
+      float alpha;
+      const bool moved = move_reference(block_max(s_next), m_run, c, alpha);
+      const float nmc = neg_ref(m_run, c);
+      // P V of block i, each product followed by two exponentials of block i + 1
+      f32x16 t;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) t[a] = __builtin_fmaf(s_next[a], c, nmc);
+      constexpr int kPer = 16 / (2 * (D / 32));  // exponentials per product
       lgkm_wait<2 * (D / 32)>(lo0, hi0);
-      pv_mma<D>(lo0, hi0, p0, o);
-      lgkm_wait<0>(lo1, hi1);
-      pv_mma<D>(lo1, hi1, p1, o);
-      if (is_masked(i + 1)) {
-        apply_mask(s_next, i + 1);
-        mx = block_max(s_next);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        pv_mfma_asm(o[db], u32x4{lo0[db].x, lo0[db].y, hi0[db].x, hi0[db].y}, p0);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) xs[db * kPer + e] = exp2_asm(t[db * kPer + e]);
       }
-      update_reference<D>(mx, m_run, l_run, l_bf, o, c);
-      s_cur = s_next;
+      lgkm_wait<0>(lo1, hi1);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        pv_mfma_asm(o[db], u32x4{lo1[db].x, lo1[db].y, hi1[db].x, hi1[db].y}, p1);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) xs[8 + db * kPer + e] = exp2_asm(t[8 + db * kPer + e]);
+      }
+      if (moved) {
+        mfma_drain();
+        l_run *= alpha;
+        l_bf *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      }
     };
     int i = 0;
+    static_assert(NBUF == 5, "the unrolled loop below walks five stages");
     for (; i + NBUF <= nb - 1; i += NBUF) {
       step(std::integral_constant<int, 0>{}, i);
       step(std::integral_constant<int, 1>{}, i + 1);
       step(std::integral_constant<int, 2>{}, i + 2);
       step(std::integral_constant<int, 3>{}, i + 3);
+      step(std::integral_constant<int, 4>{}, i + 4);
     }
     if (i + 1 <= nb - 1) step(std::integral_constant<int, 0>{}, i), ++i;
     if (i + 1 <= nb - 1) step(std::integral_constant<int, 1>{}, i), ++i;
     if (i + 1 <= nb - 1) step(std::integral_constant<int, 2>{}, i), ++i;
-    // last block (i == nb - 1, buffer i % NBUF): probabilities and P V only
+    if (i + 1 <= nb - 1) step(std::integral_constant<int, 3>{}, i), ++i;
+    // last block (i == nb - 1, stage i % NBUF): sums and P V only
     if (nb > 0) {
       bf16x8 p0, p1;
-      block_probs(s_cur, m_run, c, l_run, l_bf, p0, p1);
-      const uint32_t delta = (uint32_t)((i % NBUF) * kStage);
-      pv_chunk<D, G::kTensorBytes>(delta, p0, o, off);
-      pv_chunk<D, G::kTensorBytes + 16 * (2 * D)>(delta, p1, o, off);
+      block_sums(xs, l_run, l_bf, p0, p1);
+      const uint32_t delta = (uint32_t)((i % NBUF) * T);
+      pv_chunk<D, 0>(delta, p0, o, off);
+      pv_chunk<D, 16 * (2 * D)>(delta, p1, o, off);
     }
     __syncthreads();  // every wave is done with the stage buffers before the next tile
 

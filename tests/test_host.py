@@ -167,3 +167,52 @@ def test_combine_rejects_invalid_arguments():
     assert L.fa_combine(FAKE, FAKE, 0, 10, 128, FAKE, 128, None, None) == FA_ERR_INVALID_ARG
     assert L.fa_combine(FAKE, FAKE, 2, 10, 96, FAKE, 128, None, None) == FA_ERR_UNSUPPORTED
     assert L.fa_combine(FAKE, FAKE, 2, 10, 128, FAKE, 64, None, None) == FA_ERR_INVALID_ARG
+
+
+FULL_TILES_CHECK = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include "fa_blockinfo.h"
+int main(void) {
+  unsigned x = 12345u;
+  long bad = 0, cases = 0;
+  for (int it = 0; it < 200000; ++it) {
+    x = x * 1103515245u + 12345u; int Lk = 1 + (x >> 8) % 700;
+    x = x * 1103515245u + 12345u; int pos_lo = (int)((x >> 8) % 900) - 200;
+    x = x * 1103515245u + 12345u; int width = (x >> 8) % 64;
+    x = x * 1103515245u + 12345u; int causal = (x >> 8) & 1;
+    x = x * 1103515245u + 12345u; int wl = (int)((x >> 8) % 300) - 100; if (wl < 0) wl = -1;
+    x = x * 1103515245u + 12345u; int wr = (int)((x >> 8) % 300) - 100; if (wr < 0) wr = -1;
+    x = x * 1103515245u + 12345u; int bn = ((x >> 8) & 1) ? 32 : 16;
+    FaRowSpan s; s.pos_lo = pos_lo; s.pos_hi = pos_lo + width;
+    int f_lo, f_hi;
+    fa_full_tiles(s, Lk, causal, wl, wr, bn, &f_lo, &f_hi);
+    for (int n = 0; n * bn < Lk + bn; ++n) {
+      int full = fa_tile_class(s, Lk, causal, wl, wr, bn, n) == FA_TILE_VISIBLE;
+      int in = n >= f_lo && n < f_hi;
+      cases++;
+      if (full != in) bad++;
+    }
+  }
+  printf("%ld %ld\n", bad, cases);
+  return bad != 0;
+}
+"""
+
+
+def test_full_tile_range_matches_tile_classes(tmp_path):
+    """The closed-form range of unmasked key tiles that the prefill kernel uses
+    per wave agrees with the tile classifier on random spans, windows and
+    sequence ends (the classifier itself is pinned to the pages' figures above)."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("no host C++ compiler")
+    src = tmp_path / "full_tiles.cpp"
+    src.write_text(FULL_TILES_CHECK)
+    exe = tmp_path / "full_tiles"
+    inc = os.path.join(ROOT, "exact_attention_72_amd", "csrc")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", inc, str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    bad, cases = map(int, r.stdout.split())
+    assert cases > 1_000_000 and bad == 0, r.stdout
