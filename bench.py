@@ -100,7 +100,7 @@ def cpu_baseline(W, t, c, target_s=15.0):
         dt = time.perf_counter() - t0
         return dt, keys * 4 * d, n
     dt, fl, n = run(threads * 8)
-    n2 = int(max(threads * 8, min(200000, n * target_s / max(dt, 1e-3))))
+    n2 = int(max(threads * 8, min(2000000, n * target_s / max(dt, 1e-3))))
     dt, fl, n = run(n2)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} random query rows of the batch-4 x 16-head N=4096 d=128 causal "
@@ -143,12 +143,12 @@ def bench_decode(api, W, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
+                    help="first run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the attention forward here has no multi-GPU path "

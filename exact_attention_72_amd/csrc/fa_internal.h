@@ -62,5 +62,5 @@ hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t stream
 // Tile geometry of the prefill kernel.
 constexpr int FA_BLOCK_M = 128;     // query rows per workgroup tile (4 waves x 32)
 constexpr int FA_BLOCK_N = 32;      // keys per K/V block (one LDS stage)
-constexpr int FA_PAGED_STAGE = 128; // keys per stage in the paged kernel (4 waves x 32)
+constexpr int FA_PAGED_STAGE = 64;  // keys per stage in the paged kernel (4 waves x 16)
 constexpr int FA_PAGED_MAX_ROWS = 32;

@@ -132,6 +132,15 @@ struct DmaGeom {
   static_assert(kInstPerWave >= 1, "stage too small for four waves");
 };
 
+// Scalar load of one 32-bit value at a wave-uniform address.  A vector load
+// would be waited for with vmcnt(0), which also waits for every LDS-DMA load
+// in flight; this waits only for the scalar (and LDS) counter.
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* ptr) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
 __device__ __forceinline__ void dma16(const uint16_t* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (FA_LDS void*)lds_dst, 16, 0, 0);
 }
@@ -151,8 +160,9 @@ struct LaneOffsets {
   uint32_t k0;  // K row (lane % 32), chunk kg (kk = 0)
   uint32_t v0;  // V transposed-read address for keys 4 kg + (j >> 2), d-block 0
   __device__ __forceinline__ void init(int lane, uint32_t base) { init(lane, base, base); }
-  __device__ __forceinline__ void init(int lane, uint32_t kbase, uint32_t base) {
-    const int col = lane & 31, kg = lane >> 5;
+  // krows: K rows per operand (32, or 16 with lanes 16..31 repeating rows 0..15)
+  __device__ __forceinline__ void init(int lane, uint32_t kbase, uint32_t base, int krows = 32) {
+    const int col = lane & (krows - 1), kg = lane >> 5;
     k0 = kbase + col * (2 * D) + ((kg ^ k_swz<D>(col)) << 4);
     const int j = lane & 15, half = (lane >> 4) & 1;
     const int row = 4 * kg + (j >> 2);
@@ -873,17 +883,26 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
 // ------------------------------------------------------------------ paged split-KV kernel
 // One workgroup per (sequence b, KV head, split).  The packed query rows
 // (seqlen_q tokens x g heads, at most 32) are the same for all four waves; each
-// 128-key stage is split 32 keys per wave, and the waves' partial states are
+// 64-key stage is split 16 keys per wave, and the waves' partial states are
 // merged through LDS at the end ("Attention kernels...", section 6.3: partial
-// states combine with the same rescale as the tiles).  When the page size is a
+// states combine with the same rescale as the tiles).  Decode is bound by the
+// K/V stream: two stages per workgroup (64 KiB) let two workgroups share a CU,
+// so that one computes while the other's loads are in flight (measured faster
+// than one workgroup with a deeper ring of the same total size).  When the page size is a
 // multiple of the stage, a stage lies in one page and its physical page is one
 // scalar block-table read; otherwise every row looks its page up.
 template <int D, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 1) void fa_paged_kernel(FaParams p) {
+__global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
   constexpr int NK = FA_PAGED_STAGE;
+  constexpr int NS = 2;  // stages in the ring
   using G = DmaGeom<D, NK>;
   constexpr int kStage = 2 * G::kTensorBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+  static_assert(NK == 4 * 16, "four waves of 16 keys per stage");
+  // the stage ring, reused after the loop for the merge of the four waves'
+  // states: O [4][32][D] fp32, then m, l and l (bf16 weights) [3][4][32]
+  constexpr int kMerge = 4 * 32 * D * 4 + 3 * 4 * 32 * 4;
+  constexpr int kSmem = NS * kStage > kMerge ? NS * kStage : kMerge;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -892,8 +911,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa_paged_kernel(FaParams p) {
   const int kg = lane >> 5;
   const float c = SOFTCAP ? 1.0f : p.scale_log2;
 
+  // a wave's S^T operand covers 16 keys: lanes 16..31 repeat rows 0..15, and
+  // the repeated rows (accumulator slots 8..15) are dropped below
   LaneOffsets<D> off;
-  off.init(lane, lds_addr(smem));
+  off.init(lane, lds_addr(smem), lds_addr(smem), 16);
   const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
   const int dma_pc = lane % G::kChunksPerRow;
   const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
@@ -954,24 +975,25 @@ __global__ __launch_bounds__(kThreads, 1) void fa_paged_kernel(FaParams p) {
   const uint16_t* vpool = p.v + (int64_t)kvh * p.v_hs;
   const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks;
   const bool page_aligned = (p.page % NK) == 0;
+  // rows past the last key read the last key (finite data the mask drops)
+  const int last = kend > 0 ? kend - 1 : 0;
+  const int64_t phys_last = (page_aligned && nst > 0)
+                                ? scalar_load_i32(bt + __builtin_amdgcn_readfirstlane(last / p.page)) : 0;
+  const int slot_last = last % p.page;
   auto issue = [&](int n0, int buf) {
     char* dst = smem + buf * kStage + wave * 1024;
     if (page_aligned) {
       // the whole stage is in one page: one scalar table read
-      const int64_t phys = bt[n0 / p.page];
+      const int64_t phys = scalar_load_i32(bt + __builtin_amdgcn_readfirstlane(n0 / p.page));
       const int slot0 = n0 % p.page;
-      const uint16_t* kp = kpool + phys * p.k_bs;
-      const uint16_t* vp = vpool + phys * p.v_bs;
 #pragma unroll
       for (int i = 0; i < G::kInstPerWave; ++i) {
-        int r = dma_row + i * G::kRowStep;
-        int key = n0 + r;
-        int slot = (key < kend ? slot0 + r : (kend - 1) % p.page);
-        const int64_t ph = key < kend ? phys : (int64_t)bt[(kend - 1) / p.page];
-        const uint16_t* kq = key < kend ? kp : kpool + ph * p.k_bs;
-        const uint16_t* vq = key < kend ? vp : vpool + ph * p.v_bs;
-        dma16(kq + (int64_t)slot * p.k_ss + k_src, dst + i * 4096);
-        dma16(vq + (int64_t)slot * p.v_ss + v_src, dst + G::kTensorBytes + i * 4096);
+        const int r = dma_row + i * G::kRowStep;
+        const bool live = n0 + r < kend;
+        const int slot = live ? slot0 + r : slot_last;
+        const int64_t ph = live ? phys : phys_last;
+        dma16(kpool + ph * p.k_bs + (int64_t)slot * p.k_ss + k_src, dst + i * 4096);
+        dma16(vpool + ph * p.v_bs + (int64_t)slot * p.v_ss + v_src, dst + G::kTensorBytes + i * 4096);
       }
     } else {
 #pragma unroll
@@ -991,26 +1013,28 @@ __global__ __launch_bounds__(kThreads, 1) void fa_paged_kernel(FaParams p) {
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.0f, l_bf = 0.0f;
 
-  if (nst > 0) issue(st_first, 0);
+  for (int j = 0; j < NS - 1 && j < nst; ++j) issue(st_first + j * NK, j);
+  constexpr int kDmaPerStage = 2 * G::kInstPerWave;
   for (int i = 0; i < nst; ++i) {
-    const int buf = i & 1;
+    const int buf = i % NS;
     const int n0 = st_first + i * NK;
-    wait_vmcnt<0>();
+    // stage i landed (the stages after it may still be in flight); everyone is
+    // done with stage i - 1, whose buffer stage i + NS - 1 reuses
+    wait_vmcnt_blocks<kDmaPerStage>(min(NS - 2, nst - 1 - i));
     stage_barrier();
-    if (i + 1 < nst) issue(n0 + NK, buf ^ 1);
-    // this wave's 32 keys: rows 32 wave .. 32 wave + 31 of the stage buffer
-    const uint32_t delta = buf * kStage + wave * 32 * (2 * D);
+    if (i + NS - 1 < nst) issue(n0 + (NS - 1) * NK, (i + NS - 1) % NS);
+    // this wave's 16 keys: rows 16 wave .. 16 wave + 15 of the stage buffer
+    const uint32_t delta = buf * kStage + wave * 16 * (2 * D);
     f32x16 s = qk_block<D, 0>(delta, qreg, off);
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
-      const int key = n0 + 32 * wave + 8 * (a >> 2) + 4 * kg + (a & 3);
+      const int key = n0 + 16 * wave + 8 * ((a >> 2) & 1) + 4 * kg + (a & 3);
       float x = SOFTCAP ? softcap_log2(s[a], p.cap_in, p.cap_out) : s[a];
-      s[a] = mask.visible(key) ? x : kNegInf;
+      s[a] = (a < 8 && mask.visible(key)) ? x : kNegInf;
     }
     bf16x8 p0, p1;
     online_softmax<D>(s, m_run, l_run, l_bf, o, c, p0, p1);
     pv_chunk<D, G::kTensorBytes>(delta, p0, o, off);
-    pv_chunk<D, G::kTensorBytes + 16 * (2 * D)>(delta, p1, o, off);
   }
   __syncthreads();
 
