@@ -2,8 +2,11 @@
 
 A step is one forward pass of the dense causal prefill workload
 (batch 4, 16 heads, N = 4096, d = 128, bf16) through the C ABI.  The line also
-carries the paged split-KV decode measurement (64 sequences, 32/8 heads,
-d = 128, 256-token pages, num_splits in {1, 4, 16}) as a secondary figure.
+carries, as secondary figures, the paged split-KV decode measurement (64
+sequences, 32/8 heads, d = 128, 256-token pages, num_splits in {1, 4, 16}),
+the varlen GQA prefill (32 sequences of 64..8192 tokens, 32/4 heads, packed)
+and the long-context local attention with softcap (N = 32768, 32 heads,
+window 4096, softcap 30).
 
 Prints one JSON line:
   value        prefill TFLOP/s, FLOPs counted as 4 * B * H * N^2 * d * 1/2 (the
@@ -107,6 +110,59 @@ def cpu_baseline(W, t, c, target_s=15.0):
                       f"workload, fp64, {dt:.1f} s"}
 
 
+def bench_varlen(api, W, steps, warmup):
+    """Varlen GQA prefill: 32 sequences, lengths uniform [64, 8192], 32 Q / 4 KV heads packed,
+    causal.  FLOPs: 4 d Hq sum_b L_b (L_b + 1) / 2 (visible pairs only)."""
+    import torch
+    name = "varlen_gqa_32seq_64to8192_h32kv4_d128_causal"
+    c = W.WORKLOADS[name]
+    t = W.varlen(c["seed"], c["nseq"], c["lo"], c["hi"], c["Hq"], c["Hkv"], c["d"], device="cuda")
+    cu = t["cu_seqlens"].cuda()
+    L = t["lengths"].to(torch.float64)
+    flops = float(4 * c["d"] * c["Hq"] * (L * (L + 1) / 2).sum())
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((c["Hq"], t["q"].shape[0]), dtype=torch.float32, device="cuda")
+    fn = lambda: api.fa_fwd_varlen(t["q"], t["k"], t["v"], cu, cu, t["max_seqlen"], causal=True,  # noqa
+                                   pack_gqa=1, out=out, lse=lse)
+    wall, per = time_launches(fn, steps, warmup)
+    ms = sum(per) / len(per)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"metric": "varlen prefill TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
+            "kernel_ms": round(ms, 4), "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
+            "config": {"workload": name, "sequences": c["nseq"], "total_tokens": int(t["q"].shape[0]),
+                       "heads_q": c["Hq"], "heads_kv": c["Hkv"], "head_dim": c["d"], "pack_gqa": True,
+                       "causal": True, "flop_convention": "4*d*Hq*sum L(L+1)/2"}}
+
+
+def bench_local(api, W, steps, warmup):
+    """Long-context local attention with softcap: N = 32768, 32 heads, window (4096, 0),
+    softcap 30, inputs N(0,1) x 2.  FLOPs: 4 d H sum_i (min(i, 4096) + 1)."""
+    import torch
+    name = "local_softcap_n32768_h32_d128_w4096_cap30"
+    c = W.WORKLOADS[name]
+    B, N, H, d = c["B"], c["N"], c["Hq"], c["d"]
+    t = W.dense(c["seed"], B, N, H, c["Hkv"], d, mult=c["mult"], device="cuda")
+    wl = c["window"][0]
+    pairs = sum(min(i, wl) + 1 for i in range(N))
+    flops = 4.0 * d * B * H * pairs
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fn = lambda: api.fa_fwd(t["q"], t["k"], t["v"], causal=True, window=c["window"],  # noqa
+                            softcap=c["softcap"], out=out, lse=lse)
+    wall, per = time_launches(fn, steps, warmup)
+    ms = sum(per) / len(per)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"metric": "local softcap prefill TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
+            "kernel_ms": round(ms, 4), "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
+            "config": {"workload": name, "batch": B, "heads": H, "seq_len": N, "head_dim": d,
+                       "causal": True, "window": list(c["window"]), "softcap": c["softcap"],
+                       "flop_convention": "4*d*H*sum_i(min(i,4096)+1)"}}
+
+
 def bench_decode(api, W, steps, warmup):
     import torch
     c = W.WORKLOADS["paged_decode_b64_h32kv8_d128_page256"]
@@ -147,6 +203,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-local", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -193,10 +251,17 @@ def main():
                      "traffic": stored_traffic("fa_prefill_kernel"),
                      "kernel_ms": round(kern_ms, 4)},
     }
+    del t, out, lse
+    torch.cuda.empty_cache()
     if not args.no_decode:
-        del t, out, lse
-        torch.cuda.empty_cache()
         line["decode"] = bench_decode(api, W, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if not args.no_varlen:
+        line["varlen"] = bench_varlen(api, W, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if not args.no_local:
+        line["local_softcap"] = bench_local(api, W, max(5, args.steps // 5), max(3, args.warmup // 5))
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         tc = W.dense(c["seed"], B, N, H, c["Hkv"], d)
         line["cpu_baseline"] = cpu_baseline(W, tc, c)

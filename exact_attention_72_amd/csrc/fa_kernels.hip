@@ -606,7 +606,7 @@ __device__ __forceinline__ void wait_vmcnt_blocks(int n) {
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   constexpr int BN = FA_BLOCK_N;  // 32 keys per block
-  constexpr int NBUF = 5;
+  constexpr int NBUF = 3;  // measured best of 3, 4 and 5 stages
   using G = DmaGeom<D, BN>;
   constexpr int T = G::kTensorBytes;  // one tensor of one block
   static_assert(NBUF * T <= 65536, "stage offsets must fit the LDS immediate offset");
@@ -830,18 +830,20 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       }
     };
     int i = 0;
-    static_assert(NBUF == 5, "the unrolled loop below walks five stages");
+    static_assert(NBUF >= 3 && NBUF <= 5, "the unrolled loop below walks three to five stages");
     for (; i + NBUF <= nb - 1; i += NBUF) {
       step(std::integral_constant<int, 0>{}, i);
       step(std::integral_constant<int, 1>{}, i + 1);
       step(std::integral_constant<int, 2>{}, i + 2);
-      step(std::integral_constant<int, 3>{}, i + 3);
-      step(std::integral_constant<int, 4>{}, i + 4);
+      if constexpr (NBUF > 3) step(std::integral_constant<int, 3 % NBUF>{}, i + 3);
+      if constexpr (NBUF > 4) step(std::integral_constant<int, 4 % NBUF>{}, i + 4);
     }
     if (i + 1 <= nb - 1) step(std::integral_constant<int, 0>{}, i), ++i;
     if (i + 1 <= nb - 1) step(std::integral_constant<int, 1>{}, i), ++i;
-    if (i + 1 <= nb - 1) step(std::integral_constant<int, 2>{}, i), ++i;
-    if (i + 1 <= nb - 1) step(std::integral_constant<int, 3>{}, i), ++i;
+    if constexpr (NBUF > 3)
+      if (i + 1 <= nb - 1) step(std::integral_constant<int, 2 % NBUF>{}, i), ++i;
+    if constexpr (NBUF > 4)
+      if (i + 1 <= nb - 1) step(std::integral_constant<int, 3 % NBUF>{}, i), ++i;
     // last block (i == nb - 1, stage i % NBUF): sums and P V only
     if (nb > 0) {
       bf16x8 p0, p1;
