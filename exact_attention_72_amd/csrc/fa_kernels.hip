@@ -348,6 +348,7 @@ struct LaneMask {
 // same up to rounding, while the rescale of O (a multiply per accumulator) and
 // its exponential are skipped on most blocks.  The decision is wave-uniform.
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRescaleMax = 256.0f;  // 2^kRescaleLog2
 
 template <int D>
 __device__ __forceinline__ void online_softmax(f32x16& s, float& m_run, float& l_run, float& l_bf,
@@ -799,9 +800,17 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       read_v<D, kV + 16 * (2 * D)>(0u, off, lo1, hi1);
       transform(s_next);
       if (is_masked(i + 1)) apply_mask(s_next, i + 1);
-      float alpha;
-      const bool moved = move_reference(block_max(s_next), m_run, c, alpha);
-      const float nmc = neg_ref(m_run, c);
+      // Reference for the exponentials of block i + 1.  While some row of the
+      // wave has seen no visible key its reference must be set from this block's
+      // maximum first (rare: the first blocks of a tile).  Otherwise the
+      // exponentials use the current reference and are checked afterwards: a
+      // probability above 2^kRescaleLog2 means the maximum outgrew the reference,
+      // and the block is redone with the moved reference (the same decision as
+      // move_reference, taken off the path between the two products).
+      float alpha = 1.0f;
+      bool moved = false;
+      if (__any(m_run == kNegInf)) moved = move_reference(block_max(s_next), m_run, c, alpha);
+      float nmc = neg_ref(m_run, c);
       // P V of block i, each product followed by two exponentials of block i + 1
       f32x16 t;
 #pragma unroll
@@ -820,6 +829,20 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
         pv_mfma_asm(o[db], u32x4{lo1[db].x, lo1[db].y, hi1[db].x, hi1[db].y}, p1);
 #pragma unroll
         for (int e = 0; e < kPer; ++e) xs[8 + db * kPer + e] = exp2_asm(t[8 + db * kPer + e]);
+      }
+      float xm = fmaxf(fmaxf(xs[0], xs[1]), xs[2]);
+#pragma unroll
+      for (int a = 3; a < 15; a += 2) xm = fmaxf(fmaxf(xm, xs[a]), xs[a + 1]);
+      xm = fmaxf(xm, xs[15]);
+      if (__any(xm > kRescaleMax)) {
+        float a2;
+        if (move_reference(block_max(s_next), m_run, c, a2)) {
+          alpha *= a2;
+          moved = true;
+          nmc = neg_ref(m_run, c);
+#pragma unroll
+          for (int a = 0; a < 16; ++a) xs[a] = exp2_fast(__builtin_fmaf(s_next[a], c, nmc));
+        }
       }
       if (moved) {
         mfma_drain();
