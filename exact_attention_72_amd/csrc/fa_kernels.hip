@@ -316,10 +316,9 @@ __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\
 // Softcap transform into the log2 domain: c * tanh(scale * s / c) * log2(e),
 // tanh(y) = 1 - 2 / (exp(2y) + 1).
 __device__ __forceinline__ float softcap_log2(float s, float cap_in, float cap_out) {
-  float y = s * cap_in;
-  float t = exp2_fast(y * (2.0f * kLog2e));
-  float th = 1.0f - 2.0f * rcp_fast(t + 1.0f);
-  return th * cap_out;
+  // c tanh(y) log2(e) = c log2(e) - 2 c log2(e) / (exp(2y) + 1), y = scale s / c
+  const float t = exp2_fast(s * (cap_in * (2.0f * kLog2e)));
+  return __builtin_fmaf(-2.0f * cap_out, rcp_fast(t + 1.0f), cap_out);
 }
 
 // Per-lane view of the mask: this lane's query position and the bounds.
@@ -574,12 +573,24 @@ __device__ bool varlen_tile(const FaParams& p, int64_t t, int lane, TileId* out)
   return out->b >= 0;
 }
 
+// Dense tiles.  Without a left window, row blocks go longest first, level by
+// level over all (sequence, head group) pairs.  With a left window every row
+// block has about the same work, and the tiles running together should share
+// K/V: workgroup i runs on XCD i % 8, so XCD x takes the pairs x, x + 8, ...
+// one after the other, row blocks in order, and its concurrent tiles cover one
+// pair's neighbouring windows in that XCD's L2.
 __device__ __forceinline__ bool dense_tile(const FaParams& p, int64_t t, TileId* out) {
   if (t >= p.total_tiles) return false;
-  const int64_t per_level = (int64_t)p.B * p.hg_count;
-  const int level = (int)(t / per_level);
-  const int64_t bh = t % per_level;
-  out->mb = p.m_blocks - 1 - level;
+  const int64_t pairs = (int64_t)p.B * p.hg_count;
+  int64_t bh;
+  if (p.wl >= 0 && !p.persistent && (pairs & 7) == 0) {
+    const int64_t j = t >> 3;
+    out->mb = (int)(j % p.m_blocks);
+    bh = (j / p.m_blocks) * 8 + (t & 7);
+  } else {
+    out->mb = p.m_blocks - 1 - (int)(t / pairs);
+    bh = t % pairs;
+  }
   out->b = (int)(bh / p.hg_count);
   out->hg = (int)(bh % p.hg_count);
   return true;
@@ -798,8 +809,16 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       lgkm_wait<2 * (D / 32)>(ka);  // only the V reads just issued may be outstanding
       f32x16 s_next = qk_mma<D>(ka, qreg);
       read_v<D, kV + 16 * (2 * D)>(0u, off, lo1, hi1);
-      transform(s_next);
-      if (is_masked(i + 1)) apply_mask(s_next, i + 1);
+      // Softcapped scores of an unmasked block whose rows all have a reference
+      // are transformed inside the product loop below, beside the exponentials;
+      // otherwise (mask, or a row's first visible block) before it.
+      const bool masked = is_masked(i + 1);
+      const bool first = __any(m_run == kNegInf);
+      const bool late = SOFTCAP && !masked && !first;
+      if (!late) {
+        transform(s_next);
+        if (masked) apply_mask(s_next, i + 1);
+      }
       // Reference for the exponentials of block i + 1.  While some row of the
       // wave has seen no visible key its reference must be set from this block's
       // maximum first (rare: the first blocks of a tile).  Otherwise the
@@ -809,26 +828,27 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       // move_reference, taken off the path between the two products).
       float alpha = 1.0f;
       bool moved = false;
-      if (__any(m_run == kNegInf)) moved = move_reference(block_max(s_next), m_run, c, alpha);
+      if (first) moved = move_reference(block_max(s_next), m_run, c, alpha);
       float nmc = neg_ref(m_run, c);
-      // P V of block i, each product followed by two exponentials of block i + 1
-      f32x16 t;
-#pragma unroll
-      for (int a = 0; a < 16; ++a) t[a] = __builtin_fmaf(s_next[a], c, nmc);
+      // P V of block i, each product followed by the exponentials of block i + 1
       constexpr int kPer = 16 / (2 * (D / 32));  // exponentials per product
+      auto expo = [&](int a) {
+        if (late) s_next[a] = softcap_log2(s_next[a], p.cap_in, p.cap_out);
+        xs[a] = exp2_asm(__builtin_fmaf(s_next[a], c, nmc));
+      };
       lgkm_wait<2 * (D / 32)>(lo0, hi0);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         pv_mfma_asm(o[db], u32x4{lo0[db].x, lo0[db].y, hi0[db].x, hi0[db].y}, p0);
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) xs[db * kPer + e] = exp2_asm(t[db * kPer + e]);
+        for (int e = 0; e < kPer; ++e) expo(db * kPer + e);
       }
       lgkm_wait<0>(lo1, hi1);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         pv_mfma_asm(o[db], u32x4{lo1[db].x, lo1[db].y, hi1[db].x, hi1[db].y}, p1);
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) xs[8 + db * kPer + e] = exp2_asm(t[8 + db * kPer + e]);
+        for (int e = 0; e < kPer; ++e) expo(8 + db * kPer + e);
       }
       float xm = fmaxf(fmaxf(xs[0], xs[1]), xs[2]);
 #pragma unroll
