@@ -13,7 +13,8 @@ Prints one JSON line:
                pages' causal convention, "Attention kernels: FlashAttention and
                PagedAttention", section 8.3)
   roofline     achieved bf16 MFMA rate of the prefill kernel (FLOPs per launch /
-               average launch time from HIP events on the launch stream) against
+               mean launch time from HIP events recorded on the launch stream around the
+               timed back-to-back launches) against
                the 2.5 PFLOP/s dense bf16 peak; traffic from the committed
                rocprofv3 counter summary when it matches the current kernel source
   cpu_baseline the fp64 oracle timed on host threads on a bounded row sample of
@@ -60,22 +61,23 @@ def stored_traffic(kernel: str):
 
 
 def time_launches(fn, steps, warmup):
-    """Warm up, then time `steps` calls; per-call HIP events on the current stream."""
+    """Warm up, then time `steps` back-to-back calls between two HIP events recorded on the
+    current stream (the stream the library launches on).  Returns the wall time of the timed
+    region (s) and the mean time per call from the events (ms)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    e0.record()
+    for _ in range(steps):
         fn()
-        ends[i].record()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]   # ms
-    return wall, per
+    return wall, e0.elapsed_time(e1) / steps
 
 
 def prefill_flops(B, H, N, d, causal):
@@ -124,8 +126,7 @@ def bench_varlen(api, W, steps, warmup):
     lse = torch.empty((c["Hq"], t["q"].shape[0]), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd_varlen(t["q"], t["k"], t["v"], cu, cu, t["max_seqlen"], causal=True,  # noqa
                                    pack_gqa=1, out=out, lse=lse)
-    wall, per = time_launches(fn, steps, warmup)
-    ms = sum(per) / len(per)
+    wall, ms = time_launches(fn, steps, warmup)
     tf = flops / (ms * 1e-3) / 1e12
     return {"metric": "varlen prefill TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
             "kernel_ms": round(ms, 4), "flops": flops,
@@ -151,8 +152,7 @@ def bench_local(api, W, steps, warmup):
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd(t["q"], t["k"], t["v"], causal=True, window=c["window"],  # noqa
                             softcap=c["softcap"], out=out, lse=lse)
-    wall, per = time_launches(fn, steps, warmup)
-    ms = sum(per) / len(per)
+    wall, ms = time_launches(fn, steps, warmup)
     tf = flops / (ms * 1e-3) / 1e12
     return {"metric": "local softcap prefill TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
             "kernel_ms": round(ms, 4), "flops": flops,
@@ -179,8 +179,7 @@ def bench_decode(api, W, steps, warmup):
         fn = lambda: api.fa_fwd_kvcache_paged(t["q"], t["k_cache"], t["v_cache"], bt, sl,  # noqa
                                               num_splits=S, causal=True, out=out, lse=lse,
                                               workspace=ws)
-        wall, per = time_launches(fn, steps, warmup)
-        ms = sum(per) / len(per)
+        wall, ms = time_launches(fn, steps, warmup)
         res[S] = {"ms": ms, "kv_GBps": kv_bytes / (ms * 1e-3) / 1e9}
     best = max(res, key=lambda s: res[s]["kv_GBps"])
     return {"metric": "paged decode KV GB/s", "unit": "GB/s",
@@ -199,8 +198,8 @@ def bench_decode(api, W, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
@@ -233,10 +232,9 @@ def main():
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd(t["q"], t["k"], t["v"], causal=True, out=out, lse=lse)  # noqa
     torch.cuda.synchronize()
-    wall, per = time_launches(fn, args.steps, args.warmup)
+    wall, kern_ms = time_launches(fn, args.steps, args.warmup)
     flops = prefill_flops(B, H, N, d, True)
     ms_step = wall / args.steps * 1e3
-    kern_ms = sum(per) / len(per)
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     line = {
