@@ -21,7 +21,8 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
-EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_kvcache_workspace_size",
+EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_kvcache_num_splits",
+           "fa_kvcache_workspace_size",
            "fa_combine", "fa_tile_class", "fa_last_error", "fa_version")
 
 
@@ -57,6 +58,8 @@ def lib():
                                        S3, S3, S3, S3, P]
     L.fa_kvcache_workspace_size.argtypes = [I, I, I, I, I]
     L.fa_kvcache_workspace_size.restype = SZ
+    L.fa_kvcache_num_splits.argtypes = [I, I, I, I, I, I]
+    L.fa_kvcache_num_splits.restype = I
     L.fa_combine.argtypes = [P, P, I, I64, I, P, I64, P, P]
     L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
     L.fa_last_error.restype = ctypes.c_char_p
@@ -148,11 +151,19 @@ def fa_kvcache_workspace_size(batch, seqlen_q, heads_q, head_dim, num_splits):
     return int(lib().fa_kvcache_workspace_size(batch, seqlen_q, heads_q, head_dim, num_splits))
 
 
+def fa_kvcache_num_splits(batch, seqlen_q, heads_q, heads_kv, page_size, max_blocks_per_seq):
+    """The split count fa_fwd_kvcache_paged uses for num_splits=0."""
+    return int(lib().fa_kvcache_num_splits(batch, seqlen_q, heads_q, heads_kv, page_size,
+                                           max_blocks_per_seq))
+
+
 def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num_splits=1,
-                         softmax_scale=None, causal=True, window=None, softcap=0.0, out=None,
-                         lse=None, workspace=None, return_lse=True, stream=None):
+                         softmax_scale=None, causal=True, window=None, softcap=0.0, pack_gqa=-1,
+                         out=None, lse=None, workspace=None, return_lse=True, stream=None):
     """Paged-KV forward.  q [B, Nq, Hq, d]; caches [num_pages, page, Hkv, d];
-    block_table int32 [B, max_blocks]; cache_seqlens int32 [B] -> (out, lse [B, Hq, Nq])."""
+    block_table int32 [B, max_blocks]; cache_seqlens int32 [B] -> (out, lse [B, Hq, Nq]).
+    num_splits=0 picks the split count (fa_kvcache_num_splits); more than 32 packed
+    query rows per sequence (Nq * Hq / Hkv) run the prefill kernel over the cache."""
     _bf16_cuda(q, k_cache, v_cache)
     B, Nq, Hq, d = q.shape
     num_pages, page, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
@@ -166,11 +177,13 @@ def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num
     _bf16_cuda(out)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if num_splits == 0:
+        num_splits = fa_kvcache_num_splits(B, Nq, Hq, Hkv, page, block_table.shape[1])
     need = fa_kvcache_workspace_size(B, Nq, Hq, d, num_splits)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    o = _opts(softmax_scale, causal, window, softcap, 0)
+    o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
     _check(lib().fa_fwd_kvcache_paged(ctypes.byref(o), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                       _ptr(block_table), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
                                       B, Nq, Hq, Hkv, d, num_pages, page, block_table.shape[1],

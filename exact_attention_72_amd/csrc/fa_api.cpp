@@ -133,7 +133,7 @@ int fa_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   p.m_blocks = (int)((rows + FA_BLOCK_M - 1) / FA_BLOCK_M);
   p.total_tiles = (int64_t)p.m_blocks * batch * p.hg_count;
   p.persistent = 0;
-  hipError_t e = fa_launch_prefill(p, head_dim, false, pack, softcap, static_cast<hipStream_t>(stream));
+  hipError_t e = fa_launch_prefill(p, head_dim, false, false, pack, softcap, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return FA_OK;
 }
@@ -184,9 +184,26 @@ int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
   int64_t bound2 = ((int64_t)total_q * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M + batch;
   p.total_tiles = (bound < bound2 ? bound : bound2) * p.hg_count;
   p.persistent = 1;
-  hipError_t e = fa_launch_prefill(p, head_dim, true, pack, softcap, static_cast<hipStream_t>(stream));
+  hipError_t e = fa_launch_prefill(p, head_dim, true, false, pack, softcap, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "varlen launch");
   return FA_OK;
+}
+
+int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, int page_size,
+                          int max_blocks_per_seq) {
+  if (batch <= 0 || seqlen_q <= 0 || heads_q <= 0 || heads_kv <= 0 || heads_q % heads_kv != 0 || page_size <= 0 ||
+      max_blocks_per_seq <= 0)
+    return 1;
+  if ((int64_t)seqlen_q * (heads_q / heads_kv) > FA_PAGED_MAX_ROWS) return 1;  // prefill over the cache
+  // About eight workgroups per compute unit (two resident at a time, four
+  // rounds), so that sequences of unequal length still level out; each split
+  // keeps at least one page, and at most 64 splits.
+  const int64_t units = (int64_t)batch * heads_kv;
+  const int64_t target = 8 * (int64_t)fa_device_cus();
+  int64_t s = (target + units - 1) / units;
+  if (s > 64) s = 64;
+  if (s > max_blocks_per_seq) s = max_blocks_per_seq;
+  return s < 1 ? 1 : (int)s;
 }
 
 size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_dim, int num_splits) {
@@ -209,16 +226,25 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
     return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (batch <= 0 || seqlen_q <= 0 || num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0)
     return fail(FA_ERR_INVALID_ARG, "batch, seqlen_q, num_pages, page_size and max_blocks_per_seq must be positive");
-  if (num_splits < 1) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
   if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
     return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
   if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
       (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)))
     return rc;
   const int g = heads_q / heads_kv;
-  if ((int64_t)seqlen_q * g > FA_PAGED_MAX_ROWS)
-    return fail(FA_ERR_UNSUPPORTED, "seqlen_q * heads_q / heads_kv = %lld exceeds %d packed rows",
-                (long long)seqlen_q * g, FA_PAGED_MAX_ROWS);
+  if (num_splits == 0)
+    num_splits = fa_kvcache_num_splits(batch, seqlen_q, heads_q, heads_kv, page_size, max_blocks_per_seq);
+  // more packed query rows than the decode kernel holds: the prefill kernel
+  // over the paged cache (chunked prefill), without split-KV
+  const bool prefill = (int64_t)seqlen_q * g > FA_PAGED_MAX_ROWS;
+  if (prefill && num_splits != 1)
+    return fail(FA_ERR_UNSUPPORTED,
+                "num_splits > 1 needs seqlen_q * heads_q / heads_kv <= %d (got %lld); use 1 or 0",
+                FA_PAGED_MAX_ROWS, (long long)seqlen_q * g);
+  if (prefill && page_size % 16 != 0)
+    return fail(FA_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16 (needed for seqlen_q * heads_q / "
+                "heads_kv > %d)", page_size, FA_PAGED_MAX_ROWS);
   const size_t need = fa_kvcache_workspace_size(batch, seqlen_q, heads_q, head_dim, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : (size_t)0);
@@ -242,12 +268,26 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
   p.page = page_size;
   p.max_blocks = max_blocks_per_seq;
   p.num_splits = num_splits;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (prefill) {
+    const bool pack = resolve_pack(opts, heads_q, heads_kv);
+    p.lse_bs = (int64_t)heads_q * seqlen_q;
+    p.lse_hs = seqlen_q;
+    p.hg_count = pack ? heads_kv : heads_q;
+    p.gp = pack ? g : 1;
+    const int64_t rows_seq = (int64_t)seqlen_q * p.gp;
+    p.m_blocks = (int)((rows_seq + FA_BLOCK_M - 1) / FA_BLOCK_M);
+    p.total_tiles = (int64_t)p.m_blocks * batch * p.hg_count;
+    p.persistent = 0;
+    hipError_t e = fa_launch_prefill(p, head_dim, false, true, pack, softcap, s);
+    if (e != hipSuccess) return hip_fail(e, "paged prefill launch");
+    return FA_OK;
+  }
   const int64_t rows = (int64_t)batch * heads_q * seqlen_q;
   if (num_splits > 1) {
     p.o_part = static_cast<float*>(workspace);
     p.lse_part = p.o_part + (size_t)num_splits * rows * head_dim;
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = fa_launch_paged(p, head_dim, softcap, s);
   if (e != hipSuccess) return hip_fail(e, "paged launch");
   if (num_splits > 1) {

@@ -53,9 +53,12 @@ struct FaCombineParams {
   float* lse;  // [rows] in row order, may be null
 };
 
+// Compute units of the current device (fa_kernels.hip; 256 if the query fails).
+int fa_device_cus();
+
 // Launchers (fa_kernels.hip).  They return hipSuccess or the launch error.
-hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool pack, bool softcap,
-                             hipStream_t stream);
+hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, bool pack, bool softcap,
+                             hipStream_t s);
 hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t stream);
 hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t stream);
 

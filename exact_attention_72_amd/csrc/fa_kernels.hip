@@ -310,8 +310,18 @@ __device__ __forceinline__ float exp2_asm(float x) {
   return r;
 }
 // Wait states for a VALU access to the accumulators of the last product issued
-// by pv_mfma_asm (an 8-pass XDL op).
-__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
+// by pv_mfma_asm (an 8-pass XDL op).  The accumulators are operands of the
+// statement: the compiler does not know the products' latency and would
+// otherwise be free to move the (pure arithmetic) accesses above the wait.
+template <int N>
+__device__ __forceinline__ void mfma_drain(f32x16 (&o)[N]) {
+  static_assert(N == 2 || N == 4, "two or four accumulators");
+  if constexpr (N == 4) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+  } else {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(o[0]), "+v"(o[1]));
+  }
+}
 
 // Softcap transform into the log2 domain: c * tanh(scale * s / c) * log2(e),
 // tanh(y) = 1 - 2 / (exp(2y) + 1).
@@ -615,8 +625,16 @@ __device__ __forceinline__ void wait_vmcnt_blocks(int n) {
 // forms S^T of block i + 1, runs the softmax of block i and accumulates
 // O^T += V^T P^T of block i, so matrix products of one block and the softmax of
 // the previous one are independent work within the wave.
-template <int D, bool VARLEN, bool PACK, bool SOFTCAP>
+//
+// PAGED: K and V come from a paged cache ("Attention kernels...", section 6.1):
+// key t of sequence b is slot t % page of page block_table[b][t / page], and
+// the sequence has cache_seqlens[b] keys.  The rows of one LDS-DMA instruction
+// are 1024 / (2 D) consecutive keys starting at a multiple of that count, so
+// with page sizes that are multiples of 16 they lie in one page: one scalar
+// block-table read per instruction.
+template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
+  static_assert(!(VARLEN && PAGED), "a paged cache has its own sequence lengths");
   constexpr int BN = FA_BLOCK_N;  // 32 keys per block
   constexpr int NBUF = 3;  // measured best of 3, 4 and 5 stages
   using G = DmaGeom<D, BN>;
@@ -660,6 +678,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       k_start = p.cu_k[tile.b];
       Lk = p.cu_k[tile.b + 1] - (int)k_start;
     }
+    if (PAGED) Lk = scalar_load_i32(p.cache_seqlens + tile.b);
     const int kvh = PACK ? tile.hg : tile.hg / p.g;
     const int rows = Lq * p.gp;
     const int m0 = tile.mb * FA_BLOCK_M;
@@ -716,7 +735,21 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     auto issue = [&](int i) {
       char* dst = smem + (i % NBUF) * T + wave * 1024;
       const int n0 = (n_lo + i) * BN;
-      if (n0 + BN <= Lk) {
+      if constexpr (PAGED) {
+        // Keys past the last one are clamped to it; a clamped instruction's rows
+        // then all lie in the last key's page.
+        const int32_t* bt = p.block_table + (int64_t)tile.b * p.max_blocks;
+#pragma unroll
+        for (int j = 0; j < G::kInstPerWave; ++j) {
+          const int first = n0 + wave * G::kRowsPerKiB + j * G::kRowStep;  // first row of the instruction
+          const int pg = min(first, Lk - 1) / p.page;
+          const int64_t phys = scalar_load_i32(bt + pg);
+          const int slot = min(n0 + dma_row + j * G::kRowStep, Lk - 1) - pg * p.page;
+          dma16(p.k + phys * p.k_bs + (int64_t)slot * p.k_ss + (int64_t)kvh * p.k_hs + k_src, dst + j * 4096);
+          dma16(p.v + phys * p.v_bs + (int64_t)slot * p.v_ss + (int64_t)kvh * p.v_hs + v_src,
+                dst + NBUF * T + j * 4096);
+        }
+      } else if (n0 + BN <= Lk) {
         const uint16_t* kq = klane + (int64_t)n0 * p.k_ss;
         const uint16_t* vq = vlane + (int64_t)n0 * p.v_ss;
 #pragma unroll
@@ -865,7 +898,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
         }
       }
       if (moved) {
-        mfma_drain();
+        mfma_drain(o);
         l_run *= alpha;
         l_bf *= alpha;
 #pragma unroll
@@ -1225,10 +1258,10 @@ int occupancy(K kernel) {
   return n;
 }
 
-template <int D, bool VARLEN, bool PACK, bool SOFTCAP>
+template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED>
 hipError_t launch_prefill_t(const FaParams& p0, hipStream_t stream) {
   FaParams p = p0;
-  auto kern = fa_prefill_kernel<D, VARLEN, PACK, SOFTCAP>;
+  auto kern = fa_prefill_kernel<D, VARLEN, PACK, SOFTCAP, PAGED>;
   int64_t tiles = p.total_tiles;
   if (tiles <= 0) return hipSuccess;
   int64_t grid;
@@ -1256,16 +1289,21 @@ hipError_t launch_paged_t(const FaParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool pack, bool softcap,
+int fa_device_cus() { return device_cus(); }
+
+hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, bool pack, bool softcap,
                              hipStream_t s) {
-#define FA_PF(D_, V_, P_, S_) \
-  if (d == D_ && varlen == V_ && pack == P_ && softcap == S_) return launch_prefill_t<D_, V_, P_, S_>(p, s);
-  FA_PF(128, false, false, false) FA_PF(128, false, false, true) FA_PF(128, false, true, false)
-  FA_PF(128, false, true, true) FA_PF(128, true, false, false) FA_PF(128, true, false, true)
-  FA_PF(128, true, true, false) FA_PF(128, true, true, true)
-  FA_PF(64, false, false, false) FA_PF(64, false, false, true) FA_PF(64, false, true, false)
-  FA_PF(64, false, true, true) FA_PF(64, true, false, false) FA_PF(64, true, false, true)
-  FA_PF(64, true, true, false) FA_PF(64, true, true, true)
+#define FA_PF(D_, V_, G_, P_, S_)                                                    \
+  if (d == D_ && varlen == V_ && paged == G_ && pack == P_ && softcap == S_) \
+    return launch_prefill_t<D_, V_, P_, S_, G_>(p, s);
+#define FA_PF_D(D_)                                                                                        \
+  FA_PF(D_, false, false, false, false) FA_PF(D_, false, false, false, true)                              \
+  FA_PF(D_, false, false, true, false) FA_PF(D_, false, false, true, true)                                \
+  FA_PF(D_, true, false, false, false) FA_PF(D_, true, false, false, true) FA_PF(D_, true, false, true, false) \
+  FA_PF(D_, true, false, true, true) FA_PF(D_, false, true, false, false) FA_PF(D_, false, true, false, true)  \
+  FA_PF(D_, false, true, true, false) FA_PF(D_, false, true, true, true)
+  FA_PF_D(128) FA_PF_D(64)
+#undef FA_PF_D
 #undef FA_PF
   return hipErrorInvalidValue;
 }

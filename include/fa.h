@@ -105,7 +105,13 @@ int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
  * Logical key t of sequence b lives in page block_table[b][t / page_size] at slot
  * t % page_size.  The keys are cut into num_splits contiguous page ranges; each
  * range produces a normalised partial O and its LSE, which a combine kernel merges
- * on the same stream.  With num_splits == 1 the result is written directly.
+ * on the same stream.  With num_splits == 1 the result is written directly;
+ * num_splits == 0 takes fa_kvcache_num_splits(...).
+ * Chunked prefill ("Attention kernels ...", section 5.1): when a sequence has
+ * more than 32 packed query rows (seqlen_q * heads_q / heads_kv) the queries
+ * run through the prefill kernel over the paged cache, bottom-right aligned
+ * (query t sits at key position t + cache_seqlens[b] - seqlen_q); then
+ * num_splits must resolve to 1 and page_size must be a multiple of 16.
  *   q        [batch, seqlen_q, heads_q, head_dim]  strides q_strides = {batch, seq, head}
  *   k_cache  [num_pages, page_size, heads_kv, head_dim]  strides k_strides = {page, slot, head}
  *   v_cache  same shape, strides v_strides
@@ -115,7 +121,9 @@ int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
  *   lse      [batch, heads_q, seqlen_q] float32 (written; may be NULL)
  *   workspace: device memory of at least fa_kvcache_workspace_size(...) bytes
  *              (may be NULL when that size is 0); holds the fp32 partials.
- * Unsupported: seqlen_q * (heads_q / heads_kv) > 32.
+ * opts->pack_gqa applies to chunked prefill only (decode always packs).
+ * Errors: FA_ERR_UNSUPPORTED for num_splits > 1 with more than 32 packed rows,
+ * or a page_size that is not a multiple of 16 with more than 32 packed rows.
  * Caller contract, not checked on the device: block_table entries of live pages
  * lie in [0, num_pages) and cache_seqlens[b] <= max_blocks_per_seq * page_size. */
 int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache,
@@ -127,6 +135,14 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
                          const int64_t q_strides[3], const int64_t k_strides[3],
                          const int64_t v_strides[3], const int64_t o_strides[3],
                          void* stream);
+
+/* Split count of fa_fwd_kvcache_paged for num_splits == 0 (host only, no device
+ * work; it reads the current device's compute-unit count): about eight
+ * workgroups per compute unit over batch * heads_kv, at most 64 and at most
+ * max_blocks_per_seq splits, and 1 when the call runs as chunked prefill
+ * ("FA4 ...", section 6.2: the split count is chosen to fill the machine). */
+int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, int page_size,
+                          int max_blocks_per_seq);
 
 /* Bytes of workspace fa_fwd_kvcache_paged needs: 0 for num_splits == 1, else
  * num_splits * batch * seqlen_q * heads_q * (head_dim + 1) * 4 rounded up to 256. */

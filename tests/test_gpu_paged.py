@@ -142,3 +142,64 @@ def test_paged_full_size(num_splits):
     torch.cuda.synchronize()
     got = torch.round(torch.exp(lse0.double())).long().cpu()
     assert torch.equal(got, torch.as_tensor(lens).long().view(-1, 1, 1).expand_as(got))
+
+
+# ---------------------------------------------------------------- chunked prefill
+# More than 32 packed query rows per sequence: the prefill kernel reads K/V
+# through the block table (queries bottom-right aligned against the cache).
+@pytest.mark.parametrize("page,lens,Hq,Hkv,d,Nq,pack", [
+    (16, [40, 300, 1000], 8, 2, 128, 40, -1),    # GQA packed into rows, 16-key pages
+    (16, [40, 300, 1000], 8, 2, 128, 40, 0),     # one tile per query head
+    (256, [500, 1300], 4, 4, 64, 300, -1),       # d = 64, pages larger than a block
+    (32, [64, 257, 33], 32, 8, 128, 9, -1),      # 36 packed rows, just past the decode kernel
+    (48, [10, 100], 2, 1, 128, 50, -1),          # more queries than keys: first rows see nothing
+])
+def test_paged_prefill(page, lens, Hq, Hkv, d, Nq, pack):
+    t = W.paged(53 + page + Nq, len(lens), Hq, Hkv, d, page, 0, 0, cache_seqlens=lens, Nq=Nq)
+    kc, vc = poison_unused(t)
+    for S in (1, 0):   # 0 resolves to 1 for chunked prefill
+        out, lse = run(t, kc, vc, S, causal=True, pack_gqa=pack)
+        o_ref, l_ref = oracle.fwd_paged(bits(t["q"]), bits(t["k_cache"]), bits(t["v_cache"]),
+                                        t["block_table"].numpy(), t["cache_seqlens"].numpy(),
+                                        causal=True)
+        check_close(out, lse, o_ref, l_ref, f"paged prefill page={page} lens={lens} Nq={Nq}")
+
+
+def test_paged_prefill_window_softcap_and_count():
+    t = W.paged(61, 3, 8, 2, 128, 64, 0, 0, cache_seqlens=[200, 777, 64], Nq=70, mult=2.0)
+    kw = dict(causal=True, window=(100, 0), softcap=30.0)
+    out, lse = run(t, t["k_cache"], t["v_cache"], 1, **kw)
+    o_ref, l_ref = oracle.fwd_paged(bits(t["q"]), bits(t["k_cache"]), bits(t["v_cache"]),
+                                    t["block_table"].numpy(), t["cache_seqlens"].numpy(), **kw)
+    check_close(out, lse, o_ref, l_ref, "paged prefill window+softcap")
+    # count probe: Q = 0 -> exp(LSE) = number of visible keys of each row
+    t0 = dict(t, q=torch.zeros_like(t["q"]))
+    _, lse0 = run(t0, t["k_cache"], t["v_cache"], 1, causal=True)
+    lens = t["cache_seqlens"].tolist()
+    Nq = t["q"].shape[1]
+    for b, L in enumerate(lens):
+        want = torch.tensor([max(0, min(L, i + L - Nq + 1)) for i in range(Nq)], dtype=torch.long)
+        got = torch.round(torch.exp(lse0[b].double().cpu())).long()
+        assert torch.equal(got, want.view(1, -1).expand_as(got)), f"count probe, sequence {b}"
+
+
+def test_paged_prefill_rejects_splits():
+    t = W.paged(62, 2, 4, 4, 128, 16, 0, 0, cache_seqlens=[100, 50], Nq=40)
+    with pytest.raises(api.FaError):
+        run(t, t["k_cache"], t["v_cache"], 2, causal=True)
+
+
+def test_num_splits_heuristic():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, Hkv, maxb in [(64, 8, 128), (1, 8, 128), (4, 2, 3), (256, 8, 128)]:
+        want = max(1, min(64, maxb, -(-8 * cus // (B * Hkv))))
+        assert api.fa_kvcache_num_splits(B, 1, 4 * Hkv, Hkv, 256, maxb) == want
+    assert api.fa_kvcache_num_splits(2, 40, 8, 2, 16, 100) == 1   # chunked prefill
+
+
+def test_paged_num_splits_auto():
+    t = W.paged(63, 3, 32, 8, 128, 256, 0, 0, cache_seqlens=[1, 3000, 9000])
+    out, lse = run(t, t["k_cache"], t["v_cache"], 0, causal=True)
+    o_ref, l_ref = oracle.fwd_paged(bits(t["q"]), bits(t["k_cache"]), bits(t["v_cache"]),
+                                    t["block_table"].numpy(), t["cache_seqlens"].numpy(), causal=True)
+    check_close(out, lse, o_ref, l_ref, "paged decode num_splits=0")

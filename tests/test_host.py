@@ -145,11 +145,13 @@ def call_paged(num_splits=1, ws=None, ws_bytes=0, Nq=1, Hq=32, Hkv=8, page=256, 
 
 
 def test_paged_rejects_invalid_arguments():
-    assert call_paged(num_splits=0) == FA_ERR_INVALID_ARG
+    assert call_paged(num_splits=-1) == FA_ERR_INVALID_ARG
     assert call_paged(num_splits=4) == FA_ERR_INVALID_ARG                  # no workspace
     need = api.fa_kvcache_workspace_size(64, 1, 32, 128, 4)
     assert call_paged(num_splits=4, ws=FAKE, ws_bytes=need - 256) == FA_ERR_INVALID_ARG
-    assert call_paged(Nq=9) == FA_ERR_UNSUPPORTED                           # 9 * 4 rows > 32
+    # 9 * 4 packed rows > 32 run as chunked prefill: no split-KV, 16-multiple pages
+    assert call_paged(Nq=9, num_splits=2, ws=FAKE, ws_bytes=1 << 30) == FA_ERR_UNSUPPORTED
+    assert call_paged(Nq=9, page=24) == FA_ERR_UNSUPPORTED
     assert call_paged(page=0) == FA_ERR_INVALID_ARG
     assert call_paged(bt=None) == FA_ERR_INVALID_ARG
     assert call_paged(d=32) == FA_ERR_UNSUPPORTED
