@@ -22,7 +22,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
 EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_kvcache_num_splits",
-           "fa_kvcache_workspace_size",
+           "fa_kvcache_workspace_size", "fa_kvcache_append",
            "fa_combine", "fa_tile_class", "fa_last_error", "fa_version")
 
 
@@ -61,10 +61,12 @@ def lib():
     L.fa_kvcache_num_splits.argtypes = [I, I, I, I, I, I]
     L.fa_kvcache_num_splits.restype = I
     L.fa_combine.argtypes = [P, P, I, I64, I, P, I64, P, P]
+    L.fa_kvcache_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I64, I, I, S3, S3, S3, S3, P]
     L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = I
-    for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_combine", "fa_tile_class"):
+    for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_combine", "fa_tile_class",
+                 "fa_kvcache_append"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -192,6 +194,26 @@ def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num
                                       _strides(v_cache, (0, 1, 2)), _strides(out, (0, 1, 2)),
                                       _stream(stream)))
     return out, lse
+
+
+def fa_kvcache_append(k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, *, stream=None):
+    """Write k_new/v_new [B, L, Hkv, d] into the paged caches [num_pages, page, Hkv, d]
+    at logical positions cache_seqlens[b] + t (in place; cache_seqlens is not updated)."""
+    _bf16_cuda(k_new, v_new, k_cache, v_cache)
+    B, L, Hkv, d = k_new.shape
+    if tuple(v_new.shape) != (B, L, Hkv, d) or k_cache.shape != v_cache.shape or k_cache.shape[2:] != (Hkv, d):
+        raise ValueError("k_new/v_new [B, L, Hkv, d] and caches [num_pages, page, Hkv, d] disagree")
+    for c in (block_table, cache_seqlens):
+        if c.dtype != torch.int32 or not c.is_cuda:
+            raise TypeError("block_table and cache_seqlens must be int32 device tensors")
+    if block_table.stride(-1) != 1 or block_table.stride(0) != block_table.shape[1]:
+        raise ValueError("block_table must be a contiguous [batch, max_blocks] tensor")
+    _check(lib().fa_kvcache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_table), _ptr(cache_seqlens), B, L, Hkv, d,
+                                   k_cache.shape[0], k_cache.shape[1], block_table.shape[1],
+                                   _strides(k_new, (0, 1, 2)), _strides(v_new, (0, 1, 2)),
+                                   _strides(k_cache, (0, 1, 2)), _strides(v_cache, (0, 1, 2)),
+                                   _stream(stream)))
 
 
 def fa_combine(o_part, lse_part, *, out=None, lse=None, stream=None):

@@ -307,6 +307,44 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
   return FA_OK;
 }
 
+int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* block_table, const int32_t* cache_seqlens, int batch, int seqlen_new,
+                      int heads_kv, int head_dim, int64_t num_pages, int page_size, int max_blocks_per_seq,
+                      const int64_t kn_strides[3], const int64_t vn_strides[3], const int64_t k_strides[3],
+                      const int64_t v_strides[3], void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !cache_seqlens)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || seqlen_new < 0 || heads_kv <= 0 || num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0)
+    return fail(FA_ERR_INVALID_ARG,
+                "batch, heads_kv, num_pages, page_size and max_blocks_per_seq must be positive, seqlen_new >= 0");
+  if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
+    return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
+  if ((rc = check_strides("k_new", k_new, kn_strides, 3)) || (rc = check_strides("v_new", v_new, vn_strides, 3)) ||
+      (rc = check_strides("k_cache", k_cache, k_strides, 3)) || (rc = check_strides("v_cache", v_cache, v_strides, 3)))
+    return rc;
+  if (seqlen_new == 0) return FA_OK;
+  FaAppendParams p;
+  memset(&p, 0, sizeof p);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_cache = static_cast<uint16_t*>(k_cache);
+  p.v_cache = static_cast<uint16_t*>(v_cache);
+  p.kn_bs = kn_strides[0]; p.kn_ss = kn_strides[1]; p.kn_hs = kn_strides[2];
+  p.vn_bs = vn_strides[0]; p.vn_ss = vn_strides[1]; p.vn_hs = vn_strides[2];
+  p.k_ps = k_strides[0]; p.k_ss = k_strides[1]; p.k_hs = k_strides[2];
+  p.v_ps = v_strides[0]; p.v_ss = v_strides[1]; p.v_hs = v_strides[2];
+  p.block_table = block_table;
+  p.cache_seqlens = cache_seqlens;
+  p.B = batch; p.L = seqlen_new; p.Hkv = heads_kv; p.page = page_size; p.max_blocks = max_blocks_per_seq;
+  hipError_t e = fa_launch_append(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return FA_OK;
+}
+
 int fa_combine(const float* o_part, const float* lse_part, int num_splits, int64_t rows, int head_dim,
                void* out, int64_t out_row_stride, float* lse_out, void* stream) {
   g_err[0] = 0;

@@ -42,6 +42,21 @@ struct FaParams {
   int causal, wl, wr;
 };
 
+// In-place append of new K/V tokens to a paged cache.
+struct FaAppendParams {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int64_t kn_bs, kn_ss, kn_hs;  // new tokens: (batch, token, head) strides in elements
+  int64_t vn_bs, vn_ss, vn_hs;
+  int64_t k_ps, k_ss, k_hs;     // caches: (page, slot, head) strides in elements
+  int64_t v_ps, v_ss, v_hs;
+  const int32_t* block_table;
+  const int32_t* cache_seqlens;  // lengths before the append
+  int B, L, Hkv, page, max_blocks;
+};
+
 struct FaCombineParams {
   const float* o_part;
   const float* lse_part;
@@ -61,6 +76,7 @@ hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, 
                              hipStream_t s);
 hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t stream);
 hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t stream);
+hipError_t fa_launch_append(const FaAppendParams& p, int d, hipStream_t stream);
 
 // Tile geometry of the prefill kernel.
 constexpr int FA_BLOCK_M = 128;     // query rows per workgroup tile (4 waves x 32)

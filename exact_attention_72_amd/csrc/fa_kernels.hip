@@ -1230,6 +1230,35 @@ __global__ __launch_bounds__(kThreads) void fa_combine_kernel(FaCombineParams p)
   if (lane == 0 && p.lse) p.lse[r] = empty ? kNegInf : M + __builtin_logf(W);
 }
 
+// ------------------------------------------------------------------ K/V append
+// Incremental decoding writes the new keys and values into the cache in place
+// ("FA4 ...", section 6.2): token t of sequence b goes to logical position
+// cache_seqlens[b] + t, i.e. slot pos % page of page block_table[b][pos / page]
+// ("Attention kernels...", section 6.1).  A plain copy, bound by memory: one
+// thread per 16-byte chunk of a row, consecutive threads on consecutive chunks
+// of a row and then of the next head, so a wave writes whole rows.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa_append_kernel(FaAppendParams p) {
+  constexpr int C = D / 8;  // 16-byte chunks per row
+  const int64_t total = (int64_t)p.B * p.L * p.Hkv * C;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
+    const int c = (int)(i % C);
+    int64_t r = i / C;
+    const int h = (int)(r % p.Hkv);
+    r /= p.Hkv;
+    const int t = (int)(r % p.L);
+    const int b = (int)(r / p.L);
+    const int pos = p.cache_seqlens[b] + t;
+    const int64_t phys = p.block_table[(int64_t)b * p.max_blocks + pos / p.page];
+    const int64_t slot = pos % p.page;
+    const u32x4 kx = *reinterpret_cast<const u32x4*>(p.k_new + b * p.kn_bs + t * p.kn_ss + h * p.kn_hs + 8 * c);
+    const u32x4 vx = *reinterpret_cast<const u32x4*>(p.v_new + b * p.vn_bs + t * p.vn_ss + h * p.vn_hs + 8 * c);
+    *reinterpret_cast<u32x4*>(p.k_cache + phys * p.k_ps + slot * p.k_ss + h * p.k_hs + 8 * c) = kx;
+    *reinterpret_cast<u32x4*>(p.v_cache + phys * p.v_ps + slot * p.v_ss + h * p.v_hs + 8 * c) = vx;
+  }
+}
+
 // ------------------------------------------------------------------ launch helpers
 struct DeviceInfo {
   int cus = 0;
@@ -1321,6 +1350,21 @@ hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t s) {
     hipLaunchKernelGGL(fa_combine_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else if (d == 64)
     hipLaunchKernelGGL(fa_combine_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t fa_launch_append(const FaAppendParams& p, int d, hipStream_t s) {
+  const int64_t total = (int64_t)p.B * p.L * p.Hkv * (d / 8);
+  if (total <= 0) return hipSuccess;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  const int64_t cap = 16 * (int64_t)device_cus();  // grid-stride beyond that
+  if (blocks > cap) blocks = cap;
+  if (d == 128)
+    hipLaunchKernelGGL(fa_append_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else if (d == 64)
+    hipLaunchKernelGGL(fa_append_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -149,6 +149,28 @@ int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, in
 size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_dim,
                                  int num_splits);
 
+/* In-place append of new keys and values to a paged cache, for incremental
+ * decoding ("FA4 ...", section 6.2: the kvcache call writes the new k and v into
+ * the cache; "Attention kernels ...", section 6.1: logical key t of a sequence is
+ * slot t % page_size of page block_table[b][t / page_size]).  Token t of
+ * sequence b is written at logical position cache_seqlens[b] + t.
+ *   k_new, v_new      [batch, seqlen_new, heads_kv, head_dim]  strides {batch, seq, head}
+ *   k_cache, v_cache  [num_pages, page_size, heads_kv, head_dim]  strides {page, slot, head}
+ *                     (written in place; nothing else in them changes)
+ *   block_table       device int32 [batch, max_blocks_per_seq]
+ *   cache_seqlens     device int32 [batch]: lengths before the append (read, not updated;
+ *                     attend afterwards with cache_seqlens[b] + seqlen_new keys)
+ * seqlen_new == 0 is a no-op.  Caller contract, not checked on the device:
+ * cache_seqlens[b] + seqlen_new <= max_blocks_per_seq * page_size, the pages those
+ * positions map to lie in [0, num_pages), and no two sequences map a written
+ * position to the same slot. */
+int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* block_table, const int32_t* cache_seqlens, int batch,
+                      int seqlen_new, int heads_kv, int head_dim, int64_t num_pages,
+                      int page_size, int max_blocks_per_seq, const int64_t kn_strides[3],
+                      const int64_t vn_strides[3], const int64_t k_strides[3],
+                      const int64_t v_strides[3], void* stream);
+
 /* Merge of partial attention states ("Attention kernels ...", section 6.3: the
  * partial (O_s, LSE_s) of disjoint key ranges combine with the same rescale as
  * the tiles of one pass):

@@ -250,3 +250,29 @@ def probs_dense(q, k, v, row, *, scale=None, causal=False, window=None, softcap=
     if rc < 0:
         raise ValueError("oracle_probs_dense rejected its arguments")
     return p
+
+
+def kvcache_append(k_new, v_new, k_cache, v_cache, block_table, cache_seqlens):
+    """In-place append of new tokens to a paged cache, written out from its
+    definition ("FA4 (CuTeDSL) and engineering interfaces", section 6.2: the new
+    k, v go into the cache; "Attention kernels: FlashAttention and
+    PagedAttention", section 6.1: logical key t of sequence b is slot t % page of
+    page block_table[b][t // page]).  Token t of sequence b lands at logical
+    position cache_seqlens[b] + t.  Pure indexing (no arithmetic), so it lives
+    here rather than in oracle.c.
+
+    k_new, v_new: uint16 [B, L, Hkv, d]; caches: uint16 [num_pages, page, Hkv, d].
+    Returns new (k_cache, v_cache); the inputs are not modified.
+    """
+    k_new, v_new = _u16(k_new), _u16(v_new)
+    kc, vc = _u16(k_cache).copy(), _u16(v_cache).copy()
+    bt, sl = _i32(block_table), _i32(cache_seqlens)
+    B, L = k_new.shape[0], k_new.shape[1]
+    page = kc.shape[1]
+    for b in range(B):
+        for t in range(L):
+            pos = int(sl[b]) + t
+            phys = int(bt[b, pos // page])
+            kc[phys, pos % page] = k_new[b, t]
+            vc[phys, pos % page] = v_new[b, t]
+    return kc, vc

@@ -203,3 +203,50 @@ def test_paged_num_splits_auto():
     o_ref, l_ref = oracle.fwd_paged(bits(t["q"]), bits(t["k_cache"]), bits(t["v_cache"]),
                                     t["block_table"].numpy(), t["cache_seqlens"].numpy(), causal=True)
     check_close(out, lse, o_ref, l_ref, "paged decode num_splits=0")
+
+
+# ---------------------------------------------------------------- K/V append
+@pytest.mark.parametrize("page,lens,L,Hkv,d", [
+    (16, [0, 5, 16, 40], 7, 2, 128),     # empty cache, page boundaries crossed
+    (256, [100, 3000], 33, 8, 64),
+    (32, [31], 1, 4, 128),               # one decode token at a page edge
+])
+def test_kvcache_append_bitexact(page, lens, L, Hkv, d):
+    grown = [n + L for n in lens]
+    t = W.paged(71 + page + L, len(lens), Hkv, Hkv, d, page, 0, 0, cache_seqlens=grown)
+    g = torch.Generator().manual_seed(72 + L)
+    # new tokens as a strided view (every other head of a wider tensor)
+    wide_k = torch.randn(len(lens), L, 2 * Hkv, d, generator=g).to(torch.bfloat16)
+    wide_v = torch.randn(len(lens), L, 2 * Hkv, d, generator=g).to(torch.bfloat16)
+    kn, vn = wide_k[:, :, ::2], wide_v[:, :, ::2]
+    kc, vc = t["k_cache"].to(DEV), t["v_cache"].to(DEV)
+    api.fa_kvcache_append(wide_k.to(DEV)[:, :, ::2], wide_v.to(DEV)[:, :, ::2], kc, vc,
+                          t["block_table"].to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    k_ref, v_ref = oracle.kvcache_append(bits(kn), bits(vn), bits(t["k_cache"]), bits(t["v_cache"]),
+                                         t["block_table"].numpy(), lens)
+    assert np.array_equal(bits(kc.cpu()), k_ref)
+    assert np.array_equal(bits(vc.cpu()), v_ref)
+
+
+def test_decode_step_append_then_attend():
+    """One incremental-decoding step: append the new token's K/V, then attend with
+    the grown lengths; against the oracle on the oracle-appended cache."""
+    page, lens, Hq, Hkv, d = 16, [1, 17, 300, 1000], 32, 8, 128
+    grown = [n + 1 for n in lens]
+    t = W.paged(81, len(lens), Hq, Hkv, d, page, 0, 0, cache_seqlens=grown)
+    g = torch.Generator().manual_seed(82)
+    kn = torch.randn(len(lens), 1, Hkv, d, generator=g).to(torch.bfloat16)
+    vn = torch.randn(len(lens), 1, Hkv, d, generator=g).to(torch.bfloat16)
+    kc, vc = t["k_cache"].to(DEV), t["v_cache"].to(DEV)
+    bt = t["block_table"].to(DEV)
+    api.fa_kvcache_append(kn.to(DEV), vn.to(DEV), kc, vc, bt, torch.tensor(lens, dtype=torch.int32, device=DEV))
+    out, lse = api.fa_fwd_kvcache_paged(t["q"].to(DEV), kc, vc, bt,
+                                        torch.tensor(grown, dtype=torch.int32, device=DEV),
+                                        num_splits=0, causal=True)
+    torch.cuda.synchronize()
+    k_ref, v_ref = oracle.kvcache_append(bits(kn), bits(vn), bits(t["k_cache"]), bits(t["v_cache"]),
+                                         t["block_table"].numpy(), lens)
+    o_ref, l_ref = oracle.fwd_paged(bits(t["q"]), k_ref, v_ref, t["block_table"].numpy(), grown,
+                                    causal=True)
+    check_close(out, lse, o_ref, l_ref, "decode step after append")

@@ -218,3 +218,18 @@ def test_full_tile_range_matches_tile_classes(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     bad, cases = map(int, r.stdout.split())
     assert cases > 1_000_000 and bad == 0, r.stdout
+
+
+def test_append_rejects_invalid_arguments():
+    L = api.lib()
+    def call(kn=FAKE, d=128, B=2, Ln=3, Hkv=8, page=16, bt=FAKE, ks=S3):
+        return L.fa_kvcache_append(kn, FAKE, FAKE, FAKE, bt, FAKE, B, Ln, Hkv, d, 100, page, 10,
+                                   S3, S3, ks, S3, None)
+    assert call(kn=None) == FA_ERR_INVALID_ARG
+    assert call(bt=None) == FA_ERR_INVALID_ARG
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(B=0) == FA_ERR_INVALID_ARG
+    assert call(Ln=-1) == FA_ERR_INVALID_ARG
+    assert call(page=0) == FA_ERR_INVALID_ARG
+    assert call(ks=(ctypes.c_int64 * 3)(2048, 2050, 128)) == FA_ERR_INVALID_ARG
+    assert call(Ln=0) == 0                                           # nothing to write, no launch

@@ -326,3 +326,48 @@ def test_rows_subset_matches_full_output():
     for n, r in enumerate(rows):
         b, h, i = r // (H * N), (r // N) % H, r % N
         assert np.array_equal(os_[n], o[b, i, h]) and ls_[n] == lse[b, h, i]
+
+
+# ---------------------------------------------------------------- K/V append
+def test_append_follows_the_block_table_example(golden):
+    """Appending at cache_seqlens writes exactly the slots the pages' block-table
+    example assigns to those logical positions, and nothing else."""
+    g = golden("block_table_example.json")
+    P, npages, d = g["page_size"], g["num_pages"], 8
+    bt = np.array([g["block_table"]], np.int32)
+    kc = W.randn_bf16(W.generator(51), (npages, P, 1, d))
+    vc = W.randn_bf16(W.generator(52), (npages, P, 1, d))
+    start, L = 13, 40                      # positions 13..52: spans four logical blocks
+    kn = W.randn_bf16(W.generator(53), (1, L, 1, d))
+    vn = W.randn_bf16(W.generator(54), (1, L, 1, d))
+    k2, v2 = oracle.kvcache_append(bits(kn), bits(vn), bits(kc), bits(vc), bt, [start])
+    written = np.zeros((npages, P), bool)
+    for lo, hi, phys in g["token_ranges_to_physical"]:
+        for pos in range(max(lo, start), min(hi, start + L - 1) + 1):
+            assert np.array_equal(k2[phys, pos - lo], bits(kn)[0, pos - start])
+            assert np.array_equal(v2[phys, pos - lo], bits(vn)[0, pos - start])
+            written[phys, pos - lo] = True
+    assert written.sum() == L
+    assert np.array_equal(k2[~written], bits(kc)[~written])
+    assert np.array_equal(v2[~written], bits(vc)[~written])
+
+
+def test_append_then_attend_sees_the_new_tokens():
+    """Through the (C) paged view: after an append, a zero query over the grown
+    cache averages the old and the new value rows, and the count is exact."""
+    page, lens, L, d = 16, [5, 16, 40], 7, 8
+    t = W.paged(191, 3, 2, 2, d, page, 0, 0, cache_seqlens=[n + L for n in lens])
+    kn = W.randn_bf16(W.generator(192), (3, L, 2, d))
+    vn = W.randn_bf16(W.generator(193), (3, L, 2, d))
+    bt = t["block_table"].numpy()
+    k2, v2 = oracle.kvcache_append(bits(kn), bits(vn), bits(t["k_cache"]), bits(t["v_cache"]), bt, lens)
+    q0 = torch.zeros(3, 1, 2, d, dtype=torch.bfloat16)
+    grown = [n + L for n in lens]
+    o, lse = oracle.fwd_paged(bits(q0), k2, v2, bt, grown, causal=True)
+    vd = v_double(t["v_cache"])
+    vnd = v_double(vn)
+    for b, n in enumerate(lens):
+        old = [vd[bt[b, j // page], j % page] for j in range(n)]
+        rows = np.array(old + [vnd[b, j] for j in range(L)])       # [n + L, Hkv, d]
+        np.testing.assert_allclose(o[b, 0], rows.mean(0), rtol=0, atol=1e-12)
+        assert np.allclose(np.exp(lse[b, :, 0]), n + L, rtol=0, atol=1e-9)
