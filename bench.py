@@ -184,6 +184,8 @@ def bench_decode(api, W, steps, warmup):
     best = max(res, key=lambda s: res[s]["kv_GBps"])
     return {"metric": "paged decode KV GB/s", "unit": "GB/s",
             "value": res[best]["kv_GBps"], "num_splits": best,
+            "num_splits_auto": api.fa_kvcache_num_splits(c["B"], 1, c["Hq"], c["Hkv"], c["page"],
+                                                         c["max_blocks"]),
             "kv_bytes": kv_bytes,
             "per_split": {str(s): {"ms": round(r["ms"], 4), "kv_GBps": round(r["kv_GBps"], 1)}
                           for s, r in res.items()},

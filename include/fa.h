@@ -137,7 +137,7 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
                          void* stream);
 
 /* Split count of fa_fwd_kvcache_paged for num_splits == 0 (host only, no device
- * work; it reads the current device's compute-unit count): about eight
+ * work; it reads the current device's compute-unit count): about 32
  * workgroups per compute unit over batch * heads_kv, at most 64 and at most
  * max_blocks_per_seq splits, and 1 when the call runs as chunked prefill
  * ("FA4 ...", section 6.2: the split count is chosen to fill the machine). */

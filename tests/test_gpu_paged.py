@@ -192,7 +192,7 @@ def test_paged_prefill_rejects_splits():
 def test_num_splits_heuristic():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for B, Hkv, maxb in [(64, 8, 128), (1, 8, 128), (4, 2, 3), (256, 8, 128)]:
-        want = max(1, min(64, maxb, -(-8 * cus // (B * Hkv))))
+        want = max(1, min(64, maxb, -(-32 * cus // (B * Hkv))))
         assert api.fa_kvcache_num_splits(B, 1, 4 * Hkv, Hkv, 256, maxb) == want
     assert api.fa_kvcache_num_splits(2, 40, 8, 2, 16, 100) == 1   # chunked prefill
 
