@@ -4,9 +4,11 @@ A step is one forward pass of the dense causal prefill workload
 (batch 4, 16 heads, N = 4096, d = 128, bf16) through the C ABI.  The line also
 carries, as secondary figures, the paged split-KV decode measurement (64
 sequences, 32/8 heads, d = 128, 256-token pages, num_splits in {1, 4, 16}),
-the varlen GQA prefill (32 sequences of 64..8192 tokens, 32/4 heads, packed)
-and the long-context local attention with softcap (N = 32768, 32 heads,
-window 4096, softcap 30).
+the varlen GQA prefill (32 sequences of 64..8192 tokens, 32/4 heads, packed),
+the long-context local attention with softcap (N = 32768, 32 heads,
+window 4096, softcap 30), and the chunked prefill over a paged cache (4 x 4096
+new tokens against 16384 cached keys, 32/8 heads) with the in-place K/V append
+of that chunk.
 
 Prints one JSON line:
   value        prefill TFLOP/s, FLOPs counted as 4 * B * H * N^2 * d * 1/2 (the
@@ -163,6 +165,55 @@ def bench_local(api, W, steps, warmup):
                        "flop_convention": "4*d*H*sum_i(min(i,4096)+1)"}}
 
 
+def paged_prefill_inputs(W, device="cuda"):
+    c = W.WORKLOADS["paged_prefill_b4_h32kv8_d128_chunk4096_prefix12288_page256"]
+    Lk = c["prefix"] + c["Nq"]
+    t = W.paged(c["seed"], c["B"], c["Hq"], c["Hkv"], c["d"], c["page"], 0, 0,
+                max_blocks=c["max_blocks"], Nq=c["Nq"], cache_seqlens=[Lk] * c["B"], device=device)
+    return c, t
+
+
+def bench_paged_prefill(api, W, steps, warmup):
+    """Chunked prefill over a paged cache: 4 sequences, a 4096-token chunk against 16384 cached
+    keys (12288-token prefix + the chunk), 32 Q / 8 KV heads packed, 256-token pages.  FLOPs:
+    4 d Hq B sum_i (prefix + i + 1) (visible pairs only).  Also times the in-place append of the
+    chunk's K/V into the cache (bytes read + written per call)."""
+    import torch
+    c, t = paged_prefill_inputs(W)
+    name = "paged_prefill_b4_h32kv8_d128_chunk4096_prefix12288_page256"
+    B, Nq, P = c["B"], c["Nq"], c["prefix"]
+    flops = 4.0 * c["d"] * c["Hq"] * B * (Nq * P + Nq * (Nq + 1) / 2)
+    bt, sl = t["block_table"].cuda(), t["cache_seqlens"].cuda()
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((B, c["Hq"], Nq), dtype=torch.float32, device="cuda")
+    fn = lambda: api.fa_fwd_kvcache_paged(t["q"], t["k_cache"], t["v_cache"], bt, sl, num_splits=0,  # noqa
+                                          causal=True, out=out, lse=lse)
+    wall, ms = time_launches(fn, steps, warmup)
+    tf = flops / (ms * 1e-3) / 1e12
+    # append: the chunk's K/V (new tensors of the chunk's shape) at positions prefix .. prefix + Nq - 1
+    g = W.generator(c["seed"] + 7, "cuda")
+    kn = W.randn_bf16(g, (B, Nq, c["Hkv"], c["d"]), 1.0, "cuda")
+    vn = W.randn_bf16(g, (B, Nq, c["Hkv"], c["d"]), 1.0, "cuda")
+    start = torch.full((B,), P, dtype=torch.int32, device="cuda")
+    fa = lambda: api.fa_kvcache_append(kn, vn, t["k_cache"], t["v_cache"], bt, start)  # noqa
+    _, ms_a = time_launches(fa, steps, min(warmup, 50))
+    moved = 2.0 * 2 * kn.numel() * 2          # K and V, read once and written once, bf16
+    gbs = moved / (ms_a * 1e-3) / 1e9
+    return {"metric": "chunked prefill over a paged cache TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
+            "kernel_ms": round(ms, 4), "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
+            "config": {"workload": name, "batch": B, "chunk": Nq, "prefix": P, "heads_q": c["Hq"],
+                       "heads_kv": c["Hkv"], "head_dim": c["d"], "page_size": c["page"],
+                       "num_splits": 0, "flop_convention": "4*d*Hq*B*sum_i(prefix+i+1)"},
+            "append": {"metric": "K/V append GB/s (read + write)", "unit": "GB/s", "value": round(gbs, 1),
+                       "kernel_ms": round(ms_a, 4), "bytes": moved,
+                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
+                       "config": {"tokens": B * Nq, "heads_kv": c["Hkv"], "head_dim": c["d"],
+                                  "page_size": c["page"]}}}
+
+
 def bench_decode(api, W, steps, warmup):
     import torch
     c = W.WORKLOADS["paged_decode_b64_h32kv8_d128_page256"]
@@ -206,6 +257,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-local", action="store_true")
+    ap.add_argument("--no-paged-prefill", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -261,6 +313,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_local:
         line["local_softcap"] = bench_local(api, W, max(5, args.steps // 5), max(3, args.warmup // 5))
+        torch.cuda.empty_cache()
+    if not args.no_paged_prefill:
+        line["paged_prefill"] = bench_paged_prefill(api, W, max(10, args.steps // 5), max(5, args.warmup // 5))
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         tc = W.dense(c["seed"], B, N, H, c["Hkv"], d)

@@ -44,6 +44,11 @@ WORKLOADS = {
     "local_softcap_n32768_h32_d128_w4096_cap30": dict(kind="dense", B=1, N=32768, Hq=32, Hkv=32,
                                                       d=128, causal=True, window=(4096, 0),
                                                       softcap=30.0, mult=2.0, seed=5),
+    # chunked prefill: a 4096-token chunk of each of 4 prompts against its paged cache, which
+    # holds a 12288-token prefix plus the chunk itself (16384 keys, bottom-right causal)
+    "paged_prefill_b4_h32kv8_d128_chunk4096_prefix12288_page256": dict(
+        kind="paged_prefill", B=4, Hq=32, Hkv=8, d=128, page=256, Nq=4096, prefix=12288,
+        max_blocks=64, causal=True, window=(-1, -1), softcap=0.0, mult=1.0, seed=6),
 }
 
 

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from exact_attention_72_amd import api, workloads as W
-from gpu_util import DEV, bits, check_close
+from gpu_util import DEV, bits, check_close, gather_dense_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -250,3 +250,31 @@ def test_decode_step_append_then_attend():
     o_ref, l_ref = oracle.fwd_paged(bits(t["q"]), k_ref, v_ref, t["block_table"].numpy(), grown,
                                     causal=True)
     check_close(out, lse, o_ref, l_ref, "decode step after append")
+
+
+def test_paged_prefill_full_size_sampled():
+    """The chunked-prefill workload the benchmark times (4 x 4096 queries over 16384 cached
+    keys, 32/8 heads, 256-token pages, num_splits = 0), sampled rows against the oracle, plus
+    the count probe on every row."""
+    import bench
+    c, t = bench.paged_prefill_inputs(W, device=DEV)
+    bt, sl = t["block_table"].to(DEV), t["cache_seqlens"].to(DEV)
+    out, lse = api.fa_fwd_kvcache_paged(t["q"], t["k_cache"], t["v_cache"], bt, sl, num_splits=0,
+                                        causal=True)
+    torch.cuda.synchronize()
+    B, Nq, Hq = c["B"], c["Nq"], c["Hq"]
+    g = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([
+        g.integers(0, B * Hq * Nq, 300),
+        np.array([0, Nq - 1, 127, 128, 255, 256, B * Hq * Nq - 1])]))   # row = (b * Hq + h) * Nq + i
+    o_ref, l_ref = oracle.fwd_paged(bits(t["q"]), bits(t["k_cache"]), bits(t["v_cache"]),
+                                    t["block_table"].numpy(), t["cache_seqlens"].numpy(),
+                                    causal=True, rows=rows)
+    o_s, l_s = gather_dense_rows(out, lse, rows, B, Hq, Nq)
+    check_close(o_s, l_s, o_ref, l_ref, "chunked prefill full size, sampled rows")
+    _, lse0 = api.fa_fwd_kvcache_paged(torch.zeros_like(t["q"]), t["k_cache"], t["v_cache"], bt, sl,
+                                       num_splits=0, causal=True)
+    torch.cuda.synchronize()
+    want = torch.arange(Nq, dtype=torch.float64) + (c["prefix"] + 1)
+    got = torch.round(torch.exp(lse0.double().cpu()))
+    assert torch.equal(got, want.view(1, 1, -1).expand_as(got))
