@@ -21,7 +21,7 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
-EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_kvcache_num_splits",
+EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_varlen_paged", "fa_kvcache_num_splits",
            "fa_kvcache_workspace_size", "fa_kvcache_append",
            "fa_combine", "fa_tile_class", "fa_last_error", "fa_version")
 
@@ -62,11 +62,13 @@ def lib():
     L.fa_kvcache_num_splits.restype = I
     L.fa_combine.argtypes = [P, P, I, I64, I, P, I64, P, P]
     L.fa_kvcache_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I64, I, I, S3, S3, S3, S3, P]
+    L.fa_fwd_varlen_paged.argtypes = [OPT, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I64, I, I, S3, S3, S3,
+                                      S3, P]
     L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = I
     for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_combine", "fa_tile_class",
-                 "fa_kvcache_append"):
+                 "fa_kvcache_append", "fa_fwd_varlen_paged"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -193,6 +195,35 @@ def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num
                                       _strides(q, (0, 1, 2)), _strides(k_cache, (0, 1, 2)),
                                       _strides(v_cache, (0, 1, 2)), _strides(out, (0, 1, 2)),
                                       _stream(stream)))
+    return out, lse
+
+
+def fa_fwd_varlen_paged(q, k_cache, v_cache, cu_seqlens_q, max_seqlen_q, block_table, cache_seqlens, *,
+                        softmax_scale=None, causal=True, window=None, softcap=0.0, pack_gqa=-1,
+                        out=None, lse=None, return_lse=True, stream=None):
+    """Unified prefill + decode over a paged cache.  q [total_q, Hq, d] packed by cu_seqlens_q;
+    caches [num_pages, page, Hkv, d]; block_table int32 [B, max_blocks]; cache_seqlens int32 [B]
+    (keys per sequence, new tokens included) -> (out [total_q, Hq, d], lse [Hq, total_q])."""
+    _bf16_cuda(q, k_cache, v_cache)
+    total_q, Hq, d = q.shape
+    num_pages, page, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    for c in (cu_seqlens_q, block_table, cache_seqlens):
+        if c.dtype != torch.int32 or not c.is_cuda:
+            raise TypeError("cu_seqlens_q, block_table and cache_seqlens must be int32 device tensors")
+    if block_table.stride(-1) != 1 or block_table.stride(0) != block_table.shape[1]:
+        raise ValueError("block_table must be a contiguous [batch, max_blocks] tensor")
+    B = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _bf16_cuda(out)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
+    _check(lib().fa_fwd_varlen_paged(ctypes.byref(o), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                     _ptr(lse), _ptr(cu_seqlens_q), _ptr(block_table), _ptr(cache_seqlens),
+                                     B, int(max_seqlen_q), total_q, Hq, Hkv, d, num_pages, page,
+                                     block_table.shape[1], _strides(q, (0, 1)), _strides(k_cache, (0, 1, 2)),
+                                     _strides(v_cache, (0, 1, 2)), _strides(out, (0, 1)), _stream(stream)))
     return out, lse
 
 

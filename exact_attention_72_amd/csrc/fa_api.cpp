@@ -207,6 +207,64 @@ int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, in
   return s < 1 ? 1 : (int)s;
 }
 
+int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, const void* v_cache,
+                        void* out, float* lse, const int32_t* cu_seqlens_q, const int32_t* block_table,
+                        const int32_t* cache_seqlens, int batch, int max_seqlen_q, int total_q, int heads_q,
+                        int heads_kv, int head_dim, int64_t num_pages, int page_size, int max_blocks_per_seq,
+                        const int64_t q_strides[2], const int64_t k_strides[3], const int64_t v_strides[3],
+                        const int64_t o_strides[2], void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
+  if (!q || !k_cache || !v_cache || !out || !cu_seqlens_q || !block_table || !cache_seqlens)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || max_seqlen_q < 0 || total_q < 0 || num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0)
+    return fail(FA_ERR_INVALID_ARG,
+                "batch, num_pages, page_size and max_blocks_per_seq must be positive and sizes non-negative");
+  if (page_size % 16 != 0) return fail(FA_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", page_size);
+  if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
+    return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
+  if ((rc = check_strides("q", q, q_strides, 2)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
+      (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 2)))
+    return rc;
+  FaParams p;
+  memset(&p, 0, sizeof p);
+  bool softcap = false;
+  if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
+  if (total_q == 0 || max_seqlen_q == 0) return FA_OK;  // nothing to compute
+  const bool pack = resolve_pack(opts, heads_q, heads_kv);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.q_bs = 0; p.q_ss = q_strides[0]; p.q_hs = q_strides[1];
+  p.k_bs = k_strides[0]; p.k_ss = k_strides[1]; p.k_hs = k_strides[2];
+  p.v_bs = v_strides[0]; p.v_ss = v_strides[1]; p.v_hs = v_strides[2];
+  p.o_bs = 0; p.o_ss = o_strides[0]; p.o_hs = o_strides[1];
+  p.lse_bs = 0;
+  p.lse_hs = total_q;
+  p.B = batch; p.Nq = max_seqlen_q; p.Nk = 0; p.Hq = heads_q; p.Hkv = heads_kv;
+  p.g = heads_q / heads_kv;
+  p.hg_count = pack ? heads_kv : heads_q;
+  p.gp = pack ? p.g : 1;
+  p.cu_q = cu_seqlens_q;
+  p.block_table = block_table;
+  p.cache_seqlens = cache_seqlens;
+  p.page = page_size;
+  p.max_blocks = max_blocks_per_seq;
+  const int64_t rows = (int64_t)max_seqlen_q * p.gp;
+  if (rows > (int64_t)1 << 30) return fail(FA_ERR_UNSUPPORTED, "too many rows per sequence");
+  p.m_blocks = (int)((rows + FA_BLOCK_M - 1) / FA_BLOCK_M);
+  int64_t bound = (int64_t)p.m_blocks * batch;
+  int64_t bound2 = ((int64_t)total_q * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M + batch;
+  p.total_tiles = (bound < bound2 ? bound : bound2) * p.hg_count;
+  p.persistent = 1;
+  hipError_t e = fa_launch_prefill(p, head_dim, true, true, pack, softcap, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "varlen paged launch");
+  return FA_OK;
+}
+
 size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_dim, int num_splits) {
   if (num_splits <= 1 || batch <= 0 || seqlen_q <= 0 || heads_q <= 0 || head_dim <= 0) return 0;
   size_t rows = (size_t)batch * seqlen_q * heads_q;

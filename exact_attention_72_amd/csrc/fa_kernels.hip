@@ -136,10 +136,17 @@ struct DmaGeom {
 
 // Scalar load of one 32-bit value at a wave-uniform address.  A vector load
 // would be waited for with vmcnt(0), which also waits for every LDS-DMA load
-// in flight; this waits only for the scalar (and LDS) counter.
+// in flight; this waits only for the scalar (and LDS) counter.  The address is
+// taken from the first lane: callers pass addresses that are uniform by
+// construction, which the compiler cannot always prove (e.g. a sequence index
+// found by a ballot).
 __device__ __forceinline__ int32_t scalar_load_i32(const int32_t* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int32_t* u = reinterpret_cast<const int32_t*>(((uint64_t)hi << 32) | lo);
   int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(u) : "memory");
   return v;
 }
 
@@ -634,10 +641,10 @@ __device__ __forceinline__ void wait_vmcnt_blocks(int n) {
 // the sequence has cache_seqlens[b] keys.  The rows of one LDS-DMA instruction
 // are 1024 / (2 D) consecutive keys starting at a multiple of that count, so
 // with page sizes that are multiples of 16 they lie in one page: one scalar
-// block-table read per instruction.
+// block-table read per instruction.  VARLEN with PAGED is the unified batch:
+// packed queries by cu_seqlens_q, each sequence with its own cache length.
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
-  static_assert(!(VARLEN && PAGED), "a paged cache has its own sequence lengths");
   constexpr int BN = FA_BLOCK_N;  // 32 keys per block
   constexpr int NBUF = 3;  // measured best of 3, 4 and 5 stages
   using G = DmaGeom<D, BN>;
@@ -678,8 +685,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     if (VARLEN) {
       q_start = p.cu_q[tile.b];
       Lq = p.cu_q[tile.b + 1] - (int)q_start;
-      k_start = p.cu_k[tile.b];
-      Lk = p.cu_k[tile.b + 1] - (int)k_start;
+      if (!PAGED) {
+        k_start = p.cu_k[tile.b];
+        Lk = p.cu_k[tile.b + 1] - (int)k_start;
+      }
     }
     if (PAGED) Lk = scalar_load_i32(p.cache_seqlens + tile.b);
     const int kvh = PACK ? tile.hg : tile.hg / p.g;
@@ -1333,7 +1342,9 @@ hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, 
   FA_PF(D_, false, false, true, false) FA_PF(D_, false, false, true, true)                                \
   FA_PF(D_, true, false, false, false) FA_PF(D_, true, false, false, true) FA_PF(D_, true, false, true, false) \
   FA_PF(D_, true, false, true, true) FA_PF(D_, false, true, false, false) FA_PF(D_, false, true, false, true)  \
-  FA_PF(D_, false, true, true, false) FA_PF(D_, false, true, true, true)
+  FA_PF(D_, false, true, true, false) FA_PF(D_, false, true, true, true)                                  \
+  FA_PF(D_, true, true, false, false) FA_PF(D_, true, true, false, true) FA_PF(D_, true, true, true, false)    \
+  FA_PF(D_, true, true, true, true)
   FA_PF_D(128) FA_PF_D(64)
 #undef FA_PF_D
 #undef FA_PF

@@ -136,6 +136,32 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
                          const int64_t v_strides[3], const int64_t o_strides[3],
                          void* stream);
 
+/* Unified prefill + decode batch over a paged KV cache ("Attention kernels ...",
+ * section 5.1: a batch mixes requests that prefill a chunk of hundreds or thousands
+ * of queries with requests that decode one token, all against a cached prefix plus
+ * the new tokens; section 6.1: paged keys).  Sequence b owns the packed query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and the cache_seqlens[b] keys of its pages,
+ * the new tokens' keys included (append them first with fa_kvcache_append); its
+ * queries are bottom-right aligned (query t at key position t + Lk - Lq).
+ *   q        [total_q, heads_q, head_dim]  strides q_strides = {token, head}
+ *   k_cache, v_cache [num_pages, page_size, heads_kv, head_dim]  strides {page, slot, head}
+ *   out      [total_q, heads_q, head_dim]  strides o_strides (written)
+ *   lse      [heads_q, total_q] float32 (written; may be NULL)
+ *   cu_seqlens_q device int32 [batch + 1]; block_table device int32 [batch, max_blocks_per_seq];
+ *   cache_seqlens device int32 [batch]; max_seqlen_q: an upper bound of the query lengths.
+ * One workgroup tile covers 128 packed rows of one sequence (no split-KV).  Errors:
+ * FA_ERR_UNSUPPORTED for a page_size that is not a multiple of 16.  Caller contract,
+ * not checked on the device: cu_seqlens_q non-decreasing from 0 with
+ * cu_seqlens_q[batch] == total_q, query lengths <= max_seqlen_q, live block-table
+ * entries in [0, num_pages), cache_seqlens[b] <= max_blocks_per_seq * page_size. */
+int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_cache,
+                        const void* v_cache, void* out, float* lse, const int32_t* cu_seqlens_q,
+                        const int32_t* block_table, const int32_t* cache_seqlens, int batch,
+                        int max_seqlen_q, int total_q, int heads_q, int heads_kv, int head_dim,
+                        int64_t num_pages, int page_size, int max_blocks_per_seq,
+                        const int64_t q_strides[2], const int64_t k_strides[3],
+                        const int64_t v_strides[3], const int64_t o_strides[2], void* stream);
+
 /* Split count of fa_fwd_kvcache_paged for num_splits == 0 (host only, no device
  * work; it reads the current device's compute-unit count): about 32
  * workgroups per compute unit over batch * heads_kv, at most 64 and at most

@@ -278,3 +278,68 @@ def test_paged_prefill_full_size_sampled():
     want = torch.arange(Nq, dtype=torch.float64) + (c["prefix"] + 1)
     got = torch.round(torch.exp(lse0.double().cpu()))
     assert torch.equal(got, want.view(1, 1, -1).expand_as(got))
+
+
+# ---------------------------------------------------------------- unified prefill + decode batch
+def _varlen_paged_case(seed, qlens, lens, Hq, Hkv, d, page, mult=1.0):
+    t = W.paged(seed, len(lens), Hq, Hkv, d, page, 0, 0, cache_seqlens=lens, mult=mult)
+    g = W.generator(seed + 5)
+    t["q"] = W.randn_bf16(g, (sum(qlens), Hq, d), mult)
+    t["cu_q"] = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32)
+    return t
+
+
+def _ref_varlen_paged(t, kc=None, vc=None, **kw):
+    kc = t["k_cache"] if kc is None else kc
+    vc = t["v_cache"] if vc is None else vc
+    q, cu = t["q"], t["cu_q"].tolist()
+    Tq, Hq, d = q.shape
+    o = np.zeros((Tq, Hq, d))
+    lse = np.full((Hq, Tq), -np.inf)
+    bt, lens = t["block_table"].numpy(), t["cache_seqlens"].numpy()
+    for b in range(len(cu) - 1):
+        a, e = cu[b], cu[b + 1]
+        if e > a:   # each sequence is a batch-1 paged call of its own
+            ob, lb = oracle.fwd_paged(bits(q[a:e].unsqueeze(0)), bits(kc), bits(vc), bt[b:b + 1],
+                                      lens[b:b + 1], **kw)
+            o[a:e], lse[:, a:e] = ob[0], lb[0]
+    return o, lse
+
+
+def _run_varlen_paged(t, kc, vc, **kw):
+    qlens = (t["cu_q"][1:] - t["cu_q"][:-1])
+    out, lse = api.fa_fwd_varlen_paged(t["q"].to(DEV), kc.to(DEV), vc.to(DEV), t["cu_q"].to(DEV),
+                                       int(qlens.max()), t["block_table"].to(DEV),
+                                       t["cache_seqlens"].to(DEV), **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("qlens,lens,Hq,Hkv,d,page,pack", [
+    ([1, 1, 37, 300, 1, 129, 0], [1000, 17, 400, 300, 5000, 2000, 50], 8, 2, 128, 16, -1),
+    ([1, 1, 37, 300, 1, 129, 0], [1000, 17, 400, 300, 5000, 2000, 50], 8, 2, 128, 16, 0),
+    ([64, 1, 500], [64, 4000, 600], 4, 4, 64, 256, -1),
+    ([50, 3], [10, 3], 2, 1, 128, 32, -1),                  # more queries than keys
+])
+def test_varlen_paged_mixed_batch(qlens, lens, Hq, Hkv, d, page, pack):
+    t = _varlen_paged_case(91 + len(qlens) + d, qlens, lens, Hq, Hkv, d, page)
+    kc, vc = poison_unused(t)
+    out, lse = _run_varlen_paged(t, kc, vc, causal=True, pack_gqa=pack)
+    o_ref, l_ref = _ref_varlen_paged(t, causal=True)
+    check_close(out, lse, o_ref, l_ref, f"varlen paged qlens={qlens}")
+
+
+def test_varlen_paged_window_softcap_and_count():
+    qlens, lens = [1, 200, 33], [999, 250, 33]
+    t = _varlen_paged_case(97, qlens, lens, 8, 2, 128, 32, mult=2.0)
+    kw = dict(causal=True, window=(100, 0), softcap=30.0)
+    out, lse = _run_varlen_paged(t, t["k_cache"], t["v_cache"], **kw)
+    o_ref, l_ref = _ref_varlen_paged(t, **kw)
+    check_close(out, lse, o_ref, l_ref, "varlen paged window+softcap")
+    t0 = dict(t, q=torch.zeros_like(t["q"]))
+    _, lse0 = _run_varlen_paged(t0, t["k_cache"], t["v_cache"], causal=True)
+    cu = t["cu_q"].tolist()
+    for b, (Lq, Lk) in enumerate(zip(qlens, lens)):
+        want = torch.tensor([max(0, min(Lk, i + Lk - Lq + 1)) for i in range(Lq)], dtype=torch.long)
+        got = torch.round(torch.exp(lse0[:, cu[b]:cu[b + 1]].double().cpu())).long()
+        assert torch.equal(got, want.view(1, -1).expand_as(got)), f"count probe, sequence {b}"

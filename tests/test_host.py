@@ -233,3 +233,16 @@ def test_append_rejects_invalid_arguments():
     assert call(page=0) == FA_ERR_INVALID_ARG
     assert call(ks=(ctypes.c_int64 * 3)(2048, 2050, 128)) == FA_ERR_INVALID_ARG
     assert call(Ln=0) == 0                                           # nothing to write, no launch
+
+
+def test_varlen_paged_rejects_invalid_arguments():
+    L = api.lib()
+    o = _opts(causal=1)
+    def call(cu=FAKE, d=128, B=2, page=16, Hq=32, Hkv=8):
+        return L.fa_fwd_varlen_paged(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None, cu, FAKE, FAKE, B, 64,
+                                     100, Hq, Hkv, d, 100, page, 10, S2, S3, S3, S2, None)
+    assert call(cu=None) == FA_ERR_INVALID_ARG
+    assert call(d=80) == FA_ERR_UNSUPPORTED
+    assert call(B=0) == FA_ERR_INVALID_ARG
+    assert call(page=24) == FA_ERR_UNSUPPORTED
+    assert call(Hq=30) == FA_ERR_INVALID_ARG
