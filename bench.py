@@ -8,7 +8,8 @@ the varlen GQA prefill (32 sequences of 64..8192 tokens, 32/4 heads, packed),
 the long-context local attention with softcap (N = 32768, 32 heads,
 window 4096, softcap 30), and the chunked prefill over a paged cache (4 x 4096
 new tokens against 16384 cached keys, 32/8 heads) with the in-place K/V append
-of that chunk.
+of that chunk, and a unified batch of 64 decode requests and 4 prefill chunks
+in one launch.
 
 Prints one JSON line:
   value        prefill TFLOP/s, FLOPs counted as 4 * B * H * N^2 * d * 1/2 (the
@@ -214,6 +215,35 @@ def bench_paged_prefill(api, W, steps, warmup):
                                   "page_size": c["page"]}}}
 
 
+def bench_unified(api, W, steps, warmup):
+    """One launch over a mixed batch (fa_fwd_varlen_paged): 64 decode requests with one new
+    token and 4 prefill chunks of 2048 tokens, 32/8 heads, 256-token pages.  FLOPs on visible
+    pairs, 4 d Hq sum over queries of the keys each sees."""
+    import torch
+    name = "unified_decode64_chunk4x2048_h32kv8_d128_page256"
+    c = W.WORKLOADS[name]
+    t = W.varlen_paged(c["seed"], c["n_decode"], c["dec_lo"], c["dec_hi"], c["n_chunk"], c["chunk"],
+                       c["pre_lo"], c["pre_hi"], c["Hq"], c["Hkv"], c["d"], c["page"], device="cuda")
+    pairs = 0
+    for Lq, Lk in zip(t["qlens"], t["cache_seqlens"].tolist()):
+        pairs += sum(min(Lk, i + Lk - Lq + 1) for i in range(Lq))
+    flops = 4.0 * c["d"] * c["Hq"] * pairs
+    cu, bt, sl = t["cu_seqlens_q"].cuda(), t["block_table"].cuda(), t["cache_seqlens"].cuda()
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((c["Hq"], t["q"].shape[0]), dtype=torch.float32, device="cuda")
+    fn = lambda: api.fa_fwd_varlen_paged(t["q"], t["k_cache"], t["v_cache"], cu, c["chunk"], bt, sl,  # noqa
+                                         causal=True, out=out, lse=lse)
+    wall, ms = time_launches(fn, steps, warmup)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"metric": "unified prefill+decode batch TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
+            "kernel_ms": round(ms, 4), "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
+            "config": {"workload": name, "decode_requests": c["n_decode"], "chunks": c["n_chunk"],
+                       "chunk": c["chunk"], "heads_q": c["Hq"], "heads_kv": c["Hkv"], "head_dim": c["d"],
+                       "page_size": c["page"], "flop_convention": "4*d*Hq*sum visible pairs"}}
+
+
 def bench_decode(api, W, steps, warmup):
     import torch
     c = W.WORKLOADS["paged_decode_b64_h32kv8_d128_page256"]
@@ -258,6 +288,7 @@ def main():
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-local", action="store_true")
     ap.add_argument("--no-paged-prefill", action="store_true")
+    ap.add_argument("--no-unified", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -316,6 +347,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_paged_prefill:
         line["paged_prefill"] = bench_paged_prefill(api, W, max(10, args.steps // 5), max(5, args.warmup // 5))
+        torch.cuda.empty_cache()
+    if not args.no_unified:
+        line["unified"] = bench_unified(api, W, max(10, args.steps // 5), max(5, args.warmup // 5))
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         tc = W.dense(c["seed"], B, N, H, c["Hkv"], d)

@@ -23,6 +23,8 @@ KV ("Attention kernels: FlashAttention and PagedAttention", sections 6.1 and
 """
 from __future__ import annotations
 
+import itertools
+
 import numpy as np
 import torch
 
@@ -49,6 +51,12 @@ WORKLOADS = {
     "paged_prefill_b4_h32kv8_d128_chunk4096_prefix12288_page256": dict(
         kind="paged_prefill", B=4, Hq=32, Hkv=8, d=128, page=256, Nq=4096, prefix=12288,
         max_blocks=64, causal=True, window=(-1, -1), softcap=0.0, mult=1.0, seed=6),
+    # one launch for a mixed batch: 64 decode requests (1 new token, 1024..8192 cached keys)
+    # and 4 prefill chunks (2048 new tokens on a 0..8192-token prefix), 32/8 heads
+    "unified_decode64_chunk4x2048_h32kv8_d128_page256": dict(
+        kind="varlen_paged", n_decode=64, dec_lo=1024, dec_hi=8192, n_chunk=4, chunk=2048,
+        pre_lo=0, pre_hi=8192, Hq=32, Hkv=8, d=128, page=256, causal=True, window=(-1, -1),
+        softcap=0.0, mult=1.0, seed=7),
 }
 
 
@@ -138,3 +146,22 @@ def to_bits(t: torch.Tensor) -> np.ndarray:
 def from_float(x, device="cpu") -> torch.Tensor:
     """A float array -> bfloat16 tensor (round-to-nearest-even)."""
     return torch.as_tensor(np.asarray(x, dtype=np.float32), device=device).to(torch.bfloat16)
+
+
+def varlen_paged(seed, n_decode, dec_lo, dec_hi, n_chunk, chunk, pre_lo, pre_hi, Hq, Hkv, d, page, *,
+                 mult=1.0, device="cpu"):
+    """A mixed batch over a paged cache: n_decode sequences with one query token and
+    uniform [dec_lo, dec_hi] cached keys (the token's own key included), then n_chunk
+    sequences with `chunk` query tokens on a uniform [pre_lo, pre_hi] prefix.
+    q [total_q, Hq, d] packed by cu_seqlens_q; caches, block_table, cache_seqlens as paged()."""
+    g = generator(seed)
+    dec = torch.randint(dec_lo, dec_hi + 1, (n_decode,), generator=g)
+    pre = torch.randint(pre_lo, pre_hi + 1, (n_chunk,), generator=g)
+    qlens = [1] * n_decode + [chunk] * n_chunk
+    lens = dec.tolist() + (pre + chunk).tolist()
+    t = paged(seed + 11, len(lens), Hq, Hkv, d, page, 0, 0, cache_seqlens=lens, mult=mult, device=device)
+    gq = generator(seed + 13, device)
+    t["q"] = randn_bf16(gq, (sum(qlens), Hq, d), mult, device)
+    t["cu_seqlens_q"] = torch.tensor([0] + list(itertools.accumulate(qlens)), dtype=torch.int32)
+    t["qlens"] = qlens
+    return t

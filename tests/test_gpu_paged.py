@@ -343,3 +343,35 @@ def test_varlen_paged_window_softcap_and_count():
         want = torch.tensor([max(0, min(Lk, i + Lk - Lq + 1)) for i in range(Lq)], dtype=torch.long)
         got = torch.round(torch.exp(lse0[:, cu[b]:cu[b + 1]].double().cpu())).long()
         assert torch.equal(got, want.view(1, -1).expand_as(got)), f"count probe, sequence {b}"
+
+
+def test_unified_batch_full_size():
+    """The mixed batch the benchmark times: every decode row and sampled chunk rows against
+    the oracle (each sequence a batch-1 paged call), in the same launch configuration."""
+    c = W.WORKLOADS["unified_decode64_chunk4x2048_h32kv8_d128_page256"]
+    t = W.varlen_paged(c["seed"], c["n_decode"], c["dec_lo"], c["dec_hi"], c["n_chunk"], c["chunk"],
+                       c["pre_lo"], c["pre_hi"], c["Hq"], c["Hkv"], c["d"], c["page"])
+    out, lse = api.fa_fwd_varlen_paged(t["q"].to(DEV), t["k_cache"].to(DEV), t["v_cache"].to(DEV),
+                                       t["cu_seqlens_q"].to(DEV), c["chunk"], t["block_table"].to(DEV),
+                                       t["cache_seqlens"].to(DEV), causal=True)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    Hq = c["Hq"]
+    bt, lens, cu = t["block_table"].numpy(), t["cache_seqlens"].numpy(), t["cu_seqlens_q"].tolist()
+    kb, vb = bits(t["k_cache"]), bits(t["v_cache"])
+    rng = np.random.default_rng(7)
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for b in range(len(lens)):
+        a, e = cu[b], cu[b + 1]
+        Lq = e - a
+        rows = np.arange(Hq * Lq) if Lq == 1 else np.unique(np.concatenate(
+            [rng.integers(0, Hq * Lq, 40), [0, Lq - 1, Hq * Lq - 1]]))   # row = h * Lq + i
+        ob, lb = oracle.fwd_paged(bits(t["q"][a:e].unsqueeze(0)), kb, vb, bt[b:b + 1], lens[b:b + 1],
+                                  causal=True, rows=rows)
+        h, i = rows // Lq, rows % Lq
+        got_o.append(out[a + torch.as_tensor(i), torch.as_tensor(h)])
+        got_l.append(lse[torch.as_tensor(h), a + torch.as_tensor(i)])
+        ref_o.append(ob)
+        ref_l.append(lb)
+    check_close(torch.cat(got_o), torch.cat(got_l), np.concatenate(ref_o), np.concatenate(ref_l),
+                "unified batch full size")
