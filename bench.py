@@ -200,6 +200,14 @@ def bench_paged_prefill(api, W, steps, warmup):
     _, ms_a = time_launches(fa, steps, min(warmup, 50))
     moved = 2.0 * 2 * kn.numel() * 2          # K and V, read once and written once, bf16
     gbs = moved / (ms_a * 1e-3) / 1e9
+    # the same append with the keys rotated on the way (full head_dim, 10000^(-2i/d) frequencies)
+    r = c["d"]
+    theta = 10000.0 ** (-2.0 * torch.arange(r // 2, dtype=torch.float64, device="cuda") / r)
+    ang = torch.arange(P + Nq, dtype=torch.float64, device="cuda")[:, None] * theta[None, :]
+    cos, sin = torch.cos(ang).float(), torch.sin(ang).float()
+    fr = lambda: api.fa_kvcache_append(kn, vn, t["k_cache"], t["v_cache"], bt, start,  # noqa
+                                       rotary_cos=cos, rotary_sin=sin)
+    _, ms_r = time_launches(fr, steps, min(warmup, 50))
     return {"metric": "chunked prefill over a paged cache TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
             "kernel_ms": round(ms, 4), "flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
@@ -209,6 +217,8 @@ def bench_paged_prefill(api, W, steps, warmup):
                        "num_splits": 0, "flop_convention": "4*d*Hq*B*sum_i(prefix+i+1)"},
             "append": {"metric": "K/V append GB/s (read + write)", "unit": "GB/s", "value": round(gbs, 1),
                        "kernel_ms": round(ms_a, 4), "bytes": moved,
+                       "rotary_kernel_ms": round(ms_r, 4),
+                       "rotary_GBps": round(moved / (ms_r * 1e-3) / 1e9, 1),
                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
                        "config": {"tokens": B * Nq, "heads_kv": c["Hkv"], "head_dim": c["d"],

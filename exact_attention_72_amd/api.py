@@ -22,7 +22,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
 EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_varlen_paged", "fa_kvcache_num_splits",
-           "fa_kvcache_workspace_size", "fa_kvcache_append",
+           "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary",
            "fa_combine", "fa_tile_class", "fa_last_error", "fa_version")
 
 
@@ -61,14 +61,15 @@ def lib():
     L.fa_kvcache_num_splits.argtypes = [I, I, I, I, I, I]
     L.fa_kvcache_num_splits.restype = I
     L.fa_combine.argtypes = [P, P, I, I64, I, P, I64, P, P]
-    L.fa_kvcache_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I64, I, I, S3, S3, S3, S3, P]
+    L.fa_kvcache_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I64, I, I, S3, S3, S3, S3, P, P, I, I, P]
+    L.fa_rotary.argtypes = [P, I, I, I, I, S3, P, P, P, I, I, P]
     L.fa_fwd_varlen_paged.argtypes = [OPT, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I64, I, I, S3, S3, S3,
                                       S3, P]
     L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = I
     for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_combine", "fa_tile_class",
-                 "fa_kvcache_append", "fa_fwd_varlen_paged"):
+                 "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -227,9 +228,39 @@ def fa_fwd_varlen_paged(q, k_cache, v_cache, cu_seqlens_q, max_seqlen_q, block_t
     return out, lse
 
 
-def fa_kvcache_append(k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, *, stream=None):
+def _rotary_tables(cos, sin):
+    if cos is None and sin is None:
+        return None, None, 0
+    if cos is None or sin is None:
+        raise ValueError("rotary cos and sin go together")
+    for c in (cos, sin):
+        if c.dtype != torch.float32 or not c.is_cuda or not c.is_contiguous() or c.dim() != 2:
+            raise TypeError("rotary tables must be contiguous float32 [positions, rotary_dim / 2] device tensors")
+    if cos.shape != sin.shape:
+        raise ValueError("rotary cos and sin shapes differ")
+    return cos, sin, 2 * cos.shape[1]
+
+
+def fa_rotary(x, cos, sin, *, position_base=None, interleaved=False, stream=None):
+    """In place: rotate x [B, L, H, d] (bf16) at positions position_base[b] + t (0 + t
+    without a base) with the fp32 tables cos/sin [positions, rotary_dim / 2]."""
+    _bf16_cuda(x)
+    B, L, H, d = x.shape
+    cos, sin, rdim = _rotary_tables(cos, sin)
+    if cos is None:
+        raise ValueError("fa_rotary needs cos and sin tables")
+    if position_base is not None and (position_base.dtype != torch.int32 or not position_base.is_cuda):
+        raise TypeError("position_base must be an int32 device tensor")
+    _check(lib().fa_rotary(_ptr(x), B, L, H, d, _strides(x, (0, 1, 2)), _ptr(position_base), _ptr(cos),
+                           _ptr(sin), rdim, int(bool(interleaved)), _stream(stream)))
+    return x
+
+
+def fa_kvcache_append(k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, *, rotary_cos=None,
+                      rotary_sin=None, rotary_interleaved=False, stream=None):
     """Write k_new/v_new [B, L, Hkv, d] into the paged caches [num_pages, page, Hkv, d]
-    at logical positions cache_seqlens[b] + t (in place; cache_seqlens is not updated)."""
+    at logical positions cache_seqlens[b] + t (in place; cache_seqlens is not updated).
+    With rotary tables the keys are rotated at those positions on the way in."""
     _bf16_cuda(k_new, v_new, k_cache, v_cache)
     B, L, Hkv, d = k_new.shape
     if tuple(v_new.shape) != (B, L, Hkv, d) or k_cache.shape != v_cache.shape or k_cache.shape[2:] != (Hkv, d):
@@ -239,11 +270,13 @@ def fa_kvcache_append(k_new, v_new, k_cache, v_cache, block_table, cache_seqlens
             raise TypeError("block_table and cache_seqlens must be int32 device tensors")
     if block_table.stride(-1) != 1 or block_table.stride(0) != block_table.shape[1]:
         raise ValueError("block_table must be a contiguous [batch, max_blocks] tensor")
+    cos, sin, rdim = _rotary_tables(rotary_cos, rotary_sin)
     _check(lib().fa_kvcache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                    _ptr(block_table), _ptr(cache_seqlens), B, L, Hkv, d,
                                    k_cache.shape[0], k_cache.shape[1], block_table.shape[1],
                                    _strides(k_new, (0, 1, 2)), _strides(v_new, (0, 1, 2)),
                                    _strides(k_cache, (0, 1, 2)), _strides(v_cache, (0, 1, 2)),
+                                   _ptr(cos), _ptr(sin), rdim, int(bool(rotary_interleaved)),
                                    _stream(stream)))
 
 

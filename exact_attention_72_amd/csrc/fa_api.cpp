@@ -71,6 +71,23 @@ int check_strides(const char* name, const void* base, const int64_t* s, int n) {
   return FA_OK;
 }
 
+// Rotary tables: both or neither; rotated dims a multiple of 16, at most head_dim.
+int check_rotary(const float* cos, const float* sin, int dim, int interleaved, int head_dim, FaRotary* r) {
+  r->cos = nullptr;
+  r->sin = nullptr;
+  r->dim = 0;
+  r->interleaved = 0;
+  if (!cos && !sin) return FA_OK;
+  if (!cos || !sin) return fail(FA_ERR_INVALID_ARG, "rotary cos and sin tables go together");
+  if (dim < 16 || dim > head_dim || dim % 16 != 0)
+    return fail(FA_ERR_INVALID_ARG, "rotary_dim %d must be a multiple of 16 in [16, head_dim]", dim);
+  r->cos = cos;
+  r->sin = sin;
+  r->dim = dim;
+  r->interleaved = interleaved ? 1 : 0;
+  return FA_OK;
+}
+
 bool resolve_pack(const fa_attn_opts* o, int hq, int hkv) {
   if (o->pack_gqa > 0) return true;
   if (o->pack_gqa == 0) return false;
@@ -370,7 +387,8 @@ int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void*
                       const int32_t* block_table, const int32_t* cache_seqlens, int batch, int seqlen_new,
                       int heads_kv, int head_dim, int64_t num_pages, int page_size, int max_blocks_per_seq,
                       const int64_t kn_strides[3], const int64_t vn_strides[3], const int64_t k_strides[3],
-                      const int64_t v_strides[3], void* stream) {
+                      const int64_t v_strides[3], const float* rotary_cos, const float* rotary_sin,
+                      int rotary_dim, int rotary_interleaved, void* stream) {
   g_err[0] = 0;
   int rc;
   if (head_dim != 64 && head_dim != 128)
@@ -385,6 +403,8 @@ int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void*
   if ((rc = check_strides("k_new", k_new, kn_strides, 3)) || (rc = check_strides("v_new", v_new, vn_strides, 3)) ||
       (rc = check_strides("k_cache", k_cache, k_strides, 3)) || (rc = check_strides("v_cache", v_cache, v_strides, 3)))
     return rc;
+  FaRotary rot;
+  if ((rc = check_rotary(rotary_cos, rotary_sin, rotary_dim, rotary_interleaved, head_dim, &rot))) return rc;
   if (seqlen_new == 0) return FA_OK;
   FaAppendParams p;
   memset(&p, 0, sizeof p);
@@ -399,8 +419,35 @@ int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void*
   p.block_table = block_table;
   p.cache_seqlens = cache_seqlens;
   p.B = batch; p.L = seqlen_new; p.Hkv = heads_kv; p.page = page_size; p.max_blocks = max_blocks_per_seq;
+  p.rot = rot;
   hipError_t e = fa_launch_append(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
+  return FA_OK;
+}
+
+int fa_rotary(void* x, int batch, int seqlen, int heads, int head_dim, const int64_t x_strides[3],
+              const int32_t* position_base, const float* cos, const float* sin, int rotary_dim, int interleaved,
+              void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!x || !cos || !sin) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || seqlen < 0 || heads <= 0)
+    return fail(FA_ERR_INVALID_ARG, "batch and heads must be positive, seqlen >= 0");
+  if ((rc = check_strides("x", x, x_strides, 3))) return rc;
+  FaRotary rot;
+  if ((rc = check_rotary(cos, sin, rotary_dim, interleaved, head_dim, &rot))) return rc;
+  if (seqlen == 0) return FA_OK;
+  FaRotaryParams p;
+  memset(&p, 0, sizeof p);
+  p.x = static_cast<uint16_t*>(x);
+  p.bs = x_strides[0]; p.ss = x_strides[1]; p.hs = x_strides[2];
+  p.pos_base = position_base;
+  p.B = batch; p.L = seqlen; p.H = heads;
+  p.rot = rot;
+  hipError_t e = fa_launch_rotary(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rotary launch");
   return FA_OK;
 }
 

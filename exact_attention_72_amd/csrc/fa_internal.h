@@ -42,6 +42,26 @@ struct FaParams {
   int causal, wl, wr;
 };
 
+// Rotary position embedding from caller tables: position pos, frequency i
+// rotates the pair of dims (i, i + dim / 2) (or (2i, 2i + 1) when interleaved)
+// by cos[pos * dim / 2 + i], sin[pos * dim / 2 + i].
+struct FaRotary {
+  const float* cos;  // [positions, dim / 2] fp32; NULL = no rotation
+  const float* sin;
+  int dim;           // rotated head dims, a multiple of 16, <= head_dim
+  int interleaved;
+};
+
+// In-place rotation of x [B, L, H, head_dim]; token t of sequence b sits at
+// position (pos_base ? pos_base[b] : 0) + t.
+struct FaRotaryParams {
+  uint16_t* x;
+  int64_t bs, ss, hs;
+  const int32_t* pos_base;
+  int B, L, H;
+  FaRotary rot;
+};
+
 // In-place append of new K/V tokens to a paged cache.
 struct FaAppendParams {
   const uint16_t* k_new;
@@ -55,6 +75,7 @@ struct FaAppendParams {
   const int32_t* block_table;
   const int32_t* cache_seqlens;  // lengths before the append
   int B, L, Hkv, page, max_blocks;
+  FaRotary rot;                  // applied to the keys (rot.cos == NULL: none)
 };
 
 struct FaCombineParams {
@@ -77,6 +98,7 @@ hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, 
 hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t stream);
 hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_append(const FaAppendParams& p, int d, hipStream_t stream);
+hipError_t fa_launch_rotary(const FaRotaryParams& p, int d, hipStream_t stream);
 
 // Tile geometry of the prefill kernel.
 constexpr int FA_BLOCK_M = 128;     // query rows per workgroup tile (4 waves x 32)

@@ -1242,13 +1242,81 @@ __global__ __launch_bounds__(kThreads) void fa_combine_kernel(FaCombineParams p)
   if (lane == 0 && p.lse) p.lse[r] = empty ? kNegInf : M + __builtin_logf(W);
 }
 
-// ------------------------------------------------------------------ K/V append
+// ------------------------------------------------------------------ rotary embedding, K/V append
+// Rotary position embedding of one 16-byte chunk (8 dims) of a bf16 row at
+// position pos, from the caller's cos/sin tables (the rotation the kvcache call
+// can apply on the way into the cache, "FA4 ...", section 6.2; which pairs of
+// dims rotate together is the caller's choice, see FaRotary).  src and dst are
+// the row (they may alias).  Chunk c of a half-split rotation also owns its
+// partner chunk c + dim / 16; the partner's own call does nothing.  fp32
+// arithmetic, round-to-nearest-even to bf16.
+template <int D>
+__device__ __forceinline__ void rope_chunk(const uint16_t* src, uint16_t* dst, int c, int pos, const FaRotary& r) {
+  typedef float f32x8_ __attribute__((ext_vector_type(8)));
+  const int half = r.dim / 2;
+  const float* cs = r.cos + (int64_t)pos * half;
+  const float* sn = r.sin + (int64_t)pos * half;
+  auto load = [&](int cc) {
+    return __builtin_convertvector(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 8 * cc)), f32x8_);
+  };
+  auto store = [&](int cc, f32x8_ x) {
+    *reinterpret_cast<u32x4*>(dst + 8 * cc) = __builtin_bit_cast(u32x4, __builtin_convertvector(x, bf16x8));
+  };
+  if (8 * c >= r.dim) {  // past the rotated dims: copy
+    if (src != dst) *reinterpret_cast<u32x4*>(dst + 8 * c) = *reinterpret_cast<const u32x4*>(src + 8 * c);
+    return;
+  }
+  if (r.interleaved) {  // pairs (2i, 2i + 1) inside the chunk, i = 4 c + j
+    f32x8_ x = load(c), y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float co = cs[4 * c + j], si = sn[4 * c + j];
+      y[2 * j] = x[2 * j] * co - x[2 * j + 1] * si;
+      y[2 * j + 1] = x[2 * j] * si + x[2 * j + 1] * co;
+    }
+    store(c, y);
+    return;
+  }
+  if (8 * c >= half) return;  // written by the chunk c - dim / 16
+  const int c2 = c + half / 8;
+  f32x8_ a = load(c), b = load(c2), a2, b2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // pairs (i, i + dim / 2), i = 8 c + j
+    const float co = cs[8 * c + j], si = sn[8 * c + j];
+    a2[j] = a[j] * co - b[j] * si;
+    b2[j] = a[j] * si + b[j] * co;
+  }
+  store(c, a2);
+  store(c2, b2);
+}
+
+// In-place rotary embedding of a [B, L, H, D] tensor (the new queries of a
+// kvcache step), one thread per 16-byte chunk.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa_rotary_kernel(FaRotaryParams p) {
+  constexpr int C = D / 8;
+  const int64_t total = (int64_t)p.B * p.L * p.H * C;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
+    const int c = (int)(i % C);
+    int64_t r = i / C;
+    const int h = (int)(r % p.H);
+    r /= p.H;
+    const int t = (int)(r % p.L);
+    const int b = (int)(r / p.L);
+    const int pos = (p.pos_base ? p.pos_base[b] : 0) + t;
+    uint16_t* row = p.x + b * p.bs + t * p.ss + h * p.hs;
+    rope_chunk<D>(row, row, c, pos, p.rot);
+  }
+}
+
 // Incremental decoding writes the new keys and values into the cache in place
 // ("FA4 ...", section 6.2): token t of sequence b goes to logical position
 // cache_seqlens[b] + t, i.e. slot pos % page of page block_table[b][pos / page]
-// ("Attention kernels...", section 6.1).  A plain copy, bound by memory: one
-// thread per 16-byte chunk of a row, consecutive threads on consecutive chunks
-// of a row and then of the next head, so a wave writes whole rows.
+// ("Attention kernels...", section 6.1); the keys optionally rotated on the
+// way.  Bound by memory: one thread per 16-byte chunk of a row, consecutive
+// threads on consecutive chunks of a row and then of the next head, so a wave
+// writes whole rows.
 template <int D>
 __global__ __launch_bounds__(kThreads) void fa_append_kernel(FaAppendParams p) {
   constexpr int C = D / 8;  // 16-byte chunks per row
@@ -1264,18 +1332,18 @@ __global__ __launch_bounds__(kThreads) void fa_append_kernel(FaAppendParams p) {
     const int pos = p.cache_seqlens[b] + t;
     const int64_t phys = p.block_table[(int64_t)b * p.max_blocks + pos / p.page];
     const int64_t slot = pos % p.page;
-    const u32x4 kx = *reinterpret_cast<const u32x4*>(p.k_new + b * p.kn_bs + t * p.kn_ss + h * p.kn_hs + 8 * c);
+    const uint16_t* ks = p.k_new + b * p.kn_bs + t * p.kn_ss + h * p.kn_hs;
+    uint16_t* kd = p.k_cache + phys * p.k_ps + slot * p.k_ss + h * p.k_hs;
+    if (p.rot.cos)
+      rope_chunk<D>(ks, kd, c, pos, p.rot);
+    else
+      *reinterpret_cast<u32x4*>(kd + 8 * c) = *reinterpret_cast<const u32x4*>(ks + 8 * c);
     const u32x4 vx = *reinterpret_cast<const u32x4*>(p.v_new + b * p.vn_bs + t * p.vn_ss + h * p.vn_hs + 8 * c);
-    *reinterpret_cast<u32x4*>(p.k_cache + phys * p.k_ps + slot * p.k_ss + h * p.k_hs + 8 * c) = kx;
     *reinterpret_cast<u32x4*>(p.v_cache + phys * p.v_ps + slot * p.v_ss + h * p.v_hs + 8 * c) = vx;
   }
 }
 
 // ------------------------------------------------------------------ launch helpers
-struct DeviceInfo {
-  int cus = 0;
-};
-
 int device_cus() {
   static thread_local int cached_dev = -1;
   static thread_local int cached_cus = 0;
@@ -1379,6 +1447,21 @@ hipError_t fa_launch_append(const FaAppendParams& p, int d, hipStream_t s) {
     hipLaunchKernelGGL(fa_append_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else if (d == 64)
     hipLaunchKernelGGL(fa_append_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t fa_launch_rotary(const FaRotaryParams& p, int d, hipStream_t s) {
+  const int64_t total = (int64_t)p.B * p.L * p.H * (d / 8);
+  if (total <= 0) return hipSuccess;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  const int64_t cap = 16 * (int64_t)device_cus();
+  if (blocks > cap) blocks = cap;
+  if (d == 128)
+    hipLaunchKernelGGL(fa_rotary_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else if (d == 64)
+    hipLaunchKernelGGL(fa_rotary_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -186,16 +186,38 @@ size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_
  *   block_table       device int32 [batch, max_blocks_per_seq]
  *   cache_seqlens     device int32 [batch]: lengths before the append (read, not updated;
  *                     attend afterwards with cache_seqlens[b] + seqlen_new keys)
- * seqlen_new == 0 is a no-op.  Caller contract, not checked on the device:
- * cache_seqlens[b] + seqlen_new <= max_blocks_per_seq * page_size, the pages those
- * positions map to lie in [0, num_pages), and no two sequences map a written
- * position to the same slot. */
+ *   rotary_cos, rotary_sin  NULL, or fp32 [positions, rotary_dim / 2] tables: the keys are
+ *                     rotated on the way in, as fa_rotary does, at their cache position
+ *                     cache_seqlens[b] + t (the values are copied as they are)
+ * seqlen_new == 0 is a no-op.  Errors: FA_ERR_INVALID_ARG for one table without the
+ * other or a rotary_dim that is not a multiple of 16 in [16, head_dim].  Caller
+ * contract, not checked on the device: cache_seqlens[b] + seqlen_new <=
+ * max_blocks_per_seq * page_size (and <= the tables' positions), the pages those
+ * positions map to lie in [0, num_pages), and no two sequences map a written position
+ * to the same slot. */
 int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                       const int32_t* block_table, const int32_t* cache_seqlens, int batch,
                       int seqlen_new, int heads_kv, int head_dim, int64_t num_pages,
                       int page_size, int max_blocks_per_seq, const int64_t kn_strides[3],
                       const int64_t vn_strides[3], const int64_t k_strides[3],
-                      const int64_t v_strides[3], void* stream);
+                      const int64_t v_strides[3], const float* rotary_cos,
+                      const float* rotary_sin, int rotary_dim, int rotary_interleaved,
+                      void* stream);
+
+/* In-place rotary position embedding of x [batch, seqlen, heads, head_dim] (bf16,
+ * strides x_strides = {batch, seq, head}), for the new queries of a kvcache step
+ * ("FA4 ...", section 6.2: the kvcache call can apply the rotary embedding on the
+ * way).  Token t of sequence b sits at position (position_base ? position_base[b] :
+ * 0) + t.  Frequency i of that position rotates a pair of dims by the angle whose
+ * cosine and sine are cos[pos * rotary_dim / 2 + i] and sin[...] (fp32 tables
+ * [positions, rotary_dim / 2], chosen by the caller):
+ *   interleaved == 0: dims (i, i + rotary_dim / 2);  interleaved != 0: dims (2i, 2i + 1);
+ *   (a, b) -> (a cos - b sin, a sin + b cos), fp32, rounded to bf16 (nearest even).
+ * Dims at and past rotary_dim are unchanged.  rotary_dim: a multiple of 16 in
+ * [16, head_dim].  Caller contract: every position is a row of the tables. */
+int fa_rotary(void* x, int batch, int seqlen, int heads, int head_dim,
+              const int64_t x_strides[3], const int32_t* position_base, const float* cos,
+              const float* sin, int rotary_dim, int interleaved, void* stream);
 
 /* Merge of partial attention states ("Attention kernels ...", section 6.3: the
  * partial (O_s, LSE_s) of disjoint key ranges combine with the same rescale as

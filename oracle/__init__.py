@@ -276,3 +276,34 @@ def kvcache_append(k_new, v_new, k_cache, v_cache, block_table, cache_seqlens):
             kc[phys, pos % page] = k_new[b, t]
             vc[phys, pos % page] = v_new[b, t]
     return kc, vc
+
+
+def rotary(x, cos, sin, positions, *, interleaved=False):
+    """Rotary position embedding in fp64, from its definition (RoFormer, Su et al.
+    2021: a position rotates each pair of dims by its angle; the pages only say the
+    kvcache call can apply it, "FA4 (CuTeDSL) and engineering interfaces", section 6.2).
+
+    x: uint16 bf16 bits [..., L, H, d]; cos, sin: float [positions, r/2]; positions:
+    int [..., L] (the position of each token).  Frequency i of position p rotates the
+    pair of dims (i, i + r/2) (or (2i, 2i + 1) when interleaved) by the angle with
+    cosine cos[p, i] and sine sin[p, i]: (a, b) -> (a cos - b sin, a sin + b cos).
+    Dims from r on are unchanged.  Returns float64 of x's shape.
+    """
+    xd = _u16(x).astype(np.uint32) << 16
+    xd = xd.view(np.float32).astype(np.float64)
+    cos = np.asarray(cos, dtype=np.float64)
+    sin = np.asarray(sin, dtype=np.float64)
+    pos = np.asarray(positions, dtype=np.int64)
+    half = cos.shape[1]
+    out = xd.copy()
+    c = cos[pos][..., None, :]          # [..., L, 1, r/2]
+    s = sin[pos][..., None, :]
+    if interleaved:
+        a, b = xd[..., 0:2 * half:2], xd[..., 1:2 * half:2]
+        out[..., 0:2 * half:2] = a * c - b * s
+        out[..., 1:2 * half:2] = a * s + b * c
+    else:
+        a, b = xd[..., :half], xd[..., half:2 * half]
+        out[..., :half] = a * c - b * s
+        out[..., half:2 * half] = a * s + b * c
+    return out

@@ -375,3 +375,89 @@ def test_unified_batch_full_size():
         ref_l.append(lb)
     check_close(torch.cat(got_o), torch.cat(got_l), np.concatenate(ref_o), np.concatenate(ref_l),
                 "unified batch full size")
+
+
+# ---------------------------------------------------------------- rotary embedding
+def _rope_tables(P, r, device="cpu"):
+    theta = 10000.0 ** (-2.0 * torch.arange(r // 2, dtype=torch.float64) / r)
+    ang = torch.arange(P, dtype=torch.float64)[:, None] * theta[None, :]
+    return torch.cos(ang).float().to(device), torch.sin(ang).float().to(device)
+
+
+def _check_rotated(got_bits, ref, x_bits, r, what):
+    """bf16 rounding of the fp32 rotation: at most half a bf16 ulp of the exact value
+    (2^-8 relative) plus fp32 rounding of the two products (2^-21 of the inputs)."""
+    got = got_bits.astype(np.uint32) << 16
+    got = got.view(np.float32).astype(np.float64)
+    xin = (x_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    tol = 2.0 ** -8 * np.abs(ref[..., :r]) + 2.0 ** -21 * np.abs(xin[..., :r]).max() + 1e-30
+    assert np.all(np.abs(got[..., :r] - ref[..., :r]) <= tol), what
+    assert np.array_equal(got_bits[..., r:], x_bits[..., r:]), f"{what}: dims past rotary_dim changed"
+
+
+@pytest.mark.parametrize("d,r,inter", [(128, 128, False), (128, 64, True), (64, 32, False), (64, 64, True)])
+def test_rotary_matches_oracle(d, r, inter):
+    B, L, H = 3, 37, 8
+    x = W.randn_bf16(W.generator(211 + d + r), (B, L, H, d))
+    cos, sin = _rope_tables(2048, r)
+    base = torch.tensor([0, 100, 1000], dtype=torch.int32)
+    xd = x.to(DEV)
+    api.fa_rotary(xd, cos.to(DEV), sin.to(DEV), position_base=base.to(DEV), interleaved=inter)
+    torch.cuda.synchronize()
+    pos = base.numpy()[:, None] + np.arange(L)[None, :]
+    ref = oracle.rotary(bits(x), cos.numpy(), sin.numpy(), pos, interleaved=inter)
+    _check_rotated(bits(xd.cpu()), ref, bits(x), r, f"rotary d={d} r={r} interleaved={inter}")
+
+
+def test_append_with_rotary():
+    page, lens, L, Hkv, d, r = 16, [0, 5, 40], 9, 2, 128, 64
+    grown = [n + L for n in lens]
+    t = W.paged(221, len(lens), Hkv, Hkv, d, page, 0, 0, cache_seqlens=grown)
+    kc0, vc0 = poison_unused(t)
+    g = W.generator(222)
+    kn, vn = W.randn_bf16(g, (3, L, Hkv, d)), W.randn_bf16(g, (3, L, Hkv, d))
+    cos, sin = _rope_tables(256, r)
+    kc, vc = kc0.to(DEV), vc0.to(DEV)
+    api.fa_kvcache_append(kn.to(DEV), vn.to(DEV), kc, vc, t["block_table"].to(DEV),
+                          torch.tensor(lens, dtype=torch.int32, device=DEV),
+                          rotary_cos=cos.to(DEV), rotary_sin=sin.to(DEV))
+    torch.cuda.synchronize()
+    kc, vc = bits(kc.cpu()), bits(vc.cpu())
+    # values: exactly the plain append; keys: the plain append's slots, rotated
+    k_plain, v_ref = oracle.kvcache_append(bits(kn), bits(vn), bits(kc0), bits(vc0), t["block_table"].numpy(), lens)
+    assert np.array_equal(vc, v_ref)
+    bt = t["block_table"].numpy()
+    written = np.zeros(kc.shape[:2], bool)
+    for b, n in enumerate(lens):
+        pos = n + np.arange(L)
+        ref = oracle.rotary(bits(kn)[b], cos.numpy(), sin.numpy(), pos)
+        slots = (bt[b, pos // page], pos % page)
+        _check_rotated(kc[slots], ref, bits(kn)[b], r, f"append rotary, sequence {b}")
+        written[slots] = True
+    assert np.array_equal(kc[~written], k_plain[~written])
+
+
+def test_decode_step_with_rotary():
+    """Rotate the new query, append the rotated key, attend: against the oracle doing the
+    same steps (fp64 rotation rounded to bf16, then attention)."""
+    page, lens, Hq, Hkv, d, r = 16, [3, 64, 700], 8, 2, 128, 128
+    grown = [n + 1 for n in lens]
+    t = W.paged(231, len(lens), Hq, Hkv, d, page, 0, 0, cache_seqlens=grown)
+    g = W.generator(232)
+    kn, vn = W.randn_bf16(g, (3, 1, Hkv, d)), W.randn_bf16(g, (3, 1, Hkv, d))
+    cos, sin = _rope_tables(1024, r)
+    base = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qd, kc, vc, bt = t["q"].to(DEV), t["k_cache"].to(DEV), t["v_cache"].to(DEV), t["block_table"].to(DEV)
+    api.fa_rotary(qd, cos.to(DEV), sin.to(DEV), position_base=base)
+    api.fa_kvcache_append(kn.to(DEV), vn.to(DEV), kc, vc, bt, base, rotary_cos=cos.to(DEV), rotary_sin=sin.to(DEV))
+    out, lse = api.fa_fwd_kvcache_paged(qd, kc, vc, bt, torch.tensor(grown, dtype=torch.int32, device=DEV),
+                                        num_splits=0, causal=True)
+    torch.cuda.synchronize()
+    pos = np.array(lens)[:, None]
+    to_bf16 = lambda a: bits(torch.from_numpy(a).to(torch.bfloat16))   # noqa: fp64 -> bf16 (nearest even)
+    q_r = to_bf16(oracle.rotary(bits(t["q"]), cos.numpy(), sin.numpy(), pos))
+    k_r = to_bf16(oracle.rotary(bits(kn), cos.numpy(), sin.numpy(), pos))
+    k_ref, v_ref = oracle.kvcache_append(k_r, bits(vn), bits(t["k_cache"]), bits(t["v_cache"]),
+                                         t["block_table"].numpy(), lens)
+    o_ref, l_ref = oracle.fwd_paged(q_r, k_ref, v_ref, t["block_table"].numpy(), grown, causal=True)
+    check_close(out, lse, o_ref, l_ref, "decode step with rotary")

@@ -222,9 +222,9 @@ def test_full_tile_range_matches_tile_classes(tmp_path):
 
 def test_append_rejects_invalid_arguments():
     L = api.lib()
-    def call(kn=FAKE, d=128, B=2, Ln=3, Hkv=8, page=16, bt=FAKE, ks=S3):
+    def call(kn=FAKE, d=128, B=2, Ln=3, Hkv=8, page=16, bt=FAKE, ks=S3, cos=None, sin=None, rdim=0):
         return L.fa_kvcache_append(kn, FAKE, FAKE, FAKE, bt, FAKE, B, Ln, Hkv, d, 100, page, 10,
-                                   S3, S3, ks, S3, None)
+                                   S3, S3, ks, S3, cos, sin, rdim, 0, None)
     assert call(kn=None) == FA_ERR_INVALID_ARG
     assert call(bt=None) == FA_ERR_INVALID_ARG
     assert call(d=96) == FA_ERR_UNSUPPORTED
@@ -233,6 +233,24 @@ def test_append_rejects_invalid_arguments():
     assert call(page=0) == FA_ERR_INVALID_ARG
     assert call(ks=(ctypes.c_int64 * 3)(2048, 2050, 128)) == FA_ERR_INVALID_ARG
     assert call(Ln=0) == 0                                           # nothing to write, no launch
+    assert call(cos=FAKE) == FA_ERR_INVALID_ARG                      # cos without sin
+    assert call(cos=FAKE, sin=FAKE, rdim=24) == FA_ERR_INVALID_ARG   # not a multiple of 16
+    assert call(cos=FAKE, sin=FAKE, rdim=256) == FA_ERR_INVALID_ARG  # wider than head_dim
+    assert call(cos=FAKE, sin=FAKE, rdim=64, Ln=0) == 0
+
+
+def test_rotary_rejects_invalid_arguments():
+    L = api.lib()
+    def call(x=FAKE, d=128, B=2, Ln=3, H=8, cos=FAKE, sin=FAKE, rdim=128, xs=S3):
+        return L.fa_rotary(x, B, Ln, H, d, xs, None, cos, sin, rdim, 0, None)
+    assert call(x=None) == FA_ERR_INVALID_ARG
+    assert call(cos=None) == FA_ERR_INVALID_ARG
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(rdim=0) == FA_ERR_INVALID_ARG
+    assert call(rdim=40) == FA_ERR_INVALID_ARG
+    assert call(B=0) == FA_ERR_INVALID_ARG
+    assert call(xs=(ctypes.c_int64 * 3)(2048, 2050, 128)) == FA_ERR_INVALID_ARG
+    assert call(Ln=0) == 0
 
 
 def test_varlen_paged_rejects_invalid_arguments():

@@ -371,3 +371,72 @@ def test_append_then_attend_sees_the_new_tokens():
         rows = np.array(old + [vnd[b, j] for j in range(L)])       # [n + L, Hkv, d]
         np.testing.assert_allclose(o[b, 0], rows.mean(0), rtol=0, atol=1e-12)
         assert np.allclose(np.exp(lse[b, :, 0]), n + L, rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------- rotary embedding
+def _bits_of(x):
+    return bits(torch.as_tensor(np.asarray(x, np.float32)).to(torch.bfloat16))
+
+
+def test_rotary_hand_computed_example():
+    """x = [1, 2, 3, 4] (one token, one head, r = d = 4), frequency 0 turned by a quarter
+    turn and frequency 1 by nothing.  Half-split pairs (0, 2), (1, 3): [-3, 2, 1, 4];
+    interleaved pairs (0, 1), (2, 3): [-2, 1, 3, 4]."""
+    x = _bits_of([[[1.0, 2.0, 3.0, 4.0]]])            # [L=1, H=1, d=4]
+    cos, sin = np.array([[0.0, 1.0]]), np.array([[1.0, 0.0]])
+    assert np.array_equal(oracle.rotary(x, cos, sin, [0])[0, 0], [-3.0, 2.0, 1.0, 4.0])
+    assert np.array_equal(oracle.rotary(x, cos, sin, [0], interleaved=True)[0, 0], [-2.0, 1.0, 3.0, 4.0])
+
+
+def test_rotary_identity_quarter_turn_and_tail():
+    g = W.generator(201)
+    x = bits(W.randn_bf16(g, (5, 3, 64)))
+    xd = v_double(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
+    r = 32
+    ones, zeros = np.ones((7, r // 2)), np.zeros((7, r // 2))
+    pos = [0, 1, 2, 6, 3]
+    for inter in (False, True):
+        assert np.array_equal(oracle.rotary(x, ones, zeros, pos, interleaved=inter), xd)
+        q = oracle.rotary(x, zeros, ones, pos, interleaved=inter)        # (a, b) -> (-b, a)
+        a_i = np.arange(0, r, 2) if inter else np.arange(r // 2)
+        b_i = a_i + 1 if inter else a_i + r // 2
+        assert np.array_equal(q[..., a_i], -xd[..., b_i]) and np.array_equal(q[..., b_i], xd[..., a_i])
+        assert np.array_equal(q[..., r:], xd[..., r:])                  # dims past r untouched
+
+
+def test_rotary_interleaved_is_a_permutation_of_half_split():
+    g = W.generator(202)
+    r, d = 48, 64
+    x = bits(W.randn_bf16(g, (4, 2, d)))
+    ang = np.random.default_rng(3).uniform(-4, 4, (9, r // 2))
+    cos, sin = np.cos(ang), np.sin(ang)
+    perm = np.concatenate([np.arange(0, r, 2), np.arange(1, r, 2), np.arange(r, d)])
+    # dims (2i, 2i + 1) of the interleaved layout are dims (i, i + r/2) after the permutation
+    xi = x[..., perm.argsort()]
+    hs = oracle.rotary(x, cos, sin, [1, 3, 8, 0])
+    it = oracle.rotary(xi, cos, sin, [1, 3, 8, 0], interleaved=True)
+    assert np.array_equal(it[..., perm], hs)
+
+
+def test_rotary_preserves_norms_and_depends_on_relative_position():
+    """With the published frequencies (theta_i = 10000^(-2i/r)) the rotation keeps every
+    pair's norm, and a query-key dot product depends only on the position difference."""
+    g = W.generator(203)
+    r = d = 64
+    q = bits(W.randn_bf16(g, (1, 1, d)))
+    k = bits(W.randn_bf16(g, (1, 1, d)))
+    P = 64
+    theta = 10000.0 ** (-2.0 * np.arange(r // 2) / r)
+    ang = np.arange(P)[:, None] * theta[None, :]
+    cos, sin = np.cos(ang), np.sin(ang)
+    qd = v_double(torch.from_numpy(q.view(np.int16)).view(torch.bfloat16))
+    for m in (0, 5, 17):
+        rq = oracle.rotary(q, cos, sin, [m])
+        pairs = lambda v: v[..., : r // 2] ** 2 + v[..., r // 2:r] ** 2   # noqa
+        np.testing.assert_allclose(pairs(rq), pairs(qd), rtol=0, atol=1e-12)
+    dots = {}
+    for m, n in [(3, 1), (10, 8), (40, 38), (7, 20), (30, 43)]:
+        dots[(m, n)] = float(np.sum(oracle.rotary(q, cos, sin, [m]) * oracle.rotary(k, cos, sin, [n])))
+    assert abs(dots[(3, 1)] - dots[(10, 8)]) < 1e-10 and abs(dots[(3, 1)] - dots[(40, 38)]) < 1e-10
+    assert abs(dots[(7, 20)] - dots[(30, 43)]) < 1e-10
+    assert abs(dots[(3, 1)] - dots[(7, 20)]) > 1e-6       # and it does depend on the difference
