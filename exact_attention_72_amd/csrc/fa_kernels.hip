@@ -294,14 +294,6 @@ __device__ __forceinline__ f32x16 qk_mma(const u32x4 (&a)[D / 16], const bf16x8*
   for (int kk = 0; kk < D / 16; ++kk) s = mfma32(__builtin_bit_cast(bf16x8, a[kk]), qreg[kk], s);
   return s;
 }
-template <int D>
-__device__ __forceinline__ void pv_mma(const u32x2 (&lo)[D / 32], const u32x2 (&hi)[D / 32], bf16x8 pb, f32x16* o) {
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    u32x4 w = {lo[db].x, lo[db].y, hi[db].x, hi[db].y};
-    o[db] = mfma32(__builtin_bit_cast(bf16x8, w), pb, o[db]);
-  }
-}
 
 // O^T += V^T P^T product and exponential issued as inline assembly, so that
 // the P V phase of the prefill pipeline keeps the order written: one product,
@@ -422,49 +414,6 @@ __device__ __forceinline__ float block_max(const f32x16& s) {
   for (int a = 3; a < 15; a += 2) mx = fmaxf(fmaxf(mx, s[a]), s[a + 1]);
   mx = fmaxf(mx, s[15]);
   return pair_max(mx);
-}
-
-// Move the reference maximum to max(m_run, mx) when it grew by more than
-// 2^kRescaleLog2 (or on the first visible key), rescaling O and the row sums.
-template <int D>
-__device__ __forceinline__ void update_reference(float mx, float& m_run, float& l_run, float& l_bf,
-                                                 f32x16* o, float c) {
-  const float m_cand = fmaxf(m_run, mx);
-  if (__any((m_cand - m_run) * c > kRescaleLog2)) {
-    const float m_use = (m_cand == kNegInf) ? 0.0f : m_cand;
-    const float alpha = exp2_fast((m_run - m_use) * c);
-    l_run *= alpha;
-    l_bf *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-    m_run = m_cand;
-  }
-}
-
-// Probabilities of s relative to the reference m_run, as two bf16 MFMA operands,
-// and their contribution to both row sums.
-__device__ __forceinline__ void block_probs(const f32x16& s, float m_run, float c, float& l_run,
-                                            float& l_bf, bf16x8& p0, bf16x8& p1) {
-  const float nmc = (m_run == kNegInf) ? 0.0f : -m_run * c;
-  f32x8 x0, x1;
-#pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    x0[a] = exp2_fast(__builtin_fmaf(s[a], c, nmc));
-    x1[a] = exp2_fast(__builtin_fmaf(s[a + 8], c, nmc));
-  }
-  float rs = 0.0f;
-#pragma unroll
-  for (int a = 0; a < 8; ++a) rs += x0[a] + x1[a];
-  l_run += rs;
-  p0 = __builtin_convertvector(x0, bf16x8);
-  p1 = __builtin_convertvector(x1, bf16x8);
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    l_bf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * a], p0[2 * a + 1]}, one, l_bf, false);
-    l_bf = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * a], p1[2 * a + 1]}, one, l_bf, false);
-  }
 }
 
 // The softmax of a block split in two for the prefill pipeline: the
