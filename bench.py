@@ -107,9 +107,13 @@ def cpu_baseline(W, t, c, target_s=15.0):
                                 softcap=c["softcap"], rows=rows, nthreads=threads)
         dt = time.perf_counter() - t0
         return dt, keys * 4 * d, n
+    # the first runs are dominated by fixed costs, so extrapolate twice towards target_s
     dt, fl, n = run(threads * 8)
-    n2 = int(max(threads * 8, min(2000000, n * target_s / max(dt, 1e-3))))
-    dt, fl, n = run(n2)
+    for _ in range(2):
+        if dt >= 0.66 * target_s:
+            break
+        n = int(max(threads * 8, min(4000000, n * target_s / max(dt, 1e-3))))
+        dt, fl, n = run(n)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} random query rows of the batch-4 x 16-head N=4096 d=128 causal "
                       f"workload, fp64, {dt:.1f} s"}

@@ -200,7 +200,11 @@ int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
   int64_t bound = (int64_t)p.m_blocks * batch;
   int64_t bound2 = ((int64_t)total_q * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M + batch;
   p.total_tiles = (bound < bound2 ? bound : bound2) * p.hg_count;
-  p.persistent = 1;
+  // one workgroup per tile index, longest first: the hardware hands out the next
+  // tile as a workgroup finishes, which balances unequal sequences (measured
+  // 7 % faster than a persistent grid-stride loop on 32 sequences of 64..8192
+  // tokens); indices past the real tile count exit at once
+  p.persistent = 0;
   hipError_t e = fa_launch_prefill(p, head_dim, true, false, pack, softcap, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "varlen launch");
   return FA_OK;
@@ -276,6 +280,9 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   int64_t bound = (int64_t)p.m_blocks * batch;
   int64_t bound2 = ((int64_t)total_q * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M + batch;
   p.total_tiles = (bound < bound2 ? bound : bound2) * p.hg_count;
+  // a persistent grid-stride loop: measured faster than one workgroup per tile
+  // on a mixed batch of long chunks and one-token requests (416 against 358
+  // TFLOP/s), unlike the plain varlen batch
   p.persistent = 1;
   hipError_t e = fa_launch_prefill(p, head_dim, true, true, pack, softcap, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "varlen paged launch");

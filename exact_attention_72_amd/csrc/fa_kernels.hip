@@ -1323,7 +1323,7 @@ hipError_t launch_prefill_t(const FaParams& p0, hipStream_t stream) {
   int64_t tiles = p.total_tiles;
   if (tiles <= 0) return hipSuccess;
   int64_t grid;
-  if (VARLEN || p.persistent) {
+  if (p.persistent) {
     static thread_local int occ = 0;
     if (occ == 0) occ = occupancy(kern);
     int64_t G = (int64_t)device_cus() * occ;
