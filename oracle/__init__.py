@@ -307,3 +307,68 @@ def rotary(x, cos, sin, positions, *, interleaved=False):
         out[..., :half] = a * c - b * s
         out[..., half:2 * half] = a * s + b * c
     return out
+
+
+def _f64(a):
+    """bf16 bit patterns (uint16) -> float64."""
+    return (_u16(a).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def visible_mask(Lq, Lk, causal, window):
+    """visible[i, j] for query i of Lq and key j of Lk, bottom-right aligned (query i at
+    key position i + Lk - Lq): the same predicate the forward oracle evaluates."""
+    wl, wr = _window(window)
+    pos = np.arange(Lq)[:, None] + (Lk - Lq)
+    j = np.arange(Lk)[None, :]
+    vis = np.ones((Lq, Lk), bool)
+    if causal:
+        vis &= j <= pos
+    if wl >= 0:
+        vis &= j >= pos - wl
+    if wr >= 0:
+        vis &= j <= pos + wr
+    return vis
+
+
+def bwd_dense(q, k, v, dout, *, scale=None, causal=False, window=None, heads=None):
+    """Gradients of the attention forward, in fp64 with S and P materialised.
+
+    "Attention kernels: FlashAttention and PagedAttention", section 4.3: the
+    backward recomputes S = Q K^T, takes P from the saved log-sum-exp and forms
+    dV = P^T dO and dS.  The rest is the derivative of softmax attention written
+    out: dP = dO V^T, D = rowsum(dO * O) (the preprocess the overview page lists),
+    dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.  Query head h uses KV
+    head h // (Hq / Hkv), so dK and dV sum over the query heads of a group.
+    Rows that see no key have P = 0 and contribute nothing.
+
+    q, dout: uint16 bf16 bits [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d].  heads: None for
+    all query heads, or a list of query heads (then dK, dV hold only their share).
+    Returns float64 (dq [B, Nq, Hq, d], dk [B, Nk, Hkv, d], dv [B, Nk, Hkv, d]).
+    """
+    qd, kd, vd, od = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Nq, Hq, d = qd.shape
+    Nk, Hkv = kd.shape[1], kd.shape[2]
+    g = Hq // Hkv
+    s = _scale(scale, d)
+    vis = visible_mask(Nq, Nk, causal, window)
+    dq = np.zeros_like(qd)
+    dk = np.zeros_like(kd)
+    dv = np.zeros_like(vd)
+    for b in range(B):
+        for h in (range(Hq) if heads is None else heads):
+            hk = h // g
+            S = s * (qd[b, :, h] @ kd[b, :, hk].T)
+            S = np.where(vis, S, -np.inf)
+            m = S.max(axis=1, keepdims=True)
+            empty = ~np.isfinite(m)
+            E = np.exp(S - np.where(empty, 0.0, m))
+            P = E / np.where(empty, 1.0, E.sum(axis=1, keepdims=True))
+            O = P @ vd[b, :, hk]
+            dO = od[b, :, h]
+            Dr = np.sum(dO * O, axis=1, keepdims=True)
+            dP = dO @ vd[b, :, hk].T
+            dS = P * (dP - Dr)
+            dv[b, :, hk] += P.T @ dO
+            dq[b, :, h] = s * (dS @ kd[b, :, hk])
+            dk[b, :, hk] += s * (dS.T @ qd[b, :, h])
+    return dq, dk, dv

@@ -440,3 +440,71 @@ def test_rotary_preserves_norms_and_depends_on_relative_position():
     assert abs(dots[(3, 1)] - dots[(10, 8)]) < 1e-10 and abs(dots[(3, 1)] - dots[(40, 38)]) < 1e-10
     assert abs(dots[(7, 20)] - dots[(30, 43)]) < 1e-10
     assert abs(dots[(3, 1)] - dots[(7, 20)]) > 1e-6       # and it does depend on the difference
+
+
+# ---------------------------------------------------------------- backward
+def _torch_grads(q, k, v, do, scale, vis, g):
+    """fp64 autograd through an explicitly masked softmax attention (library routine)."""
+    Q = torch.tensor(v_double(q), requires_grad=True)
+    K = torch.tensor(v_double(k), requires_grad=True)
+    V = torch.tensor(v_double(v), requires_grad=True)
+    dO = torch.tensor(v_double(do))
+    Ke = K.repeat_interleave(g, dim=2)
+    Ve = V.repeat_interleave(g, dim=2)
+    S = torch.einsum("bihd,bjhd->bhij", Q, Ke) * scale
+    S = S.masked_fill(~torch.as_tensor(vis)[None, None], float("-inf"))
+    P = torch.softmax(S, dim=-1)
+    O = torch.einsum("bhij,bjhd->bihd", P, Ve)
+    (O * dO).sum().backward()
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+
+
+@pytest.mark.parametrize("Nq,Nk,causal,window", [(37, 37, False, None), (37, 37, True, None),
+                                                 (20, 45, True, None), (40, 40, True, (7, 0)),
+                                                 (33, 33, False, (5, 3))])
+def test_bwd_matches_torch_autograd(Nq, Nk, causal, window):
+    g = W.generator(301 + Nq + Nk)
+    B, Hq, Hkv, d = 2, 4, 2, 16
+    q, k, v = (W.randn_bf16(g, (B, n, h, d)) for n, h in ((Nq, Hq), (Nk, Hkv), (Nk, Hkv)))
+    do = W.randn_bf16(g, (B, Nq, Hq, d))
+    dq, dk, dv = oracle.bwd_dense(bits(q), bits(k), bits(v), bits(do), causal=causal, window=window)
+    vis = oracle.visible_mask(Nq, Nk, causal, window)
+    tq, tk, tv = _torch_grads(q, k, v, do, d ** -0.5, vis, Hq // Hkv)
+    for a, b_ in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-11)
+
+
+def test_bwd_closed_forms():
+    g = W.generator(311)
+    B, N, H, d = 1, 24, 2, 8
+    k, v, do = (W.randn_bf16(g, (B, N, H, d)) for _ in range(3))
+    vis = oracle.visible_mask(N, N, True, None)
+    cnt = vis.sum(axis=1)
+    # Q = 0: P is uniform over the visible keys, so dV_j = sum over rows i that see j of dO_i / count_i
+    q0 = torch.zeros(B, N, H, d, dtype=torch.bfloat16)
+    _, _, dv = oracle.bwd_dense(bits(q0), bits(k), bits(v), bits(do), causal=True)
+    dod = v_double(do)
+    want = np.einsum("ij,bihd->bjhd", vis / cnt[:, None], dod)
+    np.testing.assert_allclose(dv, want, rtol=0, atol=1e-12)
+    # identical keys: every row of dS sums to zero, so dQ = 0
+    q = W.randn_bf16(g, (B, N, H, d))
+    kc = k[:, :1].expand(B, N, H, d).contiguous()
+    dq, _, _ = oracle.bwd_dense(bits(q), bits(kc), bits(v), bits(do), causal=True)
+    assert np.abs(dq).max() < 1e-12
+    # dO = 0: no gradient at all
+    z = torch.zeros_like(do)
+    for a in oracle.bwd_dense(bits(q), bits(k), bits(v), bits(z), causal=True):
+        assert np.array_equal(a, np.zeros_like(a))
+
+
+def test_bwd_key_gradients_sum_to_zero_and_empty_rows():
+    """sum_j dK_j = scale sum_i q_i sum_j dS_ij = 0 for any inputs (each row of dS sums to
+    zero); rows that see no key (more queries than keys, causal) get dQ = 0."""
+    g = W.generator(321)
+    B, Nq, Nk, Hq, Hkv, d = 2, 30, 18, 4, 1, 16
+    q, do = W.randn_bf16(g, (B, Nq, Hq, d)), W.randn_bf16(g, (B, Nq, Hq, d))
+    k, v = W.randn_bf16(g, (B, Nk, Hkv, d)), W.randn_bf16(g, (B, Nk, Hkv, d))
+    dq, dk, _ = oracle.bwd_dense(bits(q), bits(k), bits(v), bits(do), causal=True, scale=0.3)
+    assert np.abs(dk.sum(axis=1)).max() < 1e-11
+    assert np.array_equal(dq[:, : Nq - Nk], np.zeros_like(dq[:, : Nq - Nk]))   # rows at positions < 0
+    assert np.abs(dq[:, Nq - Nk:]).max() > 0.01
