@@ -22,7 +22,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
 EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_varlen_paged", "fa_kvcache_num_splits",
-           "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary",
+           "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary", "fa_bwd", "fa_bwd_workspace_size",
            "fa_combine", "fa_tile_class", "fa_last_error", "fa_version")
 
 
@@ -63,13 +63,16 @@ def lib():
     L.fa_combine.argtypes = [P, P, I, I64, I, P, I64, P, P]
     L.fa_kvcache_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I64, I, I, S3, S3, S3, S3, P, P, I, I, P]
     L.fa_rotary.argtypes = [P, I, I, I, I, S3, P, P, P, I, I, P]
+    L.fa_bwd.argtypes = [OPT, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, S3, S3, S3, S3, S3, P, SZ, P]
+    L.fa_bwd_workspace_size.argtypes = [I, I, I]
+    L.fa_bwd_workspace_size.restype = SZ
     L.fa_fwd_varlen_paged.argtypes = [OPT, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I64, I, I, S3, S3, S3,
                                       S3, P]
     L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = I
     for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_combine", "fa_tile_class",
-                 "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary"):
+                 "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary", "fa_bwd"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -278,6 +281,31 @@ def fa_kvcache_append(k_new, v_new, k_cache, v_cache, block_table, cache_seqlens
                                    _strides(k_cache, (0, 1, 2)), _strides(v_cache, (0, 1, 2)),
                                    _ptr(cos), _ptr(sin), rdim, int(bool(rotary_interleaved)),
                                    _stream(stream)))
+
+
+def fa_bwd(q, k, v, out, lse, dout, *, softmax_scale=None, causal=False, window=None, dq=None, dk=None,
+           dv=None, workspace=None, stream=None):
+    """Gradients of fa_fwd: q/out/dout [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] bf16, lse fp32
+    [B, Hq, Nq] from the forward -> (dq, dk, dv) bf16 in the shapes of q, k, v."""
+    _bf16_cuda(q, k, v, out, dout)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] device tensor")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _bf16_cuda(dq, dk, dv)
+    need = int(lib().fa_bwd_workspace_size(B, Nq, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    o = _opts(softmax_scale, causal, window, 0.0, 0)
+    S = lambda t: _strides(t, (0, 1, 2))  # noqa: E731
+    _check(lib().fa_bwd(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                        _ptr(dk), _ptr(dv), B, Nq, Nk, Hq, Hkv, d, S(q), S(k), S(v), S(out), S(dout), S(dq), S(dk),
+                        S(dv), _ptr(workspace), ws_bytes, _stream(stream)))
+    return dq, dk, dv
 
 
 def fa_combine(o_part, lse_part, *, out=None, lse=None, stream=None):

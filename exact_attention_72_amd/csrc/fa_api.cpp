@@ -34,10 +34,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Options -> score-transform constants.  softmax_scale <= 0 or NaN selects d^-0.5
 // ("FA4 (CuTeDSL) and engineering interfaces", section 3).
-int fill_opts(const fa_attn_opts* o, int d, FaParams* p, bool* softcap) {
-  if (!o) return fail(FA_ERR_INVALID_ARG, "opts is NULL");
+float resolve_scale(const fa_attn_opts* o, int d) {
   float scale = o->softmax_scale;
   if (!(scale > 0.0f) || isnan(scale) || isinf(scale)) scale = 1.0f / sqrtf((float)d);
+  return scale;
+}
+
+int fill_opts(const fa_attn_opts* o, int d, FaParams* p, bool* softcap) {
+  if (!o) return fail(FA_ERR_INVALID_ARG, "opts is NULL");
+  const float scale = resolve_scale(o, d);
   if (isnan(o->softcap) || o->softcap < 0.0f || isinf(o->softcap))
     return fail(FA_ERR_INVALID_ARG, "softcap must be a finite value >= 0");
   const float log2e = 1.4426950408889634f;
@@ -455,6 +460,68 @@ int fa_rotary(void* x, int batch, int seqlen, int heads, int head_dim, const int
   p.rot = rot;
   hipError_t e = fa_launch_rotary(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rotary launch");
+  return FA_OK;
+}
+
+size_t fa_bwd_workspace_size(int batch, int seqlen_q, int heads_q) {
+  if (batch <= 0 || seqlen_q <= 0 || heads_q <= 0) return 0;
+  const size_t bytes = (size_t)batch * heads_q * seqlen_q * 4;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v, const void* out,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv, int batch, int seqlen_q, int seqlen_k,
+           int heads_q, int heads_kv, int head_dim, const int64_t q_strides[3], const int64_t k_strides[3],
+           const int64_t v_strides[3], const int64_t o_strides[3], const int64_t do_strides[3],
+           const int64_t dq_strides[3], const int64_t dk_strides[3], const int64_t dv_strides[3], void* workspace,
+           size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_k <= 0)
+    return fail(FA_ERR_INVALID_ARG, "batch, seqlen_q and seqlen_k must be positive");
+  if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k", k, k_strides, 3)) ||
+      (rc = check_strides("v", v, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)) ||
+      (rc = check_strides("dout", dout, do_strides, 3)) || (rc = check_strides("dq", dq, dq_strides, 3)) ||
+      (rc = check_strides("dk", dk, dk_strides, 3)) || (rc = check_strides("dv", dv, dv_strides, 3)))
+    return rc;
+  const size_t need = fa_bwd_workspace_size(batch, seqlen_q, heads_q);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  FaParams f;
+  memset(&f, 0, sizeof f);
+  bool softcap = false;
+  if ((rc = fill_opts(opts, head_dim, &f, &softcap))) return rc;
+  if (softcap) return fail(FA_ERR_UNSUPPORTED, "the backward pass has no softcap");
+  FaBwdParams p;
+  memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(out);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.delta = static_cast<float*>(workspace);
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.q_bs = q_strides[0]; p.q_ss = q_strides[1]; p.q_hs = q_strides[2];
+  p.k_bs = k_strides[0]; p.k_ss = k_strides[1]; p.k_hs = k_strides[2];
+  p.v_bs = v_strides[0]; p.v_ss = v_strides[1]; p.v_hs = v_strides[2];
+  p.o_bs = o_strides[0]; p.o_ss = o_strides[1]; p.o_hs = o_strides[2];
+  p.do_bs = do_strides[0]; p.do_ss = do_strides[1]; p.do_hs = do_strides[2];
+  p.dq_bs = dq_strides[0]; p.dq_ss = dq_strides[1]; p.dq_hs = dq_strides[2];
+  p.dk_bs = dk_strides[0]; p.dk_ss = dk_strides[1]; p.dk_hs = dk_strides[2];
+  p.dv_bs = dv_strides[0]; p.dv_ss = dv_strides[1]; p.dv_hs = dv_strides[2];
+  p.B = batch; p.Nq = seqlen_q; p.Nk = seqlen_k; p.Hq = heads_q; p.Hkv = heads_kv; p.g = heads_q / heads_kv;
+  p.scale_log2 = f.scale_log2;
+  p.scale = resolve_scale(opts, head_dim);
+  p.causal = f.causal; p.wl = f.wl; p.wr = f.wr;
+  hipError_t e = fa_launch_bwd(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
   return FA_OK;
 }
 

@@ -116,3 +116,22 @@ FA_HD int fa_tile_class(FaRowSpan s, int64_t Lk, int causal, int wl, int wr, int
   if (wl >= 0 && t0 < s.pos_hi - wl) cls |= FA_TILE_MASK_LEFT;
   return cls;
 }
+
+// Queries that see at least one key of [j_lo, j_hi] (inclusive, inside [0, Lk)):
+// the query rows [*i_lo, *i_hi) of Lq (empty when *i_lo >= *i_hi).  The
+// backward's key-block tiles loop over these (the transpose of the key range
+// of a row span).  Query t sits at p = t + Lk - Lq; it needs some key j of the
+// block with j <= p (causal) or j <= p + wr (right window) and j >= p - wl
+// (left window).
+FA_HD void fa_query_range(int64_t j_lo, int64_t j_hi, int64_t Lq, int64_t Lk, int causal, int wl, int wr,
+                          int64_t* i_lo, int64_t* i_hi) {
+  const int64_t off = Lk - Lq;
+  int64_t lo = 0, hi = Lq;
+  if (causal)
+    lo = j_lo - off;  // p >= j_lo (binds before any right window, which only adds p + wr >= j)
+  else if (wr >= 0)
+    lo = j_lo - wr - off;  // p + wr >= j_lo
+  if (wl >= 0) hi = j_hi + wl - off + 1;  // p - wl <= j_hi
+  *i_lo = fa_max64(lo, 0);
+  *i_hi = fa_min64(hi, Lq);
+}

@@ -62,6 +62,27 @@ struct FaRotaryParams {
   FaRotary rot;
 };
 
+// Backward pass (dense BSHD): gradients of q, k, v from dO, O and the
+// forward's log-sum-exp.
+struct FaBwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;  // [B, Hq, Nq] natural-log LSE of the forward
+  float* delta;      // [B, Hq, Nq] D = rowsum(dO * O) (workspace)
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  // strides in elements: (batch, token, head)
+  int64_t q_bs, q_ss, q_hs, k_bs, k_ss, k_hs, v_bs, v_ss, v_hs, o_bs, o_ss, o_hs;
+  int64_t do_bs, do_ss, do_hs, dq_bs, dq_ss, dq_hs, dk_bs, dk_ss, dk_hs, dv_bs, dv_ss, dv_hs;
+  int B, Nq, Nk, Hq, Hkv, g;
+  float scale, scale_log2;
+  int causal, wl, wr;
+};
+
 // In-place append of new K/V tokens to a paged cache.
 struct FaAppendParams {
   const uint16_t* k_new;
@@ -99,6 +120,7 @@ hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t s
 hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_append(const FaAppendParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_rotary(const FaRotaryParams& p, int d, hipStream_t stream);
+hipError_t fa_launch_bwd(const FaBwdParams& p, int d, hipStream_t stream);
 
 // Tile geometry of the prefill kernel.
 constexpr int FA_BLOCK_M = 128;     // query rows per workgroup tile (4 waves x 32)

@@ -1292,6 +1292,388 @@ __global__ __launch_bounds__(kThreads) void fa_append_kernel(FaAppendParams p) {
   }
 }
 
+// ------------------------------------------------------------------ backward
+// "Attention kernels...", section 4.3: the backward recomputes S = Q K^T block by
+// block and takes P = exp(S - L) straight from the saved log-sum-exp L, with no
+// online reduction; dV = P^T dO, dP = dO V^T, dS = P (dP - D) with
+// D = rowsum(dO O) (a preprocess pass), dQ = scale dS K, dK = scale dS^T Q.
+// P and dS enter their products rounded to bf16, like P in the forward.
+//
+// Two kernels split the work so that each accumulates its gradient in
+// registers: the dQ kernel walks key blocks for a block of queries (the
+// forward's orientation: a lane owns a query), the dK/dV kernel walks query
+// blocks (and the query heads of a KV-head group) for a block of keys, with
+// the roles of queries and keys exchanged (a lane owns a key).  Each product
+// then has its operands in the layouts the forward already reads: rows of an
+// LDS tile by ds_read_b128, or a tile read transposed by ds_read_b64_tr_b16,
+// so a tile used both ways is staged twice, once per swizzle.
+
+// D[b, h, i] = sum_c dO[b, i, h, c] O[b, i, h, c] in fp32; one row per group of
+// D / 8 lanes, 16 bytes of each tensor per lane.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa_bwd_delta_kernel(FaBwdParams p) {
+  constexpr int LPR = D / 8;       // lanes per row
+  constexpr int RPW = 64 / LPR;    // rows per wave
+  typedef float f32x8_ __attribute__((ext_vector_type(8)));
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+  const int lane = threadIdx.x & 63;
+  const int64_t w0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t nw = ((int64_t)gridDim.x * kThreads) >> 6;
+  for (int64_t r0 = w0 * RPW; r0 < rows; r0 += nw * RPW) {
+    const int64_t r = r0 + lane / LPR;  // row index in [B, Hq, Nq] order
+    const int c = lane % LPR;
+    float acc = 0.0f;
+    if (r < rows) {
+      const int i = (int)(r % p.Nq);
+      const int64_t bh = r / p.Nq;
+      const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(p.o + b * p.o_bs + i * p.o_ss + h * p.o_hs + 8 * c);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(p.dout + b * p.do_bs + i * p.do_ss + h * p.do_hs + 8 * c);
+      const f32x8_ xf = __builtin_convertvector(__builtin_bit_cast(bf16x8, x), f32x8_);
+      const f32x8_ yf = __builtin_convertvector(__builtin_bit_cast(bf16x8, y), f32x8_);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(xf[e], yf[e], acc);
+    }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (r < rows && c == 0) p.delta[r] = acc;
+  }
+}
+
+// 1 KiB LDS-DMA share of a 32-row bf16 tile: rows (row0 + dma_row + 4 RPK j) of
+// a tensor whose rows sit at base + r * stride, clamped to the last valid row
+// (the mask drops what the clamp duplicates); chunk src of each row.
+template <int D>
+__device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t stride, int row0, int dma_row, int last,
+                                         int src, char* dst) {
+  using G = DmaGeom<D, 32>;
+#pragma unroll
+  for (int j = 0; j < G::kInstPerWave; ++j) {
+    int r = row0 + dma_row + j * G::kRowStep;
+    r = r < last ? r : last;
+    dma16(base + (int64_t)r * stride + src, dst + j * 4096);
+  }
+}
+
+// O^T-style product with the accumulator in AGPRs (the dK/dV kernel holds two
+// gradient tiles, more than its VGPRs); a reader of the accumulators waits
+// with drain_acc first.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, u32x4 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <int N>
+__device__ __forceinline__ void drain_acc(f32x16 (&a)[N]) {
+  if constexpr (N == 4) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
+  } else {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(a[0]), "+a"(a[1]));
+  }
+}
+
+// dQ: one workgroup per (batch, query head, 128-row block); each wave owns 32
+// query rows and walks the key blocks the rows can see.  A stage holds a key
+// block three times: K rows (row swizzle) for S^T = K Q^T, K again in the
+// transposed-read swizzle for dQ^T += K^T dS^T, and V rows for dP^T = V dO^T.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
+  constexpr int BN = 32;
+  constexpr int NBUF = 3;
+  using G = DmaGeom<D, BN>;
+  constexpr int T = G::kTensorBytes;
+  constexpr int kStage = 3 * T;
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kStage];
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, kg = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float c = p.scale_log2;
+  LaneOffsets<D> off;
+  off.init(lane, lds_addr(smem), lds_addr(smem) + T);  // K rows at +0, K transposed at +T, V rows at +2T
+  const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
+  const int dma_pc = lane % G::kChunksPerRow;
+  const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
+  const int v_src = (dma_pc ^ v_swz<D>(dma_row)) * 8;
+
+  // tile: row blocks longest first (causal rows near the end see more keys)
+  const int m_blocks = (p.Nq + 127) / 128;
+  const int64_t pairs = (int64_t)p.B * p.Hq;
+  const int64_t t = blockIdx.x;
+  const int mb = m_blocks - 1 - (int)(t / pairs);
+  const int b = (int)((t % pairs) / p.Hq), h = (int)((t % pairs) % p.Hq), kvh = h / p.g;
+  const int Lq = p.Nq, Lk = p.Nk;
+  const int m0 = mb * 128;
+  FaRowSpan span;
+  span.pos_lo = (int64_t)m0 + (Lk - Lq);
+  span.pos_hi = (int64_t)min(m0 + 128, Lq) - 1 + (Lk - Lq);
+  int n_lo, n_hi, f_lo, f_hi;
+  fa_key_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &n_lo, &n_hi);
+  fa_full_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &f_lo, &f_hi);
+  const int nb = n_hi - n_lo;
+
+  const int row = m0 + wave * 32 + col;
+  const bool row_ok = row < Lq;
+  bf16x8 qreg[D / 16], doreg[D / 16];
+  {
+    const uint16_t* qb = p.q + b * p.q_bs + (int64_t)(row_ok ? row : 0) * p.q_ss + h * p.q_hs;
+    const uint16_t* db = p.dout + b * p.do_bs + (int64_t)(row_ok ? row : 0) * p.do_ss + h * p.do_hs;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (row_ok) {
+        x = *reinterpret_cast<const u32x4*>(qb + 16 * kk + 8 * kg);
+        y = *reinterpret_cast<const u32x4*>(db + 16 * kk + 8 * kg);
+      }
+      qreg[kk] = __builtin_bit_cast(bf16x8, x);
+      doreg[kk] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  const int64_t ri = ((int64_t)b * p.Hq + h) * Lq + (row_ok ? row : 0);
+  const float lse = row_ok ? p.lse[ri] : kNegInf;
+  const float dlt = row_ok ? p.delta[ri] : 0.0f;
+  // P = exp2(s c - L log2 e); a row that sees nothing (L = -inf) gets P = 0
+  const float nl = (lse == kNegInf) ? __builtin_inff() : lse * kLog2e;
+  LaneMask mask;
+  mask.pos = row + (Lk - Lq);
+  mask.kend = Lk;
+  mask.kbeg = 0;
+  mask.causal = p.causal;
+  mask.wl = p.wl;
+  mask.wr = p.wr;
+
+  const uint16_t* kb = p.k + b * p.k_bs + kvh * p.k_hs;
+  const uint16_t* vb = p.v + b * p.v_bs + kvh * p.v_hs;
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    char* st = smem + (i % NBUF) * kStage + wave * 1024;
+    const int n0 = (n_lo + i) * BN;
+    dma_rows<D>(kb, p.k_ss, n0, dma_row, Lk - 1, k_src, st);
+    dma_rows<D>(kb, p.k_ss, n0, dma_row, Lk - 1, v_src, st + T);
+    dma_rows<D>(vb, p.v_ss, n0, dma_row, Lk - 1, k_src, st + 2 * T);
+  };
+  constexpr int kPer = 3 * G::kInstPerWave;
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+  for (int j = 0; j < NBUF - 1 && j < nb; ++j) issue(j);
+  for (int i = 0; i < nb; ++i) {
+    wait_vmcnt_blocks<kPer>(min(i + NBUF - 2, nb - 1) - i);  // block i landed
+    stage_barrier();  // for every wave; and everyone is done with block i - 1's stage
+    if (i + NBUF - 1 < nb) issue(i + NBUF - 1);
+    const uint32_t st = (uint32_t)((i % NBUF) * kStage);
+    u32x4 ka[D / 16];
+    read_k<D, 0>(st, off, ka);
+    lgkm_wait<0>(ka);
+    f32x16 s = qk_mma<D>(ka, qreg);  // S^T = K Q^T
+    read_k<D, 0>(st + 2 * T, off, ka);
+    lgkm_wait<0>(ka);
+    const f32x16 dpt = qk_mma<D>(ka, doreg);  // dP^T = V dO^T
+    const int n = n_lo + i;
+    if (n < f_lo || n >= f_hi) {
+      int base = n * BN + 4 * kg;
+      asm volatile("" : "+v"(base));
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int key = base + 8 * (a >> 2) + (a & 3);
+        s[a] = mask.visible(key) ? s[a] : kNegInf;
+      }
+    }
+    f32x8 x0, x1;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const float pa = exp2_fast(__builtin_fmaf(s[a], c, -nl));
+      const float ds = pa * (dpt[a] - dlt);
+      if (a < 8)
+        x0[a] = ds;
+      else
+        x1[a - 8] = ds;
+    }
+    const bf16x8 d0 = __builtin_convertvector(x0, bf16x8), d1 = __builtin_convertvector(x1, bf16x8);
+    pv_chunk<D, 0>(st, d0, dq, off);  // dQ^T += K^T dS^T, K read transposed
+    pv_chunk<D, 16 * (2 * D)>(st, d1, dq, off);
+  }
+  if (row_ok) {
+    uint16_t* ob = p.dq + b * p.dq_bs + (int64_t)row * p.dq_ss + h * p.dq_hs;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x8 x = {};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = dq[db][4 * q4 + e] * p.scale;
+        const u32x4 yb = __builtin_bit_cast(u32x4, __builtin_convertvector(x, bf16x8));
+        *reinterpret_cast<u32x2*>(ob + 32 * db + 8 * q4 + 4 * kg) = u32x2{yb.x, yb.y};
+      }
+  }
+}
+
+// dK, dV: one workgroup per (batch, KV head, 128-key block); each wave owns 32
+// keys (a lane owns a key) and walks, for every query head of the group, the
+// query blocks that see the keys.  S = Q K^T and dP = dO V^T read Q and dO rows,
+// dV^T += dO^T P and dK^T += Q^T dS read them transposed, so a stage holds Q and
+// dO once per swizzle, plus the block's 32 log-sum-exp and D values.
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p) {
+  constexpr int BM = 32;
+  constexpr int NBUF = 3;
+  using G = DmaGeom<D, BM>;
+  constexpr int T = G::kTensorBytes;
+  constexpr int kStage = 4 * T + 1024;  // Q rows, Q transposed, dO rows, dO transposed, L and D
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kStage];
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, kg = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float c = p.scale_log2;
+  LaneOffsets<D> off;
+  off.init(lane, lds_addr(smem), lds_addr(smem) + T);  // Q rows +0, Q transposed +T, dO rows +2T, dO transposed +3T
+  const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
+  const int dma_pc = lane % G::kChunksPerRow;
+  const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
+  const int v_src = (dma_pc ^ v_swz<D>(dma_row)) * 8;
+
+  const int k_blocks = (p.Nk + 127) / 128;
+  const int64_t pairs = (int64_t)p.B * p.Hkv;
+  const int64_t t = blockIdx.x;
+  const int kbk = (int)(t / pairs);  // key blocks near the start first (they see the most queries)
+  const int b = (int)((t % pairs) / p.Hkv), kvh = (int)((t % pairs) % p.Hkv);
+  (void)k_blocks;
+  const int Lq = p.Nq, Lk = p.Nk;
+  const int j0 = kbk * 128;
+  int64_t i_lo, i_hi;
+  fa_query_range(j0, min(j0 + 128, Lk) - 1, Lq, Lk, p.causal, p.wl, p.wr, &i_lo, &i_hi);
+  const int qb_lo = (int)(i_lo / BM);
+  const int nqb = i_hi > i_lo ? (int)((i_hi + BM - 1) / BM) - qb_lo : 0;
+  const int steps = nqb * p.g;
+
+  const int key = j0 + wave * 32 + col;
+  const bool key_ok = key < Lk;
+  bf16x8 kreg[D / 16], vreg[D / 16];
+  {
+    const uint16_t* kr = p.k + b * p.k_bs + (int64_t)(key_ok ? key : 0) * p.k_ss + kvh * p.k_hs;
+    const uint16_t* vr = p.v + b * p.v_bs + (int64_t)(key_ok ? key : 0) * p.v_ss + kvh * p.v_hs;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (key_ok) {
+        x = *reinterpret_cast<const u32x4*>(kr + 16 * kk + 8 * kg);
+        y = *reinterpret_cast<const u32x4*>(vr + 16 * kk + 8 * kg);
+      }
+      kreg[kk] = __builtin_bit_cast(bf16x8, x);
+      vreg[kk] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  // step s: query head kvh g + s / nqb, query block qb_lo + s % nqb
+  auto issue = [&](int s_) __attribute__((always_inline)) {
+    char* st = smem + (s_ % NBUF) * kStage;
+    const int h = kvh * p.g + s_ / nqb;
+    const int q0 = (qb_lo + s_ % nqb) * BM;
+    const uint16_t* qb = p.q + b * p.q_bs + h * p.q_hs;
+    const uint16_t* db = p.dout + b * p.do_bs + h * p.do_hs;
+    char* w = st + wave * 1024;
+    dma_rows<D>(qb, p.q_ss, q0, dma_row, Lq - 1, k_src, w);
+    dma_rows<D>(qb, p.q_ss, q0, dma_row, Lq - 1, v_src, w + T);
+    dma_rows<D>(db, p.do_ss, q0, dma_row, Lq - 1, k_src, w + 2 * T);
+    dma_rows<D>(db, p.do_ss, q0, dma_row, Lq - 1, v_src, w + 3 * T);
+    // the block's L (lanes 0..31) and D (lanes 32..63), 4 bytes a lane; every
+    // wave writes the same bytes, so every wave's count of DMAs per step agrees
+    int r = q0 + col;
+    r = r < Lq ? r : Lq - 1;
+    const int64_t ri = ((int64_t)b * p.Hq + h) * Lq + r;
+    const float* src = kg ? p.delta + ri : p.lse + ri;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (FA_LDS void*)(st + 4 * T), 4, 0, 0);
+  };
+  constexpr int kPer = 4 * G::kInstPerWave + 1;
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+  const uint32_t ld_base = lds_addr(smem) + 4 * T + 16 * kg;  // L of queries 8 j + 4 kg .. + 3 at + 32 j
+  for (int j = 0; j < NBUF - 1 && j < steps; ++j) issue(j);
+  for (int s_ = 0; s_ < steps; ++s_) {
+    wait_vmcnt_blocks<kPer>(min(s_ + NBUF - 2, steps - 1) - s_);
+    stage_barrier();
+    if (s_ + NBUF - 1 < steps) issue(s_ + NBUF - 1);
+    const uint32_t st = (uint32_t)((s_ % NBUF) * kStage);
+    const int q0 = (qb_lo + s_ % nqb) * BM;
+    u32x4 qa[D / 16];
+    read_k<D, 0>(st, off, qa);
+    lgkm_wait<0>(qa);
+    f32x16 s = qk_mma<D>(qa, kreg);  // S = Q K^T: rows queries, lane column = this key
+    read_k<D, 0>(st + 2 * T, off, qa);
+    lgkm_wait<0>(qa);
+    const f32x16 dp = qk_mma<D>(qa, vreg);  // dP = dO V^T
+    // L and D of the accumulator rows: rows 8 j + 4 kg .. + 3 are slots 4 j .. 4 j + 3
+    u32x4 lr[4], dr[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      lr[jj] = ds_read_b128<0>(ld_base + st + 32 * jj);
+      dr[jj] = ds_read_b128<128>(ld_base + st + 32 * jj);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lr[0]), "+v"(lr[1]), "+v"(lr[2]), "+v"(lr[3]), "+v"(dr[0]),
+                 "+v"(dr[1]), "+v"(dr[2]), "+v"(dr[3]));
+    f32x8 p0f, p1f, d0f, d1f;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int qi = q0 + 8 * (a >> 2) + 4 * kg + (a & 3);
+      const int pos = qi + (Lk - Lq);
+      const bool vis = key_ok && qi < Lq && (!p.causal || key <= pos) && (p.wl < 0 || key >= pos - p.wl) &&
+                       (p.wr < 0 || key <= pos + p.wr);
+      const float l = __uint_as_float(lr[a >> 2][a & 3]);
+      const float dl = __uint_as_float(dr[a >> 2][a & 3]);
+      const float nl = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
+      const float pa = vis ? exp2_fast(__builtin_fmaf(s[a], c, -nl)) : 0.0f;
+      const float ds = pa * (dp[a] - dl);
+      if (a < 8) {
+        p0f[a] = pa;
+        d0f[a] = ds;
+      } else {
+        p1f[a - 8] = pa;
+        d1f[a - 8] = ds;
+      }
+    }
+    const bf16x8 p0 = __builtin_convertvector(p0f, bf16x8), p1 = __builtin_convertvector(p1f, bf16x8);
+    const bf16x8 d0 = __builtin_convertvector(d0f, bf16x8), d1 = __builtin_convertvector(d1f, bf16x8);
+    // dV^T += dO^T P (dO read transposed), dK^T += Q^T dS (Q read transposed)
+    u32x2 lo[D / 32], hi[D / 32];
+    read_v<D, 0>(st + 2 * T, off, lo, hi);
+    lgkm_wait<0>(lo, hi);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) mfma_acc(dv[db], u32x4{lo[db].x, lo[db].y, hi[db].x, hi[db].y}, p0);
+    read_v<D, 16 * (2 * D)>(st + 2 * T, off, lo, hi);
+    lgkm_wait<0>(lo, hi);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) mfma_acc(dv[db], u32x4{lo[db].x, lo[db].y, hi[db].x, hi[db].y}, p1);
+    read_v<D, 0>(st, off, lo, hi);
+    lgkm_wait<0>(lo, hi);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) mfma_acc(dk[db], u32x4{lo[db].x, lo[db].y, hi[db].x, hi[db].y}, d0);
+    read_v<D, 16 * (2 * D)>(st, off, lo, hi);
+    lgkm_wait<0>(lo, hi);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) mfma_acc(dk[db], u32x4{lo[db].x, lo[db].y, hi[db].x, hi[db].y}, d1);
+  }
+  drain_acc(dk);
+  drain_acc(dv);
+  if (key_ok) {
+    uint16_t* kout = p.dk + b * p.dk_bs + (int64_t)key * p.dk_ss + kvh * p.dk_hs;
+    uint16_t* vout = p.dv + b * p.dv_bs + (int64_t)key * p.dv_ss + kvh * p.dv_hs;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x8 x = {}, y = {};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = dk[db][4 * q4 + e] * p.scale;
+          y[e] = dv[db][4 * q4 + e];
+        }
+        const u32x4 xb = __builtin_bit_cast(u32x4, __builtin_convertvector(x, bf16x8));
+        const u32x4 yb = __builtin_bit_cast(u32x4, __builtin_convertvector(y, bf16x8));
+        *reinterpret_cast<u32x2*>(kout + 32 * db + 8 * q4 + 4 * kg) = u32x2{xb.x, xb.y};
+        *reinterpret_cast<u32x2*>(vout + 32 * db + 8 * q4 + 4 * kg) = u32x2{yb.x, yb.y};
+      }
+  }
+}
+
 // ------------------------------------------------------------------ launch helpers
 int device_cus() {
   static thread_local int cached_dev = -1;
@@ -1413,5 +1795,27 @@ hipError_t fa_launch_rotary(const FaRotaryParams& p, int d, hipStream_t s) {
     hipLaunchKernelGGL(fa_rotary_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t fa_launch_bwd(const FaBwdParams& p, int d, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
+  if (rows <= 0 || p.Nk <= 0) return hipSuccess;
+  int64_t blocks = (rows * (d / 8) + kThreads - 1) / kThreads;  // one 16-byte chunk per lane
+  const int64_t cap = 16 * (int64_t)device_cus();
+  if (blocks > cap) blocks = cap;
+  const int64_t dq_tiles = (int64_t)((p.Nq + 127) / 128) * p.B * p.Hq;
+  const int64_t dkv_tiles = (int64_t)((p.Nk + 127) / 128) * p.B * p.Hkv;
+  if (d == 128) {
+    hipLaunchKernelGGL(fa_bwd_delta_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(fa_bwd_dq_kernel<128>, dim3((unsigned)dq_tiles), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<128>, dim3((unsigned)dkv_tiles), dim3(kThreads), 0, s, p);
+  } else if (d == 64) {
+    hipLaunchKernelGGL(fa_bwd_delta_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(fa_bwd_dq_kernel<64>, dim3((unsigned)dq_tiles), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<64>, dim3((unsigned)dkv_tiles), dim3(kThreads), 0, s, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }

@@ -219,6 +219,31 @@ int fa_rotary(void* x, int batch, int seqlen, int heads, int head_dim,
               const int64_t x_strides[3], const int32_t* position_base, const float* cos,
               const float* sin, int rotary_dim, int interleaved, void* stream);
 
+/* Backward pass of the dense forward ("Attention kernels ...", section 4.3: the
+ * backward recomputes S = Q K^T by blocks and P = exp(S - L) from the saved
+ * log-sum-exp L, then dV = P^T dO and dS; "01 FlashAttention project overview &
+ * architecture", section 1 directory map: a preprocess forms D_i = rowsum(dO_i * O_i)).  With
+ * dP = dO V^T and dS = P (dP - D):  dQ = scale dS K,  dK = scale dS^T Q,
+ * dV = P^T dO, where dK and dV of a KV head sum over the query heads that share it.
+ *   q, out, dout, dq  [batch, seqlen_q, heads_q, head_dim]  (strides {batch, seq, head})
+ *   k, v, dk, dv      [batch, seqlen_k, heads_kv, head_dim]
+ *   lse               float32 [batch, heads_q, seqlen_q]: the forward's LSE (natural log)
+ *   dq, dk, dv        bf16, written (every element, zeros where nothing flows)
+ *   workspace         device memory of at least fa_bwd_workspace_size(...) bytes (holds D)
+ * opts as for fa_fwd (same scale, causal, window); softcap > 0 is FA_ERR_UNSUPPORTED.
+ * Three kernels on the stream: D, then dQ (per query block), then dK/dV (per key block).
+ * Deterministic: no atomics. */
+int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v, const void* out,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv, int batch,
+           int seqlen_q, int seqlen_k, int heads_q, int heads_kv, int head_dim,
+           const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+           const int64_t o_strides[3], const int64_t do_strides[3], const int64_t dq_strides[3],
+           const int64_t dk_strides[3], const int64_t dv_strides[3], void* workspace,
+           size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_bwd needs: batch * heads_q * seqlen_q * 4 rounded up to 256. */
+size_t fa_bwd_workspace_size(int batch, int seqlen_q, int heads_q);
+
 /* Merge of partial attention states ("Attention kernels ...", section 6.3: the
  * partial (O_s, LSE_s) of disjoint key ranges combine with the same rescale as
  * the tiles of one pass):

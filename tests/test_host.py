@@ -5,6 +5,7 @@ error codes before anything touches the device."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -264,3 +265,71 @@ def test_varlen_paged_rejects_invalid_arguments():
     assert call(B=0) == FA_ERR_INVALID_ARG
     assert call(page=24) == FA_ERR_UNSUPPORTED
     assert call(Hq=30) == FA_ERR_INVALID_ARG
+
+
+QUERY_RANGE_CHECK = r"""
+#include <stdio.h>
+#include "fa_blockinfo.h"
+static int visible(long i, long j, long Lq, long Lk, int causal, int wl, int wr) {
+  long p = i + Lk - Lq;
+  if (j < 0 || j >= Lk) return 0;
+  if (causal && j > p) return 0;
+  if (wl >= 0 && j < p - wl) return 0;
+  if (wr >= 0 && j > p + wr) return 0;
+  return 1;
+}
+int main(void) {
+  unsigned x = 777u;
+  long bad = 0, cases = 0;
+  for (int it = 0; it < 20000; ++it) {
+    x = x * 1103515245u + 12345u; long Lq = 1 + (x >> 8) % 300;
+    x = x * 1103515245u + 12345u; long Lk = 1 + (x >> 8) % 300;
+    x = x * 1103515245u + 12345u; int causal = (x >> 8) & 1;
+    x = x * 1103515245u + 12345u; int wl = (int)((x >> 8) % 120) - 40; if (wl < 0) wl = -1;
+    x = x * 1103515245u + 12345u; int wr = (int)((x >> 8) % 120) - 40; if (wr < 0) wr = -1;
+    x = x * 1103515245u + 12345u; long j_lo = (x >> 8) % Lk;
+    x = x * 1103515245u + 12345u; long j_hi = j_lo + (x >> 8) % 64; if (j_hi >= Lk) j_hi = Lk - 1;
+    int64_t lo, hi;
+    fa_query_range(j_lo, j_hi, Lq, Lk, causal, wl, wr, &lo, &hi);
+    for (long i = 0; i < Lq; ++i) {
+      int sees = 0;
+      for (long j = j_lo; j <= j_hi; ++j) sees |= visible(i, j, Lq, Lk, causal, wl, wr);
+      int in = i >= lo && i < hi;
+      cases++;
+      if (sees && !in) bad++;          /* a row that sees the block must be in the range */
+      if (in && !sees) bad++;          /* and the range is exact */
+    }
+  }
+  printf("%ld %ld\n", bad, cases);
+  return bad != 0;
+}
+"""
+
+
+def test_query_range_matches_brute_force(tmp_path):
+    """The query rows that see a key block (the backward's loop bounds over query
+    blocks), against the visibility predicate on every row of random shapes."""
+    src = tmp_path / "qr.cpp"
+    src.write_text(QUERY_RANGE_CHECK)
+    exe = tmp_path / "qr"
+    inc = os.path.join(ROOT, "exact_attention_72_amd", "csrc")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", inc, str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    bad, cases = map(int, r.stdout.split())
+    assert cases > 1_000_000 and bad == 0, r.stdout
+
+
+def test_bwd_rejects_invalid_arguments():
+    L = api.lib()
+    def call(opts=None, q=FAKE, d=128, B=1, ws=FAKE, ws_bytes=1 << 20, Hq=16, Hkv=16):
+        o = opts or _opts()
+        return L.fa_bwd(ctypes.byref(o), q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, 16, 16, Hq, Hkv, d,
+                        S3, S3, S3, S3, S3, S3, S3, S3, ws, ws_bytes, None)
+    assert call(q=None) == FA_ERR_INVALID_ARG
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(B=0) == FA_ERR_INVALID_ARG
+    assert call(Hq=6, Hkv=4) == FA_ERR_INVALID_ARG
+    assert call(ws=None) == FA_ERR_INVALID_ARG
+    assert call(ws_bytes=16) == FA_ERR_INVALID_ARG
+    assert call(opts=_opts(softcap=30.0)) == FA_ERR_UNSUPPORTED
+    assert api.lib().fa_bwd_workspace_size(4, 4096, 16) == 4 * 16 * 4096 * 4
