@@ -8,8 +8,8 @@ the varlen GQA prefill (32 sequences of 64..8192 tokens, 32/4 heads, packed),
 the long-context local attention with softcap (N = 32768, 32 heads,
 window 4096, softcap 30), and the chunked prefill over a paged cache (4 x 4096
 new tokens against 16384 cached keys, 32/8 heads) with the in-place K/V append
-of that chunk, and a unified batch of 64 decode requests and 4 prefill chunks
-in one launch.
+of that chunk, a unified batch of 64 decode requests and 4 prefill chunks
+in one launch, and the backward pass of the prefill workload.
 
 Prints one JSON line:
   value        prefill TFLOP/s, FLOPs counted as 4 * B * H * N^2 * d * 1/2 (the
@@ -258,6 +258,33 @@ def bench_unified(api, W, steps, warmup):
                        "page_size": c["page"], "flop_convention": "4*d*Hq*sum visible pairs"}}
 
 
+def bench_bwd(api, W, steps, warmup):
+    """Backward of the dense causal prefill workload (batch 4, 16 heads, N = 4096, d = 128):
+    fa_bwd per call (D preprocess, dQ kernel, dK/dV kernel).  FLOPs: 2.5 x the forward's
+    4 B H N^2 d / 2 (five products against the forward's two, "Attention kernels...",
+    section 4.3); the recomputation the kernels add is not counted."""
+    import torch
+    c = W.WORKLOADS["prefill_b4_h16_n4096_d128_causal"]
+    B, N, H, d = c["B"], c["N"], c["Hq"], c["d"]
+    t = W.dense(c["seed"], B, N, H, c["Hkv"], d, device="cuda")
+    do = W.randn_bf16(W.generator(c["seed"] + 100, "cuda"), (B, N, H, d), 1.0, "cuda")
+    out, lse = api.fa_fwd(t["q"], t["k"], t["v"], causal=True)
+    dq, dk, dv = (torch.empty_like(t[n]) for n in "qkv")
+    ws = torch.empty(api.lib().fa_bwd_workspace_size(B, N, H), dtype=torch.uint8, device="cuda")
+    fn = lambda: api.fa_bwd(t["q"], t["k"], t["v"], out, lse, do, causal=True, dq=dq, dk=dk, dv=dv,  # noqa
+                            workspace=ws)
+    wall, ms = time_launches(fn, steps, warmup)
+    flops = 2.5 * prefill_flops(B, H, N, d, True)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"metric": "attn bwd TFLOP/s (bf16 N=4k d=128 causal)", "unit": "TFLOP/s", "value": round(tf, 2),
+            "ms": round(ms, 4), "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
+            "config": {"workload": "prefill_b4_h16_n4096_d128_causal backward", "batch": B, "heads": H,
+                       "seq_len": N, "head_dim": d, "causal": True,
+                       "flop_convention": "2.5 * 4*B*H*N^2*d/2"}}
+
+
 def bench_decode(api, W, steps, warmup):
     import torch
     c = W.WORKLOADS["paged_decode_b64_h32kv8_d128_page256"]
@@ -303,6 +330,7 @@ def main():
     ap.add_argument("--no-local", action="store_true")
     ap.add_argument("--no-paged-prefill", action="store_true")
     ap.add_argument("--no-unified", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -364,6 +392,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_unified:
         line["unified"] = bench_unified(api, W, max(10, args.steps // 5), max(5, args.warmup // 5))
+        torch.cuda.empty_cache()
+    if not args.no_bwd:
+        line["bwd"] = bench_bwd(api, W, max(10, args.steps // 5), max(5, args.warmup // 5))
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         tc = W.dense(c["seed"], B, N, H, c["Hkv"], d)

@@ -255,6 +255,20 @@ __device__ __forceinline__ void read_k(uint32_t delta, const LaneOffsets<D>& off
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) a[kk] = ds_read_b128<OFF>(off.k(kk) + delta);
 }
+template <int D, int OFF, int K0, int NK>
+__device__ __forceinline__ void read_k_part(uint32_t delta, const LaneOffsets<D>& off, u32x4 (&a)[D / 16]) {
+#pragma unroll
+  for (int kk = K0; kk < K0 + NK; ++kk) a[kk] = ds_read_b128<OFF>(off.k(kk) + delta);
+}
+template <int D, int OFF, int DB0, int NDB>
+__device__ __forceinline__ void read_v_part(uint32_t delta, const LaneOffsets<D>& off, u32x2 (&lo)[NDB],
+                                            u32x2 (&hi)[NDB]) {
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    lo[i] = ds_read_tr16<OFF>(off.v(DB0 + i) + delta);
+    hi[i] = ds_read_tr16<OFF + 8 * (2 * D)>(off.v(DB0 + i) + delta);
+  }
+}
 template <int D, int OFF>
 __device__ __forceinline__ void read_v(uint32_t delta, const LaneOffsets<D>& off, u32x2 (&lo)[D / 32],
                                        u32x2 (&hi)[D / 32]) {
@@ -1356,17 +1370,21 @@ __device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t stride, i
 }
 
 // O^T-style product with the accumulator in AGPRs (the dK/dV kernel holds two
-// gradient tiles, more than its VGPRs); a reader of the accumulators waits
-// with drain_acc first.
+// gradient tiles, more than its VGPRs).  The compiler does not know this is a
+// matrix product, so nothing else may touch the accumulators (a read, or a copy
+// it makes to move them between registers) until drain_acc has covered the
+// product's latency.
 __device__ __forceinline__ void mfma_acc(f32x16& acc, u32x4 a, bf16x8 b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// 20 wait states after the last mfma_acc on either set, tied to both sets.
 template <int N>
-__device__ __forceinline__ void drain_acc(f32x16 (&a)[N]) {
+__device__ __forceinline__ void drain_acc(f32x16 (&a)[N], f32x16 (&b)[N]) {
   if constexpr (N == 4) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(b[0]), "+a"(b[1]), "+a"(b[2]), "+a"(b[3]));
   } else {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(a[0]), "+a"(a[1]));
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(a[0]), "+a"(a[1]), "+a"(b[0]), "+a"(b[1]));
   }
 }
 
@@ -1594,20 +1612,31 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     if (s_ + NBUF - 1 < steps) issue(s_ + NBUF - 1);
     const uint32_t st = (uint32_t)((s_ % NBUF) * kStage);
     const int q0 = (qb_lo + s_ % nqb) * BM;
-    u32x4 qa[D / 16];
-    read_k<D, 0>(st, off, qa);
-    lgkm_wait<0>(qa);
+    // element masks only where the query block cuts the wave's 32 keys (or runs past Lq)
+    FaRowSpan qs;
+    qs.pos_lo = (int64_t)q0 + (Lk - Lq);
+    qs.pos_hi = (int64_t)q0 + BM - 1 + (Lk - Lq);
+    const int kw = j0 + wave * 32;
+    const bool full = q0 + BM <= Lq && kw + 32 <= Lk &&
+                      fa_tile_class(qs, Lk, p.causal, p.wl, p.wr, 32, kw / 32) == FA_TILE_VISIBLE;
+    // Reads stay in flight behind the products that wait for the ones before them
+    // (LDS reads complete in issue order, so a wait names how many of the latest
+    // may still be outstanding); at most 12 are in flight at a time.
+    u32x4 qa[D / 16], oa[D / 16];
+    read_k_part<D, 0, 0, D / 32>(st, off, qa);
+    read_k_part<D, 0, D / 32, D / 32>(st, off, qa);
+    read_k_part<D, 0, 0, D / 32>(st + 2 * T, off, oa);
+    lgkm_wait<D / 32>(qa);
+    read_k_part<D, 0, D / 32, D / 32>(st + 2 * T, off, oa);
     f32x16 s = qk_mma<D>(qa, kreg);  // S = Q K^T: rows queries, lane column = this key
-    read_k<D, 0>(st + 2 * T, off, qa);
-    lgkm_wait<0>(qa);
-    const f32x16 dp = qk_mma<D>(qa, vreg);  // dP = dO V^T
     // L and D of the accumulator rows: rows 8 j + 4 kg .. + 3 are slots 4 j .. 4 j + 3
     u32x4 lr[4], dr[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      lr[jj] = ds_read_b128<0>(ld_base + st + 32 * jj);
-      dr[jj] = ds_read_b128<128>(ld_base + st + 32 * jj);
-    }
+    for (int jj = 0; jj < 4; ++jj) lr[jj] = ds_read_b128<0>(ld_base + st + 32 * jj);
+    lgkm_wait<4>(oa);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dr[jj] = ds_read_b128<128>(ld_base + st + 32 * jj);
+    const f32x16 dp = qk_mma<D>(oa, vreg);  // dP = dO V^T
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lr[0]), "+v"(lr[1]), "+v"(lr[2]), "+v"(lr[3]), "+v"(dr[0]),
                  "+v"(dr[1]), "+v"(dr[2]), "+v"(dr[3]));
     f32x8 p0f, p1f, d0f, d1f;
@@ -1615,8 +1644,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     for (int a = 0; a < 16; ++a) {
       const int qi = q0 + 8 * (a >> 2) + 4 * kg + (a & 3);
       const int pos = qi + (Lk - Lq);
-      const bool vis = key_ok && qi < Lq && (!p.causal || key <= pos) && (p.wl < 0 || key >= pos - p.wl) &&
-                       (p.wr < 0 || key <= pos + p.wr);
+      const bool vis = full || (key_ok && qi < Lq && (!p.causal || key <= pos) && (p.wl < 0 || key >= pos - p.wl) &&
+                                (p.wr < 0 || key <= pos + p.wr));
       const float l = __uint_as_float(lr[a >> 2][a & 3]);
       const float dl = __uint_as_float(dr[a >> 2][a & 3]);
       const float nl = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
@@ -1632,27 +1661,60 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     }
     const bf16x8 p0 = __builtin_convertvector(p0f, bf16x8), p1 = __builtin_convertvector(p1f, bf16x8);
     const bf16x8 d0 = __builtin_convertvector(d0f, bf16x8), d1 = __builtin_convertvector(d1f, bf16x8);
-    // dV^T += dO^T P (dO read transposed), dK^T += Q^T dS (Q read transposed)
-    u32x2 lo[D / 32], hi[D / 32];
-    read_v<D, 0>(st + 2 * T, off, lo, hi);
-    lgkm_wait<0>(lo, hi);
+    // dV^T += dO^T P (dO read transposed), dK^T += Q^T dS (Q read transposed), in
+    // eight units of D / 64 d-blocks: unit u reads chunk u / 2 (dO^T keys 0..15,
+    // dO^T keys 16..31, Q^T keys 0..15, Q^T keys 16..31), half u % 2 of the
+    // d-blocks.  Three units are in flight while a fourth feeds its products; each
+    // unit has registers of its own, so a read never lands in operands of products
+    // still waiting to start.
+    constexpr int UD = D / 64, UR = 2 * UD;
+    u32x2 lo[8][UD], hi[8][UD];
+    auto rd = [&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value, c = u / 2;
+      read_v_part<D, (c & 1) * 16 * (2 * D), (u % 2) * UD, UD>(c < 2 ? st + 2 * T : st, off, lo[u], hi[u]);
+    };
+    auto wt = [&lo, &hi](auto uc, auto nc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value, n = decltype(nc)::value;
+      asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(n));
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) mfma_acc(dv[db], u32x4{lo[db].x, lo[db].y, hi[db].x, hi[db].y}, p0);
-    read_v<D, 16 * (2 * D)>(st + 2 * T, off, lo, hi);
-    lgkm_wait<0>(lo, hi);
+      for (int i = 0; i < UD; ++i) asm volatile("" : "+v"(lo[u][i]), "+v"(hi[u][i]));
+    };
+    auto mm = [&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value, c = u / 2, h = u % 2;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) mfma_acc(dv[db], u32x4{lo[db].x, lo[db].y, hi[db].x, hi[db].y}, p1);
-    read_v<D, 0>(st, off, lo, hi);
-    lgkm_wait<0>(lo, hi);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) mfma_acc(dk[db], u32x4{lo[db].x, lo[db].y, hi[db].x, hi[db].y}, d0);
-    read_v<D, 16 * (2 * D)>(st, off, lo, hi);
-    lgkm_wait<0>(lo, hi);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) mfma_acc(dk[db], u32x4{lo[db].x, lo[db].y, hi[db].x, hi[db].y}, d1);
+      for (int i = 0; i < UD; ++i) {
+        const u32x4 a = {lo[u][i].x, lo[u][i].y, hi[u][i].x, hi[u][i].y};
+        if constexpr (c == 0) mfma_acc(dv[h * UD + i], a, p0);
+        if constexpr (c == 1) mfma_acc(dv[h * UD + i], a, p1);
+        if constexpr (c == 2) mfma_acc(dk[h * UD + i], a, d0);
+        if constexpr (c == 3) mfma_acc(dk[h * UD + i], a, d1);
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    using I6 = std::integral_constant<int, 6>;
+    using I7 = std::integral_constant<int, 7>;
+    using W2 = std::integral_constant<int, 2 * UR>;
+    using W1 = std::integral_constant<int, UR>;
+    using W0 = std::integral_constant<int, 0>;
+    rd(I0{}), rd(I1{}), rd(I2{});
+    wt(I0{}, W2{}), rd(I3{}), mm(I0{});
+    wt(I1{}, W2{}), rd(I4{}), mm(I1{});
+    wt(I2{}, W2{}), rd(I5{}), mm(I2{});
+    wt(I3{}, W2{}), rd(I6{}), mm(I3{});
+    wt(I4{}, W2{}), rd(I7{}), mm(I4{});
+    wt(I5{}, W2{}), mm(I5{});
+    wt(I6{}, W1{}), mm(I6{});
+    wt(I7{}, W0{}), mm(I7{});
+    // Settle the accumulators before the step ends: the compiler may copy them
+    // between registers at the loop's edges and does not see that the products
+    // above are still writing them.
+    drain_acc(dk, dv);
   }
-  drain_acc(dk);
-  drain_acc(dv);
   if (key_ok) {
     uint16_t* kout = p.dk + b * p.dk_bs + (int64_t)key * p.dk_ss + kvh * p.dk_hs;
     uint16_t* vout = p.dv + b * p.dv_bs + (int64_t)key * p.dv_ss + kvh * p.dv_hs;
