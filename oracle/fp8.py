@@ -1,0 +1,186 @@
+"""FP8 (e4m3) part of the oracle: exact decoding and encoding of the 8-bit
+format, the per-block quantizer, and fp64 attention over dequantized inputs.
+
+TEST INFRASTRUCTURE ONLY (like the rest of this package): the tests, the smoke
+check and the CPU-baseline leg of the benchmark may use it; the library never
+does.  Plain numpy, no code shared with the HIP path.
+
+"Attention kernels: FlashAttention and PagedAttention", section 4.2 (the FP8
+item) and "01 FlashAttention project overview & architecture", section 2.2 (the
+FP8 E4M3 forward): Q, K and V enter the products as FP8 e4m3, with per-block
+scales to keep the precision.
+The format is the OCP 8-bit float E4M3 (the one gfx950's matrix units and
+conversions use): 1 sign, 4 exponent (bias 7) and 3 mantissa bits; exponent
+field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN; there is no infinity;
+the largest finite magnitude is 1.75 * 2^8 = 448.
+
+Readings (the pages name the scheme, not its details):
+- a block's scale is amax / 448 in fp32 (1 for an all-zero block), and a code is
+  the e4m3 rounding (to nearest, ties to even, saturating at 448) of the fp32
+  quotient x / scale: the same fp32 operations the GPU quantizer performs, so
+  both sides take every rounding decision on the same fp32 number;
+- Q is scaled per (batch, head, block of query rows), K per (batch, KV head,
+  block of keys), V per (batch, KV head): the P V product accumulates across
+  key blocks into one accumulator, so one V scale per head multiplies the
+  result once.
+
+Parity pins: tests/test_oracle_pins.py (the "fp8" section).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Exact value of each e4m3 code (uint8) as float64; NaN codes give NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & ((c & 0x7) == 7), np.nan, out)
+
+
+# the 127 finite non-negative codes 0x00..0x7E in increasing order of value
+_GRID = e4m3_decode(np.arange(127, dtype=np.uint8))
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round each value to the nearest e4m3 code, ties to the even code, with
+    magnitudes beyond 448 saturating to 448 and NaN giving 0x7F.  The sign of the
+    input (also of -0.0 and of values that round to zero) is kept."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(_GRID, a, side="left"), 1, 126)   # _GRID[hi-1] < a <= _GRID[hi]
+    lo = hi - 1
+    dlo, dhi = a - _GRID[lo], _GRID[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a >= E4M3_MAX, 126, pick)
+    pick = np.where(a == 0, 0, pick)
+    code = pick.astype(np.uint8) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def _bf16_to_f32(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _quantize_block(xb: np.ndarray):
+    """xb: fp32 values of one block -> (codes, fp32 scale)."""
+    amax = np.float32(np.abs(xb).max()) if xb.size else np.float32(0)
+    scale = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    y = (xb / scale).astype(np.float32)          # one fp32 division per element, rounded to nearest
+    return e4m3_encode(y), scale
+
+
+def quantize_rows(x, block: int):
+    """Per-block quantizer of a [B, N, H, d] bf16 tensor (bit patterns): one scale
+    per (batch, head, block of `block` rows).  Returns (codes uint8 [B, N, H, d],
+    scales float32 [B, H, ceil(N / block)])."""
+    xf = _bf16_to_f32(x)
+    B, N, H, d = xf.shape
+    nb = -(-N // block)
+    codes = np.zeros(xf.shape, dtype=np.uint8)
+    scales = np.ones((B, H, nb), dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                sl = slice(i * block, min(N, (i + 1) * block))
+                codes[b, sl, h], scales[b, h, i] = _quantize_block(xf[b, sl, h])
+    return codes, scales
+
+
+def quantize_heads(x):
+    """Per-head quantizer of a [B, N, H, d] bf16 tensor: one scale per (batch,
+    head).  Returns (codes uint8 [B, N, H, d], scales float32 [B, H])."""
+    xf = _bf16_to_f32(x)
+    B, N, H, d = xf.shape
+    codes = np.zeros(xf.shape, dtype=np.uint8)
+    scales = np.ones((B, H), dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            codes[b, :, h], scales[b, h] = _quantize_block(xf[b, :, h])
+    return codes, scales
+
+
+def dequantize(codes, scales, block=None) -> np.ndarray:
+    """fp64 values of quantized [B, N, H, d] codes: scales [B, H, nblk] with rows in
+    blocks of `block`, or [B, H] when block is None."""
+    v = e4m3_decode(codes)
+    s = np.asarray(scales, dtype=np.float64)
+    if block is None:
+        return v * s[:, None, :, None]
+    N = v.shape[1]
+    idx = np.arange(N) // block
+    return v * np.transpose(s[:, :, idx], (0, 2, 1))[..., None]
+
+
+def _visible(Lq, Lk, causal, window):
+    """Key j is visible to query i (bottom-right: query i sits at key position
+    i + Lk - Lq) inside the causal limit and the window [p - left, p + right]."""
+    p = np.arange(Lq)[:, None] + (Lk - Lq)
+    j = np.arange(Lk)[None, :]
+    vis = np.ones((Lq, Lk), dtype=bool)
+    if causal:
+        vis &= j <= p
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            vis &= j >= p - left
+        if right >= 0:
+            vis &= j <= p + right
+    return vis
+
+
+def fwd(q, q_scales, q_block, k, k_scales, k_block, v, v_scales, *, scale=None, causal=False,
+        window=None, rows=None):
+    """Attention over the dequantized FP8 inputs, in fp64 with S and P materialised.
+
+    q: codes [B, Nq, Hq, d] with q_scales [B, Hq, ceil(Nq / q_block)]; k: codes
+    [B, Nk, Hkv, d] with k_scales [B, Hkv, ceil(Nk / k_block)]; v: codes
+    [B, Nk, Hkv, d] with v_scales [B, Hkv].  Query head h uses KV head h // (Hq / Hkv).
+    rows: None for all query rows, or a list of row indices (then O and LSE hold
+    those rows only, in that order).  Returns (O float64 [B, rows, Hq, d],
+    LSE float64 [B, Hq, rows]); a row that sees no key gets O = 0, LSE = -inf.
+    """
+    qd = dequantize(q, q_scales, q_block)
+    kd = dequantize(k, k_scales, k_block)
+    vd = dequantize(v, v_scales)
+    B, Nq, Hq, d = qd.shape
+    Nk, Hkv = kd.shape[1], kd.shape[2]
+    g = Hq // Hkv
+    s = d ** -0.5 if scale is None else scale
+    sel = np.arange(Nq) if rows is None else np.asarray(rows)
+    vis = _visible(Nq, Nk, causal, window)[sel]
+    O = np.zeros((B, len(sel), Hq, d))
+    L = np.full((B, Hq, len(sel)), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            S = s * (qd[b, sel, h] @ kd[b, :, h // g].T)
+            S = np.where(vis, S, -np.inf)
+            m = S.max(axis=1, keepdims=True)
+            ok = np.isfinite(m[:, 0])
+            E = np.exp(S - np.where(np.isfinite(m), m, 0.0))
+            l = E.sum(axis=1)
+            O[b, ok, h] = (E[ok] / l[ok, None]) @ vd[b, :, h // g]
+            L[b, h, ok] = m[ok, 0] + np.log(l[ok])
+    return O, L
+
+
+def probs(q, q_scales, q_block, k, k_scales, k_block, *, row, b, h, g, scale=None, causal=False,
+          window=None):
+    """fp64 softmax weights of one query row (batch b, query head h) over all keys."""
+    qd = dequantize(q, q_scales, q_block)
+    kd = dequantize(k, k_scales, k_block)
+    Nq, d = qd.shape[1], qd.shape[3]
+    Nk = kd.shape[1]
+    s = d ** -0.5 if scale is None else scale
+    S = s * (kd[b, :, h // g] @ qd[b, row, h])
+    S = np.where(_visible(Nq, Nk, causal, window)[row], S, -np.inf)
+    if not np.isfinite(S.max()):
+        return np.zeros(Nk)
+    E = np.exp(S - S.max())
+    return E / E.sum()

@@ -508,3 +508,113 @@ def test_bwd_key_gradients_sum_to_zero_and_empty_rows():
     assert np.abs(dk.sum(axis=1)).max() < 1e-11
     assert np.array_equal(dq[:, : Nq - Nk], np.zeros_like(dq[:, : Nq - Nk]))   # rows at positions < 0
     assert np.abs(dq[:, Nq - Nk:]).max() > 0.01
+
+
+# ---------------------------------------------------------------- fp8
+from oracle import fp8 as F8   # noqa: E402
+
+
+def test_fp8_decode_spec_values_and_library_type():
+    """OCP E4M3 values from the format's definition, and every code against torch's
+    float8_e4m3fn (an independent implementation of the same format)."""
+    d = F8.e4m3_decode(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x40, 0x7E, 0xFE, 0x7F, 0xFF],
+                                dtype=np.uint8))
+    want = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.5, 2.0, 448.0, -448.0]
+    assert list(d[:9]) == want and np.isnan(d[9]) and np.isnan(d[10])
+    assert np.signbit(F8.e4m3_decode(np.array([0x80], dtype=np.uint8))[0])
+    c = np.arange(256, dtype=np.uint8)
+    t = torch.tensor(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    a = F8.e4m3_decode(c)
+    assert np.all((a == t) | (np.isnan(a) & np.isnan(t)))
+    assert np.all(np.diff(a[:127]) > 0)          # 0x00..0x7E increase strictly
+
+
+def test_fp8_encode_nearest_ties_to_even_and_saturation():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.uniform(-470, 470, 4000), rng.standard_normal(4000) * 0.02,
+                        rng.standard_normal(2000) * 2.0 ** -8]).astype(np.float32).astype(np.float64)
+    grid = F8.e4m3_decode(np.arange(127, dtype=np.uint8))
+    e = F8.e4m3_encode(x)
+    for xi, ci in zip(x[:3000], e[:3000]):      # brute force over the finite codes
+        a = min(abs(xi), 448.0)
+        dist = np.abs(grid - a)
+        best = np.flatnonzero(dist == dist.min())
+        want = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+        assert (ci & 0x7F) == want and (ci >> 7) == (1 if np.signbit(xi) else 0)
+    inr = np.abs(x) <= 448
+    t = torch.tensor(x[inr], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(e[inr], t)
+    # ties: 1.0625 between 1.0 (0x38) and 1.125 (0x39) -> even 0x38; 1.1875 -> 0x3A;
+    # 3 * 2^-10 between 2^-9 (0x01) and 2^-8 (0x02) -> 0x02; 2^-10 -> 0
+    ties = F8.e4m3_encode(np.array([1.0625, 1.1875, 3 * 2.0 ** -10, 2.0 ** -10, 464.0, 1e6, -500.0]))
+    assert list(ties) == [0x38, 0x3A, 0x02, 0x00, 0x7E, 0x7E, 0xFE]
+    assert F8.e4m3_encode(np.array([np.nan]))[0] == 0x7F
+    assert F8.e4m3_encode(np.array([-0.0]))[0] == 0x80
+
+
+def test_fp8_quantizer_block_max_and_error_bound():
+    g = W.generator(41)
+    x = W.randn_bf16(g, (2, 200, 3, 64), 3.0)
+    codes, scales = F8.quantize_rows(bits(x), 64)
+    assert scales.shape == (2, 3, 4)
+    xf = x.float().numpy().astype(np.float64)
+    deq = F8.dequantize(codes, scales, 64)
+    for b in range(2):
+        for h in range(3):
+            for i in range(4):
+                blk = xf[b, i * 64:(i + 1) * 64, h]
+                c = codes[b, i * 64:(i + 1) * 64, h]
+                s = np.float32(np.float32(np.abs(blk).max()) / np.float32(448))
+                assert scales[b, h, i] == s
+                at = np.unravel_index(np.abs(blk).argmax(), blk.shape)
+                assert (c[at] & 0x7F) == 0x7E                      # the block maximum is +-448
+    # each value within half a code spacing: 2^-4 relative (normal codes), 2^-10 * scale below
+    err = np.abs(deq - xf)
+    sc = np.transpose(scales[:, :, np.arange(200) // 64], (0, 2, 1))[..., None].astype(np.float64)
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(xf), 2.0 ** -10 * sc) * (1 + 1e-6))
+    # an all-zero block: scale 1, codes 0
+    z = torch.zeros(1, 64, 1, 16, dtype=torch.bfloat16)
+    zc, zs = F8.quantize_rows(bits(z), 64)
+    assert zs[0, 0, 0] == 1.0 and not zc.any()
+    vc, vs = F8.quantize_heads(bits(x))
+    assert vs.shape == (2, 3) and np.all(np.abs(F8.e4m3_decode(vc)).max(axis=(1, 3)) == 448.0)
+
+
+@pytest.mark.parametrize("causal,window,Hq,Hkv", [(True, None, 4, 2), (False, None, 2, 2),
+                                                  (True, (40, 0), 4, 1), (False, (20, 11), 2, 1)])
+def test_fp8_attention_matches_the_bf16_oracle_on_exact_inputs(causal, window, Hq, Hkv):
+    """With power-of-two scales every dequantized value is a bf16 number, so the fp8
+    attention must equal the C oracle's bf16 attention on those values."""
+    rng = np.random.default_rng(7 + Hq)
+    B, Nq, Nk, d = 2, 70, 90, 32
+    def codes(shape):   # finite codes of moderate magnitude (|value| in [2^-9, 8])
+        c = rng.integers(0, 0x50, size=shape).astype(np.uint8)
+        return c | (rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+    q8, k8, v8 = codes((B, Nq, Hq, d)), codes((B, Nk, Hkv, d)), codes((B, Nk, Hkv, d))
+    qs = np.exp2(rng.integers(-3, 2, size=(B, Hq, 2))).astype(np.float32)
+    ks = np.exp2(rng.integers(-3, 2, size=(B, Hkv, 2))).astype(np.float32)
+    vs = np.exp2(np.arange(Hkv)[None, :] - 1 + rng.integers(0, 2, size=(B, 1))).astype(np.float32)  # distinct per head
+    O, L = F8.fwd(q8, qs, 64, k8, ks, 64, v8, vs, causal=causal, window=window)
+    def to_bf16_bits(a):
+        f = torch.tensor(a, dtype=torch.float64).to(torch.float32)
+        bb = f.to(torch.bfloat16)
+        assert torch.equal(bb.to(torch.float32), f)              # exact in bf16
+        return bb.view(torch.int16).numpy().view(np.uint16)
+    def deq(c, sc, block):   # written here from the definition, not through F8.dequantize
+        val = torch.tensor(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        out = np.empty_like(val)
+        for b in range(val.shape[0]):
+            for h in range(val.shape[2]):
+                for n in range(val.shape[1]):
+                    out[b, n, h] = val[b, n, h] * (sc[b, h] if block is None else sc[b, h, n // block])
+        return out
+    qd, kd, vd = deq(q8, qs, 64), deq(k8, ks, 64), deq(v8, vs, None)
+    ro, rl = oracle.fwd_dense(to_bf16_bits(qd), to_bf16_bits(kd), to_bf16_bits(vd), causal=causal,
+                              window=window)
+    np.testing.assert_allclose(O, ro, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(L, rl, rtol=0, atol=1e-11)
+    rows = [0, 33, 69]
+    Or, Lr = F8.fwd(q8, qs, 64, k8, ks, 64, v8, vs, causal=causal, window=window, rows=rows)
+    assert np.array_equal(Or, O[:, rows]) and np.array_equal(Lr, L[:, :, rows])
+    p = F8.probs(q8, qs, 64, k8, ks, 64, row=50, b=1, h=Hq - 1, g=Hq // Hkv, causal=causal, window=window)
+    assert abs(p.sum() - 1) < 1e-12
