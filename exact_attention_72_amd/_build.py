@@ -24,7 +24,7 @@ def hipcc() -> str:
 
 
 def sources():
-    return [os.path.join(CSRC, f) for f in ("fa_kernels.hip", "fa_api.cpp")]
+    return [os.path.join(CSRC, f) for f in ("fa_kernels.hip", "fa_fp8.hip", "fa_api.cpp")]
 
 
 def build(verbose: bool = False) -> str:

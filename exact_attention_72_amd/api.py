@@ -23,7 +23,11 @@ FA_ERR_HIP = -3
 
 EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_varlen_paged", "fa_kvcache_num_splits",
            "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary", "fa_bwd", "fa_bwd_workspace_size",
+           "fa_fp8_quantize", "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8",
            "fa_combine", "fa_tile_class", "fa_last_error", "fa_version")
+
+FA_FP8_Q_BLOCK = 128
+FA_FP8_K_BLOCK = 64
 
 
 class FaError(RuntimeError):
@@ -68,11 +72,16 @@ def lib():
     L.fa_bwd_workspace_size.restype = SZ
     L.fa_fwd_varlen_paged.argtypes = [OPT, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I64, I, I, S3, S3, S3,
                                       S3, P]
+    L.fa_fp8_quantize.argtypes = [P, I, I, I, I, S3, I, P, S3, P, P]
+    L.fa_fp8_quantize_v.argtypes = [P, I, I, I, I, S3, P, P, P]
+    L.fa_fp8_vt_len.argtypes = [I]
+    L.fa_fwd_fp8.argtypes = [OPT, P, P, P, P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, P]
     L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = I
     for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_combine", "fa_tile_class",
-                 "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary", "fa_bwd"):
+                 "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary", "fa_bwd", "fa_fp8_quantize",
+                 "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -340,3 +349,83 @@ def fa_version():
 
 def default_scale(d):
     return 1.0 / math.sqrt(d)
+
+
+def _u8_cuda(*ts):
+    for t in ts:
+        if t.dtype != torch.uint8 or not t.is_cuda:
+            raise TypeError("FP8 codes must be uint8 tensors on a HIP device")
+        if t.stride(-1) != 1:
+            raise ValueError("the head_dim dimension must be contiguous")
+
+
+def _f32_cuda(*ts):
+    for t in ts:
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError("scales must be contiguous float32 tensors on a HIP device")
+
+
+def fa_fp8_quantize(x, block_rows, *, codes=None, scales=None, stream=None):
+    """Per-block e4m3 quantizer.  x [B, N, H, d] bf16 -> (codes uint8 [B, N, H, d],
+    scales float32 [B, H, ceil(N / block_rows)])."""
+    _bf16_cuda(x)
+    B, N, H, d = x.shape
+    nblk = -(-N // block_rows)
+    if codes is None:
+        codes = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
+    _u8_cuda(codes)
+    _f32_cuda(scales)
+    if tuple(scales.shape) != (B, H, nblk):
+        raise ValueError(f"scales must be [{B}, {H}, {nblk}]")
+    _check(lib().fa_fp8_quantize(_ptr(x), B, N, H, d, _strides(x, (0, 1, 2)), int(block_rows), _ptr(codes),
+                                 _strides(codes, (0, 1, 2)), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def fa_fp8_quantize_v(v, *, vt=None, scales=None, stream=None):
+    """V quantizer: v [B, N, Hkv, d] bf16 -> (vt uint8 [B, Hkv, d, fa_fp8_vt_len(N)] in the
+    transposed, product-ordered layout, scales float32 [B, Hkv])."""
+    _bf16_cuda(v)
+    B, N, H, d = v.shape
+    L = lib().fa_fp8_vt_len(N)
+    if vt is None:
+        vt = torch.empty((B, H, d, L), dtype=torch.uint8, device=v.device)
+    if scales is None:
+        scales = torch.empty((B, H), dtype=torch.float32, device=v.device)
+    _u8_cuda(vt)
+    _f32_cuda(scales)
+    if not vt.is_contiguous() or tuple(vt.shape) != (B, H, d, L) or tuple(scales.shape) != (B, H):
+        raise ValueError(f"vt must be a dense [{B}, {H}, {d}, {L}] tensor and scales [{B}, {H}]")
+    _check(lib().fa_fp8_quantize_v(_ptr(v), B, N, H, d, _strides(v, (0, 1, 2)), _ptr(vt), _ptr(scales),
+                                   _stream(stream)))
+    return vt, scales
+
+
+def fa_fwd_fp8(q, q_scales, k, k_scales, vt, v_scales, *, softmax_scale=None, causal=False, window=None,
+               out=None, lse=None, return_lse=True, stream=None):
+    """FP8 forward.  q uint8 [B, Nq, Hq, d] with q_scales [B, Hq, ceil(Nq / 128)], k uint8
+    [B, Nk, Hkv, d] with k_scales [B, Hkv, ceil(Nk / 64)], vt / v_scales from fa_fp8_quantize_v
+    -> (out bf16 [B, Nq, Hq, d], lse [B, Hq, Nq])."""
+    _u8_cuda(q, k, vt)
+    _f32_cuda(q_scales, k_scales, v_scales)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    L = lib().fa_fp8_vt_len(Nk)
+    if (tuple(vt.shape) != (B, Hkv, d, L) or not vt.is_contiguous()
+            or tuple(q_scales.shape) != (B, Hq, -(-Nq // FA_FP8_Q_BLOCK))
+            or tuple(k_scales.shape) != (B, Hkv, -(-Nk // FA_FP8_K_BLOCK))
+            or tuple(v_scales.shape) != (B, Hkv)):
+        raise ValueError("FP8 operand or scale shapes do not match q and k")
+    if out is None:
+        out = torch.empty((B, Nq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    _bf16_cuda(out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    o = _opts(softmax_scale, causal, window, 0.0, -1)
+    _check(lib().fa_fwd_fp8(ctypes.byref(o), _ptr(q), _ptr(q_scales), _ptr(k), _ptr(k_scales), _ptr(vt),
+                            _ptr(v_scales), _ptr(out), _ptr(lse), B, Nq, Nk, Hq, Hkv, d,
+                            _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)), _strides(out, (0, 1, 2)),
+                            _stream(stream)))
+    return out, lse

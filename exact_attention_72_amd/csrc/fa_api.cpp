@@ -76,6 +76,19 @@ int check_strides(const char* name, const void* base, const int64_t* s, int n) {
   return FA_OK;
 }
 
+// Byte strides (FP8 codes): every row start 16-byte aligned.
+int check_byte_strides(const char* name, const void* base, const int64_t* s, int n) {
+  if (!s) return fail(FA_ERR_INVALID_ARG, "%s strides are NULL", name);
+  if (!aligned16(base)) return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  for (int i = 0; i < n; ++i) {
+    if (s[i] < 0) return fail(FA_ERR_INVALID_ARG, "%s stride %d is negative", name, i);
+    if (s[i] % 16 != 0)
+      return fail(FA_ERR_INVALID_ARG, "%s stride %d (%lld bytes) breaks 16-byte row alignment", name, i,
+                  (long long)s[i]);
+  }
+  return FA_OK;
+}
+
 // Rotary tables: both or neither; rotated dims a multiple of 16, at most head_dim.
 int check_rotary(const float* cos, const float* sin, int dim, int interleaved, int head_dim, FaRotary* r) {
   r->cos = nullptr;
@@ -548,6 +561,112 @@ int fa_combine(const float* o_part, const float* lse_part, int num_splits, int64
   c.lse = lse_out;
   hipError_t e = fa_launch_combine(c, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return FA_OK;
+}
+
+
+int fa_fp8_vt_len(int seqlen) {
+  return seqlen <= 0 ? 0 : (int)(((int64_t)seqlen + FA_FP8_K_BLOCK - 1) / FA_FP8_K_BLOCK * FA_FP8_K_BLOCK);
+}
+
+int fa_fp8_quantize(const void* x, int batch, int seqlen, int heads, int head_dim, const int64_t x_strides[3],
+                    int block_rows, void* codes, const int64_t codes_strides[3], float* scales, void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!x || !codes || !scales) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || seqlen < 0 || heads <= 0) return fail(FA_ERR_INVALID_ARG, "batch and heads must be positive");
+  if (block_rows <= 0) return fail(FA_ERR_INVALID_ARG, "block_rows must be positive");
+  if ((rc = check_strides("x", x, x_strides, 3)) || (rc = check_byte_strides("codes", codes, codes_strides, 3)))
+    return rc;
+  if (seqlen == 0) return FA_OK;
+  FaFp8QuantParams p;
+  memset(&p, 0, sizeof p);
+  p.x = static_cast<const uint16_t*>(x);
+  p.x_bs = x_strides[0]; p.x_ss = x_strides[1]; p.x_hs = x_strides[2];
+  p.codes = static_cast<uint8_t*>(codes);
+  p.c_bs = codes_strides[0]; p.c_ss = codes_strides[1]; p.c_hs = codes_strides[2];
+  p.scales = scales;
+  p.B = batch; p.N = seqlen; p.H = heads; p.rows = block_rows;
+  p.nblk = (int)(((int64_t)seqlen + block_rows - 1) / block_rows);
+  if ((int64_t)batch * heads * p.nblk > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "too many blocks");
+  hipError_t e = fa_launch_fp8_quant(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
+  return FA_OK;
+}
+
+int fa_fp8_quantize_v(const void* v, int batch, int seqlen, int heads_kv, int head_dim, const int64_t v_strides[3],
+                      void* vt, float* scales, void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!v || !vt || !scales) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || seqlen < 0 || heads_kv <= 0)
+    return fail(FA_ERR_INVALID_ARG, "batch and heads must be positive");
+  if ((rc = check_strides("v", v, v_strides, 3))) return rc;
+  if (!aligned16(vt)) return fail(FA_ERR_INVALID_ARG, "vt is not 16-byte aligned");
+  if (seqlen == 0) return FA_OK;
+  FaFp8QuantParams p;
+  memset(&p, 0, sizeof p);
+  p.x = static_cast<const uint16_t*>(v);
+  p.x_bs = v_strides[0]; p.x_ss = v_strides[1]; p.x_hs = v_strides[2];
+  p.vt = static_cast<uint8_t*>(vt);
+  p.scales = scales;
+  p.B = batch; p.N = seqlen; p.H = heads_kv;
+  p.npad = fa_fp8_vt_len(seqlen);
+  hipError_t e = fa_launch_fp8_quant(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantize_v launch");
+  return FA_OK;
+}
+
+int fa_fwd_fp8(const fa_attn_opts* opts, const void* q, const float* q_scales, const void* k, const float* k_scales,
+               const void* vt, const float* v_scales, void* out, float* lse, int batch, int seqlen_q, int seqlen_k,
+               int heads_q, int heads_kv, int head_dim, const int64_t q_strides[3], const int64_t k_strides[3],
+               const int64_t o_strides[3], void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
+  if (head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "the FP8 forward is built for head_dim 128");
+  if (!q || !k || !vt || !out || !q_scales || !k_scales || !v_scales)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_k <= 0)
+    return fail(FA_ERR_INVALID_ARG, "batch, seqlen_q and seqlen_k must be positive");
+  if ((rc = check_byte_strides("q", q, q_strides, 3)) || (rc = check_byte_strides("k", k, k_strides, 3)) ||
+      (rc = check_strides("out", out, o_strides, 3)))
+    return rc;
+  if (!aligned16(vt)) return fail(FA_ERR_INVALID_ARG, "vt is not 16-byte aligned");
+  FaParams tmp;
+  memset(&tmp, 0, sizeof tmp);
+  bool softcap = false;
+  if ((rc = fill_opts(opts, head_dim, &tmp, &softcap))) return rc;
+  if (softcap) return fail(FA_ERR_UNSUPPORTED, "softcap is not supported by the FP8 forward");
+  FaFp8Params p;
+  memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.vt = static_cast<const uint8_t*>(vt);
+  p.q_scale = q_scales; p.k_scale = k_scales; p.v_scale = v_scales;
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.q_bs = q_strides[0]; p.q_ss = q_strides[1]; p.q_hs = q_strides[2];
+  p.k_bs = k_strides[0]; p.k_ss = k_strides[1]; p.k_hs = k_strides[2];
+  p.o_bs = o_strides[0]; p.o_ss = o_strides[1]; p.o_hs = o_strides[2];
+  p.lse_bs = (int64_t)heads_q * seqlen_q;
+  p.lse_hs = seqlen_q;
+  p.B = batch; p.Nq = seqlen_q; p.Nk = seqlen_k; p.Hq = heads_q; p.Hkv = heads_kv;
+  p.g = heads_q / heads_kv;
+  p.npad = fa_fp8_vt_len(seqlen_k);
+  p.q_nblk = (seqlen_q + FA_FP8_Q_BLOCK - 1) / FA_FP8_Q_BLOCK;
+  p.k_nblk = (seqlen_k + FA_FP8_K_BLOCK - 1) / FA_FP8_K_BLOCK;
+  p.m_blocks = p.q_nblk;
+  p.total_tiles = (int64_t)p.m_blocks * batch * heads_q;
+  if (p.total_tiles > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "too many tiles");
+  p.scale_log2 = tmp.scale_log2;
+  p.causal = tmp.causal; p.wl = tmp.wl; p.wr = tmp.wr;
+  hipError_t e = fa_launch_fp8_fwd(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 forward launch");
   return FA_OK;
 }
 

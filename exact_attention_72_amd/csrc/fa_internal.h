@@ -42,6 +42,46 @@ struct FaParams {
   int causal, wl, wr;
 };
 
+// FP8 (OCP e4m3) forward.  Q in blocks of FA_FP8_Q_BLOCK rows and K in blocks
+// of FA_FP8_K_BLOCK keys, one fp32 scale per (batch, head, block); V one scale
+// per (batch, KV head), stored transposed (V^T rows of FA_FP8_K_BLOCK-key groups
+// in the order the P V product reads them).
+#ifndef FA_FP8_Q_BLOCK
+#define FA_FP8_Q_BLOCK 128
+#define FA_FP8_K_BLOCK 64
+#endif
+struct FaFp8Params {
+  const uint8_t* q;   // e4m3 codes; strides in bytes (batch, token, head), head_dim contiguous
+  const uint8_t* k;
+  const uint8_t* vt;  // [B, Hkv, head_dim, npad]
+  const float* q_scale;  // [B, Hq, q_nblk]
+  const float* k_scale;  // [B, Hkv, k_nblk]
+  const float* v_scale;  // [B, Hkv]
+  uint16_t* o;           // bf16; strides in elements
+  float* lse;
+  int64_t q_bs, q_ss, q_hs;
+  int64_t k_bs, k_ss, k_hs;
+  int64_t o_bs, o_ss, o_hs;
+  int64_t lse_bs, lse_hs;
+  int B, Nq, Nk, Hq, Hkv, g, npad;
+  int q_nblk, k_nblk, m_blocks;
+  int64_t total_tiles;
+  float scale_log2;  // softmax_scale * log2(e)
+  int causal, wl, wr;
+};
+// Quantizer of a [B, N, H, head_dim] bf16 tensor: rows in blocks of `rows`
+// (per-block scales) or, for vt != NULL, one scale per head and the codes
+// written transposed into vt [B, H, head_dim, npad].
+struct FaFp8QuantParams {
+  const uint16_t* x;
+  int64_t x_bs, x_ss, x_hs;  // elements
+  uint8_t* codes;            // rows form: [B, N, H, head_dim] codes
+  int64_t c_bs, c_ss, c_hs;  // bytes
+  uint8_t* vt;               // transposed form
+  float* scales;
+  int B, N, H, rows, nblk, npad;
+};
+
 // Rotary position embedding from caller tables: position pos, frequency i
 // rotates the pair of dims (i, i + dim / 2) (or (2i, 2i + 1) when interleaved)
 // by cos[pos * dim / 2 + i], sin[pos * dim / 2 + i].
@@ -120,6 +160,8 @@ hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t s
 hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_append(const FaAppendParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_rotary(const FaRotaryParams& p, int d, hipStream_t stream);
+hipError_t fa_launch_fp8_quant(const FaFp8QuantParams& p, int d, hipStream_t s);
+hipError_t fa_launch_fp8_fwd(const FaFp8Params& p, int d, hipStream_t s);
 hipError_t fa_launch_bwd(const FaBwdParams& p, int d, hipStream_t stream);
 
 // Tile geometry of the prefill kernel.

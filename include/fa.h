@@ -244,6 +244,59 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
 /* Bytes of workspace fa_bwd needs: batch * heads_q * seqlen_q * 4 rounded up to 256. */
 size_t fa_bwd_workspace_size(int batch, int seqlen_q, int heads_q);
 
+/* FP8 (OCP e4m3) forward ("Attention kernels ...", section 4.2, the FP8 item;
+ * "01 FlashAttention project overview & architecture", section 2.2): Q, K and V
+ * enter the matrix products as e4m3 codes (1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinity, largest magnitude 448) with fp32 scales: Q per
+ * (batch, head, block of FA_FP8_Q_BLOCK rows), K per (batch, KV head, block of
+ * FA_FP8_K_BLOCK keys), V per (batch, KV head).  A value is code * scale. */
+#define FA_FP8_Q_BLOCK 128
+#define FA_FP8_K_BLOCK 64
+
+/* Per-block quantizer.  x bf16 [batch, seqlen, heads, head_dim] (x_strides in
+ * elements) -> codes e4m3 [batch, seqlen, heads, head_dim] (codes_strides in
+ * bytes; written) and scales float32 [batch, heads, ceil(seqlen / block_rows)]
+ * (dense; written).  Per block of block_rows rows of one (batch, head): scale =
+ * amax / 448 in fp32 (1 for an all-zero block); code = the e4m3 rounding (to
+ * nearest even) of the fp32 quotient x / scale.  Use block_rows =
+ * FA_FP8_Q_BLOCK for Q and FA_FP8_K_BLOCK for K.  head_dim 64 or 128; rows
+ * 16-byte aligned. */
+int fa_fp8_quantize(const void* x, int batch, int seqlen, int heads, int head_dim,
+                    const int64_t x_strides[3], int block_rows, void* codes,
+                    const int64_t codes_strides[3], float* scales, void* stream);
+
+/* Length of a transposed V row: seqlen rounded up to a multiple of FA_FP8_K_BLOCK. */
+int fa_fp8_vt_len(int seqlen);
+
+/* V quantizer: one scale per (batch, KV head) (scales float32 [batch, heads_kv],
+ * written), codes written transposed into vt (dense, written):
+ * vt [batch, heads_kv, head_dim, fa_fp8_vt_len(seqlen)] bytes.  Row d of a head
+ * holds V[., d] in groups of 64 keys; position p of group n holds key
+ * 64 n + 32 ((p >> 4) & 1) + 8 ((p >> 2) & 3) + 4 (p >> 5) + (p & 3) (the key
+ * order in which the P V product reads both of its operands); keys past seqlen
+ * hold 0.  Same rounding as fa_fp8_quantize. */
+int fa_fp8_quantize_v(const void* v, int batch, int seqlen, int heads_kv, int head_dim,
+                      const int64_t v_strides[3], void* vt, float* scales, void* stream);
+
+/* FP8 attention forward.
+ *   q   e4m3 [batch, seqlen_q, heads_q, head_dim], q_strides in bytes;
+ *       q_scales float32 [batch, heads_q, ceil(seqlen_q / FA_FP8_Q_BLOCK)]
+ *   k   e4m3 [batch, seqlen_k, heads_kv, head_dim], k_strides in bytes;
+ *       k_scales float32 [batch, heads_kv, ceil(seqlen_k / FA_FP8_K_BLOCK)]
+ *   vt, v_scales as fa_fp8_quantize_v writes them for seqlen_k keys
+ *   out bf16 [batch, seqlen_q, heads_q, head_dim], o_strides in elements (written)
+ *   lse float32 [batch, heads_q, seqlen_q] (natural log; written; may be NULL)
+ * opts as for fa_fwd: scale, causal (bottom-right), window; softcap > 0 is
+ * FA_ERR_UNSUPPORTED; pack_gqa is ignored.  head_dim 128 (else
+ * FA_ERR_UNSUPPORTED).  The scores are exact products of the codes summed in
+ * fp32; the probabilities enter the P V product as e4m3 (2^8 p relative to the
+ * row maximum, rounded to nearest even) and O is divided by the fp32 row sum. */
+int fa_fwd_fp8(const fa_attn_opts* opts, const void* q, const float* q_scales, const void* k,
+               const float* k_scales, const void* vt, const float* v_scales, void* out,
+               float* lse, int batch, int seqlen_q, int seqlen_k, int heads_q, int heads_kv,
+               int head_dim, const int64_t q_strides[3], const int64_t k_strides[3],
+               const int64_t o_strides[3], void* stream);
+
 /* Merge of partial attention states ("Attention kernels ...", section 6.3: the
  * partial (O_s, LSE_s) of disjoint key ranges combine with the same rescale as
  * the tiles of one pass):

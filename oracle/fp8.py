@@ -136,7 +136,7 @@ def _visible(Lq, Lk, causal, window):
 
 
 def fwd(q, q_scales, q_block, k, k_scales, k_block, v, v_scales, *, scale=None, causal=False,
-        window=None, rows=None):
+        window=None, rows=None, with_abs=False):
     """Attention over the dequantized FP8 inputs, in fp64 with S and P materialised.
 
     q: codes [B, Nq, Hq, d] with q_scales [B, Hq, ceil(Nq / q_block)]; k: codes
@@ -145,6 +145,8 @@ def fwd(q, q_scales, q_block, k, k_scales, k_block, v, v_scales, *, scale=None, 
     rows: None for all query rows, or a list of row indices (then O and LSE hold
     those rows only, in that order).  Returns (O float64 [B, rows, Hq, d],
     LSE float64 [B, Hq, rows]); a row that sees no key gets O = 0, LSE = -inf.
+    with_abs: also return A = P |V| (the weights applied to the magnitudes of V),
+    the scale of the error a relative rounding of each weight can cause.
     """
     qd = dequantize(q, q_scales, q_block)
     kd = dequantize(k, k_scales, k_block)
@@ -156,6 +158,7 @@ def fwd(q, q_scales, q_block, k, k_scales, k_block, v, v_scales, *, scale=None, 
     sel = np.arange(Nq) if rows is None else np.asarray(rows)
     vis = _visible(Nq, Nk, causal, window)[sel]
     O = np.zeros((B, len(sel), Hq, d))
+    A = np.zeros((B, len(sel), Hq, d))
     L = np.full((B, Hq, len(sel)), -np.inf)
     for b in range(B):
         for h in range(Hq):
@@ -166,8 +169,10 @@ def fwd(q, q_scales, q_block, k, k_scales, k_block, v, v_scales, *, scale=None, 
             E = np.exp(S - np.where(np.isfinite(m), m, 0.0))
             l = E.sum(axis=1)
             O[b, ok, h] = (E[ok] / l[ok, None]) @ vd[b, :, h // g]
+            if with_abs:
+                A[b, ok, h] = (E[ok] / l[ok, None]) @ np.abs(vd[b, :, h // g])
             L[b, h, ok] = m[ok, 0] + np.log(l[ok])
-    return O, L
+    return (O, L, A) if with_abs else (O, L)
 
 
 def probs(q, q_scales, q_block, k, k_scales, k_block, *, row, b, h, g, scale=None, causal=False,
