@@ -9,7 +9,8 @@ the long-context local attention with softcap (N = 32768, 32 heads,
 window 4096, softcap 30), and the chunked prefill over a paged cache (4 x 4096
 new tokens against 16384 cached keys, 32/8 heads) with the in-place K/V append
 of that chunk, a unified batch of 64 decode requests and 4 prefill chunks
-in one launch, and the backward pass of the prefill workload.
+in one launch, the backward pass of the prefill workload, and the FP8 (e4m3)
+forward of the prefill workload.
 
 Prints one JSON line:
   value        prefill TFLOP/s, FLOPs counted as 4 * B * H * N^2 * d * 1/2 (the
@@ -36,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_72_amd", "csrc", "fa_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -285,6 +287,40 @@ def bench_bwd(api, W, steps, warmup):
                        "flop_convention": "2.5 * 4*B*H*N^2*d/2"}}
 
 
+def bench_fp8(api, W, steps, warmup):
+    """FP8 (e4m3) forward of the dense causal prefill workload (batch 4, 16 heads, N = 4096,
+    d = 128): fa_fwd_fp8 per launch on inputs quantized beforehand, TFLOP/s on the same
+    4 B H N^2 d / 2 convention against the dense FP8 matrix peak; the quantizers (Q and K
+    per block, V per head into the transposed layout) timed separately."""
+    import torch
+    c = W.WORKLOADS["prefill_b4_h16_n4096_d128_causal"]
+    B, N, H, d = c["B"], c["N"], c["Hq"], c["d"]
+    t = W.dense(c["seed"], B, N, H, c["Hkv"], d, device="cuda")
+    q8, qs = api.fa_fp8_quantize(t["q"], api.FA_FP8_Q_BLOCK)
+    k8, ks = api.fa_fp8_quantize(t["k"], api.FA_FP8_K_BLOCK)
+    vt, vs = api.fa_fp8_quantize_v(t["v"])
+    out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fn = lambda: api.fa_fwd_fp8(q8, qs, k8, ks, vt, vs, causal=True, out=out, lse=lse)  # noqa: E731
+    _, ms = time_launches(fn, steps, warmup)
+    flops = prefill_flops(B, H, N, d, True)
+    tf = flops / (ms * 1e-3) / 1e12
+
+    def quant():
+        api.fa_fp8_quantize(t["q"], api.FA_FP8_Q_BLOCK, codes=q8, scales=qs)
+        api.fa_fp8_quantize(t["k"], api.FA_FP8_K_BLOCK, codes=k8, scales=ks)
+        api.fa_fp8_quantize_v(t["v"], vt=vt, scales=vs)
+    _, qms = time_launches(quant, max(3, steps // 10), 2)
+    return {"metric": "attn fwd fp8 TFLOP/s (e4m3 N=4k d=128 causal)", "unit": "TFLOP/s", "value": round(tf, 2),
+            "ms": round(ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
+            "quantize_ms": round(qms, 4),
+            "config": {"workload": "prefill_b4_h16_n4096_d128_causal fp8", "batch": B, "heads": H, "seq_len": N,
+                       "head_dim": d, "causal": True, "flop_convention": "4*B*H*N^2*d/2",
+                       "scales": "Q per 128 rows, K per 64 keys, V per head"}}
+
+
 def bench_decode(api, W, steps, warmup):
     import torch
     c = W.WORKLOADS["paged_decode_b64_h32kv8_d128_page256"]
@@ -331,6 +367,7 @@ def main():
     ap.add_argument("--no-paged-prefill", action="store_true")
     ap.add_argument("--no-unified", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -395,6 +432,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_bwd:
         line["bwd"] = bench_bwd(api, W, max(10, args.steps // 5), max(5, args.warmup // 5))
+        torch.cuda.empty_cache()
+    if not args.no_fp8:
+        line["fp8"] = bench_fp8(api, W, max(20, args.steps // 2), max(20, args.warmup // 2))
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         tc = W.dense(c["seed"], B, N, H, c["Hkv"], d)
