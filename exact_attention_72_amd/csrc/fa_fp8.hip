@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void fa_fp8_quant_vt_kernel(FaFp8QuantPar
 
 // ------------------------------------------------------------------ attention
 // One workgroup per (batch, query head, 128-row block), longest row blocks
-// first; four waves of 32 query rows; 64-key blocks through a ring of three LDS
+// first; four waves of 32 query rows; 64-key blocks through a ring of four LDS
 // stages filled by LDS-DMA.  A stage holds the block's K rows (64 x D bytes,
 // 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7)) and its V^T rows
 // (D x 64 bytes, chunk c of row r at c ^ ((r >> 2) & 3)); both swizzles give
@@ -244,7 +244,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) {
   static_assert(D == 128, "the FP8 kernel is built for head_dim 128");
   constexpr int BN = FA_FP8_K_BLOCK;  // 64
-  constexpr int NBUF = 3;
+  constexpr int NBUF = 4;
   constexpr int KT = BN * D;  // K bytes of a block
   constexpr int VT = D * BN;  // V^T bytes of a block
   constexpr int STAGE = KT + VT;
@@ -331,26 +331,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
   const uint32_t base = lds_addr(smem);
   const uint32_t ka = base + col * D, ksw = (col >> 1) & 7;
   const uint32_t va = base + KT + col * BN, vsw = (col >> 2) & 3;
-
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  float m_run = kNegInf, l_run = 0.0f;  // m in log2 units (scores times their scales)
-
-  if (nb > 0) issue(0);
-  if (nb > 1) issue(1);
-  for (int i = 0; i < nb; ++i) {
-    if (i + 1 < nb)
-      wait_vmcnt<kDmaPerBlock>();
-    else
-      wait_vmcnt<0>();
-    stage_barrier();
-    if (i + 2 < nb) issue(i + 2);
-    const int n = n_lo + i;
-    const float cb = cq * scalar_load_f32(kscale + n);
+  auto read_k = [&](int i, u32x4 (&kr)[8]) __attribute__((always_inline)) {
     const uint32_t so = (uint32_t)((i % NBUF) * STAGE);
-    // S^T = K Q^T for the two 32-key halves
-    u32x4 kr[8];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -358,14 +340,44 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
 #pragma unroll
         for (int e = 0; e < 2; ++e)
           kr[4 * hb + 2 * c + e] = ds_read_b128(ka + so + hb * 32 * D + 16 * ((4 * c + 2 * kg + e) ^ ksw));
-    lgkm_wait0(kr);
-    f32x16 s[2];
+  };
+  // V^T reads of d-blocks [DB0, DB0 + NDB) of block i
+  auto read_v = [&](int i, u32x4 (&vr)[8], int db0, int ndb) __attribute__((always_inline)) {
+    const uint32_t so = (uint32_t)((i % NBUF) * STAGE);
+#pragma unroll
+    for (int db = db0; db < db0 + ndb; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) vr[2 * db + e] = ds_read_b128(va + so + db * 32 * BN + 16 * ((2 * kg + e) ^ vsw));
+  };
+  auto s_mfma = [&](const u32x4 (&kr)[8], f32x16 (&sv)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      s[hb] = f32x16{};
+      sv[hb] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) s[hb] = mfma_fp8(join(kr[4 * hb + 2 * c], kr[4 * hb + 2 * c + 1]), qreg[c], s[hb]);
+      for (int c = 0; c < D / 64; ++c)
+        sv[hb] = mfma_fp8(join(kr[4 * hb + 2 * c], kr[4 * hb + 2 * c + 1]), qreg[c], sv[hb]);
     }
+  };
+  // wave-uniform scalar load of block n's K scale, waited for by the next lgkm wait
+  auto load_kscale = [&](int n) __attribute__((always_inline)) {
+    const uint64_t a = reinterpret_cast<uint64_t>(kscale + n);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const float* u = reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo);
+    float v;
+    asm volatile("s_load_dword %0, %1, 0x0" : "=s"(v) : "s"(u) : "memory");
+    return v;
+  };
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.0f;  // m in log2 units (scores times their scales)
+  f32x16 x0 = {}, x1 = {};               // 2^8 p of the current block (relative to m_run)
+
+  // Scores of block i (in sv) -> masked, reference moved (O rescaled), exponentials.
+  auto softmax = [&](f32x16 (&sv)[2], int i, float cb) __attribute__((always_inline)) {
+    const int n = n_lo + i;
     if (n < n_full_lo || n >= n_full_hi) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
@@ -374,15 +386,20 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
           const int key = n * BN + 32 * hb + 8 * (a >> 2) + 4 * kg + (a & 3);
           const bool vis = (key < Lk) & (!p.causal | (key <= pos)) & ((p.wl < 0) | (key >= pos - p.wl)) &
                            ((p.wr < 0) | (key <= pos + p.wr));
-          s[hb][a] = vis ? s[hb][a] : kNegInf;
+          sv[hb][a] = vis ? sv[hb][a] : kNegInf;
         }
     }
-    // online softmax in log2 units x = s * cb (cb > 0)
     float mx = kNegInf;
 #pragma unroll
-    for (int a = 0; a < 16; ++a) mx = fmaxf(mx, fmaxf(s[0][a], s[1][a]));
+    for (int a = 0; a < 16; ++a) mx = fmaxf(mx, fmaxf(sv[0][a], sv[1][a]));
     mx = pair_max(mx) * cb;
     const float m_new = fmaxf(m_run, mx);
+    const float nmc = (m_new == kNegInf) ? 0.0f : kPShift - m_new;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      x0[a] = exp2_fast(__builtin_fmaf(sv[0][a], cb, nmc));
+      x1[a] = exp2_fast(__builtin_fmaf(sv[1][a], cb, nmc));
+    }
     if (__any(m_new > m_run)) {
       const float alpha = (m_new > m_run) ? exp2_fast(m_run - m_new) : 1.0f;
       l_run *= alpha;
@@ -390,33 +407,77 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
       m_run = m_new;
     }
-    const float nmc = (m_run == kNegInf) ? 0.0f : kPShift - m_run;
-    f32x16 x0, x1;
-#pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      x0[a] = exp2_fast(__builtin_fmaf(s[0][a], cb, nmc));
-      x1[a] = exp2_fast(__builtin_fmaf(s[1][a], cb, nmc));
+  };
+
+  // Ring of NBUF stages, the DMA of block i + NBUF - 1 issued at step i.  Step i
+  // reads block i + 1's K and forms its scores while block i's P V products run.
+  // Wait for a block whose DMA was followed by `after` later blocks' DMAs.
+  auto wait_block = [&](int after) __attribute__((always_inline)) {
+    switch (after) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<kDmaPerBlock>(); break;
+      default: wait_vmcnt<2 * kDmaPerBlock>(); break;
     }
+  };
+  if (nb > 0) {
+    for (int j = 0; j < NBUF - 1 && j < nb; ++j) issue(j);
+    wait_block(min(nb - 1, NBUF - 2));  // block 0; blocks 1 .. NBUF - 2 may be in flight
+    stage_barrier();
+    float ks = load_kscale(n_lo);
+    u32x4 kr[8];
+    read_k(0, kr);
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(kr[0]), "+v"(kr[1]), "+v"(kr[2]), "+v"(kr[3]), "+v"(kr[4]), "+v"(kr[5]), "+v"(kr[6]),
+                   "+v"(kr[7]), "+s"(ks));
+    f32x16 sv[2];
+    s_mfma(kr, sv);
+    softmax(sv, 0, cq * ks);
+  }
+  for (int i = 0; i < nb; ++i) {
+    const bool more = i + 1 < nb;
+    if (more) {
+      // block i + 1; issued so far: blocks up to i + NBUF - 2
+      wait_block(min(nb - 1, i + NBUF - 2) - (i + 1));
+      stage_barrier();  // everyone is done with block i - 1's stage
+      if (i + NBUF - 1 < nb) issue(i + NBUF - 1);
+    }
+    u32x4 kr[8], vr[8];
+    float ks = 1.0f;
+    if (more) {
+      ks = load_kscale(n_lo + i + 1);
+      read_k(i + 1, kr);
+    }
+    read_v(i, vr, 0, D / 64);
+    // block i's probabilities as the B operand (bytes 16 hb + slot of this lane's 32)
     float rs = 0.0f;
 #pragma unroll
     for (int a = 0; a < 16; ++a) rs += x0[a] + x1[a];
     l_run += rs;
-    // P^T as the B operand: bytes 16 hb + slot of this lane's 32
     i32x8 pb;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       pb[w] = (int)pack4(x0[4 * w], x0[4 * w + 1], x0[4 * w + 2], x0[4 * w + 3]);
       pb[4 + w] = (int)pack4(x1[4 * w], x1[4 * w + 1], x1[4 * w + 2], x1[4 * w + 3]);
     }
-    // O^T += V^T P^T
-    u32x4 vr[8];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) vr[2 * db + e] = ds_read_b128(va + so + db * 32 * BN + 16 * ((2 * kg + e) ^ vsw));
-    lgkm_wait0(vr);
+    // LDS reads complete in issue order: with the first half of the V reads (D / 32
+    // of them) still in flight the K reads are done at lgkmcnt(D / 32) (the scalar
+    // load of the scale, if still in flight, only makes the wait longer; the final
+    // wait covers it).  At most 13 reads are outstanding.
+    f32x16 sv[2];
+    if (more) {
+      asm volatile("s_waitcnt lgkmcnt(%8)"
+                   : "+v"(kr[0]), "+v"(kr[1]), "+v"(kr[2]), "+v"(kr[3]), "+v"(kr[4]), "+v"(kr[5]), "+v"(kr[6]),
+                     "+v"(kr[7])
+                   : "i"(D / 32));
+      s_mfma(kr, sv);
+    }
+    read_v(i, vr, D / 64, D / 64);
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]), "+v"(vr[6]),
+                   "+v"(vr[7]), "+s"(ks));
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = mfma_fp8(join(vr[2 * db], vr[2 * db + 1]), pb, o[db]);
+    if (more) softmax(sv, i + 1, cq * ks);
   }
 
   // ---- epilogue: O = v_scale O^T / l, LSE = (m - 8 + log2 l) ln 2
