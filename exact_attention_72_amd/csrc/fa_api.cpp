@@ -616,6 +616,8 @@ int fa_fp8_quantize_v(const void* v, int batch, int seqlen, int heads_kv, int he
   p.scales = scales;
   p.B = batch; p.N = seqlen; p.H = heads_kv;
   p.npad = fa_fp8_vt_len(seqlen);
+  if ((int64_t)batch * heads_kv * (p.npad / FA_FP8_K_BLOCK) > 0x7fffffff)
+    return fail(FA_ERR_UNSUPPORTED, "too many key groups");
   hipError_t e = fa_launch_fp8_quant(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fp8 quantize_v launch");
   return FA_OK;

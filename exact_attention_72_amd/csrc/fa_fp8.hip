@@ -178,20 +178,39 @@ __global__ __launch_bounds__(kThreads) void fa_fp8_quant_rows_kernel(FaFp8QuantP
   }
 }
 
-// Transposed form for V: one workgroup per (batch, KV head); one scale over the
-// head; codes written to vt [B, H, D, npad] row d, group n at bytes 64 n .. + 63,
-// position p holding key 64 n + vt_key_of_position(p) (0 past the last key).
+// Transposed form for V: one scale over each (batch, KV head), codes written to
+// vt [B, H, D, npad] row d, group n at bytes 64 n .. + 63, position p holding key
+// 64 n + vt_key_of_position(p) (0 past the last key).  Four launches: the head
+// maxima are cleared, gathered per 64-key group with an integer atomic maximum
+// (non-negative floats order like their bit patterns, so the result does not
+// depend on the order), used by every group to write its codes, and finally
+// turned into the scales.  The maxima live in the scales array meanwhile.
+__global__ __launch_bounds__(kThreads) void fa_fp8_vt_clear_kernel(FaFp8QuantParams p) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < p.B * p.H) p.scales[i] = 0.0f;
+}
+__global__ __launch_bounds__(kThreads) void fa_fp8_vt_scale_kernel(FaFp8QuantParams p) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < p.B * p.H) {
+    const float amax = p.scales[i];
+    p.scales[i] = amax > 0.0f ? amax / kFp8Max : 1.0f;
+  }
+}
+// one workgroup per (batch, KV head, 64-key group)
 template <int D>
-__global__ __launch_bounds__(kThreads) void fa_fp8_quant_vt_kernel(FaFp8QuantParams p) {
+__global__ __launch_bounds__(kThreads) void fa_fp8_vt_amax_kernel(FaFp8QuantParams p) {
   __shared__ float red[4];
-  __shared__ uint16_t tile[64][D + 8];
   constexpr int CPR = D / 8;
-  const int bh = blockIdx.x;
+  const int ng = p.npad / 64;
+  const int n = (int)(blockIdx.x % ng);
+  const int bh = (int)(blockIdx.x / ng);
   const int b = bh / p.H, h = bh % p.H;
   const uint16_t* xb = p.x + (int64_t)b * p.x_bs + (int64_t)h * p.x_hs;
   float m = 0.0f;
-  for (int64_t c = threadIdx.x; c < (int64_t)p.N * CPR; c += kThreads) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xb + (c / CPR) * p.x_ss + 8 * (c % CPR));
+  for (int c = threadIdx.x; c < 64 * CPR; c += kThreads) {
+    const int key = 64 * n + c / CPR;
+    if (key >= p.N) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xb + (int64_t)key * p.x_ss + 8 * (c % CPR));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       m = fmaxf(m, fabsf(bf16_to_f32(v[e] & 0xFFFFu)));
@@ -199,37 +218,45 @@ __global__ __launch_bounds__(kThreads) void fa_fp8_quant_vt_kernel(FaFp8QuantPar
     }
   }
   const float amax = block_amax(m, red);
+  if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(p.scales + bh), __float_as_uint(amax));
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa_fp8_vt_write_kernel(FaFp8QuantParams p) {
+  __shared__ uint16_t tile[64][D + 8];
+  constexpr int CPR = D / 8;
+  const int ng = p.npad / 64;
+  const int n = (int)(blockIdx.x % ng);
+  const int bh = (int)(blockIdx.x / ng);
+  const int b = bh / p.H, h = bh % p.H;
+  const float amax = p.scales[bh];
   const float scale = amax > 0.0f ? amax / kFp8Max : 1.0f;
-  if (threadIdx.x == 0) p.scales[bh] = scale;
+  const uint16_t* xb = p.x + (int64_t)b * p.x_bs + (int64_t)h * p.x_hs;
+  for (int c = threadIdx.x; c < 64 * CPR; c += kThreads) {
+    const int key = 64 * n + c / CPR;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (key < p.N) v = *reinterpret_cast<const u32x4*>(xb + (int64_t)key * p.x_ss + 8 * (c % CPR));
+    uint16_t* t = &tile[c / CPR][8 * (c % CPR)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[2 * e] = (uint16_t)(v[e] & 0xFFFFu);
+      t[2 * e + 1] = (uint16_t)(v[e] >> 16);
+    }
+  }
+  __syncthreads();
   uint8_t* vb = p.vt + (int64_t)bh * D * p.npad;
-  for (int n = 0; n < p.npad / 64; ++n) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < 64 * CPR; c += kThreads) {
-      const int key = 64 * n + c / CPR;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < p.N) v = *reinterpret_cast<const u32x4*>(xb + (int64_t)key * p.x_ss + 8 * (c % CPR));
-      uint16_t* t = &tile[c / CPR][8 * (c % CPR)];
+  for (int task = threadIdx.x; task < 2 * D; task += kThreads) {  // (row d, half of the group)
+    const int d = task >> 1, half = task & 1;
+    uint32_t w[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t[2 * e] = (uint16_t)(v[e] & 0xFFFFu);
-        t[2 * e + 1] = (uint16_t)(v[e] >> 16);
-      }
+    for (int q = 0; q < 8; ++q) {
+      const int p0 = 32 * half + 4 * q;
+      w[q] = quant4(bf16_to_f32(tile[vt_key_of_position(p0)][d]), bf16_to_f32(tile[vt_key_of_position(p0 + 1)][d]),
+                    bf16_to_f32(tile[vt_key_of_position(p0 + 2)][d]), bf16_to_f32(tile[vt_key_of_position(p0 + 3)][d]),
+                    scale);
     }
-    __syncthreads();
-    for (int task = threadIdx.x; task < 2 * D; task += kThreads) {  // (row d, half of the group)
-      const int d = task >> 1, half = task & 1;
-      uint32_t w[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int p0 = 32 * half + 4 * q;
-        w[q] = quant4(bf16_to_f32(tile[vt_key_of_position(p0)][d]), bf16_to_f32(tile[vt_key_of_position(p0 + 1)][d]),
-                      bf16_to_f32(tile[vt_key_of_position(p0 + 2)][d]),
-                      bf16_to_f32(tile[vt_key_of_position(p0 + 3)][d]), scale);
-      }
-      uint8_t* dst = vb + (int64_t)d * p.npad + 64 * n + 32 * half;
-      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<u32x4*>(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
-    }
+    uint8_t* dst = vb + (int64_t)d * p.npad + 64 * n + 32 * half;
+    *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
   }
 }
 
@@ -509,11 +536,17 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
 hipError_t fa_launch_fp8_quant(const FaFp8QuantParams& p, int d, hipStream_t s) {
   if (d != 128 && d != 64) return hipErrorInvalidValue;
   if (p.vt) {
-    const unsigned grid = (unsigned)((int64_t)p.B * p.H);
-    if (d == 128)
-      hipLaunchKernelGGL(fa_fp8_quant_vt_kernel<128>, dim3(grid), dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL(fa_fp8_quant_vt_kernel<64>, dim3(grid), dim3(kThreads), 0, s, p);
+    const unsigned heads = (unsigned)((p.B * p.H + kThreads - 1) / kThreads);
+    const unsigned groups = (unsigned)((int64_t)p.B * p.H * (p.npad / 64));
+    hipLaunchKernelGGL(fa_fp8_vt_clear_kernel, dim3(heads), dim3(kThreads), 0, s, p);
+    if (d == 128) {
+      hipLaunchKernelGGL(fa_fp8_vt_amax_kernel<128>, dim3(groups), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(fa_fp8_vt_write_kernel<128>, dim3(groups), dim3(kThreads), 0, s, p);
+    } else {
+      hipLaunchKernelGGL(fa_fp8_vt_amax_kernel<64>, dim3(groups), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(fa_fp8_vt_write_kernel<64>, dim3(groups), dim3(kThreads), 0, s, p);
+    }
+    hipLaunchKernelGGL(fa_fp8_vt_scale_kernel, dim3(heads), dim3(kThreads), 0, s, p);
   } else {
     const unsigned grid = (unsigned)((int64_t)p.B * p.H * p.nblk);
     if (d == 128)
