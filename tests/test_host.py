@@ -333,3 +333,24 @@ def test_bwd_rejects_invalid_arguments():
     assert call(ws_bytes=16) == FA_ERR_INVALID_ARG
     assert call(opts=_opts(softcap=30.0)) == FA_ERR_UNSUPPORTED
     assert api.lib().fa_bwd_workspace_size(4, 4096, 16) == 4 * 16 * 4096 * 4
+
+
+def test_fp8_entry_points_reject_invalid_arguments():
+    L = api.lib()
+    def fwd(opts=None, q=FAKE, d=128, B=1, Hq=16, Hkv=16, strides=S3):
+        o = opts or _opts()
+        return L.fa_fwd_fp8(ctypes.byref(o), q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, 16, 16, Hq, Hkv, d,
+                            strides, S3, S3, None)
+    assert fwd(q=None) == FA_ERR_INVALID_ARG
+    assert fwd(d=64) == FA_ERR_UNSUPPORTED            # the FP8 kernel is built for head_dim 128
+    assert fwd(d=96) == FA_ERR_UNSUPPORTED
+    assert fwd(B=0) == FA_ERR_INVALID_ARG
+    assert fwd(Hq=6, Hkv=4) == FA_ERR_INVALID_ARG
+    assert fwd(opts=_opts(softcap=30.0)) == FA_ERR_UNSUPPORTED
+    odd = (ctypes.c_int64 * 3)(4096, 136, 8)          # byte strides must keep 16-byte rows
+    assert fwd(strides=odd) == FA_ERR_INVALID_ARG
+    assert L.fa_fp8_quantize(FAKE, 1, 16, 1, 128, S3, 0, FAKE, S3, FAKE, None) == FA_ERR_INVALID_ARG
+    assert L.fa_fp8_quantize(FAKE, 1, 16, 1, 96, S3, 64, FAKE, S3, FAKE, None) == FA_ERR_UNSUPPORTED
+    assert L.fa_fp8_quantize(None, 1, 16, 1, 128, S3, 64, FAKE, S3, FAKE, None) == FA_ERR_INVALID_ARG
+    assert L.fa_fp8_quantize_v(FAKE, 1, 16, 1, 128, S3, None, FAKE, None) == FA_ERR_INVALID_ARG
+    assert [L.fa_fp8_vt_len(n) for n in (0, 1, 64, 65, 4096)] == [0, 64, 64, 128, 4096]
