@@ -372,3 +372,38 @@ def bwd_dense(q, k, v, dout, *, scale=None, causal=False, window=None, heads=Non
             dq[b, :, h] = s * (dS @ kd[b, :, hk])
             dk[b, :, hk] += s * (dS.T @ qd[b, :, h])
     return dq, dk, dv
+
+
+def fwd_dense_alibi(q, k, v, slopes, *, scale=None, causal=False, window=None, rows=None):
+    """Attention with ALiBi ("FA4 (CuTeDSL) and engineering interfaces", section 7:
+    a linear positional bias on the logits, alibi_slopes per head): the logit of
+    query i and key j is scale q_i . k_j - slope_h |p_i - j| with p_i = i + Lk - Lq
+    (the bottom-right position, as for the causal mask), then the usual masked
+    softmax.  fp64 with S and P materialised, in numpy.
+
+    q: bf16 bits [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; slopes: [Hq] or [B, Hq].
+    rows: None, or a list of query rows (O and LSE hold those rows only).
+    Returns (O float64 [B, rows, Hq, d], LSE float64 [B, Hq, rows])."""
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    B, Nq, Hq, d = qd.shape
+    Nk, Hkv = kd.shape[1], kd.shape[2]
+    g = Hq // Hkv
+    s = _scale(scale, d)
+    sl = np.asarray(slopes, dtype=np.float64)
+    sl = np.broadcast_to(sl, (B, Hq)) if sl.ndim == 1 else sl
+    sel = np.arange(Nq) if rows is None else np.asarray(rows)
+    vis = visible_mask(Nq, Nk, causal, window)[sel]
+    dist = np.abs((sel[:, None] + (Nk - Nq)) - np.arange(Nk)[None, :]).astype(np.float64)
+    O = np.zeros((B, len(sel), Hq, d))
+    L = np.full((B, Hq, len(sel)), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            S = s * (qd[b, sel, h] @ kd[b, :, h // g].T) - sl[b, h] * dist
+            S = np.where(vis, S, -np.inf)
+            m = S.max(axis=1, keepdims=True)
+            ok = np.isfinite(m[:, 0])
+            E = np.exp(S - np.where(np.isfinite(m), m, 0.0))
+            l = E.sum(axis=1)
+            O[b, ok, h] = (E[ok] / l[ok, None]) @ vd[b, :, h // g]
+            L[b, h, ok] = m[ok, 0] + np.log(l[ok])
+    return O, L

@@ -618,3 +618,48 @@ def test_fp8_attention_matches_the_bf16_oracle_on_exact_inputs(causal, window, H
     assert np.array_equal(Or, O[:, rows]) and np.array_equal(Lr, L[:, :, rows])
     p = F8.probs(q8, qs, 64, k8, ks, 64, row=50, b=1, h=Hq - 1, g=Hq // Hkv, causal=causal, window=window)
     assert abs(p.sum() - 1) < 1e-12
+
+
+# ---------------------------------------------------------------- alibi
+@pytest.mark.parametrize("causal,window,Nq,Nk", [(True, None, 40, 40), (False, None, 33, 47), (True, (9, 0), 50, 50),
+                                                 (False, (6, 5), 31, 31), (True, None, 20, 35)])
+def test_alibi_matches_sdpa_with_an_additive_mask(causal, window, Nq, Nk):
+    """torch fp64 scaled_dot_product_attention with the bias (and -inf for the mask)
+    as a float attention mask: a library routine."""
+    g = W.generator(501 + Nq)
+    B, Hq, Hkv, d = 2, 4, 2, 16
+    q = W.randn_bf16(g, (B, Nq, Hq, d))
+    k, v = W.randn_bf16(g, (B, Nk, Hkv, d)), W.randn_bf16(g, (B, Nk, Hkv, d))
+    slopes = np.array([[0.5, 0.25, 0.125, 0.0625], [0.3, 0.2, 0.1, 0.9]])
+    O, L = oracle.fwd_dense_alibi(bits(q), bits(k), bits(v), slopes, causal=causal, window=window)
+    vis = torch.as_tensor(oracle.visible_mask(Nq, Nk, causal, window))
+    pos = torch.arange(Nq, dtype=torch.float64)[:, None] + (Nk - Nq)
+    dist = (pos - torch.arange(Nk, dtype=torch.float64)[None, :]).abs()
+    Q = torch.tensor(v_double(q)).permute(0, 2, 1, 3)
+    K = torch.tensor(v_double(k)).repeat_interleave(2, dim=2).permute(0, 2, 1, 3)
+    V = torch.tensor(v_double(v)).repeat_interleave(2, dim=2).permute(0, 2, 1, 3)
+    bias = -torch.tensor(slopes)[:, :, None, None] * dist
+    bias = bias.masked_fill(~vis, float("-inf"))
+    ref = F.scaled_dot_product_attention(Q, K, V, attn_mask=bias, scale=d ** -0.5).permute(0, 2, 1, 3)
+    lse = torch.logsumexp(d ** -0.5 * Q @ K.transpose(-1, -2) + bias, dim=-1)
+    np.testing.assert_allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, lse.numpy(), rtol=0, atol=1e-12)
+
+
+def test_alibi_zero_slopes_is_the_c_oracle_and_zero_queries_give_a_geometric_series():
+    g = W.generator(511)
+    B, N, H, d = 1, 37, 2, 16
+    q, k, v = (W.randn_bf16(g, (B, N, H, d)) for _ in range(3))
+    O, L = oracle.fwd_dense_alibi(bits(q), bits(k), bits(v), np.zeros(H), causal=True)
+    Oc, Lc = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=True)
+    np.testing.assert_allclose(O, Oc, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, Lc, rtol=0, atol=1e-12)
+    # Q = 0, causal: the weights of row i are e^{-slope t}, t = i - j = 0..i, so
+    # exp(LSE_i) = (1 - e^{-slope (i + 1)}) / (1 - e^{-slope})
+    z = torch.zeros(B, N, H, d, dtype=torch.bfloat16)
+    slopes = np.array([0.3, 1.7])
+    _, Lz = oracle.fwd_dense_alibi(bits(z), bits(k), bits(v), slopes, causal=True)
+    i = np.arange(N)
+    for h, sl in enumerate(slopes):
+        want = np.log((1 - np.exp(-sl * (i + 1))) / (1 - np.exp(-sl)))
+        np.testing.assert_allclose(Lz[0, h], want, rtol=0, atol=1e-12)
