@@ -39,7 +39,8 @@ class FaError(RuntimeError):
 class fa_attn_opts(ctypes.Structure):
     _fields_ = [("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int),
                 ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
-                ("softcap", ctypes.c_float), ("pack_gqa", ctypes.c_int)]
+                ("softcap", ctypes.c_float), ("pack_gqa", ctypes.c_int),
+                ("alibi_slopes", ctypes.c_void_p), ("alibi_batch_stride", ctypes.c_int64)]
 
 
 _lib = None
@@ -107,10 +108,16 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _opts(softmax_scale, causal, window, softcap, pack_gqa):
+def _opts(softmax_scale, causal, window, softcap, pack_gqa, alibi_slopes=None):
     wl, wr = (-1, -1) if window is None else window
+    ptr, bs = None, 0
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda or alibi_slopes.stride(-1) != 1:
+            raise TypeError("alibi_slopes must be a float32 tensor on a HIP device, heads contiguous")
+        ptr = alibi_slopes.data_ptr()
+        bs = alibi_slopes.stride(0) if alibi_slopes.dim() == 2 else 0
     return fa_attn_opts(float(softmax_scale) if softmax_scale else 0.0, int(bool(causal)), int(wl),
-                        int(wr), float(softcap), int(pack_gqa))
+                        int(wr), float(softcap), int(pack_gqa), ptr, bs)
 
 
 def _bf16_cuda(*ts):
@@ -122,8 +129,9 @@ def _bf16_cuda(*ts):
 
 
 def fa_fwd(q, k, v, *, softmax_scale=None, causal=False, window=None, softcap=0.0, pack_gqa=-1,
-           out=None, lse=None, return_lse=True, stream=None):
-    """Dense forward.  q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] bf16 -> (out, lse [B, Hq, Nq])."""
+           alibi_slopes=None, out=None, lse=None, return_lse=True, stream=None):
+    """Dense forward.  q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] bf16 -> (out, lse [B, Hq, Nq]).
+    alibi_slopes: None, or float32 [Hq] / [B, Hq] on the device."""
     _bf16_cuda(q, k, v)
     B, Nq, Hq, d = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
@@ -132,7 +140,7 @@ def fa_fwd(q, k, v, *, softmax_scale=None, causal=False, window=None, softcap=0.
     _bf16_cuda(out)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
+    o = _opts(softmax_scale, causal, window, softcap, pack_gqa, alibi_slopes)
     _check(lib().fa_fwd(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Nq, Nk,
                         Hq, Hkv, d, _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)),
                         _strides(v, (0, 1, 2)), _strides(out, (0, 1, 2)), _stream(stream)))
@@ -140,7 +148,7 @@ def fa_fwd(q, k, v, *, softmax_scale=None, causal=False, window=None, softcap=0.
 
 
 def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *, softmax_scale=None,
-                  causal=False, window=None, softcap=0.0, pack_gqa=-1, out=None, lse=None,
+                  causal=False, window=None, softcap=0.0, pack_gqa=-1, alibi_slopes=None, out=None, lse=None,
                   return_lse=True, stream=None):
     """Varlen forward.  q [Tq, Hq, d], k/v [Tk, Hkv, d], cu_seqlens int32 on device
     -> (out [Tq, Hq, d], lse [Hq, Tq])."""
@@ -156,7 +164,7 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *, softmax_
     _bf16_cuda(out)
     if lse is None and return_lse:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
-    o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
+    o = _opts(softmax_scale, causal, window, softcap, pack_gqa, alibi_slopes)
     _check(lib().fa_fwd_varlen(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, int(max_seqlen_q), Tq, Tk,
                                Hq, Hkv, d, _strides(q, (0, 1)), _strides(k, (0, 1)),

@@ -53,6 +53,20 @@ int fill_opts(const fa_attn_opts* o, int d, FaParams* p, bool* softcap) {
   p->causal = o->causal ? 1 : 0;
   p->wl = o->window_left < 0 ? -1 : o->window_left;
   p->wr = o->window_right < 0 ? -1 : o->window_right;
+  p->alibi = o->alibi_slopes;
+  p->alibi_bs = o->alibi_batch_stride;
+  p->alibi_inv_scale = 1.0f / scale;
+  if (o->alibi_slopes) {
+    if ((reinterpret_cast<uintptr_t>(o->alibi_slopes) & 3u) != 0)
+      return fail(FA_ERR_INVALID_ARG, "alibi_slopes is not 4-byte aligned");
+    if (o->alibi_batch_stride < 0) return fail(FA_ERR_INVALID_ARG, "alibi_batch_stride is negative");
+    if (*softcap) return fail(FA_ERR_UNSUPPORTED, "ALiBi together with softcap is not supported");
+  }
+  return FA_OK;
+}
+
+int no_alibi(const FaParams& p, const char* what) {
+  if (p.alibi) return fail(FA_ERR_UNSUPPORTED, "ALiBi is not supported by %s", what);
   return FA_OK;
 }
 
@@ -270,6 +284,7 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   memset(&p, 0, sizeof p);
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
+  if ((rc = no_alibi(p, "fa_fwd_varlen_paged"))) return rc;
   if (total_q == 0 || max_seqlen_q == 0) return FA_OK;  // nothing to compute
   const bool pack = resolve_pack(opts, heads_q, heads_kv);
   p.q = static_cast<const uint16_t*>(q);
@@ -354,6 +369,7 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
   memset(&p, 0, sizeof p);
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
+  if ((rc = no_alibi(p, "fa_fwd_kvcache_paged"))) return rc;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k_cache);
   p.v = static_cast<const uint16_t*>(v_cache);
@@ -508,6 +524,7 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   memset(&f, 0, sizeof f);
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &f, &softcap))) return rc;
+  if ((rc = no_alibi(f, "fa_bwd"))) return rc;
   if (softcap) return fail(FA_ERR_UNSUPPORTED, "the backward pass has no softcap");
   FaBwdParams p;
   memset(&p, 0, sizeof p);
@@ -643,6 +660,7 @@ int fa_fwd_fp8(const fa_attn_opts* opts, const void* q, const float* q_scales, c
   memset(&tmp, 0, sizeof tmp);
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &tmp, &softcap))) return rc;
+  if ((rc = no_alibi(tmp, "fa_fwd_fp8"))) return rc;
   if (softcap) return fail(FA_ERR_UNSUPPORTED, "softcap is not supported by the FP8 forward");
   FaFp8Params p;
   memset(&p, 0, sizeof p);

@@ -40,6 +40,10 @@ struct FaParams {
   float cap_in;      // softmax_scale / softcap
   float cap_out;     // softcap * log2(e)
   int causal, wl, wr;
+  // ALiBi: slopes[b * alibi_bs + h] (NULL = none), divided by the softmax scale
+  const float* alibi;
+  int64_t alibi_bs;
+  float alibi_inv_scale;
 };
 
 // FP8 (OCP e4m3) forward.  Q in blocks of FA_FP8_Q_BLOCK rows and K in blocks

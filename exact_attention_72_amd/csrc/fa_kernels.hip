@@ -606,7 +606,10 @@ __device__ __forceinline__ void wait_vmcnt_blocks(int n) {
 // with page sizes that are multiples of 16 they lie in one page: one scalar
 // block-table read per instruction.  VARLEN with PAGED is the unified batch:
 // packed queries by cu_seqlens_q, each sequence with its own cache length.
-template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED>
+// ALIBI: the logits get the linear positional bias -slope_h |p - key| ("FA4
+// (CuTeDSL) and engineering interfaces", section 7), p the query's bottom-right
+// position; applied with the element mask, which then runs on every block.
+template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   constexpr int BN = FA_BLOCK_N;  // 32 keys per block
   constexpr int NBUF = 3;  // measured best of 3, 4 and 5 stages
@@ -697,6 +700,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     mask.causal = p.causal;
     mask.wl = p.wl;
     mask.wr = p.wr;
+    // ALiBi slope of this lane's head in raw-score units (the scores are scaled later)
+    float alibi_k = 0.0f;
+    if constexpr (ALIBI) alibi_k = p.alibi[(int64_t)tile.b * p.alibi_bs + head] * p.alibi_inv_scale;
 
     // DMA sources: this lane's row of every block.  Rows past the last key (only
     // in a final partial block) are clamped to the last key so that they read
@@ -758,7 +764,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         const int key = base + 8 * (a >> 2) + (a & 3);
-        sv[a] = mask.visible(key) ? sv[a] : kNegInf;
+        float x = sv[a];
+        if constexpr (ALIBI) x = __builtin_fmaf(-alibi_k, (float)abs(mask.pos - key), x);
+        sv[a] = mask.visible(key) ? x : kNegInf;
       }
     };
     auto transform = [&](f32x16& sv) {
@@ -767,7 +775,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
         for (int a = 0; a < 16; ++a) sv[a] = softcap_log2(sv[a], p.cap_in, p.cap_out);
       }
     };
-    auto is_masked = [&](int i) { return n_lo + i < n_full_lo || n_lo + i >= n_full_hi; };
+    auto is_masked = [&](int i) { return ALIBI || n_lo + i < n_full_lo || n_lo + i >= n_full_hi; };
 
     // xs: exponentials of the current block relative to m_run, whose sums and
     // bf16 operands are formed at the start of the next step
@@ -1760,10 +1768,10 @@ int occupancy(K kernel) {
   return n;
 }
 
-template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED>
+template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false>
 hipError_t launch_prefill_t(const FaParams& p0, hipStream_t stream) {
   FaParams p = p0;
-  auto kern = fa_prefill_kernel<D, VARLEN, PACK, SOFTCAP, PAGED>;
+  auto kern = fa_prefill_kernel<D, VARLEN, PACK, SOFTCAP, PAGED, ALIBI>;
   int64_t tiles = p.total_tiles;
   if (tiles <= 0) return hipSuccess;
   int64_t grid;
@@ -1795,6 +1803,16 @@ int fa_device_cus() { return device_cus(); }
 
 hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, bool pack, bool softcap,
                              hipStream_t s) {
+  // ALiBi: dense and varlen, without softcap
+  if (p.alibi) {
+    if (paged || softcap) return hipErrorInvalidValue;
+#define FA_AL(D_, V_, P_) \
+  if (d == D_ && varlen == V_ && pack == P_) return launch_prefill_t<D_, V_, P_, false, false, true>(p, s);
+    FA_AL(128, false, false) FA_AL(128, false, true) FA_AL(128, true, false) FA_AL(128, true, true)
+    FA_AL(64, false, false) FA_AL(64, false, true) FA_AL(64, true, false) FA_AL(64, true, true)
+#undef FA_AL
+    return hipErrorInvalidValue;
+  }
 #define FA_PF(D_, V_, G_, P_, S_)                                                    \
   if (d == D_ && varlen == V_ && paged == G_ && pack == P_ && softcap == S_) \
     return launch_prefill_t<D_, V_, P_, S_, G_>(p, s);

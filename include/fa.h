@@ -44,6 +44,14 @@
  *                  once for all of them ("FA4 ...", section 5; "Attention
  *                  kernels ...", section 5.3); 0: one tile per query head;
  *                  < 0: pick automatically (on when heads_q > heads_kv).
+ *   alibi_slopes   NULL: off.  Else device float32 slopes, slope of (batch b,
+ *                  query head h) at alibi_slopes[b * alibi_batch_stride + h]
+ *                  (stride 0: one row of heads_q slopes for every batch; in the
+ *                  varlen call the batch index is the sequence): the logit of
+ *                  a query at position p and key j gets -slope * |p - j|
+ *                  ("FA4 ...", section 7, alibi_slopes), p bottom-right as for
+ *                  causal.  fa_fwd and fa_fwd_varlen, without softcap; other
+ *                  entry points return FA_ERR_UNSUPPORTED.
  */
 #ifndef EXACT_ATTENTION_72_FA_H
 #define EXACT_ATTENTION_72_FA_H
@@ -67,6 +75,8 @@ typedef struct fa_attn_opts {
   int window_right;
   float softcap;
   int pack_gqa;
+  const float* alibi_slopes;
+  int64_t alibi_batch_stride;
 } fa_attn_opts;
 
 /* Dense (padded) attention forward ("FA4 ...", section 3 flash_attn_func).

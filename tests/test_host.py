@@ -354,3 +354,22 @@ def test_fp8_entry_points_reject_invalid_arguments():
     assert L.fa_fp8_quantize(None, 1, 16, 1, 128, S3, 64, FAKE, S3, FAKE, None) == FA_ERR_INVALID_ARG
     assert L.fa_fp8_quantize_v(FAKE, 1, 16, 1, 128, S3, None, FAKE, None) == FA_ERR_INVALID_ARG
     assert [L.fa_fp8_vt_len(n) for n in (0, 1, 64, 65, 4096)] == [0, 64, 64, 128, 4096]
+
+
+def test_alibi_is_rejected_where_it_is_not_built():
+    L = api.lib()
+    sl = ctypes.c_void_p(1 << 21)
+    o = fa_attn_opts(0.0, 1, -1, -1, 30.0, -1, sl, 0)           # with softcap
+    assert L.fa_fwd(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None, 1, 16, 16, 16, 16, 128, S3, S3, S3, S3,
+                    None) == FA_ERR_UNSUPPORTED
+    o = fa_attn_opts(0.0, 1, -1, -1, 0.0, -1, ctypes.c_void_p((1 << 21) + 2), 0)   # misaligned slopes
+    assert L.fa_fwd(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None, 1, 16, 16, 16, 16, 128, S3, S3, S3, S3,
+                    None) == FA_ERR_INVALID_ARG
+    o = fa_attn_opts(0.0, 1, -1, -1, 0.0, -1, sl, -1)           # negative batch stride
+    assert L.fa_fwd(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None, 1, 16, 16, 16, 16, 128, S3, S3, S3, S3,
+                    None) == FA_ERR_INVALID_ARG
+    o = fa_attn_opts(0.0, 1, -1, -1, 0.0, -1, sl, 0)
+    assert L.fa_bwd(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 16, 16, 16, 128,
+                    S3, S3, S3, S3, S3, S3, S3, S3, FAKE, 1 << 20, None) == FA_ERR_UNSUPPORTED
+    assert L.fa_fwd_fp8(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 16, 16, 16, 128,
+                        S3, S3, S3, None) == FA_ERR_UNSUPPORTED
