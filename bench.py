@@ -9,8 +9,8 @@ the long-context local attention with softcap (N = 32768, 32 heads,
 window 4096, softcap 30), and the chunked prefill over a paged cache (4 x 4096
 new tokens against 16384 cached keys, 32/8 heads) with the in-place K/V append
 of that chunk, a unified batch of 64 decode requests and 4 prefill chunks
-in one launch, the backward pass of the prefill workload, and the FP8 (e4m3)
-forward of the prefill workload.
+in one launch, the backward pass of the prefill workload, the FP8 (e4m3) forward of the
+prefill workload, and the prefill workload with ALiBi.
 
 Prints one JSON line:
   value        prefill TFLOP/s, FLOPs counted as 4 * B * H * N^2 * d * 1/2 (the
@@ -287,6 +287,27 @@ def bench_bwd(api, W, steps, warmup):
                        "flop_convention": "2.5 * 4*B*H*N^2*d/2"}}
 
 
+def bench_alibi(api, W, steps, warmup):
+    """The dense causal prefill workload with ALiBi (slopes 2^(-8 (h + 1) / H)): fa_fwd per
+    launch, TFLOP/s on the same convention (the bias is not counted)."""
+    import torch
+    c = W.WORKLOADS["prefill_b4_h16_n4096_d128_causal"]
+    B, N, H, d = c["B"], c["N"], c["Hq"], c["d"]
+    t = W.dense(c["seed"], B, N, H, c["Hkv"], d, device="cuda")
+    slopes = torch.exp2(-8.0 * (torch.arange(H, dtype=torch.float32, device="cuda") + 1) / H)
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fn = lambda: api.fa_fwd(t["q"], t["k"], t["v"], causal=True, alibi_slopes=slopes, out=out, lse=lse)  # noqa
+    _, ms = time_launches(fn, steps, warmup)
+    tf = prefill_flops(B, H, N, d, True) / (ms * 1e-3) / 1e12
+    return {"metric": "attn fwd with ALiBi TFLOP/s (bf16 N=4k d=128 causal)", "unit": "TFLOP/s",
+            "value": round(tf, 2), "ms": round(ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
+            "config": {"workload": "prefill_b4_h16_n4096_d128_causal alibi", "batch": B, "heads": H,
+                       "seq_len": N, "head_dim": d, "causal": True, "slopes": "2^(-8(h+1)/H)"}}
+
+
 def bench_fp8(api, W, steps, warmup):
     """FP8 (e4m3) forward of the dense causal prefill workload (batch 4, 16 heads, N = 4096,
     d = 128): fa_fwd_fp8 per launch on inputs quantized beforehand, TFLOP/s on the same
@@ -368,6 +389,7 @@ def main():
     ap.add_argument("--no-unified", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-alibi", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -435,6 +457,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_fp8:
         line["fp8"] = bench_fp8(api, W, max(20, args.steps // 2), max(20, args.warmup // 2))
+        torch.cuda.empty_cache()
+    if not args.no_alibi:
+        line["alibi"] = bench_alibi(api, W, max(20, args.steps // 2), max(20, args.warmup // 2))
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         tc = W.dense(c["seed"], B, N, H, c["Hkv"], d)

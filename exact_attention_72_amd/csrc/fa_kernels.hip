@@ -608,7 +608,7 @@ __device__ __forceinline__ void wait_vmcnt_blocks(int n) {
 // packed queries by cu_seqlens_q, each sequence with its own cache length.
 // ALIBI: the logits get the linear positional bias -slope_h |p - key| ("FA4
 // (CuTeDSL) and engineering interfaces", section 7), p the query's bottom-right
-// position; applied with the element mask, which then runs on every block.
+// position: with the element mask on blocks a boundary cuts, alone on the others.
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   constexpr int BN = FA_BLOCK_N;  // 32 keys per block
@@ -775,7 +775,17 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
         for (int a = 0; a < 16; ++a) sv[a] = softcap_log2(sv[a], p.cap_in, p.cap_out);
       }
     };
-    auto is_masked = [&](int i) { return ALIBI || n_lo + i < n_full_lo || n_lo + i >= n_full_hi; };
+    auto is_masked = [&](int i) { return n_lo + i < n_full_lo || n_lo + i >= n_full_hi; };
+    // ALiBi on a block no boundary cuts: the bias alone, -k |key - pos| with
+    // key - pos = fb + (a compile-time offset per slot), exact in fp32
+    auto apply_bias = [&](f32x16& sv, int i) {
+      if constexpr (ALIBI) {
+        const float fb = (float)((n_lo + i) * BN + 4 * kg - mask.pos);
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+          sv[a] = __builtin_fmaf(-alibi_k, fabsf(fb + (float)(8 * (a >> 2) + (a & 3))), sv[a]);
+      }
+    };
 
     // xs: exponentials of the current block relative to m_run, whose sums and
     // bf16 operands are formed at the start of the next step
@@ -791,7 +801,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       stage_barrier();
       f32x16 s0 = qk_block<D, 0>(0u, qreg, off);
       transform(s0);
-      if (is_masked(0)) apply_mask(s0, 0);
+      if (is_masked(0))
+        apply_mask(s0, 0);
+      else
+        apply_bias(s0, 0);
       float alpha;
       move_reference(block_max(s0), m_run, c, alpha);  // nothing accumulated yet
       exps(s0, neg_ref(m_run, c), 0, 16);
@@ -833,7 +846,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       const bool late = SOFTCAP && !masked && !first;
       if (!late) {
         transform(s_next);
-        if (masked) apply_mask(s_next, i + 1);
+        if (masked)
+          apply_mask(s_next, i + 1);
+        else
+          apply_bias(s_next, i + 1);
       }
       // Reference for the exponentials of block i + 1.  While some row of the
       // wave has seen no visible key its reference must be set from this block's
