@@ -1554,7 +1554,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p) {
   constexpr int BM = 32;
-  constexpr int NBUF = 3;
+  constexpr int NBUF = 4;
   using G = DmaGeom<D, BM>;
   constexpr int T = G::kTensorBytes;
   constexpr int kStage = 4 * T + 1024;  // Q rows, Q transposed, dO rows, dO transposed, L and D
@@ -1629,11 +1629,16 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     dv[db] = f32x16{};
   }
   const uint32_t ld_base = lds_addr(smem) + 4 * T + 16 * kg;  // L of queries 8 j + 4 kg .. + 3 at + 32 j
-  for (int j = 0; j < NBUF - 1 && j < steps; ++j) issue(j);
-  for (int s_ = 0; s_ < steps; ++s_) {
-    wait_vmcnt_blocks<kPer>(min(s_ + NBUF - 2, steps - 1) - s_);
-    stage_barrier();
-    if (s_ + NBUF - 1 < steps) issue(s_ + NBUF - 1);
+
+  // Step s in two parts.  head(s): S = Q K^T and dP = dO V^T from block s's Q and
+  // dO rows, then P and dS (bf16) from them and the block's L and D.  tail(s):
+  // dV^T += dO^T P and dK^T += Q^T dS from block s's transposed reads.  Iteration
+  // s issues head(s)'s products, then tail(s - 1)'s, then head(s)'s arithmetic,
+  // which runs while the matrix unit works through tail(s - 1).
+  struct HeadOut {
+    bf16x8 p0, p1, d0, d1;
+  };
+  auto head = [&](int s_) __attribute__((always_inline)) {
     const uint32_t st = (uint32_t)((s_ % NBUF) * kStage);
     const int q0 = (qb_lo + s_ % nqb) * BM;
     // element masks only where the query block cuts the wave's 32 keys (or runs past Lq)
@@ -1652,7 +1657,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     read_k_part<D, 0, 0, D / 32>(st + 2 * T, off, oa);
     lgkm_wait<D / 32>(qa);
     read_k_part<D, 0, D / 32, D / 32>(st + 2 * T, off, oa);
-    f32x16 s = qk_mma<D>(qa, kreg);  // S = Q K^T: rows queries, lane column = this key
+    const f32x16 sv = qk_mma<D>(qa, kreg);  // S = Q K^T: rows queries, lane column = this key
     // L and D of the accumulator rows: rows 8 j + 4 kg .. + 3 are slots 4 j .. 4 j + 3
     u32x4 lr[4], dr[4];
 #pragma unroll
@@ -1663,34 +1668,43 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     const f32x16 dp = qk_mma<D>(oa, vreg);  // dP = dO V^T
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lr[0]), "+v"(lr[1]), "+v"(lr[2]), "+v"(lr[3]), "+v"(dr[0]),
                  "+v"(dr[1]), "+v"(dr[2]), "+v"(dr[3]));
-    f32x8 p0f, p1f, d0f, d1f;
+    return [=]() __attribute__((always_inline)) {  // the arithmetic, run later
+      f32x8 p0f, p1f, d0f, d1f;
 #pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      const int qi = q0 + 8 * (a >> 2) + 4 * kg + (a & 3);
-      const int pos = qi + (Lk - Lq);
-      const bool vis = full || (key_ok && qi < Lq && (!p.causal || key <= pos) && (p.wl < 0 || key >= pos - p.wl) &&
-                                (p.wr < 0 || key <= pos + p.wr));
-      const float l = __uint_as_float(lr[a >> 2][a & 3]);
-      const float dl = __uint_as_float(dr[a >> 2][a & 3]);
-      const float nl = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
-      const float pa = vis ? exp2_fast(__builtin_fmaf(s[a], c, -nl)) : 0.0f;
-      const float ds = pa * (dp[a] - dl);
-      if (a < 8) {
-        p0f[a] = pa;
-        d0f[a] = ds;
-      } else {
-        p1f[a - 8] = pa;
-        d1f[a - 8] = ds;
+      for (int a = 0; a < 16; ++a) {
+        const int qi = q0 + 8 * (a >> 2) + 4 * kg + (a & 3);
+        const int pos = qi + (Lk - Lq);
+        const bool vis = full || (key_ok && qi < Lq && (!p.causal || key <= pos) &&
+                                  (p.wl < 0 || key >= pos - p.wl) && (p.wr < 0 || key <= pos + p.wr));
+        const float l = __uint_as_float(lr[a >> 2][a & 3]);
+        const float dl = __uint_as_float(dr[a >> 2][a & 3]);
+        const float nl = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
+        const float pa = vis ? exp2_fast(__builtin_fmaf(sv[a], c, -nl)) : 0.0f;
+        const float ds = pa * (dp[a] - dl);
+        if (a < 8) {
+          p0f[a] = pa;
+          d0f[a] = ds;
+        } else {
+          p1f[a - 8] = pa;
+          d1f[a - 8] = ds;
+        }
       }
-    }
-    const bf16x8 p0 = __builtin_convertvector(p0f, bf16x8), p1 = __builtin_convertvector(p1f, bf16x8);
-    const bf16x8 d0 = __builtin_convertvector(d0f, bf16x8), d1 = __builtin_convertvector(d1f, bf16x8);
-    // dV^T += dO^T P (dO read transposed), dK^T += Q^T dS (Q read transposed), in
-    // eight units of D / 64 d-blocks: unit u reads chunk u / 2 (dO^T keys 0..15,
-    // dO^T keys 16..31, Q^T keys 0..15, Q^T keys 16..31), half u % 2 of the
-    // d-blocks.  Three units are in flight while a fourth feeds its products; each
-    // unit has registers of its own, so a read never lands in operands of products
-    // still waiting to start.
+      HeadOut h;
+      h.p0 = __builtin_convertvector(p0f, bf16x8);
+      h.p1 = __builtin_convertvector(p1f, bf16x8);
+      h.d0 = __builtin_convertvector(d0f, bf16x8);
+      h.d1 = __builtin_convertvector(d1f, bf16x8);
+      return h;
+    };
+  };
+  // dV^T += dO^T P (dO read transposed), dK^T += Q^T dS (Q read transposed), in
+  // eight units of D / 64 d-blocks: unit u reads chunk u / 2 (dO^T keys 0..15,
+  // dO^T keys 16..31, Q^T keys 0..15, Q^T keys 16..31), half u % 2 of the
+  // d-blocks.  Three units are in flight while a fourth feeds its products; each
+  // unit has registers of its own, so a read never lands in operands of products
+  // still waiting to start.
+  auto tail = [&](int s_, const HeadOut& h) __attribute__((always_inline)) {
+    const uint32_t st = (uint32_t)((s_ % NBUF) * kStage);
     constexpr int UD = D / 64, UR = 2 * UD;
     u32x2 lo[8][UD], hi[8][UD];
     auto rd = [&](auto uc) __attribute__((always_inline)) {
@@ -1704,14 +1718,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
       for (int i = 0; i < UD; ++i) asm volatile("" : "+v"(lo[u][i]), "+v"(hi[u][i]));
     };
     auto mm = [&](auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value, c = u / 2, h = u % 2;
+      constexpr int u = decltype(uc)::value, c = u / 2, hh = u % 2;
 #pragma unroll
       for (int i = 0; i < UD; ++i) {
         const u32x4 a = {lo[u][i].x, lo[u][i].y, hi[u][i].x, hi[u][i].y};
-        if constexpr (c == 0) mfma_acc(dv[h * UD + i], a, p0);
-        if constexpr (c == 1) mfma_acc(dv[h * UD + i], a, p1);
-        if constexpr (c == 2) mfma_acc(dk[h * UD + i], a, d0);
-        if constexpr (c == 3) mfma_acc(dk[h * UD + i], a, d1);
+        if constexpr (c == 0) mfma_acc(dv[hh * UD + i], a, h.p0);
+        if constexpr (c == 1) mfma_acc(dv[hh * UD + i], a, h.p1);
+        if constexpr (c == 2) mfma_acc(dk[hh * UD + i], a, h.d0);
+        if constexpr (c == 3) mfma_acc(dk[hh * UD + i], a, h.d1);
       }
     };
     using I0 = std::integral_constant<int, 0>;
@@ -1734,9 +1748,26 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     wt(I5{}, W2{}), mm(I5{});
     wt(I6{}, W1{}), mm(I6{});
     wt(I7{}, W0{}), mm(I7{});
-    // Settle the accumulators before the step ends: the compiler may copy them
-    // between registers at the loop's edges and does not see that the products
-    // above are still writing them.
+  };
+
+  // Ring of NBUF = 4 stages, the DMA of block s + 2 issued at iteration s: its
+  // buffer last held block s - 2, whose tail ran in iteration s - 1.
+  for (int j = 0; j < 2 && j < steps; ++j) issue(j);
+  HeadOut prev;
+  for (int s_ = 0; s_ < steps; ++s_) {
+    wait_vmcnt_blocks<kPer>(min(steps - 1, s_ + 1) - s_);  // block s landed; block s + 1 may be in flight
+    stage_barrier();
+    if (s_ + 2 < steps) issue(s_ + 2);
+    auto arith = head(s_);
+    if (s_ > 0) tail(s_ - 1, prev);
+    prev = arith();
+    // Settle the accumulators before the iteration ends: the compiler may copy
+    // them between registers at the loop's edges and does not see that the
+    // products above are still writing them.
+    drain_acc(dk, dv);
+  }
+  if (steps > 0) {
+    tail(steps - 1, prev);
     drain_acc(dk, dv);
   }
   if (key_ok) {
