@@ -663,3 +663,98 @@ def test_alibi_zero_slopes_is_the_c_oracle_and_zero_queries_give_a_geometric_ser
     for h, sl in enumerate(slopes):
         want = np.log((1 - np.exp(-sl * (i + 1))) / (1 - np.exp(-sl)))
         np.testing.assert_allclose(Lz[0, h], want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- brute force
+import struct  # noqa: E402
+
+
+def _bf(bits16):
+    """bf16 bit pattern -> Python float (through the fp32 bit layout)."""
+    return struct.unpack("<f", struct.pack("<I", int(bits16) << 16))[0]
+
+
+def _naive_row(qrow, keys, vals, pos, scale, causal, wl, wr, softcap):
+    """One query row in plain Python: visibility per key, scaled dot products,
+    optional softcap, max-subtracted exponentials, weighted sum of V.  Returns
+    (O list, LSE); a row that sees no key gives (zeros, -inf)."""
+    logits = []
+    for j, kr in enumerate(keys):
+        vis = (not causal or j <= pos) and (wl < 0 or j >= pos - wl) and (wr < 0 or j <= pos + wr)
+        if not vis:
+            continue
+        s = scale * sum(a * b for a, b in zip(qrow, kr))
+        if softcap > 0:
+            s = softcap * math.tanh(s / softcap)
+        logits.append((j, s))
+    d = len(qrow)
+    if not logits:
+        return [0.0] * d, -math.inf
+    m = max(s for _, s in logits)
+    w = [(j, math.exp(s - m)) for j, s in logits]
+    tot = sum(x for _, x in w)
+    out = [sum(x * vals[j][c] for j, x in w) / tot for c in range(d)]
+    return out, m + math.log(tot)
+
+
+def _rows_of(bits, n0, n1, h):
+    return [[_bf(x) for x in bits[t, h]] for t in range(n0, n1)]
+
+
+@pytest.mark.parametrize("causal,window,softcap,Hq,Hkv,Nq,Nk", [
+    (False, None, 0.0, 2, 2, 7, 7), (True, None, 0.0, 2, 1, 9, 9), (True, None, 0.0, 2, 2, 5, 11),
+    (True, None, 0.0, 2, 2, 12, 6), (False, (2, 1), 0.0, 2, 1, 8, 8), (True, (3, 0), 5.0, 2, 2, 10, 10),
+    (False, None, 2.0, 4, 2, 6, 9)])
+def test_c_oracle_equals_a_naive_python_loop_on_tiny_dense_shapes(causal, window, softcap, Hq, Hkv, Nq, Nk):
+    g = W.generator(701 + Nq * 13 + Nk)
+    d = 8
+    q, k, v = W.randn_bf16(g, (1, Nq, Hq, d), 1.5), W.randn_bf16(g, (1, Nk, Hkv, d)), W.randn_bf16(g, (1, Nk, Hkv, d))
+    qb, kb, vb = bits(q)[0], bits(k)[0], bits(v)[0]
+    O, L = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=causal, window=window, softcap=softcap)
+    wl, wr = (-1, -1) if window is None else window
+    for h in range(Hq):
+        keys, vals = _rows_of(kb, 0, Nk, h // (Hq // Hkv)), _rows_of(vb, 0, Nk, h // (Hq // Hkv))
+        for i in range(Nq):
+            o, lse = _naive_row([_bf(x) for x in qb[i, h]], keys, vals, i + Nk - Nq, d ** -0.5, causal, wl, wr,
+                                softcap)
+            assert max(abs(a - b) for a, b in zip(o, O[0, i, h])) <= 1e-12
+            assert (lse == L[0, h, i] == -math.inf) or abs(lse - L[0, h, i]) <= 1e-12
+
+
+def test_c_oracle_equals_a_naive_python_loop_on_tiny_varlen_and_paged_shapes():
+    g = W.generator(711)
+    d, Hq, Hkv = 8, 4, 2
+    # varlen: sequences of 3, 0, 7 and 5 tokens, q and k lengths differing, causal
+    lq, lk = [3, 0, 7, 5], [5, 2, 7, 9]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = W.randn_bf16(g, (int(cq[-1]), Hq, d))
+    k, v = W.randn_bf16(g, (int(ck[-1]), Hkv, d)), W.randn_bf16(g, (int(ck[-1]), Hkv, d))
+    O, L = oracle.fwd_varlen(bits(q), bits(k), bits(v), cq.astype(np.int32), ck.astype(np.int32), causal=True)
+    qb, kb, vb = bits(q), bits(k), bits(v)
+    for b in range(4):
+        for h in range(Hq):
+            keys = _rows_of(kb, ck[b], ck[b + 1], h // 2)
+            vals = _rows_of(vb, ck[b], ck[b + 1], h // 2)
+            for t in range(lq[b]):
+                i = cq[b] + t
+                o, lse = _naive_row([_bf(x) for x in qb[i, h]], keys, vals, t + lk[b] - lq[b], d ** -0.5, True, -1,
+                                    -1, 0.0)
+                assert max(abs(a - c) for a, c in zip(o, O[i, h])) <= 1e-12
+                assert abs(lse - L[h, i]) <= 1e-12
+    # paged: 4-token pages in a shuffled pool, 2 sequences of 6 and 9 cached keys, 2 new queries each
+    page, pool = 4, 8
+    kc, vc = W.randn_bf16(g, (pool, page, Hkv, d)), W.randn_bf16(g, (pool, page, Hkv, d))
+    bt = np.array([[5, 2, 7], [0, 6, 3]], dtype=np.int32)
+    sl = np.array([6, 9], dtype=np.int32)
+    qp = W.randn_bf16(g, (2, 2, Hq, d))
+    O, L = oracle.fwd_paged(bits(qp), bits(kc), bits(vc), bt, sl, causal=True, window=(4, 0), softcap=3.0)
+    kcb, vcb, qpb = bits(kc), bits(vc), bits(qp)
+    for b in range(2):
+        for h in range(Hq):
+            keys = [[_bf(x) for x in kcb[bt[b, t // page], t % page, h // 2]] for t in range(sl[b])]
+            vals = [[_bf(x) for x in vcb[bt[b, t // page], t % page, h // 2]] for t in range(sl[b])]
+            for i in range(2):
+                o, lse = _naive_row([_bf(x) for x in qpb[b, i, h]], keys, vals, i + sl[b] - 2, d ** -0.5, True, 4, 0,
+                                    3.0)
+                assert max(abs(a - c) for a, c in zip(o, O[b, i, h])) <= 1e-12
+                assert abs(lse - L[b, h, i]) <= 1e-12
