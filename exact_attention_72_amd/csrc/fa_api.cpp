@@ -248,13 +248,18 @@ int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, in
       max_blocks_per_seq <= 0)
     return 1;
   if ((int64_t)seqlen_q * (heads_q / heads_kv) > FA_PAGED_MAX_ROWS) return 1;  // prefill over the cache
-  // About 32 workgroups per compute unit over the launch (two resident at a
-  // time), so that sequences of very unequal length still level out: on 64
-  // sequences of 1k-32k keys, 16 splits give 5.62 TB/s against 5.46 for 4 and
-  // 4.70 for 1.  Each split keeps at least one page; at most 64 splits.
+  // With more than one split the workgroups take the sequences longest first
+  // (batch <= FA_SEQ_ORDER_MAX), so a few workgroups per compute unit level
+  // out sequences of very unequal length: about 4 per compute unit and at least
+  // 2 splits.  On 64 sequences of 1k-32k keys, 32/8 heads: 2 splits 5.89 TB/s,
+  // 4 splits 5.74, 8 splits 5.65, 16 splits 5.57, 1 split 4.70.  Without the
+  // order (larger batches) about 32 per compute unit, so that the lengths level
+  // out by number.  Each split keeps at least one page; at most 64 splits.
   const int64_t units = (int64_t)batch * heads_kv;
-  const int64_t target = 32 * (int64_t)fa_device_cus();
+  const bool ordered = batch <= FA_SEQ_ORDER_MAX;
+  const int64_t target = (ordered ? 4 : 32) * (int64_t)fa_device_cus();
   int64_t s = (target + units - 1) / units;
+  if (ordered && s < 2) s = 2;
   if (s > 64) s = 64;
   if (s > max_blocks_per_seq) s = max_blocks_per_seq;
   return s < 1 ? 1 : (int)s;
@@ -322,11 +327,19 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   return FA_OK;
 }
 
-size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_dim, int num_splits) {
-  if (num_splits <= 1 || batch <= 0 || seqlen_q <= 0 || heads_q <= 0 || head_dim <= 0) return 0;
+// Partial (O, LSE) bytes of a split-KV call, rounded up to 256; the sequence
+// order (one int32 per sequence, when batch <= FA_SEQ_ORDER_MAX) follows them.
+static size_t kvcache_partial_bytes(int batch, int seqlen_q, int heads_q, int head_dim, int num_splits) {
   size_t rows = (size_t)batch * seqlen_q * heads_q;
   size_t bytes = (size_t)num_splits * rows * ((size_t)head_dim + 1) * 4;
   return (bytes + 255) & ~(size_t)255;
+}
+
+size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_dim, int num_splits) {
+  if (num_splits <= 1 || batch <= 0 || seqlen_q <= 0 || heads_q <= 0 || head_dim <= 0) return 0;
+  size_t bytes = kvcache_partial_bytes(batch, seqlen_q, heads_q, head_dim, num_splits);
+  if (batch <= FA_SEQ_ORDER_MAX) bytes += ((size_t)batch * 4 + 255) & ~(size_t)255;
+  return bytes;
 }
 
 int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, const void* v_cache,
@@ -404,6 +417,14 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
   if (num_splits > 1) {
     p.o_part = static_cast<float*>(workspace);
     p.lse_part = p.o_part + (size_t)num_splits * rows * head_dim;
+    if (batch <= FA_SEQ_ORDER_MAX) {
+      int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                  kvcache_partial_bytes(batch, seqlen_q, heads_q, head_dim,
+                                                                        num_splits));
+      hipError_t e = fa_launch_seq_order(cache_seqlens, batch, order, s);
+      if (e != hipSuccess) return hip_fail(e, "sequence order launch");
+      p.seq_order = order;
+    }
   }
   hipError_t e = fa_launch_paged(p, head_dim, softcap, s);
   if (e != hipSuccess) return hip_fail(e, "paged launch");

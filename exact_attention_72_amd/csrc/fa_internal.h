@@ -35,6 +35,9 @@ struct FaParams {
   int page, max_blocks, num_splits;
   float* o_part;
   float* lse_part;
+  // split-KV decode: sequence of the i-th group of workgroups, longest first
+  // (NULL: batch order)
+  const int32_t* seq_order;
   // score transform
   float scale_log2;  // softmax_scale * log2(e)
   float cap_in;      // softmax_scale / softcap
@@ -161,6 +164,10 @@ int fa_device_cus();
 hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, bool pack, bool softcap,
                              hipStream_t s);
 hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t stream);
+// Longest-first order of the sequences by cache length (ties by index) into
+// order[0, B); B at most FA_SEQ_ORDER_MAX.
+constexpr int FA_SEQ_ORDER_MAX = 4096;
+hipError_t fa_launch_seq_order(const int32_t* lens, int B, int32_t* order, hipStream_t stream);
 hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_append(const FaAppendParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_rotary(const FaRotaryParams& p, int d, hipStream_t stream);

@@ -957,6 +957,28 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   }
 }
 
+// ------------------------------------------------------------------ sequence order
+// Rank of each sequence by cache length, longest first, ties by index: a strict
+// total order, so order[] receives a permutation of [0, B).  Each thread ranks
+// one sequence against all B lengths, staged through LDS 256 at a time.
+__global__ __launch_bounds__(kThreads) void fa_seq_order_kernel(const int32_t* lens, int B, int32_t* order) {
+  __shared__ int32_t sl[kThreads];
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  const int mine = b < B ? lens[b] : 0;
+  int rank = 0;
+  for (int c0 = 0; c0 < B; c0 += kThreads) {
+    __syncthreads();
+    if (c0 + (int)threadIdx.x < B) sl[threadIdx.x] = lens[c0 + threadIdx.x];
+    __syncthreads();
+    const int n = min(kThreads, B - c0);
+    for (int j = 0; j < n; ++j) {
+      const int other = sl[j];
+      rank += (other > mine) | ((other == mine) & (c0 + j < b));
+    }
+  }
+  if (b < B) order[rank] = b;
+}
+
 // ------------------------------------------------------------------ paged split-KV kernel
 // One workgroup per (sequence b, KV head, split).  The packed query rows
 // (seqlen_q tokens x g heads, at most 32) are the same for all four waves; each
@@ -999,7 +1021,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
 
   const int S = p.num_splits;
   const int unit = blockIdx.x;
-  const int b = unit / (p.Hkv * S);
+  // groups of Hkv * S workgroups take the sequences longest first when an order
+  // is given, so that the short ones fill the end of the grid
+  const int b = p.seq_order ? scalar_load_i32(p.seq_order + unit / (p.Hkv * S)) : unit / (p.Hkv * S);
   const int kvh = (unit / S) % p.Hkv;
   const int split = unit % S;
 
@@ -1881,6 +1905,13 @@ hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t s
   if (d == 128) return softcap ? launch_paged_t<128, true>(p, s) : launch_paged_t<128, false>(p, s);
   if (d == 64) return softcap ? launch_paged_t<64, true>(p, s) : launch_paged_t<64, false>(p, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t fa_launch_seq_order(const int32_t* lens, int B, int32_t* order, hipStream_t s) {
+  if (B <= 0 || B > FA_SEQ_ORDER_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fa_seq_order_kernel, dim3((unsigned)((B + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                     lens, B, order);
+  return hipGetLastError();
 }
 
 hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t s) {

@@ -173,15 +173,20 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
                         const int64_t v_strides[3], const int64_t o_strides[2], void* stream);
 
 /* Split count of fa_fwd_kvcache_paged for num_splits == 0 (host only, no device
- * work; it reads the current device's compute-unit count): about 32
- * workgroups per compute unit over batch * heads_kv, at most 64 and at most
- * max_blocks_per_seq splits, and 1 when the call runs as chunked prefill
- * ("FA4 ...", section 6.2: the split count is chosen to fill the machine). */
+ * work; it reads the current device's compute-unit count): about 4 workgroups
+ * per compute unit over batch * heads_kv and at least 2 when batch <= 4096
+ * (the split workgroups then take the sequences longest first), about 32 per
+ * compute unit for larger batches; at most 64 and at most max_blocks_per_seq
+ * splits, and 1 when the call runs as chunked prefill ("FA4 ...", section 6.2:
+ * the split count is chosen to fill the machine). */
 int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, int page_size,
                           int max_blocks_per_seq);
 
 /* Bytes of workspace fa_fwd_kvcache_paged needs: 0 for num_splits == 1, else
- * num_splits * batch * seqlen_q * heads_q * (head_dim + 1) * 4 rounded up to 256. */
+ * num_splits * batch * seqlen_q * heads_q * (head_dim + 1) * 4 rounded up to 256
+ * (the fp32 partial O and LSE), plus, when batch <= 4096, batch * 4 rounded up
+ * to 256 (the order in which the split workgroups take the sequences: longest
+ * cache first, computed on the device from cache_seqlens). */
 size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_dim,
                                  int num_splits);
 

@@ -50,6 +50,23 @@ def test_paged_small(page, lens, Hq, Hkv, d, Nq, num_splits):
     check_close(out, lse, o_ref, l_ref, f"paged page={page} S={num_splits} lens={lens}")
 
 
+@pytest.mark.parametrize("num_splits", [2, 4])
+def test_paged_longest_first_order_with_ties(num_splits):
+    """With num_splits > 1 the workgroups take the sequences longest first (an order computed
+    on the device); repeated lengths, a one-key sequence and 300 sequences (more than one
+    256-wide ranking block) must still give every sequence exactly its own result."""
+    g = torch.Generator().manual_seed(77)
+    lens = [int(x) for x in torch.randint(1, 600, (300,), generator=g)]
+    lens[:40] = [257] * 40
+    lens[40:45] = [1] * 5
+    t = W.paged(78 + num_splits, len(lens), 8, 2, 64, 16, 0, 0, cache_seqlens=lens)
+    kc, vc = poison_unused(t)
+    out, lse = run(t, kc, vc, num_splits, causal=True)
+    o_ref, l_ref = oracle.fwd_paged(bits(t["q"]), bits(t["k_cache"]), bits(t["v_cache"]),
+                                    t["block_table"].numpy(), t["cache_seqlens"].numpy(), causal=True)
+    check_close(out, lse, o_ref, l_ref, f"paged longest-first S={num_splits}")
+
+
 def test_paged_window_softcap():
     t = W.paged(77, 3, 8, 2, 128, 16, 0, 0, cache_seqlens=[50, 400, 999], Nq=2, mult=2.0)
     kw = dict(causal=True, window=(100, 0), softcap=30.0)
@@ -191,9 +208,11 @@ def test_paged_prefill_rejects_splits():
 
 def test_num_splits_heuristic():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for B, Hkv, maxb in [(64, 8, 128), (1, 8, 128), (4, 2, 3), (256, 8, 128)]:
-        want = max(1, min(64, maxb, -(-32 * cus // (B * Hkv))))
+    for B, Hkv, maxb in [(64, 8, 128), (1, 8, 128), (4, 2, 3), (256, 8, 128), (4096, 8, 128), (1, 8, 1)]:
+        want = max(1, min(64, maxb, max(2, -(-4 * cus // (B * Hkv)))))
         assert api.fa_kvcache_num_splits(B, 1, 4 * Hkv, Hkv, 256, maxb) == want
+    # beyond 4096 sequences there is no longest-first order: about 32 workgroups per CU
+    assert api.fa_kvcache_num_splits(5000, 1, 32, 8, 256, 128) == max(1, -(-32 * cus // (5000 * 8)))
     assert api.fa_kvcache_num_splits(2, 40, 8, 2, 16, 100) == 1   # chunked prefill
 
 

@@ -159,9 +159,17 @@ def test_paged_rejects_invalid_arguments():
 
 
 def test_workspace_size_formula():
+    def up(x):
+        return (x + 255) // 256 * 256
     assert api.fa_kvcache_workspace_size(64, 1, 32, 128, 1) == 0
     n = 16 * 64 * 32 * (128 + 1) * 4
-    assert api.fa_kvcache_workspace_size(64, 1, 32, 128, 16) == (n + 255) // 256 * 256
+    # fp32 partials, then one int32 per sequence for the longest-first order
+    assert api.fa_kvcache_workspace_size(64, 1, 32, 128, 16) == up(n) + up(64 * 4)
+    n = 4 * 4096 * 1 * 8 * (64 + 1) * 4
+    assert api.fa_kvcache_workspace_size(4096, 1, 8, 64, 4) == up(n) + up(4096 * 4)
+    # beyond 4096 sequences the batch order is kept and no order is stored
+    n = 2 * 4097 * 1 * 8 * (64 + 1) * 4
+    assert api.fa_kvcache_workspace_size(4097, 1, 8, 64, 2) == up(n)
 
 
 def test_combine_rejects_invalid_arguments():
