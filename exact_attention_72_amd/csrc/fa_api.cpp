@@ -322,7 +322,17 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   // on a mixed batch of long chunks and one-token requests (416 against 358
   // TFLOP/s), unlike the plain varlen batch
   p.persistent = 1;
-  hipError_t e = fa_launch_prefill(p, head_dim, true, true, pack, softcap, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // sequences of at most FA_PAGED_MAX_ROWS packed rows (decode steps, short
+  // chunks) run in the decode kernel, one workgroup per (sequence, KV head) with
+  // its query heads packed into the product columns; the prefill kernel gives
+  // them no tiles
+  p.skip_rows = FA_PAGED_MAX_ROWS;
+  FaParams pd = p;
+  pd.num_splits = 1;
+  hipError_t e = fa_launch_paged(pd, head_dim, softcap, s);
+  if (e != hipSuccess) return hip_fail(e, "varlen paged decode launch");
+  e = fa_launch_prefill(p, head_dim, true, true, pack, softcap, s);
   if (e != hipSuccess) return hip_fail(e, "varlen paged launch");
   return FA_OK;
 }
@@ -398,11 +408,11 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
   p.page = page_size;
   p.max_blocks = max_blocks_per_seq;
   p.num_splits = num_splits;
+  p.lse_bs = (int64_t)heads_q * seqlen_q;
+  p.lse_hs = seqlen_q;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (prefill) {
     const bool pack = resolve_pack(opts, heads_q, heads_kv);
-    p.lse_bs = (int64_t)heads_q * seqlen_q;
-    p.lse_hs = seqlen_q;
     p.hg_count = pack ? heads_kv : heads_q;
     p.gp = pack ? g : 1;
     const int64_t rows_seq = (int64_t)seqlen_q * p.gp;

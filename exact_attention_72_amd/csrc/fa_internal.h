@@ -38,6 +38,10 @@ struct FaParams {
   // split-KV decode: sequence of the i-th group of workgroups, longest first
   // (NULL: batch order)
   const int32_t* seq_order;
+  // varlen batch over a paged cache: sequences with at most this many packed
+  // rows (new tokens x g) run in the decode kernel and get no prefill tiles
+  // (0: every sequence runs in the prefill kernel)
+  int skip_rows;
   // score transform
   float scale_log2;  // softmax_scale * log2(e)
   float cap_in;      // softmax_scale / softcap

@@ -495,51 +495,80 @@ struct TileId {
   int b, hg, mb;
 };
 
-// Varlen: number of tiles at levels above m, summed over sequences:
-// C(m) = sum_b max(0, M_b - m - 1), M_b = ceil(L_b * gp / BLOCK_M).
-__device__ int64_t varlen_tiles_above(const int32_t* cu_q, int B, int gp, int m, int lane) {
+// Row blocks of a varlen sequence with L new tokens: ceil(L gp / BLOCK_M), or
+// none when its L g packed rows go to the decode kernel (p.skip_rows).
+__device__ __forceinline__ int varlen_mblocks(const FaParams& p, int L) {
+  if (p.skip_rows > 0 && L * p.g <= p.skip_rows) return 0;
+  return (L * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M;
+}
+// Keys before a varlen sequence's first query (its cache or key length minus
+// its new tokens), in row-block units: row block m of sequence b sees about
+// (P_b + m + 1) blocks' worth of keys under a causal mask.
+__device__ __forceinline__ int varlen_prefix_blocks(const FaParams& p, int b, int L) {
+  const int Lk = p.cache_seqlens ? p.cache_seqlens[b] : p.cu_k[b + 1] - p.cu_k[b];
+  const int pre = Lk - L;
+  return pre > 0 ? (int)(((int64_t)pre * p.gp) / FA_BLOCK_M) : 0;
+}
+
+// Varlen tiles are listed by level v = P_b + m, highest first (longest first).
+// Number of tiles at levels above v, summed over sequences:
+// C(v) = sum_b clamp(M_b + P_b - v - 1, 0, M_b).  With vmax set, also the
+// number of levels, max_b (P_b + M_b).
+__device__ int64_t varlen_tiles_above(const FaParams& p, int v, int lane, int* vmax = nullptr) {
+  const int32_t* cu_q = p.cu_q;
+  const int B = p.B;
   int64_t acc = 0;
+  int top = 0;
   for (int b0 = 0; b0 < B; b0 += 64) {
     int b = b0 + lane;
     int c = 0;
     if (b < B) {
       int L = cu_q[b + 1] - cu_q[b];
-      int M = (L * gp + FA_BLOCK_M - 1) / FA_BLOCK_M;
-      c = M - m - 1;
+      int M = varlen_mblocks(p, L);
+      int P = M > 0 ? varlen_prefix_blocks(p, b, L) : 0;
+      c = M + P - v - 1;
       if (c < 0) c = 0;
+      if (c > M) c = M;
+      if (M > 0) top = max(top, P + M);
     }
     acc += wave_sum(c);
+  }
+  if (vmax) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) top = max(top, __shfl_xor(top, off));
+    *vmax = top;
   }
   return acc;
 }
 
-// Varlen tile t (levels m = max..0, each level listing (sequence, head group)).
-// Returns false when t is past the last tile.
+// Varlen tile t.  Returns false when t is past the last tile.
 __device__ bool varlen_tile(const FaParams& p, int64_t t, int lane, TileId* out) {
   const int H = p.hg_count;
-  // total = H * C(-1)
-  int64_t total = (int64_t)H * varlen_tiles_above(p.cu_q, p.B, p.gp, -1, lane);
+  int vmax = 0;
+  int64_t total = (int64_t)H * varlen_tiles_above(p, -1, lane, &vmax);
   if (t >= total) return false;
-  int lo = 0, hi = p.m_blocks - 1;
-  while (lo < hi) {  // smallest m with H * C(m) <= t
+  int lo = 0, hi = vmax - 1;
+  while (lo < hi) {  // smallest v with H * C(v) <= t
     int mid = (lo + hi) >> 1;
-    if ((int64_t)H * varlen_tiles_above(p.cu_q, p.B, p.gp, mid, lane) <= t)
+    if ((int64_t)H * varlen_tiles_above(p, mid, lane) <= t)
       hi = mid;
     else
       lo = mid + 1;
   }
-  const int m = lo;
-  int64_t j = t - (int64_t)H * varlen_tiles_above(p.cu_q, p.B, p.gp, m, lane);
+  const int v = lo;
+  int64_t j = t - (int64_t)H * varlen_tiles_above(p, v, lane);
   int idx = (int)(j / H);
   out->hg = (int)(j % H);
-  out->mb = m;
   out->b = -1;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     int b = b0 + lane;
     bool f = false;
+    int m = 0;
     if (b < p.B) {
       int L = p.cu_q[b + 1] - p.cu_q[b];
-      f = (L * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M > m;
+      int M = varlen_mblocks(p, L);
+      m = M > 0 ? v - varlen_prefix_blocks(p, b, L) : -1;
+      f = m >= 0 && m < M;
     }
     uint64_t mask = __ballot(f);
     int cnt = __popcll(mask);
@@ -547,7 +576,9 @@ __device__ bool varlen_tile(const FaParams& p, int64_t t, int lane, TileId* out)
       uint64_t below = (lane == 0) ? 0ull : (mask & (~0ull >> (64 - lane)));
       bool mine = f && __popcll(below) == idx;
       uint64_t sel = __ballot(mine);
-      out->b = b0 + (__ffsll((long long)sel) - 1);
+      const int src = __ffsll((long long)sel) - 1;
+      out->b = b0 + src;
+      out->mb = __shfl(m, src);
       break;
     }
     idx -= cnt;
@@ -1028,7 +1059,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
   const int split = unit % S;
 
   const int Lk = p.cache_seqlens[b];
-  const int Lq = p.Nq;
+  int Lq = p.Nq;
+  int64_t q_start = 0;
+  if (p.cu_q) {
+    // a varlen batch: this sequence's new tokens; sequences with more packed
+    // rows than a workgroup holds run in the prefill kernel instead
+    q_start = p.cu_q[b];
+    Lq = p.cu_q[b + 1] - (int)q_start;
+    if (Lq <= 0 || Lq * p.g > FA_PAGED_MAX_ROWS) return;
+  }
   const int rows = Lq * p.g;
   const int npages = (Lk + p.page - 1) / p.page;
   const int chunk = (npages + S - 1) / S;
@@ -1056,7 +1095,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
   const bool row_ok = col < rows;
   const int tok = row_ok ? col / p.g : 0;
   const int head = kvh * p.g + (row_ok ? col % p.g : 0);
-  const uint16_t* qb = p.q + (int64_t)b * p.q_bs + (int64_t)tok * p.q_ss + (int64_t)head * p.q_hs;
+  const uint16_t* qb = p.q + (int64_t)b * p.q_bs + (q_start + tok) * p.q_ss + (int64_t)head * p.q_hs;
   bf16x8 qreg[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
@@ -1189,7 +1228,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
     const int chead = kvh * p.g + cc % p.g;
     const int64_t r = ((int64_t)b * p.Hq + chead) * Lq + ctok;  // LSE row order
     if (S == 1) {
-      uint16_t* ob = p.o + (int64_t)b * p.o_bs + (int64_t)ctok * p.o_ss + (int64_t)chead * p.o_hs + d0;
+      uint16_t* ob = p.o + (int64_t)b * p.o_bs + (q_start + ctok) * p.o_ss + (int64_t)chead * p.o_hs + d0;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         f32x8 x;
@@ -1197,7 +1236,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
         for (int e2 = 0; e2 < 8; ++e2) x[e2] = acc[8 * h + e2];
         *reinterpret_cast<bf16x8*>(ob + 8 * h) = __builtin_convertvector(x, bf16x8);
       }
-      if (d0 == 0 && p.lse) p.lse[r] = lse;
+      if (d0 == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)chead * p.lse_hs + q_start + ctok] = lse;
     } else {
       const int64_t rows_all = (int64_t)p.B * p.Hq * Lq;
       float* op = p.o_part + ((int64_t)split * rows_all + r) * D + d0;

@@ -339,6 +339,8 @@ def _run_varlen_paged(t, kc, vc, **kw):
     ([1, 1, 37, 300, 1, 129, 0], [1000, 17, 400, 300, 5000, 2000, 50], 8, 2, 128, 16, 0),
     ([64, 1, 500], [64, 4000, 600], 4, 4, 64, 256, -1),
     ([50, 3], [10, 3], 2, 1, 128, 32, -1),                  # more queries than keys
+    # 8 x 4 = 32 packed rows run in the decode kernel, 9 x 4 = 36 in the prefill kernel
+    ([8, 9, 1, 2, 0], [300, 280, 70, 1, 40], 16, 4, 64, 16, -1),
 ])
 def test_varlen_paged_mixed_batch(qlens, lens, Hq, Hkv, d, page, pack):
     t = _varlen_paged_case(91 + len(qlens) + d, qlens, lens, Hq, Hkv, d, page)
