@@ -159,7 +159,9 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
  *   lse      [heads_q, total_q] float32 (written; may be NULL)
  *   cu_seqlens_q device int32 [batch + 1]; block_table device int32 [batch, max_blocks_per_seq];
  *   cache_seqlens device int32 [batch]; max_seqlen_q: an upper bound of the query lengths.
- * One workgroup tile covers 128 packed rows of one sequence (no split-KV).  Errors:
+ * A sequence with at most 32 packed rows (new tokens x heads_q / heads_kv) runs as
+ * a decode step, one workgroup per (sequence, KV head); the others in workgroup
+ * tiles of 128 packed rows (no split-KV); two launches, both on the stream.  Errors:
  * FA_ERR_UNSUPPORTED for a page_size that is not a multiple of 16.  Caller contract,
  * not checked on the device: cu_seqlens_q non-decreasing from 0 with
  * cu_seqlens_q[batch] == total_q, query lengths <= max_seqlen_q, live block-table
