@@ -1045,10 +1045,19 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
   // the repeated rows (accumulator slots 8..15) are dropped below
   LaneOffsets<D> off;
   off.init(lane, lds_addr(smem), lds_addr(smem), 16);
-  const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
+  // Each wave loads the 16 rows it computes on (rows 16 wave .. 16 wave + 15 of a
+  // stage; instruction i fills G::kRowsPerKiB of them), so a wave waits only for
+  // its own loads and the stages need no workgroup barrier.  The layout and the
+  // swizzles are the same as with shared stage loads.
+  constexpr int kWaveRows = NK / 4;
+  const int dma_row = kWaveRows * wave + lane / G::kChunksPerRow;  // + i * G::kRowsPerKiB
   const int dma_pc = lane % G::kChunksPerRow;
-  const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
-  const int v_src = (dma_pc ^ v_swz<D>(dma_row)) * 8;
+  int k_src[G::kInstPerWave], v_src[G::kInstPerWave];
+#pragma unroll
+  for (int i = 0; i < G::kInstPerWave; ++i) {
+    k_src[i] = (dma_pc ^ k_swz<D>(dma_row + i * G::kRowsPerKiB)) * 8;
+    v_src[i] = (dma_pc ^ v_swz<D>(dma_row + i * G::kRowsPerKiB)) * 8;
+  }
 
   const int S = p.num_splits;
   const int unit = blockIdx.x;
@@ -1121,29 +1130,29 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
                                 ? scalar_load_i32(bt + __builtin_amdgcn_readfirstlane(last / p.page)) : 0;
   const int slot_last = last % p.page;
   auto issue = [&](int n0, int buf) {
-    char* dst = smem + buf * kStage + wave * 1024;
+    char* dst = smem + buf * kStage + wave * (kWaveRows * 2 * D);
     if (page_aligned) {
       // the whole stage is in one page: one scalar table read
       const int64_t phys = scalar_load_i32(bt + __builtin_amdgcn_readfirstlane(n0 / p.page));
       const int slot0 = n0 % p.page;
 #pragma unroll
       for (int i = 0; i < G::kInstPerWave; ++i) {
-        const int r = dma_row + i * G::kRowStep;
+        const int r = dma_row + i * G::kRowsPerKiB;
         const bool live = n0 + r < kend;
         const int slot = live ? slot0 + r : slot_last;
         const int64_t ph = live ? phys : phys_last;
-        dma16(kpool + ph * p.k_bs + (int64_t)slot * p.k_ss + k_src, dst + i * 4096);
-        dma16(vpool + ph * p.v_bs + (int64_t)slot * p.v_ss + v_src, dst + G::kTensorBytes + i * 4096);
+        dma16(kpool + ph * p.k_bs + (int64_t)slot * p.k_ss + k_src[i], dst + i * 1024);
+        dma16(vpool + ph * p.v_bs + (int64_t)slot * p.v_ss + v_src[i], dst + G::kTensorBytes + i * 1024);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < G::kInstPerWave; ++i) {
-        int key = n0 + dma_row + i * G::kRowStep;
+        int key = n0 + dma_row + i * G::kRowsPerKiB;
         key = key < kend ? key : kend - 1;
         const int64_t phys = bt[key / p.page];
         const int slot = key % p.page;
-        dma16(kpool + phys * p.k_bs + (int64_t)slot * p.k_ss + k_src, dst + i * 4096);
-        dma16(vpool + phys * p.v_bs + (int64_t)slot * p.v_ss + v_src, dst + G::kTensorBytes + i * 4096);
+        dma16(kpool + phys * p.k_bs + (int64_t)slot * p.k_ss + k_src[i], dst + i * 1024);
+        dma16(vpool + phys * p.v_bs + (int64_t)slot * p.v_ss + v_src[i], dst + G::kTensorBytes + i * 1024);
       }
     }
   };
@@ -1158,10 +1167,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
   for (int i = 0; i < nst; ++i) {
     const int buf = i % NS;
     const int n0 = st_first + i * NK;
-    // stage i landed (the stages after it may still be in flight); everyone is
-    // done with stage i - 1, whose buffer stage i + NS - 1 reuses
+    // this wave's rows of stage i landed (its later stages may still be in
+    // flight); its reads of stage i - 1, whose rows stage i + NS - 1 reuses,
+    // completed before their products
     wait_vmcnt_blocks<kDmaPerStage>(min(NS - 2, nst - 1 - i));
-    stage_barrier();
     if (i + NS - 1 < nst) issue(n0 + (NS - 1) * NK, (i + NS - 1) % NS);
     // this wave's 16 keys: rows 16 wave .. 16 wave + 15 of the stage buffer
     const uint32_t delta = buf * kStage + wave * 16 * (2 * D);
