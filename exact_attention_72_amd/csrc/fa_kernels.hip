@@ -867,6 +867,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       u32x2 lo0[D / 32], hi0[D / 32], lo1[D / 32], hi1[D / 32];
       read_v<D, kV>(0u, off, lo0, hi0);
       lgkm_wait<2 * (D / 32)>(ka);  // only the V reads just issued may be outstanding
+      // a raised issue priority from the S^T products to the end of the P V
+      // phase: measured 1.7-2.5 % faster on the 4x16x4096 causal workload and
+      // neutral on the 32k window + softcap one
+      __builtin_amdgcn_s_setprio(1);
       f32x16 s_next = qk_mma<D>(ka, qreg);
       read_v<D, kV + 16 * (2 * D)>(0u, off, lo1, hi1);
       // Softcapped scores of an unmasked block whose rows all have a reference
@@ -913,6 +917,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
 #pragma unroll
         for (int e = 0; e < kPer; ++e) expo(8 + db * kPer + e);
       }
+      __builtin_amdgcn_s_setprio(0);
       float xm = fmaxf(fmaxf(xs[0], xs[1]), xs[2]);
 #pragma unroll
       for (int a = 3; a < 15; a += 2) xm = fmaxf(fmaxf(xm, xs[a]), xs[a + 1]);
