@@ -318,10 +318,11 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   int64_t bound = (int64_t)p.m_blocks * batch;
   int64_t bound2 = ((int64_t)total_q * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M + batch;
   p.total_tiles = (bound < bound2 ? bound : bound2) * p.hg_count;
-  // a persistent grid-stride loop: measured faster than one workgroup per tile
-  // on a mixed batch of long chunks and one-token requests (416 against 358
-  // TFLOP/s), unlike the plain varlen batch
-  p.persistent = 1;
+  // one workgroup per tile index, longest tiles first (by the keys each sees):
+  // with the decode-like sequences in the decode kernel this measured 562
+  // against 547 TFLOP/s for a persistent grid-stride loop on a batch of 64
+  // one-token requests and 4 chunks of 2048 tokens
+  p.persistent = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // sequences of at most FA_PAGED_MAX_ROWS packed rows (decode steps, short
   // chunks) run in the decode kernel, one workgroup per (sequence, KV head) with
