@@ -67,6 +67,19 @@ def test_paged_longest_first_order_with_ties(num_splits):
     check_close(out, lse, o_ref, l_ref, f"paged longest-first S={num_splits}")
 
 
+def test_paged_batch_beyond_the_ordered_limit():
+    """More than 4096 sequences: the split workgroups keep the batch order (no order is
+    stored in the workspace) and every sequence still gets its own result."""
+    g = torch.Generator().manual_seed(91)
+    lens = [int(x) for x in torch.randint(1, 41, (4100,), generator=g)]
+    t = W.paged(92, len(lens), 2, 1, 64, 16, 0, 0, cache_seqlens=lens)
+    kc, vc = poison_unused(t)
+    out, lse = run(t, kc, vc, 2, causal=True)
+    o_ref, l_ref = oracle.fwd_paged(bits(t["q"]), bits(t["k_cache"]), bits(t["v_cache"]),
+                                    t["block_table"].numpy(), t["cache_seqlens"].numpy(), causal=True)
+    check_close(out, lse, o_ref, l_ref, "paged 4100 sequences S=2")
+
+
 def test_paged_window_softcap():
     t = W.paged(77, 3, 8, 2, 128, 16, 0, 0, cache_seqlens=[50, 400, 999], Nq=2, mult=2.0)
     kw = dict(causal=True, window=(100, 0), softcap=30.0)
@@ -341,6 +354,7 @@ def _run_varlen_paged(t, kc, vc, **kw):
     ([50, 3], [10, 3], 2, 1, 128, 32, -1),                  # more queries than keys
     # 8 x 4 = 32 packed rows run in the decode kernel, 9 x 4 = 36 in the prefill kernel
     ([8, 9, 1, 2, 0], [300, 280, 70, 1, 40], 16, 4, 64, 16, -1),
+    ([1, 8, 2, 1], [100, 300, 5, 1000], 8, 2, 128, 16, -1),  # every sequence in the decode kernel
 ])
 def test_varlen_paged_mixed_batch(qlens, lens, Hq, Hkv, d, page, pack):
     t = _varlen_paged_case(91 + len(qlens) + d, qlens, lens, Hq, Hkv, d, page)
