@@ -120,9 +120,10 @@ __device__ __forceinline__ int v_swz(int r) {  // rotates 64-byte segments over 
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-// One wave's share of an LDS-DMA stage load: IPW instructions per tensor, each
-// moving 1 KiB (RPK rows).  Instruction p of wave w fills rows
-// (4 p + w) * RPK .. + RPK - 1 of the stage.
+// Geometry of a stage load split over four waves: kInstPerWave 1 KiB pieces
+// (kRowsPerKiB rows each) per wave and tensor.  In the prefill kernel piece p of
+// wave w fills rows (4 p + w) * kRowsPerKiB .. + kRowsPerKiB - 1 of the stage;
+// the decode kernel gives each wave its own consecutive rows instead.
 template <int D, int NK>
 struct DmaGeom {
   static constexpr int kRowBytes = 2 * D;
@@ -1021,11 +1022,11 @@ __global__ __launch_bounds__(kThreads) void fa_seq_order_kernel(const int32_t* l
 // 64-key stage is split 16 keys per wave, and the waves' partial states are
 // merged through LDS at the end ("Attention kernels...", section 6.3: partial
 // states combine with the same rescale as the tiles).  Decode is bound by the
-// K/V stream: two stages per workgroup (64 KiB) let two workgroups share a CU,
-// so that one computes while the other's loads are in flight (measured faster
-// than one workgroup with a deeper ring of the same total size).  When the page size is a
-// multiple of the stage, a stage lies in one page and its physical page is one
-// scalar block-table read; otherwise every row looks its page up.
+// K/V stream: each wave loads its own rows with plain loads one stage ahead and
+// two workgroups share a CU (the 64 KiB of LDS the merge needs sets that).  When
+// the page size is a multiple of the stage, a stage lies in one page and its
+// physical page is one scalar block-table read; otherwise every row looks its
+// page up.
 template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
   constexpr int NK = FA_PAGED_STAGE;
