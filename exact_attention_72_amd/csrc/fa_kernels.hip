@@ -511,28 +511,51 @@ __device__ __forceinline__ int varlen_prefix_blocks(const FaParams& p, int b, in
   return pre > 0 ? (int)(((int64_t)pre * p.gp) / FA_BLOCK_M) : 0;
 }
 
+// Row blocks M_b and prefix blocks P_b of sequence b (both 0 past the batch).
+__device__ __forceinline__ void varlen_seq(const FaParams& p, int b, int& M, int& P) {
+  M = 0;
+  P = 0;
+  if (b < p.B) {
+    const int L = p.cu_q[b + 1] - p.cu_q[b];
+    M = varlen_mblocks(p, L);
+    P = M > 0 ? varlen_prefix_blocks(p, b, L) : 0;
+  }
+}
+
+// (M, P) of the first kVarlenRegChunks * 64 sequences, read once per tile: lane
+// l holds sequences l, l + 64, ...  The binary search over levels then runs on
+// registers, and reads memory only for the sequences of larger batches (each
+// read is a round trip to the cache, about a microsecond per search step).
+constexpr int kVarlenRegChunks = 4;
+struct VarlenSeqs {
+  int M[kVarlenRegChunks], P[kVarlenRegChunks];
+};
+__device__ __forceinline__ void varlen_seqs_load(const FaParams& p, int lane, VarlenSeqs& vs) {
+#pragma unroll
+  for (int j = 0; j < kVarlenRegChunks; ++j) varlen_seq(p, 64 * j + lane, vs.M[j], vs.P[j]);
+}
+
 // Varlen tiles are listed by level v = P_b + m, highest first (longest first).
 // Number of tiles at levels above v, summed over sequences:
 // C(v) = sum_b clamp(M_b + P_b - v - 1, 0, M_b).  With vmax set, also the
 // number of levels, max_b (P_b + M_b).
-__device__ int64_t varlen_tiles_above(const FaParams& p, int v, int lane, int* vmax = nullptr) {
-  const int32_t* cu_q = p.cu_q;
-  const int B = p.B;
+__device__ int64_t varlen_tiles_above(const FaParams& p, const VarlenSeqs& vs, int v, int lane,
+                                      int* vmax = nullptr) {
   int64_t acc = 0;
   int top = 0;
-  for (int b0 = 0; b0 < B; b0 += 64) {
-    int b = b0 + lane;
-    int c = 0;
-    if (b < B) {
-      int L = cu_q[b + 1] - cu_q[b];
-      int M = varlen_mblocks(p, L);
-      int P = M > 0 ? varlen_prefix_blocks(p, b, L) : 0;
-      c = M + P - v - 1;
-      if (c < 0) c = 0;
-      if (c > M) c = M;
-      if (M > 0) top = max(top, P + M);
-    }
+  auto add = [&](int M, int P) {
+    int c = M + P - v - 1;
+    c = c < 0 ? 0 : (c > M ? M : c);
+    if (M > 0) top = max(top, P + M);
     acc += wave_sum(c);
+  };
+#pragma unroll
+  for (int j = 0; j < kVarlenRegChunks; ++j)
+    if (64 * j < p.B) add(vs.M[j], vs.P[j]);
+  for (int b0 = 64 * kVarlenRegChunks; b0 < p.B; b0 += 64) {
+    int M, P;
+    varlen_seq(p, b0 + lane, M, P);
+    add(M, P);
   }
   if (vmax) {
 #pragma unroll
@@ -545,44 +568,49 @@ __device__ int64_t varlen_tiles_above(const FaParams& p, int v, int lane, int* v
 // Varlen tile t.  Returns false when t is past the last tile.
 __device__ bool varlen_tile(const FaParams& p, int64_t t, int lane, TileId* out) {
   const int H = p.hg_count;
+  VarlenSeqs vs;
+  varlen_seqs_load(p, lane, vs);
   int vmax = 0;
-  int64_t total = (int64_t)H * varlen_tiles_above(p, -1, lane, &vmax);
+  int64_t total = (int64_t)H * varlen_tiles_above(p, vs, -1, lane, &vmax);
   if (t >= total) return false;
   int lo = 0, hi = vmax - 1;
   while (lo < hi) {  // smallest v with H * C(v) <= t
     int mid = (lo + hi) >> 1;
-    if ((int64_t)H * varlen_tiles_above(p, mid, lane) <= t)
+    if ((int64_t)H * varlen_tiles_above(p, vs, mid, lane) <= t)
       hi = mid;
     else
       lo = mid + 1;
   }
   const int v = lo;
-  int64_t j = t - (int64_t)H * varlen_tiles_above(p, v, lane);
+  int64_t j = t - (int64_t)H * varlen_tiles_above(p, vs, v, lane);
   int idx = (int)(j / H);
   out->hg = (int)(j % H);
   out->b = -1;
-  for (int b0 = 0; b0 < p.B; b0 += 64) {
-    int b = b0 + lane;
-    bool f = false;
-    int m = 0;
-    if (b < p.B) {
-      int L = p.cu_q[b + 1] - p.cu_q[b];
-      int M = varlen_mblocks(p, L);
-      m = M > 0 ? v - varlen_prefix_blocks(p, b, L) : -1;
-      f = m >= 0 && m < M;
-    }
-    uint64_t mask = __ballot(f);
-    int cnt = __popcll(mask);
+  // the idx-th sequence (in batch order) with a tile at level v
+  auto pick = [&](int b0, int M, int P) -> bool {
+    const int m = M > 0 ? v - P : -1;
+    const bool f = m >= 0 && m < M;
+    const uint64_t mask = __ballot(f);
+    const int cnt = __popcll(mask);
     if (idx < cnt) {
-      uint64_t below = (lane == 0) ? 0ull : (mask & (~0ull >> (64 - lane)));
-      bool mine = f && __popcll(below) == idx;
-      uint64_t sel = __ballot(mine);
+      const uint64_t below = (lane == 0) ? 0ull : (mask & (~0ull >> (64 - lane)));
+      const bool mine = f && __popcll(below) == idx;
+      const uint64_t sel = __ballot(mine);
       const int src = __ffsll((long long)sel) - 1;
       out->b = b0 + src;
       out->mb = __shfl(m, src);
-      break;
+      return true;
     }
     idx -= cnt;
+    return false;
+  };
+#pragma unroll
+  for (int jj = 0; jj < kVarlenRegChunks; ++jj)
+    if (64 * jj < p.B && out->b < 0) pick(64 * jj, vs.M[jj], vs.P[jj]);
+  for (int b0 = 64 * kVarlenRegChunks; b0 < p.B && out->b < 0; b0 += 64) {
+    int M, P;
+    varlen_seq(p, b0 + lane, M, P);
+    pick(b0, M, P);
   }
   return out->b >= 0;
 }

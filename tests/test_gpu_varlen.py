@@ -27,6 +27,8 @@ def run(t, cu_q, cu_k, max_q, **kw):
     ([64, 200, 17], 4, 4, 64, True, -1, (50, 0), 10.0),
     ([1000], 32, 4, 128, True, 1, None, 0.0),
     ([3, 5, 2], 2, 1, 128, False, 1, None, 0.0),
+    # 300 sequences: the tile search reads the sequences past the first 256 from memory
+    ([(37 * i) % 90 + 1 for i in range(300)], 4, 2, 64, True, 1, None, 0.0),
 ])
 def test_varlen_small(lens, Hq, Hkv, d, causal, pack, window, softcap):
     t = W.varlen(17 + len(lens), len(lens), 0, 0, Hq, Hkv, d, lengths=lens,
