@@ -850,6 +850,34 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     // xs: exponentials of the current block relative to m_run, whose sums and
     // bf16 operands are formed at the start of the next step
     f32x16 xs = {};
+    // sc: the prepared scores of the block whose exponentials xs holds, kept for
+    // the check below.  Exponentials that outgrew the reference (some above 2^8)
+    // are caught where they are summed: a per-lane sum above 2^8 (or not finite)
+    // sends the wave to the reference decision on the block's maximum, which
+    // moves the reference, rescales what was accumulated and redoes the
+    // exponentials.  The per-lane sums of a block stay far below 2^8 when the
+    // reference is current, so the branch is rarely taken.
+    f32x16 sc = {};
+    auto check_sums = [&]() {
+      const float r0 = (xs[0] + xs[1]) + (xs[2] + xs[3]);
+      const float r1 = (xs[4] + xs[5]) + (xs[6] + xs[7]);
+      const float r2 = (xs[8] + xs[9]) + (xs[10] + xs[11]);
+      const float r3 = (xs[12] + xs[13]) + (xs[14] + xs[15]);
+      const float rs = (r0 + r1) + (r2 + r3);
+      if (__any(!(rs <= kRescaleMax))) {
+        float a2;
+        if (move_reference(block_max(sc), m_run, c, a2)) {
+          mfma_drain(o);
+          l_run *= a2;
+          l_bf *= a2;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) o[db] *= a2;
+          const float nmc = neg_ref(m_run, c);
+#pragma unroll
+          for (int a = 0; a < 16; ++a) xs[a] = exp2_fast(__builtin_fmaf(sc[a], c, nmc));
+        }
+      }
+    };
     auto exps = [&](const f32x16& sv, float nmc, int a0, int a1) {
 #pragma unroll
       for (int a = a0; a < a1; ++a) xs[a] = exp2_fast(__builtin_fmaf(sv[a], c, nmc));
@@ -868,6 +896,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       float alpha;
       move_reference(block_max(s0), m_run, c, alpha);  // nothing accumulated yet
       exps(s0, neg_ref(m_run, c), 0, 16);
+      sc = s0;
     }
 
     // Pipeline step for block i (stage B = i % NBUF) when block i + 1 exists.
@@ -890,6 +919,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       // the sums of block i run while the K reads are in flight: the empty asm
       // statements (ordered with the reads and waits) pin them there
       asm volatile("" : "+v"(xs));
+      check_sums();
       bf16x8 p0, p1;
       block_sums(xs, l_run, l_bf, p0, p1);
       asm volatile("" : "+v"(p0), "+v"(p1), "+v"(l_run), "+v"(l_bf));
@@ -918,14 +948,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       // Reference for the exponentials of block i + 1.  While some row of the
       // wave has seen no visible key its reference must be set from this block's
       // maximum first (rare: the first blocks of a tile).  Otherwise the
-      // exponentials use the current reference and are checked afterwards: a
-      // probability above 2^kRescaleLog2 means the maximum outgrew the reference,
-      // and the block is redone with the moved reference (the same decision as
-      // move_reference, taken off the path between the two products).
+      // exponentials use the current reference and are checked where they are
+      // summed, at the next step (check_sums), off the path between the two
+      // products.
       float alpha = 1.0f;
       bool moved = false;
       if (first) moved = move_reference(block_max(s_next), m_run, c, alpha);
-      float nmc = neg_ref(m_run, c);
+      const float nmc = neg_ref(m_run, c);
       // P V of block i, each product followed by the exponentials of block i + 1
       constexpr int kPer = 16 / (2 * (D / 32));  // exponentials per product
       auto expo = [&](int a) {
@@ -947,20 +976,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
         for (int e = 0; e < kPer; ++e) expo(8 + db * kPer + e);
       }
       __builtin_amdgcn_s_setprio(0);
-      float xm = fmaxf(fmaxf(xs[0], xs[1]), xs[2]);
-#pragma unroll
-      for (int a = 3; a < 15; a += 2) xm = fmaxf(fmaxf(xm, xs[a]), xs[a + 1]);
-      xm = fmaxf(xm, xs[15]);
-      if (__any(xm > kRescaleMax)) {
-        float a2;
-        if (move_reference(block_max(s_next), m_run, c, a2)) {
-          alpha *= a2;
-          moved = true;
-          nmc = neg_ref(m_run, c);
-#pragma unroll
-          for (int a = 0; a < 16; ++a) xs[a] = exp2_fast(__builtin_fmaf(s_next[a], c, nmc));
-        }
-      }
+      sc = s_next;  // the late softcap path transformed it in place
       if (moved) {
         mfma_drain(o);
         l_run *= alpha;
@@ -986,6 +1002,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       if (i + 1 <= nb - 1) step(std::integral_constant<int, 3 % NBUF>{}, i), ++i;
     // last block (i == nb - 1, stage i % NBUF): sums and P V only
     if (nb > 0) {
+      check_sums();
       bf16x8 p0, p1;
       block_sums(xs, l_run, l_bf, p0, p1);
       const uint32_t delta = (uint32_t)((i % NBUF) * T);
