@@ -457,12 +457,17 @@ __device__ __forceinline__ bool move_reference(float mx, float& m_run, float c, 
 // -m c for the exponentials (0 while the row has seen no visible key).
 __device__ __forceinline__ float neg_ref(float m_run, float c) { return (m_run == kNegInf) ? 0.0f : -m_run * c; }
 // Sums of the exponentials x into both row sums, and x as two bf16 operands.
-__device__ __forceinline__ void block_sums(const f32x16& x, float& l_run, float& l_bf, bf16x8& p0, bf16x8& p1) {
-  float r0 = (x[0] + x[1]) + (x[2] + x[3]);
-  float r1 = (x[4] + x[5]) + (x[6] + x[7]);
-  float r2 = (x[8] + x[9]) + (x[10] + x[11]);
-  float r3 = (x[12] + x[13]) + (x[14] + x[15]);
-  l_run += (r0 + r1) + (r2 + r3);
+__device__ __forceinline__ float lane_sum16(const f32x16& x) {
+  const float r0 = (x[0] + x[1]) + (x[2] + x[3]);
+  const float r1 = (x[4] + x[5]) + (x[6] + x[7]);
+  const float r2 = (x[8] + x[9]) + (x[10] + x[11]);
+  const float r3 = (x[12] + x[13]) + (x[14] + x[15]);
+  return (r0 + r1) + (r2 + r3);
+}
+// rs: lane_sum16(x), formed by the caller.
+__device__ __forceinline__ void block_sums(const f32x16& x, float rs, float& l_run, float& l_bf, bf16x8& p0,
+                                           bf16x8& p1) {
+  l_run += rs;
   f32x8 x0, x1;
 #pragma unroll
   for (int a = 0; a < 8; ++a) {
@@ -858,12 +863,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     // exponentials.  The per-lane sums of a block stay far below 2^8 when the
     // reference is current, so the branch is rarely taken.
     f32x16 sc = {};
-    auto check_sums = [&]() {
-      const float r0 = (xs[0] + xs[1]) + (xs[2] + xs[3]);
-      const float r1 = (xs[4] + xs[5]) + (xs[6] + xs[7]);
-      const float r2 = (xs[8] + xs[9]) + (xs[10] + xs[11]);
-      const float r3 = (xs[12] + xs[13]) + (xs[14] + xs[15]);
-      const float rs = (r0 + r1) + (r2 + r3);
+    auto check_sums = [&]() -> float {
+      float rs = lane_sum16(xs);
       if (__any(!(rs <= kRescaleMax))) {
         float a2;
         if (move_reference(block_max(sc), m_run, c, a2)) {
@@ -875,8 +876,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
           const float nmc = neg_ref(m_run, c);
 #pragma unroll
           for (int a = 0; a < 16; ++a) xs[a] = exp2_fast(__builtin_fmaf(sc[a], c, nmc));
+          rs = lane_sum16(xs);
         }
       }
+      return rs;
     };
     auto exps = [&](const f32x16& sv, float nmc, int a0, int a1) {
 #pragma unroll
@@ -919,9 +922,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       // the sums of block i run while the K reads are in flight: the empty asm
       // statements (ordered with the reads and waits) pin them there
       asm volatile("" : "+v"(xs));
-      check_sums();
+      const float rs = check_sums();
       bf16x8 p0, p1;
-      block_sums(xs, l_run, l_bf, p0, p1);
+      block_sums(xs, rs, l_run, l_bf, p0, p1);
       asm volatile("" : "+v"(p0), "+v"(p1), "+v"(l_run), "+v"(l_bf));
       u32x2 lo0[D / 32], hi0[D / 32], lo1[D / 32], hi1[D / 32];
       read_v<D, kV>(0u, off, lo0, hi0);
@@ -1002,9 +1005,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       if (i + 1 <= nb - 1) step(std::integral_constant<int, 3 % NBUF>{}, i), ++i;
     // last block (i == nb - 1, stage i % NBUF): sums and P V only
     if (nb > 0) {
-      check_sums();
+      const float rs = check_sums();
       bf16x8 p0, p1;
-      block_sums(xs, l_run, l_bf, p0, p1);
+      block_sums(xs, rs, l_run, l_bf, p0, p1);
       const uint32_t delta = (uint32_t)((i % NBUF) * T);
       pv_chunk<D, 0>(delta, p0, o, off);
       pv_chunk<D, 16 * (2 * D)>(delta, p1, o, off);
