@@ -357,6 +357,21 @@ struct LaneMask {
     return (key < kend) & (key >= kbeg) & (!causal | (key <= pos)) & ((wl < 0) | (key >= pos - wl)) &
            ((wr < 0) | (key <= pos + wr));
   }
+  // The same predicate for the keys base + off of a 32-key block, off in
+  // [0, 32): visible iff lo <= off <= hi.  lo is 0 unless kbeg or a left window
+  // cuts the block; the window ends are formed in 64 bits (pos + wr, pos - wl
+  // may leave the int range).
+  __device__ __forceinline__ int off_hi(int base) const {
+    int64_t h = (int64_t)kend - 1 - base;
+    if (causal) h = min(h, (int64_t)pos - base);
+    if (wr >= 0) h = min(h, (int64_t)pos + wr - base);
+    return (int)max(h, (int64_t)-1);
+  }
+  __device__ __forceinline__ int off_lo(int base) const {
+    int64_t l = (int64_t)kbeg - base;
+    if (wl >= 0) l = max(l, (int64_t)pos - wl - base);
+    return (int)min(max(l, (int64_t)0), (int64_t)32);
+  }
 };
 
 // Online softmax over one 32-key block held in s.  Scores are in units where
@@ -844,12 +859,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
           sv[a] = off <= hi ? bias(sv[a], off) : kNegInf;
         }
       } else {
-        // window bounds in 64 bits: pos + wr and pos - wl may leave the int range
-        int64_t hi64 = (int64_t)mask.kend - 1 - base;
-        if (mask.causal) hi64 = min(hi64, (int64_t)mask.pos - base);
-        if (mask.wr >= 0) hi64 = min(hi64, (int64_t)mask.pos + mask.wr - base);
-        const int hi = (int)max(hi64, (int64_t)-1);
-        const int lo = mask.wl < 0 ? 0 : (int)min(max((int64_t)mask.pos - mask.wl - base, (int64_t)0), (int64_t)BN);
+        const int hi = mask.off_hi(base), lo = mask.off_lo(base);
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
           const int off = 8 * (a >> 2) + (a & 3);
@@ -1678,10 +1688,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
     if (n < f_lo || n >= f_hi) {
       int base = n * BN + 4 * kg;
       asm volatile("" : "+v"(base));
+      // the row's visible keys in the block as an interval of offsets
+      const int hi = mask.off_hi(base), lo = mask.off_lo(base);
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
-        const int key = base + 8 * (a >> 2) + (a & 3);
-        s[a] = mask.visible(key) ? s[a] : kNegInf;
+        const int off = 8 * (a >> 2) + (a & 3);
+        s[a] = (off <= hi && off >= lo) ? s[a] : kNegInf;
       }
     }
     f32x8 x0, x1;
