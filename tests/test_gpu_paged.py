@@ -34,7 +34,7 @@ def run(t, kc, vc, num_splits, **kw):
     return out, lse
 
 
-@pytest.mark.parametrize("num_splits", [1, 2, 4, 16])
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 4, 6, 16])
 @pytest.mark.parametrize("page,lens,Hq,Hkv,d,Nq", [
     (16, [1, 15, 16, 17, 300, 1000], 32, 8, 128, 1),
     (256, [1, 255, 256, 257, 1500, 5000], 32, 8, 128, 1),
