@@ -65,11 +65,37 @@ def stored_traffic(kernel: str):
     return e.get("bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup):
-    """Warm up, then time `steps` back-to-back calls between two HIP events recorded on the
-    current stream (the stream the library launches on).  Returns the wall time of the timed
-    region (s) and the mean time per call from the events (ms)."""
+def settle(fn, min_s=1.0, max_s=6.0, window=20, tol=0.01):
+    """Launch fn back to back until the GPU clock has settled under this load: at least
+    min_s seconds have passed and two successive windows of `window` launches agree in mean
+    time within tol (at most max_s seconds).  The kernels' clock ramps up over the first
+    hundreds of milliseconds of sustained matrix work, so a few untimed launches alone leave
+    the timed ones on a cold clock.  Returns the seconds spent."""
     import torch
+    t0 = time.perf_counter()
+    prev = None
+    while True:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(window):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / window
+        el = time.perf_counter() - t0
+        if el >= max_s or (el >= min_s and prev is not None and abs(ms - prev) <= tol * prev):
+            return el
+        prev = ms
+
+
+def time_launches(fn, steps, warmup, settle_s=0.5):
+    """Settle the clock (settle(), at least settle_s seconds), run `warmup` untimed calls, then
+    time `steps` back-to-back calls between two HIP events recorded on the current stream
+    (the stream the library launches on).  Returns the wall time of the timed region (s), the
+    mean time per call from the events (ms) and the settle time (s)."""
+    import torch
+    st = settle(fn, min_s=settle_s) if settle_s > 0 else 0.0
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -82,7 +108,7 @@ def time_launches(fn, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, e0.elapsed_time(e1) / steps
+    return wall, e0.elapsed_time(e1) / steps, st
 
 
 def prefill_flops(B, H, N, d, causal):
@@ -94,8 +120,13 @@ def cpu_baseline(W, t, c, target_s=15.0):
     FLOP convention (each sampled row counted with its visible keys)."""
     import numpy as np
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
-    threads = max(1, min(threads, os.cpu_count() or 1, 16))
+    host_cores = os.cpu_count() or 1
+    try:
+        share = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        share = host_cores
+    # every core this process may run on, up to the per-GPU CPU share the box grants (16)
+    threads = max(1, min(share, int(os.environ.get("OMP_NUM_THREADS", "16") or 16), 16))
     B, N, H, d = c["B"], c["N"], c["Hq"], c["d"]
     qb, kb, vb = (W.to_bits(t[n]) for n in "qkv")
     rng = np.random.default_rng(0)
@@ -116,7 +147,8 @@ def cpu_baseline(W, t, c, target_s=15.0):
             break
         n = int(max(threads * 8, min(4000000, n * target_s / max(dt, 1e-3))))
         dt, fl, n = run(n)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "host_cores": host_cores,
+            "affinity_cores": share, "kind": "oracle",
             "sample": f"{n} random query rows of the batch-4 x 16-head N=4096 d=128 causal "
                       f"workload, fp64, {dt:.1f} s"}
 
@@ -135,7 +167,7 @@ def bench_varlen(api, W, steps, warmup):
     lse = torch.empty((c["Hq"], t["q"].shape[0]), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd_varlen(t["q"], t["k"], t["v"], cu, cu, t["max_seqlen"], causal=True,  # noqa
                                    pack_gqa=1, out=out, lse=lse)
-    wall, ms = time_launches(fn, steps, warmup)
+    wall, ms, _ = time_launches(fn, steps, warmup)
     tf = flops / (ms * 1e-3) / 1e12
     return {"metric": "varlen prefill TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
             "kernel_ms": round(ms, 4), "flops": flops,
@@ -161,7 +193,7 @@ def bench_local(api, W, steps, warmup):
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd(t["q"], t["k"], t["v"], causal=True, window=c["window"],  # noqa
                             softcap=c["softcap"], out=out, lse=lse)
-    wall, ms = time_launches(fn, steps, warmup)
+    wall, ms, _ = time_launches(fn, steps, warmup)
     tf = flops / (ms * 1e-3) / 1e12
     return {"metric": "local softcap prefill TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
             "kernel_ms": round(ms, 4), "flops": flops,
@@ -195,7 +227,7 @@ def bench_paged_prefill(api, W, steps, warmup):
     lse = torch.empty((B, c["Hq"], Nq), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd_kvcache_paged(t["q"], t["k_cache"], t["v_cache"], bt, sl, num_splits=0,  # noqa
                                           causal=True, out=out, lse=lse)
-    wall, ms = time_launches(fn, steps, warmup)
+    wall, ms, _ = time_launches(fn, steps, warmup)
     tf = flops / (ms * 1e-3) / 1e12
     # append: the chunk's K/V (new tensors of the chunk's shape) at positions prefix .. prefix + Nq - 1
     g = W.generator(c["seed"] + 7, "cuda")
@@ -203,7 +235,7 @@ def bench_paged_prefill(api, W, steps, warmup):
     vn = W.randn_bf16(g, (B, Nq, c["Hkv"], c["d"]), 1.0, "cuda")
     start = torch.full((B,), P, dtype=torch.int32, device="cuda")
     fa = lambda: api.fa_kvcache_append(kn, vn, t["k_cache"], t["v_cache"], bt, start)  # noqa
-    _, ms_a = time_launches(fa, steps, min(warmup, 50))
+    _, ms_a, _ = time_launches(fa, steps, min(warmup, 50))
     moved = 2.0 * 2 * kn.numel() * 2          # K and V, read once and written once, bf16
     gbs = moved / (ms_a * 1e-3) / 1e9
     # the same append with the keys rotated on the way (full head_dim, 10000^(-2i/d) frequencies)
@@ -213,7 +245,7 @@ def bench_paged_prefill(api, W, steps, warmup):
     cos, sin = torch.cos(ang).float(), torch.sin(ang).float()
     fr = lambda: api.fa_kvcache_append(kn, vn, t["k_cache"], t["v_cache"], bt, start,  # noqa
                                        rotary_cos=cos, rotary_sin=sin)
-    _, ms_r = time_launches(fr, steps, min(warmup, 50))
+    _, ms_r, _ = time_launches(fr, steps, min(warmup, 50))
     return {"metric": "chunked prefill over a paged cache TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
             "kernel_ms": round(ms, 4), "flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
@@ -249,7 +281,7 @@ def bench_unified(api, W, steps, warmup):
     lse = torch.empty((c["Hq"], t["q"].shape[0]), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd_varlen_paged(t["q"], t["k_cache"], t["v_cache"], cu, c["chunk"], bt, sl,  # noqa
                                          causal=True, out=out, lse=lse)
-    wall, ms = time_launches(fn, steps, warmup)
+    wall, ms, _ = time_launches(fn, steps, warmup)
     tf = flops / (ms * 1e-3) / 1e12
     return {"metric": "unified prefill+decode batch TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
             "kernel_ms": round(ms, 4), "flops": flops,
@@ -275,7 +307,7 @@ def bench_bwd(api, W, steps, warmup):
     ws = torch.empty(api.lib().fa_bwd_workspace_size(B, N, H), dtype=torch.uint8, device="cuda")
     fn = lambda: api.fa_bwd(t["q"], t["k"], t["v"], out, lse, do, causal=True, dq=dq, dk=dk, dv=dv,  # noqa
                             workspace=ws)
-    wall, ms = time_launches(fn, steps, warmup)
+    wall, ms, _ = time_launches(fn, steps, warmup)
     flops = 2.5 * prefill_flops(B, H, N, d, True)
     tf = flops / (ms * 1e-3) / 1e12
     return {"metric": "attn bwd TFLOP/s (bf16 N=4k d=128 causal)", "unit": "TFLOP/s", "value": round(tf, 2),
@@ -298,7 +330,7 @@ def bench_alibi(api, W, steps, warmup):
     out = torch.empty_like(t["q"])
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd(t["q"], t["k"], t["v"], causal=True, alibi_slopes=slopes, out=out, lse=lse)  # noqa
-    _, ms = time_launches(fn, steps, warmup)
+    _, ms, _ = time_launches(fn, steps, warmup)
     tf = prefill_flops(B, H, N, d, True) / (ms * 1e-3) / 1e12
     return {"metric": "attn fwd with ALiBi TFLOP/s (bf16 N=4k d=128 causal)", "unit": "TFLOP/s",
             "value": round(tf, 2), "ms": round(ms, 4),
@@ -323,7 +355,7 @@ def bench_fp8(api, W, steps, warmup):
     out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd_fp8(q8, qs, k8, ks, vt, vs, causal=True, out=out, lse=lse)  # noqa: E731
-    _, ms = time_launches(fn, steps, warmup)
+    _, ms, _ = time_launches(fn, steps, warmup)
     flops = prefill_flops(B, H, N, d, True)
     tf = flops / (ms * 1e-3) / 1e12
 
@@ -331,7 +363,7 @@ def bench_fp8(api, W, steps, warmup):
         api.fa_fp8_quantize(t["q"], api.FA_FP8_Q_BLOCK, codes=q8, scales=qs)
         api.fa_fp8_quantize(t["k"], api.FA_FP8_K_BLOCK, codes=k8, scales=ks)
         api.fa_fp8_quantize_v(t["v"], vt=vt, scales=vs)
-    _, qms = time_launches(quant, max(3, steps // 10), 2)
+    _, qms, _ = time_launches(quant, max(3, steps // 10), 2, settle_s=0)
     return {"metric": "attn fwd fp8 TFLOP/s (e4m3 N=4k d=128 causal)", "unit": "TFLOP/s", "value": round(tf, 2),
             "ms": round(ms, 4),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
@@ -360,7 +392,7 @@ def bench_decode(api, W, steps, warmup):
         fn = lambda: api.fa_fwd_kvcache_paged(t["q"], t["k_cache"], t["v_cache"], bt, sl,  # noqa
                                               num_splits=S, causal=True, out=out, lse=lse,
                                               workspace=ws)
-        wall, ms = time_launches(fn, steps, warmup)
+        wall, ms, _ = time_launches(fn, steps, warmup)
         res[S] = {"ms": ms, "kv_GBps": kv_bytes / (ms * 1e-3) / 1e9}
     best = max((1, 4, 16), key=lambda s: res[s]["kv_GBps"])
     return {"metric": "paged decode KV GB/s", "unit": "GB/s",
@@ -381,7 +413,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds (at least) of untimed launches before the warm-up, until the clock "
+                         "has settled (two successive 20-launch windows within 1 %%)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
@@ -419,7 +454,7 @@ def main():
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     fn = lambda: api.fa_fwd(t["q"], t["k"], t["v"], causal=True, out=out, lse=lse)  # noqa
     torch.cuda.synchronize()
-    wall, kern_ms = time_launches(fn, args.steps, args.warmup)
+    wall, kern_ms, settle_s = time_launches(fn, args.steps, args.warmup, settle_s=args.settle)
     flops = prefill_flops(B, H, N, d, True)
     ms_step = wall / args.steps * 1e3
     value = flops / (ms_step * 1e-3) / 1e12
@@ -427,7 +462,8 @@ def main():
     line = {
         "metric": "attn fwd TFLOPS (bf16 N=4k d=128 causal) + paged decode KV GB/s, 1 GPU",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "settle_s": round(settle_s, 3), "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "batch": B, "heads": H, "seq_len": N, "head_dim": d,
                    "causal": True, "flop_convention": "4*B*H*N^2*d/2"},
