@@ -21,7 +21,8 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
-EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_varlen_paged", "fa_kvcache_num_splits",
+EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
+           "fa_fwd_varlen_paged", "fa_kvcache_num_splits",
            "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary", "fa_bwd", "fa_bwd_workspace_size",
            "fa_fp8_quantize", "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8",
            "fa_combine", "fa_tile_class", "fa_last_error", "fa_version")
@@ -61,6 +62,8 @@ def lib():
     L.fa_fwd_varlen.argtypes = [OPT, P, P, P, P, P, P, P, I, I, I, I, I, I, I, S3, S3, S3, S3, P]
     L.fa_fwd_kvcache_paged.argtypes = [OPT, P, P, P, P, P, P, P, I, I, I, I, I, I64, I, I, I, P, SZ,
                                        S3, S3, S3, S3, P]
+    L.fa_fwd_kvcache_paged_noalloc.argtypes = [OPT, P, P, P, P, P, P, P, I, I, I, I, I, I64, I, I, I,
+                                               S3, S3, S3, S3, P]
     L.fa_kvcache_workspace_size.argtypes = [I, I, I, I, I]
     L.fa_kvcache_workspace_size.restype = SZ
     L.fa_kvcache_num_splits.argtypes = [I, I, I, I, I, I]
@@ -80,7 +83,8 @@ def lib():
     L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = I
-    for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_combine", "fa_tile_class",
+    for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
+                 "fa_combine", "fa_tile_class",
                  "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary", "fa_bwd", "fa_fp8_quantize",
                  "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8"):
         getattr(L, name).restype = I
@@ -216,6 +220,33 @@ def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num
                                       _strides(q, (0, 1, 2)), _strides(k_cache, (0, 1, 2)),
                                       _strides(v_cache, (0, 1, 2)), _strides(out, (0, 1, 2)),
                                       _stream(stream)))
+    return out, lse
+
+
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def fa_fwd_kvcache_paged_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, *, num_splits=1,
+                                 softmax_scale=None, causal=True, window=None, softcap=0.0, pack_gqa=-1,
+                                 out, lse=None, stream=None):
+    """fa_fwd_kvcache_paged without a workspace: the split partials go to the library's static
+    device scratch (FA_NOALLOC_SCRATCH_BYTES per device).  The caller passes out (and lse, or
+    None); nothing is allocated here or in the library."""
+    _bf16_cuda(q, k_cache, v_cache, out)
+    B, Nq, Hq, d = q.shape
+    num_pages, page, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    for c in (block_table, cache_seqlens):
+        if c.dtype != torch.int32 or not c.is_cuda:
+            raise TypeError("block_table and cache_seqlens must be int32 device tensors")
+    if block_table.stride(-1) != 1 or block_table.stride(0) != block_table.shape[1]:
+        raise ValueError("block_table must be a contiguous [batch, max_blocks] tensor")
+    o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
+    _check(lib().fa_fwd_kvcache_paged_noalloc(ctypes.byref(o), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                              _ptr(block_table), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
+                                              B, Nq, Hq, Hkv, d, num_pages, page, block_table.shape[1],
+                                              int(num_splits), _strides(q, (0, 1, 2)),
+                                              _strides(k_cache, (0, 1, 2)), _strides(v_cache, (0, 1, 2)),
+                                              _strides(out, (0, 1, 2)), _stream(stream)))
     return out, lse
 
 

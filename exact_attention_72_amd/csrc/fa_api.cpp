@@ -14,6 +14,8 @@
 
 #define FA_VERSION_NUMBER 100  // 0.1.0
 
+static_assert(FA_SCRATCH_BYTES == FA_NOALLOC_SCRATCH_BYTES, "scratch size of the header and the kernels differ");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -353,13 +355,17 @@ size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_
   return bytes;
 }
 
-int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_table, const int32_t* cache_seqlens, void* out, float* lse,
-                         int batch, int seqlen_q, int heads_q, int heads_kv, int head_dim, int64_t num_pages,
-                         int page_size, int max_blocks_per_seq, int num_splits, void* workspace,
-                         size_t workspace_bytes, const int64_t q_strides[3], const int64_t k_strides[3],
-                         const int64_t v_strides[3], const int64_t o_strides[3], void* stream) {
-  g_err[0] = 0;
+namespace {
+
+// fa_fwd_kvcache_paged and its no-allocation twin.  With use_scratch the partials
+// and the sequence order go to the library's static device scratch (after the
+// size check, nothing else touches the device first) instead of the workspace.
+int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_table, const int32_t* cache_seqlens, void* out, float* lse, int batch,
+                  int seqlen_q, int heads_q, int heads_kv, int head_dim, int64_t num_pages, int page_size,
+                  int max_blocks_per_seq, int num_splits, void* workspace, size_t workspace_bytes,
+                  bool use_scratch, const int64_t q_strides[3], const int64_t k_strides[3],
+                  const int64_t v_strides[3], const int64_t o_strides[3], void* stream) {
   int rc;
   if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
   if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out)
@@ -386,14 +392,28 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
     return fail(FA_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16 (needed for seqlen_q * heads_q / "
                 "heads_kv > %d)", page_size, FA_PAGED_MAX_ROWS);
   const size_t need = fa_kvcache_workspace_size(batch, seqlen_q, heads_q, head_dim, num_splits);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : (size_t)0);
-  if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (use_scratch) {
+    if (need > FA_SCRATCH_BYTES)
+      return fail(FA_ERR_INVALID_ARG,
+                  "fa_fwd_kvcache_paged_noalloc: the split partials need %zu bytes, more than the %zu-byte "
+                  "static scratch; use fewer splits or fa_fwd_kvcache_paged with a workspace",
+                  need, FA_SCRATCH_BYTES);
+  } else {
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  }
   FaParams p;
   memset(&p, 0, sizeof p);
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
-  if ((rc = no_alibi(p, "fa_fwd_kvcache_paged"))) return rc;
+  if ((rc = no_alibi(p, use_scratch ? "fa_fwd_kvcache_paged_noalloc" : "fa_fwd_kvcache_paged"))) return rc;
+  if (use_scratch && need > 0) {
+    hipError_t e = fa_scratch_region(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+    workspace_bytes = FA_SCRATCH_BYTES;
+  }
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k_cache);
   p.v = static_cast<const uint16_t*>(v_cache);
@@ -454,6 +474,32 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
   return FA_OK;
+}
+
+}  // namespace
+
+int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* cache_seqlens, void* out, float* lse,
+                         int batch, int seqlen_q, int heads_q, int heads_kv, int head_dim, int64_t num_pages,
+                         int page_size, int max_blocks_per_seq, int num_splits, void* workspace,
+                         size_t workspace_bytes, const int64_t q_strides[3], const int64_t k_strides[3],
+                         const int64_t v_strides[3], const int64_t o_strides[3], void* stream) {
+  g_err[0] = 0;
+  return kvcache_paged(opts, q, k_cache, v_cache, block_table, cache_seqlens, out, lse, batch, seqlen_q, heads_q,
+                       heads_kv, head_dim, num_pages, page_size, max_blocks_per_seq, num_splits, workspace,
+                       workspace_bytes, false, q_strides, k_strides, v_strides, o_strides, stream);
+}
+
+int fa_fwd_kvcache_paged_noalloc(const fa_attn_opts* opts, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+                                 void* out, float* lse, int batch, int seqlen_q, int heads_q, int heads_kv,
+                                 int head_dim, int64_t num_pages, int page_size, int max_blocks_per_seq,
+                                 int num_splits, const int64_t q_strides[3], const int64_t k_strides[3],
+                                 const int64_t v_strides[3], const int64_t o_strides[3], void* stream) {
+  g_err[0] = 0;
+  return kvcache_paged(opts, q, k_cache, v_cache, block_table, cache_seqlens, out, lse, batch, seqlen_q, heads_q,
+                       heads_kv, head_dim, num_pages, page_size, max_blocks_per_seq, num_splits, nullptr, 0, true,
+                       q_strides, k_strides, v_strides, o_strides, stream);
 }
 
 int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

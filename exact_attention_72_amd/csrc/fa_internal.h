@@ -164,6 +164,13 @@ struct FaCombineParams {
 // Compute units of the current device (fa_kernels.hip; 256 if the query fails).
 int fa_device_cus();
 
+// Device scratch of the no-allocation paged entry point (fa_kernels.hip): a
+// static device array of FA_SCRATCH_BYTES on every device the library runs on.
+// fa_scratch_region returns the calling thread's current device's address of it
+// (looked up once per device with hipGetSymbolAddress).
+constexpr size_t FA_SCRATCH_BYTES = (size_t)32 << 20;
+hipError_t fa_scratch_region(void** ptr);
+
 // Launchers (fa_kernels.hip).  They return hipSuccess or the launch error.
 hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, bool pack, bool softcap,
                              hipStream_t s);

@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa_blockinfo.h"
@@ -2024,6 +2025,37 @@ hipError_t launch_paged_t(const FaParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// ------------------------------------------------------------------ no-allocation scratch
+// The split-KV partials and the sequence order of fa_fwd_kvcache_paged_noalloc
+// live here instead of in a caller workspace, for callers that cannot allocate
+// device memory.  Each device holds its own copy until the process ends; every
+// call on a device shares that copy, so calls that overlap on one device race.
+// Nothing in it needs to start at zero: each call writes every partial and the
+// whole order before reading them.
+static __device__ __align__(256) char scratch[FA_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t fa_scratch_region(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // the array's name is a host-side stand-in; kernels get this device address
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 int fa_device_cus() { return device_cus(); }
 

@@ -146,6 +146,28 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
                          const int64_t v_strides[3], const int64_t o_strides[3],
                          void* stream);
 
+/* fa_fwd_kvcache_paged for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, results and errors, without the workspace.
+ * The split-KV partials and the sequence order go to a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends; no call allocates or frees anything.  A call whose
+ * partials need more than that (fa_kvcache_workspace_size(...) for the resolved
+ * split count above FA_NOALLOC_SCRATCH_BYTES) returns FA_ERR_INVALID_ARG with
+ * nothing enqueued.  Every call on one device shares that device's array, so
+ * calls that overlap on one device (concurrent streams or host threads) race;
+ * calls on one stream are ordered and safe.  The first call with num_splits > 1
+ * on a device looks the array's address up once (hipGetSymbolAddress). */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int fa_fwd_kvcache_paged_noalloc(const fa_attn_opts* opts, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table,
+                                 const int32_t* cache_seqlens, void* out, float* lse, int batch,
+                                 int seqlen_q, int heads_q, int heads_kv, int head_dim,
+                                 int64_t num_pages, int page_size, int max_blocks_per_seq,
+                                 int num_splits, const int64_t q_strides[3],
+                                 const int64_t k_strides[3], const int64_t v_strides[3],
+                                 const int64_t o_strides[3], void* stream);
+
 /* Unified prefill + decode batch over a paged KV cache ("Attention kernels ...",
  * section 5.1: a batch mixes requests that prefill a chunk of hundreds or thousands
  * of queries with requests that decode one token, all against a cached prefix plus
