@@ -80,6 +80,14 @@ int check_dims(int d, int hq, int hkv) {
 }
 
 // Every row start must be 16-byte aligned: base pointer and all strides * 2 bytes.
+// The prefill kernel addresses a 32-key block of K or V through a buffer
+// resource with 32-bit byte offsets: 32 token strides must stay below 2^31 bytes.
+int check_token_stride(const char* name, int64_t ss) {
+  if (ss >= ((int64_t)1 << 25))
+    return fail(FA_ERR_UNSUPPORTED, "%s token stride %lld is 2^25 elements or more", name, (long long)ss);
+  return FA_OK;
+}
+
 int check_strides(const char* name, const void* base, const int64_t* s, int n) {
   if (!s) return fail(FA_ERR_INVALID_ARG, "%s strides are NULL", name);
   if (!aligned16(base)) return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
@@ -157,7 +165,8 @@ int fa_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   if (batch <= 0 || seqlen_q <= 0 || seqlen_k <= 0)
     return fail(FA_ERR_INVALID_ARG, "batch, seqlen_q and seqlen_k must be positive");
   if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k", k, k_strides, 3)) ||
-      (rc = check_strides("v", v, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)))
+      (rc = check_strides("v", v, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)) ||
+      (rc = check_token_stride("k", k_strides[1])) || (rc = check_token_stride("v", v_strides[1])))
     return rc;
   FaParams p;
   memset(&p, 0, sizeof p);
@@ -202,7 +211,8 @@ int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
   if (batch <= 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0)
     return fail(FA_ERR_INVALID_ARG, "batch must be positive and sizes non-negative");
   if ((rc = check_strides("q", q, q_strides, 2)) || (rc = check_strides("k", k, k_strides, 2)) ||
-      (rc = check_strides("v", v, v_strides, 2)) || (rc = check_strides("out", out, o_strides, 2)))
+      (rc = check_strides("v", v, v_strides, 2)) || (rc = check_strides("out", out, o_strides, 2)) ||
+      (rc = check_token_stride("k", k_strides[0])) || (rc = check_token_stride("v", v_strides[0])))
     return rc;
   FaParams p;
   memset(&p, 0, sizeof p);

@@ -156,6 +156,19 @@ __device__ __forceinline__ void dma16(const uint16_t* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (FA_LDS void*)lds_dst, 16, 0, 0);
 }
 
+// The same LDS-DMA load through a buffer resource (buffer_load_dwordx4 ... lds):
+// the base address lives in scalar registers and each lane adds a 32-bit byte
+// offset, so a block's source address costs scalar instructions only instead
+// of 64-bit vector address arithmetic per load.  Raw buffer (stride 0), 32-bit
+// data format (the gfx9 resource word 3).
+constexpr int kBufRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, kBufRsrcWord3);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds_dst, 16, (int)voff, (int)soff, 0, 0);
+}
+
 // ------------------------------------------------------------------ per-wave math
 // 32-bit LDS address of a pointer into shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
@@ -790,9 +803,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     // real (finite) data, which the mask then drops.
     const uint16_t* kbase = p.k + (int64_t)tile.b * p.k_bs + k_start * p.k_ss + (int64_t)kvh * p.k_hs;
     const uint16_t* vbase = p.v + (int64_t)tile.b * p.v_bs + k_start * p.v_ss + (int64_t)kvh * p.v_hs;
-    const uint16_t* klane = kbase + (int64_t)dma_row * p.k_ss + k_src;
-    const uint16_t* vlane = vbase + (int64_t)dma_row * p.v_ss + v_src;
-    const int64_t k_step = (int64_t)G::kRowStep * p.k_ss, v_step = (int64_t)G::kRowStep * p.v_ss;
+    // byte offsets of this lane's row and chunk within a block, and between the
+    // instructions of a wave (the host keeps 32 * stride * 2 below 2^31)
+    const uint32_t k_voff = (uint32_t)(dma_row * p.k_ss + k_src) * 2u;
+    const uint32_t v_voff = (uint32_t)(dma_row * p.v_ss + v_src) * 2u;
+    const uint32_t k_step = (uint32_t)(G::kRowStep * p.k_ss) * 2u, v_step = (uint32_t)(G::kRowStep * p.v_ss) * 2u;
     // block i of this tile (key block n_lo + i) goes to buffer i % NBUF
     auto issue = [&](int i) {
       char* dst = smem + (i % NBUF) * T + wave * 1024;
@@ -812,12 +827,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
                 dst + NBUF * T + j * 4096);
         }
       } else if (n0 + BN <= Lk) {
-        const uint16_t* kq = klane + (int64_t)n0 * p.k_ss;
-        const uint16_t* vq = vlane + (int64_t)n0 * p.v_ss;
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kbase + (int64_t)n0 * p.k_ss);
+        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vbase + (int64_t)n0 * p.v_ss);
 #pragma unroll
         for (int j = 0; j < G::kInstPerWave; ++j) {
-          dma16(kq + j * k_step, dst + j * 4096);
-          dma16(vq + j * v_step, dst + NBUF * T + j * 4096);
+          dma16_buf(rk, k_voff, j * k_step, dst + j * 4096);
+          dma16_buf(rv, v_voff, j * v_step, dst + NBUF * T + j * 4096);
         }
       } else {
 #pragma unroll
@@ -897,6 +912,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     // exponentials.  The per-lane sums of a block stay far below 2^8 when the
     // reference is current, so the branch is rarely taken.
     f32x16 sc = {};
+    // -m c of the current reference (0 while a row has seen no visible key),
+    // recomputed only where the reference moves; all_ref: every row of the wave
+    // has a reference (once true it stays true: a reference only moves up)
+    float nmc_run = 0.0f;
+    bool all_ref = false;
     auto check_sums = [&]() -> float {
       float rs = lane_sum16(xs);
       if (__any(!(rs <= kRescaleMax))) {
@@ -907,9 +927,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
           l_bf *= a2;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) o[db] *= a2;
-          const float nmc = neg_ref(m_run, c);
+          nmc_run = neg_ref(m_run, c);
 #pragma unroll
-          for (int a = 0; a < 16; ++a) xs[a] = exp2_fast(__builtin_fmaf(sc[a], c, nmc));
+          for (int a = 0; a < 16; ++a) xs[a] = exp2_fast(__builtin_fmaf(sc[a], c, nmc_run));
           rs = lane_sum16(xs);
         }
       }
@@ -932,7 +952,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
         apply_bias(s0, 0);
       float alpha;
       move_reference(block_max(s0), m_run, c, alpha);  // nothing accumulated yet
-      exps(s0, neg_ref(m_run, c), 0, 16);
+      nmc_run = neg_ref(m_run, c);
+      all_ref = !__any(m_run == kNegInf);
+      exps(s0, nmc_run, 0, 16);
       sc = s0;
     }
 
@@ -973,7 +995,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       // are transformed inside the product loop below, beside the exponentials;
       // otherwise (mask, or a row's first visible block) before it.
       const bool masked = is_masked(i + 1);
-      const bool first = __any(m_run == kNegInf);
+      const bool first = !all_ref;
       const bool late = SOFTCAP && !masked && !first;
       if (!late) {
         transform(s_next);
@@ -990,8 +1012,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       // products.
       float alpha = 1.0f;
       bool moved = false;
-      if (first) moved = move_reference(block_max(s_next), m_run, c, alpha);
-      const float nmc = neg_ref(m_run, c);
+      if (first) {
+        // the fence keeps the block maximum inside this rarely taken branch
+        f32x16 sv = s_next;
+        asm volatile("" : "+v"(sv));
+        moved = move_reference(block_max(sv), m_run, c, alpha);
+        nmc_run = neg_ref(m_run, c);
+        all_ref = !__any(m_run == kNegInf);
+      }
+      const float nmc = nmc_run;
       // P V of block i, each product followed by the exponentials of block i + 1
       constexpr int kPer = 16 / (2 * (D / 32));  // exponentials per product
       auto expo = [&](int a) {
