@@ -25,7 +25,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_pa
            "fa_fwd_varlen_paged", "fa_kvcache_num_splits",
            "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary", "fa_bwd", "fa_bwd_workspace_size",
            "fa_fp8_quantize", "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8",
-           "fa_combine", "fa_tile_class", "fa_last_error", "fa_version")
+           "fa_combine", "fa_merge_attn_states", "fa_tile_class", "fa_last_error", "fa_version")
 
 FA_FP8_Q_BLOCK = 128
 FA_FP8_K_BLOCK = 64
@@ -68,7 +68,8 @@ def lib():
     L.fa_kvcache_workspace_size.restype = SZ
     L.fa_kvcache_num_splits.argtypes = [I, I, I, I, I, I]
     L.fa_kvcache_num_splits.restype = I
-    L.fa_combine.argtypes = [P, P, I, I64, I, P, I64, P, P]
+    L.fa_combine.argtypes = [P, P, I, I64, I, I64, P, I64, P, P]
+    L.fa_merge_attn_states.argtypes = [P, P, P, P, I, P, P, I, I, I, I, S3, S3, S3, P]
     L.fa_kvcache_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I64, I, I, S3, S3, S3, S3, P, P, I, I, P]
     L.fa_rotary.argtypes = [P, I, I, I, I, S3, P, P, P, I, I, P]
     L.fa_bwd.argtypes = [OPT, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, S3, S3, S3, S3, S3, P, SZ, P]
@@ -84,7 +85,7 @@ def lib():
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = I
     for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
-                 "fa_combine", "fa_tile_class",
+                 "fa_combine", "fa_merge_attn_states", "fa_tile_class",
                  "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary", "fa_bwd", "fa_fp8_quantize",
                  "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8"):
         getattr(L, name).restype = I
@@ -357,19 +358,54 @@ def fa_bwd(q, k, v, out, lse, dout, *, softmax_scale=None, causal=False, window=
 
 
 def fa_combine(o_part, lse_part, *, out=None, lse=None, stream=None):
-    """Merge partial states.  o_part fp32 [S, rows, d], lse_part fp32 [S, rows]
-    -> (out bf16 [rows, d], lse fp32 [rows])."""
+    """Merge partial states.  o_part fp32 [S, rows, d] (or a view whose splits are
+    part_stride_rows rows apart: split stride = o_part.stride(0) / d), lse_part fp32
+    [S, rows] with the same split stride in rows -> (out bf16 [rows, d], lse fp32 [rows])."""
     S, rows, d = o_part.shape
     if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
         raise TypeError("partials are float32")
-    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
-        raise ValueError("partials must be contiguous")
+    if o_part.stride(2) != 1 or o_part.stride(1) != d or lse_part.stride(1) != 1:
+        raise ValueError("partial rows must be contiguous")
+    stride_rows = o_part.stride(0) // d if S > 1 else rows
+    if (S > 1 and (o_part.stride(0) % d or lse_part.stride(0) != stride_rows)):
+        raise ValueError("o_part and lse_part must share one split stride in rows")
     if out is None:
         out = torch.empty((rows, d), dtype=torch.bfloat16, device=o_part.device)
     if lse is None:
         lse = torch.empty((rows,), dtype=torch.float32, device=o_part.device)
-    _check(lib().fa_combine(_ptr(o_part), _ptr(lse_part), S, rows, d, _ptr(out), out.stride(0),
+    _check(lib().fa_combine(_ptr(o_part), _ptr(lse_part), S, rows, d, stride_rows, _ptr(out), out.stride(0),
                             _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+FA_DTYPE_FP32 = 0
+FA_DTYPE_BF16 = 1
+
+
+def fa_merge_attn_states(prefix_out, prefix_lse, suffix_out, suffix_lse, *, out=None, lse=None, stream=None):
+    """Merge two attention states from separate buffers.  prefix_out / suffix_out
+    [B, N, H, d] (bf16 or fp32, same strides), prefix_lse / suffix_lse fp32 [B, H, N]
+    (same strides) -> (out bf16 [B, N, H, d], lse fp32 [B, H, N])."""
+    if prefix_out.shape != suffix_out.shape or prefix_out.stride() != suffix_out.stride():
+        raise ValueError("prefix_out and suffix_out must have the same shape and strides")
+    if prefix_lse.stride() != suffix_lse.stride() or prefix_lse.dtype != torch.float32 or \
+            suffix_lse.dtype != torch.float32:
+        raise ValueError("the LSEs must be float32 with the same strides")
+    if prefix_out.dtype != suffix_out.dtype or prefix_out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("states are float32 or bfloat16")
+    dt = FA_DTYPE_FP32 if prefix_out.dtype == torch.float32 else FA_DTYPE_BF16
+    B, N, H, d = prefix_out.shape
+    if prefix_out.stride(3) != 1:
+        raise ValueError("head_dim must be contiguous")
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=prefix_out.device)
+    if lse is None:
+        lse = torch.empty_strided(prefix_lse.shape, prefix_lse.stride(), dtype=torch.float32,
+                                  device=prefix_out.device)
+    _check(lib().fa_merge_attn_states(_ptr(prefix_out), _ptr(prefix_lse), _ptr(suffix_out), _ptr(suffix_lse), dt,
+                                      _ptr(out), _ptr(lse), B, N, H, d, _strides(prefix_out, (0, 1, 2)),
+                                      _strides(out, (0, 1, 2)), _strides(prefix_lse, (0, 1, 2)),
+                                      _stream(stream)))
     return out, lse
 
 

@@ -263,8 +263,12 @@ int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, in
   // With more than one split the workgroups take the sequences longest first
   // (batch <= FA_SEQ_ORDER_MAX), so a few workgroups per compute unit level
   // out sequences of very unequal length: about 4 per compute unit and at least
-  // 2 splits.  On 64 sequences of 1k-32k keys, 32/8 heads: 2 splits 5.89 TB/s,
-  // 4 splits 5.74, 8 splits 5.65, 16 splits 5.57, 1 split 4.70.  Without the
+  // 2 splits.  On 64 sequences of 1k-32k keys, 32/8 heads (256-token pages):
+  // 1 split 5.01 TB/s, 2 splits 6.64, 3 6.60, 4 6.37, 5 6.59, 6 6.71, 8 6.15.
+  // The curve is not monotone because a sequence's pages are cut into
+  // ceil(pages / S)-page splits and some counts leave a short last split for
+  // many lengths; this host-side choice does not see the lengths (they are on
+  // the device) and takes 2, within 1 % of the best count there.  Without the
   // order (larger batches) about 32 per compute unit, so that the lengths level
   // out by number.  Each split keeps at least one page; at most 64 splits.
   const int64_t units = (int64_t)batch * heads_kv;
@@ -291,7 +295,7 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   if (batch <= 0 || max_seqlen_q < 0 || total_q < 0 || num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0)
     return fail(FA_ERR_INVALID_ARG,
                 "batch, num_pages, page_size and max_blocks_per_seq must be positive and sizes non-negative");
-  if (page_size % 16 != 0) return fail(FA_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16", page_size);
+  if (page_size % 16 != 0) return fail(FA_ERR_INVALID_ARG, "page_size %d is not a multiple of 16", page_size);
   if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
     return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
   if ((rc = check_strides("q", q, q_strides, 2)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
@@ -383,6 +387,7 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
   if (batch <= 0 || seqlen_q <= 0 || num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0)
     return fail(FA_ERR_INVALID_ARG, "batch, seqlen_q, num_pages, page_size and max_blocks_per_seq must be positive");
   if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
+  if (page_size % 16 != 0) return fail(FA_ERR_INVALID_ARG, "page_size %d is not a multiple of 16", page_size);
   if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
     return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
   if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
@@ -398,9 +403,6 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
     return fail(FA_ERR_UNSUPPORTED,
                 "num_splits > 1 needs seqlen_q * heads_q / heads_kv <= %d (got %lld); use 1 or 0",
                 FA_PAGED_MAX_ROWS, (long long)seqlen_q * g);
-  if (prefill && page_size % 16 != 0)
-    return fail(FA_ERR_UNSUPPORTED, "page_size %d is not a multiple of 16 (needed for seqlen_q * heads_q / "
-                "heads_kv > %d)", page_size, FA_PAGED_MAX_ROWS);
   const size_t need = fa_kvcache_workspace_size(batch, seqlen_q, heads_q, head_dim, num_splits);
   if (use_scratch) {
     if (need > FA_SCRATCH_BYTES)
@@ -470,16 +472,24 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
   hipError_t e = fa_launch_paged(p, head_dim, softcap, s);
   if (e != hipSuccess) return hip_fail(e, "paged launch");
   if (num_splits > 1) {
+    // partial row r = (b * Hq + h) * Nq + t of every split, split after split
     FaCombineParams c;
-    c.o_part = p.o_part;
-    c.lse_part = p.lse_part;
+    memset(&c, 0, sizeof c);
+    c.o_in[0] = p.o_part;
+    c.lse_in[0] = p.lse_part;
+    c.o_split = rows * head_dim;
+    c.lse_split = rows;
     c.num_splits = num_splits;
     c.rows = rows;
+    c.B = batch;
     c.Hq = heads_q;
     c.Nq = seqlen_q;
+    c.i_bs = (int64_t)heads_q * seqlen_q * head_dim; c.i_ss = head_dim; c.i_hs = (int64_t)seqlen_q * head_dim;
+    c.il_bs = (int64_t)heads_q * seqlen_q; c.il_hs = seqlen_q; c.il_ss = 1;
     c.o = p.o;
     c.o_bs = p.o_bs; c.o_ss = p.o_ss; c.o_hs = p.o_hs;
     c.lse = lse;
+    c.l_bs = p.lse_bs; c.l_hs = p.lse_hs; c.l_ss = 1;
     e = fa_launch_combine(c, head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
@@ -527,6 +537,7 @@ int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void*
   if (batch <= 0 || seqlen_new < 0 || heads_kv <= 0 || num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0)
     return fail(FA_ERR_INVALID_ARG,
                 "batch, heads_kv, num_pages, page_size and max_blocks_per_seq must be positive, seqlen_new >= 0");
+  if (page_size % 16 != 0) return fail(FA_ERR_INVALID_ARG, "page_size %d is not a multiple of 16", page_size);
   if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
     return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
   if ((rc = check_strides("k_new", k_new, kn_strides, 3)) || (rc = check_strides("v_new", v_new, vn_strides, 3)) ||
@@ -644,28 +655,85 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
 }
 
 int fa_combine(const float* o_part, const float* lse_part, int num_splits, int64_t rows, int head_dim,
-               void* out, int64_t out_row_stride, float* lse_out, void* stream) {
+               int64_t part_stride_rows, void* out, int64_t out_row_stride, float* lse_out, void* stream) {
   g_err[0] = 0;
   if (head_dim != 64 && head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
   if (!o_part || !lse_part || !out) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (num_splits < 1 || rows < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 1 and rows >= 0");
+  if (part_stride_rows < rows)
+    return fail(FA_ERR_INVALID_ARG, "part_stride_rows %lld is below rows %lld (splits would overlap)",
+                (long long)part_stride_rows, (long long)rows);
   if (out_row_stride < head_dim || (out_row_stride * 2) % 4 != 0 || (reinterpret_cast<uintptr_t>(out) & 3u))
     return fail(FA_ERR_INVALID_ARG, "out rows must be 4-byte aligned and not overlap");
-  if (reinterpret_cast<uintptr_t>(o_part) & 15u) return fail(FA_ERR_INVALID_ARG, "o_part is not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(o_part) & 3u) || (reinterpret_cast<uintptr_t>(lse_part) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "o_part and lse_part must be 4-byte aligned");
   FaCombineParams c;
-  c.o_part = o_part;
-  c.lse_part = lse_part;
+  memset(&c, 0, sizeof c);
+  c.o_in[0] = o_part;
+  c.lse_in[0] = lse_part;
+  c.o_split = part_stride_rows * head_dim;
+  c.lse_split = part_stride_rows;
   c.num_splits = num_splits;
   c.rows = rows;
+  // flat rows: row r is "batch" r of one head and one token
   c.Hq = 1;
   c.Nq = 1;
+  c.i_bs = head_dim;
+  c.il_bs = 1;
   c.o = static_cast<uint16_t*>(out);
   c.o_bs = out_row_stride;
-  c.o_ss = 0;
-  c.o_hs = 0;
   c.lse = lse_out;
+  c.l_bs = 1;
   hipError_t e = fa_launch_combine(c, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return FA_OK;
+}
+
+int fa_merge_attn_states(const void* prefix_out, const float* prefix_lse, const void* suffix_out,
+                         const float* suffix_lse, int in_dtype, void* out, float* lse_out, int batch,
+                         int seqlen, int heads, int head_dim, const int64_t in_strides[3],
+                         const int64_t out_strides[3], const int64_t lse_strides[3], void* stream) {
+  g_err[0] = 0;
+  if (head_dim != 64 && head_dim != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!prefix_out || !prefix_lse || !suffix_out || !suffix_lse || !out || !in_strides || !out_strides || !lse_strides)
+    return fail(FA_ERR_INVALID_ARG, "a pointer is NULL");
+  if (in_dtype != FA_DTYPE_FP32 && in_dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "in_dtype %d is neither FA_DTYPE_FP32 nor FA_DTYPE_BF16", in_dtype);
+  if (batch < 0 || seqlen < 0 || heads < 0) return fail(FA_ERR_INVALID_ARG, "sizes must be >= 0");
+  for (int i = 0; i < 3; ++i)
+    if (in_strides[i] < 0 || out_strides[i] < 0 || lse_strides[i] < 0)
+      return fail(FA_ERR_INVALID_ARG, "strides must be >= 0");
+  const uintptr_t ia = (in_dtype == FA_DTYPE_FP32) ? 3u : 1u;
+  if ((reinterpret_cast<uintptr_t>(prefix_out) & ia) || (reinterpret_cast<uintptr_t>(suffix_out) & ia) ||
+      (reinterpret_cast<uintptr_t>(prefix_lse) & 3u) || (reinterpret_cast<uintptr_t>(suffix_lse) & 3u) ||
+      (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u)))
+    return fail(FA_ERR_INVALID_ARG, "a tensor is not aligned to its element size");
+  // the output rows are written as 4-byte pairs of bf16
+  if ((reinterpret_cast<uintptr_t>(out) & 3u) || (out_strides[0] | out_strides[1] | out_strides[2]) & 1)
+    return fail(FA_ERR_INVALID_ARG, "out must be 4-byte aligned with even strides");
+  const int64_t rows = (int64_t)batch * seqlen * heads;
+  if (rows == 0) return FA_OK;
+  FaCombineParams c;
+  memset(&c, 0, sizeof c);
+  c.o_in[0] = prefix_out;
+  c.o_in[1] = suffix_out;
+  c.lse_in[0] = prefix_lse;
+  c.lse_in[1] = suffix_lse;
+  c.pair = 1;
+  c.in_bf16 = in_dtype == FA_DTYPE_BF16;
+  c.num_splits = 2;
+  c.rows = rows;
+  c.B = batch;
+  c.Hq = heads;
+  c.Nq = seqlen;
+  c.i_bs = in_strides[0]; c.i_ss = in_strides[1]; c.i_hs = in_strides[2];
+  c.il_bs = lse_strides[0]; c.il_hs = lse_strides[1]; c.il_ss = lse_strides[2];
+  c.o = static_cast<uint16_t*>(out);
+  c.o_bs = out_strides[0]; c.o_ss = out_strides[1]; c.o_hs = out_strides[2];
+  c.lse = lse_out;
+  c.l_bs = lse_strides[0]; c.l_hs = lse_strides[1]; c.l_ss = lse_strides[2];
+  hipError_t e = fa_launch_combine(c, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
   return FA_OK;
 }
 

@@ -150,15 +150,28 @@ struct FaAppendParams {
   FaRotary rot;                  // applied to the keys (rot.cos == NULL: none)
 };
 
+// Merge of partial attention states.  Row r = (b * Hq + h) * Nq + t of
+// rows = B * Hq * Nq.  Partial s of row (b, t, h):
+//   O   at (in_bf16 ? bf16 : fp32) element  o_in[s'] + s'' * o_split + b * i_bs + t * i_ss + h * i_hs
+//   LSE at                                lse_in[s'] + s'' * lse_split + b * il_bs + h * il_hs + t * il_ss
+// where (s', s'') = (s, 0) when pair (two separately placed states, num_splits
+// == 2) and (0, s) otherwise.  Output O bf16 at o + b * o_bs + t * o_ss + h * o_hs,
+// LSE at lse + b * l_bs + h * l_hs + t * l_ss (may be null).
 struct FaCombineParams {
-  const float* o_part;
-  const float* lse_part;
+  const void* o_in[2];
+  const float* lse_in[2];
+  int64_t o_split, lse_split;
+  int pair;
+  int in_bf16;
   int num_splits;
-  int64_t rows;  // rows per split; row r = (b * Hq + h) * Nq + t
-  int Hq, Nq;
+  int64_t rows;
+  int B, Hq, Nq;
+  int64_t i_bs, i_ss, i_hs;
+  int64_t il_bs, il_hs, il_ss;
   uint16_t* o;
   int64_t o_bs, o_ss, o_hs;
-  float* lse;  // [rows] in row order, may be null
+  float* lse;
+  int64_t l_bs, l_hs, l_ss;
 };
 
 // Compute units of the current device (fa_kernels.hip; 256 if the query fails).

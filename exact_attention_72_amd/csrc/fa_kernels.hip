@@ -1394,35 +1394,52 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
 
 // ------------------------------------------------------------------ combine kernel
 // One wave per row: M = max_s LSE_s, w_s = exp(LSE_s - M), LSE = M + ln sum w_s,
-// O = sum_s w_s O_s / sum w_s ("Attention kernels...", section 6.3).
-template <int D>
+// O = sum_s w_s O_s / sum w_s ("Attention kernels...", section 6.3).  A partial
+// whose LSE is -inf has weight 0 (its O is not read).  The partials are fp32
+// (split-KV) or bf16 (two attention outputs, e.g. over a cached prefix and the
+// new suffix).
+template <int D, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void fa_combine_kernel(FaCombineParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (r >= p.rows) return;
+  const int t = (int)(r % p.Nq);
+  const int h = (int)((r / p.Nq) % p.Hq);
+  const int64_t b = r / ((int64_t)p.Nq * p.Hq);
   const int S = p.num_splits;
+  const int64_t o_row = b * p.i_bs + (int64_t)t * p.i_ss + (int64_t)h * p.i_hs;
+  const int64_t l_row = b * p.il_bs + (int64_t)h * p.il_hs + (int64_t)t * p.il_ss;
+  auto lse_of = [&](int s_) -> float {
+    return p.pair ? p.lse_in[s_][l_row] : p.lse_in[0][(int64_t)s_ * p.lse_split + l_row];
+  };
   float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, p.lse_part[(int64_t)s * p.rows + r]);
+  for (int s_ = 0; s_ < S; ++s_) M = fmaxf(M, lse_of(s_));
   constexpr int E = D / 64;  // elements per lane
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
   float W = 0.0f;
   if (M != kNegInf) {
-    for (int s = 0; s < S; ++s) {
-      const float x = p.lse_part[(int64_t)s * p.rows + r];
-      const float w = (x == kNegInf) ? 0.0f : exp2_fast((x - M) * kLog2e);
+    for (int s_ = 0; s_ < S; ++s_) {
+      const float x = lse_of(s_);
+      if (x == kNegInf) continue;
+      const float w = exp2_fast((x - M) * kLog2e);
       W += w;
-      const float* op = p.o_part + ((int64_t)s * p.rows + r) * D + lane * E;
+      const int64_t off = (p.pair ? 0 : (int64_t)s_ * p.o_split) + o_row + lane * E;
+      const void* base = p.pair ? p.o_in[s_] : p.o_in[0];
+      if constexpr (IN_BF16) {
+        const uint16_t* op = static_cast<const uint16_t*>(base) + off;
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += w * op[e];
+        for (int e = 0; e < E; ++e) acc[e] += w * __uint_as_float((uint32_t)op[e] << 16);
+      } else {
+        const float* op = static_cast<const float*>(base) + off;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += w * op[e];
+      }
     }
   }
   const bool empty = (M == kNegInf) || !(W > 0.0f);
   const float inv = empty ? 0.0f : rcp_fast(W);
-  const int t = (int)(r % p.Nq);
-  const int h = (int)((r / p.Nq) % p.Hq);
-  const int64_t b = r / ((int64_t)p.Nq * p.Hq);
   uint16_t* ob = p.o + b * p.o_bs + (int64_t)t * p.o_ss + (int64_t)h * p.o_hs + lane * E;
   if (E == 2) {
     f32x8 x = {acc[0] * inv, acc[E - 1] * inv, 0, 0, 0, 0, 0, 0};
@@ -1433,7 +1450,8 @@ __global__ __launch_bounds__(kThreads) void fa_combine_kernel(FaCombineParams p)
     bf16x8 y = __builtin_convertvector(x, bf16x8);
     *ob = (uint16_t)(__builtin_bit_cast(u32x4, y).x & 0xffffu);
   }
-  if (lane == 0 && p.lse) p.lse[r] = empty ? kNegInf : M + __builtin_logf(W);
+  if (lane == 0 && p.lse)
+    p.lse[b * p.l_bs + (int64_t)h * p.l_hs + (int64_t)t * p.l_ss] = empty ? kNegInf : M + __builtin_logf(W);
 }
 
 // ------------------------------------------------------------------ rotary embedding, K/V append
@@ -2133,10 +2151,14 @@ hipError_t fa_launch_seq_order(const int32_t* lens, int B, int32_t* order, hipSt
 hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t s) {
   if (p.rows <= 0) return hipSuccess;
   const int64_t blocks = (p.rows + (kThreads / 64) - 1) / (kThreads / 64);
-  if (d == 128)
-    hipLaunchKernelGGL(fa_combine_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  if (d == 128 && !p.in_bf16)
+    hipLaunchKernelGGL((fa_combine_kernel<128, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else if (d == 128)
+    hipLaunchKernelGGL((fa_combine_kernel<128, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else if (d == 64 && !p.in_bf16)
+    hipLaunchKernelGGL((fa_combine_kernel<64, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else if (d == 64)
-    hipLaunchKernelGGL(fa_combine_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fa_combine_kernel<64, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -20,9 +20,13 @@
  *   - Return value: FA_OK, or a negative code with nothing enqueued:
  *       FA_ERR_INVALID_ARG  null pointer, negative or zero size, bad stride or
  *                           alignment, heads_q not a multiple of heads_kv,
- *                           workspace too small, num_splits < 1;
- *       FA_ERR_UNSUPPORTED  a head_dim other than 64 or 128, or a shape the
- *                           kernels do not cover (stated per entry point);
+ *                           workspace too small, num_splits < 0, a page_size
+ *                           that is not a multiple of 16 ("Attention kernels
+ *                           ...", section 6.1: pages of 16-multiple tokens);
+ *       FA_ERR_UNSUPPORTED  a head_dim other than 64 or 128, a K or V token
+ *                           stride of 2^25 elements or more (fa_fwd,
+ *                           fa_fwd_varlen), or a shape the kernels do not cover
+ *                           (stated per entry point);
  *       FA_ERR_HIP          a HIP runtime error while launching.
  *     fa_last_error() returns a message for the calling thread's last failure.
  *   - Rows that see no key at all get O = 0 and LSE = -inf (no NaN).
@@ -132,8 +136,7 @@ int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
  *   workspace: device memory of at least fa_kvcache_workspace_size(...) bytes
  *              (may be NULL when that size is 0); holds the fp32 partials.
  * opts->pack_gqa applies to chunked prefill only (decode always packs).
- * Errors: FA_ERR_UNSUPPORTED for num_splits > 1 with more than 32 packed rows,
- * or a page_size that is not a multiple of 16 with more than 32 packed rows.
+ * Errors: FA_ERR_UNSUPPORTED for num_splits > 1 with more than 32 packed rows.
  * Caller contract, not checked on the device: block_table entries of live pages
  * lie in [0, num_pages) and cache_seqlens[b] <= max_blocks_per_seq * page_size. */
 int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache,
@@ -183,8 +186,7 @@ int fa_fwd_kvcache_paged_noalloc(const fa_attn_opts* opts, const void* q, const 
  *   cache_seqlens device int32 [batch]; max_seqlen_q: an upper bound of the query lengths.
  * A sequence with at most 32 packed rows (new tokens x heads_q / heads_kv) runs as
  * a decode step, one workgroup per (sequence, KV head); the others in workgroup
- * tiles of 128 packed rows (no split-KV); two launches, both on the stream.  Errors:
- * FA_ERR_UNSUPPORTED for a page_size that is not a multiple of 16.  Caller contract,
+ * tiles of 128 packed rows (no split-KV); two launches, both on the stream.  Caller contract,
  * not checked on the device: cu_seqlens_q non-decreasing from 0 with
  * cu_seqlens_q[batch] == total_q, query lengths <= max_seqlen_q, live block-table
  * entries in [0, num_pages), cache_seqlens[b] <= max_blocks_per_seq * page_size. */
@@ -206,7 +208,10 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
 int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, int page_size,
                           int max_blocks_per_seq);
 
-/* Bytes of workspace fa_fwd_kvcache_paged needs: 0 for num_splits == 1, else
+/* Bytes of workspace fa_fwd_kvcache_paged needs for a resolved split count
+ * num_splits >= 1 (resolve 0 with fa_kvcache_num_splits first; 0 and 1 give 0
+ * here, so sizing with 0 under-sizes every call that resolves to more splits):
+ * 0 for num_splits == 1, else
  * num_splits * batch * seqlen_q * heads_q * (head_dim + 1) * 4 rounded up to 256
  * (the fp32 partial O and LSE), plus, when batch <= 4096, batch * 4 rounded up
  * to 256 (the order in which the split workgroups take the sequences: longest
@@ -341,14 +346,45 @@ int fa_fwd_fp8(const fa_attn_opts* opts, const void* q, const float* q_scales, c
  * the tiles of one pass):
  *   M = max_s LSE_s,  w_s = exp(LSE_s - M),  LSE = M + ln(sum_s w_s),
  *   O = sum_s (w_s / sum_s w_s) * O_s.
- * A row whose every LSE_s is -inf gets O = 0 and LSE = -inf.
- *   o_part   float32 [num_splits, rows, head_dim], split stride rows*head_dim, row stride head_dim
- *   lse_part float32 [num_splits, rows]
+ * A partial whose LSE is -inf has weight 0 and its O is not read; a row whose
+ * every LSE_s is -inf gets O = 0 and LSE = -inf.
+ *   o_part   float32: row r of split s at o_part + (s * part_stride_rows + r) * head_dim
+ *   lse_part float32: row r of split s at lse_part[s * part_stride_rows + r]
+ *   part_stride_rows  rows between consecutive splits, >= rows
  *   out      bfloat16, row r at out + r * out_row_stride (written)
  *   lse_out  float32 [rows] (written; may be NULL)
- * With num_splits == 2 this is the two-state merge used for prefix/suffix attention. */
+ * Errors: FA_ERR_INVALID_ARG for part_stride_rows < rows, out_row_stride < head_dim,
+ * or pointers that are not 4-byte aligned. */
 int fa_combine(const float* o_part, const float* lse_part, int num_splits, int64_t rows,
-               int head_dim, void* out, int64_t out_row_stride, float* lse_out, void* stream);
+               int head_dim, int64_t part_stride_rows, void* out, int64_t out_row_stride,
+               float* lse_out, void* stream);
+
+/* Element types of the states fa_merge_attn_states reads. */
+#define FA_DTYPE_FP32 0
+#define FA_DTYPE_BF16 1
+
+/* Merge of two attention states held in separate buffers, e.g. attention over a
+ * cached prefix and over the new suffix of the same queries ("Attention kernels
+ * ...", section 6.3: merge_attn_states(prefix_output, prefix_lse, suffix_output,
+ * suffix_lse)); the same formula as fa_combine with two splits.
+ *   prefix_out, suffix_out  [batch, seqlen, heads, head_dim] of in_dtype (FA_DTYPE_FP32 or
+ *                           FA_DTYPE_BF16), both with strides in_strides = {batch, seq, head}
+ *                           in elements, head_dim contiguous (as fa_fwd writes O)
+ *   prefix_lse, suffix_lse  float32, element (b, h, t) at b * lse_strides[0] +
+ *                           h * lse_strides[1] + t * lse_strides[2] (fa_fwd's [batch, heads,
+ *                           seqlen] is {heads * seqlen, seqlen, 1}; fa_fwd_varlen's
+ *                           [heads, total] is batch 1 with {0, total, 1})
+ *   out      bfloat16 [batch, seqlen, heads, head_dim], strides out_strides (written; may
+ *            alias neither input)
+ *   lse_out  float32, the same layout as the input LSEs (written; may be NULL)
+ * Errors: FA_ERR_UNSUPPORTED for another in_dtype or head_dim; FA_ERR_INVALID_ARG for
+ * NULL pointers, negative sizes or strides, or misaligned pointers (out 4-byte aligned
+ * with even strides). */
+int fa_merge_attn_states(const void* prefix_out, const float* prefix_lse, const void* suffix_out,
+                         const float* suffix_lse, int in_dtype, void* out, float* lse_out,
+                         int batch, int seqlen, int heads, int head_dim,
+                         const int64_t in_strides[3], const int64_t out_strides[3],
+                         const int64_t lse_strides[3], void* stream);
 
 /* Host-only helper, no device work: the class of key tile n (keys
  * [n*block_n, n*block_n + block_n)) for query rows at token indices

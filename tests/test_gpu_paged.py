@@ -127,6 +127,60 @@ def test_combine_against_oracle():
     check_close(out, lse, o_ref, l_ref, "combine")
 
 
+def test_combine_split_stride_wider_than_rows():
+    """Splits placed part_stride_rows > rows apart (a view into a larger buffer, e.g. partials
+    laid out for a bigger batch): only the first rows of each split are merged."""
+    S, rows, stride_rows, d = 3, 200, 257, 64
+    g = torch.Generator().manual_seed(12)
+    big_o = torch.randn(S, stride_rows, d, generator=g)
+    big_l = torch.randn(S, stride_rows, generator=g) * 3
+    big_l[2, ::5] = float("-inf")
+    o_view, l_view = big_o[:, :rows], big_l[:, :rows]
+    out, lse = api.fa_combine(big_o.to(DEV)[:, :rows], big_l.to(DEV)[:, :rows])
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.combine(o_view.double().numpy(), l_view.double().numpy())
+    check_close(out, lse, o_ref, l_ref, "combine with a split stride of 257 rows")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_merge_attn_states_two_separate_buffers(dtype):
+    """fa_merge_attn_states on a prefix and a suffix state allocated separately (bf16 as the
+    forward writes them, or fp32), LSE in the forward's [B, H, N] layout, against the
+    oracle's merge of the same two states; rows where one or both states are empty."""
+    B, N, H, d = 2, 77, 3, 128
+    g = torch.Generator().manual_seed(21)
+    po = torch.randn(B, N, H, d, generator=g).to(dtype)
+    so = torch.randn(B, N, H, d, generator=g).to(dtype)
+    pl = torch.randn(B, H, N, generator=g) * 4
+    sl = torch.randn(B, H, N, generator=g) * 4
+    pl[0, 1, ::4] = float("-inf")
+    sl[1, 2, ::3] = float("-inf")
+    pl[1, 0, 5] = sl[1, 0, 5] = float("-inf")
+    out, lse = api.fa_merge_attn_states(po.to(DEV), pl.to(DEV), so.to(DEV), sl.to(DEV))
+    torch.cuda.synchronize()
+    # oracle rows in [B, H, N] order
+    o_parts = np.stack([x.double().permute(0, 2, 1, 3).reshape(-1, d).numpy() for x in (po, so)])
+    l_parts = np.stack([x.double().reshape(-1).numpy() for x in (pl, sl)])
+    o_ref, l_ref = oracle.combine(o_parts, l_parts)
+    check_close(out.permute(0, 2, 1, 3).reshape(-1, d), lse.reshape(-1), o_ref, l_ref,
+                f"merge_attn_states {dtype}")
+    assert torch.isneginf(lse[1, 0, 5]) and bool((out[1, 5, 0] == 0).all())
+
+
+def test_merge_prefix_and_suffix_attention():
+    """Attention over a key prefix and over the suffix, by two fa_fwd calls into separate
+    buffers, merged by fa_merge_attn_states, equals the oracle's attention over all keys."""
+    B, Nq, Nk, P, H, d = 2, 96, 700, 300, 4, 128
+    t = W.dense(33, B, Nq, H, H, d, Nk=Nk)
+    q, k, v = (t[n].to(DEV) for n in "qkv")
+    o1, l1 = api.fa_fwd(q, k[:, :P].contiguous(), v[:, :P].contiguous(), causal=False)
+    o2, l2 = api.fa_fwd(q, k[:, P:].contiguous(), v[:, P:].contiguous(), causal=False)
+    out, lse = api.fa_merge_attn_states(o1, l1, o2, l2)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.fwd_dense(bits(t["q"]), bits(t["k"]), bits(t["v"]), causal=False)
+    check_close(out, lse, o_ref, l_ref, "prefix + suffix merge")
+
+
 def test_paged_deterministic():
     t = W.paged(8, 4, 32, 8, 128, 256, 0, 0, cache_seqlens=[3000, 20, 700, 4096])
     a = run(t, t["k_cache"], t["v_cache"], 4, causal=True)

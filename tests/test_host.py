@@ -112,6 +112,9 @@ def call_fwd(opts=None, q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, Nq=16, Nk=16, Hq=
     (dict(q=ctypes.c_void_p((1 << 20) + 2)), FA_ERR_INVALID_ARG),      # misaligned base
     (dict(ks=(ctypes.c_int64 * 3)(2048, 2050, 128)), FA_ERR_INVALID_ARG),  # misaligned row stride
     (dict(vs=None), FA_ERR_INVALID_ARG),
+    # K/V blocks are addressed with 32-bit byte offsets: token strides below 2^25 elements
+    (dict(ks=(ctypes.c_int64 * 3)(1 << 40, 1 << 25, 128)), FA_ERR_UNSUPPORTED),
+    (dict(vs=(ctypes.c_int64 * 3)(1 << 40, 1 << 25, 128)), FA_ERR_UNSUPPORTED),
 ])
 def test_fwd_rejects_invalid_arguments(kw, code):
     assert call_fwd(**kw) == code
@@ -150,9 +153,11 @@ def test_paged_rejects_invalid_arguments():
     assert call_paged(num_splits=4) == FA_ERR_INVALID_ARG                  # no workspace
     need = api.fa_kvcache_workspace_size(64, 1, 32, 128, 4)
     assert call_paged(num_splits=4, ws=FAKE, ws_bytes=need - 256) == FA_ERR_INVALID_ARG
-    # 9 * 4 packed rows > 32 run as chunked prefill: no split-KV, 16-multiple pages
+    # 9 * 4 packed rows > 32 run as chunked prefill: no split-KV
     assert call_paged(Nq=9, num_splits=2, ws=FAKE, ws_bytes=1 << 30) == FA_ERR_UNSUPPORTED
-    assert call_paged(Nq=9, page=24) == FA_ERR_UNSUPPORTED
+    # pages of 16-multiple tokens ("Attention kernels ...", section 6.1), decode and prefill alike
+    assert call_paged(Nq=9, page=24) == FA_ERR_INVALID_ARG
+    assert call_paged(page=24) == FA_ERR_INVALID_ARG
     assert call_paged(page=0) == FA_ERR_INVALID_ARG
     assert call_paged(bt=None) == FA_ERR_INVALID_ARG
     assert call_paged(d=32) == FA_ERR_UNSUPPORTED
@@ -174,10 +179,28 @@ def test_workspace_size_formula():
 
 def test_combine_rejects_invalid_arguments():
     L = api.lib()
-    assert L.fa_combine(None, FAKE, 2, 10, 128, FAKE, 128, None, None) == FA_ERR_INVALID_ARG
-    assert L.fa_combine(FAKE, FAKE, 0, 10, 128, FAKE, 128, None, None) == FA_ERR_INVALID_ARG
-    assert L.fa_combine(FAKE, FAKE, 2, 10, 96, FAKE, 128, None, None) == FA_ERR_UNSUPPORTED
-    assert L.fa_combine(FAKE, FAKE, 2, 10, 128, FAKE, 64, None, None) == FA_ERR_INVALID_ARG
+    assert L.fa_combine(None, FAKE, 2, 10, 128, 10, FAKE, 128, None, None) == FA_ERR_INVALID_ARG
+    assert L.fa_combine(FAKE, FAKE, 0, 10, 128, 10, FAKE, 128, None, None) == FA_ERR_INVALID_ARG
+    assert L.fa_combine(FAKE, FAKE, 2, 10, 96, 10, FAKE, 128, None, None) == FA_ERR_UNSUPPORTED
+    assert L.fa_combine(FAKE, FAKE, 2, 10, 128, 10, FAKE, 64, None, None) == FA_ERR_INVALID_ARG
+    assert L.fa_combine(FAKE, FAKE, 2, 10, 128, 9, FAKE, 128, None, None) == FA_ERR_INVALID_ARG  # splits overlap
+    assert L.fa_combine(FAKE, FAKE, 2, 0, 128, 0, FAKE, 128, None, None) == 0                     # no rows: no launch
+
+
+def test_merge_attn_states_rejects_invalid_arguments():
+    L = api.lib()
+    s3 = (ctypes.c_int64 * 3)(4096 * 16 * 128, 16 * 128, 128)
+    ls3 = (ctypes.c_int64 * 3)(16 * 4096, 4096, 1)
+    def call(po=FAKE, dt=api.FA_DTYPE_BF16, d=128, B=4, out=FAKE, os=s3, N=4096):
+        return L.fa_merge_attn_states(po, FAKE, FAKE, FAKE, dt, out, None, B, N, 16, d, s3, os, ls3, None)
+    assert call(po=None) == FA_ERR_INVALID_ARG
+    assert call(out=None) == FA_ERR_INVALID_ARG
+    assert call(dt=7) == FA_ERR_UNSUPPORTED
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(B=-1) == FA_ERR_INVALID_ARG
+    assert call(out=ctypes.c_void_p(0x1002)) == FA_ERR_INVALID_ARG                       # 2-byte aligned out
+    assert call(os=(ctypes.c_int64 * 3)(4096 * 16 * 128, 16 * 128, 129)) == FA_ERR_INVALID_ARG  # odd stride
+    assert call(B=0) == 0 and call(N=0) == 0                                              # nothing to merge
 
 
 FULL_TILES_CHECK = r"""
@@ -240,6 +263,7 @@ def test_append_rejects_invalid_arguments():
     assert call(B=0) == FA_ERR_INVALID_ARG
     assert call(Ln=-1) == FA_ERR_INVALID_ARG
     assert call(page=0) == FA_ERR_INVALID_ARG
+    assert call(page=24) == FA_ERR_INVALID_ARG                       # pages of 16-multiple tokens
     assert call(ks=(ctypes.c_int64 * 3)(2048, 2050, 128)) == FA_ERR_INVALID_ARG
     assert call(Ln=0) == 0                                           # nothing to write, no launch
     assert call(cos=FAKE) == FA_ERR_INVALID_ARG                      # cos without sin
@@ -271,7 +295,7 @@ def test_varlen_paged_rejects_invalid_arguments():
     assert call(cu=None) == FA_ERR_INVALID_ARG
     assert call(d=80) == FA_ERR_UNSUPPORTED
     assert call(B=0) == FA_ERR_INVALID_ARG
-    assert call(page=24) == FA_ERR_UNSUPPORTED
+    assert call(page=24) == FA_ERR_INVALID_ARG
     assert call(Hq=30) == FA_ERR_INVALID_ARG
 
 
