@@ -279,8 +279,11 @@ def bench_unified(api, W, steps, warmup):
     cu, bt, sl = t["cu_seqlens_q"].cuda(), t["block_table"].cuda(), t["cache_seqlens"].cuda()
     out = torch.empty_like(t["q"])
     lse = torch.empty((c["Hq"], t["q"].shape[0]), dtype=torch.float32, device="cuda")
+    S = int(api.lib().fa_varlen_paged_num_splits(len(t["qlens"]), c["Hq"], c["Hkv"], t["block_table"].shape[1]))
+    ws = torch.empty(max(1, int(api.lib().fa_varlen_paged_workspace_size(len(t["qlens"]), c["Hkv"], c["d"], S))),
+                     dtype=torch.uint8, device="cuda")
     fn = lambda: api.fa_fwd_varlen_paged(t["q"], t["k_cache"], t["v_cache"], cu, c["chunk"], bt, sl,  # noqa
-                                         causal=True, out=out, lse=lse)
+                                         causal=True, num_splits=S, out=out, lse=lse, workspace=ws)
     wall, ms, _ = time_launches(fn, steps, warmup)
     tf = flops / (ms * 1e-3) / 1e12
     return {"metric": "unified prefill+decode batch TFLOP/s", "unit": "TFLOP/s", "value": round(tf, 2),
@@ -289,7 +292,8 @@ def bench_unified(api, W, steps, warmup):
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
             "config": {"workload": name, "decode_requests": c["n_decode"], "chunks": c["n_chunk"],
                        "chunk": c["chunk"], "heads_q": c["Hq"], "heads_kv": c["Hkv"], "head_dim": c["d"],
-                       "page_size": c["page"], "flop_convention": "4*d*Hq*sum visible pairs"}}
+                       "page_size": c["page"], "decode_num_splits": S,
+                       "flop_convention": "4*d*Hq*sum visible pairs"}}
 
 
 def bench_bwd(api, W, steps, warmup):

@@ -22,7 +22,8 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
 EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
-           "fa_fwd_varlen_paged", "fa_kvcache_num_splits",
+           "fa_fwd_varlen_paged", "fa_varlen_paged_num_splits", "fa_varlen_paged_workspace_size",
+           "fa_kvcache_num_splits",
            "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary", "fa_bwd", "fa_bwd_workspace_size",
            "fa_fp8_quantize", "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8",
            "fa_combine", "fa_merge_attn_states", "fa_tile_class", "fa_last_error", "fa_version")
@@ -75,8 +76,12 @@ def lib():
     L.fa_bwd.argtypes = [OPT, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, S3, S3, S3, S3, S3, P, SZ, P]
     L.fa_bwd_workspace_size.argtypes = [I, I, I]
     L.fa_bwd_workspace_size.restype = SZ
-    L.fa_fwd_varlen_paged.argtypes = [OPT, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I64, I, I, S3, S3, S3,
-                                      S3, P]
+    L.fa_fwd_varlen_paged.argtypes = [OPT, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I64, I, I, I, P, SZ,
+                                      S3, S3, S3, S3, P]
+    L.fa_varlen_paged_num_splits.argtypes = [I, I, I, I]
+    L.fa_varlen_paged_num_splits.restype = I
+    L.fa_varlen_paged_workspace_size.argtypes = [I, I, I, I]
+    L.fa_varlen_paged_workspace_size.restype = SZ
     L.fa_fp8_quantize.argtypes = [P, I, I, I, I, S3, I, P, S3, P, P]
     L.fa_fp8_quantize_v.argtypes = [P, I, I, I, I, S3, P, P, P]
     L.fa_fp8_vt_len.argtypes = [I]
@@ -252,11 +257,12 @@ def fa_fwd_kvcache_paged_noalloc(q, k_cache, v_cache, block_table, cache_seqlens
 
 
 def fa_fwd_varlen_paged(q, k_cache, v_cache, cu_seqlens_q, max_seqlen_q, block_table, cache_seqlens, *,
-                        softmax_scale=None, causal=True, window=None, softcap=0.0, pack_gqa=-1,
-                        out=None, lse=None, return_lse=True, stream=None):
+                        num_splits=0, softmax_scale=None, causal=True, window=None, softcap=0.0, pack_gqa=-1,
+                        out=None, lse=None, workspace=None, return_lse=True, stream=None):
     """Unified prefill + decode over a paged cache.  q [total_q, Hq, d] packed by cu_seqlens_q;
     caches [num_pages, page, Hkv, d]; block_table int32 [B, max_blocks]; cache_seqlens int32 [B]
-    (keys per sequence, new tokens included) -> (out [total_q, Hq, d], lse [Hq, total_q])."""
+    (keys per sequence, new tokens included) -> (out [total_q, Hq, d], lse [Hq, total_q]).
+    num_splits: split-KV count of the decode requests (0: fa_varlen_paged_num_splits)."""
     _bf16_cuda(q, k_cache, v_cache)
     total_q, Hq, d = q.shape
     num_pages, page, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
@@ -271,11 +277,18 @@ def fa_fwd_varlen_paged(q, k_cache, v_cache, cu_seqlens_q, max_seqlen_q, block_t
     _bf16_cuda(out)
     if lse is None and return_lse:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if num_splits == 0:
+        num_splits = int(lib().fa_varlen_paged_num_splits(B, Hq, Hkv, block_table.shape[1]))
+    need = int(lib().fa_varlen_paged_workspace_size(B, Hkv, d, int(num_splits)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
     _check(lib().fa_fwd_varlen_paged(ctypes.byref(o), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
                                      _ptr(lse), _ptr(cu_seqlens_q), _ptr(block_table), _ptr(cache_seqlens),
                                      B, int(max_seqlen_q), total_q, Hq, Hkv, d, num_pages, page,
-                                     block_table.shape[1], _strides(q, (0, 1)), _strides(k_cache, (0, 1, 2)),
+                                     block_table.shape[1], int(num_splits), _ptr(workspace), ws_bytes,
+                                     _strides(q, (0, 1)), _strides(k_cache, (0, 1, 2)),
                                      _strides(v_cache, (0, 1, 2)), _strides(out, (0, 1)), _stream(stream)))
     return out, lse
 

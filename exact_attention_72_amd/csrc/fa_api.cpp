@@ -281,14 +281,41 @@ int fa_kvcache_num_splits(int batch, int seqlen_q, int heads_q, int heads_kv, in
   return s < 1 ? 1 : (int)s;
 }
 
+// Partial (O, LSE) bytes of the varlen paged decode requests: num_splits x batch x
+// heads_kv units of FA_PAGED_MAX_ROWS rows, rounded up to 256; the sequence order
+// (one int32 per sequence, batch <= FA_SEQ_ORDER_MAX) follows.
+static size_t varlen_paged_partial_bytes(int batch, int heads_kv, int head_dim, int num_splits) {
+  size_t rows = (size_t)batch * heads_kv * FA_PAGED_MAX_ROWS;
+  size_t bytes = (size_t)num_splits * rows * ((size_t)head_dim + 1) * 4;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+size_t fa_varlen_paged_workspace_size(int batch, int heads_kv, int head_dim, int num_splits) {
+  if (num_splits <= 1 || batch <= 0 || heads_kv <= 0 || head_dim <= 0) return 0;
+  size_t bytes = varlen_paged_partial_bytes(batch, heads_kv, head_dim, num_splits);
+  if (batch <= FA_SEQ_ORDER_MAX) bytes += ((size_t)batch * 4 + 255) & ~(size_t)255;
+  return bytes;
+}
+
+int fa_varlen_paged_num_splits(int batch, int heads_q, int heads_kv, int max_blocks_per_seq) {
+  // the decode requests of the batch, at most all of its sequences, as one
+  // decode step each: the split count fa_kvcache_num_splits gives for them
+  return fa_kvcache_num_splits(batch, 1, heads_q, heads_kv, 16, max_blocks_per_seq);
+}
+
 int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, const void* v_cache,
                         void* out, float* lse, const int32_t* cu_seqlens_q, const int32_t* block_table,
                         const int32_t* cache_seqlens, int batch, int max_seqlen_q, int total_q, int heads_q,
                         int heads_kv, int head_dim, int64_t num_pages, int page_size, int max_blocks_per_seq,
-                        const int64_t q_strides[2], const int64_t k_strides[3], const int64_t v_strides[3],
-                        const int64_t o_strides[2], void* stream) {
+                        int num_splits, void* workspace, size_t workspace_bytes, const int64_t q_strides[2],
+                        const int64_t k_strides[3], const int64_t v_strides[3], const int64_t o_strides[2],
+                        void* stream) {
   g_err[0] = 0;
   int rc;
+  if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
+  if (num_splits == 0 && batch > 0 && heads_q > 0 && heads_kv > 0 && heads_q % heads_kv == 0)
+    num_splits = fa_varlen_paged_num_splits(batch, heads_q, heads_kv, max_blocks_per_seq);
+  if (num_splits == 0) num_splits = 1;  // invalid sizes: reported below
   if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
   if (!q || !k_cache || !v_cache || !out || !cu_seqlens_q || !block_table || !cache_seqlens)
     return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
@@ -301,6 +328,10 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   if ((rc = check_strides("q", q, q_strides, 2)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
       (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 2)))
     return rc;
+  const size_t need = fa_varlen_paged_workspace_size(batch, heads_kv, head_dim, num_splits);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   FaParams p;
   memset(&p, 0, sizeof p);
   bool softcap = false;
@@ -346,9 +377,27 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   // them no tiles
   p.skip_rows = FA_PAGED_MAX_ROWS;
   FaParams pd = p;
-  pd.num_splits = 1;
+  pd.num_splits = num_splits;
+  if (num_splits > 1) {
+    // split-KV for the decode requests: fp32 partials per (sequence, KV head)
+    // unit and split, merged by the packed combine; the split workgroups take the
+    // sequences longest cache first
+    pd.o_part = static_cast<float*>(workspace);
+    pd.lse_part = pd.o_part + (size_t)num_splits * batch * heads_kv * FA_PAGED_MAX_ROWS * head_dim;
+    if (batch <= FA_SEQ_ORDER_MAX) {
+      int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                  varlen_paged_partial_bytes(batch, heads_kv, head_dim, num_splits));
+      hipError_t e = fa_launch_seq_order(cache_seqlens, batch, order, s);
+      if (e != hipSuccess) return hip_fail(e, "sequence order launch");
+      pd.seq_order = order;
+    }
+  }
   hipError_t e = fa_launch_paged(pd, head_dim, softcap, s);
   if (e != hipSuccess) return hip_fail(e, "varlen paged decode launch");
+  if (num_splits > 1) {
+    e = fa_launch_combine_packed(pd, head_dim, s);
+    if (e != hipSuccess) return hip_fail(e, "varlen paged combine launch");
+  }
   e = fa_launch_prefill(p, head_dim, true, true, pack, softcap, s);
   if (e != hipSuccess) return hip_fail(e, "varlen paged launch");
   return FA_OK;

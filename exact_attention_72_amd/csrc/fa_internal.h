@@ -193,6 +193,9 @@ hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t s
 constexpr int FA_SEQ_ORDER_MAX = 4096;
 hipError_t fa_launch_seq_order(const int32_t* lens, int B, int32_t* order, hipStream_t stream);
 hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t stream);
+// Combine of the varlen paged decode partials (packed per (sequence, KV head)
+// unit, FA_PAGED_MAX_ROWS rows each) into p.o / p.lse ([total_q, Hq] layouts).
+hipError_t fa_launch_combine_packed(const FaParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_append(const FaAppendParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_rotary(const FaRotaryParams& p, int d, hipStream_t stream);
 hipError_t fa_launch_fp8_quant(const FaFp8QuantParams& p, int d, hipStream_t s);

@@ -1381,6 +1381,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
         *reinterpret_cast<bf16x8*>(ob + 8 * h) = __builtin_convertvector(x, bf16x8);
       }
       if (d0 == 0 && p.lse) p.lse[(int64_t)b * p.lse_bs + (int64_t)chead * p.lse_hs + q_start + ctok] = lse;
+    } else if (p.cu_q) {
+      // varlen batch: partial rows packed per (sequence, KV head) unit, 32 each
+      const int64_t rows_all = (int64_t)p.B * p.Hkv * FA_PAGED_MAX_ROWS;
+      const int64_t pr = ((int64_t)b * p.Hkv + kvh) * FA_PAGED_MAX_ROWS + cc;
+      float* op = p.o_part + ((int64_t)split * rows_all + pr) * D + d0;
+#pragma unroll
+      for (int x = 0; x < 16; x += 4)
+        *reinterpret_cast<float4*>(op + x) = make_float4(acc[x], acc[x + 1], acc[x + 2], acc[x + 3]);
+      if (d0 == 0) p.lse_part[(int64_t)split * rows_all + pr] = lse;
     } else {
       const int64_t rows_all = (int64_t)p.B * p.Hq * Lq;
       float* op = p.o_part + ((int64_t)split * rows_all + r) * D + d0;
@@ -1452,6 +1461,59 @@ __global__ __launch_bounds__(kThreads) void fa_combine_kernel(FaCombineParams p)
   }
   if (lane == 0 && p.lse)
     p.lse[b * p.l_bs + (int64_t)h * p.l_hs + (int64_t)t * p.l_ss] = empty ? kNegInf : M + __builtin_logf(W);
+}
+
+// Combine of the varlen paged decode partials: one wave per packed row of a
+// (sequence, KV head) unit (FA_PAGED_MAX_ROWS each); rows of sequences that ran
+// in the prefill kernel, and rows past a sequence's new tokens, are skipped.
+// Packed row r of sequence b and KV head kvh is token cu_q[b] + r / g of query
+// head kvh * g + r % g.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa_combine_packed_kernel(FaParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t u = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t rows_all = (int64_t)p.B * p.Hkv * FA_PAGED_MAX_ROWS;
+  if (u >= rows_all) return;
+  const int r = (int)(u % FA_PAGED_MAX_ROWS);
+  const int kvh = (int)((u / FA_PAGED_MAX_ROWS) % p.Hkv);
+  const int b = (int)(u / ((int64_t)FA_PAGED_MAX_ROWS * p.Hkv));
+  const int q0 = p.cu_q[b];
+  const int Lq = p.cu_q[b + 1] - q0;
+  if (Lq <= 0 || Lq * p.g > FA_PAGED_MAX_ROWS || r >= Lq * p.g) return;
+  const int S = p.num_splits;
+  float M = kNegInf;
+  for (int s_ = 0; s_ < S; ++s_) M = fmaxf(M, p.lse_part[(int64_t)s_ * rows_all + u]);
+  constexpr int E = D / 64;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  float W = 0.0f;
+  if (M != kNegInf) {
+    for (int s_ = 0; s_ < S; ++s_) {
+      const float x = p.lse_part[(int64_t)s_ * rows_all + u];
+      if (x == kNegInf) continue;
+      const float w = exp2_fast((x - M) * kLog2e);
+      W += w;
+      const float* op = p.o_part + ((int64_t)s_ * rows_all + u) * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += w * op[e];
+    }
+  }
+  const bool empty = (M == kNegInf) || !(W > 0.0f);
+  const float inv = empty ? 0.0f : rcp_fast(W);
+  const int tok = q0 + r / p.g;
+  const int head = kvh * p.g + r % p.g;
+  uint16_t* ob = p.o + (int64_t)tok * p.o_ss + (int64_t)head * p.o_hs + lane * E;
+  if (E == 2) {
+    f32x8 x = {acc[0] * inv, acc[E - 1] * inv, 0, 0, 0, 0, 0, 0};
+    bf16x8 y = __builtin_convertvector(x, bf16x8);
+    *reinterpret_cast<uint32_t*>(ob) = __builtin_bit_cast(u32x4, y).x;
+  } else {
+    f32x8 x = {acc[0] * inv, 0, 0, 0, 0, 0, 0, 0};
+    bf16x8 y = __builtin_convertvector(x, bf16x8);
+    *ob = (uint16_t)(__builtin_bit_cast(u32x4, y).x & 0xffffu);
+  }
+  if (lane == 0 && p.lse) p.lse[(int64_t)head * p.lse_hs + tok] = empty ? kNegInf : M + __builtin_logf(W);
 }
 
 // ------------------------------------------------------------------ rotary embedding, K/V append
@@ -2159,6 +2221,19 @@ hipError_t fa_launch_combine(const FaCombineParams& p, int d, hipStream_t s) {
     hipLaunchKernelGGL((fa_combine_kernel<64, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else if (d == 64)
     hipLaunchKernelGGL((fa_combine_kernel<64, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t fa_launch_combine_packed(const FaParams& p, int d, hipStream_t s) {
+  const int64_t rows_all = (int64_t)p.B * p.Hkv * FA_PAGED_MAX_ROWS;
+  if (rows_all <= 0) return hipSuccess;
+  const int64_t blocks = (rows_all + (kThreads / 64) - 1) / (kThreads / 64);
+  if (d == 128)
+    hipLaunchKernelGGL(fa_combine_packed_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else if (d == 64)
+    hipLaunchKernelGGL(fa_combine_packed_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

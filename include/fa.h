@@ -184,19 +184,38 @@ int fa_fwd_kvcache_paged_noalloc(const fa_attn_opts* opts, const void* q, const 
  *   lse      [heads_q, total_q] float32 (written; may be NULL)
  *   cu_seqlens_q device int32 [batch + 1]; block_table device int32 [batch, max_blocks_per_seq];
  *   cache_seqlens device int32 [batch]; max_seqlen_q: an upper bound of the query lengths.
+ *   num_splits  split-KV count for the decode requests (>= 1; 0 takes
+ *               fa_varlen_paged_num_splits(...)); workspace: device memory of at least
+ *               fa_varlen_paged_workspace_size(batch, heads_kv, head_dim, resolved
+ *               num_splits) bytes, 16-byte aligned (may be NULL when that is 0).
  * A sequence with at most 32 packed rows (new tokens x heads_q / heads_kv) runs as
- * a decode step, one workgroup per (sequence, KV head); the others in workgroup
- * tiles of 128 packed rows (no split-KV); two launches, both on the stream.  Caller contract,
- * not checked on the device: cu_seqlens_q non-decreasing from 0 with
- * cu_seqlens_q[batch] == total_q, query lengths <= max_seqlen_q, live block-table
- * entries in [0, num_pages), cache_seqlens[b] <= max_blocks_per_seq * page_size. */
+ * a decode step, one workgroup per (sequence, KV head, split) with the splits'
+ * fp32 partials merged by a combine kernel ("Attention kernels ...", section 6.3);
+ * the others in workgroup tiles of 128 packed rows (no split-KV); all launches on
+ * the stream.  Caller contract, not checked on the device: cu_seqlens_q
+ * non-decreasing from 0 with cu_seqlens_q[batch] == total_q, query lengths <=
+ * max_seqlen_q, live block-table entries in [0, num_pages), cache_seqlens[b] <=
+ * max_blocks_per_seq * page_size. */
 int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_cache,
                         const void* v_cache, void* out, float* lse, const int32_t* cu_seqlens_q,
                         const int32_t* block_table, const int32_t* cache_seqlens, int batch,
                         int max_seqlen_q, int total_q, int heads_q, int heads_kv, int head_dim,
-                        int64_t num_pages, int page_size, int max_blocks_per_seq,
-                        const int64_t q_strides[2], const int64_t k_strides[3],
-                        const int64_t v_strides[3], const int64_t o_strides[2], void* stream);
+                        int64_t num_pages, int page_size, int max_blocks_per_seq, int num_splits,
+                        void* workspace, size_t workspace_bytes, const int64_t q_strides[2],
+                        const int64_t k_strides[3], const int64_t v_strides[3],
+                        const int64_t o_strides[2], void* stream);
+
+/* Split count fa_fwd_varlen_paged takes for num_splits == 0 (host only): the
+ * decode requests, at most all batch sequences, are sized as one decode step
+ * each, as fa_kvcache_num_splits does for seqlen_q = 1. */
+int fa_varlen_paged_num_splits(int batch, int heads_q, int heads_kv, int max_blocks_per_seq);
+
+/* Bytes of workspace fa_fwd_varlen_paged needs for a resolved num_splits >= 1: 0
+ * for num_splits == 1, else num_splits * batch * heads_kv * 32 * (head_dim + 1) * 4
+ * rounded up to 256 (fp32 partials of every (sequence, KV head) unit's up to 32
+ * packed rows), plus, when batch <= 4096, batch * 4 rounded up to 256 (the order in
+ * which the split workgroups take the sequences). */
+size_t fa_varlen_paged_workspace_size(int batch, int heads_kv, int head_dim, int num_splits);
 
 /* Split count of fa_fwd_kvcache_paged for num_splits == 0 (host only, no device
  * work; it reads the current device's compute-unit count): about 4 workgroups

@@ -410,21 +410,25 @@ def _run_varlen_paged(t, kc, vc, **kw):
     ([8, 9, 1, 2, 0], [300, 280, 70, 1, 40], 16, 4, 64, 16, -1),
     ([1, 8, 2, 1], [100, 300, 5, 1000], 8, 2, 128, 16, -1),  # every sequence in the decode kernel
 ])
-def test_varlen_paged_mixed_batch(qlens, lens, Hq, Hkv, d, page, pack):
+@pytest.mark.parametrize("num_splits", [1, 3, 6])
+def test_varlen_paged_mixed_batch(qlens, lens, Hq, Hkv, d, page, pack, num_splits):
+    """Decode requests with 1, 3 and 6 splits (short last splits included) beside prefill
+    chunks, on a pool whose unreferenced pages and tail slots are NaN."""
     t = _varlen_paged_case(91 + len(qlens) + d, qlens, lens, Hq, Hkv, d, page)
     kc, vc = poison_unused(t)
-    out, lse = _run_varlen_paged(t, kc, vc, causal=True, pack_gqa=pack)
+    out, lse = _run_varlen_paged(t, kc, vc, causal=True, pack_gqa=pack, num_splits=num_splits)
     o_ref, l_ref = _ref_varlen_paged(t, causal=True)
-    check_close(out, lse, o_ref, l_ref, f"varlen paged qlens={qlens}")
+    check_close(out, lse, o_ref, l_ref, f"varlen paged qlens={qlens} S={num_splits}")
 
 
 def test_varlen_paged_window_softcap_and_count():
     qlens, lens = [1, 200, 33], [999, 250, 33]
     t = _varlen_paged_case(97, qlens, lens, 8, 2, 128, 32, mult=2.0)
     kw = dict(causal=True, window=(100, 0), softcap=30.0)
-    out, lse = _run_varlen_paged(t, t["k_cache"], t["v_cache"], **kw)
     o_ref, l_ref = _ref_varlen_paged(t, **kw)
-    check_close(out, lse, o_ref, l_ref, "varlen paged window+softcap")
+    for S in (1, 4):
+        out, lse = _run_varlen_paged(t, t["k_cache"], t["v_cache"], num_splits=S, **kw)
+        check_close(out, lse, o_ref, l_ref, f"varlen paged window+softcap S={S}")
     t0 = dict(t, q=torch.zeros_like(t["q"]))
     _, lse0 = _run_varlen_paged(t0, t["k_cache"], t["v_cache"], causal=True)
     cu = t["cu_q"].tolist()

@@ -289,14 +289,20 @@ def test_rotary_rejects_invalid_arguments():
 def test_varlen_paged_rejects_invalid_arguments():
     L = api.lib()
     o = _opts(causal=1)
-    def call(cu=FAKE, d=128, B=2, page=16, Hq=32, Hkv=8):
+    def call(cu=FAKE, d=128, B=2, page=16, Hq=32, Hkv=8, S=1, ws=None, ws_bytes=0):
         return L.fa_fwd_varlen_paged(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None, cu, FAKE, FAKE, B, 64,
-                                     100, Hq, Hkv, d, 100, page, 10, S2, S3, S3, S2, None)
+                                     100, Hq, Hkv, d, 100, page, 10, S, ws, ws_bytes, S2, S3, S3, S2, None)
     assert call(cu=None) == FA_ERR_INVALID_ARG
     assert call(d=80) == FA_ERR_UNSUPPORTED
     assert call(B=0) == FA_ERR_INVALID_ARG
     assert call(page=24) == FA_ERR_INVALID_ARG
     assert call(Hq=30) == FA_ERR_INVALID_ARG
+    assert call(S=-1) == FA_ERR_INVALID_ARG
+    assert call(S=3) == FA_ERR_INVALID_ARG                                 # no workspace
+    need = api.lib().fa_varlen_paged_workspace_size(2, 8, 128, 3)
+    assert need == (3 * 2 * 8 * 32 * 129 * 4 + 255) // 256 * 256 + 256
+    assert call(S=3, ws=FAKE, ws_bytes=need - 1) == FA_ERR_INVALID_ARG
+    assert api.lib().fa_varlen_paged_workspace_size(2, 8, 128, 1) == 0
 
 
 QUERY_RANGE_CHECK = r"""
