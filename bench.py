@@ -10,7 +10,8 @@ window 4096, softcap 30), and the chunked prefill over a paged cache (4 x 4096
 new tokens against 16384 cached keys, 32/8 heads) with the in-place K/V append
 of that chunk, a unified batch of 64 decode requests and 4 prefill chunks
 in one launch, the backward pass of the prefill workload, the FP8 (e4m3) forward of the
-prefill workload, and the prefill workload with ALiBi.
+prefill workload, the prefill workload with ALiBi, and the prefill workload through the
+two score_mod / mask_mod hooks (relative-position bias, prefix-LM).
 
 Prints one JSON line:
   value        prefill TFLOP/s, FLOPs counted as 4 * B * H * N^2 * d * 1/2 (the
@@ -344,6 +345,38 @@ def bench_alibi(api, W, steps, warmup):
                        "seq_len": N, "head_dim": d, "causal": True, "slopes": "2^(-8(h+1)/H)"}}
 
 
+def bench_mods(api, W, steps, warmup):
+    """The dense causal prefill workload through the two score_mod / mask_mod hooks: a
+    relative-position bias table (R = 256) with causal masking, and a prefix-LM mask with
+    prefixes 0, 1024, 2048, 4096 (the four sequences).  TFLOP/s on visible pairs (the bias
+    is not counted)."""
+    import torch
+    c = W.WORKLOADS["prefill_b4_h16_n4096_d128_causal"]
+    B, N, H, d = c["B"], c["N"], c["Hq"], c["d"]
+    t = W.dense(c["seed"], B, N, H, c["Hkv"], d, device="cuda")
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    R = 256
+    table = torch.randn(H, 2 * R + 1, device="cuda")
+    fr = lambda: api.fa_fwd_relpos_bias(t["q"], t["k"], t["v"], table, causal=True, out=out, lse=lse)  # noqa
+    _, ms_r, _ = time_launches(fr, steps, warmup)
+    prefixes = [0, 1024, 2048, 4096]
+    pl = torch.tensor(prefixes, dtype=torch.int32, device="cuda")
+    fp = lambda: api.fa_fwd_prefix_lm(t["q"], t["k"], t["v"], pl, out=out, lse=lse)  # noqa
+    _, ms_p, _ = time_launches(fp, steps, warmup)
+    fl_r = prefill_flops(B, H, N, d, True)
+    pairs = sum(sum(min(N, max(P, i + 1)) for i in range(N)) for P in prefixes)
+    fl_p = 4.0 * d * H * pairs
+    tr, tp = fl_r / (ms_r * 1e-3) / 1e12, fl_p / (ms_p * 1e-3) / 1e12
+    return {"metric": "attn fwd with score_mod / mask_mod TFLOP/s", "unit": "TFLOP/s",
+            "relpos_bias": {"value": round(tr, 2), "ms": round(ms_r, 4), "max_distance": R,
+                            "frac": round(tr / PEAK_BF16_TFLOPS, 4)},
+            "prefix_lm": {"value": round(tp, 2), "ms": round(ms_p, 4), "prefix_lens": prefixes,
+                          "frac": round(tp / PEAK_BF16_TFLOPS, 4)},
+            "config": {"workload": "prefill_b4_h16_n4096_d128 mods", "batch": B, "heads": H, "seq_len": N,
+                       "head_dim": d, "flop_convention": "4*d*H*sum visible pairs"}}
+
+
 def bench_fp8(api, W, steps, warmup):
     """FP8 (e4m3) forward of the dense causal prefill workload (batch 4, 16 heads, N = 4096,
     d = 128): fa_fwd_fp8 per launch on inputs quantized beforehand, TFLOP/s on the same
@@ -430,6 +463,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-alibi", action="store_true")
+    ap.add_argument("--no-mods", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -501,6 +535,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_alibi:
         line["alibi"] = bench_alibi(api, W, max(20, args.steps // 2), max(20, args.warmup // 2))
+        torch.cuda.empty_cache()
+    if not args.no_mods:
+        line["mods"] = bench_mods(api, W, max(20, args.steps // 2), max(20, args.warmup // 2))
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         tc = W.dense(c["seed"], B, N, H, c["Hkv"], d)

@@ -21,7 +21,7 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
-EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
+EXPORTS = ("fa_fwd", "fa_fwd_relpos_bias", "fa_fwd_prefix_lm", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
            "fa_fwd_varlen_paged", "fa_varlen_paged_num_splits", "fa_varlen_paged_workspace_size",
            "fa_kvcache_num_splits",
            "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary", "fa_bwd", "fa_bwd_workspace_size",
@@ -61,6 +61,8 @@ def lib():
     OPT = ctypes.POINTER(fa_attn_opts)
     L.fa_fwd.argtypes = [OPT, P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, S3, P]
     L.fa_fwd_varlen.argtypes = [OPT, P, P, P, P, P, P, P, I, I, I, I, I, I, I, S3, S3, S3, S3, P]
+    L.fa_fwd_relpos_bias.argtypes = [OPT, P, P, P, P, P, I, I, I, I, I, I, P, I, S3, S3, S3, S3, P]
+    L.fa_fwd_prefix_lm.argtypes = [OPT, P, P, P, P, P, I, I, I, I, I, I, P, S3, S3, S3, S3, P]
     L.fa_fwd_kvcache_paged.argtypes = [OPT, P, P, P, P, P, P, P, I, I, I, I, I, I64, I, I, I, P, SZ,
                                        S3, S3, S3, S3, P]
     L.fa_fwd_kvcache_paged_noalloc.argtypes = [OPT, P, P, P, P, P, P, P, I, I, I, I, I, I64, I, I, I,
@@ -89,7 +91,7 @@ def lib():
     L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_version.restype = I
-    for name in ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
+    for name in ("fa_fwd", "fa_fwd_relpos_bias", "fa_fwd_prefix_lm", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
                  "fa_combine", "fa_merge_attn_states", "fa_tile_class",
                  "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary", "fa_bwd", "fa_fp8_quantize",
                  "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8"):
@@ -154,6 +156,52 @@ def fa_fwd(q, k, v, *, softmax_scale=None, causal=False, window=None, softcap=0.
     _check(lib().fa_fwd(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Nq, Nk,
                         Hq, Hkv, d, _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)),
                         _strides(v, (0, 1, 2)), _strides(out, (0, 1, 2)), _stream(stream)))
+    return out, lse
+
+
+def _dense_out(q, out, lse, return_lse):
+    B, Nq, Hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _bf16_cuda(out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def fa_fwd_relpos_bias(q, k, v, bias, *, softmax_scale=None, causal=False, window=None, pack_gqa=-1,
+                       out=None, lse=None, return_lse=True, stream=None):
+    """Dense forward with a relative-position bias table: bias float32 [Hq, 2R + 1] on the device;
+    the logit of query position p and key j gets bias[h, clamp(j - p, -R, R) + R]."""
+    _bf16_cuda(q, k, v)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if bias.dtype != torch.float32 or not bias.is_cuda or not bias.is_contiguous() or bias.dim() != 2 \
+            or bias.shape[0] != Hq or bias.shape[1] % 2 != 1:
+        raise TypeError("bias must be a contiguous float32 [heads_q, 2R + 1] device tensor")
+    out, lse = _dense_out(q, out, lse, return_lse)
+    o = _opts(softmax_scale, causal, window, 0.0, pack_gqa)
+    _check(lib().fa_fwd_relpos_bias(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Nq, Nk,
+                                    Hq, Hkv, d, _ptr(bias), (bias.shape[1] - 1) // 2, _strides(q, (0, 1, 2)),
+                                    _strides(k, (0, 1, 2)), _strides(v, (0, 1, 2)), _strides(out, (0, 1, 2)),
+                                    _stream(stream)))
+    return out, lse
+
+
+def fa_fwd_prefix_lm(q, k, v, prefix_lens, *, softmax_scale=None, window=None, pack_gqa=-1, out=None,
+                     lse=None, return_lse=True, stream=None):
+    """Dense forward with a prefix-LM mask: prefix_lens int32 [B] on the device; key j is visible
+    to the query at position p iff j < prefix_lens[b] or j <= p."""
+    _bf16_cuda(q, k, v)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if prefix_lens.dtype != torch.int32 or not prefix_lens.is_cuda or prefix_lens.numel() != B:
+        raise TypeError("prefix_lens must be an int32 [batch] device tensor")
+    out, lse = _dense_out(q, out, lse, return_lse)
+    o = _opts(softmax_scale, False, window, 0.0, pack_gqa)
+    _check(lib().fa_fwd_prefix_lm(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Nq, Nk, Hq,
+                                  Hkv, d, _ptr(prefix_lens), _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)),
+                                  _strides(v, (0, 1, 2)), _strides(out, (0, 1, 2)), _stream(stream)))
     return out, lse
 
 

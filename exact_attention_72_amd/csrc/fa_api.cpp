@@ -154,11 +154,13 @@ int fa_tile_class(int tok_lo, int tok_hi, int seqlen_q, int seqlen_k, int causal
                        window_right < 0 ? -1 : window_right, block_n, n);
 }
 
-int fa_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v, void* out, float* lse,
-           int batch, int seqlen_q, int seqlen_k, int heads_q, int heads_kv, int head_dim,
-           const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
-           const int64_t o_strides[3], void* stream) {
-  g_err[0] = 0;
+namespace {
+
+// fa_fwd, and the same with a mod built into the kernel (mod_id != 0, fa_mods.h).
+int dense_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v, void* out, float* lse,
+              int batch, int seqlen_q, int seqlen_k, int heads_q, int heads_kv, int head_dim,
+              const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+              const int64_t o_strides[3], int mod_id, const FaModArgs& mod, const char* what, void* stream) {
   int rc;
   if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
   if (!q || !k || !v || !out) return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
@@ -172,6 +174,10 @@ int fa_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   memset(&p, 0, sizeof p);
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
+  if (mod_id != 0) {
+    if (softcap) return fail(FA_ERR_UNSUPPORTED, "%s: softcap is not supported together with a mod", what);
+    if ((rc = no_alibi(p, what))) return rc;
+  }
   const bool pack = resolve_pack(opts, heads_q, heads_kv);
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -188,14 +194,60 @@ int fa_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   p.g = heads_q / heads_kv;
   p.hg_count = pack ? heads_kv : heads_q;
   p.gp = pack ? p.g : 1;
+  p.mod = mod;
+  p.scale = resolve_scale(opts, head_dim);
   const int64_t rows = (int64_t)seqlen_q * p.gp;
   if (rows > (int64_t)1 << 30) return fail(FA_ERR_UNSUPPORTED, "too many rows per sequence");
   p.m_blocks = (int)((rows + FA_BLOCK_M - 1) / FA_BLOCK_M);
   p.total_tiles = (int64_t)p.m_blocks * batch * p.hg_count;
   p.persistent = 0;
-  hipError_t e = fa_launch_prefill(p, head_dim, false, false, pack, softcap, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = mod_id != 0 ? fa_launch_prefill_mod(p, head_dim, pack, mod_id, st)
+                             : fa_launch_prefill(p, head_dim, false, false, pack, softcap, st);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return FA_OK;
+}
+
+}  // namespace
+
+int fa_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v, void* out, float* lse,
+           int batch, int seqlen_q, int seqlen_k, int heads_q, int heads_kv, int head_dim,
+           const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+           const int64_t o_strides[3], void* stream) {
+  g_err[0] = 0;
+  const FaModArgs none = {nullptr, 0, 0, 0.0f};
+  return dense_fwd(opts, q, k, v, out, lse, batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim, q_strides,
+                   k_strides, v_strides, o_strides, 0, none, "fa_fwd", stream);
+}
+
+int fa_fwd_relpos_bias(const fa_attn_opts* opts, const void* q, const void* k, const void* v, void* out,
+                       float* lse, int batch, int seqlen_q, int seqlen_k, int heads_q, int heads_kv, int head_dim,
+                       const float* bias, int max_distance, const int64_t q_strides[3],
+                       const int64_t k_strides[3], const int64_t v_strides[3], const int64_t o_strides[3],
+                       void* stream) {
+  g_err[0] = 0;
+  if (!bias) return fail(FA_ERR_INVALID_ARG, "bias is NULL");
+  if ((reinterpret_cast<uintptr_t>(bias) & 3u) != 0) return fail(FA_ERR_INVALID_ARG, "bias is not 4-byte aligned");
+  if (max_distance < 0 || max_distance > (1 << 30))
+    return fail(FA_ERR_INVALID_ARG, "max_distance must lie in [0, 2^30]");
+  const FaModArgs m = {bias, 2 * (int64_t)max_distance + 1, max_distance, 0.0f};
+  return dense_fwd(opts, q, k, v, out, lse, batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim, q_strides,
+                   k_strides, v_strides, o_strides, FA_MOD_RELPOS_BIAS, m, "fa_fwd_relpos_bias", stream);
+}
+
+int fa_fwd_prefix_lm(const fa_attn_opts* opts, const void* q, const void* k, const void* v, void* out, float* lse,
+                     int batch, int seqlen_q, int seqlen_k, int heads_q, int heads_kv, int head_dim,
+                     const int32_t* prefix_lens, const int64_t q_strides[3], const int64_t k_strides[3],
+                     const int64_t v_strides[3], const int64_t o_strides[3], void* stream) {
+  g_err[0] = 0;
+  if (!prefix_lens) return fail(FA_ERR_INVALID_ARG, "prefix_lens is NULL");
+  if ((reinterpret_cast<uintptr_t>(prefix_lens) & 3u) != 0)
+    return fail(FA_ERR_INVALID_ARG, "prefix_lens is not 4-byte aligned");
+  if (opts && opts->causal)
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_prefix_lm: the prefix-LM mask replaces causal; pass causal = 0");
+  const FaModArgs m = {prefix_lens, 0, 0, 0.0f};
+  return dense_fwd(opts, q, k, v, out, lse, batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim, q_strides,
+                   k_strides, v_strides, o_strides, FA_MOD_PREFIX_LM, m, "fa_fwd_prefix_lm", stream);
 }
 
 int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const void* v, void* out,

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "fa_mods.h"
+
 // Everything one launch needs, passed by value as the kernel argument.
 struct FaParams {
   const uint16_t* q;  // bfloat16 bit patterns
@@ -51,7 +53,14 @@ struct FaParams {
   const float* alibi;
   int64_t alibi_bs;
   float alibi_inv_scale;
+  // score_mod / mask_mod of a kernel built with a mod (fa_mods.h): its
+  // parameters, and the softmax scale the mod's logits carry
+  FaModArgs mod;
+  float scale;
 };
+
+// Mods the library is built with (fa_mods.h), for fa_launch_prefill_mod.
+enum FaModId { FA_MOD_RELPOS_BIAS = 1, FA_MOD_PREFIX_LM = 2 };
 
 // FP8 (OCP e4m3) forward.  Q in blocks of FA_FP8_Q_BLOCK rows and K in blocks
 // of FA_FP8_K_BLOCK keys, one fp32 scale per (batch, head, block); V one scale
@@ -188,6 +197,8 @@ hipError_t fa_scratch_region(void** ptr);
 hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, bool pack, bool softcap,
                              hipStream_t s);
 hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t stream);
+// The dense prefill kernel built with a shipped mod (no softcap, no ALiBi).
+hipError_t fa_launch_prefill_mod(const FaParams& p, int d, bool pack, int mod_id, hipStream_t s);
 // Longest-first order of the sequences by cache length (ties by index) into
 // order[0, B); B at most FA_SEQ_ORDER_MAX.
 constexpr int FA_SEQ_ORDER_MAX = 4096;

@@ -703,8 +703,15 @@ __device__ __forceinline__ void wait_vmcnt_blocks(int n) {
 // ALIBI: the logits get the linear positional bias -slope_h |p - key| ("FA4
 // (CuTeDSL) and engineering interfaces", section 7), p the query's bottom-right
 // position: with the element mask on blocks a boundary cuts, alone on the others.
-template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false>
+// MOD: a score_mod / mask_mod (fa_mods.h) applied to every score of every key
+// block in range, before the built-in element mask ("FA4 (CuTeDSL) and
+// engineering interfaces", sections 1 and 7: the hooks sit between Q K^T and the
+// softmax); with a score_mod the scores enter the softmax in log2 units, as with
+// softcap.
+template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false, class MOD = FaNoMod>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
+  constexpr bool kMod = MOD::kScore || MOD::kMask;
+  static_assert(!(kMod && (SOFTCAP || ALIBI)), "a mod replaces softcap and ALiBi");
   constexpr int BN = FA_BLOCK_N;  // 32 keys per block
   constexpr int NBUF = 3;  // measured best of 3, 4 and 5 stages
   using G = DmaGeom<D, BN>;
@@ -718,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int kg = lane >> 5;
-  const float c = SOFTCAP ? 1.0f : p.scale_log2;
+  const float c = (SOFTCAP || MOD::kScore) ? 1.0f : p.scale_log2;
 
   LaneOffsets<D> off;
   off.init(lane, lds_addr(smem), lds_addr(smem) + NBUF * T);
@@ -890,6 +897,21 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       }
     };
     auto is_masked = [&](int i) { return n_lo + i < n_full_lo || n_lo + i >= n_full_hi; };
+    // The mod on block i: the rewritten logit in log2 units, and its mask
+    auto apply_mod = [&](f32x16& sv, int i) {
+      if constexpr (kMod) {
+        const MOD mod{};
+        const int base = (n_lo + i) * BN + 4 * kg;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int key = base + 8 * (a >> 2) + (a & 3);
+          float x = sv[a];
+          if constexpr (MOD::kScore) x = mod.score(x * p.scale, tile.b, head, mask.pos, key, p.mod) * kLog2e;
+          if constexpr (MOD::kMask) x = mod.mask(tile.b, head, mask.pos, key, p.mod) ? x : kNegInf;
+          sv[a] = x;
+        }
+      }
+    };
     // ALiBi on a block no boundary cuts: the bias alone, -k |key - pos| with
     // key - pos = fb + (a compile-time offset per slot), exact in fp32
     auto apply_bias = [&](f32x16& sv, int i) {
@@ -946,6 +968,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       stage_barrier();
       f32x16 s0 = qk_block<D, 0>(0u, qreg, off);
       transform(s0);
+      apply_mod(s0, 0);
       if (is_masked(0))
         apply_mask(s0, 0);
       else
@@ -999,6 +1022,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
       const bool late = SOFTCAP && !masked && !first;
       if (!late) {
         transform(s_next);
+        apply_mod(s_next, i + 1);
         if (masked)
           apply_mask(s_next, i + 1);
         else
@@ -2104,10 +2128,10 @@ int occupancy(K kernel) {
   return n;
 }
 
-template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false>
+template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false, class MOD = FaNoMod>
 hipError_t launch_prefill_t(const FaParams& p0, hipStream_t stream) {
   FaParams p = p0;
-  auto kern = fa_prefill_kernel<D, VARLEN, PACK, SOFTCAP, PAGED, ALIBI>;
+  auto kern = fa_prefill_kernel<D, VARLEN, PACK, SOFTCAP, PAGED, ALIBI, MOD>;
   int64_t tiles = p.total_tiles;
   if (tiles <= 0) return hipSuccess;
   int64_t grid;
@@ -2194,6 +2218,19 @@ hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, 
   FA_PF_D(128) FA_PF_D(64)
 #undef FA_PF_D
 #undef FA_PF
+  return hipErrorInvalidValue;
+}
+
+hipError_t fa_launch_prefill_mod(const FaParams& p, int d, bool pack, int mod_id, hipStream_t s) {
+#define FA_MOD(M_)                                                                         \
+  if (d == 128 && pack) return launch_prefill_t<128, false, true, false, false, false, M_>(p, s);   \
+  if (d == 128) return launch_prefill_t<128, false, false, false, false, false, M_>(p, s);          \
+  if (d == 64 && pack) return launch_prefill_t<64, false, true, false, false, false, M_>(p, s);     \
+  if (d == 64) return launch_prefill_t<64, false, false, false, false, false, M_>(p, s);            \
+  return hipErrorInvalidValue;
+  if (mod_id == FA_MOD_RELPOS_BIAS) { FA_MOD(FaRelPosBias) }
+  if (mod_id == FA_MOD_PREFIX_LM) { FA_MOD(FaPrefixLM) }
+#undef FA_MOD
   return hipErrorInvalidValue;
 }
 

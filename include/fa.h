@@ -95,6 +95,39 @@ int fa_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
            int head_dim, const int64_t q_strides[3], const int64_t k_strides[3],
            const int64_t v_strides[3], const int64_t o_strides[3], void* stream);
 
+/* Dense forward with a learned relative-position bias, the first of the two
+ * score_mod / mask_mod hooks built into the library ("FA4 ...", sections 1 and 7:
+ * a score_mod rewrites each logit after Q K^T, before the softmax; the hook is a
+ * compile-time kernel specialisation, declared in fa_mods.h).  The logit of the
+ * query at position p (token t, p = t + seqlen_k - seqlen_q) and key j becomes
+ *   softmax_scale * q.k + bias[h * (2 * max_distance + 1) + clamp(j - p, -max_distance,
+ *   max_distance) + max_distance]
+ * with bias a device float32 table [heads_q, 2 * max_distance + 1] (relative
+ * distances beyond max_distance share the end entries).  Arguments, masks and
+ * results otherwise as fa_fwd (causal and window apply; pack_gqa as fa_fwd).
+ * Errors: FA_ERR_INVALID_ARG for a NULL or misaligned bias or max_distance
+ * outside [0, 2^30]; FA_ERR_UNSUPPORTED with softcap or alibi_slopes. */
+int fa_fwd_relpos_bias(const fa_attn_opts* opts, const void* q, const void* k, const void* v,
+                       void* out, float* lse, int batch, int seqlen_q, int seqlen_k, int heads_q,
+                       int heads_kv, int head_dim, const float* bias, int max_distance,
+                       const int64_t q_strides[3], const int64_t k_strides[3],
+                       const int64_t v_strides[3], const int64_t o_strides[3], void* stream);
+
+/* Dense forward with a prefix-LM mask, the second built-in hook (a mask_mod,
+ * "FA4 ...", sections 1 and 7): the first prefix_lens[b] keys of batch b are
+ * visible to every query (a bidirectional prefix), later keys causally: key j is
+ * visible to the query at position p (= t + seqlen_k - seqlen_q) iff
+ * j < prefix_lens[b] or j <= p, intersected with the sliding window if one is set.
+ * prefix_lens: device int32 [batch] (values <= 0 give plain causal attention,
+ * values >= seqlen_k full attention).  opts->causal must be 0 (the mask replaces
+ * it; FA_ERR_INVALID_ARG otherwise).  Other arguments and results as fa_fwd.
+ * Errors as fa_fwd_relpos_bias, with prefix_lens in place of bias. */
+int fa_fwd_prefix_lm(const fa_attn_opts* opts, const void* q, const void* k, const void* v,
+                     void* out, float* lse, int batch, int seqlen_q, int seqlen_k, int heads_q,
+                     int heads_kv, int head_dim, const int32_t* prefix_lens,
+                     const int64_t q_strides[3], const int64_t k_strides[3],
+                     const int64_t v_strides[3], const int64_t o_strides[3], void* stream);
+
 /* Variable-length attention forward over packed sequences ("FA4 ...", section 4;
  * "Attention kernels ...", section 7.1).  Sequence b owns query rows
  * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows [cu_seqlens_k[b], cu_seqlens_k[b+1]);

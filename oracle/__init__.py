@@ -330,6 +330,81 @@ def visible_mask(Lq, Lk, causal, window):
     return vis
 
 
+def _masked_softmax_rows(S, vis, V):
+    """Three-pass softmax of each row of S over its visible keys, then P V.
+    Returns (O [rows, d], LSE [rows]); a row with no visible key gives 0 and -inf."""
+    S = np.where(vis, S, -np.inf)
+    m = S.max(axis=1, keepdims=True)
+    ok = np.isfinite(m[:, 0])
+    E = np.exp(S - np.where(np.isfinite(m), m, 0.0))
+    l = E.sum(axis=1)
+    O = np.zeros((S.shape[0], V.shape[1]))
+    L = np.full(S.shape[0], -np.inf)
+    O[ok] = (E[ok] / l[ok, None]) @ V
+    L[ok] = m[ok, 0] + np.log(l[ok])
+    return O, L
+
+
+def fwd_dense_relpos(q, k, v, bias, *, scale=None, causal=False, window=None, rows=None):
+    """Attention with a learned relative-position bias, a score_mod ("FA4 (CuTeDSL) and
+    engineering interfaces", sections 1 and 7: a function that rewrites each logit after
+    Q K^T and before the softmax): the logit of the query at position p_i = i + Lk - Lq
+    and key j is scale q_i . k_j + bias[h, clamp(j - p_i, -R, R) + R] for a table of
+    2R + 1 entries per query head; then the usual masked softmax.  fp64 with S and P
+    materialised, in numpy.
+
+    q: bf16 bits [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; bias: float [Hq, 2R + 1].
+    rows: None, or a list of query rows (O and LSE hold those rows only).
+    Returns (O float64 [B, rows, Hq, d], LSE float64 [B, Hq, rows])."""
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    B, Nq, Hq, d = qd.shape
+    Nk, Hkv = kd.shape[1], kd.shape[2]
+    g = Hq // Hkv
+    s = _scale(scale, d)
+    tb = np.asarray(bias, dtype=np.float64)
+    R = (tb.shape[1] - 1) // 2
+    sel = np.arange(Nq) if rows is None else np.asarray(rows)
+    vis = visible_mask(Nq, Nk, causal, window)[sel]
+    rel = np.clip(np.arange(Nk)[None, :] - (sel[:, None] + (Nk - Nq)), -R, R) + R
+    O = np.zeros((B, len(sel), Hq, d))
+    L = np.full((B, Hq, len(sel)), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            S = s * (qd[b, sel, h] @ kd[b, :, h // g].T) + tb[h][rel]
+            O[b, :, h], L[b, h] = _masked_softmax_rows(S, vis, vd[b, :, h // g])
+    return O, L
+
+
+def prefix_lm_visible(Lq, Lk, prefix, window=None):
+    """visible[i, j] of the prefix-LM mask, a mask_mod ("FA4 (CuTeDSL) and engineering
+    interfaces", sections 1 and 7): the first `prefix` keys are visible to every query,
+    later keys causally (j <= p_i, p_i = i + Lk - Lq), intersected with the window and
+    with 0 <= j < Lk."""
+    pos = np.arange(Lq)[:, None] + (Lk - Lq)
+    j = np.arange(Lk)[None, :]
+    vis = (j < prefix) | (j <= pos)
+    return vis & visible_mask(Lq, Lk, False, window)
+
+
+def fwd_dense_prefix_lm(q, k, v, prefix_lens, *, scale=None, window=None, rows=None):
+    """Attention under the prefix-LM mask (prefix_lm_visible, prefix_lens [B]); otherwise
+    as fwd_dense_relpos without a bias.  fp64, S and P materialised, in numpy."""
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    B, Nq, Hq, d = qd.shape
+    Nk, Hkv = kd.shape[1], kd.shape[2]
+    g = Hq // Hkv
+    s = _scale(scale, d)
+    sel = np.arange(Nq) if rows is None else np.asarray(rows)
+    O = np.zeros((B, len(sel), Hq, d))
+    L = np.full((B, Hq, len(sel)), -np.inf)
+    for b in range(B):
+        vis = prefix_lm_visible(Nq, Nk, int(prefix_lens[b]), window)[sel]
+        for h in range(Hq):
+            S = s * (qd[b, sel, h] @ kd[b, :, h // g].T)
+            O[b, :, h], L[b, h] = _masked_softmax_rows(S, vis, vd[b, :, h // g])
+    return O, L
+
+
 def bwd_dense(q, k, v, dout, *, scale=None, causal=False, window=None, heads=None):
     """Gradients of the attention forward, in fp64 with S and P materialised.
 

@@ -129,6 +129,24 @@ def test_fwd_rejects_null_opts_and_bad_softcap():
     assert call_fwd(opts=_opts(softcap=float("nan"))) == FA_ERR_INVALID_ARG
 
 
+def test_mod_entry_points_reject_invalid_arguments():
+    L = api.lib()
+    def relpos(opts=None, bias=FAKE, R=8):
+        return L.fa_fwd_relpos_bias(ctypes.byref(opts or _opts()), FAKE, FAKE, FAKE, FAKE, None, 1, 16, 16, 16, 16,
+                                    128, bias, R, S3, S3, S3, S3, None)
+    def prefix(opts=None, pl=FAKE, d=128):
+        return L.fa_fwd_prefix_lm(ctypes.byref(opts or _opts()), FAKE, FAKE, FAKE, FAKE, None, 1, 16, 16, 16, 16,
+                                  d, pl, S3, S3, S3, S3, None)
+    assert relpos(bias=None) == FA_ERR_INVALID_ARG
+    assert relpos(R=-1) == FA_ERR_INVALID_ARG
+    assert relpos(bias=ctypes.c_void_p(0x1002)) == FA_ERR_INVALID_ARG
+    assert relpos(opts=_opts(softcap=30.0)) == FA_ERR_UNSUPPORTED
+    assert prefix(pl=None) == FA_ERR_INVALID_ARG
+    assert prefix(opts=_opts(causal=1)) == FA_ERR_INVALID_ARG       # the mask replaces causal
+    assert prefix(d=96) == FA_ERR_UNSUPPORTED
+    assert prefix(opts=_opts(softcap=30.0)) == FA_ERR_UNSUPPORTED
+
+
 def test_varlen_rejects_invalid_arguments():
     L = api.lib()
     o = _opts()

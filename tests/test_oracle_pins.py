@@ -665,6 +665,99 @@ def test_alibi_zero_slopes_is_the_c_oracle_and_zero_queries_give_a_geometric_ser
         np.testing.assert_allclose(Lz[0, h], want, rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- score_mod / mask_mod hooks
+def _sdpa_heads(q, k, v, Hq, Hkv):
+    Q = torch.tensor(v_double(q)).permute(0, 2, 1, 3)
+    K = torch.tensor(v_double(k)).repeat_interleave(Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+    V = torch.tensor(v_double(v)).repeat_interleave(Hq // Hkv, dim=2).permute(0, 2, 1, 3)
+    return Q, K, V
+
+
+@pytest.mark.parametrize("causal,window,Nq,Nk,R", [(True, None, 40, 40, 8), (False, None, 33, 47, 5),
+                                                   (True, (9, 0), 50, 50, 20), (False, (6, 5), 31, 31, 0),
+                                                   (True, None, 20, 35, 64)])
+def test_relpos_bias_matches_sdpa_with_an_additive_mask(causal, window, Nq, Nk, R):
+    """The relative-position score_mod against torch fp64 scaled_dot_product_attention with
+    the bias gathered by torch indexing (and -inf for the mask) as a float attention mask."""
+    g = W.generator(601 + Nq + R)
+    B, Hq, Hkv, d = 2, 4, 2, 16
+    q = W.randn_bf16(g, (B, Nq, Hq, d))
+    k, v = W.randn_bf16(g, (B, Nk, Hkv, d)), W.randn_bf16(g, (B, Nk, Hkv, d))
+    table = torch.randn(Hq, 2 * R + 1, generator=torch.Generator().manual_seed(R), dtype=torch.float64) * 2
+    O, L = oracle.fwd_dense_relpos(bits(q), bits(k), bits(v), table.numpy(), causal=causal, window=window)
+    vis = torch.as_tensor(oracle.visible_mask(Nq, Nk, causal, window))
+    pos = torch.arange(Nq)[:, None] + (Nk - Nq)
+    idx = (torch.arange(Nk)[None, :] - pos).clamp(-R, R) + R            # [Nq, Nk]
+    bias = table[:, idx].unsqueeze(0).expand(B, Hq, Nq, Nk).masked_fill(~vis, float("-inf"))
+    Q, K, V = _sdpa_heads(q, k, v, Hq, Hkv)
+    ref = F.scaled_dot_product_attention(Q, K, V, attn_mask=bias, scale=d ** -0.5).permute(0, 2, 1, 3)
+    lse = torch.logsumexp(d ** -0.5 * Q @ K.transpose(-1, -2) + bias, dim=-1)
+    np.testing.assert_allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, lse.numpy(), rtol=0, atol=1e-12)
+
+
+def test_relpos_constant_table_shifts_the_lse_and_a_spike_selects_one_key():
+    """A constant table c leaves O as plain attention and adds c to the LSE (softmax is
+    shift-invariant); a table that is 0 except +200 at relative distance delta gives each
+    row whose key p + delta is visible O = v of that key (the others weigh e^-200 or less)."""
+    g = W.generator(621)
+    B, N, H, d, R = 1, 45, 2, 16, 12
+    q, k, v = (W.randn_bf16(g, (B, N, H, d)) for _ in range(3))
+    Oc, Lc = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=True)
+    O, L = oracle.fwd_dense_relpos(bits(q), bits(k), bits(v), np.full((H, 2 * R + 1), 3.25), causal=True)
+    np.testing.assert_allclose(O, Oc, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, Lc + 3.25, rtol=0, atol=1e-12)
+    delta = -5
+    table = np.zeros((H, 2 * R + 1))
+    table[:, delta + R] = 200.0
+    O, _ = oracle.fwd_dense_relpos(bits(q), bits(k), bits(v), table, causal=True)
+    vd = v_double(v)
+    for i in range(-delta, N):
+        np.testing.assert_allclose(O[0, i], vd[0, i + delta], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("prefix,window,Nq,Nk", [((0, 7), None, 40, 40), ((13, 50), None, 33, 47),
+                                                  ((25, 3), (9, 4), 50, 50), ((31, 100), None, 31, 31)])
+def test_prefix_lm_matches_sdpa_with_a_boolean_mask(prefix, window, Nq, Nk):
+    """The prefix-LM mask_mod against torch fp64 SDPA with a boolean mask built from the
+    rule (key j visible iff j < prefix or j <= p) by torch comparisons."""
+    g = W.generator(641 + Nq)
+    B, Hq, Hkv, d = 2, 4, 1, 16
+    q = W.randn_bf16(g, (B, Nq, Hq, d))
+    k, v = W.randn_bf16(g, (B, Nk, Hkv, d)), W.randn_bf16(g, (B, Nk, Hkv, d))
+    O, L = oracle.fwd_dense_prefix_lm(bits(q), bits(k), bits(v), np.array(prefix), window=window)
+    Q, K, V = _sdpa_heads(q, k, v, Hq, Hkv)
+    pos = torch.arange(Nq)[:, None] + (Nk - Nq)
+    j = torch.arange(Nk)[None, :]
+    for b in range(B):
+        m = (j < prefix[b]) | (j <= pos)
+        if window is not None:
+            m &= (j >= pos - window[0]) & (j <= pos + window[1])
+        ref = F.scaled_dot_product_attention(Q[b:b + 1], K[b:b + 1], V[b:b + 1], attn_mask=m,
+                                             scale=d ** -0.5).permute(0, 2, 1, 3)
+        sc = (d ** -0.5 * Q[b:b + 1] @ K[b:b + 1].transpose(-1, -2)).masked_fill(~m, float("-inf"))
+        np.testing.assert_allclose(O[b:b + 1], ref.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L[b:b + 1], torch.logsumexp(sc, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_prefix_lm_reduces_to_causal_and_to_full_attention_and_counts_keys():
+    """prefix 0 is causal attention, a prefix covering every key is full attention (both the
+    C oracle), and with Q = 0 every visible key weighs 1: exp(LSE) = max(prefix, p + 1) keys."""
+    g = W.generator(661)
+    B, N, H, d = 1, 37, 2, 16
+    q, k, v = (W.randn_bf16(g, (B, N, H, d)) for _ in range(3))
+    for P, causal in ((0, True), (N, False), (N + 9, False)):
+        O, L = oracle.fwd_dense_prefix_lm(bits(q), bits(k), bits(v), np.array([P]))
+        Oc, Lc = oracle.fwd_dense(bits(q), bits(k), bits(v), causal=causal)
+        np.testing.assert_allclose(O, Oc, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L, Lc, rtol=0, atol=1e-12)
+    z = torch.zeros(B, N, H, d, dtype=torch.bfloat16)
+    for P in (0, 5, 20, 37):
+        _, Lz = oracle.fwd_dense_prefix_lm(bits(z), bits(k), bits(v), np.array([P]))
+        want = np.log(np.maximum(P, np.arange(N) + 1).clip(max=N).astype(np.float64))
+        np.testing.assert_allclose(Lz[0, 0], want, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- brute force
 import struct  # noqa: E402
 
