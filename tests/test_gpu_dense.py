@@ -168,6 +168,38 @@ def test_needle_probe(causal, window, softcap, N, jstar):
         np.testing.assert_allclose(lse[0, h].numpy()[~vis], np.log(counts[~vis]), atol=1e-5)
 
 
+def test_local_softcap_full_size_window_edge_needles():
+    """The long-context workload's shape (1 x 32768 x 32 heads, d = 128, causal, window
+    (4096, 0), softcap 30): K = 0 except one needle per head (logit ~90, ~29.85 after the
+    softcap) at a tile or window edge.  Every row i returns V[j*] bitwise iff
+    j* <= i <= j* + 4096 (rows j* + 4096 see it, j* + 4097 no longer), and a row that
+    does not see it has exp(LSE) = min(i, 4096) + 1 keys of weight 1."""
+    c = W.WORKLOADS["local_softcap_n32768_h32_d128_w4096_cap30"]
+    B, N, H, d = c["B"], c["N"], c["Hq"], c["d"]
+    wl = c["window"][0]
+    stars = [0, 1, 31, 32, 63, 64, 127, 128, 129, 4095, 4096, 4097, 8191, 8192, 12345, 16383,
+             16384, 20000, 24575, 24576, 28671, 28672, 28673, 30000, 32000, 32735, 32736, 32737,
+             32766, 32767, 4000, 100]
+    assert len(stars) == H
+    q = torch.zeros(B, N, H, d, dtype=torch.bfloat16, device=DEV)
+    q[..., 0] = 1.0
+    k = torch.zeros_like(q)
+    for h, j in enumerate(stars):
+        k[0, j, h, 0] = 1016.0
+    v = W.randn_bf16(W.generator(c["seed"], DEV), (B, N, H, d), c["mult"], DEV)
+    out, lse = api.fa_fwd(q, k, v, causal=True, window=c["window"], softcap=c["softcap"])
+    torch.cuda.synchronize()
+    i = torch.arange(N, device=DEV)
+    count = torch.clamp(i, max=wl) + 1
+    for h, j in enumerate(stars):
+        vis = (i >= j) & (i <= j + wl)
+        eq = (out[0, :, h].view(torch.int16) == v[0, j, h].view(torch.int16)).all(dim=-1)
+        assert torch.equal(eq, vis), f"head {h}, needle {j}"
+        assert bool((lse[0, h][vis] > 20).all())
+        lse_off = lse[0, h][~vis].double()
+        assert torch.allclose(lse_off, torch.log(count[~vis].double()), atol=1e-5, rtol=0), f"head {h}"
+
+
 # ---------------------------------------------------------------- full sizes, sampled rows
 @pytest.mark.parametrize("name", ["prefill_b4_h16_n4096_d128_causal",
                                   "local_softcap_n32768_h32_d128_w4096_cap30"])

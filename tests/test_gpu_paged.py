@@ -196,11 +196,28 @@ def _c4():
     return c, t
 
 
+def _poison_pool_on_device(t, page):
+    """NaN into every slot of the (device) pool that no sequence refers to: whole unreferenced
+    pages and the tail slots of each sequence's last page, in place."""
+    kc, vc = t["k_cache"], t["v_cache"]
+    live = torch.zeros(kc.shape[0], page, dtype=torch.bool, device=kc.device)
+    bt = t["block_table"].to(kc.device).long()
+    for b, L in enumerate(t["cache_seqlens"].tolist()):
+        n = (L + page - 1) // page
+        live[bt[b, :n]] = True
+        tail = L - (n - 1) * page
+        live[bt[b, n - 1], tail:] = False
+    kc[~live] = float("nan")
+    vc[~live] = float("nan")
+    return live
+
+
 @pytest.mark.parametrize("num_splits", [1, 4, 16])
 def test_paged_full_size(num_splits):
     """Every row of the full decode workload against the oracle; the oracle reads a
     compacted copy of the live pages (same bytes, table renumbered)."""
     c, t = _c4()
+    _poison_pool_on_device(t, c["page"])     # unreferenced pages and tail slots are NaN
     bt = t["block_table"].to(DEV)
     sl = t["cache_seqlens"].to(DEV)
     out, lse = api.fa_fwd_kvcache_paged(t["q"], t["k_cache"], t["v_cache"], bt, sl,
@@ -226,6 +243,38 @@ def test_paged_full_size(num_splits):
     torch.cuda.synchronize()
     got = torch.round(torch.exp(lse0.double())).long().cpu()
     assert torch.equal(got, torch.as_tensor(lens).long().view(-1, 1, 1).expand_as(got))
+
+
+@pytest.mark.parametrize("num_splits", [1, 4, 16])
+def test_paged_full_size_page_edge_needles(num_splits):
+    """The full decode workload's 4 GiB pool (NaN in every slot no sequence refers to), K = 0
+    on the live slots except one needle per (sequence, KV head) at a page edge or sequence end
+    (logical keys 0, 255, 256, 257, 511, 512 and L - 1), written at the physical slot the
+    block table gives.  Each query head must return its own KV head's needle value bitwise:
+    the table lookup, the page edges, the split boundaries and the GQA head map, exactly."""
+    c, t = _c4()
+    page, Hkv, g = c["page"], c["Hkv"], c["Hq"] // c["Hkv"]
+    live = _poison_pool_on_device(t, page)
+    kc, vc = t["k_cache"], t["v_cache"]
+    kc[live] = 0.0
+    q = torch.zeros_like(t["q"])
+    q[..., 0] = 1.0
+    lens = t["cache_seqlens"].tolist()
+    bt = t["block_table"]
+    want = torch.empty(c["B"], Hkv, c["d"], dtype=torch.bfloat16, device=DEV)
+    for b, L in enumerate(lens):
+        for kvh in range(Hkv):
+            cand = [x for x in (0, 255, 256, 257, 511, 512, L - 1) if x < L]
+            ts = cand[(b + kvh) % len(cand)]
+            phys, slot = int(bt[b, ts // page]), ts % page
+            kc[phys, slot, kvh, 0] = 1016.0
+            want[b, kvh] = vc[phys, slot, kvh]
+    out, lse = api.fa_fwd_kvcache_paged(q, kc, vc, bt.to(DEV), t["cache_seqlens"].to(DEV),
+                                        num_splits=num_splits, causal=True, softmax_scale=128 ** -0.5)
+    torch.cuda.synchronize()
+    exp = want.repeat_interleave(g, dim=1)                      # [B, Hq, d]
+    assert torch.equal(out[:, 0].view(torch.int16), exp.view(torch.int16))
+    assert bool((lse[:, :, 0] > 20).all())
 
 
 # ---------------------------------------------------------------- chunked prefill
