@@ -173,19 +173,3 @@ def fwd(q, q_scales, q_block, k, k_scales, k_block, v, v_scales, *, scale=None, 
                 A[b, ok, h] = (E[ok] / l[ok, None]) @ np.abs(vd[b, :, h // g])
             L[b, h, ok] = m[ok, 0] + np.log(l[ok])
     return (O, L, A) if with_abs else (O, L)
-
-
-def probs(q, q_scales, q_block, k, k_scales, k_block, *, row, b, h, g, scale=None, causal=False,
-          window=None):
-    """fp64 softmax weights of one query row (batch b, query head h) over all keys."""
-    qd = dequantize(q, q_scales, q_block)
-    kd = dequantize(k, k_scales, k_block)
-    Nq, d = qd.shape[1], qd.shape[3]
-    Nk = kd.shape[1]
-    s = d ** -0.5 if scale is None else scale
-    S = s * (kd[b, :, h // g] @ qd[b, row, h])
-    S = np.where(_visible(Nq, Nk, causal, window)[row], S, -np.inf)
-    if not np.isfinite(S.max()):
-        return np.zeros(Nk)
-    E = np.exp(S - S.max())
-    return E / E.sum()

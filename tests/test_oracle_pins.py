@@ -616,8 +616,6 @@ def test_fp8_attention_matches_the_bf16_oracle_on_exact_inputs(causal, window, H
     rows = [0, 33, 69]
     Or, Lr = F8.fwd(q8, qs, 64, k8, ks, 64, v8, vs, causal=causal, window=window, rows=rows)
     assert np.array_equal(Or, O[:, rows]) and np.array_equal(Lr, L[:, :, rows])
-    p = F8.probs(q8, qs, 64, k8, ks, 64, row=50, b=1, h=Hq - 1, g=Hq // Hkv, causal=causal, window=window)
-    assert abs(p.sum() - 1) < 1e-12
 
 
 # ---------------------------------------------------------------- alibi
