@@ -631,8 +631,10 @@ __device__ bool varlen_tile(const FaParams& p, int64_t t, int lane, TileId* out)
       const bool mine = f && __popcll(below) == idx;
       const uint64_t sel = __ballot(mine);
       const int src = __ffsll((long long)sel) - 1;
-      out->b = b0 + src;
-      out->mb = __shfl(m, src);
+      // wave-uniform by construction; made scalar so that everything derived
+      // from the tile (bounds, loop counts, addresses) stays in scalar registers
+      out->b = __builtin_amdgcn_readfirstlane(b0 + src);
+      out->mb = __builtin_amdgcn_readfirstlane(__shfl(m, src));
       return true;
     }
     idx -= cnt;
@@ -750,11 +752,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     int64_t q_start = 0, k_start = 0;
     int Lq = p.Nq, Lk = p.Nk;
     if (VARLEN) {
-      q_start = p.cu_q[tile.b];
-      Lq = p.cu_q[tile.b + 1] - (int)q_start;
+      q_start = scalar_load_i32(p.cu_q + tile.b);
+      Lq = scalar_load_i32(p.cu_q + tile.b + 1) - (int)q_start;
       if (!PAGED) {
-        k_start = p.cu_k[tile.b];
-        Lk = p.cu_k[tile.b + 1] - (int)k_start;
+        k_start = scalar_load_i32(p.cu_k + tile.b);
+        Lk = scalar_load_i32(p.cu_k + tile.b + 1) - (int)k_start;
       }
     }
     if (PAGED) Lk = scalar_load_i32(p.cache_seqlens + tile.b);
@@ -767,18 +769,20 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     span.pos_hi = (int64_t)((m_end - 1) / p.gp) + (Lk - Lq);
     int n_lo, n_hi;
     fa_key_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &n_lo, &n_hi);
-    // key blocks [n_full_lo, n_full_hi) need no element mask
+    // key blocks [n_full_lo, n_full_hi) need no element mask: the closed-form
+    // range of tiles the classifier calls full (one interval, checked against the
+    // classifier on the host), within [n_lo, n_hi)
     int n_full_lo = n_hi, n_full_hi = n_hi;
-    for (int n = n_lo; n < n_hi; ++n)
-      if (!(fa_tile_class(span, Lk, p.causal, p.wl, p.wr, BN, n) & (FA_TILE_MASK_LEFT | FA_TILE_MASK_RIGHT))) {
-        n_full_lo = n;
-        break;
+    {
+      int f_lo, f_hi;
+      fa_full_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &f_lo, &f_hi);
+      f_lo = max(f_lo, n_lo);
+      f_hi = min(f_hi, n_hi);
+      if (f_lo < f_hi) {
+        n_full_lo = f_lo;
+        n_full_hi = f_hi;
       }
-    for (int n = n_full_lo; n < n_hi; ++n)
-      if (fa_tile_class(span, Lk, p.causal, p.wl, p.wr, BN, n) & (FA_TILE_MASK_LEFT | FA_TILE_MASK_RIGHT)) {
-        n_full_hi = n;
-        break;
-      }
+    }
     const int nb = n_hi - n_lo;
 
     // ---- this lane's query row
