@@ -378,7 +378,8 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
     return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
   if ((rc = check_strides("q", q, q_strides, 2)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
-      (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 2)))
+      (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 2)) ||
+      (rc = check_token_stride("k_cache", k_strides[1])) || (rc = check_token_stride("v_cache", v_strides[1])))
     return rc;
   const size_t need = fa_varlen_paged_workspace_size(batch, heads_kv, head_dim, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -444,14 +445,13 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
       pd.seq_order = order;
     }
   }
-  hipError_t e = fa_launch_paged(pd, head_dim, softcap, s);
-  if (e != hipSuccess) return hip_fail(e, "varlen paged decode launch");
+  // decode units and prefill tiles in one launch, then the decode splits' merge
+  hipError_t e = fa_launch_unified(pd, p, head_dim, pack, softcap, s);
+  if (e != hipSuccess) return hip_fail(e, "unified varlen paged launch");
   if (num_splits > 1) {
     e = fa_launch_combine_packed(pd, head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "varlen paged combine launch");
   }
-  e = fa_launch_prefill(p, head_dim, true, true, pack, softcap, s);
-  if (e != hipSuccess) return hip_fail(e, "varlen paged launch");
   return FA_OK;
 }
 
@@ -492,7 +492,8 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
   if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
     return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
   if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
-      (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)))
+      (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)) ||
+      (rc = check_token_stride("k_cache", k_strides[1])) || (rc = check_token_stride("v_cache", v_strides[1])))
     return rc;
   const int g = heads_q / heads_kv;
   if (num_splits == 0)

@@ -197,6 +197,10 @@ hipError_t fa_scratch_region(void** ptr);
 hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, bool pack, bool softcap,
                              hipStream_t s);
 hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t stream);
+// The unified varlen batch over a paged cache in one launch: pp's prefill tiles
+// first, then pd's decode units (B * Hkv * num_splits workgroups).
+hipError_t fa_launch_unified(const FaParams& pd, const FaParams& pp, int d, bool pack, bool softcap,
+                             hipStream_t s);
 // The dense prefill kernel built with a shipped mod (no softcap, no ALiBi).
 hipError_t fa_launch_prefill_mod(const FaParams& p, int d, bool pack, int mod_id, hipStream_t s);
 // Longest-first order of the sequences by cache length (ties by index) into

@@ -710,17 +710,26 @@ __device__ __forceinline__ void wait_vmcnt_blocks(int n) {
 // engineering interfaces", sections 1 and 7: the hooks sit between Q K^T and the
 // softmax); with a score_mod the scores enter the softmax in log2 units, as with
 // softcap.
+constexpr int kPrefillStages = 3;  // measured best of 3, 4 and 5 stages
+template <int D>
+constexpr int prefill_smem_bytes() {
+  return 2 * kPrefillStages * DmaGeom<D, FA_BLOCK_N>::kTensorBytes;
+}
+
+// The prefill work of one workgroup: tile bid of a grid of `grid` workgroups
+// (or, persistent, every grid-th tile from bid), with its K/V stages in smem
+// (prefill_smem_bytes<D>(), 1 KiB aligned).  The kernel below and the unified
+// prefill + decode kernel call it.
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false, class MOD = FaNoMod>
-__global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
+__device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int bid, int grid) {
   constexpr bool kMod = MOD::kScore || MOD::kMask;
   static_assert(!(kMod && (SOFTCAP || ALIBI)), "a mod replaces softcap and ALiBi");
   constexpr int BN = FA_BLOCK_N;  // 32 keys per block
-  constexpr int NBUF = 3;  // measured best of 3, 4 and 5 stages
+  constexpr int NBUF = kPrefillStages;
   using G = DmaGeom<D, BN>;
   constexpr int T = G::kTensorBytes;  // one tensor of one block
   static_assert(NBUF * T <= 65536, "stage offsets must fit the LDS immediate offset");
   // K stages in the lower half, V stages in the upper half
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NBUF * T];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -737,9 +746,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
   const int v_src = (dma_pc ^ v_swz<D>(dma_row)) * 8;
 
-  const int G_ = gridDim.x;
+  const int G_ = grid;
   for (int64_t round = 0;; ++round) {
-    const int64_t t = p.persistent ? tile_index(round, blockIdx.x, G_) : (round == 0 ? (int64_t)blockIdx.x : -1);
+    const int64_t t = p.persistent ? tile_index(round, bid, G_) : (round == 0 ? (int64_t)bid : -1);
     if (t < 0) break;
     TileId tile;
     if (VARLEN) {
@@ -819,6 +828,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
     const uint32_t k_voff = (uint32_t)(dma_row * p.k_ss + k_src) * 2u;
     const uint32_t v_voff = (uint32_t)(dma_row * p.v_ss + v_src) * 2u;
     const uint32_t k_step = (uint32_t)(G::kRowStep * p.k_ss) * 2u, v_step = (uint32_t)(G::kRowStep * p.v_ss) * 2u;
+    // paged: the lane's row within its instruction's kRowsPerKiB rows, and chunk
+    const uint32_t kp_voff = (uint32_t)((lane / G::kChunksPerRow) * p.k_ss + k_src) * 2u;
+    const uint32_t vp_voff = (uint32_t)((lane / G::kChunksPerRow) * p.v_ss + v_src) * 2u;
     // block i of this tile (key block n_lo + i) goes to buffer i % NBUF
     auto issue = [&](int i) {
       char* dst = smem + (i % NBUF) * T + wave * 1024;
@@ -827,6 +839,24 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
         // Keys past the last one are clamped to it; a clamped instruction's rows
         // then all lie in the last key's page.
         const int32_t* bt = p.block_table + (int64_t)tile.b * p.max_blocks;
+        // (the unified varlen form keeps the per-lane addresses: measured 6 % faster
+        // there, 2.5 % slower for chunked prefill)
+        if (!VARLEN && n0 + BN <= Lk) {
+          // a full block: the instruction's rows are consecutive keys of one page,
+          // addressed from the page's row (scalar) plus the lane's row offset
+#pragma unroll
+          for (int j = 0; j < G::kInstPerWave; ++j) {
+            const int first = n0 + wave * G::kRowsPerKiB + j * G::kRowStep;
+            const int pg = first / p.page;
+            const int64_t phys = scalar_load_i32(bt + pg);
+            const int slot0 = first - pg * p.page;
+            dma16_buf(buf_rsrc(p.k + phys * p.k_bs + (int64_t)slot0 * p.k_ss + (int64_t)kvh * p.k_hs), kp_voff, 0u,
+                      dst + j * 4096);
+            dma16_buf(buf_rsrc(p.v + phys * p.v_bs + (int64_t)slot0 * p.v_ss + (int64_t)kvh * p.v_hs), vp_voff, 0u,
+                      dst + NBUF * T + j * 4096);
+          }
+          return;
+        }
 #pragma unroll
         for (int j = 0; j < G::kInstPerWave; ++j) {
           const int first = n0 + wave * G::kRowsPerKiB + j * G::kRowStep;  // first row of the instruction
@@ -1133,6 +1163,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   }
 }
 
+template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false, class MOD = FaNoMod>
+__global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[prefill_smem_bytes<D>()];
+  prefill_body<D, VARLEN, PACK, SOFTCAP, PAGED, ALIBI, MOD>(p, smem, blockIdx.x, gridDim.x);
+}
+
 // ------------------------------------------------------------------ sequence order
 // Rank of each sequence by cache length, longest first, ties by index: a strict
 // total order, so order[] receives a permutation of [0, B).  Each thread ranks
@@ -1166,18 +1202,26 @@ __global__ __launch_bounds__(kThreads) void fa_seq_order_kernel(const int32_t* l
 // the page size is a multiple of the stage, a stage lies in one page and its
 // physical page is one scalar block-table read; otherwise every row looks its
 // page up.
+constexpr int kPagedStages = 2;  // stages in the paged kernel's ring
+// LDS of the paged decode workgroup: the stage ring, reused after the loop for
+// the merge of the four waves' states: O [4][32][D] fp32, then m, l and l (bf16
+// weights) [3][4][32]
+template <int D>
+constexpr int paged_smem_bytes() {
+  constexpr int kStage = 2 * DmaGeom<D, FA_PAGED_STAGE>::kTensorBytes;
+  constexpr int kMerge = 4 * 32 * D * 4 + 3 * 4 * 32 * 4;
+  return kPagedStages * kStage > kMerge ? kPagedStages * kStage : kMerge;
+}
+
+// The decode work of one workgroup: unit `unit` = (sequence, KV head, split),
+// LDS in smem (paged_smem_bytes<D>(), 1 KiB aligned).
 template <int D, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
+__device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int unit) {
   constexpr int NK = FA_PAGED_STAGE;
-  constexpr int NS = 2;  // stages in the ring
+  constexpr int NS = kPagedStages;
   using G = DmaGeom<D, NK>;
   constexpr int kStage = 2 * G::kTensorBytes;
   static_assert(NK == 4 * 16, "four waves of 16 keys per stage");
-  // the stage ring, reused after the loop for the merge of the four waves'
-  // states: O [4][32][D] fp32, then m, l and l (bf16 weights) [3][4][32]
-  constexpr int kMerge = 4 * 32 * D * 4 + 3 * 4 * 32 * 4;
-  constexpr int kSmem = NS * kStage > kMerge ? NS * kStage : kMerge;
-  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1205,7 +1249,6 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
   }
 
   const int S = p.num_splits;
-  const int unit = blockIdx.x;
   // groups of Hkv * S workgroups take the sequences longest first when an order
   // is given, so that the short ones fill the end of the grid
   const int b = p.seq_order ? scalar_load_i32(p.seq_order + unit / (p.Hkv * S)) : unit / (p.Hkv * S);
@@ -1427,6 +1470,30 @@ __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
       if (d0 == 0) p.lse_part[(int64_t)split * rows_all + r] = lse;
     }
   }
+}
+
+template <int D, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[paged_smem_bytes<D>()];
+  paged_body<D, SOFTCAP>(p, smem, blockIdx.x);
+}
+
+// ------------------------------------------------------------------ unified batch
+// One launch for a mixed batch over a paged cache ("Attention kernels...",
+// section 5.1): the first n_tiles workgroups are the prefill tiles of the
+// sequences with many packed rows (prefill_body, longest first), the last ones
+// the decode units of the others (paged_body), so that the short HBM-bound
+// decode workgroups fill the machine beside the last MFMA-bound tiles instead
+// of running before or after them.
+template <int D, bool PACK, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void fa_unified_kernel(FaParams pd, FaParams pp, int n_tiles) {
+  constexpr int kA = prefill_smem_bytes<D>(), kB = paged_smem_bytes<D>();
+  __shared__ __attribute__((aligned(1024))) char smem[kA > kB ? kA : kB];
+  const int bid = blockIdx.x;
+  if (bid < n_tiles)
+    prefill_body<D, true, PACK, SOFTCAP, true>(pp, smem, bid, n_tiles);
+  else
+    paged_body<D, SOFTCAP>(pd, smem, bid - n_tiles);
 }
 
 // ------------------------------------------------------------------ combine kernel
@@ -2222,6 +2289,24 @@ hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, 
   FA_PF_D(128) FA_PF_D(64)
 #undef FA_PF_D
 #undef FA_PF
+  return hipErrorInvalidValue;
+}
+
+hipError_t fa_launch_unified(const FaParams& pd, const FaParams& pp, int d, bool pack, bool softcap,
+                             hipStream_t s) {
+  const int64_t nd = (int64_t)pd.B * pd.Hkv * pd.num_splits;
+  const int64_t grid = nd + pp.total_tiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+#define FA_UN(D_, P_, S_)                                                                                  \
+  if (d == D_ && pack == P_ && softcap == S_) {                                                         \
+    hipLaunchKernelGGL((fa_unified_kernel<D_, P_, S_>), dim3((unsigned)grid), dim3(kThreads), 0, s, pd, pp, \
+                       (int)pp.total_tiles);                                                             \
+    return hipGetLastError();                                                                            \
+  }
+  FA_UN(128, true, false) FA_UN(128, true, true) FA_UN(128, false, false) FA_UN(128, false, true)
+  FA_UN(64, true, false) FA_UN(64, true, true) FA_UN(64, false, false) FA_UN(64, false, true)
+#undef FA_UN
   return hipErrorInvalidValue;
 }
 

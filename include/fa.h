@@ -24,9 +24,9 @@
  *                           that is not a multiple of 16 ("Attention kernels
  *                           ...", section 6.1: pages of 16-multiple tokens);
  *       FA_ERR_UNSUPPORTED  a head_dim other than 64 or 128, a K or V token
- *                           stride of 2^25 elements or more (fa_fwd,
- *                           fa_fwd_varlen), or a shape the kernels do not cover
- *                           (stated per entry point);
+ *                           (or cache slot) stride of 2^25 elements or more,
+ *                           or a shape the kernels do not cover (stated per
+ *                           entry point);
  *       FA_ERR_HIP          a HIP runtime error while launching.
  *     fa_last_error() returns a message for the calling thread's last failure.
  *   - Rows that see no key at all get O = 0 and LSE = -inf (no NaN).
