@@ -693,10 +693,15 @@ int fa_rotary(void* x, int batch, int seqlen, int heads, int head_dim, const int
   return FA_OK;
 }
 
-size_t fa_bwd_workspace_size(int batch, int seqlen_q, int heads_q) {
-  if (batch <= 0 || seqlen_q <= 0 || heads_q <= 0) return 0;
+// D and the scaled LSE, one fp32 each per query row, each array rounded up to 256
+static size_t bwd_row_bytes(int batch, int seqlen_q, int heads_q) {
   const size_t bytes = (size_t)batch * heads_q * seqlen_q * 4;
   return (bytes + 255) & ~(size_t)255;
+}
+
+size_t fa_bwd_workspace_size(int batch, int seqlen_q, int heads_q) {
+  if (batch <= 0 || seqlen_q <= 0 || heads_q <= 0) return 0;
+  return 2 * bwd_row_bytes(batch, seqlen_q, heads_q);
 }
 
 int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v, const void* out,
@@ -736,6 +741,7 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   p.dout = static_cast<const uint16_t*>(dout);
   p.lse = lse;
   p.delta = static_cast<float*>(workspace);
+  p.nlse = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_row_bytes(batch, seqlen_q, heads_q));
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);

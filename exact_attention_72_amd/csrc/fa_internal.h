@@ -132,6 +132,7 @@ struct FaBwdParams {
   const uint16_t* dout;
   const float* lse;  // [B, Hq, Nq] natural-log LSE of the forward
   float* delta;      // [B, Hq, Nq] D = rowsum(dO * O) (workspace)
+  float* nlse;       // [B, Hq, Nq] LSE log2(e), +inf for a row that sees no key (workspace)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;

@@ -1756,7 +1756,13 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_delta_kernel(FaBwdParams p) {
     }
 #pragma unroll
     for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    if (r < rows && c == 0) p.delta[r] = acc;
+    if (r < rows && c == 0) {
+      p.delta[r] = acc;
+      // the LSE in base-2 units for P = exp2(s c - LSE log2 e); +inf keeps P = 0
+      // for a row that sees no key
+      const float l = p.lse[r];
+      p.nlse[r] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
+    }
   }
 }
 
@@ -2001,7 +2007,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     int r = q0 + col;
     r = r < Lq ? r : Lq - 1;
     const int64_t ri = ((int64_t)b * p.Hq + h) * Lq + r;
-    const float* src = kg ? p.delta + ri : p.lse + ri;
+    const float* src = kg ? p.delta + ri : p.nlse + ri;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (FA_LDS void*)(st + 4 * T), 4, 0, 0);
   };
   constexpr int kPer = 4 * G::kInstPerWave + 1;
@@ -2054,16 +2060,9 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
                  "+v"(dr[1]), "+v"(dr[2]), "+v"(dr[3]));
     return [=]() __attribute__((always_inline)) {  // the arithmetic, run later
       f32x8 p0f, p1f, d0f, d1f;
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int qi = q0 + 8 * (a >> 2) + 4 * kg + (a & 3);
-        const int pos = qi + (Lk - Lq);
-        const bool vis = full || (key_ok && qi < Lq && (!p.causal || key <= pos) &&
-                                  (p.wl < 0 || key >= pos - p.wl) && (p.wr < 0 || key <= pos + p.wr));
-        const float l = __uint_as_float(lr[a >> 2][a & 3]);
+      // L arrives in base-2 units (+inf for a row that sees no key, so P = 0)
+      auto put = [&](int a, float pa) __attribute__((always_inline)) {
         const float dl = __uint_as_float(dr[a >> 2][a & 3]);
-        const float nl = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
-        const float pa = vis ? exp2_fast(__builtin_fmaf(sv[a], c, -nl)) : 0.0f;
         const float ds = pa * (dp[a] - dl);
         if (a < 8) {
           p0f[a] = pa;
@@ -2071,6 +2070,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
         } else {
           p1f[a - 8] = pa;
           d1f[a - 8] = ds;
+        }
+      };
+      if (full) {
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+          put(a, exp2_fast(__builtin_fmaf(sv[a], c, -__uint_as_float(lr[a >> 2][a & 3]))));
+      } else {
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int qi = q0 + 8 * (a >> 2) + 4 * kg + (a & 3);
+          const int pos = qi + (Lk - Lq);
+          const bool vis = key_ok && qi < Lq && (!p.causal || key <= pos) && (p.wl < 0 || key >= pos - p.wl) &&
+                           (p.wr < 0 || key <= pos + p.wr);
+          const float nl = __uint_as_float(lr[a >> 2][a & 3]);
+          put(a, vis ? exp2_fast(__builtin_fmaf(sv[a], c, -nl)) : 0.0f);
         }
       }
       HeadOut h;

@@ -325,7 +325,8 @@ int fa_rotary(void* x, int batch, int seqlen, int heads, int head_dim,
  *   k, v, dk, dv      [batch, seqlen_k, heads_kv, head_dim]
  *   lse               float32 [batch, heads_q, seqlen_q]: the forward's LSE (natural log)
  *   dq, dk, dv        bf16, written (every element, zeros where nothing flows)
- *   workspace         device memory of at least fa_bwd_workspace_size(...) bytes (holds D)
+ *   workspace         device memory of at least fa_bwd_workspace_size(...) bytes (holds D and
+ *                     the LSE in base-2 units per query row)
  * opts as for fa_fwd (same scale, causal, window); softcap > 0 is FA_ERR_UNSUPPORTED.
  * Three kernels on the stream: D, then dQ (per query block), then dK/dV (per key block).
  * Deterministic: no atomics. */
@@ -337,7 +338,8 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
            const int64_t dk_strides[3], const int64_t dv_strides[3], void* workspace,
            size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace fa_bwd needs: batch * heads_q * seqlen_q * 4 rounded up to 256. */
+/* Bytes of workspace fa_bwd needs: twice batch * heads_q * seqlen_q * 4 rounded up to 256
+ * (D and the base-2 LSE of every query row). */
 size_t fa_bwd_workspace_size(int batch, int seqlen_q, int heads_q);
 
 /* FP8 (OCP e4m3) forward ("Attention kernels ...", section 4.2, the FP8 item;

@@ -388,7 +388,8 @@ def test_bwd_rejects_invalid_arguments():
     assert call(ws=None) == FA_ERR_INVALID_ARG
     assert call(ws_bytes=16) == FA_ERR_INVALID_ARG
     assert call(opts=_opts(softcap=30.0)) == FA_ERR_UNSUPPORTED
-    assert api.lib().fa_bwd_workspace_size(4, 4096, 16) == 4 * 16 * 4096 * 4
+    assert api.lib().fa_bwd_workspace_size(4, 4096, 16) == 2 * 4 * 16 * 4096 * 4
+    assert api.lib().fa_bwd_workspace_size(1, 3, 1) == 2 * 256
 
 
 def test_fp8_entry_points_reject_invalid_arguments():
