@@ -200,6 +200,7 @@ int dense_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void
   if (rows > (int64_t)1 << 30) return fail(FA_ERR_UNSUPPORTED, "too many rows per sequence");
   p.m_blocks = (int)((rows + FA_BLOCK_M - 1) / FA_BLOCK_M);
   p.total_tiles = (int64_t)p.m_blocks * batch * p.hg_count;
+  if (p.total_tiles > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "too many tiles");
   p.persistent = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = mod_id != 0 ? fa_launch_prefill_mod(p, head_dim, pack, mod_id, st)
@@ -296,6 +297,7 @@ int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
   int64_t bound = (int64_t)p.m_blocks * batch;
   int64_t bound2 = ((int64_t)total_q * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M + batch;
   p.total_tiles = (bound < bound2 ? bound : bound2) * p.hg_count;
+  if (p.total_tiles > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "too many tiles");
   // one workgroup per tile index, longest first: the hardware hands out the next
   // tile as a workgroup finishes, which balances unequal sequences (measured
   // 7 % faster than a persistent grid-stride loop on 32 sequences of 64..8192
@@ -418,6 +420,7 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   int64_t bound = (int64_t)p.m_blocks * batch;
   int64_t bound2 = ((int64_t)total_q * p.gp + FA_BLOCK_M - 1) / FA_BLOCK_M + batch;
   p.total_tiles = (bound < bound2 ? bound : bound2) * p.hg_count;
+  if (p.total_tiles > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "too many tiles");
   // one workgroup per tile index, longest tiles first (by the keys each sees):
   // with the decode-like sequences in the decode kernel this measured 562
   // against 547 TFLOP/s for a persistent grid-stride loop on a batch of 64
@@ -553,6 +556,7 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
     const int64_t rows_seq = (int64_t)seqlen_q * p.gp;
     p.m_blocks = (int)((rows_seq + FA_BLOCK_M - 1) / FA_BLOCK_M);
     p.total_tiles = (int64_t)p.m_blocks * batch * p.hg_count;
+    if (p.total_tiles > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "too many tiles");
     p.persistent = 0;
     hipError_t e = fa_launch_prefill(p, head_dim, false, true, pack, softcap, s);
     if (e != hipSuccess) return hip_fail(e, "paged prefill launch");

@@ -657,20 +657,26 @@ __device__ bool varlen_tile(const FaParams& p, int64_t t, int lane, TileId* out)
 // K/V: workgroup i runs on XCD i % 8, so XCD x takes the pairs x, x + 8, ...
 // one after the other, row blocks in order, and its concurrent tiles cover one
 // pair's neighbouring windows in that XCD's L2.
-__device__ __forceinline__ bool dense_tile(const FaParams& p, int64_t t, TileId* out) {
-  if (t >= p.total_tiles) return false;
-  const int64_t pairs = (int64_t)p.B * p.hg_count;
-  int64_t bh;
+__device__ __forceinline__ bool dense_tile(const FaParams& p, int64_t t64, TileId* out) {
+  if (t64 >= p.total_tiles) return false;
+  // tile counts stay below 2^31 (the host checks), so 32-bit index arithmetic
+  const uint32_t t = (uint32_t)t64;
+  const uint32_t hgc = (uint32_t)p.hg_count;
+  const uint32_t pairs = (uint32_t)p.B * hgc;
+  uint32_t bh;
   if (p.wl >= 0 && !p.persistent && (pairs & 7) == 0) {
-    const int64_t j = t >> 3;
-    out->mb = (int)(j % p.m_blocks);
-    bh = (j / p.m_blocks) * 8 + (t & 7);
+    const uint32_t j = t >> 3, mbs = (uint32_t)p.m_blocks;
+    const uint32_t q = j / mbs;
+    out->mb = (int)(j - q * mbs);
+    bh = q * 8 + (t & 7);
   } else {
-    out->mb = p.m_blocks - 1 - (int)(t / pairs);
-    bh = t % pairs;
+    const uint32_t q = t / pairs;
+    out->mb = p.m_blocks - 1 - (int)q;
+    bh = t - q * pairs;
   }
-  out->b = (int)(bh / p.hg_count);
-  out->hg = (int)(bh % p.hg_count);
+  const uint32_t b = bh / hgc;
+  out->b = (int)b;
+  out->hg = (int)(bh - b * hgc);
   return true;
 }
 
