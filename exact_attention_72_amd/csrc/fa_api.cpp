@@ -724,8 +724,13 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k", k, k_strides, 3)) ||
       (rc = check_strides("v", v, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)) ||
       (rc = check_strides("dout", dout, do_strides, 3)) || (rc = check_strides("dq", dq, dq_strides, 3)) ||
-      (rc = check_strides("dk", dk, dk_strides, 3)) || (rc = check_strides("dv", dv, dv_strides, 3)))
+      (rc = check_strides("dk", dk, dk_strides, 3)) || (rc = check_strides("dv", dv, dv_strides, 3)) ||
+      (rc = check_token_stride("q", q_strides[1])) || (rc = check_token_stride("dout", do_strides[1])))
     return rc;
+  // the dK/dV kernel reaches the L array from the D array with a 32-bit offset
+  if (bwd_row_bytes(batch, seqlen_q, heads_q) > (size_t)0x7fffff00)
+    return fail(FA_ERR_UNSUPPORTED, "batch * heads_q * seqlen_q of %lld rows is too many for the backward",
+                (long long)batch * heads_q * seqlen_q);
   const size_t need = fa_bwd_workspace_size(batch, seqlen_q, heads_q);
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : (size_t)0);

@@ -49,6 +49,8 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -1730,9 +1732,10 @@ __global__ __launch_bounds__(kThreads) void fa_append_kernel(FaAppendParams p) {
 // forward's orientation: a lane owns a query), the dK/dV kernel walks query
 // blocks (and the query heads of a KV-head group) for a block of keys, with
 // the roles of queries and keys exchanged (a lane owns a key).  Each product
-// then has its operands in the layouts the forward already reads: rows of an
-// LDS tile by ds_read_b128, or a tile read transposed by ds_read_b64_tr_b16,
-// so a tile used both ways is staged twice, once per swizzle.
+// reads its operands as the forward does: rows of an LDS tile by
+// ds_read_b128, or a tile read transposed by ds_read_b64_tr_b16.  The dQ
+// kernel stages its K tile twice, once per swizzle; the dK/dV kernel stages Q
+// and dO once, in a swizzle that serves both reads.
 
 // D[b, h, i] = sum_c dO[b, i, h, c] O[b, i, h, c] in fp32; one row per group of
 // D / 8 lanes, 16 bytes of each tensor per lane.
@@ -1942,35 +1945,86 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
   }
 }
 
+// The dK/dV kernel reads each Q and dO tile of a stage (32 rows of D bf16) both
+// ways: by rows with ds_read_b128 for S = Q K^T and dP = dO V^T, transposed
+// with ds_read_b64_tr_b16 for dV^T += dO^T P and dK^T += Q^T dS.  One swizzle
+// serves both reads, so each tile is staged once: stored 16-byte chunk =
+// logical chunk ^ u_swz(row), where u_swz takes every chunk value over any 16
+// aligned rows (the 16 rows a row read serves at once land in distinct banks)
+// and its 64-byte-segment bits differ over any 4 aligned rows (the 4 rows of a
+// transposed read land in distinct segments).  D = 64: a row is half of the
+// 256-byte bank line and the row parity is the extra bank bit; the same two
+// rules hold with the segment bit taken from row bit 1.
+template <int D>
+__device__ __forceinline__ int u_swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Per-lane LDS byte addresses of the reads of one unified tile at the start of
+// the LDS array.  A step adds its stage's offset to the registers it reads with
+// (one add per register, not per read); the tensor and chunk offsets within the
+// stage are the instructions' immediates.
+template <int D>
+struct UniOffsets {
+  uint32_t row[D / 16];               // ds_read_b128: row lane % 32, chunk 2 kk + lane / 32
+  uint32_t tlo[D / 32], thi[D / 32];  // ds_read_b64_tr_b16, d-block db: rows 0..7 / 8..15 of a 16-row chunk
+  __device__ __forceinline__ void init(int lane, uint32_t base) {
+    const int col = lane & 31, kg = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      row[kk] = base + col * (2 * D) + (((2 * kk + kg) ^ u_swz<D>(col)) << 4);
+    // within a 16-lane group, lanes 4 i .. 4 i + 3 address 32 bytes of row i
+    const int j = lane & 15, half = (lane >> 4) & 1;
+    const int r = 4 * kg + (j >> 2);
+    const int c = 2 * half + ((j & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      tlo[db] = base + r * (2 * D) + (((4 * db + c) ^ u_swz<D>(r)) << 4) + (j & 1) * 8;
+      thi[db] = base + (r + 8) * (2 * D) + (((4 * db + c) ^ u_swz<D>(r + 8)) << 4) + (j & 1) * 8;
+    }
+  }
+};
+template <int D, int OFF, int K0, int NK>
+__device__ __forceinline__ void uni_rows(const uint32_t (&row)[D / 16], u32x4 (&a)[D / 16]) {
+#pragma unroll
+  for (int kk = K0; kk < K0 + NK; ++kk) a[kk] = ds_read_b128<OFF>(row[kk]);
+}
+template <int D, int OFF, int DB0, int NDB>
+__device__ __forceinline__ void uni_tr(const uint32_t (&tlo)[D / 32], const uint32_t (&thi)[D / 32],
+                                       u32x2 (&lo)[NDB], u32x2 (&hi)[NDB]) {
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    lo[i] = ds_read_tr16<OFF>(tlo[DB0 + i]);
+    hi[i] = ds_read_tr16<OFF>(thi[DB0 + i]);
+  }
+}
+
 // dK, dV: one workgroup per (batch, KV head, 128-key block); each wave owns 32
 // keys (a lane owns a key) and walks, for every query head of the group, the
-// query blocks that see the keys.  S = Q K^T and dP = dO V^T read Q and dO rows,
-// dV^T += dO^T P and dK^T += Q^T dS read them transposed, so a stage holds Q and
-// dO once per swizzle, plus the block's 32 log-sum-exp and D values.
+// query blocks that see the keys.  A stage holds the block's Q and dO tiles
+// (unified swizzle) and, in a separate area, its 32 log-sum-exp and D values.
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p) {
   constexpr int BM = 32;
   constexpr int NBUF = 4;
   using G = DmaGeom<D, BM>;
   constexpr int T = G::kTensorBytes;
-  constexpr int kStage = 4 * T + 1024;  // Q rows, Q transposed, dO rows, dO transposed, L and D
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kStage];
+  constexpr int kLD = NBUF * 256;  // L and D of each stage: 32 + 32 fp32
+  constexpr int kStage = 2 * T;    // Q tile, dO tile
+  static_assert(kLD + T + 16 * (2 * D) < 65536, "tile offsets must fit the immediate");
+  __shared__ __attribute__((aligned(1024))) char smem[kLD + NBUF * kStage];
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, kg = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c = p.scale_log2;
-  LaneOffsets<D> off;
-  off.init(lane, lds_addr(smem), lds_addr(smem) + T);  // Q rows +0, Q transposed +T, dO rows +2T, dO transposed +3T
+  UniOffsets<D> uo;
+  uo.init(lane, lds_addr(smem));
   const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
-  const int dma_pc = lane % G::kChunksPerRow;
-  const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
-  const int v_src = (dma_pc ^ v_swz<D>(dma_row)) * 8;
+  const int u_src = ((lane % G::kChunksPerRow) ^ u_swz<D>(dma_row)) * 8;
 
-  const int k_blocks = (p.Nk + 127) / 128;
   const int64_t pairs = (int64_t)p.B * p.Hkv;
   const int64_t t = blockIdx.x;
   const int kbk = (int)(t / pairs);  // key blocks near the start first (they see the most queries)
   const int b = (int)((t % pairs) / p.Hkv), kvh = (int)((t % pairs) % p.Hkv);
-  (void)k_blocks;
   const int Lq = p.Nq, Lk = p.Nk;
   const int j0 = kbk * 128;
   int64_t i_lo, i_hi;
@@ -1996,27 +2050,73 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
       vreg[kk] = __builtin_bit_cast(bf16x8, y);
     }
   }
-  // step s: query head kvh g + s / nqb, query block qb_lo + s % nqb
-  auto issue = [&](int s_) __attribute__((always_inline)) {
-    char* st = smem + (s_ % NBUF) * kStage;
-    const int h = kvh * p.g + s_ / nqb;
-    const int q0 = (qb_lo + s_ % nqb) * BM;
-    const uint16_t* qb = p.q + b * p.q_bs + h * p.q_hs;
-    const uint16_t* db = p.dout + b * p.do_bs + h * p.do_hs;
-    char* w = st + wave * 1024;
-    dma_rows<D>(qb, p.q_ss, q0, dma_row, Lq - 1, k_src, w);
-    dma_rows<D>(qb, p.q_ss, q0, dma_row, Lq - 1, v_src, w + T);
-    dma_rows<D>(db, p.do_ss, q0, dma_row, Lq - 1, k_src, w + 2 * T);
-    dma_rows<D>(db, p.do_ss, q0, dma_row, Lq - 1, v_src, w + 3 * T);
-    // the block's L (lanes 0..31) and D (lanes 32..63), 4 bytes a lane; every
-    // wave writes the same bytes, so every wave's count of DMAs per step agrees
-    int r = q0 + col;
-    r = r < Lq ? r : Lq - 1;
-    const int64_t ri = ((int64_t)b * p.Hq + h) * Lq + r;
-    const float* src = kg ? p.delta + ri : p.nlse + ri;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (FA_LDS void*)(st + 4 * T), 4, 0, 0);
+  // K and V land before the first DMA is issued.  Left pending into the loop,
+  // their first use there would make the compiler wait for every outstanding
+  // load at each step, the DMA of the blocks ahead included.
+  wait_vmcnt<0>();
+
+  // Step s is query head kvh g + s / nqb, query block qb_lo + s % nqb.  A walk
+  // advances over (head, block) one block per step with no division: the DMA's
+  // walk runs two steps ahead of the products'.
+  struct Walk {
+    int qblk, q0;               // block index within the head's range, first query row
+    int64_t qoff, ooff, loff;   // elements to row q0 of the head in Q, dO and the [B, Hq, Nq] rows
   };
-  constexpr int kPer = 4 * G::kInstPerWave + 1;
+  Walk dw;
+  dw.qblk = 0;
+  dw.q0 = qb_lo * BM;
+  {
+    const int h0 = kvh * p.g;
+    dw.qoff = b * p.q_bs + (int64_t)h0 * p.q_hs + (int64_t)dw.q0 * p.q_ss;
+    dw.ooff = b * p.do_bs + (int64_t)h0 * p.do_hs + (int64_t)dw.q0 * p.do_ss;
+    dw.loff = ((int64_t)b * p.Hq + h0) * Lq + dw.q0;
+  }
+  const int64_t q_blk = (int64_t)BM * p.q_ss, o_blk = (int64_t)BM * p.do_ss;
+  const int64_t q_wrap = p.q_hs - (int64_t)nqb * q_blk, o_wrap = p.do_hs - (int64_t)nqb * o_blk;
+  const int64_t l_wrap = (int64_t)Lq - (int64_t)nqb * BM;
+  auto advance = [&](Walk& w) __attribute__((always_inline)) {
+    w.q0 += BM, w.qoff += q_blk, w.ooff += o_blk, w.loff += BM;
+    if (++w.qblk == nqb) {
+      w.qblk = 0, w.q0 = qb_lo * BM;
+      w.qoff += q_wrap, w.ooff += o_wrap, w.loff += l_wrap;
+    }
+  };
+  // DMA of the walk's block into stage buf.  A full block goes through buffer
+  // resources based at its first row, each lane adding a fixed byte offset (the
+  // host keeps 32 token strides, and the distance from the D array to the L
+  // array, below 2^31 bytes); a final partial block clamps its rows to the last
+  // query (the mask drops what the clamp duplicates).  The block's L (lanes
+  // 0..31) and D (lanes 32..63) go to the stage's 256-byte area; every wave
+  // writes the same bytes, so every wave's count of DMAs per step agrees.
+  const uint32_t q_voff = (uint32_t)(dma_row * p.q_ss + u_src) * 2u;
+  const uint32_t o_voff = (uint32_t)(dma_row * p.do_ss + u_src) * 2u;
+  const uint32_t q_step = (uint32_t)(G::kRowStep * p.q_ss) * 2u, o_step = (uint32_t)(G::kRowStep * p.do_ss) * 2u;
+  const uint32_t ld_voff =
+      (uint32_t)(kg ? 0 : (reinterpret_cast<const char*>(p.nlse) - reinterpret_cast<const char*>(p.delta))) +
+      4u * (uint32_t)col;
+  auto issue = [&](const Walk& w, int buf) __attribute__((always_inline)) {
+    char* st = smem + kLD + buf * kStage + wave * 1024;
+    char* ld = smem + buf * 256;
+    if (w.q0 + BM <= Lq) {
+      const __amdgpu_buffer_rsrc_t rq = buf_rsrc(p.q + w.qoff);
+      const __amdgpu_buffer_rsrc_t ro = buf_rsrc(p.dout + w.ooff);
+#pragma unroll
+      for (int j = 0; j < G::kInstPerWave; ++j) {
+        dma16_buf(rq, q_voff, j * q_step, st + j * 4096);
+        dma16_buf(ro, o_voff, j * o_step, st + T + j * 4096);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_rsrc(p.delta + w.loff), (FA_LDS void*)ld, 4, (int)ld_voff, 0, 0,
+                                               0);
+    } else {
+      const int last = Lq - 1 - w.q0;
+      dma_rows<D>(p.q + w.qoff, p.q_ss, 0, dma_row, last, u_src, st);
+      dma_rows<D>(p.dout + w.ooff, p.do_ss, 0, dma_row, last, u_src, st + T);
+      const int r = col < last ? col : last;
+      const float* src = (kg ? p.delta : p.nlse) + w.loff + r;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (FA_LDS void*)ld, 4, 0, 0);
+    }
+  };
+  constexpr int kPer = 2 * G::kInstPerWave + 1;
 
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -2024,96 +2124,134 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     dk[db] = f32x16{};
     dv[db] = f32x16{};
   }
-  const uint32_t ld_base = lds_addr(smem) + 4 * T + 16 * kg;  // L of queries 8 j + 4 kg .. + 3 at + 32 j
+  const uint32_t ld_base = lds_addr(smem) + 16 * kg;  // L of queries 8 j + 4 kg .. + 3 at + 32 j
 
   // Step s in two parts.  head(s): S = Q K^T and dP = dO V^T from block s's Q and
-  // dO rows, then P and dS (bf16) from them and the block's L and D.  tail(s):
-  // dV^T += dO^T P and dK^T += Q^T dS from block s's transposed reads.  Iteration
-  // s issues head(s)'s products, then tail(s - 1)'s, then head(s)'s arithmetic,
-  // which runs while the matrix unit works through tail(s - 1).
+  // dO rows, and the block's L and D.  tail(s): dV^T += dO^T P and
+  // dK^T += Q^T dS from block s's transposed reads, with P and dS (bf16) formed
+  // from head(s)'s results.  Iteration s issues head(s)'s products, then
+  // tail(s - 1)'s, and forms block s's P and dS two scores at a time between
+  // tail(s - 1)'s products: a wave issues in order, so arithmetic placed after
+  // the last product would leave the matrix unit idle while it runs.
   struct HeadOut {
     bf16x8 p0, p1, d0, d1;
   };
-  auto head = [&](int s_) __attribute__((always_inline)) {
-    const uint32_t st = (uint32_t)((s_ % NBUF) * kStage);
-    const int q0 = (qb_lo + s_ % nqb) * BM;
-    // element masks only where the query block cuts the wave's 32 keys (or runs past Lq)
-    FaRowSpan qs;
-    qs.pos_lo = (int64_t)q0 + (Lk - Lq);
-    qs.pos_hi = (int64_t)q0 + BM - 1 + (Lk - Lq);
-    const int kw = j0 + wave * 32;
-    const bool full = q0 + BM <= Lq && kw + 32 <= Lk &&
-                      fa_tile_class(qs, Lk, p.causal, p.wl, p.wr, 32, kw / 32) == FA_TILE_VISIBLE;
+  struct HeadState {
+    f32x16 sv, dp;
+    u32x4 lr[4], dr[4];
+  };
+  // The element mask is needed only where the query block cuts the wave's 32
+  // keys or runs past Lq.  Every (query i, key j) of blocks q0 .. q0 + 31 and
+  // keys kw .. kw + 31 is visible iff kw + 31 < Lk, q0 + 31 < Lq and, with
+  // d = Lk - Lq: causal, kw + 31 <= q0 + d; a right window, kw + 31 <= q0 + d + wr;
+  // a left window, kw >= q0 + 31 + d - wl.  So q0 in [fq_lo, fq_hi].
+  int fq_lo, fq_hi;
+  {
+    const int64_t kw = j0 + wave * 32, dd = (int64_t)Lk - Lq;
+    int64_t lo = 0, hi = (int64_t)Lq - BM;
+    if (p.causal) lo = max(lo, kw + 31 - dd);
+    if (p.wr >= 0) lo = max(lo, kw + 31 - dd - p.wr);
+    if (p.wl >= 0) hi = min(hi, kw - 31 - dd + p.wl);
+    if (kw + 32 > Lk) hi = -1;
+    fq_lo = (int)min(lo, (int64_t)0x7fffffff);
+    fq_hi = (int)max(hi, (int64_t)-1);
+  }
+  auto head = [&](int buf, int q0) __attribute__((always_inline)) {
+    constexpr int QO = kLD, OO = kLD + T;
+    const uint32_t st = (uint32_t)(buf * kStage);
+    uint32_t row[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) row[kk] = uo.row[kk] + st;
+    const uint32_t ldb = ld_base + (uint32_t)(buf * 256);
+    const bool full = q0 >= fq_lo && q0 <= fq_hi;
     // Reads stay in flight behind the products that wait for the ones before them
     // (LDS reads complete in issue order, so a wait names how many of the latest
     // may still be outstanding); at most 12 are in flight at a time.
+    HeadState hs;
     u32x4 qa[D / 16], oa[D / 16];
-    read_k_part<D, 0, 0, D / 32>(st, off, qa);
-    read_k_part<D, 0, D / 32, D / 32>(st, off, qa);
-    read_k_part<D, 0, 0, D / 32>(st + 2 * T, off, oa);
+    uni_rows<D, QO, 0, D / 32>(row, qa);
+    uni_rows<D, QO, D / 32, D / 32>(row, qa);
+    uni_rows<D, OO, 0, D / 32>(row, oa);
     lgkm_wait<D / 32>(qa);
-    read_k_part<D, 0, D / 32, D / 32>(st + 2 * T, off, oa);
-    const f32x16 sv = qk_mma<D>(qa, kreg);  // S = Q K^T: rows queries, lane column = this key
+    uni_rows<D, OO, D / 32, D / 32>(row, oa);
+    hs.sv = qk_mma<D>(qa, kreg);  // S = Q K^T: rows queries, lane column = this key
     // L and D of the accumulator rows: rows 8 j + 4 kg .. + 3 are slots 4 j .. 4 j + 3
-    u32x4 lr[4], dr[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) lr[jj] = ds_read_b128<0>(ld_base + st + 32 * jj);
+    hs.lr[0] = ds_read_b128<0>(ldb);
+    hs.lr[1] = ds_read_b128<32>(ldb);
+    hs.lr[2] = ds_read_b128<64>(ldb);
+    hs.lr[3] = ds_read_b128<96>(ldb);
     lgkm_wait<4>(oa);
+    hs.dr[0] = ds_read_b128<128>(ldb);
+    hs.dr[1] = ds_read_b128<160>(ldb);
+    hs.dr[2] = ds_read_b128<192>(ldb);
+    hs.dr[3] = ds_read_b128<224>(ldb);
+    hs.dp = qk_mma<D>(oa, vreg);  // dP = dO V^T
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(hs.lr[0]), "+v"(hs.lr[1]), "+v"(hs.lr[2]), "+v"(hs.lr[3]),
+                 "+v"(hs.dr[0]), "+v"(hs.dr[1]), "+v"(hs.dr[2]), "+v"(hs.dr[3]));
+    if (!full) {
+      // a score the mask drops becomes -inf, so its P (and dS) is 0
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dr[jj] = ds_read_b128<128>(ld_base + st + 32 * jj);
-    const f32x16 dp = qk_mma<D>(oa, vreg);  // dP = dO V^T
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lr[0]), "+v"(lr[1]), "+v"(lr[2]), "+v"(lr[3]), "+v"(dr[0]),
-                 "+v"(dr[1]), "+v"(dr[2]), "+v"(dr[3]));
-    return [=]() __attribute__((always_inline)) {  // the arithmetic, run later
-      f32x8 p0f, p1f, d0f, d1f;
-      // L arrives in base-2 units (+inf for a row that sees no key, so P = 0)
-      auto put = [&](int a, float pa) __attribute__((always_inline)) {
-        const float dl = __uint_as_float(dr[a >> 2][a & 3]);
-        const float ds = pa * (dp[a] - dl);
-        if (a < 8) {
-          p0f[a] = pa;
-          d0f[a] = ds;
-        } else {
-          p1f[a - 8] = pa;
-          d1f[a - 8] = ds;
-        }
-      };
-      if (full) {
-#pragma unroll
-        for (int a = 0; a < 16; ++a)
-          put(a, exp2_fast(__builtin_fmaf(sv[a], c, -__uint_as_float(lr[a >> 2][a & 3]))));
-      } else {
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int qi = q0 + 8 * (a >> 2) + 4 * kg + (a & 3);
-          const int pos = qi + (Lk - Lq);
-          const bool vis = key_ok && qi < Lq && (!p.causal || key <= pos) && (p.wl < 0 || key >= pos - p.wl) &&
-                           (p.wr < 0 || key <= pos + p.wr);
-          const float nl = __uint_as_float(lr[a >> 2][a & 3]);
-          put(a, vis ? exp2_fast(__builtin_fmaf(sv[a], c, -nl)) : 0.0f);
-        }
+      for (int a = 0; a < 16; ++a) {
+        const int qi = q0 + 8 * (a >> 2) + 4 * kg + (a & 3);
+        const int pos = qi + (Lk - Lq);
+        const bool vis = key_ok && qi < Lq && (!p.causal || key <= pos) && (p.wl < 0 || key >= pos - p.wl) &&
+                         (p.wr < 0 || key <= pos + p.wr);
+        hs.sv[a] = vis ? hs.sv[a] : kNegInf;
       }
-      HeadOut h;
-      h.p0 = __builtin_convertvector(p0f, bf16x8);
-      h.p1 = __builtin_convertvector(p1f, bf16x8);
-      h.d0 = __builtin_convertvector(d0f, bf16x8);
-      h.d1 = __builtin_convertvector(d1f, bf16x8);
-      return h;
-    };
+    }
+    return hs;
+  };
+  // P = exp2(s c - L) (L in base-2 units, +inf for a row that sees no key) and
+  // dS = P (dP - D) for scores A and A + 1, rounded to bf16 at once into the
+  // operand words (fewer registers live across the products than fp32 halves).
+  struct Packed {
+    u32x4 p0, p1, d0, d1;
+  };
+  auto scores = [&](const HeadState& hs, Packed& pk, auto ac) __attribute__((always_inline)) {
+    constexpr int A = decltype(ac)::value;
+    float s0 = hs.sv[A], s1 = hs.sv[A + 1], g0 = hs.dp[A], g1 = hs.dp[A + 1];
+    asm volatile("" : "+v"(s0), "+v"(s1), "+v"(g0), "+v"(g1));  // not before this point
+    const float p0 = exp2_fast(__builtin_fmaf(s0, c, -__uint_as_float(hs.lr[A >> 2][A & 3])));
+    const float p1 = exp2_fast(__builtin_fmaf(s1, c, -__uint_as_float(hs.lr[(A + 1) >> 2][(A + 1) & 3])));
+    const float d0 = p0 * (g0 - __uint_as_float(hs.dr[A >> 2][A & 3]));
+    const float d1 = p1 * (g1 - __uint_as_float(hs.dr[(A + 1) >> 2][(A + 1) & 3]));
+    uint32_t pw = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2));
+    uint32_t dw = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{d0, d1}), bf16x2));
+    asm volatile("" : "+v"(pw), "+v"(dw));  // nor after
+    if constexpr (A < 8) {
+      pk.p0[A / 2] = pw, pk.d0[A / 2] = dw;
+    } else {
+      pk.p1[(A - 8) / 2] = pw, pk.d1[(A - 8) / 2] = dw;
+    }
+  };
+  auto pack = [](const Packed& pk) __attribute__((always_inline)) {
+    HeadOut h;
+    h.p0 = __builtin_bit_cast(bf16x8, pk.p0);
+    h.p1 = __builtin_bit_cast(bf16x8, pk.p1);
+    h.d0 = __builtin_bit_cast(bf16x8, pk.d0);
+    h.d1 = __builtin_bit_cast(bf16x8, pk.d1);
+    return h;
   };
   // dV^T += dO^T P (dO read transposed), dK^T += Q^T dS (Q read transposed), in
   // eight units of D / 64 d-blocks: unit u reads chunk u / 2 (dO^T keys 0..15,
   // dO^T keys 16..31, Q^T keys 0..15, Q^T keys 16..31), half u % 2 of the
   // d-blocks.  Three units are in flight while a fourth feeds its products; each
   // unit has registers of its own, so a read never lands in operands of products
-  // still waiting to start.
-  auto tail = [&](int s_, const HeadOut& h) __attribute__((always_inline)) {
-    const uint32_t st = (uint32_t)((s_ % NBUF) * kStage);
+  // still waiting to start.  After unit u's products, work(u) runs.
+  auto tail = [&](int buf, const HeadOut& h, auto&& work) __attribute__((always_inline)) {
     constexpr int UD = D / 64, UR = 2 * UD;
+    const uint32_t st = (uint32_t)(buf * kStage);
+    uint32_t tlo[D / 32], thi[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      tlo[db] = uo.tlo[db] + st;
+      thi[db] = uo.thi[db] + st;
+    }
     u32x2 lo[8][UD], hi[8][UD];
     auto rd = [&](auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value, c = u / 2;
-      read_v_part<D, (c & 1) * 16 * (2 * D), (u % 2) * UD, UD>(c < 2 ? st + 2 * T : st, off, lo[u], hi[u]);
+      constexpr int u = decltype(uc)::value, ch = u / 2;
+      constexpr int OFF = kLD + (ch < 2 ? T : 0) + (ch & 1) * 16 * (2 * D);
+      uni_tr<D, OFF, (u % 2) * UD, UD>(tlo, thi, lo[u], hi[u]);
     };
     auto wt = [&lo, &hi](auto uc, auto nc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value, n = decltype(nc)::value;
@@ -2122,15 +2260,16 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
       for (int i = 0; i < UD; ++i) asm volatile("" : "+v"(lo[u][i]), "+v"(hi[u][i]));
     };
     auto mm = [&](auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value, c = u / 2, hh = u % 2;
+      constexpr int u = decltype(uc)::value, ch = u / 2, hh = u % 2;
 #pragma unroll
       for (int i = 0; i < UD; ++i) {
         const u32x4 a = {lo[u][i].x, lo[u][i].y, hi[u][i].x, hi[u][i].y};
-        if constexpr (c == 0) mfma_acc(dv[hh * UD + i], a, h.p0);
-        if constexpr (c == 1) mfma_acc(dv[hh * UD + i], a, h.p1);
-        if constexpr (c == 2) mfma_acc(dk[hh * UD + i], a, h.d0);
-        if constexpr (c == 3) mfma_acc(dk[hh * UD + i], a, h.d1);
+        if constexpr (ch == 0) mfma_acc(dv[hh * UD + i], a, h.p0);
+        if constexpr (ch == 1) mfma_acc(dv[hh * UD + i], a, h.p1);
+        if constexpr (ch == 2) mfma_acc(dk[hh * UD + i], a, h.d0);
+        if constexpr (ch == 3) mfma_acc(dk[hh * UD + i], a, h.d1);
       }
+      work(uc);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -2155,23 +2294,56 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
   };
 
   // Ring of NBUF = 4 stages, the DMA of block s + 2 issued at iteration s: its
-  // buffer last held block s - 2, whose tail ran in iteration s - 1.
-  for (int j = 0; j < 2 && j < steps; ++j) issue(j);
+  // buffer last held block s - 2, whose tail ran in iteration s - 1.  It is
+  // issued after block s's products, so that its scalar work runs beside them.
+  for (int j = 0; j < 2 && j < steps; ++j) {
+    issue(dw, j);
+    advance(dw);
+  }
+  Walk hw;  // the products' walk (only q0 and qblk are used)
+  hw.qblk = 0, hw.q0 = qb_lo * BM, hw.qoff = 0, hw.ooff = 0, hw.loff = 0;
   HeadOut prev;
-  for (int s_ = 0; s_ < steps; ++s_) {
-    wait_vmcnt_blocks<kPer>(min(steps - 1, s_ + 1) - s_);  // block s landed; block s + 1 may be in flight
+  auto nothing = [](auto) __attribute__((always_inline)) {};
+  // one step: block s's head, tail(s - 1) with block s's P and dS formed between
+  // its products (the first step, with no tail before it, is peeled off so that
+  // the loop has a single path for the accumulators)
+  auto step = [&](int s_, bool first) __attribute__((always_inline)) {
+    // block s landed; block s + 1 may still be in flight
+    if (s_ + 1 < steps)
+      wait_vmcnt<kPer>();
+    else
+      wait_vmcnt<0>();
     stage_barrier();
-    if (s_ + 2 < steps) issue(s_ + 2);
-    auto arith = head(s_);
-    if (s_ > 0) tail(s_ - 1, prev);
-    prev = arith();
+    const int buf = s_ % NBUF;
+    const HeadState hs = head(buf, hw.q0);
+    if (s_ + 2 < steps) {
+      issue(dw, (s_ + 2) % NBUF);
+      advance(dw);
+    }
+    Packed pk;
+    auto work = [&](auto uc) __attribute__((always_inline)) {
+      scores(hs, pk, std::integral_constant<int, 2 * decltype(uc)::value>{});
+    };
+    if (first) {
+      work(std::integral_constant<int, 0>{}), work(std::integral_constant<int, 1>{});
+      work(std::integral_constant<int, 2>{}), work(std::integral_constant<int, 3>{});
+      work(std::integral_constant<int, 4>{}), work(std::integral_constant<int, 5>{});
+      work(std::integral_constant<int, 6>{}), work(std::integral_constant<int, 7>{});
+    } else {
+      tail((s_ + NBUF - 1) % NBUF, prev, work);
+    }
+    prev = pack(pk);
+    hw.q0 += BM;
+    if (++hw.qblk == nqb) hw.qblk = 0, hw.q0 = qb_lo * BM;
     // Settle the accumulators before the iteration ends: the compiler may copy
     // them between registers at the loop's edges and does not see that the
     // products above are still writing them.
     drain_acc(dk, dv);
-  }
+  };
+  if (steps > 0) step(0, true);
+  for (int s_ = 1; s_ < steps; ++s_) step(s_, false);
   if (steps > 0) {
-    tail(steps - 1, prev);
+    tail((steps - 1) % NBUF, prev, nothing);
     drain_acc(dk, dv);
   }
   if (key_ok) {
