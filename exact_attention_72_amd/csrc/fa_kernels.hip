@@ -1809,146 +1809,10 @@ __device__ __forceinline__ void drain_acc(f32x16 (&a)[N], f32x16 (&b)[N]) {
   }
 }
 
-// dQ: one workgroup per (batch, query head, 128-row block); each wave owns 32
-// query rows and walks the key blocks the rows can see.  A stage holds a key
-// block three times: K rows (row swizzle) for S^T = K Q^T, K again in the
-// transposed-read swizzle for dQ^T += K^T dS^T, and V rows for dP^T = V dO^T.
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
-  constexpr int BN = 32;
-  constexpr int NBUF = 3;
-  using G = DmaGeom<D, BN>;
-  constexpr int T = G::kTensorBytes;
-  constexpr int kStage = 3 * T;
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kStage];
-  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, kg = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const float c = p.scale_log2;
-  LaneOffsets<D> off;
-  off.init(lane, lds_addr(smem), lds_addr(smem) + T);  // K rows at +0, K transposed at +T, V rows at +2T
-  const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
-  const int dma_pc = lane % G::kChunksPerRow;
-  const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
-  const int v_src = (dma_pc ^ v_swz<D>(dma_row)) * 8;
-
-  // tile: row blocks longest first (causal rows near the end see more keys)
-  const int m_blocks = (p.Nq + 127) / 128;
-  const int64_t pairs = (int64_t)p.B * p.Hq;
-  const int64_t t = blockIdx.x;
-  const int mb = m_blocks - 1 - (int)(t / pairs);
-  const int b = (int)((t % pairs) / p.Hq), h = (int)((t % pairs) % p.Hq), kvh = h / p.g;
-  const int Lq = p.Nq, Lk = p.Nk;
-  const int m0 = mb * 128;
-  FaRowSpan span;
-  span.pos_lo = (int64_t)m0 + (Lk - Lq);
-  span.pos_hi = (int64_t)min(m0 + 128, Lq) - 1 + (Lk - Lq);
-  int n_lo, n_hi, f_lo, f_hi;
-  fa_key_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &n_lo, &n_hi);
-  fa_full_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &f_lo, &f_hi);
-  const int nb = n_hi - n_lo;
-
-  const int row = m0 + wave * 32 + col;
-  const bool row_ok = row < Lq;
-  bf16x8 qreg[D / 16], doreg[D / 16];
-  {
-    const uint16_t* qb = p.q + b * p.q_bs + (int64_t)(row_ok ? row : 0) * p.q_ss + h * p.q_hs;
-    const uint16_t* db = p.dout + b * p.do_bs + (int64_t)(row_ok ? row : 0) * p.do_ss + h * p.do_hs;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (row_ok) {
-        x = *reinterpret_cast<const u32x4*>(qb + 16 * kk + 8 * kg);
-        y = *reinterpret_cast<const u32x4*>(db + 16 * kk + 8 * kg);
-      }
-      qreg[kk] = __builtin_bit_cast(bf16x8, x);
-      doreg[kk] = __builtin_bit_cast(bf16x8, y);
-    }
-  }
-  const int64_t ri = ((int64_t)b * p.Hq + h) * Lq + (row_ok ? row : 0);
-  const float lse = row_ok ? p.lse[ri] : kNegInf;
-  const float dlt = row_ok ? p.delta[ri] : 0.0f;
-  // P = exp2(s c - L log2 e); a row that sees nothing (L = -inf) gets P = 0
-  const float nl = (lse == kNegInf) ? __builtin_inff() : lse * kLog2e;
-  LaneMask mask;
-  mask.pos = row + (Lk - Lq);
-  mask.kend = Lk;
-  mask.kbeg = 0;
-  mask.causal = p.causal;
-  mask.wl = p.wl;
-  mask.wr = p.wr;
-
-  const uint16_t* kb = p.k + b * p.k_bs + kvh * p.k_hs;
-  const uint16_t* vb = p.v + b * p.v_bs + kvh * p.v_hs;
-  auto issue = [&](int i) __attribute__((always_inline)) {
-    char* st = smem + (i % NBUF) * kStage + wave * 1024;
-    const int n0 = (n_lo + i) * BN;
-    dma_rows<D>(kb, p.k_ss, n0, dma_row, Lk - 1, k_src, st);
-    dma_rows<D>(kb, p.k_ss, n0, dma_row, Lk - 1, v_src, st + T);
-    dma_rows<D>(vb, p.v_ss, n0, dma_row, Lk - 1, k_src, st + 2 * T);
-  };
-  constexpr int kPer = 3 * G::kInstPerWave;
-
-  f32x16 dq[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
-  for (int j = 0; j < NBUF - 1 && j < nb; ++j) issue(j);
-  for (int i = 0; i < nb; ++i) {
-    wait_vmcnt_blocks<kPer>(min(i + NBUF - 2, nb - 1) - i);  // block i landed
-    stage_barrier();  // for every wave; and everyone is done with block i - 1's stage
-    if (i + NBUF - 1 < nb) issue(i + NBUF - 1);
-    const uint32_t st = (uint32_t)((i % NBUF) * kStage);
-    u32x4 ka[D / 16];
-    read_k<D, 0>(st, off, ka);
-    lgkm_wait<0>(ka);
-    f32x16 s = qk_mma<D>(ka, qreg);  // S^T = K Q^T
-    read_k<D, 0>(st + 2 * T, off, ka);
-    lgkm_wait<0>(ka);
-    const f32x16 dpt = qk_mma<D>(ka, doreg);  // dP^T = V dO^T
-    const int n = n_lo + i;
-    if (n < f_lo || n >= f_hi) {
-      int base = n * BN + 4 * kg;
-      asm volatile("" : "+v"(base));
-      // the row's visible keys in the block as an interval of offsets
-      const int hi = mask.off_hi(base), lo = mask.off_lo(base);
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int off = 8 * (a >> 2) + (a & 3);
-        s[a] = (off <= hi && off >= lo) ? s[a] : kNegInf;
-      }
-    }
-    f32x8 x0, x1;
-#pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      const float pa = exp2_fast(__builtin_fmaf(s[a], c, -nl));
-      const float ds = pa * (dpt[a] - dlt);
-      if (a < 8)
-        x0[a] = ds;
-      else
-        x1[a - 8] = ds;
-    }
-    const bf16x8 d0 = __builtin_convertvector(x0, bf16x8), d1 = __builtin_convertvector(x1, bf16x8);
-    pv_chunk<D, 0>(st, d0, dq, off);  // dQ^T += K^T dS^T, K read transposed
-    pv_chunk<D, 16 * (2 * D)>(st, d1, dq, off);
-  }
-  if (row_ok) {
-    uint16_t* ob = p.dq + b * p.dq_bs + (int64_t)row * p.dq_ss + h * p.dq_hs;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x8 x = {};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = dq[db][4 * q4 + e] * p.scale;
-        const u32x4 yb = __builtin_bit_cast(u32x4, __builtin_convertvector(x, bf16x8));
-        *reinterpret_cast<u32x2*>(ob + 32 * db + 8 * q4 + 4 * kg) = u32x2{yb.x, yb.y};
-      }
-  }
-}
-
-// The dK/dV kernel reads each Q and dO tile of a stage (32 rows of D bf16) both
-// ways: by rows with ds_read_b128 for S = Q K^T and dP = dO V^T, transposed
-// with ds_read_b64_tr_b16 for dV^T += dO^T P and dK^T += Q^T dS.  One swizzle
-// serves both reads, so each tile is staged once: stored 16-byte chunk =
+// The backward kernels read some stage tiles (32 rows of D bf16) both ways: by
+// rows with ds_read_b128 and transposed with ds_read_b64_tr_b16 (K in the dQ
+// kernel, Q and dO in the dK/dV kernel).  One swizzle serves both reads, so
+// each tile is staged once: stored 16-byte chunk =
 // logical chunk ^ u_swz(row), where u_swz takes every chunk value over any 16
 // aligned rows (the 16 rows a row read serves at once land in distinct banks)
 // and its 64-byte-segment bits differ over any 4 aligned rows (the 4 rows of a
@@ -1996,6 +1860,186 @@ __device__ __forceinline__ void uni_tr(const uint32_t (&tlo)[D / 32], const uint
   for (int i = 0; i < NDB; ++i) {
     lo[i] = ds_read_tr16<OFF>(tlo[DB0 + i]);
     hi[i] = ds_read_tr16<OFF>(thi[DB0 + i]);
+  }
+}
+
+// dQ: one workgroup per (batch, query head, 128-row block); each wave owns 32
+// query rows and walks the key blocks the rows can see.  A stage holds the key
+// block's K and V tiles in the unified swizzle: K rows for S^T = K Q^T, K read
+// transposed for dQ^T += K^T dS^T, V rows for dP^T = V dO^T.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
+  constexpr int BN = 32;
+  constexpr int NBUF = 3;
+  using G = DmaGeom<D, BN>;
+  constexpr int T = G::kTensorBytes;
+  constexpr int kStage = 2 * T;  // K tile, V tile
+  static_assert(T + 16 * (2 * D) < 65536, "tile offsets must fit the immediate");
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kStage];
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, kg = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float c = p.scale_log2;
+  UniOffsets<D> uo;
+  uo.init(lane, lds_addr(smem));
+  const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
+  const int u_src = ((lane % G::kChunksPerRow) ^ u_swz<D>(dma_row)) * 8;
+
+  // tile: row blocks longest first (causal rows near the end see more keys)
+  const int m_blocks = (p.Nq + 127) / 128;
+  const int64_t pairs = (int64_t)p.B * p.Hq;
+  const int64_t t = blockIdx.x;
+  const int mb = m_blocks - 1 - (int)(t / pairs);
+  const int b = (int)((t % pairs) / p.Hq), h = (int)((t % pairs) % p.Hq), kvh = h / p.g;
+  const int Lq = p.Nq, Lk = p.Nk;
+  const int m0 = mb * 128;
+  FaRowSpan span;
+  span.pos_lo = (int64_t)m0 + (Lk - Lq);
+  span.pos_hi = (int64_t)min(m0 + 128, Lq) - 1 + (Lk - Lq);
+  int n_lo, n_hi, f_lo, f_hi;
+  fa_key_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &n_lo, &n_hi);
+  fa_full_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &f_lo, &f_hi);
+  const int nb = n_hi - n_lo;
+
+  const int row = m0 + wave * 32 + col;
+  const bool row_ok = row < Lq;
+  bf16x8 qreg[D / 16], doreg[D / 16];
+  {
+    const uint16_t* qb = p.q + b * p.q_bs + (int64_t)(row_ok ? row : 0) * p.q_ss + h * p.q_hs;
+    const uint16_t* db = p.dout + b * p.do_bs + (int64_t)(row_ok ? row : 0) * p.do_ss + h * p.do_hs;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+      if (row_ok) {
+        x = *reinterpret_cast<const u32x4*>(qb + 16 * kk + 8 * kg);
+        y = *reinterpret_cast<const u32x4*>(db + 16 * kk + 8 * kg);
+      }
+      qreg[kk] = __builtin_bit_cast(bf16x8, x);
+      doreg[kk] = __builtin_bit_cast(bf16x8, y);
+    }
+  }
+  const int64_t ri = ((int64_t)b * p.Hq + h) * Lq + (row_ok ? row : 0);
+  const float dlt = row_ok ? p.delta[ri] : 0.0f;
+  // P = exp2(s c - L log2 e); a row that sees nothing (L = -inf) gets P = 0
+  const float nl = row_ok ? p.nlse[ri] : __builtin_inff();
+  // Q, dO, L and D land before the first DMA is issued (left pending, their first
+  // use in the loop would wait for the DMA of the blocks ahead too)
+  wait_vmcnt<0>();
+  LaneMask mask;
+  mask.pos = row + (Lk - Lq);
+  mask.kend = Lk;
+  mask.kbeg = 0;
+  mask.causal = p.causal;
+  mask.wl = p.wl;
+  mask.wr = p.wr;
+
+  // DMA of key block n_lo + i into stage i % NBUF: buffer resources based at the
+  // block's first key for a full block (the host keeps 32 token strides below
+  // 2^31 bytes), rows clamped to the last key for a final partial one.
+  const uint16_t* kb = p.k + b * p.k_bs + kvh * p.k_hs;
+  const uint16_t* vb = p.v + b * p.v_bs + kvh * p.v_hs;
+  const uint32_t k_voff = (uint32_t)(dma_row * p.k_ss + u_src) * 2u;
+  const uint32_t v_voff = (uint32_t)(dma_row * p.v_ss + u_src) * 2u;
+  const uint32_t k_step = (uint32_t)(G::kRowStep * p.k_ss) * 2u, v_step = (uint32_t)(G::kRowStep * p.v_ss) * 2u;
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    char* st = smem + (i % NBUF) * kStage + wave * 1024;
+    const int n0 = (n_lo + i) * BN;
+    if (n0 + BN <= Lk) {
+      const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kb + (int64_t)n0 * p.k_ss);
+      const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vb + (int64_t)n0 * p.v_ss);
+#pragma unroll
+      for (int j = 0; j < G::kInstPerWave; ++j) {
+        dma16_buf(rk, k_voff, j * k_step, st + j * 4096);
+        dma16_buf(rv, v_voff, j * v_step, st + T + j * 4096);
+      }
+    } else {
+      dma_rows<D>(kb, p.k_ss, n0, dma_row, Lk - 1, u_src, st);
+      dma_rows<D>(vb, p.v_ss, n0, dma_row, Lk - 1, u_src, st + T);
+    }
+  };
+  constexpr int kPer = 2 * G::kInstPerWave;
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+  for (int j = 0; j < NBUF - 1 && j < nb; ++j) issue(j);
+  for (int i = 0; i < nb; ++i) {
+    // block i landed (block i + 1 may still be in flight); everyone is done with
+    // block i - 1, whose stage the DMA of block i + 2 reuses
+    if (i + 1 < nb)
+      wait_vmcnt<kPer>();
+    else
+      wait_vmcnt<0>();
+    stage_barrier();
+    if (i + NBUF - 1 < nb) issue(i + NBUF - 1);
+    const uint32_t st = (uint32_t)((i % NBUF) * kStage);
+    uint32_t rows[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) rows[kk] = uo.row[kk] + st;
+    u32x4 ka[D / 16];
+    uni_rows<D, 0, 0, D / 16>(rows, ka);
+    lgkm_wait<0>(ka);
+    f32x16 s = qk_mma<D>(ka, qreg);  // S^T = K Q^T
+    uni_rows<D, T, 0, D / 16>(rows, ka);
+    lgkm_wait<0>(ka);
+    const f32x16 dpt = qk_mma<D>(ka, doreg);  // dP^T = V dO^T
+    const int n = n_lo + i;
+    if (n < f_lo || n >= f_hi) {
+      int base = n * BN + 4 * kg;
+      asm volatile("" : "+v"(base));
+      // the row's visible keys in the block as an interval of offsets
+      const int hi = mask.off_hi(base), lo = mask.off_lo(base);
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int off = 8 * (a >> 2) + (a & 3);
+        s[a] = (off <= hi && off >= lo) ? s[a] : kNegInf;
+      }
+    }
+    f32x8 x0, x1;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const float pa = exp2_fast(__builtin_fmaf(s[a], c, -nl));
+      const float ds = pa * (dpt[a] - dlt);
+      if (a < 8)
+        x0[a] = ds;
+      else
+        x1[a - 8] = ds;
+    }
+    const bf16x8 d0 = __builtin_convertvector(x0, bf16x8), d1 = __builtin_convertvector(x1, bf16x8);
+    // dQ^T += K^T dS^T, K read transposed: keys 0..15 of the block, then 16..31
+    uint32_t tlo[D / 32], thi[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      tlo[db] = uo.tlo[db] + st;
+      thi[db] = uo.thi[db] + st;
+    }
+    u32x2 lo0[D / 32], hi0[D / 32], lo1[D / 32], hi1[D / 32];
+    uni_tr<D, 0, 0, D / 32>(tlo, thi, lo0, hi0);
+    uni_tr<D, 16 * (2 * D), 0, D / 32>(tlo, thi, lo1, hi1);
+    lgkm_wait<2 * (D / 32)>(lo0, hi0);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const u32x4 w = {lo0[db].x, lo0[db].y, hi0[db].x, hi0[db].y};
+      dq[db] = mfma32(__builtin_bit_cast(bf16x8, w), d0, dq[db]);
+    }
+    lgkm_wait<0>(lo1, hi1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const u32x4 w = {lo1[db].x, lo1[db].y, hi1[db].x, hi1[db].y};
+      dq[db] = mfma32(__builtin_bit_cast(bf16x8, w), d1, dq[db]);
+    }
+  }
+  if (row_ok) {
+    uint16_t* ob = p.dq + b * p.dq_bs + (int64_t)row * p.dq_ss + h * p.dq_hs;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x8 x = {};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = dq[db][4 * q4 + e] * p.scale;
+        const u32x4 yb = __builtin_bit_cast(u32x4, __builtin_convertvector(x, bf16x8));
+        *reinterpret_cast<u32x2*>(ob + 32 * db + 8 * q4 + 4 * kg) = u32x2{yb.x, yb.y};
+      }
   }
 }
 
