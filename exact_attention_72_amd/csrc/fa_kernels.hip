@@ -1724,7 +1724,8 @@ __global__ __launch_bounds__(kThreads) void fa_append_kernel(FaAppendParams p) {
 // "Attention kernels...", section 4.3: the backward recomputes S = Q K^T block by
 // block and takes P = exp(S - L) straight from the saved log-sum-exp L, with no
 // online reduction; dV = P^T dO, dP = dO V^T, dS = P (dP - D) with
-// D = rowsum(dO O) (a preprocess pass), dQ = scale dS K, dK = scale dS^T Q.
+// D = rowsum(dO O) (the pages' preprocess; here the dQ kernel's prologue, which
+// also hands D and L to the dK/dV kernel), dQ = scale dS K, dK = scale dS^T Q.
 // P and dS enter their products rounded to bf16, like P in the forward.
 //
 // Two kernels split the work so that each accumulates its gradient in
@@ -1733,47 +1734,9 @@ __global__ __launch_bounds__(kThreads) void fa_append_kernel(FaAppendParams p) {
 // blocks (and the query heads of a KV-head group) for a block of keys, with
 // the roles of queries and keys exchanged (a lane owns a key).  Each product
 // reads its operands as the forward does: rows of an LDS tile by
-// ds_read_b128, or a tile read transposed by ds_read_b64_tr_b16.  The dQ
-// kernel stages its K tile twice, once per swizzle; the dK/dV kernel stages Q
-// and dO once, in a swizzle that serves both reads.
-
-// D[b, h, i] = sum_c dO[b, i, h, c] O[b, i, h, c] in fp32; one row per group of
-// D / 8 lanes, 16 bytes of each tensor per lane.
-template <int D>
-__global__ __launch_bounds__(kThreads) void fa_bwd_delta_kernel(FaBwdParams p) {
-  constexpr int LPR = D / 8;       // lanes per row
-  constexpr int RPW = 64 / LPR;    // rows per wave
-  typedef float f32x8_ __attribute__((ext_vector_type(8)));
-  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
-  const int lane = threadIdx.x & 63;
-  const int64_t w0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const int64_t nw = ((int64_t)gridDim.x * kThreads) >> 6;
-  for (int64_t r0 = w0 * RPW; r0 < rows; r0 += nw * RPW) {
-    const int64_t r = r0 + lane / LPR;  // row index in [B, Hq, Nq] order
-    const int c = lane % LPR;
-    float acc = 0.0f;
-    if (r < rows) {
-      const int i = (int)(r % p.Nq);
-      const int64_t bh = r / p.Nq;
-      const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-      const u32x4 x = *reinterpret_cast<const u32x4*>(p.o + b * p.o_bs + i * p.o_ss + h * p.o_hs + 8 * c);
-      const u32x4 y = *reinterpret_cast<const u32x4*>(p.dout + b * p.do_bs + i * p.do_ss + h * p.do_hs + 8 * c);
-      const f32x8_ xf = __builtin_convertvector(__builtin_bit_cast(bf16x8, x), f32x8_);
-      const f32x8_ yf = __builtin_convertvector(__builtin_bit_cast(bf16x8, y), f32x8_);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(xf[e], yf[e], acc);
-    }
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    if (r < rows && c == 0) {
-      p.delta[r] = acc;
-      // the LSE in base-2 units for P = exp2(s c - LSE log2 e); +inf keeps P = 0
-      // for a row that sees no key
-      const float l = p.lse[r];
-      p.nlse[r] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
-    }
-  }
-}
+// ds_read_b128, or a tile read transposed by ds_read_b64_tr_b16; a tile read
+// both ways (K in the dQ kernel, Q and dO in the dK/dV kernel) is staged once,
+// in a swizzle that serves both reads.
 
 // 1 KiB LDS-DMA share of a 32-row bf16 tile: rows (row0 + dma_row + 4 RPK j) of
 // a tensor whose rows sit at base + r * stride, clamped to the last valid row
@@ -1917,11 +1880,35 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
       doreg[kk] = __builtin_bit_cast(bf16x8, y);
     }
   }
+  // D = rowsum(dO O) of the row (fp32) and its L in base-2 units; both also go
+  // to the workspace for the dK/dV kernel (the grid covers every query row once).
+  // P = exp2(s c - L log2 e); a row that sees nothing (L = -inf) gets P = 0.
   const int64_t ri = ((int64_t)b * p.Hq + h) * Lq + (row_ok ? row : 0);
-  const float dlt = row_ok ? p.delta[ri] : 0.0f;
-  // P = exp2(s c - L log2 e); a row that sees nothing (L = -inf) gets P = 0
-  const float nl = row_ok ? p.nlse[ri] : __builtin_inff();
-  // Q, dO, L and D land before the first DMA is issued (left pending, their first
+  float dlt, nl = __builtin_inff();
+  {
+    float acc = 0.0f;
+    if (row_ok) {
+      const uint16_t* ob = p.o + b * p.o_bs + (int64_t)row * p.o_ss + h * p.o_hs;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(ob + 16 * kk + 8 * kg);
+        const f32x8 xf = __builtin_convertvector(__builtin_bit_cast(bf16x8, x), f32x8);
+        const f32x8 yf = __builtin_convertvector(doreg[kk], f32x8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(xf[e], yf[e], acc);
+      }
+    }
+    dlt = pair_sum(acc);  // the row's other half of the columns sits in lane ^ 32
+    if (row_ok) {
+      const float l = p.lse[ri];
+      nl = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
+      if (kg == 0) {
+        p.delta[ri] = dlt;
+        p.nlse[ri] = nl;
+      }
+    }
+  }
+  // Q, dO, O and L land before the first DMA is issued (left pending, their first
   // use in the loop would wait for the DMA of the blocks ahead too)
   wait_vmcnt<0>();
   LaneMask mask;
@@ -2634,17 +2621,13 @@ hipError_t fa_launch_rotary(const FaRotaryParams& p, int d, hipStream_t s) {
 hipError_t fa_launch_bwd(const FaBwdParams& p, int d, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
   if (rows <= 0 || p.Nk <= 0) return hipSuccess;
-  int64_t blocks = (rows * (d / 8) + kThreads - 1) / kThreads;  // one 16-byte chunk per lane
-  const int64_t cap = 16 * (int64_t)device_cus();
-  if (blocks > cap) blocks = cap;
+  // the dQ kernel also writes D and the base-2 LSE that the dK/dV kernel reads
   const int64_t dq_tiles = (int64_t)((p.Nq + 127) / 128) * p.B * p.Hq;
   const int64_t dkv_tiles = (int64_t)((p.Nk + 127) / 128) * p.B * p.Hkv;
   if (d == 128) {
-    hipLaunchKernelGGL(fa_bwd_delta_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL(fa_bwd_dq_kernel<128>, dim3((unsigned)dq_tiles), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL(fa_bwd_dkdv_kernel<128>, dim3((unsigned)dkv_tiles), dim3(kThreads), 0, s, p);
   } else if (d == 64) {
-    hipLaunchKernelGGL(fa_bwd_delta_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL(fa_bwd_dq_kernel<64>, dim3((unsigned)dq_tiles), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL(fa_bwd_dkdv_kernel<64>, dim3((unsigned)dkv_tiles), dim3(kThreads), 0, s, p);
   } else {
