@@ -1753,24 +1753,6 @@ __device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t stride, i
   }
 }
 
-// O^T-style product with the accumulator in AGPRs (the dK/dV kernel holds two
-// gradient tiles, more than its VGPRs).  The compiler does not know this is a
-// matrix product, so nothing else may touch the accumulators (a read, or a copy
-// it makes to move them between registers) until drain_acc has covered the
-// product's latency.
-__device__ __forceinline__ void mfma_acc(f32x16& acc, u32x4 a, bf16x8 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// 20 wait states after the last mfma_acc on either set, tied to both sets.
-template <int N>
-__device__ __forceinline__ void drain_acc(f32x16 (&a)[N], f32x16 (&b)[N]) {
-  if constexpr (N == 4) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
-                 : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(b[0]), "+a"(b[1]), "+a"(b[2]), "+a"(b[3]));
-  } else {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(a[0]), "+a"(a[1]), "+a"(b[0]), "+a"(b[1]));
-  }
-}
 
 // The backward kernels read some stage tiles (32 rows of D bf16) both ways: by
 // rows with ds_read_b128 and transposed with ds_read_b64_tr_b16 (K in the dQ
@@ -1787,28 +1769,37 @@ __device__ __forceinline__ int u_swz(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// Per-lane LDS byte addresses of the reads of one unified tile at the start of
-// the LDS array.  A step adds its stage's offset to the registers it reads with
-// (one add per register, not per read); the tensor and chunk offsets within the
-// stage are the instructions' immediates.
+// Per-lane LDS byte addresses of the reads of one unified tile at a base that is
+// a multiple of 256 bytes.  The chunk pair kk of a row read and the d-block db
+// of a transposed read only flip address bits 5..7 (bits no row offset, stage
+// offset or base touches), so three registers serve every read: row(kk) =
+// row0 ^ (kk << 5), tlo(db) = tlo0 ^ (db << 6), thi(db) = thi0 ^ (db << 6).  A
+// step adds its stage's offset to the base before the flips; the tensor and
+// chunk offsets within the stage are the instructions' immediates.
 template <int D>
 struct UniOffsets {
-  uint32_t row[D / 16];               // ds_read_b128: row lane % 32, chunk 2 kk + lane / 32
-  uint32_t tlo[D / 32], thi[D / 32];  // ds_read_b64_tr_b16, d-block db: rows 0..7 / 8..15 of a 16-row chunk
+  uint32_t row0;        // ds_read_b128: row lane % 32, chunk lane / 32 (kk = 0)
+  uint32_t tlo0, thi0;  // ds_read_b64_tr_b16, d-block 0: rows 0..7 / 8..15 of a 16-row chunk
   __device__ __forceinline__ void init(int lane, uint32_t base) {
     const int col = lane & 31, kg = lane >> 5;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      row[kk] = base + col * (2 * D) + (((2 * kk + kg) ^ u_swz<D>(col)) << 4);
+    row0 = base + col * (2 * D) + ((kg ^ u_swz<D>(col)) << 4);
     // within a 16-lane group, lanes 4 i .. 4 i + 3 address 32 bytes of row i
     const int j = lane & 15, half = (lane >> 4) & 1;
     const int r = 4 * kg + (j >> 2);
     const int c = 2 * half + ((j & 3) >> 1);
+    tlo0 = base + r * (2 * D) + ((c ^ u_swz<D>(r)) << 4) + (j & 1) * 8;
+    thi0 = base + (r + 8) * (2 * D) + ((c ^ u_swz<D>(r + 8)) << 4) + (j & 1) * 8;
+  }
+  // the stage at byte st of the base: row-read and transposed-read addresses
+  __device__ __forceinline__ void rows(uint32_t st, uint32_t (&a)[D / 16]) const {
+    const uint32_t r = row0 + st;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      tlo[db] = base + r * (2 * D) + (((4 * db + c) ^ u_swz<D>(r)) << 4) + (j & 1) * 8;
-      thi[db] = base + (r + 8) * (2 * D) + (((4 * db + c) ^ u_swz<D>(r + 8)) << 4) + (j & 1) * 8;
-    }
+    for (int kk = 0; kk < D / 16; ++kk) a[kk] = r ^ (uint32_t)(kk << 5);
+  }
+  __device__ __forceinline__ void trs(uint32_t st, uint32_t (&lo)[D / 32], uint32_t (&hi)[D / 32]) const {
+    const uint32_t l = tlo0 + st, h = thi0 + st;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) lo[db] = l ^ (uint32_t)(db << 6), hi[db] = h ^ (uint32_t)(db << 6);
   }
 };
 template <int D, int OFF, int K0, int NK>
@@ -1960,8 +1951,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
     if (i + NBUF - 1 < nb) issue(i + NBUF - 1);
     const uint32_t st = (uint32_t)((i % NBUF) * kStage);
     uint32_t rows[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) rows[kk] = uo.row[kk] + st;
+    uo.rows(st, rows);
     u32x4 ka[D / 16];
     uni_rows<D, 0, 0, D / 16>(rows, ka);
     lgkm_wait<0>(ka);
@@ -1994,11 +1984,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
     const bf16x8 d0 = __builtin_convertvector(x0, bf16x8), d1 = __builtin_convertvector(x1, bf16x8);
     // dQ^T += K^T dS^T, K read transposed: keys 0..15 of the block, then 16..31
     uint32_t tlo[D / 32], thi[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      tlo[db] = uo.tlo[db] + st;
-      thi[db] = uo.thi[db] + st;
-    }
+    uo.trs(st, tlo, thi);
     u32x2 lo0[D / 32], hi0[D / 32], lo1[D / 32], hi1[D / 32];
     uni_tr<D, 0, 0, D / 32>(tlo, thi, lo0, hi0);
     uni_tr<D, 16 * (2 * D), 0, D / 32>(tlo, thi, lo1, hi1);
@@ -2030,26 +2016,84 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
   }
 }
 
-// dK, dV: one workgroup per (batch, KV head, 128-key block); each wave owns 32
-// keys (a lane owns a key) and walks, for every query head of the group, the
-// query blocks that see the keys.  A stage holds the block's Q and dO tiles
-// (unified swizzle) and, in a separate area, its 32 log-sum-exp and D values.
+// dV^T or dK^T += X^T Y for one 32-row tile read transposed (X: the tile at byte
+// OFF of the stage registers' base, Y: y0 for its rows 0..15, y1 for rows
+// 16..31), in four units of D / 64 d-blocks: unit u reads rows 16 (u / 2) ..
+// + 15, half u % 2 of the d-blocks.  Three units are in flight while a fourth
+// feeds its products, each in registers of its own.
+template <int D, int OFF>
+__device__ __forceinline__ void tr_products(const uint32_t (&tlo)[D / 32], const uint32_t (&thi)[D / 32],
+                                            f32x16 (&acc)[D / 32], bf16x8 y0, bf16x8 y1) {
+  constexpr int UD = D / 64, UR = 2 * UD;
+  u32x2 lo[4][UD], hi[4][UD];
+  auto rd = [&](auto uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+    uni_tr<D, OFF + (u / 2) * 16 * (2 * D), (u % 2) * UD, UD>(tlo, thi, lo[u], hi[u]);
+  };
+  auto wt = [&lo, &hi](auto uc, auto nc) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value, n = decltype(nc)::value;
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(n));
+#pragma unroll
+    for (int i = 0; i < UD; ++i) asm volatile("" : "+v"(lo[u][i]), "+v"(hi[u][i]));
+  };
+  auto mm = [&](auto uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+#pragma unroll
+    for (int i = 0; i < UD; ++i)
+      acc[(u % 2) * UD + i] = mfma32(__builtin_bit_cast(bf16x8, u32x4{lo[u][i].x, lo[u][i].y, hi[u][i].x, hi[u][i].y}),
+                                     u < 2 ? y0 : y1, acc[(u % 2) * UD + i]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using W2 = std::integral_constant<int, 2 * UR>;
+  using W1 = std::integral_constant<int, UR>;
+  using W0 = std::integral_constant<int, 0>;
+  rd(I0{}), rd(I1{}), rd(I2{});
+  wt(I0{}, W2{}), rd(I3{}), mm(I0{});
+  wt(I1{}, W2{}), mm(I1{});
+  wt(I2{}, W1{}), mm(I2{});
+  wt(I3{}, W0{}), mm(I3{});
+}
+
+template <int OFF>
+__device__ __forceinline__ void ds_write_b128(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF));
+}
+
+// dK, dV: one workgroup of eight waves per (batch, KV head, 128-key block).  The
+// 128 keys are four slices of 32 (a lane owns a key); each slice has two waves,
+// s and s + 4, which the hardware places on one SIMD.  The steps walk, for every
+// query head of the KV-head group, the query blocks that see the keys.  Wave s
+// (the P wave) holds the slice's K rows; for block t it forms S = Q K^T,
+// P = exp(S - L) and dV^T += dO^T P, and hands P (fp32) to the other wave
+// through LDS.  Wave s + 4 (the dK wave) holds the slice's V rows and, one step
+// behind, forms dP = dO V^T, dS = P (dP - D) and dK^T += Q^T dS.  Each wave
+// accumulates one gradient, so the two fit one SIMD's registers and issue in
+// each other's gaps, with no product computed twice.  A stage holds the query
+// block's Q and dO tiles (unified swizzle) and its 32 L and D values; the P
+// waves issue its DMA.
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p) {
+__global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p) {
   constexpr int BM = 32;
   constexpr int NBUF = 4;
-  using G = DmaGeom<D, BM>;
+  using G = DmaGeom<D, BM>;  // four DMA waves
   constexpr int T = G::kTensorBytes;
-  constexpr int kLD = NBUF * 256;  // L and D of each stage: 32 + 32 fp32
-  constexpr int kStage = 2 * T;    // Q tile, dO tile
-  static_assert(kLD + T + 16 * (2 * D) < 65536, "tile offsets must fit the immediate");
-  __shared__ __attribute__((aligned(1024))) char smem[kLD + NBUF * kStage];
+  constexpr int kLD = NBUF * 256;        // L and D of each stage: 32 + 32 fp32
+  constexpr int kPB = 4 * 1024;          // P of one wave: 64 lanes x 16 fp32
+  constexpr int kSt = kLD + 8 * kPB;     // P of two steps x four slices, then the stages
+  constexpr int kStage = 2 * T;          // Q tile, dO tile
+  static_assert(T + 16 * (2 * D) < 65536, "tile offsets must fit the immediate");
+  __shared__ __attribute__((aligned(1024))) char smem[kSt + NBUF * kStage];
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, kg = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wave & 3;
+  const bool pwave = wave < 4;
   const float c = p.scale_log2;
   UniOffsets<D> uo;
-  uo.init(lane, lds_addr(smem));
-  const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
+  uo.init(lane, lds_addr(smem) + kSt);
+  const int dma_row = slot * G::kRowsPerKiB + lane / G::kChunksPerRow;
   const int u_src = ((lane % G::kChunksPerRow) ^ u_swz<D>(dma_row)) * 8;
 
   const int64_t pairs = (int64_t)p.B * p.Hkv;
@@ -2064,31 +2108,28 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
   const int nqb = i_hi > i_lo ? (int)((i_hi + BM - 1) / BM) - qb_lo : 0;
   const int steps = nqb * p.g;
 
-  const int key = j0 + wave * 32 + col;
+  const int key = j0 + slot * 32 + col;
   const bool key_ok = key < Lk;
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // the P wave holds the slice's K rows (S = Q K^T), the dK wave its V rows (dP = dO V^T)
+  bf16x8 kv[D / 16];
   {
-    const uint16_t* kr = p.k + b * p.k_bs + (int64_t)(key_ok ? key : 0) * p.k_ss + kvh * p.k_hs;
-    const uint16_t* vr = p.v + b * p.v_bs + (int64_t)(key_ok ? key : 0) * p.v_ss + kvh * p.v_hs;
+    const uint16_t* src = pwave ? p.k + b * p.k_bs + (int64_t)(key_ok ? key : 0) * p.k_ss + kvh * p.k_hs
+                                : p.v + b * p.v_bs + (int64_t)(key_ok ? key : 0) * p.v_ss + kvh * p.v_hs;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (key_ok) {
-        x = *reinterpret_cast<const u32x4*>(kr + 16 * kk + 8 * kg);
-        y = *reinterpret_cast<const u32x4*>(vr + 16 * kk + 8 * kg);
-      }
-      kreg[kk] = __builtin_bit_cast(bf16x8, x);
-      vreg[kk] = __builtin_bit_cast(bf16x8, y);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key_ok) x = *reinterpret_cast<const u32x4*>(src + 16 * kk + 8 * kg);
+      kv[kk] = __builtin_bit_cast(bf16x8, x);
     }
   }
-  // K and V land before the first DMA is issued.  Left pending into the loop,
-  // their first use there would make the compiler wait for every outstanding
+  // K or V lands before the first DMA is issued.  Left pending into the loop,
+  // its first use there would make the compiler wait for every outstanding
   // load at each step, the DMA of the blocks ahead included.
   wait_vmcnt<0>();
 
-  // Step s is query head kvh g + s / nqb, query block qb_lo + s % nqb.  A walk
+  // Step t is query head kvh g + t / nqb, query block qb_lo + t % nqb.  A walk
   // advances over (head, block) one block per step with no division: the DMA's
-  // walk runs two steps ahead of the products'.
+  // walk runs two steps ahead of the P waves'.
   struct Walk {
     int qblk, q0;               // block index within the head's range, first query row
     int64_t qoff, ooff, loff;   // elements to row q0 of the head in Q, dO and the [B, Hq, Nq] rows
@@ -2112,13 +2153,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
       w.qoff += q_wrap, w.ooff += o_wrap, w.loff += l_wrap;
     }
   };
-  // DMA of the walk's block into stage buf.  A full block goes through buffer
-  // resources based at its first row, each lane adding a fixed byte offset (the
-  // host keeps 32 token strides, and the distance from the D array to the L
-  // array, below 2^31 bytes); a final partial block clamps its rows to the last
-  // query (the mask drops what the clamp duplicates).  The block's L (lanes
-  // 0..31) and D (lanes 32..63) go to the stage's 256-byte area; every wave
-  // writes the same bytes, so every wave's count of DMAs per step agrees.
+  // DMA of the walk's block into stage buf (by the four P waves).  A full block
+  // goes through buffer resources based at its first row, each lane adding a
+  // fixed byte offset (the host keeps 32 token strides, and the distance from
+  // the D array to the L array, below 2^31 bytes); a final partial block clamps
+  // its rows to the last query (the P wave's mask drops what the clamp
+  // duplicates).  The block's L (lanes 0..31) and D (lanes 32..63) go to the
+  // stage's 256-byte area; every P wave writes the same bytes, so every P wave's
+  // count of DMAs per step agrees.
   const uint32_t q_voff = (uint32_t)(dma_row * p.q_ss + u_src) * 2u;
   const uint32_t o_voff = (uint32_t)(dma_row * p.do_ss + u_src) * 2u;
   const uint32_t q_step = (uint32_t)(G::kRowStep * p.q_ss) * 2u, o_step = (uint32_t)(G::kRowStep * p.do_ss) * 2u;
@@ -2126,7 +2168,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
       (uint32_t)(kg ? 0 : (reinterpret_cast<const char*>(p.nlse) - reinterpret_cast<const char*>(p.delta))) +
       4u * (uint32_t)col;
   auto issue = [&](const Walk& w, int buf) __attribute__((always_inline)) {
-    char* st = smem + kLD + buf * kStage + wave * 1024;
+    char* st = smem + kSt + buf * kStage + slot * 1024;
     char* ld = smem + buf * 256;
     if (w.q0 + BM <= Lq) {
       const __amdgpu_buffer_rsrc_t rq = buf_rsrc(p.q + w.qoff);
@@ -2149,36 +2191,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
   };
   constexpr int kPer = 2 * G::kInstPerWave + 1;
 
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
-  }
-  const uint32_t ld_base = lds_addr(smem) + 16 * kg;  // L of queries 8 j + 4 kg .. + 3 at + 32 j
-
-  // Step s in two parts.  head(s): S = Q K^T and dP = dO V^T from block s's Q and
-  // dO rows, and the block's L and D.  tail(s): dV^T += dO^T P and
-  // dK^T += Q^T dS from block s's transposed reads, with P and dS (bf16) formed
-  // from head(s)'s results.  Iteration s issues head(s)'s products, then
-  // tail(s - 1)'s, and forms block s's P and dS two scores at a time between
-  // tail(s - 1)'s products: a wave issues in order, so arithmetic placed after
-  // the last product would leave the matrix unit idle while it runs.
-  struct HeadOut {
-    bf16x8 p0, p1, d0, d1;
-  };
-  struct HeadState {
-    f32x16 sv, dp;
-    u32x4 lr[4], dr[4];
-  };
-  // The element mask is needed only where the query block cuts the wave's 32
+  // The element mask is needed only where the query block cuts the slice's 32
   // keys or runs past Lq.  Every (query i, key j) of blocks q0 .. q0 + 31 and
   // keys kw .. kw + 31 is visible iff kw + 31 < Lk, q0 + 31 < Lq and, with
   // d = Lk - Lq: causal, kw + 31 <= q0 + d; a right window, kw + 31 <= q0 + d + wr;
   // a left window, kw >= q0 + 31 + d - wl.  So q0 in [fq_lo, fq_hi].
   int fq_lo, fq_hi;
   {
-    const int64_t kw = j0 + wave * 32, dd = (int64_t)Lk - Lq;
+    const int64_t kw = j0 + slot * 32, dd = (int64_t)Lk - Lq;
     int64_t lo = 0, hi = (int64_t)Lq - BM;
     if (p.causal) lo = max(lo, kw + 31 - dd);
     if (p.wr >= 0) lo = max(lo, kw + 31 - dd - p.wr);
@@ -2187,213 +2207,147 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p)
     fq_lo = (int)min(lo, (int64_t)0x7fffffff);
     fq_hi = (int)max(hi, (int64_t)-1);
   }
-  auto head = [&](int buf, int q0) __attribute__((always_inline)) {
-    constexpr int QO = kLD, OO = kLD + T;
-    const uint32_t st = (uint32_t)(buf * kStage);
-    uint32_t row[D / 16];
+
+  f32x16 acc[D / 32];  // dV (P wave) or dK (dK wave)
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) row[kk] = uo.row[kk] + st;
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  const uint32_t ld_base = lds_addr(smem) + 16 * kg;  // L of queries 8 j + 4 kg .. + 3 at + 32 j, D at + 128
+  // P of this slice, step parity 0, this lane: 16 fp32 as four 16-byte pieces 1 KiB apart
+  const uint32_t p_base = lds_addr(smem) + kLD + slot * kPB + 16 * lane;
+
+  // P wave, block t in stage t % NBUF
+  int pq0 = qb_lo * BM, pqblk = 0;  // the P waves' walk (first query row only)
+  auto p_step = [&](int t_) __attribute__((always_inline)) {
+    const int buf = t_ % NBUF;
+    const uint32_t st = (uint32_t)(buf * kStage);
+    uint32_t rows[D / 16];
+    uo.rows(st, rows);
+    u32x4 qa[D / 16];
+    uni_rows<D, 0, 0, D / 16>(rows, qa);
+    lgkm_wait<0>(qa);
+    f32x16 sv = qk_mma<D>(qa, kv);  // S = Q K^T: rows queries, lane column = this key
     const uint32_t ldb = ld_base + (uint32_t)(buf * 256);
-    const bool full = q0 >= fq_lo && q0 <= fq_hi;
-    // Reads stay in flight behind the products that wait for the ones before them
-    // (LDS reads complete in issue order, so a wait names how many of the latest
-    // may still be outstanding); at most 12 are in flight at a time.
-    HeadState hs;
-    u32x4 qa[D / 16], oa[D / 16];
-    uni_rows<D, QO, 0, D / 32>(row, qa);
-    uni_rows<D, QO, D / 32, D / 32>(row, qa);
-    uni_rows<D, OO, 0, D / 32>(row, oa);
-    lgkm_wait<D / 32>(qa);
-    uni_rows<D, OO, D / 32, D / 32>(row, oa);
-    hs.sv = qk_mma<D>(qa, kreg);  // S = Q K^T: rows queries, lane column = this key
-    // L and D of the accumulator rows: rows 8 j + 4 kg .. + 3 are slots 4 j .. 4 j + 3
-    hs.lr[0] = ds_read_b128<0>(ldb);
-    hs.lr[1] = ds_read_b128<32>(ldb);
-    hs.lr[2] = ds_read_b128<64>(ldb);
-    hs.lr[3] = ds_read_b128<96>(ldb);
-    lgkm_wait<4>(oa);
-    hs.dr[0] = ds_read_b128<128>(ldb);
-    hs.dr[1] = ds_read_b128<160>(ldb);
-    hs.dr[2] = ds_read_b128<192>(ldb);
-    hs.dr[3] = ds_read_b128<224>(ldb);
-    hs.dp = qk_mma<D>(oa, vreg);  // dP = dO V^T
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(hs.lr[0]), "+v"(hs.lr[1]), "+v"(hs.lr[2]), "+v"(hs.lr[3]),
-                 "+v"(hs.dr[0]), "+v"(hs.dr[1]), "+v"(hs.dr[2]), "+v"(hs.dr[3]));
-    if (!full) {
+    u32x4 lr[4];
+    lr[0] = ds_read_b128<0>(ldb);
+    lr[1] = ds_read_b128<32>(ldb);
+    lr[2] = ds_read_b128<64>(ldb);
+    lr[3] = ds_read_b128<96>(ldb);
+    if (t_ + 2 < steps) {
+      issue(dw, (t_ + 2) % NBUF);
+      advance(dw);
+    }
+    lgkm_wait<0>(lr);
+    if (!(pq0 >= fq_lo && pq0 <= fq_hi)) {
       // a score the mask drops becomes -inf, so its P (and dS) is 0
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
-        const int qi = q0 + 8 * (a >> 2) + 4 * kg + (a & 3);
+        const int qi = pq0 + 8 * (a >> 2) + 4 * kg + (a & 3);
         const int pos = qi + (Lk - Lq);
-        const bool vis = key_ok && qi < Lq && (!p.causal || key <= pos) && (p.wl < 0 || key >= pos - p.wl) &&
-                         (p.wr < 0 || key <= pos + p.wr);
-        hs.sv[a] = vis ? hs.sv[a] : kNegInf;
+        const bool vis = key_ok & (qi < Lq) & (!p.causal | (key <= pos)) & ((p.wl < 0) | (key >= pos - p.wl)) &
+                         ((p.wr < 0) | (key <= pos + p.wr));
+        sv[a] = vis ? sv[a] : kNegInf;
       }
     }
-    return hs;
-  };
-  // P = exp2(s c - L) (L in base-2 units, +inf for a row that sees no key) and
-  // dS = P (dP - D) for scores A and A + 1, rounded to bf16 at once into the
-  // operand words (fewer registers live across the products than fp32 halves).
-  struct Packed {
-    u32x4 p0, p1, d0, d1;
-  };
-  auto scores = [&](const HeadState& hs, Packed& pk, auto ac) __attribute__((always_inline)) {
-    constexpr int A = decltype(ac)::value;
-    float s0 = hs.sv[A], s1 = hs.sv[A + 1], g0 = hs.dp[A], g1 = hs.dp[A + 1];
-    asm volatile("" : "+v"(s0), "+v"(s1), "+v"(g0), "+v"(g1));  // not before this point
-    const float p0 = exp2_fast(__builtin_fmaf(s0, c, -__uint_as_float(hs.lr[A >> 2][A & 3])));
-    const float p1 = exp2_fast(__builtin_fmaf(s1, c, -__uint_as_float(hs.lr[(A + 1) >> 2][(A + 1) & 3])));
-    const float d0 = p0 * (g0 - __uint_as_float(hs.dr[A >> 2][A & 3]));
-    const float d1 = p1 * (g1 - __uint_as_float(hs.dr[(A + 1) >> 2][(A + 1) & 3]));
-    uint32_t pw = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2));
-    uint32_t dw = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{d0, d1}), bf16x2));
-    asm volatile("" : "+v"(pw), "+v"(dw));  // nor after
-    if constexpr (A < 8) {
-      pk.p0[A / 2] = pw, pk.d0[A / 2] = dw;
-    } else {
-      pk.p1[(A - 8) / 2] = pw, pk.d1[(A - 8) / 2] = dw;
-    }
-  };
-  auto pack = [](const Packed& pk) __attribute__((always_inline)) {
-    HeadOut h;
-    h.p0 = __builtin_bit_cast(bf16x8, pk.p0);
-    h.p1 = __builtin_bit_cast(bf16x8, pk.p1);
-    h.d0 = __builtin_bit_cast(bf16x8, pk.d0);
-    h.d1 = __builtin_bit_cast(bf16x8, pk.d1);
-    return h;
-  };
-  // dV^T += dO^T P (dO read transposed), dK^T += Q^T dS (Q read transposed), in
-  // eight units of D / 64 d-blocks: unit u reads chunk u / 2 (dO^T keys 0..15,
-  // dO^T keys 16..31, Q^T keys 0..15, Q^T keys 16..31), half u % 2 of the
-  // d-blocks.  Three units are in flight while a fourth feeds its products; each
-  // unit has registers of its own, so a read never lands in operands of products
-  // still waiting to start.  After unit u's products, work(u) runs.
-  auto tail = [&](int buf, const HeadOut& h, auto&& work) __attribute__((always_inline)) {
-    constexpr int UD = D / 64, UR = 2 * UD;
-    const uint32_t st = (uint32_t)(buf * kStage);
+    // P = exp2(s c - L), L in base-2 units (+inf for a row that sees no key, so P = 0)
+    f32x16 pa;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) pa[a] = exp2_fast(__builtin_fmaf(sv[a], c, -__uint_as_float(lr[a >> 2][a & 3])));
+    const uint32_t pw = p_base + (uint32_t)((t_ & 1) * 4 * kPB);
+    ds_write_b128<0>(pw, u32x4{__float_as_uint(pa[0]), __float_as_uint(pa[1]), __float_as_uint(pa[2]),
+                               __float_as_uint(pa[3])});
+    ds_write_b128<1024>(pw, u32x4{__float_as_uint(pa[4]), __float_as_uint(pa[5]), __float_as_uint(pa[6]),
+                                  __float_as_uint(pa[7])});
+    ds_write_b128<2048>(pw, u32x4{__float_as_uint(pa[8]), __float_as_uint(pa[9]), __float_as_uint(pa[10]),
+                                  __float_as_uint(pa[11])});
+    ds_write_b128<3072>(pw, u32x4{__float_as_uint(pa[12]), __float_as_uint(pa[13]), __float_as_uint(pa[14]),
+                                  __float_as_uint(pa[15])});
+    f32x8 x0, x1;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) x0[a] = pa[a], x1[a] = pa[8 + a];
+    const bf16x8 p0 = __builtin_convertvector(x0, bf16x8), p1 = __builtin_convertvector(x1, bf16x8);
     uint32_t tlo[D / 32], thi[D / 32];
+    uo.trs(st, tlo, thi);
+    tr_products<D, T>(tlo, thi, acc, p0, p1);  // dV^T += dO^T P, dO read transposed
+    pq0 += BM;
+    if (++pqblk == nqb) pqblk = 0, pq0 = qb_lo * BM;
+  };
+  // dK wave, block t (one step behind the P wave) in stage t % NBUF
+  auto k_step = [&](int t_) __attribute__((always_inline)) {
+    const int buf = t_ % NBUF;
+    const uint32_t st = (uint32_t)(buf * kStage);
+    uint32_t rows[D / 16];
+    uo.rows(st, rows);
+    u32x4 oa[D / 16];
+    uni_rows<D, T, 0, D / 16>(rows, oa);
+    lgkm_wait<0>(oa);
+    const f32x16 dp = qk_mma<D>(oa, kv);  // dP = dO V^T
+    const uint32_t ldb = ld_base + (uint32_t)(buf * 256);
+    const uint32_t pr_ = p_base + (uint32_t)((t_ & 1) * 4 * kPB);
+    u32x4 dr[4], pr[4];
+    dr[0] = ds_read_b128<128>(ldb);
+    dr[1] = ds_read_b128<160>(ldb);
+    dr[2] = ds_read_b128<192>(ldb);
+    dr[3] = ds_read_b128<224>(ldb);
+    pr[0] = ds_read_b128<0>(pr_);
+    pr[1] = ds_read_b128<1024>(pr_);
+    pr[2] = ds_read_b128<2048>(pr_);
+    pr[3] = ds_read_b128<3072>(pr_);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(dr[0]), "+v"(dr[1]), "+v"(dr[2]), "+v"(dr[3]), "+v"(pr[0]),
+                 "+v"(pr[1]), "+v"(pr[2]), "+v"(pr[3]));
+    f32x8 x0, x1;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      tlo[db] = uo.tlo[db] + st;
-      thi[db] = uo.thi[db] + st;
+    for (int a = 0; a < 16; ++a) {
+      const float ds = __uint_as_float(pr[a >> 2][a & 3]) * (dp[a] - __uint_as_float(dr[a >> 2][a & 3]));
+      if (a < 8)
+        x0[a] = ds;
+      else
+        x1[a - 8] = ds;
     }
-    u32x2 lo[8][UD], hi[8][UD];
-    auto rd = [&](auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value, ch = u / 2;
-      constexpr int OFF = kLD + (ch < 2 ? T : 0) + (ch & 1) * 16 * (2 * D);
-      uni_tr<D, OFF, (u % 2) * UD, UD>(tlo, thi, lo[u], hi[u]);
-    };
-    auto wt = [&lo, &hi](auto uc, auto nc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value, n = decltype(nc)::value;
-      asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(n));
-#pragma unroll
-      for (int i = 0; i < UD; ++i) asm volatile("" : "+v"(lo[u][i]), "+v"(hi[u][i]));
-    };
-    auto mm = [&](auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value, ch = u / 2, hh = u % 2;
-#pragma unroll
-      for (int i = 0; i < UD; ++i) {
-        const u32x4 a = {lo[u][i].x, lo[u][i].y, hi[u][i].x, hi[u][i].y};
-        if constexpr (ch == 0) mfma_acc(dv[hh * UD + i], a, h.p0);
-        if constexpr (ch == 1) mfma_acc(dv[hh * UD + i], a, h.p1);
-        if constexpr (ch == 2) mfma_acc(dk[hh * UD + i], a, h.d0);
-        if constexpr (ch == 3) mfma_acc(dk[hh * UD + i], a, h.d1);
-      }
-      work(uc);
-    };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    using I4 = std::integral_constant<int, 4>;
-    using I5 = std::integral_constant<int, 5>;
-    using I6 = std::integral_constant<int, 6>;
-    using I7 = std::integral_constant<int, 7>;
-    using W2 = std::integral_constant<int, 2 * UR>;
-    using W1 = std::integral_constant<int, UR>;
-    using W0 = std::integral_constant<int, 0>;
-    rd(I0{}), rd(I1{}), rd(I2{});
-    wt(I0{}, W2{}), rd(I3{}), mm(I0{});
-    wt(I1{}, W2{}), rd(I4{}), mm(I1{});
-    wt(I2{}, W2{}), rd(I5{}), mm(I2{});
-    wt(I3{}, W2{}), rd(I6{}), mm(I3{});
-    wt(I4{}, W2{}), rd(I7{}), mm(I4{});
-    wt(I5{}, W2{}), mm(I5{});
-    wt(I6{}, W1{}), mm(I6{});
-    wt(I7{}, W0{}), mm(I7{});
+    const bf16x8 d0 = __builtin_convertvector(x0, bf16x8), d1 = __builtin_convertvector(x1, bf16x8);
+    uint32_t tlo[D / 32], thi[D / 32];
+    uo.trs(st, tlo, thi);
+    tr_products<D, 0>(tlo, thi, acc, d0, d1);  // dK^T += Q^T dS, Q read transposed
   };
 
-  // Ring of NBUF = 4 stages, the DMA of block s + 2 issued at iteration s: its
-  // buffer last held block s - 2, whose tail ran in iteration s - 1.  It is
-  // issued after block s's products, so that its scalar work runs beside them.
-  for (int j = 0; j < 2 && j < steps; ++j) {
-    issue(dw, j);
-    advance(dw);
-  }
-  Walk hw;  // the products' walk (only q0 and qblk are used)
-  hw.qblk = 0, hw.q0 = qb_lo * BM, hw.qoff = 0, hw.ooff = 0, hw.loff = 0;
-  HeadOut prev;
-  auto nothing = [](auto) __attribute__((always_inline)) {};
-  // one step: block s's head, tail(s - 1) with block s's P and dS formed between
-  // its products (the first step, with no tail before it, is peeled off so that
-  // the loop has a single path for the accumulators)
-  auto step = [&](int s_, bool first) __attribute__((always_inline)) {
-    // block s landed; block s + 1 may still be in flight
-    if (s_ + 1 < steps)
-      wait_vmcnt<kPer>();
-    else
-      wait_vmcnt<0>();
-    stage_barrier();
-    const int buf = s_ % NBUF;
-    const HeadState hs = head(buf, hw.q0);
-    if (s_ + 2 < steps) {
-      issue(dw, (s_ + 2) % NBUF);
+  // Ring of NBUF = 4 stages.  Iteration t: the P waves process block t (its DMA
+  // landed; they issue block t + 2's, whose stage last held block t - 2, read
+  // by the dK waves in iteration t - 1) and the dK waves block t - 1 (P written
+  // by the P waves in iteration t - 1, before this iteration's barrier).  Every
+  // wave passes the same steps + 1 barriers.
+  if (pwave) {
+    for (int j = 0; j < 2 && j < steps; ++j) {
+      issue(dw, j);
       advance(dw);
     }
-    Packed pk;
-    auto work = [&](auto uc) __attribute__((always_inline)) {
-      scores(hs, pk, std::integral_constant<int, 2 * decltype(uc)::value>{});
-    };
-    if (first) {
-      work(std::integral_constant<int, 0>{}), work(std::integral_constant<int, 1>{});
-      work(std::integral_constant<int, 2>{}), work(std::integral_constant<int, 3>{});
-      work(std::integral_constant<int, 4>{}), work(std::integral_constant<int, 5>{});
-      work(std::integral_constant<int, 6>{}), work(std::integral_constant<int, 7>{});
-    } else {
-      tail((s_ + NBUF - 1) % NBUF, prev, work);
+  }
+  for (int it = 0; it <= steps; ++it) {
+    if (pwave && it < steps) {
+      // block it landed; block it + 1 may still be in flight
+      if (it + 1 < steps)
+        wait_vmcnt<kPer>();
+      else
+        wait_vmcnt<0>();
     }
-    prev = pack(pk);
-    hw.q0 += BM;
-    if (++hw.qblk == nqb) hw.qblk = 0, hw.q0 = qb_lo * BM;
-    // Settle the accumulators before the iteration ends: the compiler may copy
-    // them between registers at the loop's edges and does not see that the
-    // products above are still writing them.
-    drain_acc(dk, dv);
-  };
-  if (steps > 0) step(0, true);
-  for (int s_ = 1; s_ < steps; ++s_) step(s_, false);
-  if (steps > 0) {
-    tail((steps - 1) % NBUF, prev, nothing);
-    drain_acc(dk, dv);
+    stage_barrier();
+    if (pwave) {
+      if (it < steps) p_step(it);
+    } else {
+      if (it > 0) k_step(it - 1);
+    }
   }
   if (key_ok) {
-    uint16_t* kout = p.dk + b * p.dk_bs + (int64_t)key * p.dk_ss + kvh * p.dk_hs;
-    uint16_t* vout = p.dv + b * p.dv_bs + (int64_t)key * p.dv_ss + kvh * p.dv_hs;
+    uint16_t* out = pwave ? p.dv + b * p.dv_bs + (int64_t)key * p.dv_ss + kvh * p.dv_hs
+                          : p.dk + b * p.dk_bs + (int64_t)key * p.dk_ss + kvh * p.dk_hs;
+    const float sc = pwave ? 1.0f : p.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        f32x8 x = {}, y = {};
+        f32x8 x = {};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = dk[db][4 * q4 + e] * p.scale;
-          y[e] = dv[db][4 * q4 + e];
-        }
+        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * q4 + e] * sc;
         const u32x4 xb = __builtin_bit_cast(u32x4, __builtin_convertvector(x, bf16x8));
-        const u32x4 yb = __builtin_bit_cast(u32x4, __builtin_convertvector(y, bf16x8));
-        *reinterpret_cast<u32x2*>(kout + 32 * db + 8 * q4 + 4 * kg) = u32x2{xb.x, xb.y};
-        *reinterpret_cast<u32x2*>(vout + 32 * db + 8 * q4 + 4 * kg) = u32x2{yb.x, yb.y};
+        *reinterpret_cast<u32x2*>(out + 32 * db + 8 * q4 + 4 * kg) = u32x2{xb.x, xb.y};
       }
   }
 }
@@ -2626,10 +2580,10 @@ hipError_t fa_launch_bwd(const FaBwdParams& p, int d, hipStream_t s) {
   const int64_t dkv_tiles = (int64_t)((p.Nk + 127) / 128) * p.B * p.Hkv;
   if (d == 128) {
     hipLaunchKernelGGL(fa_bwd_dq_kernel<128>, dim3((unsigned)dq_tiles), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<128>, dim3((unsigned)dkv_tiles), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<128>, dim3((unsigned)dkv_tiles), dim3(2 * kThreads), 0, s, p);
   } else if (d == 64) {
     hipLaunchKernelGGL(fa_bwd_dq_kernel<64>, dim3((unsigned)dq_tiles), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<64>, dim3((unsigned)dkv_tiles), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<64>, dim3((unsigned)dkv_tiles), dim3(2 * kThreads), 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }
