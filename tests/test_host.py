@@ -375,12 +375,24 @@ def test_query_range_matches_brute_force(tmp_path):
     assert cases > 1_000_000 and bad == 0, r.stdout
 
 
+def test_prefill_rejects_grids_of_2_31_tiles():
+    """The prefill kernels map a workgroup to its tile in 32-bit arithmetic: a call with
+    2^31 tiles or more is refused before any device work (2^20 or 2^19 sequences x 4096
+    heads x one row block)."""
+    L = api.lib()
+    o = _opts()
+    assert L.fa_fwd(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None, 1 << 20, 16, 16, 4096, 4096, 128,
+                    S3, S3, S3, S3, None) == FA_ERR_UNSUPPORTED
+    assert L.fa_fwd(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None, 1 << 19, 16, 16, 4096, 4096, 128,
+                    S3, S3, S3, S3, None) == FA_ERR_UNSUPPORTED          # exactly 2^31
+
+
 def test_bwd_rejects_invalid_arguments():
     L = api.lib()
-    def call(opts=None, q=FAKE, d=128, B=1, ws=FAKE, ws_bytes=1 << 20, Hq=16, Hkv=16):
+    def call(opts=None, q=FAKE, d=128, B=1, ws=FAKE, ws_bytes=1 << 20, Hq=16, Hkv=16, qs=S3, dos=S3):
         o = opts or _opts()
         return L.fa_bwd(ctypes.byref(o), q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, 16, 16, Hq, Hkv, d,
-                        S3, S3, S3, S3, S3, S3, S3, S3, ws, ws_bytes, None)
+                        qs, S3, S3, S3, dos, S3, S3, S3, ws, ws_bytes, None)
     assert call(q=None) == FA_ERR_INVALID_ARG
     assert call(d=96) == FA_ERR_UNSUPPORTED
     assert call(B=0) == FA_ERR_INVALID_ARG
@@ -388,6 +400,12 @@ def test_bwd_rejects_invalid_arguments():
     assert call(ws=None) == FA_ERR_INVALID_ARG
     assert call(ws_bytes=16) == FA_ERR_INVALID_ARG
     assert call(opts=_opts(softcap=30.0)) == FA_ERR_UNSUPPORTED
+    # the dK/dV kernel addresses a 32-row Q or dO block with 32-bit offsets, and reaches the
+    # base-2 LSE array from the D array with one
+    far = (ctypes.c_int64 * 3)(1 << 40, 1 << 25, 128)
+    assert call(qs=far) == FA_ERR_UNSUPPORTED
+    assert call(dos=far) == FA_ERR_UNSUPPORTED
+    assert call(B=2_200_000, ws_bytes=1 << 34) == FA_ERR_UNSUPPORTED   # 5.6e8 query rows
     assert api.lib().fa_bwd_workspace_size(4, 4096, 16) == 2 * 4 * 16 * 4096 * 4
     assert api.lib().fa_bwd_workspace_size(1, 3, 1) == 2 * 256
 
