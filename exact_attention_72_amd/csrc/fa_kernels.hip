@@ -163,9 +163,17 @@ __device__ __forceinline__ void dma16(const uint16_t* src, char* lds_dst) {
 // offset, so a block's source address costs scalar instructions only instead
 // of 64-bit vector address arithmetic per load.  Raw buffer (stride 0), 32-bit
 // data format (the gfx9 resource word 3).
+// The base must be the same in every lane (callers pass wave-uniform addresses);
+// it is taken from the first lane, so that the resource lives in scalar registers
+// even where the compiler cannot prove the address uniform (a varlen tile found
+// by a ballot) and would otherwise wrap each load in a loop over distinct values.
 constexpr int kBufRsrcWord3 = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, kBufRsrcWord3);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, 0x7fffffff, kBufRsrcWord3);
 }
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char* lds_dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds_dst, 16, (int)voff, (int)soff, 0, 0);
