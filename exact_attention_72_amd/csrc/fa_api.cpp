@@ -929,6 +929,11 @@ int fa_fwd_fp8(const fa_attn_opts* opts, const void* q, const float* q_scales, c
       (rc = check_strides("out", out, o_strides, 3)))
     return rc;
   if (!aligned16(vt)) return fail(FA_ERR_INVALID_ARG, "vt is not 16-byte aligned");
+  // the kernel addresses a 64-key block of K and a block of V^T with 32-bit byte offsets
+  if (k_strides[1] >= ((int64_t)1 << 25))
+    return fail(FA_ERR_UNSUPPORTED, "k token stride %lld is 2^25 bytes or more", (long long)k_strides[1]);
+  if ((int64_t)head_dim * fa_fp8_vt_len(seqlen_k) >= ((int64_t)1 << 31))
+    return fail(FA_ERR_UNSUPPORTED, "seqlen_k %d is too long for the FP8 forward", seqlen_k);
   FaParams tmp;
   memset(&tmp, 0, sizeof tmp);
   bool softcap = false;

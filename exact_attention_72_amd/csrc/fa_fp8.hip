@@ -120,6 +120,17 @@ __device__ __forceinline__ float scalar_load_f32(const float* ptr) {
   return v;
 }
 
+// LDS-DMA through a buffer resource (buffer_load_dwordx4 ... lds): the base in
+// scalar registers (taken from the first lane; callers pass wave-uniform
+// addresses), a 32-bit byte offset per lane and one per instruction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, 0x7fffffff, 0x00020000);
+}
+
 // Position p of a 64-key group in the product's k order <-> key of the group:
 // p = 32 kg + 16 hb + 4 j + i holds key 32 hb + 8 j + 4 kg + i, which is where
 // the S^T accumulator of half hb keeps that key for lane half kg (slot 4 j + i).
@@ -296,17 +307,19 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
   span.pos_hi = (int64_t)(m_end - 1) + (Lk - Lq);
   int n_lo, n_hi;
   fa_key_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &n_lo, &n_hi);
-  int n_full_lo = n_hi, n_full_hi = n_hi;  // key blocks [n_full_lo, n_full_hi) need no element mask
-  for (int n = n_lo; n < n_hi; ++n)
-    if (!(fa_tile_class(span, Lk, p.causal, p.wl, p.wr, BN, n) & (FA_TILE_MASK_LEFT | FA_TILE_MASK_RIGHT))) {
-      n_full_lo = n;
-      break;
+  // key blocks [n_full_lo, n_full_hi) need no element mask: the closed-form range
+  // of tiles the classifier calls full (one interval), within [n_lo, n_hi)
+  int n_full_lo = n_hi, n_full_hi = n_hi;
+  {
+    int f_lo, f_hi;
+    fa_full_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &f_lo, &f_hi);
+    f_lo = max(f_lo, n_lo);
+    f_hi = min(f_hi, n_hi);
+    if (f_lo < f_hi) {
+      n_full_lo = f_lo;
+      n_full_hi = f_hi;
     }
-  for (int n = n_full_lo; n < n_hi; ++n)
-    if (fa_tile_class(span, Lk, p.causal, p.wl, p.wr, BN, n) & (FA_TILE_MASK_LEFT | FA_TILE_MASK_RIGHT)) {
-      n_full_hi = n;
-      break;
-    }
+  }
   const int nb = n_hi - n_lo;
 
   // ---- this lane's query row: Q as the B operand (32 bytes of each 64-dim chunk)
@@ -334,9 +347,32 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
   // and 1 KiB of V^T (rows (4 j + w) * 16 ..); this lane's chunk of each
   const uint8_t* kbase = p.k + (int64_t)b * p.k_bs + (int64_t)kvh * p.k_hs;
   const uint8_t* vtbase = p.vt + ((int64_t)b * p.Hkv + kvh) * D * p.npad;
+  // A full block goes through buffer resources based at its first key: this
+  // lane's row of instruction 0 and its chunk are fixed (the swizzles depend on
+  // row bits that the 32- and 64-row steps between instructions leave alone), so
+  // each instruction adds only a scalar offset (the host keeps 64 K rows and the
+  // D V^T rows below 2^31 bytes).  A final partial block keeps per-lane
+  // addresses, its rows clamped to the last key.
+  const int kr0 = wave * 8 + lane / 8, vr0 = wave * 16 + lane / 4;
+  const uint32_t k_voff = (uint32_t)(kr0 * p.k_ss) + 16u * (uint32_t)((lane & 7) ^ ((kr0 >> 1) & 7));
+  const uint32_t v_voff = (uint32_t)(vr0 * p.npad) + 16u * (uint32_t)((lane & 3) ^ ((vr0 >> 2) & 3));
+  const uint32_t k_step = (uint32_t)(32 * p.k_ss), v_step = (uint32_t)(64 * p.npad);
   auto issue = [&](int i) __attribute__((always_inline)) {
     char* st = smem + (i % NBUF) * STAGE;
     const int n = n_lo + i;
+    if ((n + 1) * BN <= Lk) {
+      const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kbase + (int64_t)n * BN * p.k_ss);
+      const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vtbase + (int64_t)n * BN);
+#pragma unroll
+      for (int j = 0; j < KT / 4096; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(st + (4 * j + wave) * 1024), 16, (int)k_voff,
+                                                 (int)(j * k_step), 0, 0);
+#pragma unroll
+      for (int j = 0; j < VT / 4096; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(st + KT + (4 * j + wave) * 1024), 16,
+                                                 (int)v_voff, (int)(j * v_step), 0, 0);
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < KT / 4096; ++j) {
       const int r = (4 * j + wave) * 8 + lane / 8;
