@@ -794,6 +794,12 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
     span.pos_hi = (int64_t)((m_end - 1) / p.gp) + (Lk - Lq);
     int n_lo, n_hi;
     fa_key_tiles(span, Lk, p.causal, p.wl, p.wr, BN, &n_lo, &n_hi);
+    // the mod's per-tile state, and the key blocks its mask leaves in range
+    const typename MOD::Tile mod_tile = MOD{}.tile(tile.b, p.mod);
+    if constexpr (MOD::kBlocks) {
+      const int k_end = MOD{}.key_end((int)span.pos_lo, (int)span.pos_hi, mod_tile);
+      n_hi = max(n_lo, min(n_hi, (int)(((int64_t)k_end + BN - 1) / BN)));
+    }
     // key blocks [n_full_lo, n_full_hi) need no element mask: the closed-form
     // range of tiles the classifier calls full (one interval, checked against the
     // classifier on the host), within [n_lo, n_hi)
@@ -952,13 +958,24 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
       if constexpr (kMod) {
         const MOD mod{};
         const int base = (n_lo + i) * BN + 4 * kg;
+        // the mask only on blocks the mod cannot vouch for as visible whole
+        bool masks = MOD::kMask;
+        if constexpr (MOD::kMask && MOD::kBlocks)
+          masks = !mod.block_visible((int)span.pos_lo, (int)span.pos_hi, (n_lo + i) * BN, (n_lo + i) * BN + BN - 1,
+                                     mod_tile);
+        if constexpr (MOD::kScore) {
 #pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int key = base + 8 * (a >> 2) + (a & 3);
-          float x = sv[a];
-          if constexpr (MOD::kScore) x = mod.score(x * p.scale, tile.b, head, mask.pos, key, p.mod) * kLog2e;
-          if constexpr (MOD::kMask) x = mod.mask(tile.b, head, mask.pos, key, p.mod) ? x : kNegInf;
-          sv[a] = x;
+          for (int a = 0; a < 16; ++a) {
+            const int key = base + 8 * (a >> 2) + (a & 3);
+            sv[a] = mod.score(sv[a] * p.scale, tile.b, head, mask.pos, key, mod_tile, p.mod) * kLog2e;
+          }
+        }
+        if (MOD::kMask && masks) {
+#pragma unroll
+          for (int a = 0; a < 16; ++a) {
+            const int key = base + 8 * (a >> 2) + (a & 3);
+            sv[a] = mod.mask(tile.b, head, mask.pos, key, mod_tile, p.mod) ? sv[a] : kNegInf;
+          }
         }
       }
     };

@@ -10,8 +10,13 @@
  *
  *   static constexpr bool kScore;   // score() is applied
  *   static constexpr bool kMask;    // mask() is applied
- *   __device__ float score(float s, int b, int h, int p, int j, const FaModArgs& a) const;
- *   __device__ bool  mask(int b, int h, int p, int j, const FaModArgs& a) const;
+ *   static constexpr bool kBlocks;  // key_end() and block_visible() narrow the work
+ *   struct Tile;                    // per-tile state
+ *   __device__ Tile  tile(int b, const FaModArgs& a) const;
+ *   __device__ float score(float s, int b, int h, int p, int j, const Tile& t, const FaModArgs& a) const;
+ *   __device__ bool  mask(int b, int h, int p, int j, const Tile& t, const FaModArgs& a) const;
+ *   __device__ int   key_end(int p_lo, int p_hi, const Tile& t) const;
+ *   __device__ bool  block_visible(int p_lo, int p_hi, int j0, int j1, const Tile& t) const;
  *
  * where s is the scaled logit softmax_scale * q.k in natural-log units, b the
  * batch index, h the query head, p the query's position on the key axis
@@ -22,6 +27,15 @@
  * key the built-in masks drop is dropped whatever mask() says, and score() is
  * not consulted for it.  A key every rule leaves visible enters the softmax with
  * the rewritten logit; a row left with no visible key gets O = 0, LSE = -inf.
+ *
+ * tile() runs once per tile of query rows (all of sequence b) and loads what the
+ * mod needs of sequence b, so that score() and mask() touch no memory per score;
+ * it must read wave-uniform addresses only (fa_mod_uniform_i32 does a scalar
+ * load).  With kBlocks, key_end() bounds the keys mask() can keep for query
+ * positions p_lo .. p_hi (keys at or past it are never visible; the kernel skips
+ * their blocks) and block_visible() says whether mask() keeps every pair of those
+ * positions with keys j0 .. j1 (the kernel then skips mask() on that block).  Both
+ * may be conservative (a larger bound, false) but never optimistic.
  *
  * FaModArgs carries the launch's parameters for the mod (a device pointer and
  * a few scalars), filled by the entry point that instantiates it.  To add a
@@ -42,12 +56,28 @@ struct FaModArgs {
 
 #ifdef __HIPCC__
 
+// A 32-bit value at a wave-uniform address, by a scalar load.
+__device__ __forceinline__ int32_t fa_mod_uniform_i32(const int32_t* ptr) {
+  const uint64_t u = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  const int32_t* q = reinterpret_cast<const int32_t*>(((uint64_t)hi << 32) | lo);
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(q) : "memory");
+  return v;
+}
+
 // No rewrite, no extra mask: the plain kernel.
 struct FaNoMod {
   static constexpr bool kScore = false;
   static constexpr bool kMask = false;
-  __device__ __forceinline__ float score(float s, int, int, int, int, const FaModArgs&) const { return s; }
-  __device__ __forceinline__ bool mask(int, int, int, int, const FaModArgs&) const { return true; }
+  static constexpr bool kBlocks = false;
+  struct Tile {};
+  __device__ __forceinline__ Tile tile(int, const FaModArgs&) const { return {}; }
+  __device__ __forceinline__ float score(float s, int, int, int, int, const Tile&, const FaModArgs&) const { return s; }
+  __device__ __forceinline__ bool mask(int, int, int, int, const Tile&, const FaModArgs&) const { return true; }
+  __device__ __forceinline__ int key_end(int, int, const Tile&) const { return 0x7fffffff; }
+  __device__ __forceinline__ bool block_visible(int, int, int, int, const Tile&) const { return true; }
 };
 
 // Learned relative-position bias (score_mod): the logit of query position p and
@@ -57,25 +87,45 @@ struct FaNoMod {
 struct FaRelPosBias {
   static constexpr bool kScore = true;
   static constexpr bool kMask = false;
-  __device__ __forceinline__ float score(float s, int, int h, int p, int j, const FaModArgs& a) const {
+  static constexpr bool kBlocks = false;
+  struct Tile {};
+  __device__ __forceinline__ Tile tile(int, const FaModArgs&) const { return {}; }
+  __device__ __forceinline__ float score(float s, int, int h, int p, int j, const Tile&, const FaModArgs& a) const {
     const int R = (int)a.i1;
     int r = j - p;
     r = r < -R ? -R : (r > R ? R : r);
     return s + static_cast<const float*>(a.ptr)[(int64_t)h * a.i0 + r + R];
   }
-  __device__ __forceinline__ bool mask(int, int, int, int, const FaModArgs&) const { return true; }
+  __device__ __forceinline__ bool mask(int, int, int, int, const Tile&, const FaModArgs&) const { return true; }
+  __device__ __forceinline__ int key_end(int, int, const Tile&) const { return 0x7fffffff; }
+  __device__ __forceinline__ bool block_visible(int, int, int, int, const Tile&) const { return true; }
 };
 
 // Prefix-LM mask (mask_mod): the first prefix_len[b] keys of sequence b are
 // visible to every query (a bidirectional prefix), later keys causally (key j
 // visible to the query at position p iff j < prefix_len[b] or j <= p).
-// a.ptr: device int32 [batch].
+// a.ptr: device int32 [batch].  Keys at or past max(prefix_len[b], p_hi + 1) are
+// never visible; a block of keys is visible whole when it ends inside the prefix
+// or at or before the first position.
 struct FaPrefixLM {
   static constexpr bool kScore = false;
   static constexpr bool kMask = true;
-  __device__ __forceinline__ float score(float s, int, int, int, int, const FaModArgs&) const { return s; }
-  __device__ __forceinline__ bool mask(int b, int, int p, int j, const FaModArgs& a) const {
-    return j < static_cast<const int32_t*>(a.ptr)[b] || j <= p;
+  static constexpr bool kBlocks = true;
+  struct Tile {
+    int prefix;
+  };
+  __device__ __forceinline__ Tile tile(int b, const FaModArgs& a) const {
+    return {fa_mod_uniform_i32(static_cast<const int32_t*>(a.ptr) + b)};
+  }
+  __device__ __forceinline__ float score(float s, int, int, int, int, const Tile&, const FaModArgs&) const { return s; }
+  __device__ __forceinline__ bool mask(int, int, int p, int j, const Tile& t, const FaModArgs&) const {
+    return j < t.prefix || j <= p;
+  }
+  __device__ __forceinline__ int key_end(int, int p_hi, const Tile& t) const {
+    return t.prefix > p_hi + 1 ? t.prefix : p_hi + 1;
+  }
+  __device__ __forceinline__ bool block_visible(int p_lo, int, int, int j1, const Tile& t) const {
+    return j1 < t.prefix || j1 <= p_lo;
   }
 };
 
