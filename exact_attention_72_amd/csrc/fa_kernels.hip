@@ -970,6 +970,13 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
             sv[a] = mod.score(sv[a] * p.scale, tile.b, head, mask.pos, key, mod_tile, p.mod) * kLog2e;
           }
         }
+        if constexpr (MOD::kMask && MOD::kBlocks) {
+          // The path that skips the mask loop joins the one that runs it, and
+          // the compiler's hazard search (one visit per block) then misses the
+          // S product on the shorter path: wait for the product before the
+          // branch.
+          asm volatile("s_nop 7\n\ts_nop 3" : "+v"(sv));
+        }
         if (MOD::kMask && masks) {
 #pragma unroll
           for (int a = 0; a < 16; ++a) {
