@@ -3,8 +3,8 @@
 A step is one forward pass of the dense causal prefill workload
 (batch 4, 16 heads, N = 4096, d = 128, bf16) through the C ABI.  The line also
 carries, as secondary figures, the paged split-KV decode measurement (64
-sequences, 32/8 heads, d = 128, 256-token pages, num_splits in {1, 4, 16}),
-the varlen GQA prefill (32 sequences of 64..8192 tokens, 32/4 heads, packed),
+sequences, 32/8 heads, d = 128, 256-token pages, num_splits in {1, 4, 16}) and
+the same decode over an FP8 (e4m3) cache, the varlen GQA prefill (32 sequences of 64..8192 tokens, 32/4 heads, packed),
 the long-context local attention with softcap (N = 32768, 32 heads,
 window 4096, softcap 30), and the chunked prefill over a paged cache (4 x 4096
 new tokens against 16384 cached keys, 32/8 heads) with the in-place K/V append
@@ -435,7 +435,7 @@ def bench_decode(api, W, steps, warmup):
     # gets with num_splits = 0)
     best = max((1, 4, 16, 0), key=lambda s: res[s]["kv_GBps"])
     return {"metric": "paged decode KV GB/s", "unit": "GB/s",
-            "value": res[best]["kv_GBps"], "num_splits": best or auto,
+            "value": res[best]["kv_GBps"], "ms": round(res[best]["ms"], 4), "num_splits": best or auto,
             "num_splits_auto": auto,
             "kv_bytes": kv_bytes,
             "per_split": {(str(s) if s else "auto"): {"ms": round(r["ms"], 4), "kv_GBps": round(r["kv_GBps"], 1)}
@@ -448,6 +448,46 @@ def bench_decode(api, W, steps, warmup):
                        "page_size": c["page"], "cache_seqlens": "uniform [1024, 32768]"}}
 
 
+def bench_decode_fp8(api, W, steps, warmup, bf16_ms=None):
+    """The decode workload over an FP8 (e4m3) cache (fa_fwd_kvcache_paged_fp8): the same
+    sequences, heads and pages, one byte per cached element."""
+    import torch
+    c = W.WORKLOADS["paged_decode_b64_h32kv8_d128_page256"]
+    t = W.paged_fp8(c["seed"], c["B"], c["Hq"], c["Hkv"], c["d"], c["page"], c["lo"], c["hi"],
+                    max_blocks=c["max_blocks"], device="cuda")
+    del t["k_cache"], t["v_cache"]
+    torch.cuda.empty_cache()
+    bt, sl = t["block_table"].cuda(), t["cache_seqlens"].cuda()
+    kv_bytes = 2048.0 * float(t["cache_seqlens"].sum())   # K and V of live tokens, one byte each
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((c["B"], c["Hq"], 1), dtype=torch.float32, device="cuda")
+    res = {}
+    auto = api.fa_kvcache_num_splits(c["B"], 1, c["Hq"], c["Hkv"], c["page"], c["max_blocks"])
+    for S in (1, 4, 16, 0):
+        need = api.fa_kvcache_workspace_size(c["B"], 1, c["Hq"], c["d"], S or auto)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        fn = lambda: api.fa_fwd_kvcache_paged_fp8(t["q"], t["k_codes"], t["v_codes"], t["k_scale"],  # noqa
+                                                  t["v_scale"], bt, sl, num_splits=S, out=out, lse=lse,
+                                                  workspace=ws)
+        wall, ms, _ = time_launches(fn, steps, warmup)
+        res[S] = {"ms": ms, "kv_GBps": kv_bytes / (ms * 1e-3) / 1e9}
+    best = max((1, 4, 16, 0), key=lambda s: res[s]["kv_GBps"])
+    r = {"metric": "paged decode over an FP8 KV cache, KV GB/s", "unit": "GB/s",
+         "value": res[best]["kv_GBps"], "ms": round(res[best]["ms"], 4), "num_splits": best or auto,
+         "kv_bytes": kv_bytes,
+         "per_split": {(str(s) if s else "auto"): {"ms": round(q["ms"], 4), "kv_GBps": round(q["kv_GBps"], 1)}
+                       for s, q in res.items()},
+         "roofline": {"bound": "hbm", "achieved": res[best]["kv_GBps"], "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": res[best]["kv_GBps"] / PEAK_HBM_GBS,
+                      "traffic": stored_traffic("fa_paged_kernel_fp8")},
+         "config": {"workload": "paged_decode_b64_h32kv8_d128_page256 (e4m3 cache)", "batch": c["B"],
+                    "heads_q": c["Hq"], "heads_kv": c["Hkv"], "head_dim": c["d"],
+                    "page_size": c["page"], "cache_seqlens": "uniform [1024, 32768]"}}
+    if bf16_ms:
+        r["speedup_vs_bf16_cache"] = round(bf16_ms / res[best]["ms"], 3)
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -458,6 +498,7 @@ def main():
                          "has settled (two successive 20-launch windows within 1 %%)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode-fp8", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-local", action="store_true")
     ap.add_argument("--no-paged-prefill", action="store_true")
@@ -516,6 +557,10 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_decode:
         line["decode"] = bench_decode(api, W, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if not args.no_decode_fp8:
+        line["decode_fp8"] = bench_decode_fp8(api, W, args.steps, args.warmup,
+                                              line.get("decode", {}).get("ms"))
         torch.cuda.empty_cache()
     if not args.no_varlen:
         line["varlen"] = bench_varlen(api, W, args.steps, args.warmup)

@@ -26,6 +26,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_relpos_bias", "fa_fwd_prefix_lm", "fa_fwd_varlen", 
            "fa_kvcache_num_splits",
            "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary", "fa_bwd", "fa_bwd_workspace_size",
            "fa_fp8_quantize", "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8",
+           "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8",
            "fa_combine", "fa_merge_attn_states", "fa_tile_class", "fa_last_error", "fa_version")
 
 FA_FP8_Q_BLOCK = 128
@@ -67,6 +68,9 @@ def lib():
                                        S3, S3, S3, S3, P]
     L.fa_fwd_kvcache_paged_noalloc.argtypes = [OPT, P, P, P, P, P, P, P, I, I, I, I, I, I64, I, I, I,
                                                S3, S3, S3, S3, P]
+    L.fa_fwd_kvcache_paged_fp8.argtypes = [OPT, P, P, P, F, F, P, P, P, P, I, I, I, I, I, I64, I, I, I, P, SZ,
+                                           S3, S3, S3, S3, P]
+    L.fa_kvcache_append_fp8.argtypes = [P, P, P, P, F, F, P, P, I, I, I, I, I64, I, I, S3, S3, S3, S3, P]
     L.fa_kvcache_workspace_size.argtypes = [I, I, I, I, I]
     L.fa_kvcache_workspace_size.restype = SZ
     L.fa_kvcache_num_splits.argtypes = [I, I, I, I, I, I]
@@ -94,6 +98,7 @@ def lib():
     for name in ("fa_fwd", "fa_fwd_relpos_bias", "fa_fwd_prefix_lm", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
                  "fa_combine", "fa_merge_attn_states", "fa_tile_class",
                  "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary", "fa_bwd", "fa_fp8_quantize",
+                 "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8",
                  "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8"):
         getattr(L, name).restype = I
     _lib = L
@@ -277,6 +282,44 @@ def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num
     return out, lse
 
 
+def fa_fwd_kvcache_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cache_seqlens, *, num_splits=1,
+                             softmax_scale=None, causal=True, window=None, softcap=0.0, out=None, lse=None,
+                             workspace=None, return_lse=True, stream=None):
+    """Paged-KV decode over an FP8 (e4m3) cache.  q [B, Nq, Hq, d] bf16 with Nq * Hq / Hkv <= 32;
+    caches uint8 [num_pages, page, Hkv, d] of codes whose values are code * k_scale and
+    code * v_scale (floats); block_table int32 [B, max_blocks]; cache_seqlens int32 [B]
+    -> (out, lse [B, Hq, Nq]).  num_splits=0 picks the split count (fa_kvcache_num_splits)."""
+    _bf16_cuda(q)
+    _u8_cuda(k_cache, v_cache)
+    B, Nq, Hq, d = q.shape
+    num_pages, page, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    for c in (block_table, cache_seqlens):
+        if c.dtype != torch.int32 or not c.is_cuda:
+            raise TypeError("block_table and cache_seqlens must be int32 device tensors")
+    if block_table.stride(-1) != 1 or block_table.stride(0) != block_table.shape[1]:
+        raise ValueError("block_table must be a contiguous [batch, max_blocks] tensor")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _bf16_cuda(out)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if num_splits == 0:
+        num_splits = fa_kvcache_num_splits(B, Nq, Hq, Hkv, page, block_table.shape[1])
+    need = fa_kvcache_workspace_size(B, Nq, Hq, d, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    o = _opts(softmax_scale, causal, window, softcap, -1)
+    _check(lib().fa_fwd_kvcache_paged_fp8(ctypes.byref(o), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                          float(k_scale), float(v_scale), _ptr(block_table), _ptr(cache_seqlens),
+                                          _ptr(out), _ptr(lse), B, Nq, Hq, Hkv, d, num_pages, page,
+                                          block_table.shape[1], int(num_splits), _ptr(workspace), ws_bytes,
+                                          _strides(q, (0, 1, 2)), _strides(k_cache, (0, 1, 2)),
+                                          _strides(v_cache, (0, 1, 2)), _strides(out, (0, 1, 2)),
+                                          _stream(stream)))
+    return out, lse
+
+
 FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -391,6 +434,29 @@ def fa_kvcache_append(k_new, v_new, k_cache, v_cache, block_table, cache_seqlens
                                    _strides(k_cache, (0, 1, 2)), _strides(v_cache, (0, 1, 2)),
                                    _ptr(cos), _ptr(sin), rdim, int(bool(rotary_interleaved)),
                                    _stream(stream)))
+
+
+def fa_kvcache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, cache_seqlens, *,
+                          stream=None):
+    """Quantize k_new/v_new [B, L, Hkv, d] (bf16) to e4m3 codes of x / k_scale and x / v_scale
+    and write them into the uint8 caches [num_pages, page, Hkv, d] at logical positions
+    cache_seqlens[b] + t (in place; cache_seqlens is not updated)."""
+    _bf16_cuda(k_new, v_new)
+    _u8_cuda(k_cache, v_cache)
+    B, L, Hkv, d = k_new.shape
+    if tuple(v_new.shape) != (B, L, Hkv, d) or k_cache.shape != v_cache.shape or k_cache.shape[2:] != (Hkv, d):
+        raise ValueError("k_new/v_new [B, L, Hkv, d] and caches [num_pages, page, Hkv, d] disagree")
+    for c in (block_table, cache_seqlens):
+        if c.dtype != torch.int32 or not c.is_cuda:
+            raise TypeError("block_table and cache_seqlens must be int32 device tensors")
+    if block_table.stride(-1) != 1 or block_table.stride(0) != block_table.shape[1]:
+        raise ValueError("block_table must be a contiguous [batch, max_blocks] tensor")
+    _check(lib().fa_kvcache_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), float(k_scale),
+                                       float(v_scale), _ptr(block_table), _ptr(cache_seqlens), B, L, Hkv, d,
+                                       k_cache.shape[0], k_cache.shape[1], block_table.shape[1],
+                                       _strides(k_new, (0, 1, 2)), _strides(v_new, (0, 1, 2)),
+                                       _strides(k_cache, (0, 1, 2)), _strides(v_cache, (0, 1, 2)),
+                                       _stream(stream)))
 
 
 def fa_bwd(q, k, v, out, lse, dout, *, softmax_scale=None, causal=False, window=None, dq=None, dk=None,

@@ -475,15 +475,23 @@ size_t fa_kvcache_workspace_size(int batch, int seqlen_q, int heads_q, int head_
 
 namespace {
 
-// fa_fwd_kvcache_paged and its no-allocation twin.  With use_scratch the partials
-// and the sequence order go to the library's static device scratch (after the
-// size check, nothing else touches the device first) instead of the workspace.
+// FP8 (e4m3) cache of fa_fwd_kvcache_paged_fp8: its two scales.
+struct KvFp8 {
+  bool on;
+  float k_scale, v_scale;
+};
+
+// fa_fwd_kvcache_paged, its no-allocation twin and its FP8-cache variant.  With
+// use_scratch the partials and the sequence order go to the library's static
+// device scratch (after the size check, nothing else touches the device first)
+// instead of the workspace.
 int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_table, const int32_t* cache_seqlens, void* out, float* lse, int batch,
                   int seqlen_q, int heads_q, int heads_kv, int head_dim, int64_t num_pages, int page_size,
                   int max_blocks_per_seq, int num_splits, void* workspace, size_t workspace_bytes,
                   bool use_scratch, const int64_t q_strides[3], const int64_t k_strides[3],
-                  const int64_t v_strides[3], const int64_t o_strides[3], void* stream) {
+                  const int64_t v_strides[3], const int64_t o_strides[3], void* stream,
+                  KvFp8 fp8 = {false, 1.0f, 1.0f}) {
   int rc;
   if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
   if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out)
@@ -494,16 +502,27 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
   if (page_size % 16 != 0) return fail(FA_ERR_INVALID_ARG, "page_size %d is not a multiple of 16", page_size);
   if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
     return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
-  if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
-      (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)) ||
-      (rc = check_token_stride("k_cache", k_strides[1])) || (rc = check_token_stride("v_cache", v_strides[1])))
+  if (fp8.on) {
+    if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_byte_strides("k_cache", k_cache, k_strides, 3)) ||
+        (rc = check_byte_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)))
+      return rc;
+    if (!(fp8.k_scale > 0.0f) || !(fp8.v_scale > 0.0f) || isinf(fp8.k_scale) || isinf(fp8.v_scale))
+      return fail(FA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  } else if ((rc = check_strides("q", q, q_strides, 3)) || (rc = check_strides("k_cache", k_cache, k_strides, 3)) ||
+             (rc = check_strides("v_cache", v_cache, v_strides, 3)) || (rc = check_strides("out", out, o_strides, 3)) ||
+             (rc = check_token_stride("k_cache", k_strides[1])) || (rc = check_token_stride("v_cache", v_strides[1]))) {
     return rc;
+  }
   const int g = heads_q / heads_kv;
   if (num_splits == 0)
     num_splits = fa_kvcache_num_splits(batch, seqlen_q, heads_q, heads_kv, page_size, max_blocks_per_seq);
   // more packed query rows than the decode kernel holds: the prefill kernel
   // over the paged cache (chunked prefill), without split-KV
   const bool prefill = (int64_t)seqlen_q * g > FA_PAGED_MAX_ROWS;
+  if (prefill && fp8.on)
+    return fail(FA_ERR_UNSUPPORTED,
+                "fa_fwd_kvcache_paged_fp8 needs seqlen_q * heads_q / heads_kv <= %d (got %lld)",
+                FA_PAGED_MAX_ROWS, (long long)seqlen_q * g);
   if (prefill && num_splits != 1)
     return fail(FA_ERR_UNSUPPORTED,
                 "num_splits > 1 needs seqlen_q * heads_q / heads_kv <= %d (got %lld); use 1 or 0",
@@ -525,7 +544,13 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
   memset(&p, 0, sizeof p);
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
-  if ((rc = no_alibi(p, use_scratch ? "fa_fwd_kvcache_paged_noalloc" : "fa_fwd_kvcache_paged"))) return rc;
+  if ((rc = no_alibi(p, use_scratch ? "fa_fwd_kvcache_paged_noalloc"
+                                    : (fp8.on ? "fa_fwd_kvcache_paged_fp8" : "fa_fwd_kvcache_paged"))))
+    return rc;
+  // S = scale q.(k_scale c_k) = (scale k_scale) q.c_k; O = v_scale sum p c_v
+  p.scale_log2 *= fp8.k_scale;
+  p.cap_in *= fp8.k_scale;
+  p.v_scale = fp8.v_scale;
   if (use_scratch && need > 0) {
     hipError_t e = fa_scratch_region(&workspace);
     if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
@@ -575,7 +600,7 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
       p.seq_order = order;
     }
   }
-  hipError_t e = fa_launch_paged(p, head_dim, softcap, s);
+  hipError_t e = fa_launch_paged(p, head_dim, softcap, fp8.on, s);
   if (e != hipSuccess) return hip_fail(e, "paged launch");
   if (num_splits > 1) {
     // partial row r = (b * Hq + h) * Nq + t of every split, split after split
@@ -614,6 +639,20 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
   return kvcache_paged(opts, q, k_cache, v_cache, block_table, cache_seqlens, out, lse, batch, seqlen_q, heads_q,
                        heads_kv, head_dim, num_pages, page_size, max_blocks_per_seq, num_splits, workspace,
                        workspace_bytes, false, q_strides, k_strides, v_strides, o_strides, stream);
+}
+
+int fa_fwd_kvcache_paged_fp8(const fa_attn_opts* opts, const void* q, const void* k_cache, const void* v_cache,
+                             float k_scale, float v_scale, const int32_t* block_table,
+                             const int32_t* cache_seqlens, void* out, float* lse, int batch, int seqlen_q,
+                             int heads_q, int heads_kv, int head_dim, int64_t num_pages, int page_size,
+                             int max_blocks_per_seq, int num_splits, void* workspace, size_t workspace_bytes,
+                             const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+                             const int64_t o_strides[3], void* stream) {
+  g_err[0] = 0;
+  return kvcache_paged(opts, q, k_cache, v_cache, block_table, cache_seqlens, out, lse, batch, seqlen_q, heads_q,
+                       heads_kv, head_dim, num_pages, page_size, max_blocks_per_seq, num_splits, workspace,
+                       workspace_bytes, false, q_strides, k_strides, v_strides, o_strides, stream,
+                       KvFp8{true, k_scale, v_scale});
 }
 
 int fa_fwd_kvcache_paged_noalloc(const fa_attn_opts* opts, const void* q, const void* k_cache,
@@ -666,6 +705,51 @@ int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void*
   p.cache_seqlens = cache_seqlens;
   p.B = batch; p.L = seqlen_new; p.Hkv = heads_kv; p.page = page_size; p.max_blocks = max_blocks_per_seq;
   p.rot = rot;
+  hipError_t e = fa_launch_append(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return FA_OK;
+}
+
+int fa_kvcache_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache, float k_scale,
+                          float v_scale, const int32_t* block_table, const int32_t* cache_seqlens, int batch,
+                          int seqlen_new, int heads_kv, int head_dim, int64_t num_pages, int page_size,
+                          int max_blocks_per_seq, const int64_t kn_strides[3], const int64_t vn_strides[3],
+                          const int64_t k_strides[3], const int64_t v_strides[3], void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !cache_seqlens)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || seqlen_new < 0 || heads_kv <= 0 || num_pages <= 0 || page_size <= 0 || max_blocks_per_seq <= 0)
+    return fail(FA_ERR_INVALID_ARG,
+                "batch, heads_kv, num_pages, page_size and max_blocks_per_seq must be positive, seqlen_new >= 0");
+  if (page_size % 16 != 0) return fail(FA_ERR_INVALID_ARG, "page_size %d is not a multiple of 16", page_size);
+  if ((int64_t)max_blocks_per_seq * page_size > ((int64_t)1 << 31) - 1)
+    return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size exceeds 2^31 - 1 keys");
+  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale))
+    return fail(FA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+  if ((rc = check_strides("k_new", k_new, kn_strides, 3)) || (rc = check_strides("v_new", v_new, vn_strides, 3)) ||
+      (rc = check_byte_strides("k_cache", k_cache, k_strides, 3)) ||
+      (rc = check_byte_strides("v_cache", v_cache, v_strides, 3)))
+    return rc;
+  if (seqlen_new == 0) return FA_OK;
+  FaAppendParams p;
+  memset(&p, 0, sizeof p);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_cache = static_cast<uint16_t*>(k_cache);
+  p.v_cache = static_cast<uint16_t*>(v_cache);
+  p.kn_bs = kn_strides[0]; p.kn_ss = kn_strides[1]; p.kn_hs = kn_strides[2];
+  p.vn_bs = vn_strides[0]; p.vn_ss = vn_strides[1]; p.vn_hs = vn_strides[2];
+  p.k_ps = k_strides[0]; p.k_ss = k_strides[1]; p.k_hs = k_strides[2];
+  p.v_ps = v_strides[0]; p.v_ss = v_strides[1]; p.v_hs = v_strides[2];
+  p.block_table = block_table;
+  p.cache_seqlens = cache_seqlens;
+  p.B = batch; p.L = seqlen_new; p.Hkv = heads_kv; p.page = page_size; p.max_blocks = max_blocks_per_seq;
+  p.fp8 = 1;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   hipError_t e = fa_launch_append(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return FA_OK;

@@ -57,6 +57,9 @@ struct FaParams {
   // parameters, and the softmax scale the mod's logits carry
   FaModArgs mod;
   float scale;
+  // paged decode over an FP8 (e4m3) cache: the V scale, which multiplies O (the
+  // K scale is folded into scale_log2 / cap_in)
+  float v_scale;
 };
 
 // Mods the library is built with (fa_mods.h), for fa_launch_prefill_mod.
@@ -158,6 +161,10 @@ struct FaAppendParams {
   const int32_t* cache_seqlens;  // lengths before the append
   int B, L, Hkv, page, max_blocks;
   FaRotary rot;                  // applied to the keys (rot.cos == NULL: none)
+  // fp8: the caches hold e4m3 codes (uint8, strides in bytes), x / scale rounded
+  // to nearest even and saturated at +-448; no rotation
+  int fp8;
+  float k_scale, v_scale;
 };
 
 // Merge of partial attention states.  Row r = (b * Hq + h) * Nq + t of
@@ -197,7 +204,8 @@ hipError_t fa_scratch_region(void** ptr);
 // Launchers (fa_kernels.hip).  They return hipSuccess or the launch error.
 hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, bool pack, bool softcap,
                              hipStream_t s);
-hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t stream);
+// fp8: the caches hold e4m3 codes (strides in bytes), p.v_scale multiplies O.
+hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, bool fp8, hipStream_t stream);
 // The unified varlen batch over a paged cache in one launch: pp's prefill tiles
 // first, then pd's decode units (B * Hkv * num_splits workgroups).
 hipError_t fa_launch_unified(const FaParams& pd, const FaParams& pp, int d, bool pack, bool softcap,

@@ -1253,9 +1253,25 @@ constexpr int paged_smem_bytes() {
   return kPagedStages * kStage > kMerge ? kPagedStages * kStage : kMerge;
 }
 
+// Eight e4m3 codes (two dwords, first code lowest) -> eight bf16 values.  Every
+// e4m3 value is a bf16 value (3 mantissa bits, exponents 2^-9 .. 2^8), so the
+// conversion (unit scale) is exact.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x2 c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[0], 1.0f, true);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[1], 1.0f, false);
+  const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c[1], 1.0f, true);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, d),
+               __builtin_bit_cast(uint32_t, e)};
+}
+
 // The decode work of one workgroup: unit `unit` = (sequence, KV head, split),
-// LDS in smem (paged_smem_bytes<D>(), 1 KiB aligned).
-template <int D, bool SOFTCAP>
+// LDS in smem (paged_smem_bytes<D>(), 1 KiB aligned).  FP8: the cache holds
+// e4m3 codes (strides in bytes), widened to bf16 between the load and the LDS
+// store (the stage layout is the bf16 one); the K scale is folded into the
+// score scale by the host and the V scale multiplies O here.
+template <int D, bool SOFTCAP, bool FP8 = false>
 __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int unit) {
   constexpr int NK = FA_PAGED_STAGE;
   constexpr int NS = kPagedStages;
@@ -1286,6 +1302,28 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   for (int i = 0; i < G::kInstPerWave; ++i) {
     k_src[i] = (dma_pc ^ k_swz<D>(dma_row + i * G::kRowsPerKiB)) * 8;
     v_src[i] = (dma_pc ^ v_swz<D>(dma_row + i * G::kRowsPerKiB)) * 8;
+  }
+  // FP8: a lane loads 16 codes, two adjacent 8-element chunks of a row (the even
+  // logical chunk E and E + 1), and writes them widened as two 16-byte LDS chunks.
+  // LDS chunk c of row r holds logical chunk c ^ swz(r), so E = 2 pp ^ (swz & ~1)
+  // fills LDS chunk 2 pp ^ (swz & 1) and E + 1 the other chunk of the pair.
+  constexpr int kPairs = D / 16;                     // chunk pairs per row
+  constexpr int kRows8 = 64 / kPairs;                // rows per load instruction
+  constexpr int kInst8 = FP8 ? kWaveRows / kRows8 : 1;
+  int r8[kInst8], k_src8[kInst8], v_src8[kInst8], k_lds8[kInst8], v_lds8[kInst8];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < kInst8; ++i) {
+      const int rw = i * kRows8 + lane / kPairs;     // row among the wave's 16
+      const int r = kWaveRows * wave + rw;           // row of the stage
+      const int c2 = 2 * (lane % kPairs);
+      const int sk = k_swz<D>(r), sv = v_swz<D>(r);
+      r8[i] = r;
+      k_src8[i] = (c2 ^ (sk & ~1)) * 8;
+      v_src8[i] = (c2 ^ (sv & ~1)) * 8;
+      k_lds8[i] = rw * (2 * D) + (c2 ^ (sk & 1)) * 16;
+      v_lds8[i] = rw * (2 * D) + (c2 ^ (sv & 1)) * 16;
+    }
   }
 
   const int S = p.num_splits;
@@ -1348,8 +1386,10 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   mask.wl = p.wl;
   mask.wr = p.wr;
 
-  const uint16_t* kpool = p.k + (int64_t)kvh * p.k_hs;
-  const uint16_t* vpool = p.v + (int64_t)kvh * p.v_hs;
+  // element offsets scale to bytes by kEs (bf16 2, e4m3 1)
+  constexpr int64_t kEs = FP8 ? 1 : 2;
+  const char* kpool = reinterpret_cast<const char*>(p.k) + (int64_t)kvh * p.k_hs * kEs;
+  const char* vpool = reinterpret_cast<const char*>(p.v) + (int64_t)kvh * p.v_hs * kEs;
   const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks;
   const bool page_aligned = (p.page % NK) == 0;
   // rows past the last key read the last key (finite data the mask drops)
@@ -1362,43 +1402,92 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   // load i holds the 16 bytes that the stage layout puts at byte l * 16 of the
   // wave's i-th KiB (row dma_row + i * kRowsPerKiB, swizzled chunk).  The loads of
   // stage i + 1 are in flight while stage i is computed.
-  u32x4 kr[G::kInstPerWave], vr[G::kInstPerWave];
-  auto load = [&](int n0) {
+  u32x4 kr[FP8 ? kInst8 : G::kInstPerWave], vr[FP8 ? kInst8 : G::kInstPerWave];
+  auto load8 = [&](int n0, u32x4 (&kr)[FP8 ? kInst8 : G::kInstPerWave], u32x4 (&vr)[FP8 ? kInst8 : G::kInstPerWave]) {
     if (page_aligned) {
-      // the whole stage is in one page: one scalar table read
       const int64_t phys = scalar_load_i32(bt + __builtin_amdgcn_readfirstlane(n0 / p.page));
       const int slot0 = n0 % p.page;
 #pragma unroll
-      for (int i = 0; i < G::kInstPerWave; ++i) {
-        const int r = dma_row + i * G::kRowsPerKiB;
-        const bool live = n0 + r < kend;
-        const int slot = live ? slot0 + r : slot_last;
+      for (int i = 0; i < kInst8; ++i) {
+        const bool live = n0 + r8[i] < kend;
+        const int slot = live ? slot0 + r8[i] : slot_last;
         const int64_t ph = live ? phys : phys_last;
         kr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(kpool + ph * p.k_bs + (int64_t)slot * p.k_ss + k_src[i]));
+            reinterpret_cast<const u32x4*>(kpool + ph * p.k_bs + (int64_t)slot * p.k_ss + k_src8[i]));
         vr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(vpool + ph * p.v_bs + (int64_t)slot * p.v_ss + v_src[i]));
+            reinterpret_cast<const u32x4*>(vpool + ph * p.v_bs + (int64_t)slot * p.v_ss + v_src8[i]));
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < G::kInstPerWave; ++i) {
-        int key = n0 + dma_row + i * G::kRowsPerKiB;
+      for (int i = 0; i < kInst8; ++i) {
+        int key = n0 + r8[i];
         key = key < kend ? key : kend - 1;
         const int64_t phys = bt[key / p.page];
         const int slot = key % p.page;
         kr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(kpool + phys * p.k_bs + (int64_t)slot * p.k_ss + k_src[i]));
+            reinterpret_cast<const u32x4*>(kpool + phys * p.k_bs + (int64_t)slot * p.k_ss + k_src8[i]));
         vr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(vpool + phys * p.v_bs + (int64_t)slot * p.v_ss + v_src[i]));
+            reinterpret_cast<const u32x4*>(vpool + phys * p.v_bs + (int64_t)slot * p.v_ss + v_src8[i]));
       }
     }
   };
-  auto store = [&](int buf) {
-    char* dst = smem + buf * kStage + wave * (kWaveRows * 2 * D) + lane * 16;
+  auto load = [&](int n0) {
+    if constexpr (FP8) {
+      load8(n0, kr, vr);
+    } else {
+      if (page_aligned) {
+        // the whole stage is in one page: one scalar table read
+        const int64_t phys = scalar_load_i32(bt + __builtin_amdgcn_readfirstlane(n0 / p.page));
+        const int slot0 = n0 % p.page;
 #pragma unroll
-    for (int i = 0; i < G::kInstPerWave; ++i) {
-      *reinterpret_cast<u32x4*>(dst + i * 1024) = kr[i];
-      *reinterpret_cast<u32x4*>(dst + G::kTensorBytes + i * 1024) = vr[i];
+        for (int i = 0; i < G::kInstPerWave; ++i) {
+          const int r = dma_row + i * G::kRowsPerKiB;
+          const bool live = n0 + r < kend;
+          const int slot = live ? slot0 + r : slot_last;
+          const int64_t ph = live ? phys : phys_last;
+          kr[i] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(kpool + (ph * p.k_bs + (int64_t)slot * p.k_ss + k_src[i]) * kEs));
+          vr[i] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(vpool + (ph * p.v_bs + (int64_t)slot * p.v_ss + v_src[i]) * kEs));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < G::kInstPerWave; ++i) {
+          int key = n0 + dma_row + i * G::kRowsPerKiB;
+          key = key < kend ? key : kend - 1;
+          const int64_t phys = bt[key / p.page];
+          const int slot = key % p.page;
+          kr[i] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(kpool + (phys * p.k_bs + (int64_t)slot * p.k_ss + k_src[i]) * kEs));
+          vr[i] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(vpool + (phys * p.v_bs + (int64_t)slot * p.v_ss + v_src[i]) * kEs));
+        }
+      }
+    }
+  };
+  auto store8 = [&](int buf, const u32x4 (&kr)[FP8 ? kInst8 : G::kInstPerWave],
+                    const u32x4 (&vr)[FP8 ? kInst8 : G::kInstPerWave]) {
+    char* wb = smem + buf * kStage + wave * (kWaveRows * 2 * D);
+#pragma unroll
+    for (int i = 0; i < kInst8; ++i) {
+      *reinterpret_cast<u32x4*>(wb + k_lds8[i]) = e4m3x8_to_bf16(u32x2{kr[i][0], kr[i][1]});
+      *reinterpret_cast<u32x4*>(wb + (k_lds8[i] ^ 16)) = e4m3x8_to_bf16(u32x2{kr[i][2], kr[i][3]});
+      *reinterpret_cast<u32x4*>(wb + G::kTensorBytes + v_lds8[i]) = e4m3x8_to_bf16(u32x2{vr[i][0], vr[i][1]});
+      *reinterpret_cast<u32x4*>(wb + G::kTensorBytes + (v_lds8[i] ^ 16)) =
+          e4m3x8_to_bf16(u32x2{vr[i][2], vr[i][3]});
+    }
+    asm volatile("" ::: "memory");
+  };
+  auto store = [&](int buf) {
+    if constexpr (FP8) {
+      store8(buf, kr, vr);
+    } else {
+      char* dst = smem + buf * kStage + wave * (kWaveRows * 2 * D) + lane * 16;
+#pragma unroll
+      for (int i = 0; i < G::kInstPerWave; ++i) {
+        *reinterpret_cast<u32x4*>(dst + i * 1024) = kr[i];
+        *reinterpret_cast<u32x4*>(dst + G::kTensorBytes + i * 1024) = vr[i];
+      }
     }
     // the operand reads below are inline assembly: keep the stores above them
     // (LDS operations of one wave complete in order, so no wait is needed)
@@ -1410,14 +1499,9 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
   float m_run = kNegInf, l_run = 0.0f, l_bf = 0.0f;
 
-  if (nst > 0) load(st_first);
-  for (int i = 0; i < nst; ++i) {
-    const int buf = i % NS;
+  // the products, mask and online softmax of stage i (from LDS buffer buf)
+  auto compute = [&](int i, int buf) {
     const int n0 = st_first + i * NK;
-    // stage i arrives in the registers (the compiler waits for the loads); this
-    // wave's reads of the buffer, from stage i - NS, completed before their products
-    store(buf);
-    if (i + 1 < nst) load(n0 + NK);
     // this wave's 16 keys: rows 16 wave .. 16 wave + 15 of the stage buffer
     const uint32_t delta = buf * kStage + wave * 16 * (2 * D);
     f32x16 s = qk_block<D, 0>(delta, qreg, off);
@@ -1430,6 +1514,33 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
     bf16x8 p0, p1;
     online_softmax<D>(s, m_run, l_run, l_bf, o, c, p0, p1);
     pv_chunk<D, G::kTensorBytes>(delta, p0, o, off);
+  };
+  if constexpr (FP8) {
+    // An FP8 stage is half the bytes of a bf16 one: the loads run two stages ahead
+    // (register sets A and B in turn) so that as many bytes are in flight.
+    u32x4 kb[kInst8], vb[kInst8];
+    if (nst > 0) load8(st_first, kr, vr);
+    if (nst > 1) load8(st_first + NK, kb, vb);
+    for (int i = 0; i < nst; i += 2) {
+      store8(0, kr, vr);
+      if (i + 2 < nst) load8(st_first + (i + 2) * NK, kr, vr);
+      compute(i, 0);
+      if (i + 1 < nst) {
+        store8(1, kb, vb);
+        if (i + 3 < nst) load8(st_first + (i + 3) * NK, kb, vb);
+        compute(i + 1, 1);
+      }
+    }
+  } else {
+    if (nst > 0) load(st_first);
+    for (int i = 0; i < nst; ++i) {
+      const int buf = i % NS;
+      // stage i arrives in the registers (the compiler waits for the loads); this
+      // wave's reads of the buffer, from stage i - NS, completed before their products
+      store(buf);
+      if (i + 1 < nst) load(st_first + (i + 1) * NK);
+      compute(i, buf);
+    }
   }
   __syncthreads();
 
@@ -1469,7 +1580,8 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
       Lb += e[w] * ml[256 + w * 32 + cc];
     }
     const bool empty = (M == kNegInf) || !(L > 0.0f) || !(Lb > 0.0f);
-    const float inv = empty ? 0.0f : rcp_fast(Lb);
+    float inv = empty ? 0.0f : rcp_fast(Lb);
+    if constexpr (FP8) inv *= p.v_scale;
     float acc[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
@@ -1512,10 +1624,10 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   }
 }
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void fa_paged_kernel(FaParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[paged_smem_bytes<D>()];
-  paged_body<D, SOFTCAP>(p, smem, blockIdx.x);
+  paged_body<D, SOFTCAP, FP8>(p, smem, blockIdx.x);
 }
 
 // ------------------------------------------------------------------ unified batch
@@ -1749,6 +1861,54 @@ __global__ __launch_bounds__(kThreads) void fa_append_kernel(FaAppendParams p) {
       *reinterpret_cast<u32x4*>(kd + 8 * c) = *reinterpret_cast<const u32x4*>(ks + 8 * c);
     const u32x4 vx = *reinterpret_cast<const u32x4*>(p.v_new + b * p.vn_bs + t * p.vn_ss + h * p.vn_hs + 8 * c);
     *reinterpret_cast<u32x4*>(p.v_cache + phys * p.v_ps + slot * p.v_ss + h * p.v_hs + 8 * c) = vx;
+  }
+}
+
+// e4m3 code of x / scale, rounded to nearest even and saturated at +-448 (a NaN
+// stays NaN), two values per conversion; the quotient is the correctly rounded
+// fp32 division.
+__device__ __forceinline__ float e4m3_clamp(float x, float scale) {
+  const float q = x / scale;
+  return q > 448.0f ? 448.0f : (q < -448.0f ? -448.0f : q);
+}
+// Eight bf16 values (16 bytes, first value lowest) -> eight e4m3 codes.
+__device__ __forceinline__ u32x2 bf16x8_to_e4m3(u32x4 x, float scale) {
+  u32x2 r;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t a = x[2 * w], b = x[2 * w + 1];
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(__uint_as_float(a << 16), scale),
+                                            e4m3_clamp(__uint_as_float(a & 0xffff0000u), scale), 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(__uint_as_float(b << 16), scale),
+                                        e4m3_clamp(__uint_as_float(b & 0xffff0000u), scale), c, true);
+    r[w] = (uint32_t)c;
+  }
+  return r;
+}
+
+// Append to an FP8 (e4m3) cache: the same walk as fa_append_kernel, each 16-byte
+// chunk of a new bf16 row written as 8 codes (cache strides in bytes).
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa_append_fp8_kernel(FaAppendParams p) {
+  constexpr int C = D / 8;  // 8-element chunks per row
+  const int64_t total = (int64_t)p.B * p.L * p.Hkv * C;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint8_t* kc = reinterpret_cast<uint8_t*>(p.k_cache);
+  uint8_t* vc = reinterpret_cast<uint8_t*>(p.v_cache);
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
+    const int c = (int)(i % C);
+    int64_t r = i / C;
+    const int h = (int)(r % p.Hkv);
+    r /= p.Hkv;
+    const int t = (int)(r % p.L);
+    const int b = (int)(r / p.L);
+    const int pos = p.cache_seqlens[b] + t;
+    const int64_t phys = p.block_table[(int64_t)b * p.max_blocks + pos / p.page];
+    const int64_t slot = pos % p.page;
+    const u32x4 kx = *reinterpret_cast<const u32x4*>(p.k_new + b * p.kn_bs + t * p.kn_ss + h * p.kn_hs + 8 * c);
+    const u32x4 vx = *reinterpret_cast<const u32x4*>(p.v_new + b * p.vn_bs + t * p.vn_ss + h * p.vn_hs + 8 * c);
+    *reinterpret_cast<u32x2*>(kc + phys * p.k_ps + slot * p.k_ss + h * p.k_hs + 8 * c) = bf16x8_to_e4m3(kx, p.k_scale);
+    *reinterpret_cast<u32x2*>(vc + phys * p.v_ps + slot * p.v_ss + h * p.v_hs + 8 * c) = bf16x8_to_e4m3(vx, p.v_scale);
   }
 }
 
@@ -2428,11 +2588,11 @@ hipError_t launch_prefill_t(const FaParams& p0, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool FP8>
 hipError_t launch_paged_t(const FaParams& p, hipStream_t stream) {
   int64_t units = (int64_t)p.B * p.Hkv * p.num_splits;
   if (units <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fa_paged_kernel<D, SOFTCAP>), dim3((unsigned)units), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa_paged_kernel<D, SOFTCAP, FP8>), dim3((unsigned)units), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -2532,9 +2692,14 @@ hipError_t fa_launch_prefill_mod(const FaParams& p, int d, bool pack, int mod_id
   return hipErrorInvalidValue;
 }
 
-hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, hipStream_t s) {
-  if (d == 128) return softcap ? launch_paged_t<128, true>(p, s) : launch_paged_t<128, false>(p, s);
-  if (d == 64) return softcap ? launch_paged_t<64, true>(p, s) : launch_paged_t<64, false>(p, s);
+hipError_t fa_launch_paged(const FaParams& p, int d, bool softcap, bool fp8, hipStream_t s) {
+  if (fp8) {
+    if (d == 128) return softcap ? launch_paged_t<128, true, true>(p, s) : launch_paged_t<128, false, true>(p, s);
+    if (d == 64) return softcap ? launch_paged_t<64, true, true>(p, s) : launch_paged_t<64, false, true>(p, s);
+    return hipErrorInvalidValue;
+  }
+  if (d == 128) return softcap ? launch_paged_t<128, true, false>(p, s) : launch_paged_t<128, false, false>(p, s);
+  if (d == 64) return softcap ? launch_paged_t<64, true, false>(p, s) : launch_paged_t<64, false, false>(p, s);
   return hipErrorInvalidValue;
 }
 
@@ -2580,7 +2745,11 @@ hipError_t fa_launch_append(const FaAppendParams& p, int d, hipStream_t s) {
   int64_t blocks = (total + kThreads - 1) / kThreads;
   const int64_t cap = 16 * (int64_t)device_cus();  // grid-stride beyond that
   if (blocks > cap) blocks = cap;
-  if (d == 128)
+  if (p.fp8 && d == 128)
+    hipLaunchKernelGGL(fa_append_fp8_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else if (p.fp8 && d == 64)
+    hipLaunchKernelGGL(fa_append_fp8_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  else if (d == 128)
     hipLaunchKernelGGL(fa_append_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
   else if (d == 64)
     hipLaunchKernelGGL(fa_append_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p);

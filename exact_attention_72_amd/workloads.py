@@ -136,6 +136,23 @@ def paged(seed, B, Hq, Hkv, d, page, lo, hi, *, max_blocks=None, Nq=1, cache_seq
                 cache_seqlens=cache_seqlens, page=page, max_blocks=max_blocks)
 
 
+def paged_fp8(seed, B, Hq, Hkv, d, page, lo, hi, *, max_blocks=None, Nq=1, cache_seqlens=None,
+              amax=4.0, device="cpu"):
+    """An FP8 (e4m3) paged cache: paged() of the same seed, its K and V divided by
+    scale = amax / 448 and cast to e4m3 codes by torch's float8_e4m3fn conversion
+    (values beyond +-448 clamped first).  Returns paged()'s dict with k_codes,
+    v_codes (uint8, the caches' shape) and k_scale = v_scale = amax / 448 added."""
+    t = paged(seed, B, Hq, Hkv, d, page, lo, hi, max_blocks=max_blocks, Nq=Nq, cache_seqlens=cache_seqlens,
+              device=device)
+    scale = float(np.float32(amax / 448.0))
+    for n in ("k", "v"):
+        x = t[n + "_cache"].float().div_(scale).clamp_(-448.0, 448.0)
+        t[n + "_codes"] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        del x
+    t["k_scale"] = t["v_scale"] = scale
+    return t
+
+
 def to_bits(t: torch.Tensor) -> np.ndarray:
     """bfloat16 tensor -> numpy uint16 bit patterns (a reinterpretation, no rounding)."""
     if t.dtype != torch.bfloat16:

@@ -182,6 +182,33 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
                          const int64_t v_strides[3], const int64_t o_strides[3],
                          void* stream);
 
+/* fa_fwd_kvcache_paged over an FP8 (OCP e4m3) KV cache: the cache holds one byte
+ * per element, and logical key / value element x of every row is code * k_scale /
+ * code * v_scale ("Attention kernels ...", section 5.2: a KV cache stored in FP8
+ * halves the bytes a decode step reads, and decode time is those bytes over the
+ * bandwidth).  Q, O and LSE are as in fa_fwd_kvcache_paged.  The codes are
+ * widened to bf16 exactly and the products run in bf16 with fp32 accumulation;
+ * k_scale multiplies the softmax scale (and the softcap argument) and v_scale
+ * multiplies O, so the result is attention over the dequantized cache.
+ *   k_cache, v_cache  uint8 [num_pages, page_size, heads_kv, head_dim], strides in
+ *                     BYTES {page, slot, head}, every row 16-byte aligned
+ *   k_scale, v_scale  finite, > 0 (one scale per tensor)
+ * Write the cache with fa_kvcache_append_fp8 (same scales).  The other arguments,
+ * the workspace and num_splits are those of fa_fwd_kvcache_paged.
+ * Errors: FA_ERR_INVALID_ARG for a scale that is not finite and positive;
+ * FA_ERR_UNSUPPORTED for more than 32 packed rows (seqlen_q * heads_q / heads_kv:
+ * FP8 caches are read by the decode kernel only) and for ALiBi.  A NaN code reads
+ * as NaN and poisons the rows that see it, like a NaN in a bf16 cache. */
+int fa_fwd_kvcache_paged_fp8(const fa_attn_opts* opts, const void* q, const void* k_cache,
+                             const void* v_cache, float k_scale, float v_scale,
+                             const int32_t* block_table, const int32_t* cache_seqlens, void* out,
+                             float* lse, int batch, int seqlen_q, int heads_q, int heads_kv,
+                             int head_dim, int64_t num_pages, int page_size,
+                             int max_blocks_per_seq, int num_splits, void* workspace,
+                             size_t workspace_bytes, const int64_t q_strides[3],
+                             const int64_t k_strides[3], const int64_t v_strides[3],
+                             const int64_t o_strides[3], void* stream);
+
 /* fa_fwd_kvcache_paged for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments, results and errors, without the workspace.
@@ -299,6 +326,22 @@ int fa_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void*
                       const int64_t v_strides[3], const float* rotary_cos,
                       const float* rotary_sin, int rotary_dim, int rotary_interleaved,
                       void* stream);
+
+/* fa_kvcache_append for an FP8 (OCP e4m3) cache: each new bf16 element x is
+ * written as the e4m3 code of the fp32 quotient x / k_scale (keys) or x / v_scale
+ * (values), rounded to nearest with ties to even and saturated at +-448 ("Attention
+ * kernels ...", section 5.2: the KV cache stored in FP8).  The caches are uint8
+ * [num_pages, page_size, heads_kv, head_dim] with strides in BYTES, rows 16-byte
+ * aligned; the other arguments are those of fa_kvcache_append, without the rotary
+ * tables (rotate the new keys first with fa_rotary).  New values must be finite
+ * (a NaN is written as a NaN code).
+ * Errors: FA_ERR_INVALID_ARG for a scale that is not finite and positive. */
+int fa_kvcache_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                          float k_scale, float v_scale, const int32_t* block_table,
+                          const int32_t* cache_seqlens, int batch, int seqlen_new, int heads_kv,
+                          int head_dim, int64_t num_pages, int page_size, int max_blocks_per_seq,
+                          const int64_t kn_strides[3], const int64_t vn_strides[3],
+                          const int64_t k_strides[3], const int64_t v_strides[3], void* stream);
 
 /* In-place rotary position embedding of x [batch, seqlen, heads, head_dim] (bf16,
  * strides x_strides = {batch, seq, head}), for the new queries of a kvcache step

@@ -173,3 +173,88 @@ def fwd(q, q_scales, q_block, k, k_scales, k_block, v, v_scales, *, scale=None, 
                 A[b, ok, h] = (E[ok] / l[ok, None]) @ np.abs(vd[b, :, h // g])
             L[b, h, ok] = m[ok, 0] + np.log(l[ok])
     return (O, L, A) if with_abs else (O, L)
+
+
+# ---------------------------------------------------------------- FP8 KV cache
+# "Attention kernels: FlashAttention and PagedAttention", section 5.2: a KV cache
+# stored in FP8 halves the bytes a decode step reads.  Readings (the pages name the
+# storage, not its scaling): one fp32 scale per cache tensor (k_scale, v_scale), an
+# element's value is decode(code) * scale, and a new bf16 element x is stored as the
+# e4m3 rounding of the fp32 quotient x / scale (the quantizer's rule above).  Pages
+# follow section 6.1 of the same page: logical key t of sequence b is slot
+# t % page of page block_table[b][t // page].
+
+
+def encode_scaled(x_bits, scale) -> np.ndarray:
+    """e4m3 codes of bf16 values (bit patterns) divided by a fp32 scale: one fp32
+    division per element, then round to nearest even, saturating at 448."""
+    y = (_bf16_to_f32(x_bits) / np.float32(scale)).astype(np.float32)
+    return e4m3_encode(y)
+
+
+def kvcache_append_fp8(k_new, v_new, k_codes, v_codes, k_scale, v_scale, block_table, cache_seqlens):
+    """Append new bf16 tokens k_new, v_new [B, L, Hkv, d] (bit patterns) to the FP8
+    caches [num_pages, page, Hkv, d] (uint8 codes): token t of sequence b lands at
+    logical position cache_seqlens[b] + t.  Returns new (k_codes, v_codes); the
+    inputs are not modified."""
+    kn = np.asarray(k_new, dtype=np.uint16)
+    vn = np.asarray(v_new, dtype=np.uint16)
+    kc = np.array(k_codes, dtype=np.uint8, copy=True)
+    vc = np.array(v_codes, dtype=np.uint8, copy=True)
+    bt = np.asarray(block_table, dtype=np.int64)
+    sl = np.asarray(cache_seqlens, dtype=np.int64)
+    page = kc.shape[1]
+    for b in range(kn.shape[0]):
+        for t in range(kn.shape[1]):
+            pos = int(sl[b]) + t
+            phys = int(bt[b, pos // page])
+            kc[phys, pos % page] = encode_scaled(kn[b, t], k_scale)
+            vc[phys, pos % page] = encode_scaled(vn[b, t], v_scale)
+    return kc, vc
+
+
+def _gather(codes, bt_row, Lk, kvh):
+    """Decoded [Lk, d] rows of KV head kvh of one sequence (logical key order)."""
+    page = codes.shape[1]
+    t = np.arange(Lk)
+    return e4m3_decode(codes[bt_row[t // page], t % page, kvh])
+
+
+def fwd_paged_fp8(q, k_codes, v_codes, k_scale, v_scale, block_table, cache_seqlens, *, scale=None,
+                  causal=True, window=None, softcap=0.0, batches=None):
+    """Attention of bf16 queries q [B, Nq, Hq, d] (bit patterns) over the paged FP8
+    cache, in fp64 with S and P materialised: key j of sequence b is
+    decode(k_codes[page, slot, h // g]) * k_scale (value likewise with v_scale),
+    Lk = cache_seqlens[b] keys, query i at key position i + Lk - Nq (bottom-right).
+    softcap c > 0 replaces each scaled logit s by c tanh(s / c).  batches: None for
+    every sequence, or a list of sequence indices (O and LSE then hold those, in
+    that order).  Returns (O float64 [nb, Nq, Hq, d], LSE float64 [nb, Hq, Nq]); a
+    row that sees no key gets O = 0 and LSE = -inf."""
+    qf = _bf16_to_f32(q).astype(np.float64)
+    B, Nq, Hq, d = qf.shape
+    Hkv = k_codes.shape[2]
+    g = Hq // Hkv
+    s = d ** -0.5 if scale is None else scale
+    bt = np.asarray(block_table, dtype=np.int64)
+    sl = np.asarray(cache_seqlens, dtype=np.int64)
+    sel = list(range(B)) if batches is None else list(batches)
+    O = np.zeros((len(sel), Nq, Hq, d))
+    L = np.full((len(sel), Hq, Nq), -np.inf)
+    for n, b in enumerate(sel):
+        Lk = int(sl[b])
+        vis = _visible(Nq, Lk, causal, window)
+        for kvh in range(Hkv):
+            kd = _gather(k_codes, bt[b], Lk, kvh) * np.float64(k_scale)
+            vd = _gather(v_codes, bt[b], Lk, kvh) * np.float64(v_scale)
+            for h in range(kvh * g, (kvh + 1) * g):
+                S = s * (qf[b, :, h] @ kd.T)
+                if softcap > 0:
+                    S = softcap * np.tanh(S / softcap)
+                S = np.where(vis, S, -np.inf)
+                m = S.max(axis=1, keepdims=True) if Lk > 0 else np.full((Nq, 1), -np.inf)
+                ok = np.isfinite(m[:, 0])
+                E = np.exp(S - np.where(np.isfinite(m), m, 0.0))
+                l = E.sum(axis=1)
+                O[n, ok, h] = (E[ok] / l[ok, None]) @ vd
+                L[n, h, ok] = m[ok, 0] + np.log(l[ok])
+    return O, L

@@ -448,3 +448,36 @@ def test_alibi_is_rejected_where_it_is_not_built():
                     S3, S3, S3, S3, S3, S3, S3, S3, FAKE, 1 << 20, None) == FA_ERR_UNSUPPORTED
     assert L.fa_fwd_fp8(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 16, 16, 16, 128,
                         S3, S3, S3, None) == FA_ERR_UNSUPPORTED
+
+
+def test_fp8_cache_entry_points_reject_invalid_arguments():
+    """FP8 (e4m3) KV cache: scales must be finite and positive, cache strides are bytes with
+    16-byte rows, and only the decode kernel (at most 32 packed rows) reads such a cache."""
+    L = api.lib()
+    B3 = (ctypes.c_int64 * 3)(256 * 8 * 128, 8 * 128, 128)       # byte strides of a [pages, 256, 8, 128] cache
+
+    def paged(ks=1.0, vs=1.0, Nq=1, kstr=B3, page=256, d=128, ns=1, opts=None):
+        o = opts if opts is not None else _opts(causal=1)
+        return L.fa_fwd_kvcache_paged_fp8(ctypes.byref(o), FAKE, FAKE, FAKE, ks, vs, FAKE, FAKE, FAKE, None,
+                                          64, Nq, 32, 8, d, 8192, page, 128, ns, None, 0, S3, kstr, kstr, S3, None)
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert paged(ks=bad) == FA_ERR_INVALID_ARG
+        assert paged(vs=bad) == FA_ERR_INVALID_ARG
+    assert paged(Nq=9) == FA_ERR_UNSUPPORTED                       # 36 packed rows: prefill kernel, bf16 only
+    assert paged(kstr=(ctypes.c_int64 * 3)(256 * 1024, 1032, 128)) == FA_ERR_INVALID_ARG
+    assert paged(page=24) == FA_ERR_INVALID_ARG
+    assert paged(d=96) == FA_ERR_UNSUPPORTED
+    assert paged(ns=4) == FA_ERR_INVALID_ARG                       # split partials need a workspace
+    alibi = fa_attn_opts(0.0, 1, -1, -1, 0.0, -1, ctypes.c_void_p(1 << 21), 0)
+    assert paged(opts=alibi) == FA_ERR_UNSUPPORTED
+
+    def append(ks=1.0, vs=1.0, kstr=B3, page=16, d=128, Ln=3):
+        return L.fa_kvcache_append_fp8(FAKE, FAKE, FAKE, FAKE, ks, vs, FAKE, FAKE, 2, Ln, 8, d, 100, page, 10,
+                                       S3, S3, kstr, kstr, None)
+    for bad in (0.0, -2.0, float("inf"), float("nan")):
+        assert append(ks=bad) == FA_ERR_INVALID_ARG
+        assert append(vs=bad) == FA_ERR_INVALID_ARG
+    assert append(kstr=(ctypes.c_int64 * 3)(2048, 1032, 128)) == FA_ERR_INVALID_ARG
+    assert append(page=24) == FA_ERR_INVALID_ARG
+    assert append(d=96) == FA_ERR_UNSUPPORTED
+    assert append(Ln=0) == 0                                       # nothing to write, no launch

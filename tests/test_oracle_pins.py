@@ -849,3 +849,106 @@ def test_c_oracle_equals_a_naive_python_loop_on_tiny_varlen_and_paged_shapes():
                                     3.0)
                 assert max(abs(a - c) for a, c in zip(o, O[b, i, h])) <= 1e-12
                 assert abs(lse - L[b, h, i]) <= 1e-12
+
+
+# ---------------------------------------------------------------- fp8 KV cache
+def _e4m3_by_torch(codes):
+    """fp64 values of e4m3 codes through torch's float8_e4m3fn type (a library decoder)."""
+    return torch.tensor(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _bf16_bits_exact(a):
+    f = torch.tensor(a, dtype=torch.float64).to(torch.float32)
+    bb = f.to(torch.bfloat16)
+    ok = torch.isnan(f) | (bb.to(torch.float32) == f)
+    assert bool(ok.all())                                       # exact in bf16
+    return bb.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("Nq,causal,window,softcap", [(1, True, None, 0.0), (3, True, None, 0.0),
+                                                      (2, True, (40, 0), 0.0), (1, True, None, 7.0),
+                                                      (2, False, None, 0.0)])
+def test_fp8_paged_matches_the_bf16_paged_oracle_on_exact_caches(Nq, causal, window, softcap):
+    """Power-of-two scales make every dequantized cache value a bf16 number, so the FP8
+    cache oracle must equal the C oracle's bf16 paged attention over those values
+    (pages, slots, GQA map, masks and softcap included).  Pages no sequence uses hold
+    NaN codes in both forms and must not reach any row."""
+    rng = np.random.default_rng(11 + Nq)
+    B, Hq, Hkv, d, page, max_blocks = 3, 8, 2, 32, 16, 5
+    lens = [1, 37, 80]
+    num_pages = B * max_blocks + 2
+    kc = rng.integers(0, 0x58, size=(num_pages, page, Hkv, d)).astype(np.uint8)
+    kc |= (rng.integers(0, 2, size=kc.shape).astype(np.uint8) << 7)
+    vc = rng.integers(0, 0x58, size=kc.shape).astype(np.uint8) | (rng.integers(0, 2, size=kc.shape).astype(np.uint8) << 7)
+    bt = rng.permutation(num_pages)[:B * max_blocks].reshape(B, max_blocks).astype(np.int32)
+    used = {int(bt[b, j]) for b, L in enumerate(lens) for j in range(-(-L // page))}
+    for pg in range(num_pages):
+        if pg not in used:
+            kc[pg] = 0x7F
+            vc[pg] = 0xFF
+    q = bits(torch.randn(B, Nq, Hq, d, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16))
+    ks, vs = 0.25, 2.0
+    O, L = F8.fwd_paged_fp8(q, kc, vc, ks, vs, bt, lens, causal=causal, window=window, softcap=softcap)
+    kb, vb = _bf16_bits_exact(_e4m3_by_torch(kc) * ks), _bf16_bits_exact(_e4m3_by_torch(vc) * vs)
+    ro, rl = oracle.fwd_paged(q, kb, vb, bt, lens, causal=causal, window=window, softcap=softcap)
+    np.testing.assert_allclose(O, ro, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(L, rl, rtol=0, atol=1e-11)
+    Os, Ls = F8.fwd_paged_fp8(q, kc, vc, ks, vs, bt, lens, causal=causal, window=window, softcap=softcap,
+                              batches=[2, 0])
+    assert np.array_equal(Os, O[[2, 0]]) and np.array_equal(Ls, L[[2, 0]])
+
+
+def test_fp8_paged_scales_enter_the_logits_and_the_output():
+    """k_scale multiplies every logit (the same as a softmax scale k_scale times larger) and
+    v_scale multiplies O, for arbitrary scales; swapping their roles fails both."""
+    t = W.paged_fp8(23, 2, 4, 1, 16, 16, 20, 60, Nq=2)
+    q, kc, vc, bt, sl = bits(t["q"]), t["k_codes"].numpy(), t["v_codes"].numpy(), t["block_table"].numpy(), \
+        t["cache_seqlens"].numpy()
+    a, b, s = 0.37, 1.9, 0.3
+    O1, L1 = F8.fwd_paged_fp8(q, kc, vc, a, b, bt, sl, scale=s)
+    O0, L0 = F8.fwd_paged_fp8(q, kc, vc, 1.0, 1.0, bt, sl, scale=a * s)
+    np.testing.assert_allclose(O1, b * O0, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(L1, L0, rtol=1e-12, atol=1e-12)
+    Ow, Lw = F8.fwd_paged_fp8(q, kc, vc, b, a, bt, sl, scale=s)
+    assert not np.allclose(Ow, O1) and not np.allclose(Lw, L1)
+
+
+def test_fp8_scaled_encoding_matches_torch_and_saturates():
+    """x / scale in fp32, then e4m3 to nearest even: torch's float8_e4m3fn cast of the same
+    fp32 quotient for in-range values; magnitudes past 448 give the 448 codes."""
+    rng = np.random.default_rng(3)
+    x = torch.tensor(rng.standard_normal(4096) * 3, dtype=torch.float32).to(torch.bfloat16)
+    for scale in (np.float32(4.0 / 448.0), np.float32(0.0123), np.float32(1.0)):
+        got = F8.encode_scaled(bits(x), scale)
+        y = (x.to(torch.float32) / torch.tensor(scale)).clamp(-448, 448)
+        want = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(got, want)
+    big = bits(torch.tensor([1e4, -1e4, 449.0, -460.0], dtype=torch.float32).to(torch.bfloat16))
+    assert list(F8.encode_scaled(big, np.float32(1.0))) == [0x7E, 0xFE, 0x7E, 0xFE]
+
+
+def test_fp8_append_writes_each_token_at_its_page_slot():
+    """Values that are codes times a power-of-two scale survive the append exactly, at slot
+    pos % page of page block_table[b][pos // page]; the K and V scales stay separate and no
+    other slot changes."""
+    rng = np.random.default_rng(9)
+    B, Lnew, Hkv, d, page, max_blocks = 2, 21, 2, 16, 16, 4
+    num_pages = B * max_blocks
+    bt = rng.permutation(num_pages).reshape(B, max_blocks).astype(np.int32)
+    sl = np.array([3, 17], np.int32)
+    kcodes = rng.integers(0, 0x77, size=(B, Lnew, Hkv, d)).astype(np.uint8)
+    vcodes = rng.integers(0x80, 0xF7, size=(B, Lnew, Hkv, d)).astype(np.uint8)
+    ks, vs = 0.125, 4.0
+    kn = _bf16_bits_exact(_e4m3_by_torch(kcodes) * ks)
+    vn = _bf16_bits_exact(_e4m3_by_torch(vcodes) * vs)
+    kc0 = rng.integers(0, 256, size=(num_pages, page, Hkv, d)).astype(np.uint8)
+    vc0 = rng.integers(0, 256, size=(num_pages, page, Hkv, d)).astype(np.uint8)
+    kc, vc = F8.kvcache_append_fp8(kn, vn, kc0, vc0, ks, vs, bt, sl)
+    written = np.zeros((num_pages, page), bool)
+    for b in range(B):
+        for t in range(Lnew):
+            pos = sl[b] + t
+            pg, slot = bt[b, pos // page], pos % page
+            assert np.array_equal(kc[pg, slot], kcodes[b, t]) and np.array_equal(vc[pg, slot], vcodes[b, t])
+            written[pg, slot] = True
+    assert np.array_equal(kc[~written], kc0[~written]) and np.array_equal(vc[~written], vc0[~written])
