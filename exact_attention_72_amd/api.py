@@ -247,7 +247,7 @@ def fa_kvcache_num_splits(batch, seqlen_q, heads_q, heads_kv, page_size, max_blo
 
 def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num_splits=1,
                          softmax_scale=None, causal=True, window=None, softcap=0.0, pack_gqa=-1,
-                         out=None, lse=None, workspace=None, return_lse=True, stream=None):
+                         alibi_slopes=None, out=None, lse=None, workspace=None, return_lse=True, stream=None):
     """Paged-KV forward.  q [B, Nq, Hq, d]; caches [num_pages, page, Hkv, d];
     block_table int32 [B, max_blocks]; cache_seqlens int32 [B] -> (out, lse [B, Hq, Nq]).
     num_splits=0 picks the split count (fa_kvcache_num_splits); more than 32 packed
@@ -271,7 +271,7 @@ def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
+    o = _opts(softmax_scale, causal, window, softcap, pack_gqa, alibi_slopes)
     _check(lib().fa_fwd_kvcache_paged(ctypes.byref(o), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                       _ptr(block_table), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
                                       B, Nq, Hq, Hkv, d, num_pages, page, block_table.shape[1],
@@ -283,8 +283,8 @@ def fa_fwd_kvcache_paged(q, k_cache, v_cache, block_table, cache_seqlens, *, num
 
 
 def fa_fwd_kvcache_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cache_seqlens, *, num_splits=1,
-                             softmax_scale=None, causal=True, window=None, softcap=0.0, out=None, lse=None,
-                             workspace=None, return_lse=True, stream=None):
+                             softmax_scale=None, causal=True, window=None, softcap=0.0, alibi_slopes=None, out=None,
+                             lse=None, workspace=None, return_lse=True, stream=None):
     """Paged-KV decode over an FP8 (e4m3) cache.  q [B, Nq, Hq, d] bf16 with Nq * Hq / Hkv <= 32;
     caches uint8 [num_pages, page, Hkv, d] of codes whose values are code * k_scale and
     code * v_scale (floats); block_table int32 [B, max_blocks]; cache_seqlens int32 [B]
@@ -309,7 +309,7 @@ def fa_fwd_kvcache_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table,
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    o = _opts(softmax_scale, causal, window, softcap, -1)
+    o = _opts(softmax_scale, causal, window, softcap, -1, alibi_slopes)
     _check(lib().fa_fwd_kvcache_paged_fp8(ctypes.byref(o), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                           float(k_scale), float(v_scale), _ptr(block_table), _ptr(cache_seqlens),
                                           _ptr(out), _ptr(lse), B, Nq, Hq, Hkv, d, num_pages, page,
@@ -325,7 +325,7 @@ FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 def fa_fwd_kvcache_paged_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, *, num_splits=1,
                                  softmax_scale=None, causal=True, window=None, softcap=0.0, pack_gqa=-1,
-                                 out, lse=None, stream=None):
+                                 alibi_slopes=None, out, lse=None, stream=None):
     """fa_fwd_kvcache_paged without a workspace: the split partials go to the library's static
     device scratch (FA_NOALLOC_SCRATCH_BYTES per device).  The caller passes out (and lse, or
     None); nothing is allocated here or in the library."""
@@ -337,7 +337,7 @@ def fa_fwd_kvcache_paged_noalloc(q, k_cache, v_cache, block_table, cache_seqlens
             raise TypeError("block_table and cache_seqlens must be int32 device tensors")
     if block_table.stride(-1) != 1 or block_table.stride(0) != block_table.shape[1]:
         raise ValueError("block_table must be a contiguous [batch, max_blocks] tensor")
-    o = _opts(softmax_scale, causal, window, softcap, pack_gqa)
+    o = _opts(softmax_scale, causal, window, softcap, pack_gqa, alibi_slopes)
     _check(lib().fa_fwd_kvcache_paged_noalloc(ctypes.byref(o), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                               _ptr(block_table), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
                                               B, Nq, Hq, Hkv, d, num_pages, page, block_table.shape[1],

@@ -544,12 +544,10 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
   memset(&p, 0, sizeof p);
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &p, &softcap))) return rc;
-  if ((rc = no_alibi(p, use_scratch ? "fa_fwd_kvcache_paged_noalloc"
-                                    : (fp8.on ? "fa_fwd_kvcache_paged_fp8" : "fa_fwd_kvcache_paged"))))
-    return rc;
   // S = scale q.(k_scale c_k) = (scale k_scale) q.c_k; O = v_scale sum p c_v
   p.scale_log2 *= fp8.k_scale;
   p.cap_in *= fp8.k_scale;
+  p.alibi_inv_scale /= fp8.k_scale;   // the bias in raw-score units: q.c_k
   p.v_scale = fp8.v_scale;
   if (use_scratch && need > 0) {
     hipError_t e = fa_scratch_region(&workspace);

@@ -1371,6 +1371,9 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   const int tok = row_ok ? col / p.g : 0;
   const int head = kvh * p.g + (row_ok ? col % p.g : 0);
   const uint16_t* qb = p.q + (int64_t)b * p.q_bs + (q_start + tok) * p.q_ss + (int64_t)head * p.q_hs;
+  // ALiBi (not with softcap): this lane's slope in raw-score units
+  const bool alibi = !SOFTCAP && p.alibi != nullptr;
+  const float alibi_k = alibi ? p.alibi[(int64_t)b * p.alibi_bs + head] * p.alibi_inv_scale : 0.0f;
   bf16x8 qreg[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
@@ -1505,6 +1508,14 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
     // this wave's 16 keys: rows 16 wave .. 16 wave + 15 of the stage buffer
     const uint32_t delta = buf * kStage + wave * 16 * (2 * D);
     f32x16 s = qk_block<D, 0>(delta, qreg, off);
+    if (alibi) {
+      // -slope |p - key| on the raw score (the softmax scales both)
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const int key = n0 + 16 * wave + 8 * ((a >> 2) & 1) + 4 * kg + (a & 3);
+        s[a] = __builtin_fmaf(-alibi_k, (float)abs(mask.pos - key), s[a]);
+      }
+    }
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
       const int key = n0 + 16 * wave + 8 * ((a >> 2) & 1) + 4 * kg + (a & 3);
@@ -2634,13 +2645,16 @@ int fa_device_cus() { return device_cus(); }
 
 hipError_t fa_launch_prefill(const FaParams& p, int d, bool varlen, bool paged, bool pack, bool softcap,
                              hipStream_t s) {
-  // ALiBi: dense and varlen, without softcap
+  // ALiBi: dense, varlen and chunked prefill over a paged cache, without softcap
   if (p.alibi) {
-    if (paged || softcap) return hipErrorInvalidValue;
-#define FA_AL(D_, V_, P_) \
-  if (d == D_ && varlen == V_ && pack == P_) return launch_prefill_t<D_, V_, P_, false, false, true>(p, s);
-    FA_AL(128, false, false) FA_AL(128, false, true) FA_AL(128, true, false) FA_AL(128, true, true)
-    FA_AL(64, false, false) FA_AL(64, false, true) FA_AL(64, true, false) FA_AL(64, true, true)
+    if (softcap || (paged && varlen)) return hipErrorInvalidValue;
+#define FA_AL(D_, V_, P_, G_) \
+  if (d == D_ && varlen == V_ && pack == P_ && paged == G_) return launch_prefill_t<D_, V_, P_, false, G_, true>(p, s);
+    FA_AL(128, false, false, false) FA_AL(128, false, true, false) FA_AL(128, true, false, false)
+    FA_AL(128, true, true, false) FA_AL(64, false, false, false) FA_AL(64, false, true, false)
+    FA_AL(64, true, false, false) FA_AL(64, true, true, false)
+    FA_AL(128, false, false, true) FA_AL(128, false, true, true) FA_AL(64, false, false, true)
+    FA_AL(64, false, true, true)
 #undef FA_AL
     return hipErrorInvalidValue;
   }

@@ -54,8 +54,10 @@
  *                  varlen call the batch index is the sequence): the logit of
  *                  a query at position p and key j gets -slope * |p - j|
  *                  ("FA4 ...", section 7, alibi_slopes), p bottom-right as for
- *                  causal.  fa_fwd and fa_fwd_varlen, without softcap; other
- *                  entry points return FA_ERR_UNSUPPORTED.
+ *                  causal.  fa_fwd, fa_fwd_varlen and the kvcache calls
+ *                  (fa_fwd_kvcache_paged, its _noalloc and _fp8 variants: the
+ *                  batch index is the sequence), without softcap; other entry
+ *                  points return FA_ERR_UNSUPPORTED.
  */
 #ifndef EXACT_ATTENTION_72_FA_H
 #define EXACT_ATTENTION_72_FA_H
@@ -197,7 +199,7 @@ int fa_fwd_kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_
  * the workspace and num_splits are those of fa_fwd_kvcache_paged.
  * Errors: FA_ERR_INVALID_ARG for a scale that is not finite and positive;
  * FA_ERR_UNSUPPORTED for more than 32 packed rows (seqlen_q * heads_q / heads_kv:
- * FP8 caches are read by the decode kernel only) and for ALiBi.  A NaN code reads
+ * FP8 caches are read by the decode kernel only).  A NaN code reads
  * as NaN and poisons the rows that see it, like a NaN in a bf16 cache. */
 int fa_fwd_kvcache_paged_fp8(const fa_attn_opts* opts, const void* q, const void* k_cache,
                              const void* v_cache, float k_scale, float v_scale,

@@ -71,3 +71,58 @@ def test_alibi_full_size_sampled_rows():
     O, L = oracle.fwd_dense_alibi(bits(cpu["q"]), bits(cpu["k"]), bits(cpu["v"]),
                                   torch.tensor(sl, dtype=torch.float32).double().numpy(), causal=True, rows=rows)
     check_close(out[:, rows], lse[:, :, rows], O, L, "alibi 4x16x4096 causal, sampled rows")
+
+
+# ---------------------------------------------------------------- paged KV (the kvcache call)
+def _logical(cache, bt_row, L):
+    """The first L logical rows [L, Hkv, d] of one sequence's paged cache."""
+    page = cache.shape[1]
+    t = torch.arange(L)
+    return cache[bt_row[t // page].long(), t % page]
+
+
+def _paged_alibi_ref(q, kc, vc, bt, lens, sl, causal=True):
+    """Per sequence: the oracle's ALiBi attention over its gathered logical keys."""
+    Os, Ls = [], []
+    for b, L in enumerate(lens):
+        kb, vb = _logical(kc, bt[b], L)[None], _logical(vc, bt[b], L)[None]
+        O, Lse = oracle.fwd_dense_alibi(bits(q[b:b + 1]), bits(kb), bits(vb), sl[b].astype(np.float64), causal=causal)
+        Os.append(O[0])
+        Ls.append(Lse[0])
+    return np.stack(Os), np.stack(Ls)
+
+
+@pytest.mark.parametrize("num_splits", [1, 4])
+@pytest.mark.parametrize("page,lens,Hq,Hkv,d,Nq", [
+    (16, [1, 17, 300, 1000], 32, 8, 128, 1),     # decode kernel
+    (256, [3, 700], 8, 2, 64, 4),                # decode kernel, 4 new tokens x 4 heads
+    (16, [40, 300], 8, 2, 128, 40),              # 160 packed rows: chunked prefill (one split)
+])
+def test_alibi_paged(page, lens, Hq, Hkv, d, Nq, num_splits):
+    if Nq * Hq // Hkv > 32 and num_splits > 1:
+        pytest.skip("chunked prefill runs one split")
+    t = W.paged(621 + page + Nq, len(lens), Hq, Hkv, d, page, 0, 0, cache_seqlens=lens, Nq=Nq)
+    sl = np.stack([slopes_for(Hq) * (1 + 0.3 * b) for b in range(len(lens))]).astype(np.float32)
+    out, lse = api.fa_fwd_kvcache_paged(t["q"].to(DEV), t["k_cache"].to(DEV), t["v_cache"].to(DEV),
+                                        t["block_table"].to(DEV), t["cache_seqlens"].to(DEV), num_splits=num_splits,
+                                        causal=True, alibi_slopes=torch.tensor(sl).to(DEV))
+    torch.cuda.synchronize()
+    O, L = _paged_alibi_ref(t["q"], t["k_cache"], t["v_cache"], t["block_table"], lens, sl)
+    check_close(out, lse, O, L, f"alibi paged page={page} Nq={Nq} S={num_splits}")
+
+
+def test_alibi_paged_fp8_cache():
+    """ALiBi over an FP8 cache with a k_scale that is not 1 (the bias is not scaled by it): with
+    power-of-two scales the dequantized cache is a bf16 cache, so the reference is the bf16 one."""
+    lens = [5, 260, 999]
+    t = W.paged_fp8(631, len(lens), 16, 4, 128, 16, 0, 0, cache_seqlens=lens, Nq=2)
+    ks, vs = 2.0 ** -7, 2.0 ** -7     # codes of N(0, 1) / (4 / 448): dequantized values of size ~1
+    deq = lambda c, s: (torch.tensor(c.numpy()).view(torch.float8_e4m3fn).to(torch.float32) * s).to(torch.bfloat16)  # noqa
+    kb, vb = deq(t["k_codes"], ks), deq(t["v_codes"], vs)
+    sl = np.stack([slopes_for(16) * (1 + 0.5 * b) for b in range(len(lens))]).astype(np.float32)
+    out, lse = api.fa_fwd_kvcache_paged_fp8(t["q"].to(DEV), t["k_codes"].to(DEV), t["v_codes"].to(DEV), ks, vs,
+                                            t["block_table"].to(DEV), t["cache_seqlens"].to(DEV), num_splits=2,
+                                            alibi_slopes=torch.tensor(sl).to(DEV))
+    torch.cuda.synchronize()
+    O, L = _paged_alibi_ref(t["q"], kb, vb, t["block_table"], lens, sl)
+    check_close(out, lse, O, L, "alibi paged fp8 cache")

@@ -448,6 +448,12 @@ def test_alibi_is_rejected_where_it_is_not_built():
                     S3, S3, S3, S3, S3, S3, S3, S3, FAKE, 1 << 20, None) == FA_ERR_UNSUPPORTED
     assert L.fa_fwd_fp8(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 16, 16, 16, 128,
                         S3, S3, S3, None) == FA_ERR_UNSUPPORTED
+    # the unified batch has no ALiBi; the kvcache call has it, but not with softcap
+    assert L.fa_fwd_varlen_paged(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 8, 64, 32, 8,
+                                 128, 8192, 256, 128, 1, None, 0, S2, S3, S3, S2, None) == FA_ERR_UNSUPPORTED
+    o = fa_attn_opts(0.0, 1, -1, -1, 30.0, -1, sl, 0)
+    assert L.fa_fwd_kvcache_paged(ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 1, 32, 8, 128,
+                                  8192, 256, 128, 1, None, 0, S3, S3, S3, S3, None) == FA_ERR_UNSUPPORTED
 
 
 def test_fp8_cache_entry_points_reject_invalid_arguments():
@@ -468,8 +474,8 @@ def test_fp8_cache_entry_points_reject_invalid_arguments():
     assert paged(page=24) == FA_ERR_INVALID_ARG
     assert paged(d=96) == FA_ERR_UNSUPPORTED
     assert paged(ns=4) == FA_ERR_INVALID_ARG                       # split partials need a workspace
-    alibi = fa_attn_opts(0.0, 1, -1, -1, 0.0, -1, ctypes.c_void_p(1 << 21), 0)
-    assert paged(opts=alibi) == FA_ERR_UNSUPPORTED
+    alibi_softcap = fa_attn_opts(0.0, 1, -1, -1, 30.0, -1, ctypes.c_void_p(1 << 21), 0)
+    assert paged(opts=alibi_softcap) == FA_ERR_UNSUPPORTED
 
     def append(ks=1.0, vs=1.0, kstr=B3, page=16, d=128, Ln=3):
         return L.fa_kvcache_append_fp8(FAKE, FAKE, FAKE, FAKE, ks, vs, FAKE, FAKE, 2, Ln, 8, d, 100, page, 10,
