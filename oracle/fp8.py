@@ -258,3 +258,50 @@ def fwd_paged_fp8(q, k_codes, v_codes, k_scale, v_scale, block_table, cache_seql
                 O[n, ok, h] = (E[ok] / l[ok, None]) @ vd
                 L[n, h, ok] = m[ok, 0] + np.log(l[ok])
     return O, L
+
+
+# ---------------------------------------------------------------- incoherent processing
+# "Attention kernels: FlashAttention and PagedAttention", section 4.2 (the FP8
+# item): Q and K are multiplied by a random orthogonal matrix before they are
+# quantized, which spreads an outlier channel over every channel while leaving
+# Q K^T unchanged ((Q R)(K R)^T = Q K^T for orthogonal R).  Reading (the pages
+# name the idea, not the matrix): R = diag(s) H / sqrt(d), H the Sylvester
+# Hadamard matrix of order d and s a caller-drawn vector of signs (+1 / -1), the
+# randomized Hadamard transform, applied to every row of Q and of K with the same
+# s.  The rotated values are formed in fp32 by the radix-2 Walsh-Hadamard
+# butterfly (pairs i, i + h for h = 1, 2, 4, ..., d / 2 in that order, each giving
+# a + b and a - b) and one multiply by fp32(1 / sqrt(d)); the quantizer's codes
+# are decided on those fp32 values, as on the GPU.
+
+
+def hadamard_rotate_f32(x, signs) -> np.ndarray:
+    """Rows of x (float32 [..., d], d a power of two) times diag(signs) H / sqrt(d),
+    computed in fp32 by the butterfly stages h = 1, 2, ..., d / 2."""
+    y = np.asarray(x, dtype=np.float32) * np.asarray(signs, dtype=np.float32)
+    d = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < d:
+        z = y.reshape(lead + (d // (2 * h), 2, h))
+        a, b = z[..., 0, :], z[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2).reshape(lead + (d,))
+        h *= 2
+    return (y * np.float32(1.0 / np.sqrt(d))).astype(np.float32)
+
+
+def quantize_rows_rotated(x, block: int, signs):
+    """quantize_rows of the rotated rows: every row of the [B, N, H, d] bf16 tensor
+    (bit patterns) goes through hadamard_rotate_f32 with the given signs, then one
+    scale per (batch, head, block of `block` rows) over the rotated values.
+    Returns (codes uint8 [B, N, H, d], scales float32 [B, H, ceil(N / block)])."""
+    yf = hadamard_rotate_f32(_bf16_to_f32(x), signs)
+    B, N, H, d = yf.shape
+    nb = -(-N // block)
+    codes = np.zeros(yf.shape, dtype=np.uint8)
+    scales = np.ones((B, H, nb), dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                sl = slice(i * block, min(N, (i + 1) * block))
+                codes[b, sl, h], scales[b, h, i] = _quantize_block(yf[b, sl, h])
+    return codes, scales

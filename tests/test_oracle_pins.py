@@ -952,3 +952,61 @@ def test_fp8_append_writes_each_token_at_its_page_slot():
             assert np.array_equal(kc[pg, slot], kcodes[b, t]) and np.array_equal(vc[pg, slot], vcodes[b, t])
             written[pg, slot] = True
     assert np.array_equal(kc[~written], kc0[~written]) and np.array_equal(vc[~written], vc0[~written])
+
+
+# ---------------------------------------------------------------- fp8 incoherent processing
+def test_hadamard_rotation_matches_the_matrix_and_is_orthogonal():
+    """The fp32 butterfly equals rows times diag(s) H / sqrt(d) with scipy's Hadamard matrix
+    (fp64, to fp32 rounding), R R^T = I, and rotating Q and K alike leaves Q K^T unchanged."""
+    from scipy.linalg import hadamard
+    rng = np.random.default_rng(2)
+    for d in (64, 128):
+        s = rng.choice([-1.0, 1.0], size=d)
+        R = np.diag(s) @ hadamard(d) / np.sqrt(d)
+        np.testing.assert_allclose(R @ R.T, np.eye(d), atol=1e-12)
+        x = rng.standard_normal((5, 7, d)).astype(np.float32)
+        got = F8.hadamard_rotate_f32(x, s).astype(np.float64)
+        want = x.astype(np.float64) @ R
+        assert np.abs(got - want).max() <= 2.0 ** -18 * np.abs(x).sum(axis=-1).max()
+        q, k = rng.standard_normal((9, d)), rng.standard_normal((11, d))
+        np.testing.assert_allclose((q @ R) @ (k @ R).T, q @ k.T, atol=1e-11)
+
+
+def test_hadamard_rotation_spreads_a_one_hot_row():
+    """A one-hot row e_j becomes s_j times row j of H over sqrt(d): every entry +-1/sqrt(d)
+    (exact in fp32 for d = 64), with the sign pattern of H's row j."""
+    from scipy.linalg import hadamard
+    d = 64
+    s = np.where(np.arange(d) % 3 == 0, -1.0, 1.0)
+    for j in (0, 5, 63):
+        e = np.zeros((1, d), np.float32)
+        e[0, j] = 1.0
+        got = F8.hadamard_rotate_f32(e, s)[0]
+        assert np.array_equal(got, (s[j] * hadamard(d)[j] / 8.0).astype(np.float32))
+
+
+def test_rotated_quantizer_is_the_plain_quantizer_of_the_rotated_rows():
+    """quantize_rows_rotated = per-block quantization (same scale rule) of the fp32 rotated
+    rows; an outlier channel that forces a coarse scale in the plain quantizer is spread out,
+    so the rotated codes reproduce Q K^T more closely."""
+    rng = np.random.default_rng(4)
+    B, N, H, d = 1, 96, 2, 128
+    x = rng.standard_normal((B, N, H, d)).astype(np.float32)
+    x[..., 7] *= 60.0                                     # an outlier channel
+    xb = bits(torch.tensor(x).to(torch.bfloat16))
+    s = rng.choice([-1.0, 1.0], size=d)
+    c, sc = F8.quantize_rows_rotated(xb, 64, s)
+    y = F8.hadamard_rotate_f32(F8._bf16_to_f32(xb), s)
+    for i in range(2):
+        sl = slice(64 * i, min(N, 64 * (i + 1)))
+        amax = np.float32(np.abs(y[0, sl, 1]).max())
+        assert sc[0, 1, i] == np.float32(amax / np.float32(448.0))
+        assert np.array_equal(c[0, sl, 1], F8.e4m3_encode((y[0, sl, 1] / sc[0, 1, i]).astype(np.float32)))
+    xf = F8._bf16_to_f32(xb).astype(np.float64)[0, :, 0]
+    exact = xf @ xf.T
+    c0, s0 = F8.quantize_rows(xb, 64)
+    plain = F8.dequantize(c0, s0, 64)[0, :, 0]
+    rot = F8.dequantize(c, sc, 64)[0, :, 0]
+    err_plain = np.abs(plain @ plain.T - exact).mean()
+    err_rot = np.abs(rot @ rot.T - exact).mean()
+    assert err_rot < 0.5 * err_plain, (err_rot, err_plain)
