@@ -26,7 +26,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_relpos_bias", "fa_fwd_prefix_lm", "fa_fwd_varlen", 
            "fa_kvcache_num_splits",
            "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary", "fa_bwd", "fa_bwd_workspace_size",
            "fa_fp8_quantize", "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8",
-           "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8",
+           "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8", "fa_fp8_quantize_rotated",
            "fa_combine", "fa_merge_attn_states", "fa_tile_class", "fa_last_error", "fa_version")
 
 FA_FP8_Q_BLOCK = 128
@@ -90,6 +90,7 @@ def lib():
     L.fa_varlen_paged_workspace_size.restype = SZ
     L.fa_fp8_quantize.argtypes = [P, I, I, I, I, S3, I, P, S3, P, P]
     L.fa_fp8_quantize_v.argtypes = [P, I, I, I, I, S3, P, P, P]
+    L.fa_fp8_quantize_rotated.argtypes = [P, I, I, I, I, S3, I, P, P, S3, P, P]
     L.fa_fp8_vt_len.argtypes = [I]
     L.fa_fwd_fp8.argtypes = [OPT, P, P, P, P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, P]
     L.fa_tile_class.argtypes = [I, I, I, I, I, I, I, I, I]
@@ -98,7 +99,7 @@ def lib():
     for name in ("fa_fwd", "fa_fwd_relpos_bias", "fa_fwd_prefix_lm", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
                  "fa_combine", "fa_merge_attn_states", "fa_tile_class",
                  "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary", "fa_bwd", "fa_fp8_quantize",
-                 "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8",
+                 "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8", "fa_fp8_quantize_rotated",
                  "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8"):
         getattr(L, name).restype = I
     _lib = L
@@ -583,6 +584,27 @@ def fa_fp8_quantize(x, block_rows, *, codes=None, scales=None, stream=None):
         raise ValueError(f"scales must be [{B}, {H}, {nblk}]")
     _check(lib().fa_fp8_quantize(_ptr(x), B, N, H, d, _strides(x, (0, 1, 2)), int(block_rows), _ptr(codes),
                                  _strides(codes, (0, 1, 2)), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def fa_fp8_quantize_rotated(x, block_rows, signs, *, codes=None, scales=None, stream=None):
+    """fa_fp8_quantize of the rows of x rotated by diag(signs) H / sqrt(d) (randomized Hadamard
+    transform; signs float32 [d] of +-1 on the device, the same for Q and K)."""
+    _bf16_cuda(x)
+    B, N, H, d = x.shape
+    nblk = -(-N // block_rows)
+    if signs.dtype != torch.float32 or not signs.is_cuda or not signs.is_contiguous() or signs.numel() != d:
+        raise TypeError(f"signs must be a contiguous float32 device tensor of {d} values")
+    if codes is None:
+        codes = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device)
+    _u8_cuda(codes)
+    _f32_cuda(scales)
+    if tuple(scales.shape) != (B, H, nblk):
+        raise ValueError(f"scales must be [{B}, {H}, {nblk}]")
+    _check(lib().fa_fp8_quantize_rotated(_ptr(x), B, N, H, d, _strides(x, (0, 1, 2)), int(block_rows), _ptr(signs),
+                                         _ptr(codes), _strides(codes, (0, 1, 2)), _ptr(scales), _stream(stream)))
     return codes, scales
 
 

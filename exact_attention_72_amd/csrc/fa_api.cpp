@@ -941,9 +941,10 @@ int fa_fp8_vt_len(int seqlen) {
   return seqlen <= 0 ? 0 : (int)(((int64_t)seqlen + FA_FP8_K_BLOCK - 1) / FA_FP8_K_BLOCK * FA_FP8_K_BLOCK);
 }
 
-int fa_fp8_quantize(const void* x, int batch, int seqlen, int heads, int head_dim, const int64_t x_strides[3],
-                    int block_rows, void* codes, const int64_t codes_strides[3], float* scales, void* stream) {
-  g_err[0] = 0;
+namespace {
+int fp8_quantize_rows(const void* x, int batch, int seqlen, int heads, int head_dim, const int64_t x_strides[3],
+                      int block_rows, const float* signs, void* codes, const int64_t codes_strides[3], float* scales,
+                      void* stream) {
   int rc;
   if (head_dim != 64 && head_dim != 128)
     return fail(FA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
@@ -961,11 +962,30 @@ int fa_fp8_quantize(const void* x, int batch, int seqlen, int heads, int head_di
   p.c_bs = codes_strides[0]; p.c_ss = codes_strides[1]; p.c_hs = codes_strides[2];
   p.scales = scales;
   p.B = batch; p.N = seqlen; p.H = heads; p.rows = block_rows;
+  p.signs = signs;
   p.nblk = (int)(((int64_t)seqlen + block_rows - 1) / block_rows);
   if ((int64_t)batch * heads * p.nblk > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "too many blocks");
   hipError_t e = fa_launch_fp8_quant(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
   return FA_OK;
+}
+}  // namespace
+
+int fa_fp8_quantize(const void* x, int batch, int seqlen, int heads, int head_dim, const int64_t x_strides[3],
+                    int block_rows, void* codes, const int64_t codes_strides[3], float* scales, void* stream) {
+  g_err[0] = 0;
+  return fp8_quantize_rows(x, batch, seqlen, heads, head_dim, x_strides, block_rows, nullptr, codes, codes_strides,
+                           scales, stream);
+}
+
+int fa_fp8_quantize_rotated(const void* x, int batch, int seqlen, int heads, int head_dim,
+                            const int64_t x_strides[3], int block_rows, const float* signs, void* codes,
+                            const int64_t codes_strides[3], float* scales, void* stream) {
+  g_err[0] = 0;
+  if (!signs) return fail(FA_ERR_INVALID_ARG, "signs is NULL");
+  if ((reinterpret_cast<uintptr_t>(signs) & 3u) != 0) return fail(FA_ERR_INVALID_ARG, "signs is not 4-byte aligned");
+  return fp8_quantize_rows(x, batch, seqlen, heads, head_dim, x_strides, block_rows, signs, codes, codes_strides,
+                           scales, stream);
 }
 
 int fa_fp8_quantize_v(const void* v, int batch, int seqlen, int heads_kv, int head_dim, const int64_t v_strides[3],

@@ -153,39 +153,90 @@ __device__ __forceinline__ float block_amax(float m, float* red) {
 // Rows form: one workgroup per (batch, head, block of p.rows rows).  The block's
 // amax gives scale = amax / 448 (1 for an all-zero block); a code is the e4m3
 // rounding of the fp32 quotient x / scale.
-template <int D>
+//
+// ROT (incoherent processing, "Attention kernels...", section 4.2): every row x
+// is first replaced by x diag(s) H / sqrt(D) (H the Sylvester Hadamard matrix,
+// s the caller's signs), formed in fp32 by the Walsh-Hadamard butterfly: pairs
+// (i, i + h) become (a + b, a - b) for h = 1, 2, ..., D / 2 in that order.  A
+// thread holds 8 consecutive values of a row and the row's D / 8 chunks sit in
+// consecutive lanes, so h = 1, 2, 4 run in registers and h = 8 .. D / 2 across
+// lanes (lane bit j = chunk bit j); the amax pass and the code pass both form
+// the rotated values (the same operations, so the same numbers).
+template <int D, bool ROT>
 __global__ __launch_bounds__(kThreads) void fa_fp8_quant_rows_kernel(FaFp8QuantParams p) {
   __shared__ float red[4];
   constexpr int CPR = D / 8;  // 16-byte chunks (8 values) per row
+  static_assert(kThreads % CPR == 0 && 64 % CPR == 0, "a row's chunks in consecutive lanes of one wave");
   const int blk = (int)(blockIdx.x % p.nblk);
   const int bh = (int)(blockIdx.x / p.nblk);
   const int b = bh / p.H, h = bh % p.H;
   const int r0 = blk * p.rows;
   const int rows = min(p.rows, p.N - r0);
   const int nch = rows * CPR;
+  const int cc = threadIdx.x % CPR;  // this thread's chunk of every row it touches
   const uint16_t* xb = p.x + (int64_t)b * p.x_bs + (int64_t)h * p.x_hs;
-  float m = 0.0f;
-  for (int c = threadIdx.x; c < nch; c += kThreads) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xb + (int64_t)(r0 + c / CPR) * p.x_ss + 8 * (c % CPR));
+  float sg[8];
+  if constexpr (ROT) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sg[e] = p.signs[8 * cc + e];
+  }
+  // the 8 fp32 values of chunk c (rotated with ROT); every lane of the wave runs
+  // this (the butterfly's lane exchanges), lanes past the block load zeros
+  auto values = [&](int c, bool valid, float (&y)[8]) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (valid) v = *reinterpret_cast<const u32x4*>(xb + (int64_t)(r0 + c / CPR) * p.x_ss + 8 * cc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      m = fmaxf(m, fabsf(bf16_to_f32(v[e] & 0xFFFFu)));
-      m = fmaxf(m, fabsf(bf16_to_f32(v[e] >> 16)));
+      y[2 * e] = bf16_to_f32(v[e] & 0xFFFFu);
+      y[2 * e + 1] = bf16_to_f32(v[e] >> 16);
     }
+    if constexpr (ROT) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= sg[e];
+#pragma unroll
+      for (int hh = 1; hh < 8; hh <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if ((i & hh) == 0) {
+            const float a = y[i], bb = y[i | hh];
+            y[i] = a + bb;
+            y[i | hh] = a - bb;
+          }
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int m = 1; m < CPR; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float o = __shfl_xor(y[e], m);
+          y[e] = (lane & m) ? o - y[e] : y[e] + o;   // the low index's value minus the high one's
+        }
+      constexpr float kInvSqrtD = D == 128 ? (float)0.08838834764831845 : 0.125f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= kInvSqrtD;
+    }
+  };
+  float m = 0.0f;
+  for (int c0 = 0; c0 < nch; c0 += kThreads) {
+    const int c = c0 + (int)threadIdx.x;
+    float y[8];
+    values(c, c < nch, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[e]));
   }
   const float amax = block_amax(m, red);
   const float scale = amax > 0.0f ? amax / kFp8Max : 1.0f;
   if (threadIdx.x == 0) p.scales[(int64_t)bh * p.nblk + blk] = scale;
   uint8_t* cb = p.codes + (int64_t)b * p.c_bs + (int64_t)h * p.c_hs;
-  for (int c = threadIdx.x; c < nch; c += kThreads) {
-    const int r = r0 + c / CPR;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xb + (int64_t)r * p.x_ss + 8 * (c % CPR));
-    u32x2 out;
-    out.x = quant4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xFFFFu),
-                   bf16_to_f32(v.y >> 16), scale);
-    out.y = quant4(bf16_to_f32(v.z & 0xFFFFu), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xFFFFu),
-                   bf16_to_f32(v.w >> 16), scale);
-    *reinterpret_cast<u32x2*>(cb + (int64_t)r * p.c_ss + 8 * (c % CPR)) = out;
+  for (int c0 = 0; c0 < nch; c0 += kThreads) {
+    const int c = c0 + (int)threadIdx.x;
+    float y[8];
+    values(c, c < nch, y);
+    if (c < nch) {
+      u32x2 out;
+      out.x = quant4(y[0], y[1], y[2], y[3], scale);
+      out.y = quant4(y[4], y[5], y[6], y[7], scale);
+      *reinterpret_cast<u32x2*>(cb + (int64_t)(r0 + c / CPR) * p.c_ss + 8 * cc) = out;
+    }
   }
 }
 
@@ -585,10 +636,14 @@ hipError_t fa_launch_fp8_quant(const FaFp8QuantParams& p, int d, hipStream_t s) 
     hipLaunchKernelGGL(fa_fp8_vt_scale_kernel, dim3(heads), dim3(kThreads), 0, s, p);
   } else {
     const unsigned grid = (unsigned)((int64_t)p.B * p.H * p.nblk);
-    if (d == 128)
-      hipLaunchKernelGGL(fa_fp8_quant_rows_kernel<128>, dim3(grid), dim3(kThreads), 0, s, p);
+    if (d == 128 && p.signs)
+      hipLaunchKernelGGL((fa_fp8_quant_rows_kernel<128, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    else if (d == 128)
+      hipLaunchKernelGGL((fa_fp8_quant_rows_kernel<128, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    else if (p.signs)
+      hipLaunchKernelGGL((fa_fp8_quant_rows_kernel<64, true>), dim3(grid), dim3(kThreads), 0, s, p);
     else
-      hipLaunchKernelGGL(fa_fp8_quant_rows_kernel<64>, dim3(grid), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((fa_fp8_quant_rows_kernel<64, false>), dim3(grid), dim3(kThreads), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -103,6 +103,9 @@ struct FaFp8QuantParams {
   uint8_t* vt;               // transposed form
   float* scales;
   int B, N, H, rows, nblk, npad;
+  // rows form: fp32 signs [head_dim] of the randomized Hadamard rotation applied
+  // to every row before quantization (NULL: none)
+  const float* signs;
 };
 
 // Rotary position embedding from caller tables: position pos, frequency i

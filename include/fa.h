@@ -410,6 +410,23 @@ int fa_fp8_quantize(const void* x, int batch, int seqlen, int heads, int head_di
                     const int64_t x_strides[3], int block_rows, void* codes,
                     const int64_t codes_strides[3], float* scales, void* stream);
 
+/* fa_fp8_quantize of rotated rows, for Q and K (incoherent processing,
+ * "Attention kernels ...", section 4.2: multiplying Q and K by one random
+ * orthogonal matrix spreads an outlier channel over all channels before the
+ * FP8 rounding, and leaves Q K^T unchanged).  Every row x is first replaced by
+ * x diag(signs) H / sqrt(head_dim) in fp32, H the Sylvester Hadamard matrix of
+ * order head_dim, formed by the Walsh-Hadamard butterfly (pairs (i, i + h)
+ * become (a + b, a - b) for h = 1, 2, ..., head_dim / 2, then one multiply by
+ * fp32(1 / sqrt(head_dim))); the block scales and codes are those of the
+ * rotated values.  signs: device float32 [head_dim], each +1 or -1, drawn by
+ * the caller and the same for Q and K (then fa_fwd_fp8 over the rotated Q and
+ * K codes computes the same attention; V is not rotated).  Other arguments and
+ * errors as fa_fp8_quantize; FA_ERR_INVALID_ARG for NULL or unaligned signs. */
+int fa_fp8_quantize_rotated(const void* x, int batch, int seqlen, int heads, int head_dim,
+                            const int64_t x_strides[3], int block_rows, const float* signs,
+                            void* codes, const int64_t codes_strides[3], float* scales,
+                            void* stream);
+
 /* Length of a transposed V row: seqlen rounded up to a multiple of FA_FP8_K_BLOCK. */
 int fa_fp8_vt_len(int seqlen);
 

@@ -153,3 +153,69 @@ def test_fp8_fwd_full_size_sampled_rows():
     rows = [0, 1, 63, 64, 127, 128, 1000, 2047, 2048, 4094, 4095]
     O, L, A = F8.fwd(rq[0], rq[1], 128, rk[0], rk[1], 64, rv[0], rv[1], causal=True, rows=rows, with_abs=True)
     check_fp8(out[:, rows], lse[:, :, rows], O, L, A, "fp8 4x16x4096 causal, sampled rows")
+
+
+# ---------------------------------------------------------------- incoherent processing
+def _signs(d, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randint(0, 2, (d,), generator=g) * 2 - 1).to(torch.float32)
+
+
+@pytest.mark.parametrize("d,block,N,strided", [(128, 128, 300, False), (128, 64, 200, True), (64, 64, 77, False),
+                                                 (128, 128, 1, False)])
+def test_quantize_rows_rotated_bit_exact(d, block, N, strided):
+    x = W.randn_bf16(W.generator(161 + N), (2, N, 3, d), 2.0)
+    s = _signs(d, N)
+    xd = x.to(DEV)
+    if strided:
+        wide = torch.zeros(2, N, 6, d, dtype=torch.bfloat16, device=DEV)
+        wide[:, :, ::2] = xd
+        xd = wide[:, :, ::2]
+    codes, scales = api.fa_fp8_quantize_rotated(xd, block, s.to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = F8.quantize_rows_rotated(bits(x), block, s.numpy())
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,causal", [(2, 200, 200, 4, 2, True), (1, 190, 300, 2, 2, False)])
+def test_fp8_fwd_rotated_parity(B, Nq, Nk, Hq, Hkv, causal):
+    """Q and K rotated by the same signs, V plain: the attention over those codes against the
+    oracle over the oracle's rotated codes."""
+    t = W.dense(171 + Nq, B, Nq, Hq, Hkv, 128, Nk=Nk)
+    s = _signs(128, 7)
+    q8, qs = api.fa_fp8_quantize_rotated(t["q"].to(DEV), 128, s.to(DEV))
+    k8, ks = api.fa_fp8_quantize_rotated(t["k"].to(DEV), 64, s.to(DEV))
+    vt, vs = api.fa_fp8_quantize_v(t["v"].to(DEV))
+    out, lse = api.fa_fwd_fp8(q8, qs, k8, ks, vt, vs, causal=causal)
+    torch.cuda.synchronize()
+    rq = F8.quantize_rows_rotated(bits(t["q"]), 128, s.numpy())
+    rk = F8.quantize_rows_rotated(bits(t["k"]), 64, s.numpy())
+    rv = F8.quantize_heads(bits(t["v"]))
+    O, L, A = F8.fwd(rq[0], rq[1], 128, rk[0], rk[1], 64, rv[0], rv[1], causal=causal, with_abs=True)
+    check_fp8(out, lse, O, L, A, f"fp8 rotated {B}x{Nq}x{Nk} causal={causal}")
+
+
+def test_fp8_rotation_reduces_the_error_of_outlier_channels():
+    """Q and K with a few outlier channels (x 30): the FP8 attention with the rotation is closer
+    to the exact bf16 attention (fp64 oracle) than without it."""
+    import oracle
+    B, N, H, d = 1, 256, 2, 128
+    t = W.dense(181, B, N, H, H, d)
+    for n in "qk":
+        x = t[n].float()
+        x[..., [3, 40, 77]] *= 30.0
+        t[n] = x.to(torch.bfloat16)
+    exact_o, exact_l = oracle.fwd_dense(bits(t["q"]), bits(t["k"]), bits(t["v"]), causal=True)
+    vt, vs = api.fa_fp8_quantize_v(t["v"].to(DEV))
+    errs = {}
+    for rot in (False, True):
+        s = _signs(d, 3).to(DEV)
+        qz = api.fa_fp8_quantize_rotated(t["q"].to(DEV), 128, s) if rot else api.fa_fp8_quantize(t["q"].to(DEV), 128)
+        kz = api.fa_fp8_quantize_rotated(t["k"].to(DEV), 64, s) if rot else api.fa_fp8_quantize(t["k"].to(DEV), 64)
+        out, lse = api.fa_fwd_fp8(*qz, *kz, vt, vs, causal=True)
+        torch.cuda.synchronize()
+        errs[rot] = (np.abs(out.float().cpu().numpy() - exact_o).mean(),
+                     np.abs(lse.cpu().numpy() - exact_l).mean())
+    print("fp8 outlier channels, mean |error| (O, LSE): plain", errs[False], "rotated", errs[True])
+    assert errs[True][0] < 0.7 * errs[False][0] and errs[True][1] < 0.7 * errs[False][1]

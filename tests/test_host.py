@@ -487,3 +487,15 @@ def test_fp8_cache_entry_points_reject_invalid_arguments():
     assert append(page=24) == FA_ERR_INVALID_ARG
     assert append(d=96) == FA_ERR_UNSUPPORTED
     assert append(Ln=0) == 0                                       # nothing to write, no launch
+
+
+def test_fp8_rotated_quantizer_rejects_invalid_arguments():
+    L = api.lib()
+    B3 = (ctypes.c_int64 * 3)(2048, 128 * 16, 128)
+
+    def call(signs=FAKE, d=128, blk=64):
+        return L.fa_fp8_quantize_rotated(FAKE, 2, 100, 16, d, S3, blk, signs, FAKE, B3, FAKE, None)
+    assert call(signs=None) == FA_ERR_INVALID_ARG
+    assert call(signs=ctypes.c_void_p((1 << 20) + 2)) == FA_ERR_INVALID_ARG
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(blk=0) == FA_ERR_INVALID_ARG
