@@ -26,7 +26,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_relpos_bias", "fa_fwd_prefix_lm", "fa_fwd_varlen", 
            "fa_kvcache_num_splits",
            "fa_kvcache_workspace_size", "fa_kvcache_append", "fa_rotary", "fa_bwd", "fa_bwd_workspace_size",
            "fa_fp8_quantize", "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8",
-           "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8", "fa_fp8_quantize_rotated",
+           "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8", "fa_fp8_quantize_rotated", "fa_bwd_varlen",
            "fa_combine", "fa_merge_attn_states", "fa_tile_class", "fa_last_error", "fa_version")
 
 FA_FP8_Q_BLOCK = 128
@@ -80,6 +80,8 @@ def lib():
     L.fa_kvcache_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I64, I, I, S3, S3, S3, S3, P, P, I, I, P]
     L.fa_rotary.argtypes = [P, I, I, I, I, S3, P, P, P, I, I, P]
     L.fa_bwd.argtypes = [OPT, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, S3, S3, S3, S3, S3, S3, S3, S3, P, SZ, P]
+    L.fa_bwd_varlen.argtypes = [OPT, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                S3, S3, S3, S3, S3, S3, S3, S3, P, SZ, P]
     L.fa_bwd_workspace_size.argtypes = [I, I, I]
     L.fa_bwd_workspace_size.restype = SZ
     L.fa_fwd_varlen_paged.argtypes = [OPT, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I64, I, I, I, P, SZ,
@@ -99,7 +101,7 @@ def lib():
     for name in ("fa_fwd", "fa_fwd_relpos_bias", "fa_fwd_prefix_lm", "fa_fwd_varlen", "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc",
                  "fa_combine", "fa_merge_attn_states", "fa_tile_class",
                  "fa_kvcache_append", "fa_fwd_varlen_paged", "fa_rotary", "fa_bwd", "fa_fp8_quantize",
-                 "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8", "fa_fp8_quantize_rotated",
+                 "fa_fwd_kvcache_paged_fp8", "fa_kvcache_append_fp8", "fa_fp8_quantize_rotated", "fa_bwd_varlen",
                  "fa_fp8_quantize_v", "fa_fp8_vt_len", "fa_fwd_fp8"):
         getattr(L, name).restype = I
     _lib = L
@@ -482,6 +484,37 @@ def fa_bwd(q, k, v, out, lse, dout, *, softmax_scale=None, causal=False, window=
     _check(lib().fa_bwd(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
                         _ptr(dk), _ptr(dv), B, Nq, Nk, Hq, Hkv, d, S(q), S(k), S(v), S(out), S(dout), S(dq), S(dk),
                         S(dv), _ptr(workspace), ws_bytes, _stream(stream)))
+    return dq, dk, dv
+
+
+def fa_bwd_varlen(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *,
+                  softmax_scale=None, causal=False, window=None, dq=None, dk=None, dv=None, workspace=None,
+                  stream=None):
+    """Gradients of fa_fwd_varlen: q/out/dout [total_q, Hq, d], k/v [total_k, Hkv, d] bf16, lse fp32
+    [Hq, total_q] from the forward, cu_seqlens int32 [B + 1] -> (dq, dk, dv) in the shapes of q, k, v."""
+    _bf16_cuda(q, k, v, out, dout)
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous() or c.numel() != B + 1:
+            raise TypeError("cu_seqlens must be contiguous int32 device tensors of batch + 1 entries")
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or tuple(lse.shape) != (Hq, Tq):
+        raise ValueError("lse must be a contiguous float32 [Hq, total_q] device tensor")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    _bf16_cuda(dq, dk, dv)
+    need = int(lib().fa_bwd_workspace_size(1, Tq, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    o = _opts(softmax_scale, causal, window, 0.0, 0)
+    S = lambda t: _strides(t, (0, 1))  # noqa: E731
+    _check(lib().fa_bwd_varlen(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B,
+                               int(max_seqlen_q), int(max_seqlen_k), Tq, Tk, Hq, Hkv, d, S(q), S(k), S(v), S(out),
+                               S(dout), S(dq), S(dk), S(dv), _ptr(workspace), ws_bytes, _stream(stream)))
     return dq, dk, dv
 
 

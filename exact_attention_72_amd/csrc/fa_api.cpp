@@ -853,6 +853,77 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   return FA_OK;
 }
 
+int fa_bwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const void* v, const void* out,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
+                  int total_k, int heads_q, int heads_kv, int head_dim, const int64_t q_strides[2],
+                  const int64_t k_strides[2], const int64_t v_strides[2], const int64_t o_strides[2],
+                  const int64_t do_strides[2], const int64_t dq_strides[2], const int64_t dk_strides[2],
+                  const int64_t dv_strides[2], void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc;
+  if ((rc = check_dims(head_dim, heads_q, heads_kv))) return rc;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(FA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (batch <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "batch must be positive and sizes non-negative");
+  if (((reinterpret_cast<uintptr_t>(cu_seqlens_q) | reinterpret_cast<uintptr_t>(cu_seqlens_k)) & 3u) != 0)
+    return fail(FA_ERR_INVALID_ARG, "cu_seqlens are not 4-byte aligned");
+  if ((rc = check_strides("q", q, q_strides, 2)) || (rc = check_strides("k", k, k_strides, 2)) ||
+      (rc = check_strides("v", v, v_strides, 2)) || (rc = check_strides("out", out, o_strides, 2)) ||
+      (rc = check_strides("dout", dout, do_strides, 2)) || (rc = check_strides("dq", dq, dq_strides, 2)) ||
+      (rc = check_strides("dk", dk, dk_strides, 2)) || (rc = check_strides("dv", dv, dv_strides, 2)) ||
+      (rc = check_token_stride("q", q_strides[0])) || (rc = check_token_stride("dout", do_strides[0])) ||
+      (rc = check_token_stride("k", k_strides[0])) || (rc = check_token_stride("v", v_strides[0])))
+    return rc;
+  // the dK/dV kernel reaches the L array from the D array with a 32-bit offset
+  if (bwd_row_bytes(1, total_q, heads_q) > (size_t)0x7fffff00)
+    return fail(FA_ERR_UNSUPPORTED, "heads_q * total_q of %lld rows is too many for the backward",
+                (long long)heads_q * total_q);
+  const size_t need = fa_bwd_workspace_size(1, total_q, heads_q);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FA_ERR_INVALID_ARG, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && !aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  FaParams f;
+  memset(&f, 0, sizeof f);
+  bool softcap = false;
+  if ((rc = fill_opts(opts, head_dim, &f, &softcap))) return rc;
+  if ((rc = no_alibi(f, "fa_bwd_varlen"))) return rc;
+  if (softcap) return fail(FA_ERR_UNSUPPORTED, "the backward pass has no softcap");
+  FaBwdParams p;
+  memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(out);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.delta = static_cast<float*>(workspace);
+  p.nlse = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_row_bytes(1, total_q, heads_q));
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.q_ss = q_strides[0]; p.q_hs = q_strides[1];
+  p.k_ss = k_strides[0]; p.k_hs = k_strides[1];
+  p.v_ss = v_strides[0]; p.v_hs = v_strides[1];
+  p.o_ss = o_strides[0]; p.o_hs = o_strides[1];
+  p.do_ss = do_strides[0]; p.do_hs = do_strides[1];
+  p.dq_ss = dq_strides[0]; p.dq_hs = dq_strides[1];
+  p.dk_ss = dk_strides[0]; p.dk_hs = dk_strides[1];
+  p.dv_ss = dv_strides[0]; p.dv_hs = dv_strides[1];
+  p.B = batch; p.Nq = max_seqlen_q; p.Nk = max_seqlen_k; p.Hq = heads_q; p.Hkv = heads_kv;
+  p.g = heads_q / heads_kv;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.scale_log2 = f.scale_log2;
+  p.scale = resolve_scale(opts, head_dim);
+  p.causal = f.causal; p.wl = f.wl; p.wr = f.wr;
+  hipError_t e = fa_launch_bwd(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return FA_OK;
+}
+
 int fa_combine(const float* o_part, const float* lse_part, int num_splits, int64_t rows, int head_dim,
                int64_t part_stride_rows, void* out, int64_t out_row_stride, float* lse_out, void* stream) {
   g_err[0] = 0;

@@ -136,9 +136,9 @@ struct FaBwdParams {
   const uint16_t* v;
   const uint16_t* o;
   const uint16_t* dout;
-  const float* lse;  // [B, Hq, Nq] natural-log LSE of the forward
-  float* delta;      // [B, Hq, Nq] D = rowsum(dO * O) (workspace)
-  float* nlse;       // [B, Hq, Nq] LSE log2(e), +inf for a row that sees no key (workspace)
+  const float* lse;  // [B, Hq, Nq] (varlen: [Hq, total_q]) natural-log LSE of the forward
+  float* delta;      // D = rowsum(dO * O), same layout (workspace)
+  float* nlse;       // LSE log2(e), +inf for a row that sees no key, same layout (workspace)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -148,6 +148,12 @@ struct FaBwdParams {
   int B, Nq, Nk, Hq, Hkv, g;
   float scale, scale_log2;
   int causal, wl, wr;
+  // varlen (cu_q != NULL): sequence b's tokens start at cu_q[b] / cu_k[b] of the
+  // token axis (batch strides 0), Nq / Nk are the longest lengths, and the LSE-row
+  // arrays are [Hq, total_q]
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int64_t total_q;
 };
 
 // In-place append of new K/V tokens to a paged cache.

@@ -2024,7 +2024,7 @@ __device__ __forceinline__ void uni_tr(const uint32_t (&tlo)[D / 32], const uint
 // query rows and walks the key blocks the rows can see.  A stage holds the key
 // block's K and V tiles in the unified swizzle: K rows for S^T = K Q^T, K read
 // transposed for dQ^T += K^T dS^T, V rows for dP^T = V dO^T.
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
   constexpr int BN = 32;
   constexpr int NBUF = 3;
@@ -2047,8 +2047,18 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
   const int64_t t = blockIdx.x;
   const int mb = m_blocks - 1 - (int)(t / pairs);
   const int b = (int)((t % pairs) / p.Hq), h = (int)((t % pairs) % p.Hq), kvh = h / p.g;
-  const int Lq = p.Nq, Lk = p.Nk;
   const int m0 = mb * 128;
+  // the sequence: lengths, token offsets and its (head, row 0) in the LSE-row arrays
+  int Lq = p.Nq, Lk = p.Nk;
+  int64_t tq = 0, tk = 0, lrow = ((int64_t)b * p.Hq + h) * p.Nq;
+  if constexpr (VARLEN) {
+    tq = scalar_load_i32(p.cu_q + b);
+    Lq = scalar_load_i32(p.cu_q + b + 1) - (int)tq;
+    tk = scalar_load_i32(p.cu_k + b);
+    Lk = scalar_load_i32(p.cu_k + b + 1) - (int)tk;
+    lrow = (int64_t)h * p.total_q + tq;
+    if (m0 >= Lq) return;  // past this sequence's rows (the grid covers the longest)
+  }
   FaRowSpan span;
   span.pos_lo = (int64_t)m0 + (Lk - Lq);
   span.pos_hi = (int64_t)min(m0 + 128, Lq) - 1 + (Lk - Lq);
@@ -2061,8 +2071,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
   const bool row_ok = row < Lq;
   bf16x8 qreg[D / 16], doreg[D / 16];
   {
-    const uint16_t* qb = p.q + b * p.q_bs + (int64_t)(row_ok ? row : 0) * p.q_ss + h * p.q_hs;
-    const uint16_t* db = p.dout + b * p.do_bs + (int64_t)(row_ok ? row : 0) * p.do_ss + h * p.do_hs;
+    const uint16_t* qb = p.q + b * p.q_bs + (tq + (row_ok ? row : 0)) * p.q_ss + h * p.q_hs;
+    const uint16_t* db = p.dout + b * p.do_bs + (tq + (row_ok ? row : 0)) * p.do_ss + h * p.do_hs;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
@@ -2077,12 +2087,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
   // D = rowsum(dO O) of the row (fp32) and its L in base-2 units; both also go
   // to the workspace for the dK/dV kernel (the grid covers every query row once).
   // P = exp2(s c - L log2 e); a row that sees nothing (L = -inf) gets P = 0.
-  const int64_t ri = ((int64_t)b * p.Hq + h) * Lq + (row_ok ? row : 0);
+  const int64_t ri = lrow + (row_ok ? row : 0);
   float dlt, nl = __builtin_inff();
   {
     float acc = 0.0f;
     if (row_ok) {
-      const uint16_t* ob = p.o + b * p.o_bs + (int64_t)row * p.o_ss + h * p.o_hs;
+      const uint16_t* ob = p.o + b * p.o_bs + (tq + row) * p.o_ss + h * p.o_hs;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(ob + 16 * kk + 8 * kg);
@@ -2116,8 +2126,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
   // DMA of key block n_lo + i into stage i % NBUF: buffer resources based at the
   // block's first key for a full block (the host keeps 32 token strides below
   // 2^31 bytes), rows clamped to the last key for a final partial one.
-  const uint16_t* kb = p.k + b * p.k_bs + kvh * p.k_hs;
-  const uint16_t* vb = p.v + b * p.v_bs + kvh * p.v_hs;
+  const uint16_t* kb = p.k + b * p.k_bs + tk * p.k_ss + kvh * p.k_hs;
+  const uint16_t* vb = p.v + b * p.v_bs + tk * p.v_ss + kvh * p.v_hs;
   const uint32_t k_voff = (uint32_t)(dma_row * p.k_ss + u_src) * 2u;
   const uint32_t v_voff = (uint32_t)(dma_row * p.v_ss + u_src) * 2u;
   const uint32_t k_step = (uint32_t)(G::kRowStep * p.k_ss) * 2u, v_step = (uint32_t)(G::kRowStep * p.v_ss) * 2u;
@@ -2205,7 +2215,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
     }
   }
   if (row_ok) {
-    uint16_t* ob = p.dq + b * p.dq_bs + (int64_t)row * p.dq_ss + h * p.dq_hs;
+    uint16_t* ob = p.dq + b * p.dq_bs + (tq + row) * p.dq_ss + h * p.dq_hs;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -2277,7 +2287,7 @@ __device__ __forceinline__ void ds_write_b128(uint32_t addr, u32x4 v) {
 // each other's gaps, with no product computed twice.  A stage holds the query
 // block's Q and dO tiles (unified swizzle) and its 32 L and D values; the P
 // waves issue its DMA.
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p) {
   constexpr int BM = 32;
   constexpr int NBUF = 4;
@@ -2303,8 +2313,20 @@ __global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParam
   const int64_t t = blockIdx.x;
   const int kbk = (int)(t / pairs);  // key blocks near the start first (they see the most queries)
   const int b = (int)((t % pairs) / p.Hkv), kvh = (int)((t % pairs) % p.Hkv);
-  const int Lq = p.Nq, Lk = p.Nk;
   const int j0 = kbk * 128;
+  // the sequence: lengths, token offsets, and where its rows of head h sit in the
+  // LSE-row arrays (lbase + h * lhead + row)
+  int Lq = p.Nq, Lk = p.Nk;
+  int64_t tq = 0, tk = 0, lbase = (int64_t)b * p.Hq * p.Nq, lhead = p.Nq;
+  if constexpr (VARLEN) {
+    tq = scalar_load_i32(p.cu_q + b);
+    Lq = scalar_load_i32(p.cu_q + b + 1) - (int)tq;
+    tk = scalar_load_i32(p.cu_k + b);
+    Lk = scalar_load_i32(p.cu_k + b + 1) - (int)tk;
+    lbase = tq;
+    lhead = p.total_q;
+    if (j0 >= Lk) return;  // past this sequence's keys (the grid covers the longest)
+  }
   int64_t i_lo, i_hi;
   fa_query_range(j0, min(j0 + 128, Lk) - 1, Lq, Lk, p.causal, p.wl, p.wr, &i_lo, &i_hi);
   const int qb_lo = (int)(i_lo / BM);
@@ -2316,8 +2338,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParam
   // the P wave holds the slice's K rows (S = Q K^T), the dK wave its V rows (dP = dO V^T)
   bf16x8 kv[D / 16];
   {
-    const uint16_t* src = pwave ? p.k + b * p.k_bs + (int64_t)(key_ok ? key : 0) * p.k_ss + kvh * p.k_hs
-                                : p.v + b * p.v_bs + (int64_t)(key_ok ? key : 0) * p.v_ss + kvh * p.v_hs;
+    const uint16_t* src = pwave ? p.k + b * p.k_bs + (tk + (key_ok ? key : 0)) * p.k_ss + kvh * p.k_hs
+                                : p.v + b * p.v_bs + (tk + (key_ok ? key : 0)) * p.v_ss + kvh * p.v_hs;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
@@ -2342,13 +2364,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParam
   dw.q0 = qb_lo * BM;
   {
     const int h0 = kvh * p.g;
-    dw.qoff = b * p.q_bs + (int64_t)h0 * p.q_hs + (int64_t)dw.q0 * p.q_ss;
-    dw.ooff = b * p.do_bs + (int64_t)h0 * p.do_hs + (int64_t)dw.q0 * p.do_ss;
-    dw.loff = ((int64_t)b * p.Hq + h0) * Lq + dw.q0;
+    dw.qoff = b * p.q_bs + (int64_t)h0 * p.q_hs + (tq + dw.q0) * p.q_ss;
+    dw.ooff = b * p.do_bs + (int64_t)h0 * p.do_hs + (tq + dw.q0) * p.do_ss;
+    dw.loff = lbase + h0 * lhead + dw.q0;
   }
   const int64_t q_blk = (int64_t)BM * p.q_ss, o_blk = (int64_t)BM * p.do_ss;
   const int64_t q_wrap = p.q_hs - (int64_t)nqb * q_blk, o_wrap = p.do_hs - (int64_t)nqb * o_blk;
-  const int64_t l_wrap = (int64_t)Lq - (int64_t)nqb * BM;
+  const int64_t l_wrap = lhead - (int64_t)nqb * BM;
   auto advance = [&](Walk& w) __attribute__((always_inline)) {
     w.q0 += BM, w.qoff += q_blk, w.ooff += o_blk, w.loff += BM;
     if (++w.qblk == nqb) {
@@ -2539,8 +2561,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParam
     }
   }
   if (key_ok) {
-    uint16_t* out = pwave ? p.dv + b * p.dv_bs + (int64_t)key * p.dv_ss + kvh * p.dv_hs
-                          : p.dk + b * p.dk_bs + (int64_t)key * p.dk_ss + kvh * p.dk_hs;
+    uint16_t* out = pwave ? p.dv + b * p.dv_bs + (tk + key) * p.dv_ss + kvh * p.dv_hs
+                          : p.dk + b * p.dk_bs + (tk + key) * p.dk_ss + kvh * p.dk_hs;
     const float sc = pwave ? 1.0f : p.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -2788,19 +2810,25 @@ hipError_t fa_launch_rotary(const FaRotaryParams& p, int d, hipStream_t s) {
 }
 
 hipError_t fa_launch_bwd(const FaBwdParams& p, int d, hipStream_t s) {
-  const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
-  if (rows <= 0 || p.Nk <= 0) return hipSuccess;
-  // the dQ kernel also writes D and the base-2 LSE that the dK/dV kernel reads
+  // varlen: Nq / Nk are the longest lengths; the workgroups past a sequence's
+  // rows or keys return at once
   const int64_t dq_tiles = (int64_t)((p.Nq + 127) / 128) * p.B * p.Hq;
   const int64_t dkv_tiles = (int64_t)((p.Nk + 127) / 128) * p.B * p.Hkv;
-  if (d == 128) {
-    hipLaunchKernelGGL(fa_bwd_dq_kernel<128>, dim3((unsigned)dq_tiles), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<128>, dim3((unsigned)dkv_tiles), dim3(2 * kThreads), 0, s, p);
-  } else if (d == 64) {
-    hipLaunchKernelGGL(fa_bwd_dq_kernel<64>, dim3((unsigned)dq_tiles), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<64>, dim3((unsigned)dkv_tiles), dim3(2 * kThreads), 0, s, p);
-  } else {
-    return hipErrorInvalidValue;
+  if (dq_tiles > 0x7fffffff || dkv_tiles > 0x7fffffff) return hipErrorInvalidValue;
+  if (d != 128 && d != 64) return hipErrorInvalidValue;
+  // the dQ kernel also writes D and the base-2 LSE that the dK/dV kernel reads
+  const bool vl = p.cu_q != nullptr;
+#define FA_BWD(K_, D_, T_, N_)                                                                    \
+  if (vl) hipLaunchKernelGGL((K_<D_, true>), dim3((unsigned)(T_)), dim3(N_), 0, s, p);            \
+  else hipLaunchKernelGGL((K_<D_, false>), dim3((unsigned)(T_)), dim3(N_), 0, s, p);
+  if (dq_tiles > 0) {
+    if (d == 128) { FA_BWD(fa_bwd_dq_kernel, 128, dq_tiles, kThreads) }
+    else { FA_BWD(fa_bwd_dq_kernel, 64, dq_tiles, kThreads) }
   }
+  if (dkv_tiles > 0) {
+    if (d == 128) { FA_BWD(fa_bwd_dkdv_kernel, 128, dkv_tiles, 2 * kThreads) }
+    else { FA_BWD(fa_bwd_dkdv_kernel, 64, dkv_tiles, 2 * kThreads) }
+  }
+#undef FA_BWD
   return hipGetLastError();
 }

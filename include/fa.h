@@ -385,6 +385,30 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
            const int64_t dk_strides[3], const int64_t dv_strides[3], void* workspace,
            size_t workspace_bytes, void* stream);
 
+/* fa_bwd for packed variable-length sequences (the layout of fa_fwd_varlen):
+ * sequence b's queries are tokens cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1 and
+ * its keys cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1, each sequence bottom-right
+ * aligned on its own ("FA4 ...", sections 3 and 4: the varlen call has the same
+ * autograd as the dense one).
+ *   q, out, dout, dq  [total_q, heads_q, head_dim]  (strides {token, head})
+ *   k, v, dk, dv      [total_k, heads_kv, head_dim]
+ *   lse               float32 [heads_q, total_q]: fa_fwd_varlen's LSE
+ *   cu_seqlens_q/_k   device int32 [batch + 1]; max_seqlen_q / max_seqlen_k: upper
+ *                     bounds of the lengths (they size the grids)
+ *   workspace         at least fa_bwd_workspace_size(1, total_q, heads_q) bytes
+ * Errors and the rest as fa_bwd (also K/V token strides of 2^25 elements or more are
+ * FA_ERR_UNSUPPORTED).  Caller contract, not checked on the device: cu_seqlens_q[batch]
+ * == total_q, cu_seqlens_k[batch] <= total_k, every length <= its maximum. */
+int fa_bwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const void* v,
+                  const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                  void* dv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                  int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int heads_q,
+                  int heads_kv, int head_dim, const int64_t q_strides[2], const int64_t k_strides[2],
+                  const int64_t v_strides[2], const int64_t o_strides[2],
+                  const int64_t do_strides[2], const int64_t dq_strides[2],
+                  const int64_t dk_strides[2], const int64_t dv_strides[2], void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace fa_bwd needs: twice batch * heads_q * seqlen_q * 4 rounded up to 256
  * (D and the base-2 LSE of every query row). */
 size_t fa_bwd_workspace_size(int batch, int seqlen_q, int heads_q);

@@ -109,3 +109,64 @@ def test_bwd_full_size_heads():
                            heads=heads)
     got = [x[:1, :, heads] for x in (dq, dk, dv)]
     check_grads(got, [r[:, :, heads] for r in ref], "bwd full size, batch 0, heads 0/7/15")
+
+
+# ---------------------------------------------------------------- varlen (fa_bwd_varlen)
+VARLEN_CASES = [
+    # query lengths, key lengths, Hq, Hkv, d, causal, window
+    ([1, 64, 130, 257, 3], None, 8, 2, 128, True, None),
+    ([5, 200, 0, 77, 40], [300, 200, 10, 77, 0], 4, 4, 128, True, None),   # Lk > Lq, an empty query set, no keys
+    ([100, 333, 17], None, 4, 1, 64, False, (40, 20)),
+    ([129, 31], [150, 31], 2, 2, 128, True, (64, 0)),
+]
+
+
+@pytest.mark.parametrize("lq,lk,Hq,Hkv,d,causal,window", VARLEN_CASES)
+def test_bwd_varlen(lq, lk, Hq, Hkv, d, causal, window):
+    """Packed sequences (the varlen forward's layout) against the oracle's dense backward of
+    each sequence on its own (bottom-right per sequence; GQA sums over the group)."""
+    lk = lq if lk is None else lk
+    print(f"bwd varlen lq={lq} lk={lk} h{Hq}/{Hkv} d{d}", flush=True)
+    g = W.generator(501 + sum(lq) + d)
+    cq, ck = W.prefix_sum(torch.tensor(lq)), W.prefix_sum(torch.tensor(lk))
+    Tq, Tk = int(cq[-1]), int(ck[-1])
+    q = W.randn_bf16(g, (Tq, Hq, d))
+    k = W.randn_bf16(g, (Tk, Hkv, d))
+    v = W.randn_bf16(g, (Tk, Hkv, d))
+    do = W.randn_bf16(g, (Tq, Hq, d))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    cqd, ckd = cq.to(DEV), ck.to(DEV)
+    out, lse = api.fa_fwd_varlen(qd, kd, vd, cqd, ckd, max(lq), causal=causal, window=window)
+    dq, dk, dv = api.fa_bwd_varlen(qd, kd, vd, out, lse, do.to(DEV), cqd, ckd, max(lq), max(lk), causal=causal,
+                                   window=window)
+    torch.cuda.synchronize()
+    cqh, ckh = cq.tolist(), ck.tolist()
+    for s in range(len(lq)):
+        a, b = cqh[s], cqh[s + 1]
+        c, e = ckh[s], ckh[s + 1]
+        got = (dq[a:b], dk[c:e], dv[c:e])
+        if b == a or e == c:
+            # no queries or no keys: nothing flows, every gradient element is zero
+            for x in got:
+                assert torch.count_nonzero(x.float()) == 0, f"sequence {s}"
+            continue
+        ref = oracle.bwd_dense(bits(q[a:b][None]), bits(k[c:e][None]), bits(v[c:e][None]), bits(do[a:b][None]),
+                               causal=causal, window=window)
+        check_grads(got, tuple(r[0] for r in ref), f"bwd varlen sequence {s} ({b - a} x {e - c})")
+
+
+def test_bwd_varlen_equals_dense_on_equal_lengths():
+    """Four sequences of one length packed: bitwise the dense backward of the same tensors."""
+    B, N, Hq, Hkv, d = 4, 300, 4, 2, 128
+    t = W.dense(511, B, N, Hq, Hkv, d, device=DEV)
+    do = W.randn_bf16(W.generator(512), (B, N, Hq, d)).to(DEV)
+    out, lse = api.fa_fwd(t["q"], t["k"], t["v"], causal=True)
+    dense = api.fa_bwd(t["q"], t["k"], t["v"], out, lse, do, causal=True)
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device=DEV)
+    flat = lambda x: x.reshape(B * x.shape[1], x.shape[2], x.shape[3])  # noqa: E731
+    lse_v = lse.permute(1, 0, 2).reshape(Hq, B * N).contiguous()
+    packed = api.fa_bwd_varlen(flat(t["q"]), flat(t["k"]), flat(t["v"]), flat(out), lse_v, flat(do), cu, cu, N, N,
+                               causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(dense, packed):
+        assert torch.equal(x.reshape(y.shape), y)

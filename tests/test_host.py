@@ -499,3 +499,21 @@ def test_fp8_rotated_quantizer_rejects_invalid_arguments():
     assert call(signs=ctypes.c_void_p((1 << 20) + 2)) == FA_ERR_INVALID_ARG
     assert call(d=96) == FA_ERR_UNSUPPORTED
     assert call(blk=0) == FA_ERR_INVALID_ARG
+
+
+def test_bwd_varlen_rejects_invalid_arguments():
+    L = api.lib()
+    o = _opts(causal=1)
+
+    def call(cu=FAKE, d=128, B=4, Hq=16, Hkv=4, ws_bytes=1 << 30, opts=o, mq=100, tq=400):
+        return L.fa_bwd_varlen(ctypes.byref(opts), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cu, FAKE,
+                               B, mq, mq, tq, tq, Hq, Hkv, d, S2, S2, S2, S2, S2, S2, S2, S2, FAKE, ws_bytes, None)
+    assert call(cu=None) == FA_ERR_INVALID_ARG
+    assert call(cu=ctypes.c_void_p((1 << 20) + 2)) == FA_ERR_INVALID_ARG
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(B=0) == FA_ERR_INVALID_ARG
+    assert call(mq=-1) == FA_ERR_INVALID_ARG
+    assert call(Hq=18) == FA_ERR_INVALID_ARG
+    assert call(ws_bytes=16) == FA_ERR_INVALID_ARG                    # D and L need 2 x 16 x 400 x 4 bytes
+    assert call(opts=_opts(causal=1, softcap=30.0)) == FA_ERR_UNSUPPORTED
+    assert call(tq=1 << 30) == FA_ERR_UNSUPPORTED                     # rows past the 32-bit D-to-L offset
