@@ -405,7 +405,7 @@ def fwd_dense_prefix_lm(q, k, v, prefix_lens, *, scale=None, window=None, rows=N
     return O, L
 
 
-def bwd_dense(q, k, v, dout, *, scale=None, causal=False, window=None, heads=None):
+def bwd_dense(q, k, v, dout, *, scale=None, causal=False, window=None, softcap=0.0, heads=None):
     """Gradients of the attention forward, in fp64 with S and P materialised.
 
     "Attention kernels: FlashAttention and PagedAttention", section 4.3: the
@@ -415,6 +415,9 @@ def bwd_dense(q, k, v, dout, *, scale=None, causal=False, window=None, heads=Non
     dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.  Query head h uses KV
     head h // (Hq / Hkv), so dK and dV sum over the query heads of a group.
     Rows that see no key have P = 0 and contribute nothing.
+    softcap c > 0: the logit is c tanh(scale q.k / c) (the forward's transform,
+    "FA4 (CuTeDSL) and engineering interfaces", section 7), so by the chain rule dS
+    is multiplied by its derivative 1 - tanh^2(scale q.k / c) before dQ and dK.
 
     q, dout: uint16 bf16 bits [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d].  heads: None for
     all query heads, or a list of query heads (then dK, dV hold only their share).
@@ -433,6 +436,11 @@ def bwd_dense(q, k, v, dout, *, scale=None, causal=False, window=None, heads=Non
         for h in (range(Hq) if heads is None else heads):
             hk = h // g
             S = s * (qd[b, :, h] @ kd[b, :, hk].T)
+            dcap = 1.0
+            if softcap > 0:
+                th = np.tanh(S / softcap)
+                S = softcap * th
+                dcap = 1.0 - th * th
             S = np.where(vis, S, -np.inf)
             m = S.max(axis=1, keepdims=True)
             empty = ~np.isfinite(m)
@@ -442,7 +450,7 @@ def bwd_dense(q, k, v, dout, *, scale=None, causal=False, window=None, heads=Non
             dO = od[b, :, h]
             Dr = np.sum(dO * O, axis=1, keepdims=True)
             dP = dO @ vd[b, :, hk].T
-            dS = P * (dP - Dr)
+            dS = P * (dP - Dr) * dcap
             dv[b, :, hk] += P.T @ dO
             dq[b, :, h] = s * (dS @ kd[b, :, hk])
             dk[b, :, hk] += s * (dS.T @ qd[b, :, h])

@@ -443,8 +443,9 @@ def test_rotary_preserves_norms_and_depends_on_relative_position():
 
 
 # ---------------------------------------------------------------- backward
-def _torch_grads(q, k, v, do, scale, vis, g):
-    """fp64 autograd through an explicitly masked softmax attention (library routine)."""
+def _torch_grads(q, k, v, do, scale, vis, g, softcap=0.0):
+    """fp64 autograd through an explicitly masked softmax attention (library routine),
+    with the logit c tanh(s / c) when softcap c > 0."""
     Q = torch.tensor(v_double(q), requires_grad=True)
     K = torch.tensor(v_double(k), requires_grad=True)
     V = torch.tensor(v_double(v), requires_grad=True)
@@ -452,6 +453,8 @@ def _torch_grads(q, k, v, do, scale, vis, g):
     Ke = K.repeat_interleave(g, dim=2)
     Ve = V.repeat_interleave(g, dim=2)
     S = torch.einsum("bihd,bjhd->bhij", Q, Ke) * scale
+    if softcap > 0:
+        S = softcap * torch.tanh(S / softcap)
     S = S.masked_fill(~torch.as_tensor(vis)[None, None], float("-inf"))
     P = torch.softmax(S, dim=-1)
     O = torch.einsum("bhij,bjhd->bihd", P, Ve)
@@ -472,6 +475,28 @@ def test_bwd_matches_torch_autograd(Nq, Nk, causal, window):
     tq, tk, tv = _torch_grads(q, k, v, do, d ** -0.5, vis, Hq // Hkv)
     for a, b_ in ((dq, tq), (dk, tk), (dv, tv)):
         np.testing.assert_allclose(a, b_, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("Nq,Nk,causal,window,cap", [(37, 37, True, None, 1.5), (20, 45, True, None, 0.7),
+                                                     (33, 33, False, (5, 3), 3.0)])
+def test_bwd_softcap_matches_torch_autograd(Nq, Nk, causal, window, cap):
+    """Softcapped logits (caps small enough that tanh bends the scores): the oracle's chain
+    rule against torch's fp64 autograd; a cap this small changes the gradients visibly."""
+    g = W.generator(331 + Nq + Nk)
+    B, Hq, Hkv, d = 2, 4, 2, 16
+    q, k, v = (W.randn_bf16(g, (B, n, h, d), 2.0) for n, h in ((Nq, Hq), (Nk, Hkv), (Nk, Hkv)))
+    do = W.randn_bf16(g, (B, Nq, Hq, d))
+    dq, dk, dv = oracle.bwd_dense(bits(q), bits(k), bits(v), bits(do), causal=causal, window=window, softcap=cap)
+    vis = oracle.visible_mask(Nq, Nk, causal, window)
+    tq, tk, tv = _torch_grads(q, k, v, do, d ** -0.5, vis, Hq // Hkv, softcap=cap)
+    for a, b_ in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-11)
+    plain = oracle.bwd_dense(bits(q), bits(k), bits(v), bits(do), causal=causal, window=window)
+    assert np.abs(plain[0] - dq).max() > 1e-2
+    # a cap far above every score is the plain backward
+    big = oracle.bwd_dense(bits(q), bits(k), bits(v), bits(do), causal=causal, window=window, softcap=1e7)
+    for a, b_ in zip(big, plain):
+        np.testing.assert_allclose(a, b_, rtol=0, atol=1e-9)
 
 
 def test_bwd_closed_forms():
