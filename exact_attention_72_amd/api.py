@@ -462,8 +462,8 @@ def fa_kvcache_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, bloc
                                        _stream(stream)))
 
 
-def fa_bwd(q, k, v, out, lse, dout, *, softmax_scale=None, causal=False, window=None, dq=None, dk=None,
-           dv=None, workspace=None, stream=None):
+def fa_bwd(q, k, v, out, lse, dout, *, softmax_scale=None, causal=False, window=None, softcap=0.0, dq=None,
+           dk=None, dv=None, workspace=None, stream=None):
     """Gradients of fa_fwd: q/out/dout [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] bf16, lse fp32
     [B, Hq, Nq] from the forward -> (dq, dk, dv) bf16 in the shapes of q, k, v."""
     _bf16_cuda(q, k, v, out, dout)
@@ -479,7 +479,7 @@ def fa_bwd(q, k, v, out, lse, dout, *, softmax_scale=None, causal=False, window=
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    o = _opts(softmax_scale, causal, window, 0.0, 0)
+    o = _opts(softmax_scale, causal, window, softcap, 0)
     S = lambda t: _strides(t, (0, 1, 2))  # noqa: E731
     _check(lib().fa_bwd(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
                         _ptr(dk), _ptr(dv), B, Nq, Nk, Hq, Hkv, d, S(q), S(k), S(v), S(out), S(dout), S(dq), S(dk),
@@ -488,8 +488,8 @@ def fa_bwd(q, k, v, out, lse, dout, *, softmax_scale=None, causal=False, window=
 
 
 def fa_bwd_varlen(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *,
-                  softmax_scale=None, causal=False, window=None, dq=None, dk=None, dv=None, workspace=None,
-                  stream=None):
+                  softmax_scale=None, causal=False, window=None, softcap=0.0, dq=None, dk=None, dv=None,
+                  workspace=None, stream=None):
     """Gradients of fa_fwd_varlen: q/out/dout [total_q, Hq, d], k/v [total_k, Hkv, d] bf16, lse fp32
     [Hq, total_q] from the forward, cu_seqlens int32 [B + 1] -> (dq, dk, dv) in the shapes of q, k, v."""
     _bf16_cuda(q, k, v, out, dout)
@@ -509,7 +509,7 @@ def fa_bwd_varlen(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqle
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    o = _opts(softmax_scale, causal, window, 0.0, 0)
+    o = _opts(softmax_scale, causal, window, softcap, 0)
     S = lambda t: _strides(t, (0, 1))  # noqa: E731
     _check(lib().fa_bwd_varlen(ctypes.byref(o), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B,

@@ -822,7 +822,6 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &f, &softcap))) return rc;
   if ((rc = no_alibi(f, "fa_bwd"))) return rc;
-  if (softcap) return fail(FA_ERR_UNSUPPORTED, "the backward pass has no softcap");
   FaBwdParams p;
   memset(&p, 0, sizeof p);
   p.q = static_cast<const uint16_t*>(q);
@@ -848,6 +847,7 @@ int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v
   p.scale_log2 = f.scale_log2;
   p.scale = resolve_scale(opts, head_dim);
   p.causal = f.causal; p.wl = f.wl; p.wr = f.wr;
+  p.softcap = softcap ? 1 : 0; p.cap_in = f.cap_in; p.cap_out = f.cap_out;
   hipError_t e = fa_launch_bwd(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return FA_OK;
@@ -889,7 +889,6 @@ int fa_bwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
   bool softcap = false;
   if ((rc = fill_opts(opts, head_dim, &f, &softcap))) return rc;
   if ((rc = no_alibi(f, "fa_bwd_varlen"))) return rc;
-  if (softcap) return fail(FA_ERR_UNSUPPORTED, "the backward pass has no softcap");
   FaBwdParams p;
   memset(&p, 0, sizeof p);
   p.q = static_cast<const uint16_t*>(q);
@@ -919,6 +918,7 @@ int fa_bwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
   p.scale_log2 = f.scale_log2;
   p.scale = resolve_scale(opts, head_dim);
   p.causal = f.causal; p.wl = f.wl; p.wr = f.wr;
+  p.softcap = softcap ? 1 : 0; p.cap_in = f.cap_in; p.cap_out = f.cap_out;
   hipError_t e = fa_launch_bwd(p, head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return FA_OK;

@@ -154,6 +154,10 @@ struct FaBwdParams {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int64_t total_q;
+  // softcap (the forward's transform): cap_in = scale / softcap, cap_out =
+  // softcap log2(e); softcap == 0: none
+  int softcap;
+  float cap_in, cap_out;
 };
 
 // In-place append of new K/V tokens to a paged cache.

@@ -2024,7 +2024,7 @@ __device__ __forceinline__ void uni_tr(const uint32_t (&tlo)[D / 32], const uint
 // query rows and walks the key blocks the rows can see.  A stage holds the key
 // block's K and V tiles in the unified swizzle: K rows for S^T = K Q^T, K read
 // transposed for dQ^T += K^T dS^T, V rows for dP^T = V dO^T.
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
   constexpr int BN = 32;
   constexpr int NBUF = 3;
@@ -2036,6 +2036,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, kg = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float c = p.scale_log2;
+  const float cap2 = p.cap_in * (2.0f * kLog2e);  // softcap: exp(2 s cap_in) = exp2(s cap2)
   UniOffsets<D> uo;
   uo.init(lane, lds_addr(smem));
   const int dma_row = wave * G::kRowsPerKiB + lane / G::kChunksPerRow;
@@ -2187,8 +2188,16 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(FaBwdParams p) {
     f32x8 x0, x1;
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
-      const float pa = exp2_fast(__builtin_fmaf(s[a], c, -nl));
-      const float ds = pa * (dpt[a] - dlt);
+      float ds;
+      if constexpr (SOFTCAP) {
+        // the forward's logit cap_out (1 - u), u = 2 / (exp(2 s cap_in) + 1), and
+        // its derivative in the scaled score, 1 - tanh^2 = u (2 - u)
+        const float u = 2.0f * rcp_fast(exp2_fast(s[a] * cap2) + 1.0f);
+        const float la = s[a] == kNegInf ? kNegInf : __builtin_fmaf(-p.cap_out, u, p.cap_out);
+        ds = exp2_fast(la - nl) * (dpt[a] - dlt) * (u * (2.0f - u));
+      } else {
+        ds = exp2_fast(__builtin_fmaf(s[a], c, -nl)) * (dpt[a] - dlt);
+      }
       if (a < 8)
         x0[a] = ds;
       else
@@ -2287,7 +2296,7 @@ __device__ __forceinline__ void ds_write_b128(uint32_t addr, u32x4 v) {
 // each other's gaps, with no product computed twice.  A stage holds the query
 // block's Q and dO tiles (unified swizzle) and its 32 L and D values; the P
 // waves issue its DMA.
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool SOFTCAP>
 __global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParams p) {
   constexpr int BM = 32;
   constexpr int NBUF = 4;
@@ -2304,6 +2313,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParam
   const int slot = wave & 3;
   const bool pwave = wave < 4;
   const float c = p.scale_log2;
+  const float cap2 = p.cap_in * (2.0f * kLog2e);  // softcap: exp(2 s cap_in) = exp2(s cap2)
   UniOffsets<D> uo;
   uo.init(lane, lds_addr(smem) + kSt);
   const int dma_row = slot * G::kRowsPerKiB + lane / G::kChunksPerRow;
@@ -2473,19 +2483,32 @@ __global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParam
         sv[a] = vis ? sv[a] : kNegInf;
       }
     }
-    // P = exp2(s c - L), L in base-2 units (+inf for a row that sees no key, so P = 0)
-    f32x16 pa;
+    // P = exp2(s c - L), L in base-2 units (+inf for a row that sees no key, so P = 0);
+    // the dK wave gets P, or with softcap P times the transform's derivative
+    // 1 - tanh^2 = u (2 - u) (the logit is cap_out (1 - u), u = 2 / (exp(2 s cap_in) + 1))
+    f32x16 pa, ph;
 #pragma unroll
-    for (int a = 0; a < 16; ++a) pa[a] = exp2_fast(__builtin_fmaf(sv[a], c, -__uint_as_float(lr[a >> 2][a & 3])));
+    for (int a = 0; a < 16; ++a) {
+      const float la = -__uint_as_float(lr[a >> 2][a & 3]);
+      if constexpr (SOFTCAP) {
+        const float u = 2.0f * rcp_fast(exp2_fast(sv[a] * cap2) + 1.0f);
+        const float lg = sv[a] == kNegInf ? kNegInf : __builtin_fmaf(-p.cap_out, u, p.cap_out);
+        pa[a] = exp2_fast(lg + la);
+        ph[a] = pa[a] * (u * (2.0f - u));
+      } else {
+        pa[a] = exp2_fast(__builtin_fmaf(sv[a], c, la));
+        ph[a] = pa[a];
+      }
+    }
     const uint32_t pw = p_base + (uint32_t)((t_ & 1) * 4 * kPB);
-    ds_write_b128<0>(pw, u32x4{__float_as_uint(pa[0]), __float_as_uint(pa[1]), __float_as_uint(pa[2]),
-                               __float_as_uint(pa[3])});
-    ds_write_b128<1024>(pw, u32x4{__float_as_uint(pa[4]), __float_as_uint(pa[5]), __float_as_uint(pa[6]),
-                                  __float_as_uint(pa[7])});
-    ds_write_b128<2048>(pw, u32x4{__float_as_uint(pa[8]), __float_as_uint(pa[9]), __float_as_uint(pa[10]),
-                                  __float_as_uint(pa[11])});
-    ds_write_b128<3072>(pw, u32x4{__float_as_uint(pa[12]), __float_as_uint(pa[13]), __float_as_uint(pa[14]),
-                                  __float_as_uint(pa[15])});
+    ds_write_b128<0>(pw, u32x4{__float_as_uint(ph[0]), __float_as_uint(ph[1]), __float_as_uint(ph[2]),
+                               __float_as_uint(ph[3])});
+    ds_write_b128<1024>(pw, u32x4{__float_as_uint(ph[4]), __float_as_uint(ph[5]), __float_as_uint(ph[6]),
+                                  __float_as_uint(ph[7])});
+    ds_write_b128<2048>(pw, u32x4{__float_as_uint(ph[8]), __float_as_uint(ph[9]), __float_as_uint(ph[10]),
+                                  __float_as_uint(ph[11])});
+    ds_write_b128<3072>(pw, u32x4{__float_as_uint(ph[12]), __float_as_uint(ph[13]), __float_as_uint(ph[14]),
+                                  __float_as_uint(ph[15])});
     f32x8 x0, x1;
 #pragma unroll
     for (int a = 0; a < 8; ++a) x0[a] = pa[a], x1[a] = pa[8 + a];
@@ -2817,10 +2840,12 @@ hipError_t fa_launch_bwd(const FaBwdParams& p, int d, hipStream_t s) {
   if (dq_tiles > 0x7fffffff || dkv_tiles > 0x7fffffff) return hipErrorInvalidValue;
   if (d != 128 && d != 64) return hipErrorInvalidValue;
   // the dQ kernel also writes D and the base-2 LSE that the dK/dV kernel reads
-  const bool vl = p.cu_q != nullptr;
-#define FA_BWD(K_, D_, T_, N_)                                                                    \
-  if (vl) hipLaunchKernelGGL((K_<D_, true>), dim3((unsigned)(T_)), dim3(N_), 0, s, p);            \
-  else hipLaunchKernelGGL((K_<D_, false>), dim3((unsigned)(T_)), dim3(N_), 0, s, p);
+  const bool vl = p.cu_q != nullptr, sc = p.softcap != 0;
+#define FA_BWD(K_, D_, T_, N_)                                                                         \
+  if (vl && sc) hipLaunchKernelGGL((K_<D_, true, true>), dim3((unsigned)(T_)), dim3(N_), 0, s, p);      \
+  else if (vl) hipLaunchKernelGGL((K_<D_, true, false>), dim3((unsigned)(T_)), dim3(N_), 0, s, p);      \
+  else if (sc) hipLaunchKernelGGL((K_<D_, false, true>), dim3((unsigned)(T_)), dim3(N_), 0, s, p);      \
+  else hipLaunchKernelGGL((K_<D_, false, false>), dim3((unsigned)(T_)), dim3(N_), 0, s, p);
   if (dq_tiles > 0) {
     if (d == 128) { FA_BWD(fa_bwd_dq_kernel, 128, dq_tiles, kThreads) }
     else { FA_BWD(fa_bwd_dq_kernel, 64, dq_tiles, kThreads) }

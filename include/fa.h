@@ -372,9 +372,11 @@ int fa_rotary(void* x, int batch, int seqlen, int heads, int head_dim,
  *   dq, dk, dv        bf16, written (every element, zeros where nothing flows)
  *   workspace         device memory of at least fa_bwd_workspace_size(...) bytes (holds D and
  *                     the LSE in base-2 units per query row)
- * opts as for fa_fwd (same scale, causal, window); softcap > 0 is FA_ERR_UNSUPPORTED, and so
- * are a token stride of q or dout of 2^25 elements or more and batch * heads_q * seqlen_q * 4
- * above 2^31 - 256 bytes (32-bit offsets in the kernels).
+ * opts as for fa_fwd (same scale, causal, window, softcap).  With softcap c the logit is
+ * c tanh(scale q.k / c), so dS is multiplied by 1 - tanh^2(scale q.k / c) before dQ and dK (the
+ * chain rule through the forward's transform, "FA4 ...", section 7); ALiBi is
+ * FA_ERR_UNSUPPORTED, and so are a token stride of q or dout of 2^25 elements or more and
+ * batch * heads_q * seqlen_q * 4 above 2^31 - 256 bytes (32-bit offsets in the kernels).
  * Two kernels on the stream: dQ (per query block; it also forms D and the base-2 LSE of its
  * rows in the workspace), then dK/dV (per key block).  Deterministic: no atomics. */
 int fa_bwd(const fa_attn_opts* opts, const void* q, const void* k, const void* v, const void* out,

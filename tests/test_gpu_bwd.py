@@ -170,3 +170,48 @@ def test_bwd_varlen_equals_dense_on_equal_lengths():
     torch.cuda.synchronize()
     for x, y in zip(dense, packed):
         assert torch.equal(x.reshape(y.shape), y)
+
+
+# ---------------------------------------------------------------- softcap
+SOFTCAP_CASES = [
+    # B, Nq, Nk, Hq, Hkv, d, causal, window, softcap, input scale
+    (2, 200, 200, 4, 4, 128, True, None, 30.0, 2.0),     # the long-context workload's cap on its inputs
+    (1, 333, 333, 4, 2, 128, False, None, 3.0, 2.0),     # a small cap that bends most scores
+    (1, 190, 120, 2, 2, 64, True, None, 5.0, 1.0),       # rows that see no key
+    (1, 300, 300, 2, 2, 128, True, (70, 0), 4.0, 2.0),   # window
+]
+
+
+@pytest.mark.parametrize("B,Nq,Nk,Hq,Hkv,d,causal,window,cap,mult", SOFTCAP_CASES)
+def test_bwd_softcap(B, Nq, Nk, Hq, Hkv, d, causal, window, cap, mult):
+    t = W.dense(451 + Nq + Nk, B, Nq, Hq, Hkv, d, Nk=Nk, mult=mult)
+    do = W.randn_bf16(W.generator(452 + Nq), (B, Nq, Hq, d))
+    q, k, v = (t[n].to(DEV) for n in "qkv")
+    out, lse = api.fa_fwd(q, k, v, causal=causal, window=window, softcap=cap)
+    got = api.fa_bwd(q, k, v, out, lse, do.to(DEV), causal=causal, window=window, softcap=cap)
+    torch.cuda.synchronize()
+    ref = oracle.bwd_dense(bits(t["q"]), bits(t["k"]), bits(t["v"]), bits(do), causal=causal, window=window,
+                           softcap=cap)
+    check_grads(got, ref, f"bwd softcap {cap} {B}x{Nq}x{Nk} h{Hq}/{Hkv} d{d}")
+    if causal and Nq > Nk:
+        assert torch.count_nonzero(got[0][:, : Nq - Nk].float()) == 0
+
+
+def test_bwd_varlen_softcap():
+    lq = [1, 64, 130, 257]
+    g = W.generator(461)
+    cu = W.prefix_sum(torch.tensor(lq))
+    T, Hq, Hkv, d, cap = int(cu[-1]), 8, 2, 128, 4.0
+    q, k, v = W.randn_bf16(g, (T, Hq, d), 2.0), W.randn_bf16(g, (T, Hkv, d), 2.0), W.randn_bf16(g, (T, Hkv, d), 2.0)
+    do = W.randn_bf16(g, (T, Hq, d))
+    cud = cu.to(DEV)
+    out, lse = api.fa_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cud, cud, max(lq), causal=True, softcap=cap)
+    dq, dk, dv = api.fa_bwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), out, lse, do.to(DEV), cud, cud, max(lq), max(lq),
+                                   causal=True, softcap=cap)
+    torch.cuda.synchronize()
+    c = cu.tolist()
+    for s in range(len(lq)):
+        a, b = c[s], c[s + 1]
+        ref = oracle.bwd_dense(bits(q[a:b][None]), bits(k[a:b][None]), bits(v[a:b][None]), bits(do[a:b][None]),
+                               causal=True, softcap=cap)
+        check_grads((dq[a:b], dk[a:b], dv[a:b]), tuple(r[0] for r in ref), f"bwd varlen softcap sequence {s}")

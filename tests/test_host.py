@@ -399,7 +399,7 @@ def test_bwd_rejects_invalid_arguments():
     assert call(Hq=6, Hkv=4) == FA_ERR_INVALID_ARG
     assert call(ws=None) == FA_ERR_INVALID_ARG
     assert call(ws_bytes=16) == FA_ERR_INVALID_ARG
-    assert call(opts=_opts(softcap=30.0)) == FA_ERR_UNSUPPORTED
+    assert call(opts=_opts(softcap=-1.0)) == FA_ERR_INVALID_ARG      # softcap itself is supported
     # the dK/dV kernel addresses a 32-row Q or dO block with 32-bit offsets, and reaches the
     # base-2 LSE array from the D array with one
     far = (ctypes.c_int64 * 3)(1 << 40, 1 << 25, 128)
@@ -515,5 +515,5 @@ def test_bwd_varlen_rejects_invalid_arguments():
     assert call(mq=-1) == FA_ERR_INVALID_ARG
     assert call(Hq=18) == FA_ERR_INVALID_ARG
     assert call(ws_bytes=16) == FA_ERR_INVALID_ARG                    # D and L need 2 x 16 x 400 x 4 bytes
-    assert call(opts=_opts(causal=1, softcap=30.0)) == FA_ERR_UNSUPPORTED
+    assert call(opts=_opts(causal=1, softcap=float("inf"))) == FA_ERR_INVALID_ARG
     assert call(tq=1 << 30) == FA_ERR_UNSUPPORTED                     # rows past the 32-bit D-to-L offset
