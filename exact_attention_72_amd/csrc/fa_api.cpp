@@ -201,7 +201,6 @@ int dense_fwd(const fa_attn_opts* opts, const void* q, const void* k, const void
   p.m_blocks = (int)((rows + FA_BLOCK_M - 1) / FA_BLOCK_M);
   p.total_tiles = (int64_t)p.m_blocks * batch * p.hg_count;
   if (p.total_tiles > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "too many tiles");
-  p.persistent = 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = mod_id != 0 ? fa_launch_prefill_mod(p, head_dim, pack, mod_id, st)
                              : fa_launch_prefill(p, head_dim, false, false, pack, softcap, st);
@@ -302,7 +301,6 @@ int fa_fwd_varlen(const fa_attn_opts* opts, const void* q, const void* k, const 
   // tile as a workgroup finishes, which balances unequal sequences (measured
   // 7 % faster than a persistent grid-stride loop on 32 sequences of 64..8192
   // tokens); indices past the real tile count exit at once
-  p.persistent = 0;
   hipError_t e = fa_launch_prefill(p, head_dim, true, false, pack, softcap, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "varlen launch");
   return FA_OK;
@@ -425,7 +423,6 @@ int fa_fwd_varlen_paged(const fa_attn_opts* opts, const void* q, const void* k_c
   // with the decode-like sequences in the decode kernel this measured 562
   // against 547 TFLOP/s for a persistent grid-stride loop on a batch of 64
   // one-token requests and 4 chunks of 2048 tokens
-  p.persistent = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // sequences of at most FA_PAGED_MAX_ROWS packed rows (decode steps, short
   // chunks) run in the decode kernel, one workgroup per (sequence, KV head) with
@@ -580,7 +577,6 @@ int kvcache_paged(const fa_attn_opts* opts, const void* q, const void* k_cache, 
     p.m_blocks = (int)((rows_seq + FA_BLOCK_M - 1) / FA_BLOCK_M);
     p.total_tiles = (int64_t)p.m_blocks * batch * p.hg_count;
     if (p.total_tiles > 0x7fffffff) return fail(FA_ERR_UNSUPPORTED, "too many tiles");
-    p.persistent = 0;
     hipError_t e = fa_launch_prefill(p, head_dim, false, true, pack, softcap, s);
     if (e != hipSuccess) return hip_fail(e, "paged prefill launch");
     return FA_OK;

@@ -26,8 +26,7 @@ struct FaParams {
   int hg_count;  // tile head axis: heads_kv when GQA heads are packed into rows, else heads_q
   int gp;        // rows per token in a tile: g when packed, else 1
   int m_blocks;  // row blocks per (sequence, head group); for varlen an upper bound
-  int64_t total_tiles;  // dense: exact tile count; varlen: an upper bound
-  int persistent;       // 1: grid-stride loop over tiles; 0: one tile per workgroup
+  int64_t total_tiles;  // dense: exact tile count; varlen: an upper bound (one workgroup per tile)
   // varlen
   const int32_t* cu_q;
   const int32_t* cu_k;

@@ -526,15 +526,8 @@ __device__ __forceinline__ void block_sums(const f32x16& x, float rs, float& l_r
 
 // ------------------------------------------------------------------ tile scheduling
 // Linear tile index -> tile, longest first (row blocks nearer the end of a
-// sequence see more keys under a causal mask, so they go first).  Round r of a
-// persistent workgroup w takes index r * G + w on even rounds and the mirror
-// index within its XCD group on odd rounds, so that the sum of work per
-// workgroup stays level.
-__device__ __forceinline__ int64_t tile_index(int64_t round, int w, int G) {
-  if ((round & 1) == 0) return round * G + w;
-  int mirrored = ((G & 7) == 0) ? (G - 8 - (w & ~7)) + (w & 7) : (G - 1 - w);
-  return round * G + mirrored;
-}
+// sequence see more keys under a causal mask, so they go first); one workgroup
+// per tile index, so the hardware hands out the next tile as a workgroup ends.
 
 struct TileId {
   int b, hg, mb;
@@ -674,7 +667,7 @@ __device__ __forceinline__ bool dense_tile(const FaParams& p, int64_t t64, TileI
   const uint32_t hgc = (uint32_t)p.hg_count;
   const uint32_t pairs = (uint32_t)p.B * hgc;
   uint32_t bh;
-  if (p.wl >= 0 && !p.persistent && (pairs & 7) == 0) {
+  if (p.wl >= 0 && (pairs & 7) == 0) {
     const uint32_t j = t >> 3, mbs = (uint32_t)p.m_blocks;
     const uint32_t q = j / mbs;
     out->mb = (int)(j - q * mbs);
@@ -732,12 +725,11 @@ constexpr int prefill_smem_bytes() {
   return 2 * kPrefillStages * DmaGeom<D, FA_BLOCK_N>::kTensorBytes;
 }
 
-// The prefill work of one workgroup: tile bid of a grid of `grid` workgroups
-// (or, persistent, every grid-th tile from bid), with its K/V stages in smem
+// The prefill work of one workgroup: tile bid, with its K/V stages in smem
 // (prefill_smem_bytes<D>(), 1 KiB aligned).  The kernel below and the unified
 // prefill + decode kernel call it.
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false, class MOD = FaNoMod>
-__device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int bid, int grid) {
+__device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int bid) {
   constexpr bool kMod = MOD::kScore || MOD::kMask;
   static_assert(!(kMod && (SOFTCAP || ALIBI)), "a mod replaces softcap and ALiBi");
   constexpr int BN = FA_BLOCK_N;  // 32 keys per block
@@ -762,15 +754,13 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
   const int k_src = (dma_pc ^ k_swz<D>(dma_row)) * 8;
   const int v_src = (dma_pc ^ v_swz<D>(dma_row)) * 8;
 
-  const int G_ = grid;
-  for (int64_t round = 0;; ++round) {
-    const int64_t t = p.persistent ? tile_index(round, bid, G_) : (round == 0 ? (int64_t)bid : -1);
-    if (t < 0) break;
+  {
+    const int64_t t = bid;
     TileId tile;
     if (VARLEN) {
-      if (!varlen_tile(p, t, lane, &tile)) break;
+      if (!varlen_tile(p, t, lane, &tile)) return;
     } else {
-      if (!dense_tile(p, t, &tile)) break;
+      if (!dense_tile(p, t, &tile)) return;
     }
 
     // ---- sequence view
@@ -861,9 +851,7 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
         // Keys past the last one are clamped to it; a clamped instruction's rows
         // then all lie in the last key's page.
         const int32_t* bt = p.block_table + (int64_t)tile.b * p.max_blocks;
-        // (the unified varlen form keeps the per-lane addresses: measured 6 % faster
-        // there, 2.5 % slower for chunked prefill)
-        if (!VARLEN && n0 + BN <= Lk) {
+        if (n0 + BN <= Lk) {
           // a full block: the instruction's rows are consecutive keys of one page,
           // addressed from the page's row (scalar) plus the lane's row offset
 #pragma unroll
@@ -1199,14 +1187,13 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
         p.lse[(int64_t)tile.b * p.lse_bs + (int64_t)head * p.lse_hs + q_start + tok] = lse;
       }
     }
-    if (!p.persistent) break;
   }
 }
 
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false, class MOD = FaNoMod>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(FaParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[prefill_smem_bytes<D>()];
-  prefill_body<D, VARLEN, PACK, SOFTCAP, PAGED, ALIBI, MOD>(p, smem, blockIdx.x, gridDim.x);
+  prefill_body<D, VARLEN, PACK, SOFTCAP, PAGED, ALIBI, MOD>(p, smem, blockIdx.x);
 }
 
 // ------------------------------------------------------------------ sequence order
@@ -1654,7 +1641,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_unified_kernel(FaParams pd, Fa
   __shared__ __attribute__((aligned(1024))) char smem[kA > kB ? kA : kB];
   const int bid = blockIdx.x;
   if (bid < n_tiles)
-    prefill_body<D, true, PACK, SOFTCAP, true>(pp, smem, bid, n_tiles);
+    prefill_body<D, true, PACK, SOFTCAP, true>(pp, smem, bid);
   else
     paged_body<D, SOFTCAP>(pd, smem, bid - n_tiles);
 }
@@ -2616,31 +2603,12 @@ int device_cus() {
   return cached_cus;
 }
 
-template <typename K>
-int occupancy(K kernel) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess || n <= 0)
-    n = 1;
-  return n;
-}
-
 template <int D, bool VARLEN, bool PACK, bool SOFTCAP, bool PAGED, bool ALIBI = false, class MOD = FaNoMod>
-hipError_t launch_prefill_t(const FaParams& p0, hipStream_t stream) {
-  FaParams p = p0;
+hipError_t launch_prefill_t(const FaParams& p, hipStream_t stream) {
   auto kern = fa_prefill_kernel<D, VARLEN, PACK, SOFTCAP, PAGED, ALIBI, MOD>;
-  int64_t tiles = p.total_tiles;
+  const int64_t tiles = p.total_tiles;
   if (tiles <= 0) return hipSuccess;
-  int64_t grid;
-  if (p.persistent) {
-    static thread_local int occ = 0;
-    if (occ == 0) occ = occupancy(kern);
-    int64_t G = (int64_t)device_cus() * occ;
-    grid = tiles < G ? tiles : G;
-    p.persistent = 1;
-  } else {
-    grid = tiles;
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
