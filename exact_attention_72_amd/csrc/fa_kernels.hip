@@ -2549,24 +2549,28 @@ __global__ __launch_bounds__(2 * kThreads, 1) void fa_bwd_dkdv_kernel(FaBwdParam
   // by the dK waves in iteration t - 1) and the dK waves block t - 1 (P written
   // by the P waves in iteration t - 1, before this iteration's barrier).  Every
   // wave passes the same steps + 1 barriers.
+  // One loop per role (the same steps + 1 barriers in each): a role branch inside
+  // one loop would make the compiler give each role's accumulators their own
+  // registers and copy them at the join on every step.
   if (pwave) {
     for (int j = 0; j < 2 && j < steps; ++j) {
       issue(dw, j);
       advance(dw);
     }
-  }
-  for (int it = 0; it <= steps; ++it) {
-    if (pwave && it < steps) {
-      // block it landed; block it + 1 may still be in flight
-      if (it + 1 < steps)
-        wait_vmcnt<kPer>();
-      else
-        wait_vmcnt<0>();
-    }
-    stage_barrier();
-    if (pwave) {
+    for (int it = 0; it <= steps; ++it) {
+      if (it < steps) {
+        // block it landed; block it + 1 may still be in flight
+        if (it + 1 < steps)
+          wait_vmcnt<kPer>();
+        else
+          wait_vmcnt<0>();
+      }
+      stage_barrier();
       if (it < steps) p_step(it);
-    } else {
+    }
+  } else {
+    for (int it = 0; it <= steps; ++it) {
+      stage_barrier();
       if (it > 0) k_step(it - 1);
     }
   }
