@@ -1076,14 +1076,20 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
       __builtin_amdgcn_s_setprio(1);
       f32x16 s_next = qk_mma<D>(ka, qreg);
       read_v<D, kV + 16 * (2 * D)>(0u, off, lo1, hi1);
-      // Softcapped scores of an unmasked block whose rows all have a reference
-      // are transformed inside the product loop below, beside the exponentials;
-      // otherwise (mask, or a row's first visible block) before it.
+      // Softcapped scores are transformed inside the product loop below, beside
+      // the exponentials, on every block; a cut block's mask then zeroes the
+      // exponentials of its hidden keys after that loop.  (As a per-block choice
+      // between this and transforming before the loop, the compiler formed the
+      // transform on both paths and selected, one select per score; as two
+      // copies of the loop, it spilled.)
       const bool masked = is_masked(i + 1);
       const bool first = !all_ref;
-      const bool late = SOFTCAP && !masked && !first;
-      if (!late) {
-        transform(s_next);
+      if constexpr (SOFTCAP) {
+        // The compiler left 11 wait states between the S product and the
+        // transform's first read on one path out of the loop: wait for the
+        // product here, before both paths.
+        asm volatile("s_nop 7\n\ts_nop 3" : "+v"(s_next));
+      } else {
         apply_mod(s_next, i + 1);
         if (masked)
           apply_mask(s_next, i + 1);
@@ -1102,6 +1108,10 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
         // the fence keeps the block maximum inside this rarely taken branch
         f32x16 sv = s_next;
         asm volatile("" : "+v"(sv));
+        if constexpr (SOFTCAP) {
+          transform(sv);
+          if (masked) apply_mask(sv, i + 1);
+        }
         moved = move_reference(block_max(sv), m_run, c, alpha);
         nmc_run = neg_ref(m_run, c);
         all_ref = !__any(m_run == kNegInf);
@@ -1110,7 +1120,7 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
       // P V of block i, each product followed by the exponentials of block i + 1
       constexpr int kPer = 16 / (2 * (D / 32));  // exponentials per product
       auto expo = [&](int a) {
-        if (late) s_next[a] = softcap_log2(s_next[a], p.cap_in, p.cap_out);
+        if constexpr (SOFTCAP) s_next[a] = softcap_log2(s_next[a], p.cap_in, p.cap_out);
         xs[a] = exp2_asm(__builtin_fmaf(s_next[a], c, nmc));
       };
       lgkm_wait<2 * (D / 32)>(lo0, hi0);
@@ -1128,7 +1138,15 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
         for (int e = 0; e < kPer; ++e) expo(8 + db * kPer + e);
       }
       __builtin_amdgcn_s_setprio(0);
-      sc = s_next;  // the late softcap path transformed it in place
+      if constexpr (SOFTCAP) {
+        if (masked) {
+          // a capped logit is at least -cap, so -inf marks exactly the hidden keys
+          apply_mask(s_next, i + 1);
+#pragma unroll
+          for (int a = 0; a < 16; ++a) xs[a] = s_next[a] == kNegInf ? 0.0f : xs[a];
+        }
+      }
+      sc = s_next;  // transformed in place (softcap)
       if (moved) {
         mfma_drain(o);
         l_run *= alpha;
