@@ -995,7 +995,12 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
     // moves the reference, rescales what was accumulated and redoes the
     // exponentials.  The per-lane sums of a block stay far below 2^8 when the
     // reference is current, so the branch is rarely taken.
+    // With softcap sc holds r = 1 / (exp(2 y) + 1) instead (+inf for a hidden
+    // key), from which the capped logit is cap_out - 2 cap_out r and the
+    // exponential exp2(logit - m) one multiply-add.
     f32x16 sc = {};
+    const float cap_k = p.cap_in * (2.0f * kLog2e), cap_m2 = -2.0f * p.cap_out;
+    auto softcap_r = [&](float x) { return rcp_fast(exp2_fast(x * cap_k) + 1.0f); };
     // -m c of the current reference (0 while a row has seen no visible key),
     // recomputed only where the reference moves; all_ref: every row of the wave
     // has a reference (once true it stays true: a reference only moves up)
@@ -1005,15 +1010,25 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
       float rs = lane_sum16(xs);
       if (__any(!(rs <= kRescaleMax))) {
         float a2;
-        if (move_reference(block_max(sc), m_run, c, a2)) {
+        f32x16 lg = sc;
+        if constexpr (SOFTCAP) {
+#pragma unroll
+          for (int a = 0; a < 16; ++a) lg[a] = __builtin_fmaf(cap_m2, sc[a], p.cap_out);
+        }
+        if (move_reference(block_max(lg), m_run, c, a2)) {
           mfma_drain(o);
           l_run *= a2;
           l_bf *= a2;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) o[db] *= a2;
           nmc_run = neg_ref(m_run, c);
+          if constexpr (SOFTCAP) {
 #pragma unroll
-          for (int a = 0; a < 16; ++a) xs[a] = exp2_fast(__builtin_fmaf(sc[a], c, nmc_run));
+            for (int a = 0; a < 16; ++a) xs[a] = exp2_fast(__builtin_fmaf(cap_m2, sc[a], p.cap_out + nmc_run));
+          } else {
+#pragma unroll
+            for (int a = 0; a < 16; ++a) xs[a] = exp2_fast(__builtin_fmaf(sc[a], c, nmc_run));
+          }
           rs = lane_sum16(xs);
         }
       }
@@ -1029,7 +1044,14 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
       wait_vmcnt_blocks<kDmaPerBlock>(min(NBUF - 2, nb - 1));
       stage_barrier();
       f32x16 s0 = qk_block<D, 0>(0u, qreg, off);
-      transform(s0);
+      f32x16 r0 = {};
+      if constexpr (SOFTCAP) {
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          r0[a] = softcap_r(s0[a]);
+          s0[a] = __builtin_fmaf(cap_m2, r0[a], p.cap_out);
+        }
+      }
       apply_mod(s0, 0);
       if (is_masked(0))
         apply_mask(s0, 0);
@@ -1040,7 +1062,12 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
       nmc_run = neg_ref(m_run, c);
       all_ref = !__any(m_run == kNegInf);
       exps(s0, nmc_run, 0, 16);
-      sc = s0;
+      if constexpr (SOFTCAP) {
+#pragma unroll
+        for (int a = 0; a < 16; ++a) sc[a] = s0[a] == kNegInf ? __builtin_inff() : r0[a];
+      } else {
+        sc = s0;
+      }
     }
 
     // Pipeline step for block i (stage B = i % NBUF) when block i + 1 exists.
@@ -1117,11 +1144,16 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
         all_ref = !__any(m_run == kNegInf);
       }
       const float nmc = nmc_run;
+      const float cap_nmc = p.cap_out + nmc;
       // P V of block i, each product followed by the exponentials of block i + 1
       constexpr int kPer = 16 / (2 * (D / 32));  // exponentials per product
       auto expo = [&](int a) {
-        if constexpr (SOFTCAP) s_next[a] = softcap_log2(s_next[a], p.cap_in, p.cap_out);
-        xs[a] = exp2_asm(__builtin_fmaf(s_next[a], c, nmc));
+        if constexpr (SOFTCAP) {
+          s_next[a] = softcap_r(s_next[a]);
+          xs[a] = exp2_asm(__builtin_fmaf(cap_m2, s_next[a], cap_nmc));
+        } else {
+          xs[a] = exp2_asm(__builtin_fmaf(s_next[a], c, nmc));
+        }
       };
       lgkm_wait<2 * (D / 32)>(lo0, hi0);
 #pragma unroll
@@ -1140,13 +1172,17 @@ __device__ __forceinline__ void prefill_body(const FaParams& p, char* smem, int 
       __builtin_amdgcn_s_setprio(0);
       if constexpr (SOFTCAP) {
         if (masked) {
-          // a capped logit is at least -cap, so -inf marks exactly the hidden keys
+          // r lies in [0, 1], so -inf marks exactly the hidden keys
           apply_mask(s_next, i + 1);
 #pragma unroll
-          for (int a = 0; a < 16; ++a) xs[a] = s_next[a] == kNegInf ? 0.0f : xs[a];
+          for (int a = 0; a < 16; ++a) {
+            const bool hidden = s_next[a] == kNegInf;
+            xs[a] = hidden ? 0.0f : xs[a];
+            s_next[a] = hidden ? __builtin_inff() : s_next[a];
+          }
         }
       }
-      sc = s_next;  // transformed in place (softcap)
+      sc = s_next;  // r in place (softcap)
       if (moved) {
         mfma_drain(o);
         l_run *= alpha;
