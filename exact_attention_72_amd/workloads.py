@@ -24,8 +24,10 @@ KV ("Attention kernels: FlashAttention and PagedAttention", sections 6.1 and
 from __future__ import annotations
 
 import itertools
+import math
 
 import numpy as np
+
 import torch
 
 # The five workloads, by name.  Sizes are those of the problem statement.
@@ -82,6 +84,19 @@ def dense(seed, B, N, Hq, Hkv, d, *, Nk=None, mult=1.0, device="cpu"):
     k = randn_bf16(g, (B, Nk, Hkv, d), mult, device)
     v = randn_bf16(g, (B, Nk, Hkv, d), mult, device)
     return dict(q=q, k=k, v=v)
+
+
+def rising_logits(seed, B, Nq, Nk, H, d, *, top=22.0, device="cpu"):
+    """q, k, v [B, N, H, d] bf16 whose logits rise along the key axis: q rows are
+    20 e plus noise and k row j is a_j e plus noise, e the unit vector of equal
+    entries and a_j running linearly from -top to top, so q . k_j is about 20 a_j."""
+    g = generator(seed, device)
+    e = torch.full((d,), 1.0 / math.sqrt(d), device=device)
+    a = torch.linspace(-top, top, Nk, device=device)
+    q = 20.0 * e + 0.05 * torch.randn((B, Nq, H, d), generator=g, device=device)
+    k = a[None, :, None, None] * e + 0.05 * torch.randn((B, Nk, H, d), generator=g, device=device)
+    v = torch.randn((B, Nk, H, d), generator=g, device=device)
+    return dict(q=q.to(torch.bfloat16), k=k.to(torch.bfloat16), v=v.to(torch.bfloat16))
 
 
 def lengths_uniform(seed, n, lo, hi) -> torch.Tensor:

@@ -66,6 +66,20 @@ def test_dense_small(B, Nq, Nk, Hq, Hkv, d, causal, window, softcap, mult, pack)
     check_close(out, lse, o_ref, l_ref, f"dense {B}x{Nq}x{Nk} h{Hq}/{Hkv} d{d}")
 
 
+@pytest.mark.parametrize("softcap,window,causal", [
+    (0.0, None, False), (30.0, None, False), (0.0, (300, 0), True), (30.0, (300, 0), True)])
+def test_rising_logits_move_the_reference(softcap, window, causal):
+    """Logits that rise along the key axis (up to ~40 apart in natural units, or capped at
+    +-30): a few key blocks after each reference is set the exponentials outgrow it, so the
+    kernel's reference moves, O and the row sums are rescaled and the exponentials redone,
+    on unmasked blocks, on the window's cut blocks and on the ragged last block (700 keys)."""
+    t = W.rising_logits(31, 1, 200, 700, 2, 128)
+    kw = dict(causal=causal, window=window, softcap=softcap)
+    out, lse = run(t, **kw)
+    o_ref, l_ref = ref(t, **kw)
+    check_close(out, lse, o_ref, l_ref, f"rising logits softcap {softcap} window {window}")
+
+
 def test_custom_scale_and_strided_inputs():
     t = W.dense(99, 2, 150, 4, 2, 128)
     big = {n: torch.zeros(2, 150, 6, 128, dtype=torch.bfloat16) for n in "kv"}
