@@ -1314,11 +1314,14 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x2 c) {
 // score scale by the host and the V scale multiplies O here.
 template <int D, bool SOFTCAP, bool FP8 = false>
 __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int unit) {
-  constexpr int NK = FA_PAGED_STAGE;
+  // keys per stage: four waves of 16 (bf16), or of 32 (FP8, each wave in an LDS
+  // buffer of its own)
+  constexpr int NK = FP8 ? 2 * FA_PAGED_STAGE : FA_PAGED_STAGE;
   constexpr int NS = kPagedStages;
-  using G = DmaGeom<D, NK>;
+  using G = DmaGeom<D, FA_PAGED_STAGE>;  // the bf16 stage
   constexpr int kStage = 2 * G::kTensorBytes;
-  static_assert(NK == 4 * 16, "four waves of 16 keys per stage");
+  static_assert(FA_PAGED_STAGE == 4 * 16, "four waves of 16 keys per bf16 stage");
+  static_assert(!FP8 || 4 * 2 * (NK / 4) * 2 * D <= NS * kStage, "FP8 wave buffers fit the stages' LDS");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1327,10 +1330,11 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   const int kg = lane >> 5;
   const float c = SOFTCAP ? 1.0f : p.scale_log2;
 
-  // a wave's S^T operand covers 16 keys: lanes 16..31 repeat rows 0..15, and
-  // the repeated rows (accumulator slots 8..15) are dropped below
+  // bf16: a wave's S^T operand covers 16 keys: lanes 16..31 repeat rows 0..15,
+  // and the repeated rows (accumulator slots 8..15) are dropped below.  FP8: 32
+  // keys, all slots live.
   LaneOffsets<D> off;
-  off.init(lane, lds_addr(smem), lds_addr(smem), 16);
+  off.init(lane, lds_addr(smem), lds_addr(smem), FP8 ? 32 : 16);
   // Each wave loads the 16 rows it computes on (rows 16 wave .. 16 wave + 15 of a
   // stage; instruction i fills G::kRowsPerKiB of them), so a wave waits only for
   // its own loads and the stages need no workgroup barrier.  The layout and the
@@ -1345,9 +1349,11 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
     v_src[i] = (dma_pc ^ v_swz<D>(dma_row + i * G::kRowsPerKiB)) * 8;
   }
   // FP8: a lane loads 16 codes, two adjacent 8-element chunks of a row (the even
-  // logical chunk E and E + 1), and writes them widened as two 16-byte LDS chunks.
-  // LDS chunk c of row r holds logical chunk c ^ swz(r), so E = 2 pp ^ (swz & ~1)
-  // fills LDS chunk 2 pp ^ (swz & 1) and E + 1 the other chunk of the pair.
+  // logical chunk E and E + 1), and writes them widened as two 16-byte LDS chunks
+  // into the wave's own buffer (its 32 K rows, then its 32 V rows, in the bf16
+  // row layout).  LDS chunk c of buffer row r holds logical chunk c ^ swz(r), so
+  // E = 2 pp ^ (swz & ~1) fills LDS chunk 2 pp ^ (swz & 1) and E + 1 the other
+  // chunk of the pair.
   constexpr int kPairs = D / 16;                     // chunk pairs per row
   constexpr int kRows8 = 64 / kPairs;                // rows per load instruction
   constexpr int kInst8 = FP8 ? kWaveRows / kRows8 : 1;
@@ -1355,11 +1361,10 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   if constexpr (FP8) {
 #pragma unroll
     for (int i = 0; i < kInst8; ++i) {
-      const int rw = i * kRows8 + lane / kPairs;     // row among the wave's 16
-      const int r = kWaveRows * wave + rw;           // row of the stage
+      const int rw = i * kRows8 + lane / kPairs;     // row among the wave's 32
       const int c2 = 2 * (lane % kPairs);
-      const int sk = k_swz<D>(r), sv = v_swz<D>(r);
-      r8[i] = r;
+      const int sk = k_swz<D>(rw), sv = v_swz<D>(rw);
+      r8[i] = rw;
       k_src8[i] = (c2 ^ (sk & ~1)) * 8;
       v_src8[i] = (c2 ^ (sv & ~1)) * 8;
       k_lds8[i] = rw * (2 * D) + (c2 ^ (sk & 1)) * 16;
@@ -1435,7 +1440,8 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   const char* kpool = reinterpret_cast<const char*>(p.k) + (int64_t)kvh * p.k_hs * kEs;
   const char* vpool = reinterpret_cast<const char*>(p.v) + (int64_t)kvh * p.v_hs * kEs;
   const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks;
-  const bool page_aligned = (p.page % NK) == 0;
+  // a stage (bf16) or a wave's 32 rows of one (FP8) lies in one page
+  const bool page_aligned = (p.page % (FP8 ? NK / 4 : NK)) == 0;
   // rows past the last key read the last key (finite data the mask drops)
   const int last = kend > 0 ? kend - 1 : 0;
   const int64_t phys_last = (page_aligned && nst > 0)
@@ -1448,8 +1454,11 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   // stage i + 1 are in flight while stage i is computed.
   u32x4 kr[FP8 ? kInst8 : G::kInstPerWave], vr[FP8 ? kInst8 : G::kInstPerWave];
   auto load8 = [&](int n0, u32x4 (&kr)[FP8 ? kInst8 : G::kInstPerWave], u32x4 (&vr)[FP8 ? kInst8 : G::kInstPerWave]) {
+    n0 += kWaveRows * wave;  // this wave's first key
     if (page_aligned) {
-      const int64_t phys = scalar_load_i32(bt + __builtin_amdgcn_readfirstlane(n0 / p.page));
+      // a wave whose rows all lie past the last key reads the last key's page
+      // entry (its rows are clamped to that key), never an entry past the table
+      const int64_t phys = scalar_load_i32(bt + __builtin_amdgcn_readfirstlane(min(n0, last) / p.page));
       const int slot0 = n0 % p.page;
 #pragma unroll
       for (int i = 0; i < kInst8; ++i) {
@@ -1509,22 +1518,27 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
       }
     }
   };
-  auto store8 = [&](int buf, const u32x4 (&kr)[FP8 ? kInst8 : G::kInstPerWave],
+  // the wave's buffer: its K rows, then its V rows
+  constexpr int kWaveBuf = 2 * kWaveRows * (2 * D);
+  constexpr int kWaveV = kWaveRows * (2 * D);
+  auto store8 = [&](const u32x4 (&kr)[FP8 ? kInst8 : G::kInstPerWave],
                     const u32x4 (&vr)[FP8 ? kInst8 : G::kInstPerWave]) {
-    char* wb = smem + buf * kStage + wave * (kWaveRows * 2 * D);
+    // the previous stage's operand reads (inline assembly) stay above these
+    // stores into the same buffer; LDS operations of one wave complete in order
+    asm volatile("" ::: "memory");
+    char* wb = smem + wave * kWaveBuf;
 #pragma unroll
     for (int i = 0; i < kInst8; ++i) {
       *reinterpret_cast<u32x4*>(wb + k_lds8[i]) = e4m3x8_to_bf16(u32x2{kr[i][0], kr[i][1]});
       *reinterpret_cast<u32x4*>(wb + (k_lds8[i] ^ 16)) = e4m3x8_to_bf16(u32x2{kr[i][2], kr[i][3]});
-      *reinterpret_cast<u32x4*>(wb + G::kTensorBytes + v_lds8[i]) = e4m3x8_to_bf16(u32x2{vr[i][0], vr[i][1]});
-      *reinterpret_cast<u32x4*>(wb + G::kTensorBytes + (v_lds8[i] ^ 16)) =
-          e4m3x8_to_bf16(u32x2{vr[i][2], vr[i][3]});
+      *reinterpret_cast<u32x4*>(wb + kWaveV + v_lds8[i]) = e4m3x8_to_bf16(u32x2{vr[i][0], vr[i][1]});
+      *reinterpret_cast<u32x4*>(wb + kWaveV + (v_lds8[i] ^ 16)) = e4m3x8_to_bf16(u32x2{vr[i][2], vr[i][3]});
     }
     asm volatile("" ::: "memory");
   };
   auto store = [&](int buf) {
     if constexpr (FP8) {
-      store8(buf, kr, vr);
+      store8(kr, vr);
     } else {
       char* dst = smem + buf * kStage + wave * (kWaveRows * 2 * D) + lane * 16;
 #pragma unroll
@@ -1546,6 +1560,24 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
   // the products, mask and online softmax of stage i (from LDS buffer buf)
   auto compute = [&](int i, int buf) {
     const int n0 = st_first + i * NK;
+    if constexpr (FP8) {
+      // this wave's 32 keys, rows 0..31 of its buffer
+      const uint32_t delta = wave * kWaveBuf;
+      f32x16 s = qk_block<D, 0>(delta, qreg, off);
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int key = n0 + kWaveRows * wave + 8 * (a >> 2) + 4 * kg + (a & 3);
+        float x = s[a];
+        if (alibi) x = __builtin_fmaf(-alibi_k, (float)abs(mask.pos - key), x);
+        if (SOFTCAP) x = softcap_log2(x, p.cap_in, p.cap_out);
+        s[a] = mask.visible(key) ? x : kNegInf;
+      }
+      bf16x8 p0, p1;
+      online_softmax<D>(s, m_run, l_run, l_bf, o, c, p0, p1);
+      pv_chunk<D, kWaveV>(delta, p0, o, off);
+      pv_chunk<D, kWaveV + 16 * (2 * D)>(delta, p1, o, off);
+      return;
+    }
     // this wave's 16 keys: rows 16 wave .. 16 wave + 15 of the stage buffer
     const uint32_t delta = buf * kStage + wave * 16 * (2 * D);
     f32x16 s = qk_block<D, 0>(delta, qreg, off);
@@ -1568,20 +1600,14 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
     pv_chunk<D, G::kTensorBytes>(delta, p0, o, off);
   };
   if constexpr (FP8) {
-    // An FP8 stage is half the bytes of a bf16 one: the loads run two stages ahead
-    // (register sets A and B in turn) so that as many bytes are in flight.
-    u32x4 kb[kInst8], vb[kInst8];
+    // An FP8 stage of 32 keys a wave is the bytes of a bf16 stage of 16: the
+    // loads of stage i + 1 are in flight while stage i is computed, and each
+    // wave stores into and reads from its own buffer only (no barrier).
     if (nst > 0) load8(st_first, kr, vr);
-    if (nst > 1) load8(st_first + NK, kb, vb);
-    for (int i = 0; i < nst; i += 2) {
-      store8(0, kr, vr);
-      if (i + 2 < nst) load8(st_first + (i + 2) * NK, kr, vr);
+    for (int i = 0; i < nst; ++i) {
+      store8(kr, vr);
+      if (i + 1 < nst) load8(st_first + (i + 1) * NK, kr, vr);
       compute(i, 0);
-      if (i + 1 < nst) {
-        store8(1, kb, vb);
-        if (i + 3 < nst) load8(st_first + (i + 3) * NK, kb, vb);
-        compute(i + 1, 1);
-      }
     }
   } else {
     if (nst > 0) load(st_first);
