@@ -1282,7 +1282,9 @@ __global__ __launch_bounds__(kThreads) void fa_seq_order_kernel(const int32_t* l
 // two workgroups share a CU (the 64 KiB of LDS the merge needs sets that).  When
 // the page size is a multiple of the stage, a stage lies in one page and its
 // physical page is one scalar block-table read; otherwise every row looks its
-// page up.
+// page up.  Over an FP8 cache a stage is 128 keys, 32 per wave in an LDS buffer
+// of the wave's own (the bytes per wave of a bf16 stage, and no key row of the
+// products repeated).
 constexpr int kPagedStages = 2;  // stages in the paged kernel's ring
 // LDS of the paged decode workgroup: the stage ring, reused after the loop for
 // the merge of the four waves' states: O [4][32][D] fp32, then m, l and l (bf16
