@@ -38,6 +38,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kFp8Max = 448.0f;
 constexpr float kPShift = 8.0f;  // log2 of the factor probabilities carry into the P V product
+// Largest lead (log2 units) of a score over the row reference left without a
+// move: 2^(kPShift + kLazy) = 430 stays inside e4m3's 448.
+constexpr float kLazy = 0.75f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
@@ -503,23 +506,45 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
           sv[hb][a] = vis ? sv[hb][a] : kNegInf;
         }
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int a = 0; a < 16; ++a) mx = fmaxf(mx, fmaxf(sv[0][a], sv[1][a]));
-    mx = pair_max(mx) * cb;
-    const float m_new = fmaxf(m_run, mx);
-    const float nmc = (m_new == kNegInf) ? 0.0f : kPShift - m_new;
+    // Exponent arguments relative to the current reference first (multiply-adds,
+    // whose results the block maximum then takes without canonicalising each
+    // score), the reference moved only when the block's maximum exceeds it by
+    // more than kLazy: then 2^8 p stays below 2^(8 + kLazy) < 448 without a move,
+    // and a move (which rescales O) is rare once a row has seen a few blocks.
+    const float nmc_old = (m_run == kNegInf) ? 0.0f : kPShift - m_run;
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
-      x0[a] = exp2_fast(__builtin_fmaf(sv[0][a], cb, nmc));
-      x1[a] = exp2_fast(__builtin_fmaf(sv[1][a], cb, nmc));
+      x0[a] = __builtin_fmaf(sv[0][a], cb, nmc_old);
+      x1[a] = __builtin_fmaf(sv[1][a], cb, nmc_old);
     }
-    if (__any(m_new > m_run)) {
-      const float alpha = (m_new > m_run) ? exp2_fast(m_run - m_new) : 1.0f;
+    float ym = fmaxf(fmaxf(x0[0], x0[1]), x1[0]);
+    ym = fmaxf(ym, x1[1]);
+#pragma unroll
+    for (int a = 2; a < 16; ++a) ym = fmaxf(fmaxf(ym, x0[a]), x1[a]);
+    ym = pair_max(ym);
+    // the block maximum in log2 units is ym + m_run - kPShift (ym while the row has
+    // no reference); -inf - (-inf) is NaN, which compares false: no move while
+    // nothing is visible
+    const float mx = (m_run == kNegInf) ? ym : ym - nmc_old;
+    const bool mv = mx - m_run > kLazy;
+    if (__any(mv)) {
+      const float m_new = mv ? mx : m_run;
+      const float alpha = mv ? exp2_fast(m_run - m_new) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
       m_run = m_new;
+      const float nmc = (m_run == kNegInf) ? 0.0f : kPShift - m_run;
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        x0[a] = __builtin_fmaf(sv[0][a], cb, nmc);
+        x1[a] = __builtin_fmaf(sv[1][a], cb, nmc);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      x0[a] = exp2_fast(x0[a]);
+      x1[a] = exp2_fast(x1[a]);
     }
   };
 
