@@ -97,17 +97,8 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// LDS reads as inline assembly (the compiler would otherwise wait for every
-// LDS-DMA load in flight before them), waited for explicitly.
-__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
-__device__ __forceinline__ void lgkm_wait0(u32x4 (&a)[8]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]));
-}
+// LDS reads go out as inline assembly (the compiler would otherwise wait for
+// every LDS-DMA load in flight before them), each statement with its own wait.
 __device__ __forceinline__ i32x8 join(u32x4 a, u32x4 b) {
   return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
@@ -448,23 +439,25 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
   const uint32_t base = lds_addr(smem);
   const uint32_t ka = base + col * D, ksw = (col >> 1) & 7;
   const uint32_t va = base + KT + col * BN, vsw = (col >> 2) & 3;
-  auto read_k = [&](int i, u32x4 (&kr)[8]) __attribute__((always_inline)) {
+  // The operand reads go out as one asm statement with the wait for them (and
+  // for the block's K scale, loaded in the same statement), so that the
+  // compiler sees the results defined only once they have landed: with reads
+  // and wait in separate statements it copied read results into the 8-register
+  // operand tuples before the wait.  kr[4 hb + 2 c + e]: K row 32 hb + col,
+  // chunk 4 c + 2 kg + e (hb is an immediate offset of 32 rows); vr[2 db + e]:
+  // V^T row 32 db + col, chunk 2 kg + e (db an immediate offset of 32 rows).
+  static_assert(D == 128 && 32 * D == 4096 && 32 * BN == 2048, "the immediate offsets below");
+  auto k_addrs = [&](int i, uint32_t (&a)[4]) __attribute__((always_inline)) {
     const uint32_t so = (uint32_t)((i % NBUF) * STAGE);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c)
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-          kr[4 * hb + 2 * c + e] = ds_read_b128(ka + so + hb * 32 * D + 16 * ((4 * c + 2 * kg + e) ^ ksw));
+      for (int e = 0; e < 2; ++e) a[2 * c + e] = ka + so + 16 * ((4 * c + 2 * kg + e) ^ ksw);
   };
-  // V^T reads of d-blocks [DB0, DB0 + NDB) of block i
-  auto read_v = [&](int i, u32x4 (&vr)[8], int db0, int ndb) __attribute__((always_inline)) {
+  auto v_addrs = [&](int i, uint32_t (&a)[2]) __attribute__((always_inline)) {
     const uint32_t so = (uint32_t)((i % NBUF) * STAGE);
 #pragma unroll
-    for (int db = db0; db < db0 + ndb; ++db)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) vr[2 * db + e] = ds_read_b128(va + so + db * 32 * BN + 16 * ((2 * kg + e) ^ vsw));
+    for (int e = 0; e < 2; ++e) a[e] = va + so + 16 * ((2 * kg + e) ^ vsw);
   };
   auto s_mfma = [&](const u32x4 (&kr)[8], f32x16 (&sv)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -475,15 +468,63 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
         sv[hb] = mfma_fp8(join(kr[4 * hb + 2 * c], kr[4 * hb + 2 * c + 1]), qreg[c], sv[hb]);
     }
   };
-  // wave-uniform scalar load of block n's K scale, waited for by the next lgkm wait
-  auto load_kscale = [&](int n) __attribute__((always_inline)) {
+  // block n's K scale address, wave-uniform (for a scalar load)
+  auto kscale_ptr = [&](int n) __attribute__((always_inline)) {
     const uint64_t a = reinterpret_cast<uint64_t>(kscale + n);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const float* u = reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo);
-    float v;
-    asm volatile("s_load_dword %0, %1, 0x0" : "=s"(v) : "s"(u) : "memory");
-    return v;
+    return reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo);
+  };
+  // K of block ik with its scale, and V^T of block iv: reads and wait in one statement
+  auto read_kv = [&](int ik, int iv, u32x4 (&kr)[8], u32x4 (&vr)[8], float& ks) __attribute__((always_inline)) {
+    uint32_t a[4], b2[2];
+    k_addrs(ik, a);
+    v_addrs(iv, b2);
+    asm volatile(
+        "s_load_dword %16, %23, 0x0\n\t"
+        "ds_read_b128 %0, %17\n\tds_read_b128 %1, %18\n\tds_read_b128 %2, %19\n\tds_read_b128 %3, %20\n\t"
+        "ds_read_b128 %4, %17 offset:4096\n\tds_read_b128 %5, %18 offset:4096\n\t"
+        "ds_read_b128 %6, %19 offset:4096\n\tds_read_b128 %7, %20 offset:4096\n\t"
+        "ds_read_b128 %8, %21\n\tds_read_b128 %9, %22\n\t"
+        "ds_read_b128 %10, %21 offset:2048\n\tds_read_b128 %11, %22 offset:2048\n\t"
+        "ds_read_b128 %12, %21 offset:4096\n\tds_read_b128 %13, %22 offset:4096\n\t"
+        "ds_read_b128 %14, %21 offset:6144\n\tds_read_b128 %15, %22 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
+          "=&v"(kr[7]), "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]),
+          "=&v"(vr[6]), "=&v"(vr[7]), "=&s"(ks)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b2[0]), "v"(b2[1]), "s"(kscale_ptr(n_lo + ik))
+        : "memory");
+  };
+  // K of block ik with its scale only (the first block)
+  auto read_k = [&](int ik, u32x4 (&kr)[8], float& ks) __attribute__((always_inline)) {
+    uint32_t a[4];
+    k_addrs(ik, a);
+    asm volatile(
+        "s_load_dword %8, %13, 0x0\n\t"
+        "ds_read_b128 %0, %9\n\tds_read_b128 %1, %10\n\tds_read_b128 %2, %11\n\tds_read_b128 %3, %12\n\t"
+        "ds_read_b128 %4, %9 offset:4096\n\tds_read_b128 %5, %10 offset:4096\n\t"
+        "ds_read_b128 %6, %11 offset:4096\n\tds_read_b128 %7, %12 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(kr[4]), "=&v"(kr[5]), "=&v"(kr[6]),
+          "=&v"(kr[7]), "=&s"(ks)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "s"(kscale_ptr(n_lo + ik))
+        : "memory");
+  };
+  // V^T of block iv only (the last block)
+  auto read_v = [&](int iv, u32x4 (&vr)[8]) __attribute__((always_inline)) {
+    uint32_t b2[2];
+    v_addrs(iv, b2);
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %9 offset:2048\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %9 offset:4096\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %9 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
+          "=&v"(vr[7])
+        : "v"(b2[0]), "v"(b2[1])
+        : "memory");
   };
 
   f32x16 o[D / 32];
@@ -562,12 +603,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
     for (int j = 0; j < NBUF - 1 && j < nb; ++j) issue(j);
     wait_block(min(nb - 1, NBUF - 2));  // block 0; blocks 1 .. NBUF - 2 may be in flight
     stage_barrier();
-    float ks = load_kscale(n_lo);
+    float ks;
     u32x4 kr[8];
-    read_k(0, kr);
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(kr[0]), "+v"(kr[1]), "+v"(kr[2]), "+v"(kr[3]), "+v"(kr[4]), "+v"(kr[5]), "+v"(kr[6]),
-                   "+v"(kr[7]), "+s"(ks));
+    read_k(0, kr, ks);
     f32x16 sv[2];
     s_mfma(kr, sv);
     softmax(sv, 0, cq * ks);
@@ -580,13 +618,6 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
       stage_barrier();  // everyone is done with block i - 1's stage
       if (i + NBUF - 1 < nb) issue(i + NBUF - 1);
     }
-    u32x4 kr[8], vr[8];
-    float ks = 1.0f;
-    if (more) {
-      ks = load_kscale(n_lo + i + 1);
-      read_k(i + 1, kr);
-    }
-    read_v(i, vr, 0, D / 64);
     // block i's probabilities as the B operand (bytes 16 hb + slot of this lane's 32)
     float rs = 0.0f;
 #pragma unroll
@@ -598,22 +629,16 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
       pb[w] = (int)pack4(x0[4 * w], x0[4 * w + 1], x0[4 * w + 2], x0[4 * w + 3]);
       pb[4 + w] = (int)pack4(x1[4 * w], x1[4 * w + 1], x1[4 * w + 2], x1[4 * w + 3]);
     }
-    // LDS reads complete in issue order: with the first half of the V reads (D / 32
-    // of them) still in flight the K reads are done at lgkmcnt(D / 32) (the scalar
-    // load of the scale, if still in flight, only makes the wait longer; the final
-    // wait covers it).  At most 13 reads are outstanding.
+    // block i + 1's K (and scale) and block i's V^T, landed when the statement ends
+    u32x4 kr[8], vr[8];
+    float ks = 1.0f;
     f32x16 sv[2];
     if (more) {
-      asm volatile("s_waitcnt lgkmcnt(%8)"
-                   : "+v"(kr[0]), "+v"(kr[1]), "+v"(kr[2]), "+v"(kr[3]), "+v"(kr[4]), "+v"(kr[5]), "+v"(kr[6]),
-                     "+v"(kr[7])
-                   : "i"(D / 32));
+      read_kv(i + 1, i, kr, vr, ks);
       s_mfma(kr, sv);
+    } else {
+      read_v(i, vr);
     }
-    read_v(i, vr, D / 64, D / 64);
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]), "+v"(vr[6]),
-                   "+v"(vr[7]), "+s"(ks));
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = mfma_fp8(join(vr[2 * db], vr[2 * db + 1]), pb, o[db]);
     if (more) softmax(sv, i + 1, cq * ks);

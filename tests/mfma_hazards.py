@@ -33,18 +33,41 @@ def tools_available():
         shutil.which("objcopy") is not None
 
 
-def disassemble(so_path, arch="gfx950"):
-    """Disassembly text of the library's device code object."""
-    with tempfile.TemporaryDirectory() as tmp:
-        fat = os.path.join(tmp, "fatbin")
-        co = os.path.join(tmp, "code.o")
-        subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", so_path, fat], check=True)
+def code_objects(so_path, tmp, arch="gfx950"):
+    """Paths of the library's gfx950 code objects, one per compiled source: the
+    .hip_fatbin section holds one offload bundle per translation unit, each
+    starting with the bundle magic."""
+    fat = os.path.join(tmp, "fatbin")
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", so_path, fat], check=True)
+    data = open(fat, "rb").read()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = []
+    i = data.find(magic)
+    while i >= 0:
+        starts.append(i)
+        i = data.find(magic, i + 1)
+    out = []
+    for n, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
+        part = os.path.join(tmp, f"bundle{n}")
+        with open(part, "wb") as f:
+            f.write(data[a:b])
+        co = os.path.join(tmp, f"code{n}.o")
         subprocess.run([os.path.join(ROCM_LLVM, "clang-offload-bundler"), "--unbundle", "--type=o",
-                        f"--input={fat}", f"--targets=hipv4-amdgcn-amd-amdhsa--{arch}", f"--output={co}"],
+                        f"--input={part}", f"--targets=hipv4-amdgcn-amd-amdhsa--{arch}", f"--output={co}"],
                        check=True)
-        out = subprocess.run([os.path.join(ROCM_LLVM, "llvm-objdump"), "-d", "--no-show-raw-insn", co],
-                             check=True, capture_output=True, text=True)
-    return out.stdout
+        out.append(co)
+    return out
+
+
+def disassemble(so_path, arch="gfx950"):
+    """Disassembly text of all of the library's device code objects."""
+    with tempfile.TemporaryDirectory() as tmp:
+        texts = []
+        for co in code_objects(so_path, tmp, arch):
+            out = subprocess.run([os.path.join(ROCM_LLVM, "llvm-objdump"), "-d", "--no-show-raw-insn", co],
+                                 check=True, capture_output=True, text=True)
+            texts.append(out.stdout)
+    return "\n".join(texts)
 
 
 def parse(text):
