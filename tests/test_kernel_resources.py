@@ -26,16 +26,12 @@ ALLOWED_SPILLS = {
 
 
 def kernel_notes(so_path, arch="gfx950"):
-    """{kernel symbol: {field: int}} from the code object's AMDGPU metadata."""
+    """{kernel symbol: {field: int}} from the AMDGPU metadata of every code object."""
     with tempfile.TemporaryDirectory() as tmp:
-        fat = os.path.join(tmp, "fatbin")
-        co = os.path.join(tmp, "code.o")
-        subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", so_path, fat], check=True)
-        subprocess.run([os.path.join(H.ROCM_LLVM, "clang-offload-bundler"), "--unbundle", "--type=o",
-                        f"--input={fat}", f"--targets=hipv4-amdgcn-amd-amdhsa--{arch}", f"--output={co}"],
-                       check=True)
-        text = subprocess.run([os.path.join(H.ROCM_LLVM, "llvm-readelf"), "--notes", co], check=True,
-                              capture_output=True, text=True).stdout
+        text = "\n".join(
+            subprocess.run([os.path.join(H.ROCM_LLVM, "llvm-readelf"), "--notes", co], check=True,
+                           capture_output=True, text=True).stdout
+            for co in H.code_objects(so_path, tmp, arch))
     out, cur = {}, None
     for line in text.splitlines():
         m = re.match(r"\s+\.name:\s+(\S+)", line)
@@ -107,7 +103,8 @@ def test_kernels_do_not_spill_beyond_the_allowed():
     if not os.path.exists(api.LIB_PATH):
         pytest.skip("library not built")
     notes = kernel_notes(api.LIB_PATH)
-    assert any("fa_prefill_kernel" in k for k in notes), "no prefill kernel in the metadata"
+    assert any("fa_prefill_kernel" in k for k in notes) and any("fa_fp8_fwd_kernel" in k for k in notes), \
+        "every code object's metadata is read"
     bad = [f"{k}: {v.get('vgpr_spill_count')} VGPRs spilled" for k, v in notes.items()
            if v.get("vgpr_spill_count", 0) > ALLOWED_SPILLS.get(k, 0)]
     assert not bad, "\n".join(bad)
