@@ -537,15 +537,36 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fp8_fwd_kernel(FaFp8Params p) 
   auto softmax = [&](f32x16 (&sv)[2], int i, float cb) __attribute__((always_inline)) {
     const int n = n_lo + i;
     if (n < n_full_lo || n >= n_full_hi) {
+      // the row's visible keys in the block are the offsets [lo, hi] from base;
+      // slot (hb, a) holds offset 32 hb + 8 (a / 4) + a % 4, a compile-time
+      // constant, so a score costs one compare (two with a left window)
+      int base = n * BN + 4 * kg;
+      asm volatile("" : "+v"(base));  // keeps the offsets out of loop-invariant registers
+      int64_t hi = (int64_t)Lk - 1 - base;
+      if (p.causal) hi = min(hi, (int64_t)pos - base);
+      if (p.wr >= 0) hi = min(hi, (int64_t)pos + p.wr - base);
+      int h = (int)max(min(hi, (int64_t)BN), (int64_t)-1);
+      asm volatile("" : "+v"(h));  // 32-bit compares below (the bound fits)
+      if (p.wl < 0) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+        for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int key = n * BN + 32 * hb + 8 * (a >> 2) + 4 * kg + (a & 3);
-          const bool vis = (key < Lk) & (!p.causal | (key <= pos)) & ((p.wl < 0) | (key >= pos - p.wl)) &
-                           ((p.wr < 0) | (key <= pos + p.wr));
-          sv[hb][a] = vis ? sv[hb][a] : kNegInf;
-        }
+          for (int a = 0; a < 16; ++a) {
+            const int off = 32 * hb + 8 * (a >> 2) + (a & 3);
+            sv[hb][a] = off <= h ? sv[hb][a] : kNegInf;
+          }
+      } else {
+        const int64_t lo = (int64_t)pos - p.wl - base;
+        int l = (int)max(min(lo, (int64_t)BN), (int64_t)0);
+        asm volatile("" : "+v"(l));
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int a = 0; a < 16; ++a) {
+            const int off = 32 * hb + 8 * (a >> 2) + (a & 3);
+            sv[hb][a] = (off <= h && off >= l) ? sv[hb][a] : kNegInf;
+          }
+      }
     }
     // Exponent arguments relative to the current reference first (multiply-adds,
     // whose results the block maximum then takes without canonicalising each
