@@ -401,10 +401,10 @@ struct LaneMask {
 // Online softmax over one 32-key block held in s.  Scores are in units where
 // p = exp2(s * c - m * c): raw scores with c = scale * log2(e), or softcapped
 // log2-domain scores with c = 1 (a positive c keeps the maximum where it is).
-// m_run is the reference maximum in the same units.  Two partial row sums are
-// kept for this lane: l_run of the fp32 probabilities (for the log-sum-exp) and
-// l_bf of the bf16-rounded probabilities that enter the P V product (for the
-// division of O, so the weights of O sum to one exactly).  Masked entries are -inf.
+// Two partial row sums are kept for this lane: l_run of the fp32 probabilities
+// (for the log-sum-exp) and l_bf of the bf16-rounded probabilities that enter
+// the P V product (for the division of O, so the weights of O sum to one
+// exactly).  Masked entries are -inf.
 //
 // The reference moves only when the running maximum exceeds it by more than
 // 2^kRescaleLog2 (or on the first visible key): exponents stay below that bound,
@@ -414,34 +414,45 @@ struct LaneMask {
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kRescaleMax = 256.0f;  // 2^kRescaleLog2
 
+// Online softmax of one block of the decode kernel (S^T accumulator s, raw
+// scores; c turns them into log2 units).  M is the row's reference in log2
+// units (-inf while the row has seen no visible key).  The exponent arguments
+// are formed against the current reference first (multiply-adds, whose results
+// the block maximum then takes without canonicalising each score); the
+// reference moves, rescaling O and the sums, only when the block's maximum
+// exceeds it by more than kRescaleLog2 ("Attention kernels...", section 7.3: a
+// row with no visible key yet uses 0 as the offset, so exp2(-inf - 0) = 0).
 template <int D>
-__device__ __forceinline__ void online_softmax(f32x16& s, float& m_run, float& l_run, float& l_bf,
+__device__ __forceinline__ void online_softmax(const f32x16& s, float& M, float& l_run, float& l_bf,
                                                f32x16* o, float c, bf16x8& p0, bf16x8& p1) {
-  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+  const float nm = (M == kNegInf) ? 0.0f : -M;
+  f32x16 y;
 #pragma unroll
-  for (int a = 3; a < 15; a += 2) mx = fmaxf(fmaxf(mx, s[a]), s[a + 1]);
-  mx = fmaxf(mx, s[15]);
-  mx = pair_max(mx);
-  const float m_cand = fmaxf(m_run, mx);
-  // (-inf) - (-inf) is NaN, which compares false: no move while nothing is visible
-  if (__any((m_cand - m_run) * c > kRescaleLog2)) {
-    // a row that has seen no visible key keeps m = -inf; use 0 as the offset so
-    // that exp2(-inf - offset) = 0 instead of NaN ("Attention kernels...", section 7.3)
-    const float m_use = (m_cand == kNegInf) ? 0.0f : m_cand;
-    const float alpha = exp2_fast((m_run - m_use) * c);
+  for (int a = 0; a < 16; ++a) y[a] = __builtin_fmaf(s[a], c, nm);
+  float ym = fmaxf(fmaxf(y[0], y[1]), y[2]);
+#pragma unroll
+  for (int a = 3; a < 15; a += 2) ym = fmaxf(fmaxf(ym, y[a]), y[a + 1]);
+  ym = fmaxf(ym, y[15]);
+  ym = pair_max(ym);
+  const bool mv = (M == kNegInf) ? (ym != kNegInf) : (ym > kRescaleLog2);
+  if (__any(mv)) {
+    const float m_new = mv ? ym - nm : M;
+    const float alpha = mv ? exp2_fast(M - m_new) : 1.0f;
     l_run *= alpha;
     l_bf *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-    m_run = m_cand;
+    M = m_new;
+    const float nn = (M == kNegInf) ? 0.0f : -M;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) y[a] = __builtin_fmaf(s[a], c, nn);
   }
-  const float nmc = (m_run == kNegInf) ? 0.0f : -m_run * c;
   float rs = 0.0f;
   f32x8 x0, x1;
 #pragma unroll
   for (int a = 0; a < 8; ++a) {
-    x0[a] = exp2_fast(__builtin_fmaf(s[a], c, nmc));
-    x1[a] = exp2_fast(__builtin_fmaf(s[a + 8], c, nmc));
+    x0[a] = exp2_fast(y[a]);
+    x1[a] = exp2_fast(y[a + 8]);
   }
 #pragma unroll
   for (int a = 0; a < 8; ++a) rs += x0[a] + x1[a];
@@ -1637,7 +1648,7 @@ __device__ __forceinline__ void paged_body(const FaParams& p, char* smem, int un
       mo[(wave * 32 + col) * D + d] = o[db][a];
     }
   if (kg == 0) {
-    ml[wave * 32 + col] = m_run * c;   // log2 units
+    ml[wave * 32 + col] = m_run;       // log2 units
     ml[128 + wave * 32 + col] = l_w;
     ml[256 + wave * 32 + col] = lb_w;
   }
