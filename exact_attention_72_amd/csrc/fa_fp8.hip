@@ -16,8 +16,9 @@
 // Scales: a Q block is the 128 query rows of a workgroup, a K block the 64 keys
 // of a step, so both fold into the exponent's scalar factor; V has one scale per
 // (batch, KV head), applied once to O.  Probabilities enter the P V product as
-// 2^8 p relative to the row maximum (at most 256, inside e4m3's 448), so that
-// they keep e4m3's normal range down to 2^-14 of the maximum.
+// 2^8 p relative to the row's reference, which trails the running maximum by
+// at most 0.75 in log2 units (so at most 2^8.75 = 430, inside e4m3's 448), and
+// keep e4m3's normal range down to 2^-14 of the maximum or less.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
